@@ -1,0 +1,179 @@
+"""Pins of the oracle's group quantizers.
+
+* hand-worked examples (tests/golden/quant_examples.json);
+* the per-element rounding bound |v - q s| <= s/2 whenever the fp16 scale is
+  normal (the magnitude bound on rounding error the method's second
+  proposition rests on: reading note "note-257", section "Key results");
+* exact rational arithmetic for scales and codes (definition, not numpy casts);
+* exact round trip on the integer grid; ties to even; zero groups; packing.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import quant, formats
+from tests.exact import rn_fp32, rn_fp16, rn_e4m3_sat, rint_even
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "quant_examples.json")
+
+
+def _group(vals, G):
+    v = np.zeros((1, G), np.float32)
+    v[0, :len(vals)] = np.array(vals, np.float32)
+    return v
+
+
+def test_golden_int4_examples():
+    ex = json.load(open(GOLD))["int4"]
+    for e in ex:
+        v = _group(e["v"], 64)
+        q, s = quant.quantize_int(v, 7, 64)
+        assert int(s.view(np.uint16)[0, 0]) == e["scale_fp16_bits"], e["derivation"]
+        assert list(q[0, :len(e["codes"])]) == e["codes"]
+        assert not q[0, len(e["codes"]):].any()
+        p = quant.pack_nibbles(q)
+        assert list(p[0, :len(e["packed_first_bytes"])]) == e["packed_first_bytes"]
+
+
+def test_golden_fp4_examples():
+    ex = json.load(open(GOLD))["fp4"]
+    for e in ex:
+        v = _group(e["v"], 16)
+        q, s = quant.quantize_fp4(v, 16)
+        assert int(s[0, 0]) == e["scale_e4m3"], e["derivation"]
+        assert list(q[0, :len(e["nibbles"])]) == e["nibbles"]
+        p = quant.pack_nibbles(q)
+        assert list(p[0, :len(e["packed_first_bytes"])]) == e["packed_first_bytes"]
+
+
+def _data(rng, rows, K, kind):
+    if kind == "normal":
+        return rng.standard_normal((rows, K)).astype(np.float32)
+    if kind == "outlier":
+        x = rng.standard_normal((rows, K))
+        x[:, rng.choice(K, max(1, K // 100), replace=False)] *= 30
+        return x.astype(np.float16).astype(np.float32)
+    if kind == "tiny":     # pushes scales into fp16 subnormals
+        return (rng.standard_normal((rows, K)) * 1e-6).astype(np.float32)
+    if kind == "wide":
+        return (rng.standard_normal((rows, K)) * 10.0 ** rng.integers(-3, 3, (rows, 1))).astype(np.float32)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("qmax", [7, 127])
+@pytest.mark.parametrize("kind", ["normal", "outlier", "wide"])
+def test_rounding_error_bound_int(rng, qmax, kind):
+    v = _data(rng, 64, 512, kind)
+    q, s16 = quant.quantize_int(v, qmax, 64)
+    s = np.repeat(s16.astype(np.float64), 64, axis=1)
+    normal = np.repeat((np.abs(s16.astype(np.float32)) >= np.float32(2.0 ** -14)), 64, axis=1)
+    err = np.abs(v.astype(np.float64) - q.astype(np.float64) * s)
+    assert (err[normal] <= s[normal] / 2 * (1 + 1e-6)).all()
+    # the clamp is inactive where the scale is normal: the unclamped code is within range
+    t = np.rint(v.astype(np.float64) / np.where(s == 0, 1, s))
+    assert (np.abs(t[normal]) <= qmax).all()
+    assert q.min() >= -qmax and q.max() <= qmax
+
+
+def test_int4_never_minus_eight(rng):
+    v = _data(rng, 128, 1024, "tiny")
+    q, _ = quant.quantize_int(v, 7, 64)
+    assert q.min() >= -7
+
+
+@pytest.mark.parametrize("qmax,kind", [(7, "normal"), (7, "tiny"), (127, "outlier"), (7, "wide")])
+def test_scales_and_codes_exact_rational(rng, qmax, kind):
+    v = _data(rng, 4, 128, kind)
+    q, s16 = quant.quantize_int(v, qmax, 64)
+    for i in range(v.shape[0]):
+        for g in range(2):
+            grp = [Fraction(float(x)) for x in v[i, g * 64:(g + 1) * 64]]
+            a = max(abs(x) for x in grp)
+            s = rn_fp16(rn_fp32(a / qmax))
+            assert Fraction(float(s16[i, g])) == s
+            for k, x in enumerate(grp):
+                code = 0 if s == 0 else max(-qmax, min(qmax, rint_even(rn_fp32(x / s))))
+                assert int(q[i, g * 64 + k]) == code
+
+
+def test_fp4_exact_rational(rng):
+    v = _data(rng, 8, 64, "wide")
+    q, s8 = quant.quantize_fp4(v, 16)
+    for i in range(v.shape[0]):
+        for g in range(4):
+            grp = [Fraction(float(x)) for x in v[i, g * 16:(g + 1) * 16]]
+            a = max(abs(x) for x in grp)
+            s = rn_e4m3_sat(rn_fp32(a / 6))
+            assert Fraction(float(formats.e4m3_decode(s8[i, g]))) == s
+            for k, x in enumerate(grp):
+                t = rn_fp32(x / s) if s else Fraction(0)
+                # nearest E2M1 magnitude with ties to the even mantissa, computed from the grid
+                mags = [Fraction(m) for m in (0, 0.5, 1, 1.5, 2, 3, 4, 6)]
+                at = min(abs(t), Fraction(6))
+                d = [abs(at - m) for m in mags]
+                best = min(d)
+                cands = [j for j in range(8) if d[j] == best]
+                j = [c for c in cands if c % 2 == 0][0] if len(cands) > 1 else cands[0]
+                val = -mags[j] if t < 0 else mags[j]
+                assert Fraction(float(formats.e2m1_decode(q[i, g * 16 + k]))) == val
+
+
+def test_fp4_error_bounds(rng):
+    v = _data(rng, 64, 256, "outlier")
+    q, s8 = quant.quantize_fp4(v, 16)
+    s = np.repeat(formats.e4m3_decode(s8), 16, axis=1)
+    deq = formats.e2m1_decode(q) * s
+    t = np.abs(v.astype(np.float64)) / np.where(s == 0, 1, s)
+    spacing = np.where(t < 2, 0.5, np.where(t < 4, 1.0, 2.0))
+    inside = t <= 6
+    err = np.abs(v - deq)
+    assert (err[inside] <= (spacing * s / 2)[inside] * (1 + 1e-6)).all()
+    sat = ~inside
+    assert (err[sat] <= (np.abs(v) - 6 * s)[sat] * (1 + 1e-6) + 1e-30).all()
+
+
+def test_exact_grid_round_trip(rng):
+    # v = q * 2^-4 with |q| <= 7 and a +-7 in every group: s = 2^-4 exactly and codes come back
+    rows, K = 16, 256
+    q = rng.integers(-7, 8, (rows, K))
+    for g in range(K // 64):
+        q[:, g * 64 + rng.integers(0, 64)] = rng.choice([-7, 7], rows)
+    v = (q * 2.0 ** -4).astype(np.float32)
+    qq, s = quant.quantize_int(v, 7, 64)
+    assert np.array_equal(qq, q)
+    assert (s.astype(np.float64) == 2.0 ** -4).all()
+
+
+def test_ties_go_to_even():
+    # s = 1 (absmax 7): v = n + 1/2 -> even neighbour
+    v = np.zeros((1, 64), np.float32)
+    v[0, 0] = 7.0
+    halves = [-6.5, -5.5, -4.5, -3.5, -2.5, -1.5, -0.5, 0.5, 1.5, 2.5, 3.5, 4.5, 5.5, 6.5]
+    v[0, 1:1 + len(halves)] = halves
+    q, s = quant.quantize_int(v, 7, 64)
+    assert float(s[0, 0]) == 1.0
+    assert list(q[0, 1:1 + len(halves)]) == [-6, -6, -4, -4, -2, -2, 0, 0, 2, 2, 4, 4, 6, 6]
+
+
+def test_zero_group():
+    v = np.zeros((2, 128), np.float32)
+    v[1, 64:] = 1.0
+    q, s = quant.quantize_int(v, 7, 64)
+    assert float(s[0, 0]) == 0 and float(s[0, 1]) == 0 and float(s[1, 0]) == 0
+    assert not q[0].any() and not q[1, :64].any()
+    qf, sf = quant.quantize_fp4(v, 16)
+    assert not qf[0].any() and not sf[0].any()
+
+
+def test_packing_round_trip(rng):
+    q = rng.integers(-7, 8, (5, 128)).astype(np.int8)
+    p = quant.pack_nibbles(q)
+    assert p.shape == (5, 64)
+    assert (p[:, 0] & 0xF).tolist() == (q[:, 0] & 0xF).tolist()
+    assert (p[:, 0] >> 4).tolist() == (q[:, 1] & 0xF).tolist()
+    assert np.array_equal(quant.unpack_int4(p), q)
+    nib = rng.integers(0, 16, (3, 32)).astype(np.uint8)
+    assert np.array_equal(quant.unpack_nibbles(quant.pack_nibbles(nib)), nib)
