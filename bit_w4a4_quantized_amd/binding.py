@@ -1,0 +1,229 @@
+"""ctypes binding over libsvdq.so (the C ABI in include/svdq.h).
+
+Argument marshalling only: every computation runs in the HIP kernels of the
+library.  Tensors are torch tensors on the current HIP device (PyTorch is used
+for device memory and streams); their data pointers and the current stream
+are handed to the C entry points of the same names.  The module refuses to
+run when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsvdq.so")
+
+FORMATS = {"int4": 0, "int8": 1, "fp4": 2}
+GROUP = {"int4": 64, "int8": 64, "fp4": 16}
+
+_lib = None
+
+_c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+
+_SIGS = {
+    "svdq_code_row_bytes": (_c_size, [_c_int, _c_int]),
+    "svdq_scale_row_bytes": (_c_size, [_c_int, _c_int]),
+    "svdq_quantize_down": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp]),
+    "svdq_gemm_w4a4_up": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
+    "svdq_linear_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
+    "svdq_linear": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _c_size, _vp, _vp]),
+    "svdq_quantize_weight": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "svdq_linear_unfused_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "svdq_linear_unfused": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _c_size, _vp, _vp]),
+    "svdq_gemm_w4a16": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
+    "svdq_gelu_tanh_smooth": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp]),
+    "svdq_status_string": (ctypes.c_char_p, [_c_int]),
+    "svdq_version": (ctypes.c_char_p, []),
+}
+
+
+class SvdqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsvdq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bit_w4a4_quantized_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().svdq_status_string(s).decode()
+
+
+def version() -> str:
+    return lib().svdq_version().decode()
+
+
+def _fmt(fmt) -> int:
+    return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def _p(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(name: str, st: int):
+    if st != 0:
+        raise SvdqError(name, st)
+
+
+def _need(t, dtype, shape, what):
+    import torch
+    if t is None:
+        raise ValueError(f"{what} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t
+
+
+# ------------------------------------------------------------------ sizes
+def code_row_bytes(K: int, fmt) -> int:
+    return int(lib().svdq_code_row_bytes(K, _fmt(fmt)))
+
+
+def scale_row_entries(K: int, fmt) -> int:
+    return K // GROUP[fmt] if isinstance(fmt, str) else K // (16 if int(fmt) == 2 else 64)
+
+
+def scale_dtype(fmt):
+    import torch
+    return torch.uint8 if _fmt(fmt) == 2 else torch.float16
+
+
+def linear_workspace_bytes(M: int, K: int, r: int, fmt) -> int:
+    return int(lib().svdq_linear_workspace_bytes(M, K, r, _fmt(fmt)))
+
+
+def linear_unfused_workspace_bytes(M: int, N: int, K: int, r: int, fmt) -> int:
+    return int(lib().svdq_linear_unfused_workspace_bytes(M, N, K, r, _fmt(fmt)))
+
+
+# ------------------------------------------------------------------ entry points (same names as the C ABI)
+def svdq_quantize_down(x_hat, l1t, fmt, xq=None, xs=None, t=None, stream=None):
+    """Kernel A.  x_hat fp16 [M, K]; l1t fp16 [r, K] or None.  Returns (xq, xs, t)."""
+    import torch
+    M, K = x_hat.shape
+    r = 0 if l1t is None else l1t.shape[0]
+    _need(x_hat, torch.float16, None, "x_hat")
+    if l1t is not None:
+        _need(l1t, torch.float16, (r, K), "l1t")
+    dev = x_hat.device
+    if xq is None:
+        xq = torch.empty((M, code_row_bytes(K, fmt)), dtype=torch.uint8, device=dev)
+    if xs is None:
+        xs = torch.empty((M, scale_row_entries(K, fmt)), dtype=scale_dtype(fmt), device=dev)
+    if r and t is None:
+        t = torch.empty((M, r), dtype=torch.float16, device=dev)
+    _check("svdq_quantize_down", lib().svdq_quantize_down(
+        _p(x_hat), _p(l1t), M, K, r, _fmt(fmt), _p(xq), _p(xs), _p(t), _stream(stream)))
+    return xq, xs, t
+
+
+def svdq_gemm_w4a4_up(xq, xs, t, wq, ws, l2, bias, K, fmt, y=None, stream=None):
+    """Kernel B.  Returns y fp16 [M, N]."""
+    import torch
+    M = xq.shape[0]
+    N = wq.shape[0]
+    r = 0 if l2 is None else l2.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=xq.device)
+    _check("svdq_gemm_w4a4_up", lib().svdq_gemm_w4a4_up(
+        _p(xq), _p(xs), _p(t), _p(wq), _p(ws), _p(l2), _p(bias), M, N, K, r, _fmt(fmt), _p(y), _stream(stream)))
+    return y
+
+
+def svdq_linear(x_hat, l1t, wq, ws, l2, bias, fmt, workspace=None, y=None, stream=None):
+    """Kernel A then Kernel B.  Returns y fp16 [M, N]."""
+    import torch
+    M, K = x_hat.shape
+    N = wq.shape[0]
+    r = 0 if l1t is None else l1t.shape[0]
+    need = linear_workspace_bytes(M, K, r, fmt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x_hat.device)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x_hat.device)
+    _check("svdq_linear", lib().svdq_linear(
+        _p(x_hat), _p(l1t), _p(wq), _p(ws), _p(l2), _p(bias), M, N, K, r, _fmt(fmt),
+        _p(workspace), workspace.numel() * workspace.element_size(), _p(y), _stream(stream)))
+    return y
+
+
+def svdq_quantize_weight(r_t, fmt, wq=None, ws=None, stream=None):
+    """Offline: R^T fp32 [N, K] -> (wq, ws)."""
+    import torch
+    N, K = r_t.shape
+    _need(r_t, torch.float32, None, "r_t")
+    if wq is None:
+        wq = torch.empty((N, code_row_bytes(K, fmt)), dtype=torch.uint8, device=r_t.device)
+    if ws is None:
+        ws = torch.empty((N, scale_row_entries(K, fmt)), dtype=scale_dtype(fmt), device=r_t.device)
+    _check("svdq_quantize_weight", lib().svdq_quantize_weight(
+        _p(r_t), N, K, _fmt(fmt), _p(wq), _p(ws), _stream(stream)))
+    return wq, ws
+
+
+def svdq_linear_unfused(x_hat, l1t, wq, ws, l2, bias, fmt, workspace=None, y=None, stream=None):
+    """The branch as separate kernels (measurement only).  Returns y fp16 [M, N]."""
+    import torch
+    M, K = x_hat.shape
+    N = wq.shape[0]
+    r = 0 if l1t is None else l1t.shape[0]
+    need = linear_unfused_workspace_bytes(M, N, K, r, fmt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x_hat.device)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x_hat.device)
+    _check("svdq_linear_unfused", lib().svdq_linear_unfused(
+        _p(x_hat), _p(l1t), _p(wq), _p(ws), _p(l2), _p(bias), M, N, K, r, _fmt(fmt),
+        _p(workspace), workspace.numel() * workspace.element_size(), _p(y), _stream(stream)))
+    return y
+
+
+def svdq_gemm_w4a16(x, wq, ws, bias, y=None, stream=None):
+    """W4A16 control.  x fp16 [M, K]; wq uint8 [N, K/2]; ws fp16 [N, K/64]."""
+    import torch
+    M, K = x.shape
+    N = wq.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _check("svdq_gemm_w4a16", lib().svdq_gemm_w4a16(
+        _p(x), _p(wq), _p(ws), _p(bias), M, N, K, _p(y), _stream(stream)))
+    return y
+
+
+def svdq_gelu_tanh_smooth(y, lam, out=None, stream=None):
+    """fp16(gelu_tanh(y) / lam) for y fp16 [M, C], lam fp32 [C]."""
+    import torch
+    M, C = y.shape
+    if out is None:
+        out = torch.empty_like(y)
+    _check("svdq_gelu_tanh_smooth", lib().svdq_gelu_tanh_smooth(
+        _p(y), _p(lam), M, C, _p(out), _stream(stream)))
+    return out

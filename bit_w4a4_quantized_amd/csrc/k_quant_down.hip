@@ -1,0 +1,202 @@
+// Kernel A: quantize the smoothed activations and compute the down projection
+// T = X_hat L1 in one pass over X_hat.
+//
+// Practice page "sota-314", section "Do this": the down projection is fused
+// with quantization because the two read the same input; reading note
+// "note-257", section "Key results": unfused, the branch pays an extra 16-bit
+// read of the activations.
+//
+// Work decomposition (gfx950, wave64):
+//   one workgroup = 4 waves = 16 token rows; the waves split K into 64-column
+//   chunks round-robin and each keeps its 16 x r partial of T in MFMA
+//   accumulators; the partials are summed through LDS at the end (fixed order,
+//   deterministic, no atomics).
+//   Lane l of a wave owns row (l % 16) and the 8-column slices
+//   [8 (l/16), +8) and [32 + 8 (l/16), +8) of each chunk: one 16-byte load
+//   each.  That is exactly the operand layout of v_mfma_f32_16x16x32_f16 for
+//   the chunk's two 32-column halves, so the fp16 values feed the matrix core
+//   straight from the registers they were quantized from.
+//   Group absmax: within the lane, then across the 4 lanes of the row with two
+//   cross-lane xor shuffles (INT, group 64) or one (FP4, group 16).
+//   NB chunks are loaded before any is processed, to keep enough HBM reads
+//   in flight.
+#include "kernels.h"
+#include "quant_core.h"
+
+namespace svdq {
+
+template <int FMT, int RB, bool QUANT>
+__global__ void __launch_bounds__(256)
+k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M, int K,
+             uint8_t* __restrict__ xq, uint8_t* __restrict__ xs, __half* __restrict__ t) {
+  constexpr int NB = 4;                     // chunks in flight per wave
+  constexpr int R = RB * 16;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row = lane & 15;
+  const int sub = lane >> 4;
+  const int m = blockIdx.x * 16 + row;
+  const bool valid = m < M;
+  const int nchunks = K >> 6;
+  const __half* xrow = x + (size_t)(valid ? m : 0) * K;
+
+  v4f acc[RB > 0 ? RB : 1];
+#pragma unroll
+  for (int j = 0; j < (RB > 0 ? RB : 1); j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = wave; c0 < nchunks; c0 += 4 * NB) {
+    uint4 xv[NB][2];
+    uint4 bv[NB][RB > 0 ? RB : 1][2];
+#pragma unroll
+    for (int i = 0; i < NB; i++) {
+      const int c = c0 + 4 * i;
+      if (c < nchunks) {
+        const int col = c * 64 + sub * 8;
+        if (valid) {
+          xv[i][0] = *reinterpret_cast<const uint4*>(xrow + col);
+          xv[i][1] = *reinterpret_cast<const uint4*>(xrow + col + 32);
+        } else {
+          xv[i][0] = make_uint4(0, 0, 0, 0);
+          xv[i][1] = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < RB; j++) {
+          const __half* lrow = l1t + (size_t)(j * 16 + row) * K + col;
+          bv[i][j][0] = *reinterpret_cast<const uint4*>(lrow);
+          bv[i][j][1] = *reinterpret_cast<const uint4*>(lrow + 32);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NB; i++) {
+      const int c = c0 + 4 * i;
+      if (c >= nchunks) break;
+      // ---- down projection on the matrix core (fp16 in, fp32 accumulate)
+#pragma unroll
+      for (int j = 0; j < RB; j++) {
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(xv[i][0]), as_h8(bv[i][j][0]), acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(xv[i][1]), as_h8(bv[i][j][1]), acc[j], 0, 0, 0);
+      }
+      if (!QUANT) continue;
+      // ---- quantize
+      float v[16];
+      unpack_h8(xv[i][0], v);
+      unpack_h8(xv[i][1], v + 8);
+      const int col = c * 64 + sub * 8;
+      if (FMT == FMT_INT4 || FMT == FMT_INT8) {
+        const float qmax = FMT == FMT_INT4 ? 7.0f : 127.0f;
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; e++) amax = fmaxf(amax, fabsf(v[e]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        uint16_t sbits;
+        const float s = int_scale(amax, qmax, &sbits);
+        int q[16];
+#pragma unroll
+        for (int e = 0; e < 16; e++) q[e] = int_code(v[e], s, qmax);
+        if (valid) {
+          if (FMT == FMT_INT4) {
+            uint8_t* dst = xq + (size_t)m * (K >> 1);
+            *reinterpret_cast<uint32_t*>(dst + (col >> 1)) = pack8(q);
+            *reinterpret_cast<uint32_t*>(dst + ((col + 32) >> 1)) = pack8(q + 8);
+          } else {
+            uint8_t* dst = xq + (size_t)m * K;
+            *reinterpret_cast<uint2*>(dst + col) = make_uint2(pack4_i8(q), pack4_i8(q + 4));
+            *reinterpret_cast<uint2*>(dst + col + 32) = make_uint2(pack4_i8(q + 8), pack4_i8(q + 12));
+          }
+          if (sub == 0) reinterpret_cast<uint16_t*>(xs)[(size_t)m * (K >> 6) + c] = sbits;
+        }
+      } else {  // FP4: groups of 16 = two lanes (sub, sub^1) x 8 values
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) { a0 = fmaxf(a0, fabsf(v[e])); a1 = fmaxf(a1, fabsf(v[8 + e])); }
+        a0 = fmaxf(a0, __shfl_xor(a0, 16));
+        a1 = fmaxf(a1, __shfl_xor(a1, 16));
+        uint32_t b0, b1;
+        const float s0 = fp4_scale(a0, &b0);
+        const float s1 = fp4_scale(a1, &b1);
+        int q[16];
+#pragma unroll
+        for (int e = 0; e < 8; e++) { q[e] = (int)fp4_code(v[e], s0); q[8 + e] = (int)fp4_code(v[8 + e], s1); }
+        if (valid) {
+          uint8_t* dst = xq + (size_t)m * (K >> 1);
+          *reinterpret_cast<uint32_t*>(dst + (col >> 1)) = pack8(q);
+          *reinterpret_cast<uint32_t*>(dst + ((col + 32) >> 1)) = pack8(q + 8);
+          if ((sub & 1) == 0) {
+            uint8_t* sd = xs + (size_t)m * (K >> 4) + c * 4 + (sub >> 1);
+            sd[0] = (uint8_t)b0;
+            sd[2] = (uint8_t)b1;
+          }
+        }
+      }
+    }
+  }
+
+  if (RB > 0) {
+    // ---- reduce the four waves' partials of T (fixed order) and store fp16
+    __shared__ float part[4][16][R > 0 ? R : 1];
+#pragma unroll
+    for (int j = 0; j < RB; j++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) part[wave][4 * sub + i][j * 16 + row] = acc[j][i];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 16 * R; idx += 256) {
+      const int rr = idx / R, cc = idx % R;
+      const int mm = blockIdx.x * 16 + rr;
+      if (mm < M) {
+        const float s = ((part[0][rr][cc] + part[1][rr][cc]) + part[2][rr][cc]) + part[3][rr][cc];
+        t[(size_t)mm * R + cc] = __float2half_rn(s);
+      }
+    }
+  }
+}
+
+template <int FMT, int RB, bool QUANT = true>
+static hipError_t launch_qd(const QuantDownArgs& a, hipStream_t s) {
+  dim3 grid((a.M + 15) / 16);
+  hipLaunchKernelGGL((k_quant_down<FMT, RB, QUANT>), grid, dim3(256), 0, s, (const __half*)a.x, (const __half*)a.l1t,
+                     a.M, a.K, (uint8_t*)a.xq, (uint8_t*)a.xs, (__half*)a.t);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_qd_r(const QuantDownArgs& a, hipStream_t s) {
+  switch (a.r) {
+    case 0: return launch_qd<FMT, 0>(a, s);
+    case 16: return launch_qd<FMT, 1>(a, s);
+    case 32: return launch_qd<FMT, 2>(a, s);
+    case 48: return launch_qd<FMT, 3>(a, s);
+    case 64: return launch_qd<FMT, 4>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_quant_down(const QuantDownArgs& a, hipStream_t s) {
+  switch (a.fmt) {
+    case FMT_INT4: return launch_qd_r<FMT_INT4>(a, s);
+    case FMT_INT8: return launch_qd_r<FMT_INT8>(a, s);
+    case FMT_FP4: return launch_qd_r<FMT_FP4>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Unfused comparison: quantization alone (no branch) ...
+hipError_t launch_quant_only(const void* x, int M, int K, int fmt, void* xq, void* xs, hipStream_t s) {
+  QuantDownArgs a{x, nullptr, M, K, 0, fmt, xq, xs, nullptr};
+  return launch_quant_down(a, s);
+}
+
+// ... and the down projection alone, a second full read of X_hat.
+hipError_t launch_down_only(const void* x, const void* l1t, int M, int K, int r, void* t, hipStream_t s) {
+  QuantDownArgs a{x, l1t, M, K, r, FMT_INT4, nullptr, nullptr, t};
+  switch (r) {
+    case 16: return launch_qd<FMT_INT4, 1, false>(a, s);
+    case 32: return launch_qd<FMT_INT4, 2, false>(a, s);
+    case 48: return launch_qd<FMT_INT4, 3, false>(a, s);
+    case 64: return launch_qd<FMT_INT4, 4, false>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace svdq

@@ -1,0 +1,80 @@
+// Offline weight quantizer: the residual R = W_hat - L1 L2 (given as R^T fp32
+// [N, K], K contiguous per output column) to the codes and scales Kernel B
+// reads.  Practice page "sota-314", section "Do this": only the residual is
+// quantized, per group along K with a symmetric absmax scale.  One thread
+// per group; not on the timed path.
+#include "kernels.h"
+#include "quant_core.h"
+
+namespace svdq {
+
+template <int FMT>
+__global__ void __launch_bounds__(256)
+k_quant_weight(const float* __restrict__ r_t, int N, int K, uint8_t* __restrict__ wq,
+               uint8_t* __restrict__ ws) {
+  constexpr int G = FMT == FMT_FP4 ? 16 : 64;
+  const int gpr = K / G;
+  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (size_t)N * gpr) return;
+  const int n = (int)(gid / gpr), g = (int)(gid % gpr);
+  const float* src = r_t + (size_t)n * K + (size_t)g * G;
+  float v[G];
+#pragma unroll
+  for (int e = 0; e < G; e += 4) {
+    const float4 f = *reinterpret_cast<const float4*>(src + e);
+    v[e] = f.x; v[e + 1] = f.y; v[e + 2] = f.z; v[e + 3] = f.w;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < G; e++) amax = fmaxf(amax, fabsf(v[e]));
+  if (FMT == FMT_INT4 || FMT == FMT_INT8) {
+    const float qmax = FMT == FMT_INT4 ? 7.0f : 127.0f;
+    uint16_t sbits;
+    const float s = int_scale(amax, qmax, &sbits);
+    reinterpret_cast<uint16_t*>(ws)[(size_t)n * gpr + g] = sbits;
+    int q[G];
+#pragma unroll
+    for (int e = 0; e < G; e++) q[e] = int_code(v[e], s, qmax);
+    if (FMT == FMT_INT4) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(wq + (size_t)n * (K >> 1) + (size_t)g * (G >> 1));
+#pragma unroll
+      for (int e = 0; e < G; e += 8) dst[e >> 3] = pack8(q + e);
+    } else {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(wq + (size_t)n * K + (size_t)g * G);
+#pragma unroll
+      for (int e = 0; e < G; e += 4) dst[e >> 2] = pack4_i8(q + e);
+    }
+  } else {
+    uint32_t b;
+    const float s = fp4_scale(amax, &b);
+    ws[(size_t)n * gpr + g] = (uint8_t)b;
+    int q[G];
+#pragma unroll
+    for (int e = 0; e < G; e++) q[e] = (int)fp4_code(v[e], s);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(wq + (size_t)n * (K >> 1) + (size_t)g * (G >> 1));
+#pragma unroll
+    for (int e = 0; e < G; e += 8) dst[e >> 3] = pack8(q + e);
+  }
+}
+
+hipError_t launch_quant_weight(const float* r_t, int N, int K, int fmt, void* wq, void* ws, hipStream_t s) {
+  const int G = fmt == FMT_FP4 ? 16 : 64;
+  const size_t groups = (size_t)N * (K / G);
+  dim3 grid((unsigned)((groups + 255) / 256));
+  switch (fmt) {
+    case FMT_INT4:
+      hipLaunchKernelGGL(k_quant_weight<FMT_INT4>, grid, dim3(256), 0, s, r_t, N, K, (uint8_t*)wq, (uint8_t*)ws);
+      break;
+    case FMT_INT8:
+      hipLaunchKernelGGL(k_quant_weight<FMT_INT8>, grid, dim3(256), 0, s, r_t, N, K, (uint8_t*)wq, (uint8_t*)ws);
+      break;
+    case FMT_FP4:
+      hipLaunchKernelGGL(k_quant_weight<FMT_FP4>, grid, dim3(256), 0, s, r_t, N, K, (uint8_t*)wq, (uint8_t*)ws);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace svdq

@@ -1,0 +1,91 @@
+// Device-side quantizer core for gfx950: absmax group scales, round-half-even
+// codes, E4M3 / E2M1 encoders and nibble packing.
+//
+// The group quantization rule is the per-group symmetric quantization of the
+// practice page "sota-314", section "Do this" (INT4 group 64 with 16-bit
+// scales, NVFP4 group 16 with FP8 scales).  The exact arithmetic:
+//   INT  : s16 = fp16_rne(fp32(absmax) / qmax); code = clamp(rint(fp32(v) / s), +-qmax)
+//   FP4  : s8  = e4m3_rne_sat(fp32(absmax) / 6); code = nearest E2M1 (even-mantissa ties)
+// Divisions are IEEE fp32 (correctly rounded: the HIP default without
+// fast-math); rintf is round-half-even; fp32 -> fp16 conversion is RNE with
+// subnormals kept.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace svdq {
+
+// fp16 scale for an INT group: returns the fp16 bits and the scale as float.
+__device__ __forceinline__ float int_scale(float amax, float qmax, uint16_t* bits) {
+  __half h = __float2half_rn(amax / qmax);
+  *bits = __half_as_ushort(h);
+  return __half2float(h);
+}
+
+// Code of one value against a stored scale s (s == 0 -> 0).
+__device__ __forceinline__ int int_code(float v, float s, float qmax) {
+  if (s == 0.0f) return 0;
+  float t = rintf(v / s);
+  t = fminf(fmaxf(t, -qmax), qmax);
+  return (int)t;
+}
+
+// fp32 (finite, >= 0) -> E4M3FN byte, round to nearest even, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_encode_pos(float a) {
+  if (!(a < 448.0f)) return 0x7Eu;
+  if (a < 0.015625f) {                        // below the smallest normal 2^-6: spacing 2^-9
+    return (uint32_t)rintf(a * 512.0f);       // 0..8 (8 == smallest normal, code 0x08)
+  }
+  int e;
+  (void)frexpf(a, &e);                        // a = f * 2^e, f in [0.5, 1)
+  e -= 1;                                     // a in [2^e, 2^(e+1)), e in [-6, 8]
+  float m = rintf(ldexpf(a, 3 - e));          // 8..16, exact scaling by a power of two
+  uint32_t mi = (uint32_t)m;
+  uint32_t code;
+  if (mi == 16u) code = (uint32_t)(e + 1 + 7) << 3;
+  else code = ((uint32_t)(e + 7) << 3) | (mi - 8u);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t b) {
+  uint32_t e = (b >> 3) & 0xFu, m = b & 7u;
+  float v = (e == 0) ? ldexpf((float)m, -9) : ldexpf((float)(8u + m), (int)e - 10);
+  return (b & 0x80u) ? -v : v;
+}
+
+// E4M3 scale of an FP4 group.
+__device__ __forceinline__ float fp4_scale(float amax, uint32_t* byte) {
+  uint32_t b = e4m3_encode_pos(amax / 6.0f);
+  *byte = b;
+  return e4m3_decode(b);
+}
+
+// E2M1 nibble of v against scale s: sign<<3 | magnitude index; ties to the
+// even mantissa (0.25->0, 0.75->1, 1.25->1, 1.75->2, 2.5->2, 3.5->4, 5->4).
+__device__ __forceinline__ uint32_t fp4_code(float v, float s) {
+  if (s == 0.0f) return 0u;
+  float t = v / s;
+  float a = fabsf(t);
+  uint32_t idx = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                 (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                 (uint32_t)(a > 5.0f);
+  return (t < 0.0f && idx != 0u) ? (idx | 8u) : idx;
+}
+
+// Pack 8 4-bit codes (low nibble first) into one 32-bit word.
+__device__ __forceinline__ uint32_t pack8(const int* q) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) w |= ((uint32_t)q[i] & 0xFu) << (4 * i);
+  return w;
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(const int* q) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) w |= ((uint32_t)q[i] & 0xFFu) << (8 * i);
+  return w;
+}
+
+}  // namespace svdq

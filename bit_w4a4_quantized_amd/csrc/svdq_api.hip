@@ -1,0 +1,227 @@
+// C-ABI layer: host-side argument validation and kernel launches for the
+// entry points declared in include/svdq.h.  Every check happens before any
+// HIP call; no exception leaves this file.
+#include "../../include/svdq.h"
+#include "kernels.h"
+
+using namespace svdq;
+
+namespace {
+
+constexpr int kMaxDim = 1 << 24;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+inline bool fmt_ok(int f) { return f == SVDQ_INT4_G64 || f == SVDQ_INT8_G64 || f == SVDQ_FP4_G16; }
+
+inline size_t code_bytes(int K, int fmt) { return fmt == SVDQ_INT8_G64 ? (size_t)K : (size_t)K / 2; }
+inline size_t scale_bytes(int K, int fmt) {
+  return fmt == SVDQ_FP4_G16 ? (size_t)K / 16 : (size_t)K / 64 * 2;
+}
+
+svdq_status check_dims(int M, int N, int K, int r) {
+  if (M < 0 || N < 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return SVDQ_ERR_SHAPE;
+  if (K % 64 != 0 || N % 16 != 0) return SVDQ_ERR_SHAPE;
+  if (r < 0 || r > 64 || r % 16 != 0) return SVDQ_ERR_SHAPE;
+  return SVDQ_OK;
+}
+
+svdq_status map_launch(hipError_t e) {
+  if (e == hipSuccess) return SVDQ_OK;
+  if (e == hipErrorNoBinaryForGpu || e == hipErrorInvalidDeviceFunction) return SVDQ_ERR_DEVICE;
+  return SVDQ_ERR_LAUNCH;
+}
+
+struct Workspace {
+  void* xq; void* xs; void* t; void* y0; size_t total;
+};
+
+Workspace carve(void* base, int M, int N, int K, int r, int fmt, bool with_y0) {
+  Workspace w{};
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  w.xq = b ? b + off : nullptr; off += round256((size_t)M * code_bytes(K, fmt));
+  w.xs = b ? b + off : nullptr; off += round256((size_t)M * scale_bytes(K, fmt));
+  w.t = (r > 0 && b) ? b + off : nullptr; off += round256((size_t)M * r * 2);
+  if (with_y0) { w.y0 = b ? b + off : nullptr; off += round256((size_t)M * N * 2); }
+  w.total = off;
+  return w;
+}
+
+svdq_status check_quant_down(const void* x_hat, const void* l1t, int M, int K, int r, int fmt,
+                             const void* xq, const void* xs, const void* t) {
+  if (!fmt_ok(fmt)) return SVDQ_ERR_FORMAT;
+  svdq_status st = check_dims(M, 16, K, r);
+  if (st != SVDQ_OK) return st;
+  if (M == 0) return SVDQ_OK;
+  if (!x_hat || !xq || !xs) return SVDQ_ERR_NULL;
+  if (r > 0 && (!l1t || !t)) return SVDQ_ERR_NULL;
+  if (!aligned16(x_hat) || !aligned16(xq) || !aligned16(xs)) return SVDQ_ERR_ALIGN;
+  if (r > 0 && (!aligned16(l1t) || !aligned16(t))) return SVDQ_ERR_ALIGN;
+  return SVDQ_OK;
+}
+
+svdq_status check_gemm(const void* xq, const void* xs, const void* t, const void* wq, const void* ws,
+                       const void* l2, const void* bias, int M, int N, int K, int r, int fmt,
+                       const void* y) {
+  if (!fmt_ok(fmt)) return SVDQ_ERR_FORMAT;
+  svdq_status st = check_dims(M, N, K, r);
+  if (st != SVDQ_OK) return st;
+  if (M == 0 || N == 0) return SVDQ_OK;
+  if (!xq || !xs || !wq || !ws || !y) return SVDQ_ERR_NULL;
+  if (r > 0 && (!t || !l2)) return SVDQ_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(wq) || !aligned16(ws) || !aligned16(y)) return SVDQ_ERR_ALIGN;
+  if (r > 0 && (!aligned16(t) || !aligned16(l2))) return SVDQ_ERR_ALIGN;
+  if (bias && !aligned16(bias)) return SVDQ_ERR_ALIGN;
+  return SVDQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t svdq_code_row_bytes(int K, svdq_format fmt) {
+  if (!fmt_ok(fmt) || K <= 0 || K % 64) return 0;
+  return code_bytes(K, fmt);
+}
+
+size_t svdq_scale_row_bytes(int K, svdq_format fmt) {
+  if (!fmt_ok(fmt) || K <= 0 || K % 64) return 0;
+  return scale_bytes(K, fmt);
+}
+
+svdq_status svdq_quantize_down(const void* x_hat, const void* l1t, int M, int K, int r, svdq_format fmt,
+                               void* xq, void* xs, void* t, void* stream) {
+  svdq_status st = check_quant_down(x_hat, l1t, M, K, r, fmt, xq, xs, t);
+  if (st != SVDQ_OK) return st;
+  if (M == 0) return SVDQ_OK;
+  QuantDownArgs a{x_hat, l1t, M, K, r, (int)fmt, xq, xs, t};
+  return map_launch(launch_quant_down(a, static_cast<hipStream_t>(stream)));
+}
+
+svdq_status svdq_gemm_w4a4_up(const void* xq, const void* xs, const void* t, const void* wq, const void* ws,
+                              const void* l2, const void* bias, int M, int N, int K, int r, svdq_format fmt,
+                              void* y, void* stream) {
+  svdq_status st = check_gemm(xq, xs, t, wq, ws, l2, bias, M, N, K, r, fmt, y);
+  if (st != SVDQ_OK) return st;
+  if (M == 0 || N == 0) return SVDQ_OK;
+  GemmArgs a{xq, xs, t, wq, ws, l2, bias, M, N, K, r, (int)fmt, y};
+  return map_launch(launch_gemm(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t svdq_linear_workspace_bytes(int M, int K, int r, svdq_format fmt) {
+  if (!fmt_ok(fmt) || check_dims(M, 16, K, r) != SVDQ_OK) return 0;
+  return carve(nullptr, M, 0, K, r, fmt, false).total;
+}
+
+svdq_status svdq_linear(const void* x_hat, const void* l1t, const void* wq, const void* ws, const void* l2,
+                        const void* bias, int M, int N, int K, int r, svdq_format fmt, void* workspace,
+                        size_t workspace_bytes, void* y, void* stream) {
+  if (!fmt_ok(fmt)) return SVDQ_ERR_FORMAT;
+  svdq_status st = check_dims(M, N, K, r);
+  if (st != SVDQ_OK) return st;
+  if (M == 0 || N == 0) return SVDQ_OK;
+  if (!x_hat || !wq || !ws || !y || !workspace) return SVDQ_ERR_NULL;
+  if (r > 0 && (!l1t || !l2)) return SVDQ_ERR_NULL;
+  if (!aligned16(workspace)) return SVDQ_ERR_ALIGN;
+  const Workspace w = carve(workspace, M, N, K, r, fmt, false);
+  if (workspace_bytes < w.total) return SVDQ_ERR_WORKSPACE;
+  st = check_quant_down(x_hat, l1t, M, K, r, fmt, w.xq, w.xs, w.t);
+  if (st != SVDQ_OK) return st;
+  st = check_gemm(w.xq, w.xs, w.t, wq, ws, l2, bias, M, N, K, r, fmt, y);
+  if (st != SVDQ_OK) return st;
+  if (M == 0 || N == 0) return SVDQ_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QuantDownArgs qa{x_hat, l1t, M, K, r, (int)fmt, w.xq, w.xs, w.t};
+  st = map_launch(launch_quant_down(qa, s));
+  if (st != SVDQ_OK) return st;
+  GemmArgs ga{w.xq, w.xs, w.t, wq, ws, l2, bias, M, N, K, r, (int)fmt, y};
+  return map_launch(launch_gemm(ga, s));
+}
+
+svdq_status svdq_quantize_weight(const float* r_t, int N, int K, svdq_format fmt, void* wq, void* ws,
+                                 void* stream) {
+  if (!fmt_ok(fmt)) return SVDQ_ERR_FORMAT;
+  svdq_status st = check_dims(0, N, K, 0);
+  if (st != SVDQ_OK) return st;
+  if (N == 0) return SVDQ_OK;
+  if (!r_t || !wq || !ws) return SVDQ_ERR_NULL;
+  if (!aligned16(r_t) || !aligned16(wq) || !aligned16(ws)) return SVDQ_ERR_ALIGN;
+  if (N == 0) return SVDQ_OK;
+  return map_launch(launch_quant_weight(r_t, N, K, (int)fmt, wq, ws, static_cast<hipStream_t>(stream)));
+}
+
+size_t svdq_linear_unfused_workspace_bytes(int M, int N, int K, int r, svdq_format fmt) {
+  if (!fmt_ok(fmt) || check_dims(M, N, K, r) != SVDQ_OK) return 0;
+  return carve(nullptr, M, N, K, r, fmt, true).total;
+}
+
+svdq_status svdq_linear_unfused(const void* x_hat, const void* l1t, const void* wq, const void* ws,
+                                const void* l2, const void* bias, int M, int N, int K, int r, svdq_format fmt,
+                                void* workspace, size_t workspace_bytes, void* y, void* stream) {
+  if (!fmt_ok(fmt)) return SVDQ_ERR_FORMAT;
+  svdq_status st = check_dims(M, N, K, r);
+  if (st != SVDQ_OK) return st;
+  if (M == 0 || N == 0) return SVDQ_OK;
+  if (!x_hat || !wq || !ws || !y || !workspace) return SVDQ_ERR_NULL;
+  if (r > 0 && (!l1t || !l2)) return SVDQ_ERR_NULL;
+  if (!aligned16(workspace)) return SVDQ_ERR_ALIGN;
+  const Workspace w = carve(workspace, M, N, K, r, fmt, true);
+  if (workspace_bytes < w.total) return SVDQ_ERR_WORKSPACE;
+  st = check_quant_down(x_hat, l1t, M, K, r, fmt, w.xq, w.xs, w.t);
+  if (st != SVDQ_OK) return st;
+  st = check_gemm(w.xq, w.xs, w.t, wq, ws, l2, bias, M, N, K, r, fmt, y);
+  if (st != SVDQ_OK) return st;
+  if (M == 0 || N == 0) return SVDQ_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = map_launch(launch_quant_only(x_hat, M, K, (int)fmt, w.xq, w.xs, s));
+  if (st != SVDQ_OK) return st;
+  if (r > 0) {
+    st = map_launch(launch_down_only(x_hat, l1t, M, K, r, w.t, s));
+    if (st != SVDQ_OK) return st;
+  }
+  GemmArgs ga{w.xq, w.xs, nullptr, wq, ws, nullptr, bias, M, N, K, 0, (int)fmt, r > 0 ? w.y0 : y};
+  st = map_launch(launch_gemm(ga, s));
+  if (st != SVDQ_OK || r == 0) return st;
+  return map_launch(launch_up_add(w.y0, w.t, l2, M, N, r, y, s));
+}
+
+svdq_status svdq_gemm_w4a16(const void* x, const void* wq, const void* ws, const void* bias, int M, int N,
+                            int K, void* y, void* stream) {
+  svdq_status st = check_dims(M, N, K, 0);
+  if (st != SVDQ_OK) return st;
+  if (M == 0 || N == 0) return SVDQ_OK;
+  if (!x || !wq || !ws || !y) return SVDQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(ws) || !aligned16(y)) return SVDQ_ERR_ALIGN;
+  if (bias && !aligned16(bias)) return SVDQ_ERR_ALIGN;
+  if (M == 0 || N == 0) return SVDQ_OK;
+  return map_launch(launch_w4a16(x, wq, ws, bias, M, N, K, y, static_cast<hipStream_t>(stream)));
+}
+
+svdq_status svdq_gelu_tanh_smooth(const void* y, const float* lambda, int M, int C, void* out, void* stream) {
+  if (M < 0 || C <= 0 || C % 8 != 0 || M > kMaxDim || C > kMaxDim) return SVDQ_ERR_SHAPE;
+  if (M == 0) return SVDQ_OK;
+  if (!y || !lambda || !out) return SVDQ_ERR_NULL;
+  if (!aligned16(y) || !aligned16(lambda) || !aligned16(out)) return SVDQ_ERR_ALIGN;
+  if (M == 0) return SVDQ_OK;
+  return map_launch(launch_gelu_smooth(y, lambda, M, C, out, static_cast<hipStream_t>(stream)));
+}
+
+const char* svdq_status_string(svdq_status s) {
+  switch (s) {
+    case SVDQ_OK: return "ok";
+    case SVDQ_ERR_NULL: return "a required pointer is NULL";
+    case SVDQ_ERR_SHAPE: return "shape outside the supported constraints (K % 64 == 0, N % 16 == 0, r in {0,16,32,48,64}, dims <= 2^24)";
+    case SVDQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case SVDQ_ERR_FORMAT: return "unknown or unsupported format";
+    case SVDQ_ERR_WORKSPACE: return "workspace too small";
+    case SVDQ_ERR_DEVICE: return "no gfx950 code object for the current device";
+    case SVDQ_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* svdq_version(void) { return "svdq-mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

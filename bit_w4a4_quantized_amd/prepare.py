@@ -1,0 +1,95 @@
+"""Offline preparation of one SVDQuant layer (host side, not on the timed path).
+
+Practice page "sota-314", section "Do this": smooth the activation outliers
+into the weight, take the SVD of the smoothed weight, keep the top r singular
+directions as a 16-bit branch and quantize only the residual.  Reading note
+"note-257", section "Key results": L1 = U Sigma[:, :r], L2 = V[:r, :].
+
+Host arithmetic (float64 LAPACK SVD; the smoothing factor and the smoothed
+activations in fp32 then fp16):
+    lambda_j = sqrt(fp32(max_i |X_ij|) / fp32(max_n |W_jn|))   (1 if either is 0)
+    X_hat    = fp16(fp32(X) / lambda)
+    W_hat    = lambda W                                     (float64)
+    L1 = fp16(U_r Sigma_r), L2 = fp16(V_r^T), R = W_hat - L1 L2   (float64 -> fp32)
+The residual's codes and scales are then produced on the GPU by
+svdq_quantize_weight.  The device tensors are laid out the way the kernels
+read them: L1^T [r, K], L2 [r, N], codes / scales per output column [N, ...].
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+
+def _channel_factor(x_cal: np.ndarray, w: np.ndarray) -> np.ndarray:
+    act_max = np.max(np.abs(np.asarray(x_cal, dtype=np.float32)), axis=0)
+    wt_max = np.max(np.abs(np.asarray(w, dtype=np.float32)), axis=1)
+    lam = np.ones(act_max.shape, dtype=np.float32)
+    nz = np.logical_and(act_max > 0, wt_max > 0)
+    lam[nz] = np.sqrt(act_max[nz] / wt_max[nz])
+    return lam
+
+
+@dataclass
+class HostLayer:
+    """Host-side result of the offline preparation."""
+    lam: np.ndarray       # fp32 [K]
+    l1t: np.ndarray       # fp16 [r, K]
+    l2: np.ndarray        # fp16 [r, N]
+    r_t: np.ndarray       # fp32 [N, K], residual transposed (K contiguous per output column)
+    bias: np.ndarray      # fp16 [N]
+
+    def smooth(self, x: np.ndarray) -> np.ndarray:
+        """Smoothed activations fp16(fp32(x) / lambda)."""
+        return (np.asarray(x, dtype=np.float32) / self.lam).astype(np.float16)
+
+
+def prepare_host(x_cal: np.ndarray, w: np.ndarray, bias: np.ndarray, r: int) -> HostLayer:
+    """Smoothing from calibration activations x_cal [M, K], SVD split of lambda W [K, N]."""
+    lam = _channel_factor(x_cal, w)
+    w_s = np.asarray(w, dtype=np.float64) * lam.astype(np.float64)[:, None]
+    K, N = w_s.shape
+    u, sig, vt = np.linalg.svd(w_s, full_matrices=False)
+    if r:
+        l1 = (u[:, :r] * sig[None, :r]).astype(np.float16)
+        l2 = vt[:r].astype(np.float16)
+        resid = w_s - np.matmul(l1.astype(np.float64), l2.astype(np.float64))
+    else:
+        l1 = np.zeros((K, 0), np.float16)
+        l2 = np.zeros((0, N), np.float16)
+        resid = w_s
+    return HostLayer(lam, np.ascontiguousarray(l1.T), l2, np.ascontiguousarray(resid.astype(np.float32).T),
+                     np.asarray(bias, dtype=np.float16))
+
+
+@dataclass
+class DeviceLayer:
+    """The prepared layer resident in device memory, ready for svdq_linear."""
+    fmt: str
+    K: int
+    N: int
+    r: int
+    l1t: Optional[object]   # torch fp16 [r, K] or None
+    l2: Optional[object]    # torch fp16 [r, N] or None
+    wq: object              # torch uint8 codes [N, ...]
+    ws: object              # torch scales [N, ...]
+    bias: Optional[object]  # torch fp16 [N]
+    lam: object             # torch fp32 [K]
+
+
+def to_device(h: HostLayer, fmt: str, device="cuda", stream=None) -> DeviceLayer:
+    """Upload the host layer and quantize its residual on the GPU."""
+    import torch
+    from .binding import svdq_quantize_weight
+    r = h.l1t.shape[0]
+    N, K = h.r_t.shape
+    r_t = torch.from_numpy(h.r_t).to(device)
+    wq, ws = svdq_quantize_weight(r_t, fmt, stream=stream)
+    l1t = torch.from_numpy(h.l1t).to(device) if r else None
+    l2 = torch.from_numpy(h.l2).to(device) if r else None
+    bias = torch.from_numpy(h.bias).to(device)
+    lam = torch.from_numpy(h.lam).to(device)
+    del r_t
+    return DeviceLayer(fmt, K, N, r, l1t, l2, wq, ws, bias, lam)

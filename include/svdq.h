@@ -1,0 +1,190 @@
+/*
+ * svdq.h -- C ABI of the fused SVDQuant W4A4 linear layer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer (SVDQuant, Li, Lin, Zhang, Cai, Li, Guo, Xie, Meng, Zhu, Han 2024,
+ * as described by the practice page "sota-314", section "Do this", and the
+ * reading note "note-257", section "Key results"):
+ *
+ *     Y = X_hat L1 L2  +  Q(X_hat) Q(R)  +  b,     R = W_hat - L1 L2,
+ *
+ * where X_hat / W_hat are the smoothed activations / weight, L1 L2 is the
+ * 16-bit rank-r branch taken off W_hat by truncated SVD, and Q() is per-group
+ * symmetric quantization along the reduction axis K.  The two fusions the
+ * pages name are the two kernels behind this ABI:
+ *   Kernel A  (svdq_quantize_down): quantize X_hat and compute the down
+ *             projection T = X_hat L1 in the same pass (same input);
+ *   Kernel B  (svdq_gemm_w4a4_up):  the low-bit GEMM with the up projection
+ *             T L2 and the bias in its epilogue (same output).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor pointers are DEVICE pointers, owned by the caller, row-major,
+ *    16-byte aligned.  The library never allocates or frees memory and keeps
+ *    no mutable global state; calls are thread-safe.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *    enqueued on it asynchronously; nothing synchronizes the device and there
+ *    are no host<->device copies.
+ *  - Arguments are validated on the host before any HIP call; a failed check
+ *    returns an error status and enqueues nothing.  A launch failure reported
+ *    by the runtime returns SVDQ_ERR_LAUNCH.  No C++ exception crosses the ABI.
+ *  - Shapes: M >= 0 and N >= 0 (0 = nothing to do: SVDQ_OK once the format
+ *    and the other dimensions check out, and the pointers may then be NULL,
+ *    as a zero-size tensor's are); K > 0 with
+ *    K % 64 == 0; N % 16 == 0; r % 16 == 0 and 0 <= r <= 64; M, N, K <= 2^24.
+ *  - Non-finite inputs are undefined behaviour.
+ *
+ * Formats (group quantization along K; groups per token row for activations,
+ * per output column for the weight; "sota-314", "Do this": INT4 group 64 with
+ * 16-bit scales, NVFP4 group 16 with FP8 scales, rank 16 at 8 bits):
+ *  SVDQ_INT4_G64 : codes in [-7, 7], two's-complement nibbles, two per byte
+ *                  (byte b = code 2b | code 2b+1 << 4); fp16 scale per 64.
+ *                  scale = fp16_rne(fp32(absmax) / 7.0f); code =
+ *                  clamp(rint_half_even(fp32(v) / scale), -7, 7); scale 0 ->
+ *                  codes 0.
+ *  SVDQ_INT8_G64 : same rule with 127; one int8 code per byte.
+ *  SVDQ_FP4_G16  : E2M1 codes (sign<<3 | magnitude index, magnitudes
+ *                  0,0.5,1,1.5,2,3,4,6), packed as INT4; one E4M3FN scale byte
+ *                  per 16: scale = e4m3_rne_sat(fp32(absmax) / 6.0f); code =
+ *                  nearest E2M1 to fp32(v)/scale, ties to the even mantissa,
+ *                  -0 -> +0.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SVDQ_OK = 0,
+  SVDQ_ERR_NULL = -1,      /* a required pointer is NULL                         */
+  SVDQ_ERR_SHAPE = -2,     /* M/N/K/r/C outside the documented constraints       */
+  SVDQ_ERR_ALIGN = -3,     /* a pointer is not 16-byte aligned                   */
+  SVDQ_ERR_FORMAT = -4,    /* unknown or unsupported format for this entry point */
+  SVDQ_ERR_WORKSPACE = -5, /* workspace smaller than the *_workspace_bytes value */
+  SVDQ_ERR_DEVICE = -6,    /* the current device is not a gfx950 GPU             */
+  SVDQ_ERR_LAUNCH = -7     /* the HIP runtime reported a launch error            */
+} svdq_status;
+
+typedef enum {
+  SVDQ_INT4_G64 = 0,
+  SVDQ_INT8_G64 = 1,
+  SVDQ_FP4_G16 = 2
+} svdq_format;
+
+/* Bytes of one row of codes for K columns (K/2 for 4-bit formats, K for INT8),
+ * and number of scale entries per row (K/64 or K/16).  Scales are fp16 (2 B)
+ * for the INT formats and E4M3 (1 B) for FP4.  Returns 0 for a bad format. */
+size_t svdq_code_row_bytes(int K, svdq_format fmt);
+size_t svdq_scale_row_bytes(int K, svdq_format fmt);
+
+/*
+ * Kernel A: quantize + down projection ("sota-314", "Do this": the down
+ * projection is fused with quantization because both read the same input;
+ * "note-257", "Key results").
+ *   x_hat : fp16 [M, K], the smoothed activations (smoothing already applied).
+ *   l1t   : fp16 [r, K] = L1^T; NULL iff r == 0.
+ *   xq    : out, codes [M, code_row_bytes(K)].
+ *   xs    : out, scales [M, K/G] (fp16 or E4M3 bytes).
+ *   t     : out, fp16 [M, r] = fp16_rne(X_hat L1), fp32 accumulation; NULL iff r == 0.
+ * The branch reads the unquantized 16-bit X_hat.
+ */
+svdq_status svdq_quantize_down(const void* x_hat, const void* l1t, int M, int K, int r,
+                               svdq_format fmt, void* xq, void* xs, void* t, void* stream);
+
+/*
+ * Kernel B: low-bit GEMM + up projection + bias ("sota-314", "Do this": the up
+ * projection is fused with the 4-bit compute because both write the same
+ * output).
+ *   Y = fp16_rne( sum_g sx[m,g] sw[n,g] P_g[m,n] + T L2 + b ),
+ *   P_g = sum over the group's K of q_x q_w (exact integers; fp32 accumulation
+ *   of the rescaled partials).
+ *   xq, xs : Kernel A's codes and scales for M rows.
+ *   t      : fp16 [M, r]; NULL iff r == 0.
+ *   wq     : codes [N, code_row_bytes(K)] -- K contiguous per output column.
+ *   ws     : scales [N, K/G].
+ *   l2     : fp16 [r, N]; NULL iff r == 0.
+ *   bias   : fp16 [N], or NULL for none.
+ *   y      : out, fp16 [M, N].
+ * r == 0 selects the bare low-bit GEMM (no branch).
+ */
+svdq_status svdq_gemm_w4a4_up(const void* xq, const void* xs, const void* t, const void* wq,
+                              const void* ws, const void* l2, const void* bias, int M, int N, int K,
+                              int r, svdq_format fmt, void* y, void* stream);
+
+/* Workspace svdq_linear needs: codes, scales and T for M rows, each part
+ * 256-byte aligned.  0 for a bad format or shape. */
+size_t svdq_linear_workspace_bytes(int M, int K, int r, svdq_format fmt);
+
+/*
+ * The fused layer: Kernel A then Kernel B on one stream, with codes, scales
+ * and T in the caller's workspace (>= svdq_linear_workspace_bytes).
+ * Arguments as for the two kernels above.
+ */
+svdq_status svdq_linear(const void* x_hat, const void* l1t, const void* wq, const void* ws,
+                        const void* l2, const void* bias, int M, int N, int K, int r,
+                        svdq_format fmt, void* workspace, size_t workspace_bytes, void* y,
+                        void* stream);
+
+/*
+ * Offline weight quantizer: the residual R = W_hat - L1 L2, given as
+ * R^T fp32 [N, K] (K contiguous per output column), to codes wq and scales ws
+ * in the layouts Kernel B reads ("sota-314", "Do this": quantize only the
+ * residual; round-to-nearest-even here, where the pages' own pipeline uses
+ * GPTQ).
+ */
+svdq_status svdq_quantize_weight(const float* r_t, int N, int K, svdq_format fmt, void* wq,
+                                 void* ws, void* stream);
+
+/* Workspace of the unfused comparison: svdq_linear's workspace plus an fp16
+ * [M, N] intermediate, 256-byte aligned. */
+size_t svdq_linear_unfused_workspace_bytes(int M, int N, int K, int r, svdq_format fmt);
+
+/*
+ * Unfused comparison (measurement only; "sota-314", "Do this", latency table:
+ * a rank-32 branch run as separate kernels): four launches -- quantize;
+ * down projection T = X_hat L1 (a second read of X_hat); the low-bit GEMM
+ * writing fp16 Y0 = fp16(Q(X_hat) Q(R) + b); up projection
+ * Y = fp16(Y0 + T L2) (a second read and write of the output).  Note the extra
+ * fp16 rounding of Y0: results agree with svdq_linear to fp16 tolerance, not
+ * bitwise.
+ */
+svdq_status svdq_linear_unfused(const void* x_hat, const void* l1t, const void* wq, const void* ws,
+                                const void* l2, const void* bias, int M, int N, int K, int r,
+                                svdq_format fmt, void* workspace, size_t workspace_bytes,
+                                void* y, void* stream);
+
+/*
+ * W4A16 control ("sota-314", "Do this" and "What it buys": the W4A16
+ * baseline and the layers kept at W4A16): Y = fp16_rne( X deq(W) + b ) with
+ * X fp16 [M, K] unquantized, W as SVDQ_INT4_G64 codes wq [N, K/2] and fp16
+ * scales ws [N, K/64], fp32 accumulation; bias may be NULL.  No branch.
+ */
+svdq_status svdq_gemm_w4a16(const void* x, const void* wq, const void* ws, const void* bias,
+                            int M, int N, int K, void* y, void* stream);
+
+/*
+ * GELU(tanh) + smoothing glue between an MLP's two linears:
+ *   out[m, c] = fp16_rne( gelu_tanh(float(y[m, c])) / lambda[c] ),
+ *   gelu_tanh(v) = 0.5 v (1 + tanh( sqrt(2/pi) (v + 0.044715 v^3) )), in fp32.
+ *   y: fp16 [M, C]; lambda: fp32 [C] (the second layer's smoothing factors);
+ *   out: fp16 [M, C] (may not alias y).  C % 8 == 0.
+ */
+svdq_status svdq_gelu_tanh_smooth(const void* y, const float* lambda, int M, int C, void* out,
+                                  void* stream);
+
+/* Static description of a status code. */
+const char* svdq_status_string(svdq_status s);
+
+/* Library version string. */
+const char* svdq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

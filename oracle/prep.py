@@ -44,9 +44,12 @@ def smooth_weight(w: np.ndarray, lam: np.ndarray) -> np.ndarray:
     return lam.astype(np.float64)[:, None] * np.asarray(w).astype(np.float64)
 
 
-def low_rank(w_hat: np.ndarray, r: int):
-    """Truncated SVD split.  Returns (L1 fp16 [K, r], L2 fp16 [r, N], R fp32 [K, N], sigma float64)."""
-    u, sig, vt = np.linalg.svd(w_hat, full_matrices=False)
+def low_rank(w_hat: np.ndarray, r: int, svd=None):
+    """Truncated SVD split.  Returns (L1 fp16 [K, r], L2 fp16 [r, N], R fp32 [K, N], sigma float64).
+
+    `svd` may pass in np.linalg.svd(w_hat, full_matrices=False) when several ranks
+    are split off the same smoothed weight."""
+    u, sig, vt = np.linalg.svd(w_hat, full_matrices=False) if svd is None else svd
     K, N = w_hat.shape
     if r == 0:
         l1 = np.zeros((K, 0), np.float16)
@@ -69,10 +72,11 @@ class PreparedLayer:
     sigma: np.ndarray    # float64, singular values of W_hat
 
 
-def prepare_layer(x: np.ndarray, w: np.ndarray, b: np.ndarray, r: int, x_cal: np.ndarray = None) -> PreparedLayer:
+def prepare_layer(x: np.ndarray, w: np.ndarray, b: np.ndarray, r: int, x_cal: np.ndarray = None,
+                  svd=None) -> PreparedLayer:
     """Offline setup of one linear: smoothing from x_cal (default x), SVD split of W_hat."""
     lam = smoothing_factors(x if x_cal is None else x_cal, w)
     x_hat = smooth_activations(x, lam)
     w_hat = smooth_weight(w, lam)
-    l1, l2, res, sig = low_rank(w_hat, r)
+    l1, l2, res, sig = low_rank(w_hat, r, svd)
     return PreparedLayer(lam, x_hat, l1, l2, res, np.asarray(b, np.float16), sig)

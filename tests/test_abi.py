@@ -1,0 +1,134 @@
+"""C-ABI library tests that need no GPU: it loads, exports every symbol the header
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_w4a4_quantized_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svdq.h")
+
+OK, NULL, SHAPE, ALIGN, FORMAT, WORKSPACE = 0, -1, -2, -3, -4, -5
+P = 4096          # a fake, 16-byte aligned "device" pointer: never dereferenced on these paths
+MIS = 4100        # misaligned
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(svdq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = binding.lib()
+    syms = declared_symbols()
+    assert len(syms) >= 13
+    for s in syms:
+        assert hasattr(L, s), s
+    assert set(syms) == set(binding._SIGS), "binding signatures out of sync with the header"
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in binding.version()
+    for s in (OK, NULL, SHAPE, ALIGN, FORMAT, WORKSPACE, -6, -7):
+        assert binding.status_string(s)
+    assert binding.status_string(12345) == "unknown status"
+
+
+def test_sizes():
+    assert binding.code_row_bytes(3072, "int4") == 1536
+    assert binding.code_row_bytes(3072, "int8") == 3072
+    assert binding.code_row_bytes(3072, "fp4") == 1536
+    L = binding.lib()
+    assert L.svdq_scale_row_bytes(3072, 0) == 96
+    assert L.svdq_scale_row_bytes(3072, 2) == 192
+    assert L.svdq_code_row_bytes(100, 0) == 0
+    assert L.svdq_code_row_bytes(64, 7) == 0
+    # codes + scales + T, each 256-byte aligned
+    M, K, r = 4608, 3072, 32
+    exp = sum(((b + 255) // 256) * 256 for b in (M * K // 2, M * K // 64 * 2, M * r * 2))
+    assert binding.linear_workspace_bytes(M, K, r, "int4") == exp
+    assert binding.linear_workspace_bytes(M, 100, r, "int4") == 0
+    assert binding.linear_unfused_workspace_bytes(M, 9216, K, r, "int4") == exp + M * 9216 * 2
+
+
+def qd(x=P, l1=P, M=16, K=64, r=16, fmt=0, xq=P, xs=P, t=P):
+    return binding.lib().svdq_quantize_down(x, l1, M, K, r, fmt, xq, xs, t, None)
+
+
+def test_quantize_down_validation():
+    assert qd(x=None) == NULL
+    assert qd(xq=None) == NULL
+    assert qd(l1=None) == NULL
+    assert qd(l1=None, t=None, r=0, xq=None) == NULL
+    assert qd(K=100) == SHAPE
+    assert qd(K=0) == SHAPE
+    assert qd(M=-1) == SHAPE
+    assert qd(r=8) == SHAPE
+    assert qd(r=80) == SHAPE
+    assert qd(fmt=3) == FORMAT
+    assert qd(x=MIS) == ALIGN
+    assert qd(t=MIS) == ALIGN
+    assert qd(M=0) == OK            # empty input: nothing enqueued
+    assert qd(M=0, r=0, l1=None, t=None) == OK
+    assert qd(M=0, x=None, xq=None, xs=None, l1=None, t=None) == OK   # zero-size tensors have NULL data
+    assert qd(M=0, K=100) == SHAPE
+
+
+def gm(xq=P, xs=P, t=P, wq=P, ws=P, l2=P, bias=P, M=16, N=16, K=64, r=16, fmt=0, y=P):
+    return binding.lib().svdq_gemm_w4a4_up(xq, xs, t, wq, ws, l2, bias, M, N, K, r, fmt, y, None)
+
+
+def test_gemm_validation():
+    assert gm(y=None) == NULL
+    assert gm(t=None) == NULL
+    assert gm(l2=None) == NULL
+    assert gm(N=24) == SHAPE
+    assert gm(K=32) == SHAPE
+    assert gm(fmt=-1) == FORMAT
+    assert gm(bias=MIS) == ALIGN
+    assert gm(wq=MIS) == ALIGN
+    assert gm(M=0) == OK
+    assert gm(N=0) == OK
+
+
+def test_linear_validation():
+    L = binding.lib()
+    need = L.svdq_linear_workspace_bytes(16, 64, 16, 0)
+    f = lambda ws=P, nbytes=need, M=16, N=16, K=64, r=16, fmt=0, x=P, l1=P: L.svdq_linear(
+        x, l1, P, P, P, None, M, N, K, r, fmt, ws, nbytes, P, None)
+    assert f(nbytes=need - 1) == WORKSPACE
+    assert f(ws=None) == NULL
+    assert f(ws=MIS) == ALIGN
+    assert f(l1=None) == NULL
+    assert f(fmt=9) == FORMAT
+    assert f(M=0) == OK
+    g = lambda nbytes, M=16, N=16: L.svdq_linear_unfused(P, P, P, P, P, None, M, N, 64, 16, 0, P, nbytes, P, None)
+    needu = L.svdq_linear_unfused_workspace_bytes(16, 16, 64, 16, 0)
+    assert needu > need
+    assert g(needu - 1) == WORKSPACE
+    assert g(needu, M=0) == OK
+
+
+def test_weight_gelu_w4a16_validation():
+    L = binding.lib()
+    assert L.svdq_quantize_weight(None, 16, 64, 0, P, P, None) == NULL
+    assert L.svdq_quantize_weight(P, 15, 64, 0, P, P, None) == SHAPE
+    assert L.svdq_quantize_weight(P, 16, 64, 5, P, P, None) == FORMAT
+    assert L.svdq_quantize_weight(P, 0, 64, 0, P, P, None) == OK
+    assert L.svdq_gelu_tanh_smooth(P, P, 4, 12, P, None) == SHAPE
+    assert L.svdq_gelu_tanh_smooth(P, None, 4, 16, P, None) == NULL
+    assert L.svdq_gelu_tanh_smooth(P, P, 0, 16, P, None) == OK
+    assert L.svdq_gemm_w4a16(P, P, P, None, 4, 16, 96, P, None) == SHAPE
+    assert L.svdq_gemm_w4a16(P, P, MIS, None, 4, 16, 64, P, None) == ALIGN
+    assert L.svdq_gemm_w4a16(P, P, P, None, 0, 16, 64, P, None) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()

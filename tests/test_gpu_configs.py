@@ -1,0 +1,154 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the
+benchmark times (svdq_linear: Kernel A then Kernel B on one stream).
+
+The oracle computes every output at these sizes (float64 BLAS), so the
+comparison is complete, not sampled: codes and scales bit-exact on the full
+tensors, Y within 1e-3 relative Frobenius error and within the elementwise fp32
+reassociation bound.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+import oracle  # noqa: E402
+from bit_w4a4_quantized_amd import binding  # noqa: E402
+from tests.layers import (log, prepared, raw_layer, reference, rel_fro, within_sum_bound,  # noqa: E402
+                          linear_abs_sum, branch_slack)
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.lib()
+    yield
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def same_bytes(a, b):
+    a, b = np.ascontiguousarray(a), np.ascontiguousarray(b)
+    return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def run_layer(P, fmt, x_hat=None, check_codes=True):
+    """GPU: weight quantizer, Kernel A, Kernel B and the fused call; oracle: the same layer."""
+    x_hat = P.x_hat if x_hat is None else x_hat
+    M, K = x_hat.shape
+    N = P.res.shape[1]
+    r = P.l1.shape[1]
+    G = 16 if fmt == "fp4" else 64
+    log(f"GPU {fmt} M={M} K={K} N={N} r={r}")
+    ref = reference(P, fmt, x_hat)
+    gx = dev(x_hat)
+    gl1t = dev(P.l1.T) if r else None
+    gl2 = dev(P.l2) if r else None
+    gb = dev(P.bias)
+    wq, ws = binding.svdq_quantize_weight(dev(P.res.T), fmt)
+    if check_codes:
+        assert same_bytes(host(wq), ref["wstored"]), "weight codes"
+        assert same_bytes(host(ws), ref["ws"]), "weight scales"
+        xq, xs, t = binding.svdq_quantize_down(gx, gl1t, fmt)
+        assert same_bytes(host(xq), ref["xstored"]), "activation codes"
+        assert same_bytes(host(xs), ref["xs"]), "activation scales"
+        if r:
+            tg = host(t)
+            assert rel_fro(tg, ref["t"]) <= TOL
+            ok, worst = within_sum_bound(tg, ref["t"], np.abs(x_hat.astype(np.float64)) @ np.abs(P.l1.astype(np.float64)), K)
+            assert ok, worst
+        del xq, xs, t
+    y = host(binding.svdq_linear(gx, gl1t, wq, ws, gl2, gb, fmt))
+    err = rel_fro(y, ref["y"])
+    log(f"  rel_fro={err:.3e}")
+    assert np.isfinite(y.astype(np.float32)).all()
+    assert err <= TOL
+    # the fused call rounds its own T: allow for T's own bound through L2
+    slack = branch_slack(x_hat, P.l1, ref["t"], P.l2) if r else 0.0
+    ok, worst = within_sum_bound(y, ref["y"], linear_abs_sum(ref["xq"], ref["xs"], ref["t"], ref["wq"], ref["ws"],
+                                                             P.l2, P.bias, fmt), K // G + r + 2, slack)
+    assert ok, worst
+    return y, ref, (wq, ws)
+
+
+def test_c0_tiny_layer():
+    run_layer(prepared("c0", 32), "int4")
+
+
+def test_c1_qkv():
+    run_layer(prepared("c1_qkv", 32), "int4")
+
+
+def test_c2_mlp_pair():
+    P1 = prepared("c2_fc1", 32)
+    y1, ref1, _ = run_layer(P1, "int4")
+    P2 = prepared("c2_fc2", 32)
+    # glue on the oracle's fc1 output: GPU vs oracle
+    xg = host(binding.svdq_gelu_tanh_smooth(dev(ref1["y"]), dev(P2.lam)))
+    x2_ref = oracle.forward.gelu_smooth(ref1["y"], P2.lam)
+    assert rel_fro(xg, x2_ref) <= TOL
+    # fc2 on the same smoothed input for both sides: codes bit-exact
+    run_layer(P2, "int4", x_hat=x2_ref)
+    # the whole chain on the GPU against the oracle's chain (tolerance only)
+    y2_ref = reference(P2, "int4", x2_ref)["y"]
+    g = binding
+    wq2, ws2 = g.svdq_quantize_weight(dev(P2.res.T), "int4")
+    wq1, ws1 = g.svdq_quantize_weight(dev(P1.res.T), "int4")
+    y1g = g.svdq_linear(dev(P1.x_hat), dev(P1.l1.T), wq1, ws1, dev(P1.l2), dev(P1.bias), "int4")
+    x2g = g.svdq_gelu_tanh_smooth(y1g, dev(P2.lam))
+    y2g = host(g.svdq_linear(x2g, dev(P2.l1.T), wq2, ws2, dev(P2.l2), dev(P2.bias), "int4"))
+    err = rel_fro(y2g, y2_ref)
+    log(f"  chained fc1 -> gelu -> fc2 rel_fro={err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("m", [64, 256, 1024])
+def test_c3_small_batch(m):
+    P = prepared("c2_fc1", 32)
+    run_layer(P, "int4", x_hat=np.ascontiguousarray(P.x_hat[:m]))
+
+
+def test_c3_w4a16_control():
+    L = raw_layer("c2_fc1")
+    q, s, st = oracle.quant.quantize(L.w.T.astype(np.float32), "int4")
+    ref = oracle.forward.w4a16(L.x, q, s, L.b)
+    y = host(binding.svdq_gemm_w4a16(dev(L.x), dev(st), dev(s), dev(L.b)))
+    err = rel_fro(y, ref)
+    log(f"  w4a16 rel_fro={err:.3e}")
+    assert err <= TOL
+    absum = np.abs(L.x.astype(np.float64)) @ np.abs(oracle.quant.dequantize(q, s, "int4")).T + np.abs(L.b.astype(np.float64))
+    ok, worst = within_sum_bound(y, ref, absum, L.x.shape[1] + 2)
+    assert ok, worst
+
+
+def test_c4_fp4():
+    run_layer(prepared("c2_fc1", 32), "fp4")
+
+
+def test_c4_int8():
+    run_layer(prepared("c2_fc1", 16), "int8")
+
+
+def test_c1_unfused_and_bare():
+    P = prepared("c1_qkv", 32)
+    ref = reference(P, "int4")
+    wq, ws = binding.svdq_quantize_weight(dev(P.res.T), "int4")
+    args = (dev(P.x_hat), dev(P.l1.T), wq, ws, dev(P.l2), dev(P.bias), "int4")
+    yu = host(binding.svdq_linear_unfused(*args))
+    assert rel_fro(yu, ref["y"]) <= TOL
+    y0 = host(binding.svdq_linear(dev(P.x_hat), None, wq, ws, None, dev(P.bias), "int4"))
+    M, N = y0.shape
+    ref0 = oracle.forward.linear(ref["xq"], ref["xs"], np.zeros((M, 0), np.float16), ref["wq"], ref["ws"],
+                                 np.zeros((0, N), np.float16), P.bias, "int4")
+    assert rel_fro(y0, ref0) <= TOL

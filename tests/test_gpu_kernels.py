@@ -1,0 +1,252 @@
+"""GPU parity of every entry point against the CPU oracle, at sizes the oracle
+finishes in seconds that still span several tiles and ragged tails.
+
+Bar: codes and scales bit-exact; fp16 outputs within 1e-3 relative Frobenius
+error of the oracle (and, where the result is one rounding of a sum, within
+one fp16 ulp elementwise); the exact int4 grid bit for bit.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+from bit_w4a4_quantized_amd import binding  # noqa: E402
+from tests.layers import log, rel_fro, fp16_ulp_diff, within_sum_bound, linear_abs_sum  # noqa: E402
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def same_bytes(a, b):
+    a, b = np.ascontiguousarray(a), np.ascontiguousarray(b)
+    return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def draw(seed, M, K, N, r, xscale=0.7, rscale=0.05):
+    g = np.random.default_rng(seed)
+    x_hat = (g.standard_normal((M, K)) * xscale)
+    cols = g.choice(K, max(1, K // 100), replace=False)
+    x_hat[:, cols] *= 5.0
+    x_hat = x_hat.astype(np.float16)
+    r_t = (g.standard_normal((N, K)) * rscale).astype(np.float32)
+    l1 = (g.standard_normal((K, r)) * 0.3).astype(np.float16)
+    l2 = (g.standard_normal((r, N)) * 0.3).astype(np.float16)
+    b = (g.standard_normal(N) * 0.01).astype(np.float16)
+    return x_hat, r_t, l1, l2, b
+
+
+SHAPES = [  # M, K, N, r
+    (1, 64, 16, 0), (3, 128, 32, 16), (17, 192, 48, 32), (64, 64, 128, 32),
+    (130, 320, 272, 32), (257, 256, 144, 64), (300, 128, 400, 48), (128, 256, 256, 32),
+]
+
+
+@pytest.mark.parametrize("fmt", ["int4", "int8", "fp4"])
+@pytest.mark.parametrize("M,K,N,r", SHAPES)
+def test_quantize_down_parity(fmt, M, K, N, r):
+    log(f"quantize_down {fmt} M={M} K={K} r={r}")
+    x_hat, _, l1, _, _ = draw(M * 7 + K + r, M, K, 16, r)
+    q, s, stored = oracle.quant.quantize(x_hat, fmt)
+    xq, xs, t = binding.svdq_quantize_down(dev(x_hat), dev(l1.T) if r else None, fmt)
+    assert same_bytes(host(xq), stored)
+    assert same_bytes(host(xs), s)
+    if r:
+        tr = oracle.forward.down_projection(x_hat, l1)
+        tg = host(t)
+        assert rel_fro(tg, tr) <= TOL
+        ok, worst = within_sum_bound(tg, tr, np.abs(x_hat.astype(np.float64)) @ np.abs(l1.astype(np.float64)), K)
+        assert ok, worst
+
+
+@pytest.mark.parametrize("fmt", ["int4", "int8", "fp4"])
+@pytest.mark.parametrize("N,K", [(16, 64), (48, 192), (272, 320), (1024, 512)])
+def test_quantize_weight_parity(fmt, N, K):
+    log(f"quantize_weight {fmt} N={N} K={K}")
+    g = np.random.default_rng(N + K)
+    r_t = (g.standard_normal((N, K)) * 10.0 ** g.integers(-4, 1, (N, 1))).astype(np.float32)
+    q, s, stored = oracle.quant.quantize(r_t, fmt)
+    wq, ws = binding.svdq_quantize_weight(dev(r_t), fmt)
+    assert same_bytes(host(wq), stored)
+    assert same_bytes(host(ws), s)
+
+
+def test_quantizers_subnormal_scales_and_zero_groups():
+    # tiny values push fp16 scales into subnormals; a zero group gives scale 0 and codes 0
+    g = np.random.default_rng(3)
+    x = (g.standard_normal((5, 256)) * 1e-6).astype(np.float16)
+    x[:, 64:128] = 0
+    for fmt in ("int4", "int8", "fp4"):
+        q, s, stored = oracle.quant.quantize(x, fmt)
+        xq, xs, _ = binding.svdq_quantize_down(dev(x), None, fmt)
+        assert same_bytes(host(xq), stored), fmt
+        assert same_bytes(host(xs), s), fmt
+        wq, ws = binding.svdq_quantize_weight(dev(x.astype(np.float32)[:, :].repeat(16, axis=0)[:80]), fmt)
+        q2, s2, st2 = oracle.quant.quantize(x.astype(np.float32).repeat(16, axis=0)[:80], fmt)
+        assert same_bytes(host(wq), st2), fmt
+        assert same_bytes(host(ws), s2), fmt
+
+
+def _gemm_inputs(fmt, M, K, N, r, seed):
+    x_hat, r_t, l1, l2, b = draw(seed, M, K, N, r)
+    xq, xs, xst = oracle.quant.quantize(x_hat, fmt)
+    wq, ws, wst = oracle.quant.quantize(r_t, fmt)
+    t = oracle.forward.down_projection(x_hat, l1)
+    return x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t
+
+
+@pytest.mark.parametrize("fmt", ["int4", "int8", "fp4"])
+@pytest.mark.parametrize("M,K,N,r", SHAPES)
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_gemm_up_parity(fmt, M, K, N, r, with_bias):
+    log(f"gemm_w4a4_up {fmt} M={M} K={K} N={N} r={r} bias={with_bias}")
+    x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs(fmt, M, K, N, r, M + N + K + r)
+    bias = b if with_bias else None
+    ref = oracle.forward.linear(xq, xs, t, wq, ws, l2, bias, fmt)
+    y = binding.svdq_gemm_w4a4_up(dev(xst), dev(xs), dev(t) if r else None, dev(wst), dev(ws),
+                                  dev(l2) if r else None, dev(bias) if with_bias else None, K, fmt)
+    yg = host(y)
+    assert np.isfinite(yg.astype(np.float32)).all()
+    assert rel_fro(yg, ref) <= TOL
+    G = 16 if fmt == "fp4" else 64
+    ok, worst = within_sum_bound(yg, ref, linear_abs_sum(xq, xs, t, wq, ws, l2, bias, fmt), K // G + r + 2)
+    assert ok, worst
+
+
+@pytest.mark.parametrize("fmt", ["int4", "int8", "fp4"])
+@pytest.mark.parametrize("M,K,N,r", [(17, 192, 48, 32), (130, 320, 272, 32), (257, 256, 144, 64), (1, 64, 16, 0)])
+def test_linear_end_to_end(fmt, M, K, N, r):
+    log(f"linear {fmt} M={M} K={K} N={N} r={r}")
+    x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs(fmt, M, K, N, r, 99 + M)
+    ref = oracle.forward.linear(xq, xs, t, wq, ws, l2, b, fmt)
+    gw, gs = binding.svdq_quantize_weight(dev(np.ascontiguousarray(_rt(fmt, M, K, N, r))), fmt)
+    y = binding.svdq_linear(dev(x_hat), dev(l1.T) if r else None, gw, gs, dev(l2) if r else None, dev(b), fmt)
+    assert rel_fro(host(y), ref) <= TOL
+
+
+def _rt(fmt, M, K, N, r):
+    return draw(99 + M, M, K, N, r)[1]
+
+
+def _grid(g, rows, K):
+    q = g.integers(-7, 8, (rows, K))
+    for gi in range(K // 64):
+        q[np.arange(rows), gi * 64 + g.integers(0, 64, rows)] = g.choice([-7, 7], rows)
+    return q
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 64, 16), (33, 192, 48), (200, 320, 144)])
+def test_exact_grid_bit_for_bit(M, K, N):
+    g = np.random.default_rng(M + K + N)
+    qx, qr = _grid(g, M, K), _grid(g, N, K)
+    x_hat = (qx * 2.0 ** -4).astype(np.float16)
+    r_t = (qr * 2.0 ** -4).astype(np.float32)
+    exact = (qx.astype(object) @ qr.T.astype(object))
+    ref = np.array([[float(v) * 2.0 ** -8 for v in row] for row in exact]).astype(np.float16)
+    wq, ws = binding.svdq_quantize_weight(dev(r_t), "int4")
+    y = binding.svdq_linear(dev(x_hat), None, wq, ws, None, None, "int4")
+    assert np.array_equal(host(y).view(np.uint16), ref.view(np.uint16))
+
+
+def test_unfused_matches_fused():
+    M, K, N, r = 130, 320, 272, 32
+    x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs("int4", M, K, N, r, 5)
+    ref = oracle.forward.linear(xq, xs, t, wq, ws, l2, b, "int4")
+    args = (dev(x_hat), dev(l1.T), dev(wst), dev(ws), dev(l2), dev(b), "int4")
+    yu = host(binding.svdq_linear_unfused(*args))
+    yf = host(binding.svdq_linear(*args))
+    assert rel_fro(yu, ref) <= TOL
+    assert rel_fro(yu, yf) <= TOL
+    # r = 0: the unfused path is the bare GEMM
+    y0 = host(binding.svdq_linear_unfused(dev(x_hat), None, dev(wst), dev(ws), None, dev(b), "int4"))
+    ref0 = oracle.forward.linear(xq, xs, np.zeros((M, 0), np.float16), wq, ws, np.zeros((0, N), np.float16), b, "int4")
+    assert rel_fro(y0, ref0) <= TOL
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 64, 16), (130, 320, 272), (300, 256, 144)])
+def test_w4a16_parity(M, K, N):
+    g = np.random.default_rng(M * N)
+    x = g.standard_normal((M, K)).astype(np.float16)
+    w_t = (g.standard_normal((N, K)) * 0.05).astype(np.float32)
+    b = (g.standard_normal(N) * 0.01).astype(np.float16)
+    q, s, st = oracle.quant.quantize(w_t, "int4")
+    ref = oracle.forward.w4a16(x, q, s, b)
+    y = binding.svdq_gemm_w4a16(dev(x), dev(st), dev(s), dev(b))
+    yg = host(y)
+    assert rel_fro(yg, ref) <= TOL
+    absum = np.abs(x.astype(np.float64)) @ np.abs(oracle.quant.dequantize(q, s, "int4")).T + np.abs(b.astype(np.float64))
+    ok, worst = within_sum_bound(yg, ref, absum, K + 2)
+    assert ok, worst
+
+
+@pytest.mark.parametrize("M,C", [(1, 8), (7, 264), (300, 1024)])
+def test_gelu_smooth_parity(M, C):
+    g = np.random.default_rng(M + C)
+    y = (g.standard_normal((M, C)) * 3).astype(np.float16)
+    lam = g.uniform(0.3, 8.0, C).astype(np.float32)
+    ref = oracle.forward.gelu_smooth(y, lam)
+    out = host(binding.svdq_gelu_tanh_smooth(dev(y), dev(lam)))
+    assert rel_fro(out, ref) <= TOL
+    assert fp16_ulp_diff(out, ref) <= 1
+
+
+def test_repeat_runs_are_bitwise_identical():
+    M, K, N, r = 257, 256, 144, 32
+    x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs("int4", M, K, N, r, 11)
+    args = (dev(x_hat), dev(l1.T), dev(wst), dev(ws), dev(l2), dev(b), "int4")
+    first = host(binding.svdq_linear(*args))
+    for _ in range(9):
+        assert np.array_equal(host(binding.svdq_linear(*args)).view(np.uint16), first.view(np.uint16))
+
+
+def test_outputs_stay_inside_their_buffers():
+    M, K, N, r = 130, 192, 48, 32
+    x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs("int4", M, K, N, r, 12)
+    guard = 4096
+    canary = 0x5A
+
+    def guarded(nbytes, dtype, shape):
+        buf = torch.full((nbytes + 2 * guard,), canary, dtype=torch.uint8, device="cuda")
+        view = buf[guard:guard + nbytes].view(dtype).view(*shape)
+        return buf, view
+
+    bq, gq = guarded(M * K // 2, torch.uint8, (M, K // 2))
+    bs, gs = guarded(M * K // 64 * 2, torch.float16, (M, K // 64))
+    bt, gt = guarded(M * r * 2, torch.float16, (M, r))
+    binding.svdq_quantize_down(dev(x_hat), dev(l1.T), "int4", xq=gq, xs=gs, t=gt)
+    by, gy = guarded(M * N * 2, torch.float16, (M, N))
+    binding.svdq_gemm_w4a4_up(gq, gs, gt, dev(wst), dev(ws), dev(l2), dev(b), K, "int4", y=gy)
+    for buf in (bq, bs, bt, by):
+        h = host(buf)
+        assert (h[:guard] == canary).all() and (h[-guard:] == canary).all()
+    assert same_bytes(host(gq), xst)
+
+
+def test_empty_inputs_are_no_ops():
+    # zero-size tensors have NULL data pointers: an empty call must still succeed
+    K, N = 64, 16
+    x = torch.zeros((0, K), dtype=torch.float16, device="cuda")
+    xq, xs, t = binding.svdq_quantize_down(x, None, "int4")
+    assert xq.shape == (0, K // 2)
+    wq, ws = binding.svdq_quantize_weight(torch.zeros((N, K), dtype=torch.float32, device="cuda"), "int4")
+    y = binding.svdq_linear(x, None, wq, ws, None, None, "int4")
+    assert y.shape == (0, N)

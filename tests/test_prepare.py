@@ -1,0 +1,26 @@
+"""The package's offline preparation against the oracle's offline setup (CPU).
+
+The two are written separately; on the same raw layer they must agree bit for
+bit (same fp32/fp16 rounding points, same LAPACK routine), so the GPU path and
+the oracle see the same prepared layer whichever of the two made it.
+"""
+import numpy as np
+import pytest
+
+from bit_w4a4_quantized_amd.prepare import prepare_host
+from oracle import prep
+from synth import draw_layer, LayerShape
+
+
+@pytest.mark.parametrize("shape", [LayerShape("a", 128, 256, 256, 32, "int4", 1000, 8),
+                                   LayerShape("b", 64, 192, 96, 16, "int8", 5, 4),
+                                   LayerShape("c", 33, 128, 48, 0, "int4", 6, 4)])
+def test_product_prep_equals_oracle_prep(shape):
+    raw = draw_layer(shape)
+    h = prepare_host(raw.x, raw.w, raw.b, shape.r)
+    o = prep.prepare_layer(raw.x, raw.w, raw.b, shape.r)
+    assert np.array_equal(h.lam.view(np.uint32), o.lam.view(np.uint32))
+    assert np.array_equal(h.smooth(raw.x).view(np.uint16), o.x_hat.view(np.uint16))
+    assert np.array_equal(h.l1t.T.view(np.uint16), o.l1.view(np.uint16))
+    assert np.array_equal(h.l2.view(np.uint16), o.l2.view(np.uint16))
+    assert np.array_equal(h.r_t.T.view(np.uint32), o.res.view(np.uint32))
