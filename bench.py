@@ -35,10 +35,10 @@ INT8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA, 5.0 POP/s
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 
 WORKLOADS = {
-    # name: (M, K, N, r, fmt, synth config layer)
-    "qkv": (4608, 3072, 9216, 32, "int4", "c1_qkv"),
-    "fc1": (4608, 3072, 12288, 32, "int4", "c2_fc1"),
-    "fc2": (4608, 12288, 3072, 32, "int4", "c2_fc2"),
+    # name: (M, K, N, r, synth config layer)
+    "qkv": (4608, 3072, 9216, 32, "c1_qkv"),
+    "fc1": (4608, 3072, 12288, 32, "c2_fc1"),
+    "fc2": (4608, 12288, 3072, 32, "c2_fc2"),
 }
 ROTATE = 3
 
@@ -53,13 +53,16 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
     ap.add_argument("--variant", choices=["fused", "unfused", "w4a16"], default="fused")
+    ap.add_argument("--fmt", choices=["int4_e2m3", "int4"], default="int4_e2m3",
+                    help="INT4 g64 codes in the 6-bit E2M3 container (FP6 MFMA) or packed nibbles (INT8 MFMA)")
     return ap.parse_args()
 
 
-def algorithmic_bytes(M, K, N, r, G=64):
-    """HBM bytes the two kernels must move at minimum (int4 codes, fp16 scales / T / Y)."""
-    ka = 2 * M * K + 2 * K * r + M * K // 2 + 2 * M * K // G + 2 * M * r
-    kb = (M * K // 2 + 2 * M * K // G + 2 * M * r + K * N // 2 + 2 * K * N // G + 2 * r * N + 2 * N
+def algorithmic_bytes(M, K, N, r, code_bits=4, G=64):
+    """HBM bytes the two kernels must move at minimum (codes at code_bits, fp16 scales / T / Y)."""
+    cb = code_bits / 8
+    ka = 2 * M * K + 2 * K * r + int(M * K * cb) + 2 * M * K // G + 2 * M * r
+    kb = (int(M * K * cb) + 2 * M * K // G + 2 * M * r + int(K * N * cb) + 2 * K * N // G + 2 * r * N + 2 * N
           + 2 * M * N)
     return ka, kb
 
@@ -115,7 +118,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     binding.lib()
-    M, K, N, r, fmt, lname = WORKLOADS[args.workload]
+    M, K, N, r, lname = WORKLOADS[args.workload]
+    fmt = args.fmt
     if args.rank is not None:
         r = args.rank
     shapes = {s.name: s for v in CONFIGS.values() for s in v}
@@ -141,7 +145,7 @@ def main():
             x=x_hat.clone(), l1t=cp(layer.l1t), wq=layer.wq.clone(), ws=layer.ws.clone(), l2=cp(layer.l2),
             b=layer.bias.clone(),
             xq=torch.empty((M, binding.code_row_bytes(K, fmt)), dtype=torch.uint8, device="cuda"),
-            xs=torch.empty((M, binding.scale_row_entries(K, fmt)), dtype=binding.scale_dtype(fmt), device="cuda"),
+            xs=torch.empty(binding.scale_shape(M, K, fmt), dtype=binding.scale_dtype(fmt), device="cuda"),
             t=torch.empty((M, r), dtype=torch.float16, device="cuda") if r else None,
             y=torch.empty((M, N), dtype=torch.float16, device="cuda"),
             ws_buf=torch.empty(max(16, binding.linear_unfused_workspace_bytes(M, N, K, r, fmt)), dtype=torch.uint8, device="cuda"),
@@ -206,7 +210,7 @@ def main():
 
     ops = 2.0 * M * N * K
     tops = ops / (ms_per_step * 1e-3) / 1e12
-    ka_bytes, kb_bytes = algorithmic_bytes(M, K, N, r)
+    ka_bytes, kb_bytes = algorithmic_bytes(M, K, N, r, 6 if fmt == "int4_e2m3" else 4)
     kb_us = float(np.mean(kb_ms)) * 1e3
     ka_us = float(np.mean(ka_ms)) * 1e3
     if args.variant == "fused":
@@ -232,9 +236,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4",
+        "dtype": "int4 codes; fp6(e2m3) MFMA" if fmt == "int4_e2m3" else "int4 codes; i8 MFMA",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {lname} M={M} K={K} N={N} r={r} {fmt} group 64",
+        "config": {"workload": f"{args.workload}: {lname} M={M} K={K} N={N} r={r} int4 group 64, fp16 scales",
+                   "storage": fmt,
                    "variant": args.variant, "rotated_buffer_sets": ROTATE},
         "us_per_layer": round(ms_per_step * 1e3, 2),
         "us_per_layer_events": round(ev_ms * 1e3, 2),
@@ -248,7 +253,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(raw, host, fmt, M, K, N, r, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(raw, host, "int4", M, K, N, r, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

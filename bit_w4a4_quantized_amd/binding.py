@@ -13,10 +13,12 @@ import os
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsvdq.so")
+# SVDQ_LIBRARY may name another build of the same library (same ABI), e.g. a tuning variant.
+LIB_PATH = os.environ.get("SVDQ_LIBRARY") or os.path.join(HERE, "libsvdq.so")
 
-FORMATS = {"int4": 0, "int8": 1, "fp4": 2}
-GROUP = {"int4": 64, "int8": 64, "fp4": 16}
+FORMATS = {"int4": 0, "int8": 1, "fp4": 2, "int4_e2m3": 3}
+GROUP = {"int4": 64, "int8": 64, "fp4": 16, "int4_e2m3": 64}
+FMT_NAMES = {v: k for k, v in FORMATS.items()}
 
 _lib = None
 
@@ -108,7 +110,14 @@ def code_row_bytes(K: int, fmt) -> int:
 
 
 def scale_row_entries(K: int, fmt) -> int:
-    return K // GROUP[fmt] if isinstance(fmt, str) else K // (16 if int(fmt) == 2 else 64)
+    name = fmt if isinstance(fmt, str) else FMT_NAMES[int(fmt)]
+    return K // GROUP[name]
+
+
+def scale_shape(rows: int, K: int, fmt):
+    """Shape of the scale tensor: [rows, K/G], or group-major [K/64, rows] for the E2M3 container."""
+    name = fmt if isinstance(fmt, str) else FMT_NAMES[int(fmt)]
+    return (K // 64, rows) if name == "int4_e2m3" else (rows, K // GROUP[name])
 
 
 def scale_dtype(fmt):
@@ -137,7 +146,7 @@ def svdq_quantize_down(x_hat, l1t, fmt, xq=None, xs=None, t=None, stream=None):
     if xq is None:
         xq = torch.empty((M, code_row_bytes(K, fmt)), dtype=torch.uint8, device=dev)
     if xs is None:
-        xs = torch.empty((M, scale_row_entries(K, fmt)), dtype=scale_dtype(fmt), device=dev)
+        xs = torch.empty(scale_shape(M, K, fmt), dtype=scale_dtype(fmt), device=dev)
     if r and t is None:
         t = torch.empty((M, r), dtype=torch.float16, device=dev)
     _check("svdq_quantize_down", lib().svdq_quantize_down(
@@ -183,7 +192,7 @@ def svdq_quantize_weight(r_t, fmt, wq=None, ws=None, stream=None):
     if wq is None:
         wq = torch.empty((N, code_row_bytes(K, fmt)), dtype=torch.uint8, device=r_t.device)
     if ws is None:
-        ws = torch.empty((N, scale_row_entries(K, fmt)), dtype=scale_dtype(fmt), device=r_t.device)
+        ws = torch.empty(scale_shape(N, K, fmt), dtype=scale_dtype(fmt), device=r_t.device)
     _check("svdq_quantize_weight", lib().svdq_quantize_weight(
         _p(r_t), N, K, _fmt(fmt), _p(wq), _p(ws), _stream(stream)))
     return wq, ws

@@ -1,0 +1,335 @@
+// Kernel B, LDS-staged: low-bit GEMM on the matrix cores, per-group rescale
+// into fp32, up projection and bias in the epilogue.
+//
+// Practice page "sota-314", section "Do this": the up projection is fused
+// with the 4-bit compute because both write the same output.
+//
+//   Y[m,n] = fp16_rne( sum_g sx[m,g] sw[n,g] P_g[m,n] + (T L2)[m,n] + b[n] )
+//   P_g    = sum_{k in group g} q_x[m,k] q_w[n,k]   (exact)
+//
+// Two operand cores share the skeleton:
+//   CORE_E2M3 -- INT4 codes stored in the 6-bit container (SVDQ_INT4_G64_E2M3):
+//     each code q is the E2M3 subnormal of q/8, so a group half (32 codes of a
+//     row) is exactly the 6-dword operand of v_mfma_scale_f32_32x32x64_f8f6f4
+//     in FP6 mode.  One MFMA per 32x32 tile per group gives P_g/64 in fp32,
+//     exactly (products of eighths, sums far below 2^24 units), at twice the
+//     INT8 rate and with no int->float conversion.  Scales are group-major.
+//   CORE_I4 -- canonical packed nibbles (SVDQ_INT4_G64): each lane reads 16
+//     bytes and turns them into int8 16q with two masks and a shift; two
+//     v_mfma_i32_32x32x32_i8 per tile per group; the int32 partial is
+//     converted to fp32.  Scales are row-major.
+//
+// Tiling (gfx950, wave64): workgroup tile 128 x 128, four waves in 2 x 2 of
+// 64 x 64 (2 x 2 MFMA tiles of 32 x 32), two workgroups per CU.  K advances in
+// stages of KC groups of 64: the workgroup stages both code tiles and the
+// 256 fp16 scales per group in LDS, in a ring of two stages, and the
+// global loads run two stages ahead of the compute (registers hold stage s+2
+// while LDS holds s and s+1), so a stage's HBM/L2 latency is covered by a full
+// stage of compute.  LDS row strides (56 and 48 bytes) make the
+// per-lane 8- and 16-byte reads of 16 / 8 consecutive rows hit distinct banks.
+// The block index is remapped so that each XCD (own L2) works on a
+// contiguous range of tiles, rastered in groups of 8 tile rows.
+//
+// Rescale: the per-group scale products S = sx sw^T of a 32 x 32 tile come from
+// one v_mfma_f32_32x32x16_f16 with the scales in a single K slot (exact), so
+// the vector ALU does one fma per element and group, acc += P_g * S.
+//
+// Epilogue: acc += T L2 on v_mfma_f32_32x32x16_f16 (fp16 in, fp32 out),
+// + bias, RNE to fp16, store.
+#include <type_traits>
+
+#include "kernels.h"
+#include "quant_core.h"
+
+namespace svdq {
+
+namespace {
+
+constexpr int BM = 128, BN = 128, NTHREADS = 256;
+
+template <int CORE> struct CoreCfg;
+template <> struct CoreCfg<CORE_E2M3> {
+  static constexpr int GB = 48;      // bytes per row per group in global memory
+  static constexpr int LS = 56;      // LDS row stride
+  static constexpr int CHUNKS = 3;   // 16-byte chunks per row per group
+};
+template <> struct CoreCfg<CORE_I4> {
+  static constexpr int GB = 32;
+  static constexpr int LS = 48;
+  static constexpr int CHUNKS = 2;
+};
+
+__device__ __forceinline__ uint32_t nib_lo16(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t nib_hi16(uint32_t w) { return w & 0xF0F0F0F0u; }
+
+// Map the launch index to an output tile: contiguous ranges per XCD (blocks are
+// dealt round-robin to the 8 XCDs), then 8-tile-row groups within a range.
+__device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, int* tm, int* tn) {
+  const int n8 = nblocks & ~7;
+  int lid = bid;
+  if (bid < n8) lid = (bid & 7) * (n8 >> 3) + (bid >> 3);
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int grp = lid / per_group;
+  const int first_m = grp * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int in = lid - grp * per_group;
+  *tm = first_m + in % gm;
+  *tn = in / gm;
+}
+
+}  // namespace
+
+template <int CORE, int RB, bool BIAS>
+__global__ void __launch_bounds__(NTHREADS, 2)
+k_gemm2(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __half* __restrict__ t,
+        const uint8_t* __restrict__ wq, const __half* __restrict__ ws, const __half* __restrict__ l2,
+        const __half* __restrict__ bias, int M, int N, int K, __half* __restrict__ y) {
+  using C = CoreCfg<CORE>;
+  constexpr int R = RB * 16;
+  constexpr int KC = 2;                                  // groups per stage
+  constexpr int TILE_BYTES = BM * C::LS;                 // one operand tile of one group in LDS
+  constexpr int GROUP_BYTES = 2 * TILE_BYTES + 256 * 2;  // A, B, 128 + 128 fp16 scales
+  constexpr int STAGE_BYTES = KC * GROUP_BYTES;
+  // The MFMA partial of one group times PFACT is P_g (E2M3: operands are q/8; I4: 16q).
+  // Every rescaled partial carries the same factor, so it is applied once to the
+  // accumulator (exact: a power of two) before the branch is added.
+  constexpr float PFACT = CORE == CORE_E2M3 ? 64.0f : (1.0f / 256.0f);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, r32 = lane & 31;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int G = K >> 6;
+  const int NS = (G + KC - 1) / KC;                       // stages
+  const size_t row_bytes = (size_t)G * C::GB;
+
+  // ---- per-thread staging assignment (global -> registers -> LDS)
+  const uint8_t* src[C::CHUNKS];
+  int dst[C::CHUNKS];
+  bool ok[C::CHUNKS];
+#pragma unroll
+  for (int i = 0; i < C::CHUNKS; i++) {
+    const int c = tid + NTHREADS * i;                        // chunk id over both tiles
+    const int per_tile = BM * C::CHUNKS;
+    const int tile = c / per_tile, rr = c % per_tile;
+    const int row = rr / C::CHUNKS, part = rr % C::CHUNKS;
+    const int grow = (tile == 0 ? m0 : n0) + row;
+    ok[i] = grow < (tile == 0 ? M : N);
+    // rows past the edge re-read row 0 of the tile's operand and are never stored
+    src[i] = (tile == 0 ? xq : wq) + (size_t)(ok[i] ? grow : 0) * row_bytes + part * 16;
+    dst[i] = tile * TILE_BYTES + row * C::LS + part * 16;
+  }
+  // scale staging: thread < 128 -> sx of row m0+tid, else sw of column n0+tid-128 (raw fp16)
+  const bool s_is_x = tid < 128;
+  const int s_row = (s_is_x ? m0 : n0) + (tid & 127);
+  const bool s_ok = s_row < (s_is_x ? M : N);
+  const unsigned short* s_base = reinterpret_cast<const unsigned short*>(s_is_x ? xs : ws);
+  const int s_rows = s_is_x ? M : N;
+  const unsigned short* s_ptr = s_base + (CORE == CORE_E2M3 ? (size_t)(s_ok ? s_row : 0)
+                                                          : (size_t)(s_ok ? s_row : 0) * G);
+  const size_t s_step = CORE == CORE_E2M3 ? (size_t)s_rows : 1;   // between consecutive groups
+
+  uint4 stage_reg[KC][C::CHUNKS];
+  unsigned short stage_s[KC];
+  auto load_stage = [&](int st) {
+#pragma unroll
+    for (int k = 0; k < KC; k++) {
+      const int g = min(st * KC + k, G - 1);   // a group past the end re-reads the last one (unused)
+#pragma unroll
+      for (int i = 0; i < C::CHUNKS; i++) stage_reg[k][i] = *reinterpret_cast<const uint4*>(src[i] + (size_t)g * C::GB);
+      stage_s[k] = s_ptr[(size_t)g * s_step];
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < KC; k++) {
+      uint8_t* base = lds + buf * STAGE_BYTES + k * GROUP_BYTES;
+#pragma unroll
+      for (int i = 0; i < C::CHUNKS; i++) {
+        uint4 v = ok[i] ? stage_reg[k][i] : make_uint4(0, 0, 0, 0);
+        if (CORE == CORE_E2M3) {   // 8-byte aligned rows
+          uint2* p = reinterpret_cast<uint2*>(base + dst[i]);
+          p[0] = make_uint2(v.x, v.y);
+          p[1] = make_uint2(v.z, v.w);
+        } else {
+          *reinterpret_cast<uint4*>(base + dst[i]) = v;
+        }
+      }
+      reinterpret_cast<unsigned short*>(base + 2 * TILE_BYTES)[tid] = s_ok ? stage_s[k] : (unsigned short)0;
+    }
+  };
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; a++)
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
+
+  load_stage(0);
+  store_stage(0);
+  if (NS > 1) load_stage(1);
+  __syncthreads();
+
+  const int arow0 = wm * 64 + r32;          // LDS row of this lane's A operand (tile 0)
+  const int brow0 = wn * 64 + r32;
+  const int a_off = arow0 * C::LS + h * (CORE == CORE_E2M3 ? 24 : 16);
+  const int b_off = TILE_BYTES + brow0 * C::LS + h * (CORE == CORE_E2M3 ? 24 : 16);
+  const int sx_off = 2 * TILE_BYTES + 2 * arow0;
+  const int sw_off = 2 * TILE_BYTES + 2 * (128 + brow0);
+  for (int st = 0; st < NS; st++) {
+    const int buf = st & 1;
+#pragma unroll
+    for (int k = 0; k < KC; k++) {
+      if (st * KC + k >= G) break;
+      const uint8_t* base = lds + buf * STAGE_BYTES + k * GROUP_BYTES;
+      // scale operands for the outer product S = sx sw^T on v_mfma_f32_32x32x16_f16: the
+      // scale sits in K-slot 0 (element 0 of the lanes of the first half), every other slot
+      // is zero, so the MFMA returns sx[m] * sw[n] exactly (fp16 x fp16 in fp32) in the
+      // accumulator layout of the partials.
+      v8h sa[2], sb[2];
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        const unsigned short xa = *reinterpret_cast<const unsigned short*>(base + sx_off + 64 * i);
+        const unsigned short xb = *reinterpret_cast<const unsigned short*>(base + sw_off + 64 * i);
+        sa[i] = as_h8(make_uint4(h ? 0u : (uint32_t)xa, 0u, 0u, 0u));
+        sb[i] = as_h8(make_uint4(h ? 0u : (uint32_t)xb, 0u, 0u, 0u));
+      }
+      if constexpr (CORE == CORE_E2M3) {
+        v8i a[2], b[2];
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+          // 32 bytes per operand read; the hardware uses the first 24 (six dwords of FP6)
+          const uint2* pa = reinterpret_cast<const uint2*>(base + a_off + i * 32 * C::LS);
+          const uint2* pb = reinterpret_cast<const uint2*>(base + b_off + i * 32 * C::LS);
+          const uint2 a0 = pa[0], a1 = pa[1], a2 = pa[2], a3 = pa[3];
+          const uint2 b0 = pb[0], b1 = pb[1], b2 = pb[2], b3 = pb[3];
+          a[i] = v8i{(int)a0.x, (int)a0.y, (int)a1.x, (int)a1.y, (int)a2.x, (int)a2.y, (int)a3.x, (int)a3.y};
+          b[i] = v8i{(int)b0.x, (int)b0.y, (int)b1.x, (int)b1.y, (int)b2.x, (int)b2.y, (int)b3.x, (int)b3.y};
+        }
+#pragma unroll
+        for (int ti = 0; ti < 2; ti++)
+#pragma unroll
+          for (int tj = 0; tj < 2; tj++) {
+            const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ti], b[tj], v16f{}, 2, 2, 0, 127, 0, 127);
+            const v16f sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[ti], sb[tj], v16f{}, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 16; i++) acc[ti][tj][i] = __builtin_fmaf(p[i], sc[i], acc[ti][tj][i]);
+          }
+      } else {
+        v4i a[2][2], b[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+          const uint4 ua = *reinterpret_cast<const uint4*>(base + a_off + i * 32 * C::LS);
+          const uint4 ub = *reinterpret_cast<const uint4*>(base + b_off + i * 32 * C::LS);
+          a[i][0] = v4i{(int)nib_lo16(ua.x), (int)nib_hi16(ua.x), (int)nib_lo16(ua.y), (int)nib_hi16(ua.y)};
+          a[i][1] = v4i{(int)nib_lo16(ua.z), (int)nib_hi16(ua.z), (int)nib_lo16(ua.w), (int)nib_hi16(ua.w)};
+          b[i][0] = v4i{(int)nib_lo16(ub.x), (int)nib_hi16(ub.x), (int)nib_lo16(ub.y), (int)nib_hi16(ub.y)};
+          b[i][1] = v4i{(int)nib_lo16(ub.z), (int)nib_hi16(ub.z), (int)nib_lo16(ub.w), (int)nib_hi16(ub.w)};
+        }
+#pragma unroll
+        for (int ti = 0; ti < 2; ti++)
+#pragma unroll
+          for (int tj = 0; tj < 2; tj++) {
+            v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ti][0], b[tj][0], v16i{}, 0, 0, 0);
+            p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ti][1], b[tj][1], p, 0, 0, 0);
+            const v16f sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[ti], sb[tj], v16f{}, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 16; i++) acc[ti][tj][i] = __builtin_fmaf((float)p[i], sc[i], acc[ti][tj][i]);
+          }
+      }
+    }
+    // keep the next stage's LDS writes (and their wait on the global loads) after this compute
+    __builtin_amdgcn_sched_barrier(0);
+    if (st + 1 < NS) {
+      store_stage(buf ^ 1);
+      if (st + 2 < NS) load_stage(st + 2);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 2; a++)
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) acc[a][b][i] *= PFACT;
+
+  // ---- epilogue: up projection T L2 on the matrix core, bias, fp16 store
+  int arow[2], bcol[2];
+  bool aok[2], bok[2];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    arow[i] = m0 + arow0 + i * 32; aok[i] = arow[i] < M;
+    bcol[i] = n0 + brow0 + i * 32; bok[i] = bcol[i] < N;
+  }
+  if (RB > 0) {
+#pragma unroll
+    for (int kb = 0; kb < RB; kb++) {
+      uint4 ta[2], lb[2];
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        ta[i] = aok[i] ? *reinterpret_cast<const uint4*>(t + (size_t)arow[i] * R + kb * 16 + 8 * h) : make_uint4(0, 0, 0, 0);
+        uint16_t hv[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+          hv[e] = bok[i] ? __half_as_ushort(l2[(size_t)(kb * 16 + 8 * h + e) * N + bcol[i]]) : (uint16_t)0;
+        lb[i] = make_uint4(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16),
+                           hv[4] | ((uint32_t)hv[5] << 16), hv[6] | ((uint32_t)hv[7] << 16));
+      }
+#pragma unroll
+      for (int ti = 0; ti < 2; ti++)
+#pragma unroll
+        for (int tj = 0; tj < 2; tj++)
+          acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(ta[ti]), as_h8(lb[tj]), acc[ti][tj], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int tj = 0; tj < 2; tj++) {
+    if (!bok[tj]) continue;
+    const float bv = BIAS ? __half2float(bias[bcol[tj]]) : 0.f;
+#pragma unroll
+    for (int ti = 0; ti < 2; ti++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int mrow = m0 + wm * 64 + ti * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (mrow < M) y[(size_t)mrow * N + bcol[tj]] = __float2half_rn(acc[ti][tj][i] + bv);
+      }
+  }
+}
+
+template <int CORE, int RB, bool BIAS>
+static hipError_t launch_g2(const GemmArgs& a, hipStream_t s) {
+  const int nb = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((k_gemm2<CORE, RB, BIAS>), dim3(nb), dim3(NTHREADS), 0, s, (const uint8_t*)a.xq,
+                     (const __half*)a.xs, (const __half*)a.t, (const uint8_t*)a.wq, (const __half*)a.ws,
+                     (const __half*)a.l2, (const __half*)a.bias, a.M, a.N, a.K, (__half*)a.y);
+  return hipGetLastError();
+}
+
+template <int CORE, bool BIAS>
+static hipError_t launch_g2_r(const GemmArgs& a, hipStream_t s) {
+  switch (a.r) {
+    case 0: return launch_g2<CORE, 0, BIAS>(a, s);
+    case 16: return launch_g2<CORE, 1, BIAS>(a, s);
+    case 32: return launch_g2<CORE, 2, BIAS>(a, s);
+    case 48: return launch_g2<CORE, 3, BIAS>(a, s);
+    case 64: return launch_g2<CORE, 4, BIAS>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm2(const GemmArgs& a, hipStream_t s) {
+  const bool b = a.bias != nullptr;
+  if (a.fmt == FMT_INT4_E2M3) return b ? launch_g2_r<CORE_E2M3, true>(a, s) : launch_g2_r<CORE_E2M3, false>(a, s);
+  if (a.fmt == FMT_INT4) return b ? launch_g2_r<CORE_I4, true>(a, s) : launch_g2_r<CORE_I4, false>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace svdq

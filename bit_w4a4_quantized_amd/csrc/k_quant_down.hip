@@ -83,8 +83,8 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
       unpack_h8(xv[i][0], v);
       unpack_h8(xv[i][1], v + 8);
       const int col = c * 64 + sub * 8;
-      if (FMT == FMT_INT4 || FMT == FMT_INT8) {
-        const float qmax = FMT == FMT_INT4 ? 7.0f : 127.0f;
+      if (FMT == FMT_INT4 || FMT == FMT_INT8 || FMT == FMT_INT4_E2M3) {
+        const float qmax = FMT == FMT_INT8 ? 127.0f : 7.0f;
         float amax = 0.f;
 #pragma unroll
         for (int e = 0; e < 16; e++) amax = fmaxf(amax, fabsf(v[e]));
@@ -100,12 +100,33 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
             uint8_t* dst = xq + (size_t)m * (K >> 1);
             *reinterpret_cast<uint32_t*>(dst + (col >> 1)) = pack8(q);
             *reinterpret_cast<uint32_t*>(dst + ((col + 32) >> 1)) = pack8(q + 8);
+          } else if (FMT == FMT_INT4_E2M3) {
+            // 6-bit container: group c occupies 48 bytes of the row, half h (codes 32h..32h+31)
+            // 24 bytes; this lane's 8 codes of each half are fields 8 sub .. 8 sub + 7, i.e. the
+            // 6 bytes at offset 6 sub of the half.
+            uint8_t* dst = xq + (size_t)m * (size_t)(K >> 6) * 48 + (size_t)c * 48 + 6 * sub;
+#pragma unroll
+            for (int hh = 0; hh < 2; hh++) {
+              const uint64_t w = pack6x8(q + 8 * hh);
+              uint8_t* d = dst + 24 * hh;
+              if ((sub & 1) == 0) {
+                *reinterpret_cast<uint32_t*>(d) = (uint32_t)w;
+                *reinterpret_cast<uint16_t*>(d + 4) = (uint16_t)(w >> 32);
+              } else {
+                *reinterpret_cast<uint16_t*>(d) = (uint16_t)w;
+                *reinterpret_cast<uint32_t*>(d + 2) = (uint32_t)(w >> 16);
+              }
+            }
           } else {
             uint8_t* dst = xq + (size_t)m * K;
             *reinterpret_cast<uint2*>(dst + col) = make_uint2(pack4_i8(q), pack4_i8(q + 4));
             *reinterpret_cast<uint2*>(dst + col + 32) = make_uint2(pack4_i8(q + 8), pack4_i8(q + 12));
           }
-          if (sub == 0) reinterpret_cast<uint16_t*>(xs)[(size_t)m * (K >> 6) + c] = sbits;
+          if (sub == 0) {
+            // row-major scales [M, K/64]; the 6-bit container format keeps them group-major [K/64, M]
+            const size_t si = FMT == FMT_INT4_E2M3 ? (size_t)c * M + m : (size_t)m * (K >> 6) + c;
+            reinterpret_cast<uint16_t*>(xs)[si] = sbits;
+          }
         }
       } else {  // FP4: groups of 16 = two lanes (sub, sub^1) x 8 values
         float a0 = 0.f, a1 = 0.f;
@@ -175,6 +196,7 @@ static hipError_t launch_qd_r(const QuantDownArgs& a, hipStream_t s) {
 hipError_t launch_quant_down(const QuantDownArgs& a, hipStream_t s) {
   switch (a.fmt) {
     case FMT_INT4: return launch_qd_r<FMT_INT4>(a, s);
+    case FMT_INT4_E2M3: return launch_qd_r<FMT_INT4_E2M3>(a, s);
     case FMT_INT8: return launch_qd_r<FMT_INT8>(a, s);
     case FMT_FP4: return launch_qd_r<FMT_FP4>(a, s);
   }

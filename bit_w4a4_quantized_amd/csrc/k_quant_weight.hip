@@ -27,15 +27,36 @@ k_quant_weight(const float* __restrict__ r_t, int N, int K, uint8_t* __restrict_
   float amax = 0.f;
 #pragma unroll
   for (int e = 0; e < G; e++) amax = fmaxf(amax, fabsf(v[e]));
-  if (FMT == FMT_INT4 || FMT == FMT_INT8) {
-    const float qmax = FMT == FMT_INT4 ? 7.0f : 127.0f;
+  if (FMT == FMT_INT4 || FMT == FMT_INT8 || FMT == FMT_INT4_E2M3) {
+    const float qmax = FMT == FMT_INT8 ? 127.0f : 7.0f;
     uint16_t sbits;
     const float s = int_scale(amax, qmax, &sbits);
-    reinterpret_cast<uint16_t*>(ws)[(size_t)n * gpr + g] = sbits;
+    // the 6-bit container format keeps its scales group-major [K/64, N]
+    reinterpret_cast<uint16_t*>(ws)[FMT == FMT_INT4_E2M3 ? (size_t)g * N + n : (size_t)n * gpr + g] = sbits;
     int q[G];
 #pragma unroll
     for (int e = 0; e < G; e++) q[e] = int_code(v[e], s, qmax);
-    if (FMT == FMT_INT4) {
+    if (FMT == FMT_INT4_E2M3) {
+      // 48 bytes per group: two halves of 32 six-bit fields
+      uint32_t wv[12];
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++) {
+        uint64_t f[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) f[j] = pack6x8(q + 32 * hh + 8 * j);
+        // 4 x 48 bits -> 6 dwords
+        wv[6 * hh + 0] = (uint32_t)f[0];
+        wv[6 * hh + 1] = (uint32_t)(f[0] >> 32) | (uint32_t)(f[1] << 16);
+        wv[6 * hh + 2] = (uint32_t)(f[1] >> 16);
+        wv[6 * hh + 3] = (uint32_t)f[2];
+        wv[6 * hh + 4] = (uint32_t)(f[2] >> 32) | (uint32_t)(f[3] << 16);
+        wv[6 * hh + 5] = (uint32_t)(f[3] >> 16);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(wq + (size_t)n * (size_t)gpr * 48 + (size_t)g * 48);
+      dst[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      dst[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+      dst[2] = make_uint4(wv[8], wv[9], wv[10], wv[11]);
+    } else if (FMT == FMT_INT4) {
       uint32_t* dst = reinterpret_cast<uint32_t*>(wq + (size_t)n * (K >> 1) + (size_t)g * (G >> 1));
 #pragma unroll
       for (int e = 0; e < G; e += 8) dst[e >> 3] = pack8(q + e);
@@ -64,6 +85,9 @@ hipError_t launch_quant_weight(const float* r_t, int N, int K, int fmt, void* wq
   switch (fmt) {
     case FMT_INT4:
       hipLaunchKernelGGL(k_quant_weight<FMT_INT4>, grid, dim3(256), 0, s, r_t, N, K, (uint8_t*)wq, (uint8_t*)ws);
+      break;
+    case FMT_INT4_E2M3:
+      hipLaunchKernelGGL(k_quant_weight<FMT_INT4_E2M3>, grid, dim3(256), 0, s, r_t, N, K, (uint8_t*)wq, (uint8_t*)ws);
       break;
     case FMT_INT8:
       hipLaunchKernelGGL(k_quant_weight<FMT_INT8>, grid, dim3(256), 0, s, r_t, N, K, (uint8_t*)wq, (uint8_t*)ws);

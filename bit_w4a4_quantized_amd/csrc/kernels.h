@@ -8,7 +8,8 @@
 
 namespace svdq {
 
-enum Fmt { FMT_INT4 = 0, FMT_INT8 = 1, FMT_FP4 = 2 };
+enum Fmt { FMT_INT4 = 0, FMT_INT8 = 1, FMT_FP4 = 2, FMT_INT4_E2M3 = 3 };
+enum Core { CORE_E2M3 = 0, CORE_I4 = 1 };
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -51,6 +52,7 @@ struct GemmArgs {
 
 hipError_t launch_quant_down(const QuantDownArgs& a, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm2(const GemmArgs& a, hipStream_t s);
 hipError_t launch_quant_weight(const float* r_t, int N, int K, int fmt, void* wq, void* ws, hipStream_t s);
 
 // unfused comparison pieces

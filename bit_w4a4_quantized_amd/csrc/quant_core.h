@@ -81,6 +81,18 @@ __device__ __forceinline__ uint32_t pack8(const int* q) {
   return w;
 }
 
+// 8 INT4 codes as 6-bit E2M3 fields (sign<<5 | |q|: the E2M3 subnormal of q/8),
+// code i at bits [6i, 6i+6) of a 48-bit value.
+__device__ __forceinline__ uint64_t pack6x8(const int* q) {
+  uint64_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const uint32_t f = (q[i] < 0 ? 32u : 0u) | (uint32_t)(q[i] < 0 ? -q[i] : q[i]);
+    w |= (uint64_t)f << (6 * i);
+  }
+  return w;
+}
+
 __device__ __forceinline__ uint32_t pack4_i8(const int* q) {
   uint32_t w = 0;
 #pragma unroll

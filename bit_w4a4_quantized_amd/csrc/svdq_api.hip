@@ -13,9 +13,15 @@ constexpr int kMaxDim = 1 << 24;
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-inline bool fmt_ok(int f) { return f == SVDQ_INT4_G64 || f == SVDQ_INT8_G64 || f == SVDQ_FP4_G16; }
+inline bool fmt_ok(int f) {
+  return f == SVDQ_INT4_G64 || f == SVDQ_INT8_G64 || f == SVDQ_FP4_G16 || f == SVDQ_INT4_G64_E2M3;
+}
 
-inline size_t code_bytes(int K, int fmt) { return fmt == SVDQ_INT8_G64 ? (size_t)K : (size_t)K / 2; }
+inline size_t code_bytes(int K, int fmt) {
+  if (fmt == SVDQ_INT8_G64) return (size_t)K;
+  if (fmt == SVDQ_INT4_G64_E2M3) return (size_t)K / 4 * 3;
+  return (size_t)K / 2;
+}
 inline size_t scale_bytes(int K, int fmt) {
   return fmt == SVDQ_FP4_G16 ? (size_t)K / 16 : (size_t)K / 64 * 2;
 }

@@ -48,6 +48,17 @@
  *                  per 16: scale = e4m3_rne_sat(fp32(absmax) / 6.0f); code =
  *                  nearest E2M1 to fp32(v)/scale, ties to the even mantissa,
  *                  -0 -> +0.
+ *  SVDQ_INT4_G64_E2M3 : the SVDQ_INT4_G64 codes and scales, bit for bit, in the
+ *                  storage the gfx950 FP6 matrix cores read directly: each code
+ *                  q becomes the 6-bit E2M3 pattern of q/8 (a subnormal:
+ *                  sign<<5 | |q|).  A row has 48 bytes per group of 64; bytes
+ *                  [48g, 48g+24) hold codes 0..31 of group g and [48g+24, 48g+48)
+ *                  codes 32..63, code j of a half in bits [6j, 6j+6) of the
+ *                  little-endian 24 bytes.  Code rows are 3K/4 bytes.  Scales
+ *                  are fp16 and group-major: [K/64, rows].  The 4-bit values
+ *                  sit in a 6-bit container (1.5x the bytes of SVDQ_INT4_G64)
+ *                  so that the GEMM runs on FP6 MFMA at twice the INT8 rate
+ *                  with fp32 partials.
  */
 #ifndef SVDQ_H
 #define SVDQ_H
@@ -73,12 +84,13 @@ typedef enum {
 typedef enum {
   SVDQ_INT4_G64 = 0,
   SVDQ_INT8_G64 = 1,
-  SVDQ_FP4_G16 = 2
+  SVDQ_FP4_G16 = 2,
+  SVDQ_INT4_G64_E2M3 = 3
 } svdq_format;
 
-/* Bytes of one row of codes for K columns (K/2 for 4-bit formats, K for INT8),
- * and number of scale entries per row (K/64 or K/16).  Scales are fp16 (2 B)
- * for the INT formats and E4M3 (1 B) for FP4.  Returns 0 for a bad format. */
+/* Bytes of one row of codes for K columns (K/2 for 4-bit formats, K for INT8,
+ * 3K/4 for the E2M3 container), and bytes of scales per row (K/64 fp16 for the
+ * INT formats, K/16 E4M3 bytes for FP4).  Returns 0 for a bad format. */
 size_t svdq_code_row_bytes(int K, svdq_format fmt);
 size_t svdq_scale_row_bytes(int K, svdq_format fmt);
 

@@ -106,12 +106,38 @@ def dequant_fp4(codes: np.ndarray, scales8: np.ndarray, G: int = 16) -> np.ndarr
     return (q.reshape(q.shape[0], -1, G) * s[..., None]).reshape(q.shape)
 
 
+def pack_e2m3(codes: np.ndarray) -> np.ndarray:
+    """INT4 codes [rows, K] -> the 6-bit E2M3 container [rows, 3K/4].
+
+    Storage variant of INT4 (same codes and scales): code q is the E2M3 bit
+    pattern of q/8, a subnormal, sign<<5 | |q|.  Each run of 32 codes along K
+    (one half of a group of 64) fills 24 bytes, code j in bits [6j, 6j+6) of the
+    little-endian run."""
+    q = np.asarray(codes).astype(np.int64)
+    rows, K = q.shape
+    f = np.where(q < 0, 32, 0) | np.abs(q)                        # 6-bit fields
+    bits = ((f[..., None] >> np.arange(6)) & 1).astype(np.uint8)   # [rows, K, 6], LSB first
+    bits = bits.reshape(rows, K // 32, 32 * 6)
+    return np.packbits(bits, axis=-1, bitorder="little").reshape(rows, K // 32 * 24)
+
+
+def unpack_e2m3(stored: np.ndarray, K: int) -> np.ndarray:
+    """Inverse of pack_e2m3."""
+    b = np.asarray(stored, np.uint8)
+    rows = b.shape[0]
+    bits = np.unpackbits(b.reshape(rows, K // 32, 24), axis=-1, bitorder="little").reshape(rows, K, 6)
+    f = (bits.astype(np.int64) << np.arange(6)).sum(axis=-1)
+    mag = f & 31
+    return np.where(f & 32, -mag, mag).astype(np.int8)
+
+
 # ------------------------------------------------------------------ format table
 FORMATS = {
     # name: (group size, bits per code, scale dtype)
     "int4": (64, 4, "fp16"),
     "int8": (64, 8, "fp16"),
     "fp4": (16, 4, "e4m3"),
+    "int4_e2m3": (64, 6, "fp16"),   # INT4 codes in a 6-bit container
 }
 
 
@@ -127,6 +153,9 @@ def quantize(v: np.ndarray, fmt: str):
     if fmt == "int8":
         q, s = quantize_int(v, INT8_QMAX, 64)
         return q, s, q.copy()
+    if fmt == "int4_e2m3":
+        q, s = quantize_int(v, INT4_QMAX, 64)
+        return q, s, pack_e2m3(q)
     if fmt == "fp4":
         q, s = quantize_fp4(v, 16)
         return q, s, pack_nibbles(q)
@@ -134,7 +163,7 @@ def quantize(v: np.ndarray, fmt: str):
 
 
 def dequantize(codes, scales, fmt: str) -> np.ndarray:
-    if fmt in ("int4", "int8"):
+    if fmt in ("int4", "int8", "int4_e2m3"):
         return dequant_int(codes, scales, 64)
     if fmt == "fp4":
         return dequant_fp4(codes, scales, 16)

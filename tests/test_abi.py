@@ -69,7 +69,7 @@ def test_quantize_down_validation():
     assert qd(M=-1) == SHAPE
     assert qd(r=8) == SHAPE
     assert qd(r=80) == SHAPE
-    assert qd(fmt=3) == FORMAT
+    assert qd(fmt=4) == FORMAT
     assert qd(x=MIS) == ALIGN
     assert qd(t=MIS) == ALIGN
     assert qd(M=0) == OK            # empty input: nothing enqueued

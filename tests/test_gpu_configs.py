@@ -43,6 +43,10 @@ def same_bytes(a, b):
     return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
+def dev_scales(s, fmt):
+    return np.ascontiguousarray(s.T) if fmt == "int4_e2m3" else s
+
+
 def run_layer(P, fmt, x_hat=None, check_codes=True):
     """GPU: weight quantizer, Kernel A, Kernel B and the fused call; oracle: the same layer."""
     x_hat = P.x_hat if x_hat is None else x_hat
@@ -59,10 +63,10 @@ def run_layer(P, fmt, x_hat=None, check_codes=True):
     wq, ws = binding.svdq_quantize_weight(dev(P.res.T), fmt)
     if check_codes:
         assert same_bytes(host(wq), ref["wstored"]), "weight codes"
-        assert same_bytes(host(ws), ref["ws"]), "weight scales"
+        assert same_bytes(host(ws), dev_scales(ref["ws"], fmt)), "weight scales"
         xq, xs, t = binding.svdq_quantize_down(gx, gl1t, fmt)
         assert same_bytes(host(xq), ref["xstored"]), "activation codes"
-        assert same_bytes(host(xs), ref["xs"]), "activation scales"
+        assert same_bytes(host(xs), dev_scales(ref["xs"], fmt)), "activation scales"
         if r:
             tg = host(t)
             assert rel_fro(tg, ref["t"]) <= TOL
@@ -86,8 +90,13 @@ def test_c0_tiny_layer():
     run_layer(prepared("c0", 32), "int4")
 
 
-def test_c1_qkv():
-    run_layer(prepared("c1_qkv", 32), "int4")
+@pytest.mark.parametrize("fmt", ["int4", "int4_e2m3"])
+def test_c1_qkv(fmt):
+    run_layer(prepared("c1_qkv", 32), fmt)
+
+
+def test_c2_fc1_e2m3_container():
+    run_layer(prepared("c2_fc1", 32), "int4_e2m3")
 
 
 def test_c2_mlp_pair():

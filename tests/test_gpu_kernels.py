@@ -42,6 +42,14 @@ def same_bytes(a, b):
     return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
+def dev_scales(s, fmt):
+    """Scales in the device layout of the format (group-major for the E2M3 container)."""
+    return np.ascontiguousarray(s.T) if fmt == "int4_e2m3" else s
+
+
+FMTS = ["int4", "int8", "fp4", "int4_e2m3"]
+
+
 def draw(seed, M, K, N, r, xscale=0.7, rscale=0.05):
     g = np.random.default_rng(seed)
     x_hat = (g.standard_normal((M, K)) * xscale)
@@ -61,7 +69,7 @@ SHAPES = [  # M, K, N, r
 ]
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int8", "fp4"])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,K,N,r", SHAPES)
 def test_quantize_down_parity(fmt, M, K, N, r):
     log(f"quantize_down {fmt} M={M} K={K} r={r}")
@@ -69,7 +77,7 @@ def test_quantize_down_parity(fmt, M, K, N, r):
     q, s, stored = oracle.quant.quantize(x_hat, fmt)
     xq, xs, t = binding.svdq_quantize_down(dev(x_hat), dev(l1.T) if r else None, fmt)
     assert same_bytes(host(xq), stored)
-    assert same_bytes(host(xs), s)
+    assert same_bytes(host(xs), dev_scales(s, fmt))
     if r:
         tr = oracle.forward.down_projection(x_hat, l1)
         tg = host(t)
@@ -78,7 +86,7 @@ def test_quantize_down_parity(fmt, M, K, N, r):
         assert ok, worst
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int8", "fp4"])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("N,K", [(16, 64), (48, 192), (272, 320), (1024, 512)])
 def test_quantize_weight_parity(fmt, N, K):
     log(f"quantize_weight {fmt} N={N} K={K}")
@@ -87,7 +95,7 @@ def test_quantize_weight_parity(fmt, N, K):
     q, s, stored = oracle.quant.quantize(r_t, fmt)
     wq, ws = binding.svdq_quantize_weight(dev(r_t), fmt)
     assert same_bytes(host(wq), stored)
-    assert same_bytes(host(ws), s)
+    assert same_bytes(host(ws), dev_scales(s, fmt))
 
 
 def test_quantizers_subnormal_scales_and_zero_groups():
@@ -95,15 +103,15 @@ def test_quantizers_subnormal_scales_and_zero_groups():
     g = np.random.default_rng(3)
     x = (g.standard_normal((5, 256)) * 1e-6).astype(np.float16)
     x[:, 64:128] = 0
-    for fmt in ("int4", "int8", "fp4"):
+    for fmt in FMTS:
         q, s, stored = oracle.quant.quantize(x, fmt)
         xq, xs, _ = binding.svdq_quantize_down(dev(x), None, fmt)
         assert same_bytes(host(xq), stored), fmt
-        assert same_bytes(host(xs), s), fmt
+        assert same_bytes(host(xs), dev_scales(s, fmt)), fmt
         wq, ws = binding.svdq_quantize_weight(dev(x.astype(np.float32)[:, :].repeat(16, axis=0)[:80]), fmt)
         q2, s2, st2 = oracle.quant.quantize(x.astype(np.float32).repeat(16, axis=0)[:80], fmt)
         assert same_bytes(host(wq), st2), fmt
-        assert same_bytes(host(ws), s2), fmt
+        assert same_bytes(host(ws), dev_scales(s2, fmt)), fmt
 
 
 def _gemm_inputs(fmt, M, K, N, r, seed):
@@ -114,7 +122,7 @@ def _gemm_inputs(fmt, M, K, N, r, seed):
     return x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int8", "fp4"])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,K,N,r", SHAPES)
 @pytest.mark.parametrize("with_bias", [True, False])
 def test_gemm_up_parity(fmt, M, K, N, r, with_bias):
@@ -122,8 +130,9 @@ def test_gemm_up_parity(fmt, M, K, N, r, with_bias):
     x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs(fmt, M, K, N, r, M + N + K + r)
     bias = b if with_bias else None
     ref = oracle.forward.linear(xq, xs, t, wq, ws, l2, bias, fmt)
-    y = binding.svdq_gemm_w4a4_up(dev(xst), dev(xs), dev(t) if r else None, dev(wst), dev(ws),
-                                  dev(l2) if r else None, dev(bias) if with_bias else None, K, fmt)
+    y = binding.svdq_gemm_w4a4_up(dev(xst), dev(dev_scales(xs, fmt)), dev(t) if r else None, dev(wst),
+                                  dev(dev_scales(ws, fmt)), dev(l2) if r else None,
+                                  dev(bias) if with_bias else None, K, fmt)
     yg = host(y)
     assert np.isfinite(yg.astype(np.float32)).all()
     assert rel_fro(yg, ref) <= TOL
@@ -132,7 +141,7 @@ def test_gemm_up_parity(fmt, M, K, N, r, with_bias):
     assert ok, worst
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int8", "fp4"])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,K,N,r", [(17, 192, 48, 32), (130, 320, 272, 32), (257, 256, 144, 64), (1, 64, 16, 0)])
 def test_linear_end_to_end(fmt, M, K, N, r):
     log(f"linear {fmt} M={M} K={K} N={N} r={r}")
@@ -154,31 +163,34 @@ def _grid(g, rows, K):
     return q
 
 
+@pytest.mark.parametrize("fmt", ["int4", "int4_e2m3"])
 @pytest.mark.parametrize("M,K,N", [(1, 64, 16), (33, 192, 48), (200, 320, 144)])
-def test_exact_grid_bit_for_bit(M, K, N):
+def test_exact_grid_bit_for_bit(M, K, N, fmt):
     g = np.random.default_rng(M + K + N)
     qx, qr = _grid(g, M, K), _grid(g, N, K)
     x_hat = (qx * 2.0 ** -4).astype(np.float16)
     r_t = (qr * 2.0 ** -4).astype(np.float32)
     exact = (qx.astype(object) @ qr.T.astype(object))
     ref = np.array([[float(v) * 2.0 ** -8 for v in row] for row in exact]).astype(np.float16)
-    wq, ws = binding.svdq_quantize_weight(dev(r_t), "int4")
-    y = binding.svdq_linear(dev(x_hat), None, wq, ws, None, None, "int4")
+    wq, ws = binding.svdq_quantize_weight(dev(r_t), fmt)
+    y = binding.svdq_linear(dev(x_hat), None, wq, ws, None, None, fmt)
     assert np.array_equal(host(y).view(np.uint16), ref.view(np.uint16))
 
 
-def test_unfused_matches_fused():
+@pytest.mark.parametrize("fmt", ["int4", "int4_e2m3"])
+def test_unfused_matches_fused(fmt):
     M, K, N, r = 130, 320, 272, 32
-    x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs("int4", M, K, N, r, 5)
-    ref = oracle.forward.linear(xq, xs, t, wq, ws, l2, b, "int4")
-    args = (dev(x_hat), dev(l1.T), dev(wst), dev(ws), dev(l2), dev(b), "int4")
+    x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs(fmt, M, K, N, r, 5)
+    ref = oracle.forward.linear(xq, xs, t, wq, ws, l2, b, fmt)
+    ws_d = dev(dev_scales(ws, fmt))
+    args = (dev(x_hat), dev(l1.T), dev(wst), ws_d, dev(l2), dev(b), fmt)
     yu = host(binding.svdq_linear_unfused(*args))
     yf = host(binding.svdq_linear(*args))
     assert rel_fro(yu, ref) <= TOL
     assert rel_fro(yu, yf) <= TOL
     # r = 0: the unfused path is the bare GEMM
-    y0 = host(binding.svdq_linear_unfused(dev(x_hat), None, dev(wst), dev(ws), None, dev(b), "int4"))
-    ref0 = oracle.forward.linear(xq, xs, np.zeros((M, 0), np.float16), wq, ws, np.zeros((0, N), np.float16), b, "int4")
+    y0 = host(binding.svdq_linear_unfused(dev(x_hat), None, dev(wst), ws_d, None, dev(b), fmt))
+    ref0 = oracle.forward.linear(xq, xs, np.zeros((M, 0), np.float16), wq, ws, np.zeros((0, N), np.float16), b, fmt)
     assert rel_fro(y0, ref0) <= TOL
 
 
@@ -209,18 +221,20 @@ def test_gelu_smooth_parity(M, C):
     assert fp16_ulp_diff(out, ref) <= 1
 
 
-def test_repeat_runs_are_bitwise_identical():
+@pytest.mark.parametrize("fmt", ["int4", "int4_e2m3"])
+def test_repeat_runs_are_bitwise_identical(fmt):
     M, K, N, r = 257, 256, 144, 32
-    x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs("int4", M, K, N, r, 11)
-    args = (dev(x_hat), dev(l1.T), dev(wst), dev(ws), dev(l2), dev(b), "int4")
+    x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs(fmt, M, K, N, r, 11)
+    args = (dev(x_hat), dev(l1.T), dev(wst), dev(dev_scales(ws, fmt)), dev(l2), dev(b), fmt)
     first = host(binding.svdq_linear(*args))
     for _ in range(9):
         assert np.array_equal(host(binding.svdq_linear(*args)).view(np.uint16), first.view(np.uint16))
 
 
-def test_outputs_stay_inside_their_buffers():
+@pytest.mark.parametrize("fmt", ["int4", "int4_e2m3"])
+def test_outputs_stay_inside_their_buffers(fmt):
     M, K, N, r = 130, 192, 48, 32
-    x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs("int4", M, K, N, r, 12)
+    x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs(fmt, M, K, N, r, 12)
     guard = 4096
     canary = 0x5A
 
@@ -229,12 +243,13 @@ def test_outputs_stay_inside_their_buffers():
         view = buf[guard:guard + nbytes].view(dtype).view(*shape)
         return buf, view
 
-    bq, gq = guarded(M * K // 2, torch.uint8, (M, K // 2))
-    bs, gs = guarded(M * K // 64 * 2, torch.float16, (M, K // 64))
+    cb = binding.code_row_bytes(K, fmt)
+    bq, gq = guarded(M * cb, torch.uint8, (M, cb))
+    bs, gs = guarded(M * K // 64 * 2, torch.float16, binding.scale_shape(M, K, fmt))
     bt, gt = guarded(M * r * 2, torch.float16, (M, r))
-    binding.svdq_quantize_down(dev(x_hat), dev(l1.T), "int4", xq=gq, xs=gs, t=gt)
+    binding.svdq_quantize_down(dev(x_hat), dev(l1.T), fmt, xq=gq, xs=gs, t=gt)
     by, gy = guarded(M * N * 2, torch.float16, (M, N))
-    binding.svdq_gemm_w4a4_up(gq, gs, gt, dev(wst), dev(ws), dev(l2), dev(b), K, "int4", y=gy)
+    binding.svdq_gemm_w4a4_up(gq, gs, gt, dev(wst), dev(dev_scales(ws, fmt)), dev(l2), dev(b), K, fmt, y=gy)
     for buf in (bq, bs, bt, by):
         h = host(buf)
         assert (h[:guard] == canary).all() and (h[-guard:] == canary).all()
