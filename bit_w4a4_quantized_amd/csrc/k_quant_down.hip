@@ -7,10 +7,12 @@
 // read of the activations.
 //
 // Work decomposition (gfx950, wave64):
-//   one workgroup = 4 waves = 16 token rows; the waves split K into 64-column
+//   one workgroup = NW waves = 16 token rows; the waves split K into 64-column
 //   chunks round-robin and each keeps its 16 x r partial of T in MFMA
 //   accumulators; the partials are summed through LDS at the end (fixed order,
-//   deterministic, no atomics).
+//   deterministic, no atomics).  Eight waves per workgroup and at most 128
+//   VGPRs let two workgroups share a CU, so the last partial round of
+//   workgroups does not leave most CUs idle.
 //   Lane l of a wave owns row (l % 16) and the 8-column slices
 //   [8 (l/16), +8) and [32 + 8 (l/16), +8) of each chunk: one 16-byte load
 //   each.  That is exactly the operand layout of v_mfma_f32_16x16x32_f16 for
@@ -18,18 +20,22 @@
 //   straight from the registers they were quantized from.
 //   Group absmax: within the lane, then across the 4 lanes of the row with two
 //   cross-lane xor shuffles (INT, group 64) or one (FP4, group 16).
-//   NB chunks are loaded before any is processed, to keep enough HBM reads
-//   in flight.
+//   INT codes use the division-free rule of int_code_f16 (exact for fp16
+//   inputs); NB chunks are loaded before any is processed, to keep HBM reads in
+//   flight.
 #include "kernels.h"
 #include "quant_core.h"
 
 namespace svdq {
 
+constexpr int QD_WAVES = 8;
+
 template <int FMT, int RB, bool QUANT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * QD_WAVES, 2)
 k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M, int K,
              uint8_t* __restrict__ xq, uint8_t* __restrict__ xs, __half* __restrict__ t) {
-  constexpr int NB = 4;                     // chunks in flight per wave
+  constexpr int NB = 2;                     // chunks in flight per wave
+  constexpr int NW = QD_WAVES;
   constexpr int R = RB * 16;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -44,33 +50,30 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
 #pragma unroll
   for (int j = 0; j < (RB > 0 ? RB : 1); j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int c0 = wave; c0 < nchunks; c0 += 4 * NB) {
+  for (int c0 = wave; c0 < nchunks; c0 += NW * NB) {
     uint4 xv[NB][2];
     uint4 bv[NB][RB > 0 ? RB : 1][2];
 #pragma unroll
     for (int i = 0; i < NB; i++) {
-      const int c = c0 + 4 * i;
-      if (c < nchunks) {
-        const int col = c * 64 + sub * 8;
-        if (valid) {
-          xv[i][0] = *reinterpret_cast<const uint4*>(xrow + col);
-          xv[i][1] = *reinterpret_cast<const uint4*>(xrow + col + 32);
-        } else {
-          xv[i][0] = make_uint4(0, 0, 0, 0);
-          xv[i][1] = make_uint4(0, 0, 0, 0);
-        }
+      const int c = min(c0 + NW * i, nchunks - 1);   // a chunk past the end re-reads the last (unused)
+      const int col = c * 64 + sub * 8;
+      xv[i][0] = *reinterpret_cast<const uint4*>(xrow + col);
+      xv[i][1] = *reinterpret_cast<const uint4*>(xrow + col + 32);
 #pragma unroll
-        for (int j = 0; j < RB; j++) {
-          const __half* lrow = l1t + (size_t)(j * 16 + row) * K + col;
-          bv[i][j][0] = *reinterpret_cast<const uint4*>(lrow);
-          bv[i][j][1] = *reinterpret_cast<const uint4*>(lrow + 32);
-        }
+      for (int j = 0; j < RB; j++) {
+        const __half* lrow = l1t + (size_t)(j * 16 + row) * K + col;
+        bv[i][j][0] = *reinterpret_cast<const uint4*>(lrow);
+        bv[i][j][1] = *reinterpret_cast<const uint4*>(lrow + 32);
       }
     }
 #pragma unroll
     for (int i = 0; i < NB; i++) {
-      const int c = c0 + 4 * i;
+      const int c = c0 + NW * i;
       if (c >= nchunks) break;
+      if (!valid) {                          // rows past M contribute zeros to the MFMA
+        xv[i][0] = make_uint4(0, 0, 0, 0);
+        xv[i][1] = make_uint4(0, 0, 0, 0);
+      }
       // ---- down projection on the matrix core (fp16 in, fp32 accumulate)
 #pragma unroll
       for (int j = 0; j < RB; j++) {
@@ -92,14 +95,21 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
         amax = fmaxf(amax, __shfl_xor(amax, 32));
         uint16_t sbits;
         const float s = int_scale(amax, qmax, &sbits);
-        int q[16];
+        const float rs = s == 0.0f ? 0.0f : 1.0f / s;
+        float q[16];
 #pragma unroll
-        for (int e = 0; e < 16; e++) q[e] = int_code(v[e], s, qmax);
+        for (int e = 0; e < 16; e++) q[e] = int_code_f16(v[e], rs, qmax);
         if (valid) {
           if (FMT == FMT_INT4) {
             uint8_t* dst = xq + (size_t)m * (K >> 1);
-            *reinterpret_cast<uint32_t*>(dst + (col >> 1)) = pack8(q);
-            *reinterpret_cast<uint32_t*>(dst + ((col + 32) >> 1)) = pack8(q + 8);
+            uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+              w0 |= ((uint32_t)(int)q[e] & 0xFu) << (4 * e);
+              w1 |= ((uint32_t)(int)q[8 + e] & 0xFu) << (4 * e);
+            }
+            *reinterpret_cast<uint32_t*>(dst + (col >> 1)) = w0;
+            *reinterpret_cast<uint32_t*>(dst + ((col + 32) >> 1)) = w1;
           } else if (FMT == FMT_INT4_E2M3) {
             // 6-bit container: group c occupies 48 bytes of the row, half h (codes 32h..32h+31)
             // 24 bytes; this lane's 8 codes of each half are fields 8 sub .. 8 sub + 7, i.e. the
@@ -107,20 +117,33 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
             uint8_t* dst = xq + (size_t)m * (size_t)(K >> 6) * 48 + (size_t)c * 48 + 6 * sub;
 #pragma unroll
             for (int hh = 0; hh < 2; hh++) {
-              const uint64_t w = pack6x8(q + 8 * hh);
+              uint32_t lo = 0;                   // bits 0..31 of the 48-bit run
+#pragma unroll
+              for (int e = 0; e < 5; e++) lo |= e2m3_field(q[8 * hh + e]) << (6 * e);
+              const uint32_t f5 = e2m3_field(q[8 * hh + 5]);
+              lo |= f5 << 30;
+              // bits 32..47
+              const uint32_t hi = (f5 >> 2) | (e2m3_field(q[8 * hh + 6]) << 4) | (e2m3_field(q[8 * hh + 7]) << 10);
               uint8_t* d = dst + 24 * hh;
               if ((sub & 1) == 0) {
-                *reinterpret_cast<uint32_t*>(d) = (uint32_t)w;
-                *reinterpret_cast<uint16_t*>(d + 4) = (uint16_t)(w >> 32);
+                *reinterpret_cast<uint32_t*>(d) = lo;
+                *reinterpret_cast<uint16_t*>(d + 4) = (uint16_t)hi;
               } else {
-                *reinterpret_cast<uint16_t*>(d) = (uint16_t)w;
-                *reinterpret_cast<uint32_t*>(d + 2) = (uint32_t)(w >> 16);
+                *reinterpret_cast<uint16_t*>(d) = (uint16_t)lo;
+                *reinterpret_cast<uint32_t*>(d + 2) = (lo >> 16) | (hi << 16);
               }
             }
           } else {
             uint8_t* dst = xq + (size_t)m * K;
-            *reinterpret_cast<uint2*>(dst + col) = make_uint2(pack4_i8(q), pack4_i8(q + 4));
-            *reinterpret_cast<uint2*>(dst + col + 32) = make_uint2(pack4_i8(q + 8), pack4_i8(q + 12));
+            uint32_t w[4];
+#pragma unroll
+            for (int k4 = 0; k4 < 4; k4++) {
+              w[k4] = 0;
+#pragma unroll
+              for (int e = 0; e < 4; e++) w[k4] |= ((uint32_t)(int)q[4 * k4 + e] & 0xFFu) << (8 * e);
+            }
+            *reinterpret_cast<uint2*>(dst + col) = make_uint2(w[0], w[1]);
+            *reinterpret_cast<uint2*>(dst + col + 32) = make_uint2(w[2], w[3]);
           }
           if (sub == 0) {
             // row-major scales [M, K/64]; the 6-bit container format keeps them group-major [K/64, M]
@@ -155,18 +178,20 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
   }
 
   if (RB > 0) {
-    // ---- reduce the four waves' partials of T (fixed order) and store fp16
-    __shared__ float part[4][16][R > 0 ? R : 1];
+    // ---- reduce the waves' partials of T (fixed order) and store fp16
+    __shared__ float part[NW][16][R > 0 ? R : 1];
 #pragma unroll
     for (int j = 0; j < RB; j++)
 #pragma unroll
       for (int i = 0; i < 4; i++) part[wave][4 * sub + i][j * 16 + row] = acc[j][i];
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * R; idx += 256) {
+    for (int idx = threadIdx.x; idx < 16 * R; idx += 64 * NW) {
       const int rr = idx / R, cc = idx % R;
       const int mm = blockIdx.x * 16 + rr;
       if (mm < M) {
-        const float s = ((part[0][rr][cc] + part[1][rr][cc]) + part[2][rr][cc]) + part[3][rr][cc];
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; w++) s += part[w][rr][cc];
         t[(size_t)mm * R + cc] = __float2half_rn(s);
       }
     }
@@ -176,8 +201,8 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
 template <int FMT, int RB, bool QUANT = true>
 static hipError_t launch_qd(const QuantDownArgs& a, hipStream_t s) {
   dim3 grid((a.M + 15) / 16);
-  hipLaunchKernelGGL((k_quant_down<FMT, RB, QUANT>), grid, dim3(256), 0, s, (const __half*)a.x, (const __half*)a.l1t,
-                     a.M, a.K, (uint8_t*)a.xq, (uint8_t*)a.xs, (__half*)a.t);
+  hipLaunchKernelGGL((k_quant_down<FMT, RB, QUANT>), grid, dim3(64 * QD_WAVES), 0, s, (const __half*)a.x,
+                     (const __half*)a.l1t, a.M, a.K, (uint8_t*)a.xq, (uint8_t*)a.xs, (__half*)a.t);
   return hipGetLastError();
 }
 

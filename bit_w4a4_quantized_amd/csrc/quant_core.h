@@ -31,6 +31,32 @@ __device__ __forceinline__ int int_code(float v, float s, float qmax) {
   return (int)t;
 }
 
+// Code of an fp16 value x (as float) against an fp16 scale s, given r = 1/s
+// (fp32, correctly rounded; r = 0 when s == 0).  Equals
+// clamp(rint(fp32(x) / s), -qmax, qmax) for qmax <= 127 without the division:
+//   * x and s are fp16, so x/s is either exactly a half-integer n + 1/2 or at
+//     least 2^-13 away from every half-integer (the difference x - (n+1/2) s is
+//     a nonzero multiple of the finer of the two fp16 grids);
+//   * t = x * r is within |x/s| 2^-23 (< 2^-16 while |x/s| <= 128) of x/s, and
+//     the IEEE quotient is within half an fp32 ulp of it, so away from a tie both
+//     round to the same integer;
+//   * an exact tie shows as |t - floor(t) - 1/2| < 2^-14 and is rounded from the
+//     exact half, i.e. to even, as rint does for the tied fp32 quotient.
+// Past |x/s| = 128 the result is clamped whatever the rounding.
+__device__ __forceinline__ float int_code_f16(float x, float r, float qmax) {
+  const float t = x * r;
+  const float tf = floorf(t);
+  const bool tie = fabsf((t - tf) - 0.5f) < 0x1p-14f;
+  const float q = rintf(tie ? tf + 0.5f : t);
+  return fminf(fmaxf(q, -qmax), qmax);
+}
+
+// 6-bit E2M3 field of an INT4 code held as a float: sign<<5 | |q| (q = 0 -> 0).
+__device__ __forceinline__ uint32_t e2m3_field(float q) {
+  const uint32_t a = (uint32_t)fabsf(q);
+  return q < 0.0f ? (a | 32u) : a;
+}
+
 // fp32 (finite, >= 0) -> E4M3FN byte, round to nearest even, saturating at 448.
 __device__ __forceinline__ uint32_t e4m3_encode_pos(float a) {
   if (!(a < 448.0f)) return 0x7Eu;

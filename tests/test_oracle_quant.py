@@ -208,3 +208,35 @@ def test_e2m3_format_has_int4_codes_and_scales(rng):
     q6, s6, st6 = quant.quantize(v, "int4_e2m3")
     assert np.array_equal(q4, q6) and np.array_equal(s4.view(np.uint16), s6.view(np.uint16))
     assert np.array_equal(quant.unpack_e2m3(st6, 128), q4)
+
+
+def _fast_code(x32, s32, qmax):
+    """Kernel A's division-free code rule, simulated in IEEE fp32 (numpy float32 ops)."""
+    with np.errstate(divide="ignore"):
+        r = np.where(s32 == 0, np.float32(0), np.float32(1) / s32).astype(np.float32)
+    t = (x32 * r).astype(np.float32)
+    tf = np.floor(t).astype(np.float32)
+    tie = np.abs((t - tf).astype(np.float32) - np.float32(0.5)) < np.float32(2.0 ** -14)
+    q = np.rint(np.where(tie, (tf + np.float32(0.5)).astype(np.float32), t))
+    return np.clip(q, -qmax, qmax)
+
+
+@pytest.mark.parametrize("qmax", [7, 127])
+def test_division_free_code_rule_matches_definition_exhaustively(qmax):
+    """Every fp16 value against a spread of fp16 scales (normal and subnormal): the kernel's
+    reciprocal-and-tie rule gives clamp(rint(fp32(x) / s)) exactly."""
+    xs = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float32)   # all finite >= 0
+    xs = np.concatenate([xs, -xs])
+    g = np.random.default_rng(qmax)
+    scales = np.concatenate([
+        np.arange(1, 1024, 37, dtype=np.uint16),                 # subnormal fp16 scales
+        g.integers(0x0400, 0x7BFF, 120).astype(np.uint16),       # normal fp16 scales
+        np.array([0x3C00, 0x3800, 0x2E66, 0x0001, 0x03FF], np.uint16),
+    ]).view(np.float16).astype(np.float32)
+    for s in scales:
+        s32 = np.float32(s)
+        ref = np.clip(np.rint((xs / s32).astype(np.float32)), -qmax, qmax)
+        got = _fast_code(xs, np.full_like(xs, s32), qmax)
+        assert np.array_equal(got, ref), float(s)
+    # the zero scale gives code 0
+    assert not _fast_code(xs[:100], np.zeros(100, np.float32), qmax).any()
