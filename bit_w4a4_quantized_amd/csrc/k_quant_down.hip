@@ -50,6 +50,14 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
 #pragma unroll
   for (int j = 0; j < (RB > 0 ? RB : 1); j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // Codes of one chunk (16 rows x CB bytes) are assembled in this wave's LDS slot and
+  // written back with whole 16-byte stores per lane: the per-lane pieces (2 to 6 bytes,
+  // odd offsets for the 6-bit container) would otherwise be many small scattered stores.
+  constexpr int CB = FMT == FMT_INT4_E2M3 ? 48 : (FMT == FMT_INT8 ? 64 : 32);   // code bytes per row per chunk
+  __shared__ __attribute__((aligned(16))) uint8_t cstage[NW][16 * CB];
+  uint8_t* slot = cstage[wave];
+  const size_t code_row = FMT == FMT_INT4_E2M3 ? (size_t)(K >> 6) * 48 : (FMT == FMT_INT8 ? (size_t)K : (size_t)(K >> 1));
+
   for (int c0 = wave; c0 < nchunks; c0 += NW * NB) {
     uint4 xv[NB][2];
     uint4 bv[NB][RB > 0 ? RB : 1][2];
@@ -99,22 +107,22 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
         float q[16];
 #pragma unroll
         for (int e = 0; e < 16; e++) q[e] = int_code_f16(v[e], rs, qmax);
-        if (valid) {
+        {
+          uint8_t* srow = slot + row * CB;   // this row's bytes of the chunk, in LDS
           if (FMT == FMT_INT4) {
-            uint8_t* dst = xq + (size_t)m * (K >> 1);
             uint32_t w0 = 0, w1 = 0;
 #pragma unroll
             for (int e = 0; e < 8; e++) {
               w0 |= ((uint32_t)(int)q[e] & 0xFu) << (4 * e);
               w1 |= ((uint32_t)(int)q[8 + e] & 0xFu) << (4 * e);
             }
-            *reinterpret_cast<uint32_t*>(dst + (col >> 1)) = w0;
-            *reinterpret_cast<uint32_t*>(dst + ((col + 32) >> 1)) = w1;
+            *reinterpret_cast<uint32_t*>(srow + 4 * sub) = w0;
+            *reinterpret_cast<uint32_t*>(srow + 16 + 4 * sub) = w1;
           } else if (FMT == FMT_INT4_E2M3) {
             // 6-bit container: group c occupies 48 bytes of the row, half h (codes 32h..32h+31)
             // 24 bytes; this lane's 8 codes of each half are fields 8 sub .. 8 sub + 7, i.e. the
             // 6 bytes at offset 6 sub of the half.
-            uint8_t* dst = xq + (size_t)m * (size_t)(K >> 6) * 48 + (size_t)c * 48 + 6 * sub;
+            uint8_t* dst = srow + 6 * sub;
 #pragma unroll
             for (int hh = 0; hh < 2; hh++) {
               uint32_t lo = 0;                   // bits 0..31 of the 48-bit run
@@ -134,7 +142,6 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
               }
             }
           } else {
-            uint8_t* dst = xq + (size_t)m * K;
             uint32_t w[4];
 #pragma unroll
             for (int k4 = 0; k4 < 4; k4++) {
@@ -142,9 +149,20 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
 #pragma unroll
               for (int e = 0; e < 4; e++) w[k4] |= ((uint32_t)(int)q[4 * k4 + e] & 0xFFu) << (8 * e);
             }
-            *reinterpret_cast<uint2*>(dst + col) = make_uint2(w[0], w[1]);
-            *reinterpret_cast<uint2*>(dst + col + 32) = make_uint2(w[2], w[3]);
+            *reinterpret_cast<uint2*>(srow + 8 * sub) = make_uint2(w[0], w[1]);
+            *reinterpret_cast<uint2*>(srow + 32 + 8 * sub) = make_uint2(w[2], w[3]);
           }
+        }
+        // the wave's 16 x CB bytes go out as CB/16 16-byte pieces per row
+        __builtin_amdgcn_wave_barrier();
+        if (lane < CB) {
+          const int rr = lane / (CB / 16), part = lane % (CB / 16);
+          const int mm = blockIdx.x * 16 + rr;
+          const uint4 v16 = *reinterpret_cast<const uint4*>(slot + rr * CB + part * 16);
+          if (mm < M) *reinterpret_cast<uint4*>(xq + (size_t)mm * code_row + (size_t)c * CB + part * 16) = v16;
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
           if (sub == 0) {
             // row-major scales [M, K/64]; the 6-bit container format keeps them group-major [K/64, M]
             const size_t si = FMT == FMT_INT4_E2M3 ? (size_t)c * M + m : (size_t)m * (K >> 6) + c;
