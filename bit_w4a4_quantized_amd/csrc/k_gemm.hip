@@ -240,8 +240,8 @@ static hipError_t launch_g_b(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   switch (a.fmt) {
-    case FMT_INT4:
-    case FMT_INT4_E2M3: return launch_gemm2(a, s);
+    case FMT_INT4: return launch_gemm2(a, s);
+    case FMT_INT4_E2M3: return launch_gemm3(a, s);
     case FMT_INT8: return launch_g_b<FMT_INT8>(a, s);
     case FMT_FP4: return launch_g_b<FMT_FP4>(a, s);
   }
