@@ -144,7 +144,7 @@ def main():
         sets.append(dict(
             x=x_hat.clone(), l1t=cp(layer.l1t), wq=layer.wq.clone(), ws=layer.ws.clone(), l2=cp(layer.l2),
             b=layer.bias.clone(),
-            xq=torch.empty((M, binding.code_row_bytes(K, fmt)), dtype=torch.uint8, device="cuda"),
+            xq=torch.empty(binding.code_shape(M, K, fmt), dtype=torch.uint8, device="cuda"),
             xs=torch.empty(binding.scale_shape(M, K, fmt), dtype=binding.scale_dtype(fmt), device="cuda"),
             t=torch.empty((M, r), dtype=torch.float16, device="cuda") if r else None,
             y=torch.empty((M, N), dtype=torch.float16, device="cuda"),

@@ -109,6 +109,18 @@ def code_row_bytes(K: int, fmt) -> int:
     return int(lib().svdq_code_row_bytes(K, _fmt(fmt)))
 
 
+def code_shape(rows: int, K: int, fmt):
+    """Shape of a code tensor: [rows, row bytes], or group-major [K/64, rows, 48] for the
+    E2M3 container."""
+    name = fmt if isinstance(fmt, str) else FMT_NAMES[int(fmt)]
+    return (K // 64, rows, 48) if name == "int4_e2m3" else (rows, code_row_bytes(K, fmt))
+
+
+def code_rows(q) -> int:
+    """Rows (tokens or output columns) of a code tensor in either layout."""
+    return int(q.shape[1]) if q.dim() == 3 else int(q.shape[0])
+
+
 def scale_row_entries(K: int, fmt) -> int:
     name = fmt if isinstance(fmt, str) else FMT_NAMES[int(fmt)]
     return K // GROUP[name]
@@ -144,7 +156,7 @@ def svdq_quantize_down(x_hat, l1t, fmt, xq=None, xs=None, t=None, stream=None):
         _need(l1t, torch.float16, (r, K), "l1t")
     dev = x_hat.device
     if xq is None:
-        xq = torch.empty((M, code_row_bytes(K, fmt)), dtype=torch.uint8, device=dev)
+        xq = torch.empty(code_shape(M, K, fmt), dtype=torch.uint8, device=dev)
     if xs is None:
         xs = torch.empty(scale_shape(M, K, fmt), dtype=scale_dtype(fmt), device=dev)
     if r and t is None:
@@ -157,8 +169,8 @@ def svdq_quantize_down(x_hat, l1t, fmt, xq=None, xs=None, t=None, stream=None):
 def svdq_gemm_w4a4_up(xq, xs, t, wq, ws, l2, bias, K, fmt, y=None, stream=None):
     """Kernel B.  Returns y fp16 [M, N]."""
     import torch
-    M = xq.shape[0]
-    N = wq.shape[0]
+    M = code_rows(xq)
+    N = code_rows(wq)
     r = 0 if l2 is None else l2.shape[0]
     if y is None:
         y = torch.empty((M, N), dtype=torch.float16, device=xq.device)
@@ -171,7 +183,7 @@ def svdq_linear(x_hat, l1t, wq, ws, l2, bias, fmt, workspace=None, y=None, strea
     """Kernel A then Kernel B.  Returns y fp16 [M, N]."""
     import torch
     M, K = x_hat.shape
-    N = wq.shape[0]
+    N = code_rows(wq)
     r = 0 if l1t is None else l1t.shape[0]
     need = linear_workspace_bytes(M, K, r, fmt)
     if workspace is None:
@@ -190,7 +202,7 @@ def svdq_quantize_weight(r_t, fmt, wq=None, ws=None, stream=None):
     N, K = r_t.shape
     _need(r_t, torch.float32, None, "r_t")
     if wq is None:
-        wq = torch.empty((N, code_row_bytes(K, fmt)), dtype=torch.uint8, device=r_t.device)
+        wq = torch.empty(code_shape(N, K, fmt), dtype=torch.uint8, device=r_t.device)
     if ws is None:
         ws = torch.empty(scale_shape(N, K, fmt), dtype=scale_dtype(fmt), device=r_t.device)
     _check("svdq_quantize_weight", lib().svdq_quantize_weight(
@@ -202,7 +214,7 @@ def svdq_linear_unfused(x_hat, l1t, wq, ws, l2, bias, fmt, workspace=None, y=Non
     """The branch as separate kernels (measurement only).  Returns y fp16 [M, N]."""
     import torch
     M, K = x_hat.shape
-    N = wq.shape[0]
+    N = code_rows(wq)
     r = 0 if l1t is None else l1t.shape[0]
     need = linear_unfused_workspace_bytes(M, N, K, r, fmt)
     if workspace is None:
@@ -219,7 +231,7 @@ def svdq_gemm_w4a16(x, wq, ws, bias, y=None, stream=None):
     """W4A16 control.  x fp16 [M, K]; wq uint8 [N, K/2]; ws fp16 [N, K/64]."""
     import torch
     M, K = x.shape
-    N = wq.shape[0]
+    N = code_rows(wq)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float16, device=x.device)
     _check("svdq_gemm_w4a16", lib().svdq_gemm_w4a16(

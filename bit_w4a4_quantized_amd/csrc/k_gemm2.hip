@@ -1,5 +1,6 @@
-// Kernel B, LDS-staged: low-bit GEMM on the matrix cores, per-group rescale
-// into fp32, up projection and bias in the epilogue.
+// Kernel B for the canonical packed-nibble format (SVDQ_INT4_G64), LDS-staged:
+// low-bit GEMM on the INT8 matrix cores, per-group rescale into fp32, up
+// projection and bias in the epilogue.
 //
 // Practice page "sota-314", section "Do this": the up projection is fused
 // with the 4-bit compute because both write the same output.
@@ -7,17 +8,10 @@
 //   Y[m,n] = fp16_rne( sum_g sx[m,g] sw[n,g] P_g[m,n] + (T L2)[m,n] + b[n] )
 //   P_g    = sum_{k in group g} q_x[m,k] q_w[n,k]   (exact)
 //
-// Two operand cores share the skeleton:
-//   CORE_E2M3 -- INT4 codes stored in the 6-bit container (SVDQ_INT4_G64_E2M3):
-//     each code q is the E2M3 subnormal of q/8, so a group half (32 codes of a
-//     row) is exactly the 6-dword operand of v_mfma_scale_f32_32x32x64_f8f6f4
-//     in FP6 mode.  One MFMA per 32x32 tile per group gives P_g/64 in fp32,
-//     exactly (products of eighths, sums far below 2^24 units), at twice the
-//     INT8 rate and with no int->float conversion.  Scales are group-major.
-//   CORE_I4 -- canonical packed nibbles (SVDQ_INT4_G64): each lane reads 16
-//     bytes and turns them into int8 16q with two masks and a shift; two
-//     v_mfma_i32_32x32x32_i8 per tile per group; the int32 partial is
-//     converted to fp32.  Scales are row-major.
+// Each lane reads 16 bytes of packed nibbles and turns them into int8 16q with
+// two masks and a shift; two v_mfma_i32_32x32x32_i8 per tile per group; the
+// int32 partial is converted to fp32.  Scales are row-major.  (The 6-bit
+// container format has its own kernel on the FP6 matrix cores.)
 //
 // Tiling (gfx950, wave64): workgroup tile 128 x 128, four waves in 2 x 2 of
 // 64 x 64 (2 x 2 MFMA tiles of 32 x 32), two workgroups per CU.  K advances in
@@ -48,11 +42,6 @@ namespace {
 constexpr int BM = 128, BN = 128, NTHREADS = 256;
 
 template <int CORE> struct CoreCfg;
-template <> struct CoreCfg<CORE_E2M3> {
-  static constexpr int GB = 48;      // bytes per row per group in global memory
-  static constexpr int LS = 56;      // LDS row stride
-  static constexpr int CHUNKS = 3;   // 16-byte chunks per row per group
-};
 template <> struct CoreCfg<CORE_I4> {
   static constexpr int GB = 32;
   static constexpr int LS = 48;
@@ -91,10 +80,10 @@ k_gemm2(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
   constexpr int TILE_BYTES = BM * C::LS;                 // one operand tile of one group in LDS
   constexpr int GROUP_BYTES = 2 * TILE_BYTES + 256 * 2;  // A, B, 128 + 128 fp16 scales
   constexpr int STAGE_BYTES = KC * GROUP_BYTES;
-  // The MFMA partial of one group times PFACT is P_g (E2M3: operands are q/8; I4: 16q).
+  // The MFMA partial of one group times PFACT is P_g (the operands are 16q).
   // Every rescaled partial carries the same factor, so it is applied once to the
   // accumulator (exact: a power of two) before the branch is added.
-  constexpr float PFACT = CORE == CORE_E2M3 ? 64.0f : (1.0f / 256.0f);
+  constexpr float PFACT = 1.0f / 256.0f;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE_BYTES];
 
   const int tid = threadIdx.x;
@@ -130,10 +119,8 @@ k_gemm2(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
   const int s_row = (s_is_x ? m0 : n0) + (tid & 127);
   const bool s_ok = s_row < (s_is_x ? M : N);
   const unsigned short* s_base = reinterpret_cast<const unsigned short*>(s_is_x ? xs : ws);
-  const int s_rows = s_is_x ? M : N;
-  const unsigned short* s_ptr = s_base + (CORE == CORE_E2M3 ? (size_t)(s_ok ? s_row : 0)
-                                                          : (size_t)(s_ok ? s_row : 0) * G);
-  const size_t s_step = CORE == CORE_E2M3 ? (size_t)s_rows : 1;   // between consecutive groups
+  const unsigned short* s_ptr = s_base + (size_t)(s_ok ? s_row : 0) * G;
+  const size_t s_step = 1;   // between consecutive groups
 
   uint4 stage_reg[KC][C::CHUNKS];
   unsigned short stage_s[KC];
@@ -153,13 +140,7 @@ k_gemm2(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
 #pragma unroll
       for (int i = 0; i < C::CHUNKS; i++) {
         uint4 v = ok[i] ? stage_reg[k][i] : make_uint4(0, 0, 0, 0);
-        if (CORE == CORE_E2M3) {   // 8-byte aligned rows
-          uint2* p = reinterpret_cast<uint2*>(base + dst[i]);
-          p[0] = make_uint2(v.x, v.y);
-          p[1] = make_uint2(v.z, v.w);
-        } else {
-          *reinterpret_cast<uint4*>(base + dst[i]) = v;
-        }
+        *reinterpret_cast<uint4*>(base + dst[i]) = v;
       }
       reinterpret_cast<unsigned short*>(base + 2 * TILE_BYTES)[tid] = s_ok ? stage_s[k] : (unsigned short)0;
     }
@@ -180,8 +161,8 @@ k_gemm2(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
 
   const int arow0 = wm * 64 + r32;          // LDS row of this lane's A operand (tile 0)
   const int brow0 = wn * 64 + r32;
-  const int a_off = arow0 * C::LS + h * (CORE == CORE_E2M3 ? 24 : 16);
-  const int b_off = TILE_BYTES + brow0 * C::LS + h * (CORE == CORE_E2M3 ? 24 : 16);
+  const int a_off = arow0 * C::LS + h * 16;
+  const int b_off = TILE_BYTES + brow0 * C::LS + h * 16;
   const int sx_off = 2 * TILE_BYTES + 2 * arow0;
   const int sw_off = 2 * TILE_BYTES + 2 * (128 + brow0);
   for (int st = 0; st < NS; st++) {
@@ -202,49 +183,26 @@ k_gemm2(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
         sa[i] = as_h8(make_uint4(h ? 0u : (uint32_t)xa, 0u, 0u, 0u));
         sb[i] = as_h8(make_uint4(h ? 0u : (uint32_t)xb, 0u, 0u, 0u));
       }
-      if constexpr (CORE == CORE_E2M3) {
-        v8i a[2], b[2];
+      v4i a[2][2], b[2][2];
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
-          // 32 bytes per operand read; the hardware uses the first 24 (six dwords of FP6)
-          const uint2* pa = reinterpret_cast<const uint2*>(base + a_off + i * 32 * C::LS);
-          const uint2* pb = reinterpret_cast<const uint2*>(base + b_off + i * 32 * C::LS);
-          const uint2 a0 = pa[0], a1 = pa[1], a2 = pa[2], a3 = pa[3];
-          const uint2 b0 = pb[0], b1 = pb[1], b2 = pb[2], b3 = pb[3];
-          a[i] = v8i{(int)a0.x, (int)a0.y, (int)a1.x, (int)a1.y, (int)a2.x, (int)a2.y, (int)a3.x, (int)a3.y};
-          b[i] = v8i{(int)b0.x, (int)b0.y, (int)b1.x, (int)b1.y, (int)b2.x, (int)b2.y, (int)b3.x, (int)b3.y};
-        }
-#pragma unroll
-        for (int ti = 0; ti < 2; ti++)
-#pragma unroll
-          for (int tj = 0; tj < 2; tj++) {
-            const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ti], b[tj], v16f{}, 2, 2, 0, 127, 0, 127);
-            const v16f sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[ti], sb[tj], v16f{}, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 16; i++) acc[ti][tj][i] = __builtin_fmaf(p[i], sc[i], acc[ti][tj][i]);
-          }
-      } else {
-        v4i a[2][2], b[2][2];
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-          const uint4 ua = *reinterpret_cast<const uint4*>(base + a_off + i * 32 * C::LS);
-          const uint4 ub = *reinterpret_cast<const uint4*>(base + b_off + i * 32 * C::LS);
-          a[i][0] = v4i{(int)nib_lo16(ua.x), (int)nib_hi16(ua.x), (int)nib_lo16(ua.y), (int)nib_hi16(ua.y)};
-          a[i][1] = v4i{(int)nib_lo16(ua.z), (int)nib_hi16(ua.z), (int)nib_lo16(ua.w), (int)nib_hi16(ua.w)};
-          b[i][0] = v4i{(int)nib_lo16(ub.x), (int)nib_hi16(ub.x), (int)nib_lo16(ub.y), (int)nib_hi16(ub.y)};
-          b[i][1] = v4i{(int)nib_lo16(ub.z), (int)nib_hi16(ub.z), (int)nib_lo16(ub.w), (int)nib_hi16(ub.w)};
-        }
-#pragma unroll
-        for (int ti = 0; ti < 2; ti++)
-#pragma unroll
-          for (int tj = 0; tj < 2; tj++) {
-            v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ti][0], b[tj][0], v16i{}, 0, 0, 0);
-            p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ti][1], b[tj][1], p, 0, 0, 0);
-            const v16f sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[ti], sb[tj], v16f{}, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 16; i++) acc[ti][tj][i] = __builtin_fmaf((float)p[i], sc[i], acc[ti][tj][i]);
-          }
+      for (int i = 0; i < 2; i++) {
+        const uint4 ua = *reinterpret_cast<const uint4*>(base + a_off + i * 32 * C::LS);
+        const uint4 ub = *reinterpret_cast<const uint4*>(base + b_off + i * 32 * C::LS);
+        a[i][0] = v4i{(int)nib_lo16(ua.x), (int)nib_hi16(ua.x), (int)nib_lo16(ua.y), (int)nib_hi16(ua.y)};
+        a[i][1] = v4i{(int)nib_lo16(ua.z), (int)nib_hi16(ua.z), (int)nib_lo16(ua.w), (int)nib_hi16(ua.w)};
+        b[i][0] = v4i{(int)nib_lo16(ub.x), (int)nib_hi16(ub.x), (int)nib_lo16(ub.y), (int)nib_hi16(ub.y)};
+        b[i][1] = v4i{(int)nib_lo16(ub.z), (int)nib_hi16(ub.z), (int)nib_lo16(ub.w), (int)nib_hi16(ub.w)};
       }
+#pragma unroll
+      for (int ti = 0; ti < 2; ti++)
+#pragma unroll
+        for (int tj = 0; tj < 2; tj++) {
+          v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ti][0], b[tj][0], v16i{}, 0, 0, 0);
+          p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ti][1], b[tj][1], p, 0, 0, 0);
+          const v16f sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[ti], sb[tj], v16f{}, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 16; i++) acc[ti][tj][i] = __builtin_fmaf((float)p[i], sc[i], acc[ti][tj][i]);
+        }
     }
     // keep the next stage's LDS writes (and their wait on the global loads) after this compute
     __builtin_amdgcn_sched_barrier(0);
@@ -327,7 +285,6 @@ static hipError_t launch_g2_r(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm2(const GemmArgs& a, hipStream_t s) {
   const bool b = a.bias != nullptr;
-  if (a.fmt == FMT_INT4_E2M3) return b ? launch_g2_r<CORE_E2M3, true>(a, s) : launch_g2_r<CORE_E2M3, false>(a, s);
   if (a.fmt == FMT_INT4) return b ? launch_g2_r<CORE_I4, true>(a, s) : launch_g2_r<CORE_I4, false>(a, s);
   return hipErrorInvalidValue;
 }

@@ -25,13 +25,15 @@
 // 2 x 2 of 64 x 64 (2 x 2 MFMA tiles), two workgroups per CU.  K advances in
 // stages of two groups.  Global -> LDS staging goes through registers: buffer
 // loads whose per-group offset is a scalar, so the address arithmetic costs no
-// vector instructions; registers hold stage s+2 while LDS holds s and s+1.
+// vector instructions; while the waves compute stage s from LDS, stage s+1 is
+// written to the other LDS buffer and the loads of stages s+2 and s+3 are in
+// flight in two register slots (two stages of compute cover their latency).
 // LDS keeps, per group and operand, bytes 0..15 of each (row, half) in one
-// 16-byte slot and bytes 16..23 in one 8-byte slot, so every MFMA operand is
+// 16-byte slot and bytes 16..23 in one 8-byte slot (the slot order swizzled
+// against bank conflicts), so every MFMA operand is
 // one 16-byte and one 8-byte LDS read straight into its registers.  Scale
-// slots are 16 bytes, [scale, 0, ..., 0] as fp16: the lanes of the lower K half
-// read bytes 0..7 and those of the upper half the zero bytes 8..15; only the
-// first dword is rewritten per group.
+// slots are 8 bytes, [scale, 0, 0, 0] as fp16, read by the lanes of the lower K
+// half; the upper-half lanes read a zero block that is written once.
 // The block index is remapped so that each XCD (own L2) works on a contiguous
 // range of tiles, rastered in groups of 8 tile rows.
 #include "kernels.h"
@@ -41,16 +43,17 @@ namespace svdq {
 namespace {
 
 constexpr int BM = 128, BN = 128, NT = 256, KC = 2;
-constexpr int GB = 48;                      // container bytes per row per group
+constexpr int GB = 48;                      // container bytes per (row, group)
 // LDS layout of one group (byte offsets)
-constexpr int L_XP0 = 0;                    // X: bytes 0..15 of each half, [2 halves][128 rows] x 16
-constexpr int L_XP1 = 4096;                 // X: bytes 16..23 of each half, [2][128] x 8
+constexpr int L_XP0 = 0;                    // X: bytes 0..15 of each half, [128 rows][2 slots] x 16
+constexpr int L_XP1 = 4096;                 // X: bytes 16..23 of each half, [128 rows][2 slots] x 8
 constexpr int L_WP0 = 6144;                 // W: as X
 constexpr int L_WP1 = 10240;
-constexpr int L_S = 12288;                  // scale slots: [128 X rows + 128 W rows] x 16
-constexpr int GROUP = 16384;
+constexpr int L_S = 12288;                  // scale slots: [128 X rows + 128 W rows] x 8, then 256 zero bytes
+constexpr int L_Z = L_S + 2048;
+constexpr int GROUP = L_Z + 256;            // 14592
 constexpr int STAGE = KC * GROUP;
-constexpr int RING = 2 * STAGE;             // 65536 bytes
+constexpr int RING = 2 * STAGE;             // 58368 bytes
 // epilogue reuse of the ring
 constexpr int E_Y = 20480;                  // per-wave fp16 output staging, 64 rows x 136 bytes
 constexpr int E_YS = 136;
@@ -79,6 +82,17 @@ __device__ __forceinline__ uint2 ld8(rsrc_t r, uint32_t voff, uint32_t soff) {
   typedef int v2i_t __attribute__((ext_vector_type(2)));
   v2i_t v = __builtin_bit_cast(v2i_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
   return make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+}
+
+// LDS position of (row, half) in the 16-byte and 8-byte slot arrays: the two halves of a
+// row are neighbours, swapped on a row-bit pattern so that both the writers (neighbouring
+// lanes = the two halves of one row) and the readers (neighbouring lanes = consecutive
+// rows, one half) touch distinct banks, with 32 or with 64 four-byte banks.
+__device__ __forceinline__ int slot16(int row, int half) {
+  return row * 32 + 16 * (half ^ (((row >> 2) ^ (row >> 3)) & 1));
+}
+__device__ __forceinline__ int slot8(int row, int half) {
+  return row * 16 + 8 * (half ^ (((row >> 3) ^ (row >> 4)) & 1));
 }
 
 // Launch index -> output tile: contiguous ranges per XCD (blocks are dealt
@@ -119,15 +133,17 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
   const int mrows = min(BM, M - m0), nrows = min(BN, N - n0);
   const int G = K >> 6;
   const int NS = (G + KC - 1) / KC;
-  const uint32_t row_bytes = (uint32_t)G * GB;
 
-  // ---- staging assignment: thread -> (row tid/2, half tid%2) of both code tiles;
-  // rows past the edge re-read the tile's last valid row (their outputs are never stored)
+  // ---- staging assignment: thread -> (row tid/2, half tid%2) of both code tiles (a row's
+  // 48 bytes come from two neighbouring lanes); rows past the edge re-read the tile's last
+  // valid row (their outputs are never stored)
   const int srow = tid >> 1, shalf = tid & 1;
-  const rsrc_t rx = make_rsrc(xq + (size_t)m0 * row_bytes, (size_t)mrows * row_bytes);
-  const rsrc_t rw = make_rsrc(wq + (size_t)n0 * row_bytes, (size_t)nrows * row_bytes);
-  const uint32_t vx = (uint32_t)min(srow, mrows - 1) * row_bytes + 24u * shalf;
-  const uint32_t vw = (uint32_t)min(srow, nrows - 1) * row_bytes + 24u * shalf;
+  // codes are group-major [G][rows][48]: a tile's rows of one group are contiguous
+  const rsrc_t rx = make_rsrc(xq + (size_t)m0 * GB, ((size_t)(G - 1) * M + mrows) * GB);
+  const rsrc_t rw = make_rsrc(wq + (size_t)n0 * GB, ((size_t)(G - 1) * N + nrows) * GB);
+  const uint32_t vx = (uint32_t)min(srow, mrows - 1) * GB + 24u * shalf;
+  const uint32_t vw = (uint32_t)min(srow, nrows - 1) * GB + 24u * shalf;
+  const uint32_t gx_step = (uint32_t)M * GB, gw_step = (uint32_t)N * GB;   // bytes between groups
   // scales (group-major [G, rows]): waves 0-1 stage sx of rows m0 + tid, waves 2-3 sw of
   // columns n0 + tid - 128
   const bool s_x = wave < 2;
@@ -137,41 +153,41 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
                               ((size_t)(G - 1) * s_stride + s_rows) * 2);
   const uint32_t vs = (uint32_t)min(tid & 127, s_rows - 1) * 2;
 
-  uint4 xlo[KC], wlo[KC];
-  uint2 xhi[KC], whi[KC];
-  uint32_t sv[KC];
-  auto load_stage = [&](int st) {
+  // two register slots of staged global data: stage s+1 and s+2 are in flight while LDS
+  // holds stage s
+  uint4 xlo[2][KC], wlo[2][KC];
+  uint2 xhi[2][KC], whi[2][KC];
+  uint32_t sv[2][KC];
+  auto load_stage = [&](int st, int slot) {
 #pragma unroll
     for (int k = 0; k < KC; k++) {
       const int g = min(st * KC + k, G - 1);   // a group past the end re-reads the last one (unused)
-      const uint32_t so = (uint32_t)g * GB;
-      xlo[k] = ld16(rx, vx, so);
-      xhi[k] = ld8(rx, vx + 16, so);
-      wlo[k] = ld16(rw, vw, so);
-      whi[k] = ld8(rw, vw + 16, so);
-      sv[k] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)vs, (int)((uint32_t)g * s_stride * 2), 0);
+      const uint32_t sox = (uint32_t)g * gx_step, sow = (uint32_t)g * gw_step;
+      xlo[slot][k] = ld16(rx, vx, sox);
+      xhi[slot][k] = ld8(rx, vx + 16, sox);
+      wlo[slot][k] = ld16(rw, vw, sow);
+      whi[slot][k] = ld8(rw, vw + 16, sow);
+      sv[slot][k] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)vs, (int)((uint32_t)g * s_stride * 2), 0);
     }
   };
-  const int w_p0 = (shalf * 128 + srow) * 16, w_p1 = (shalf * 128 + srow) * 8;
-  const int w_s = tid * 16;   // slot of X row tid (waves 0-1) or W row tid - 128 (waves 2-3)
-  auto store_stage = [&](int buf) {
+  const int w_p0 = slot16(srow, shalf), w_p1 = slot8(srow, shalf);
+  const int w_s = tid * 8;    // slot of X row tid (waves 0-1) or W row tid - 128 (waves 2-3)
+  auto store_stage = [&](int buf, int slot) {
 #pragma unroll
     for (int k = 0; k < KC; k++) {
       uint8_t* b = lds + buf * STAGE + k * GROUP;
-      *reinterpret_cast<uint4*>(b + L_XP0 + w_p0) = xlo[k];
-      *reinterpret_cast<uint2*>(b + L_XP1 + w_p1) = xhi[k];
-      *reinterpret_cast<uint4*>(b + L_WP0 + w_p0) = wlo[k];
-      *reinterpret_cast<uint2*>(b + L_WP1 + w_p1) = whi[k];
-      *reinterpret_cast<uint32_t*>(b + L_S + w_s) = sv[k];   // high half 0 = K slot 1
+      *reinterpret_cast<uint4*>(b + L_XP0 + w_p0) = xlo[slot][k];
+      *reinterpret_cast<uint2*>(b + L_XP1 + w_p1) = xhi[slot][k];
+      *reinterpret_cast<uint4*>(b + L_WP0 + w_p0) = wlo[slot][k];
+      *reinterpret_cast<uint2*>(b + L_WP1 + w_p1) = whi[slot][k];
+      *reinterpret_cast<uint2*>(b + L_S + w_s) = make_uint2(sv[slot][k], 0u);   // K slots 0..3: s, 0, 0, 0
     }
   };
 
-  // dwords 1..3 of every scale slot (K slots 2..7 for the lower-K-half lanes, 0..3 for the
-  // upper half), written once
+  // the zero bytes read by the upper-K-half lanes, written once
+  if (tid < 32) {
 #pragma unroll
-  for (int b = 0; b < 2 * KC; b++) {
-    *reinterpret_cast<uint32_t*>(lds + b * GROUP + L_S + tid * 16 + 4) = 0u;
-    *reinterpret_cast<uint2*>(lds + b * GROUP + L_S + tid * 16 + 8) = make_uint2(0u, 0u);
+    for (int b = 0; b < 2 * KC; b++) *reinterpret_cast<uint2*>(lds + b * GROUP + L_Z + tid * 8) = make_uint2(0u, 0u);
   }
 
   v16f acc[2][2];   // [tj][ti]: lane -> row m = ti*32 + r32, reg v -> column 8(v/4) + 4h + v%4 of tile tj
@@ -186,70 +202,90 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
   int rx_p0[2], rx_p1[2], rw_p0[2], rw_p1[2], rs_x[2], rs_w[2];
 #pragma unroll
   for (int i = 0; i < 2; i++) {
-    rx_p0[i] = (h * 128 + wm * 64 + i * 32 + r32) * 16;
-    rw_p0[i] = (h * 128 + wn * 64 + i * 32 + r32) * 16;
-    rx_p1[i] = opaque((h * 128 + wm * 64 + i * 32 + r32) * 8);
-    rw_p1[i] = opaque((h * 128 + wn * 64 + i * 32 + r32) * 8);
-    rs_x[i] = opaque((wm * 64 + i * 32 + r32) * 16 + 8 * h);
-    rs_w[i] = opaque((128 + wn * 64 + i * 32 + r32) * 16 + 8 * h);
+    rx_p0[i] = slot16(wm * 64 + i * 32 + r32, h);
+    rw_p0[i] = slot16(wn * 64 + i * 32 + r32, h);
+    rx_p1[i] = opaque(slot8(wm * 64 + i * 32 + r32, h));
+    rw_p1[i] = opaque(slot8(wn * 64 + i * 32 + r32, h));
+    rs_x[i] = opaque(h ? L_Z - L_S + r32 * 8 : (wm * 64 + i * 32 + r32) * 8);
+    rs_w[i] = opaque(h ? L_Z - L_S + r32 * 8 : (128 + wn * 64 + i * 32 + r32) * 8);
   }
-  // scale operands: only element 0 (K slot 0/1 pair) is reloaded; the rest stays zero
-  uint4 sxo[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-  uint4 swo[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-  v8i xo[2], wo[2];
+  // MFMA operands of one group.  Scale operands: only the first two dwords are reloaded,
+  // the rest stays zero; code operands: dwords 6 and 7 are not read by the FP6 MFMA.
+  struct Ops {
+    v8i xo[2], wo[2];
+    uint4 sxo[2], swo[2];
+  };
+  Ops ops;
 #pragma unroll
-  for (int i = 0; i < 2; i++)
+  for (int i = 0; i < 2; i++) {
 #pragma unroll
-    for (int e = 0; e < 8; e++) { xo[i][e] = 0; wo[i][e] = 0; }
+    for (int e = 0; e < 8; e++) { ops.xo[i][e] = 0; ops.wo[i][e] = 0; }
+    ops.sxo[i] = make_uint4(0, 0, 0, 0);
+    ops.swo[i] = make_uint4(0, 0, 0, 0);
+  }
 
-  auto compute_group = [&](const uint8_t* b) {
+  auto read_ops = [&](const uint8_t* b, Ops& o) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
       const uint4 x0 = *reinterpret_cast<const uint4*>(b + L_XP0 + rx_p0[i]);
       const uint2 x1 = *reinterpret_cast<const uint2*>(b + L_XP1 + rx_p1[i]);
       const uint4 w0 = *reinterpret_cast<const uint4*>(b + L_WP0 + rw_p0[i]);
       const uint2 w1 = *reinterpret_cast<const uint2*>(b + L_WP1 + rw_p1[i]);
-      xo[i][0] = (int)x0.x; xo[i][1] = (int)x0.y; xo[i][2] = (int)x0.z; xo[i][3] = (int)x0.w;
-      xo[i][4] = (int)x1.x; xo[i][5] = (int)x1.y;
-      wo[i][0] = (int)w0.x; wo[i][1] = (int)w0.y; wo[i][2] = (int)w0.z; wo[i][3] = (int)w0.w;
-      wo[i][4] = (int)w1.x; wo[i][5] = (int)w1.y;
+      o.xo[i][0] = (int)x0.x; o.xo[i][1] = (int)x0.y; o.xo[i][2] = (int)x0.z; o.xo[i][3] = (int)x0.w;
+      o.xo[i][4] = (int)x1.x; o.xo[i][5] = (int)x1.y;
+      o.wo[i][0] = (int)w0.x; o.wo[i][1] = (int)w0.y; o.wo[i][2] = (int)w0.z; o.wo[i][3] = (int)w0.w;
+      o.wo[i][4] = (int)w1.x; o.wo[i][5] = (int)w1.y;
       const uint2 sxv = *reinterpret_cast<const uint2*>(b + L_S + rs_x[i]);
       const uint2 swv = *reinterpret_cast<const uint2*>(b + L_S + rs_w[i]);
-      sxo[i].x = sxv.x; sxo[i].y = sxv.y;
-      swo[i].x = swv.x; swo[i].y = swv.y;
+      o.sxo[i].x = sxv.x; o.sxo[i].y = sxv.y;
+      o.swo[i].x = swv.x; o.swo[i].y = swv.y;
     }
+  };
+  auto mma_ops = [&](const Ops& o) {
 #pragma unroll
     for (int tj = 0; tj < 2; tj++)
 #pragma unroll
       for (int ti = 0; ti < 2; ti++) {
-        const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wo[tj], xo[ti], v16f{}, 2, 2, 0, 127, 0, 127);
-        const v16f sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(swo[tj]), as_h8(sxo[ti]), v16f{}, 0, 0, 0);
+        const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.wo[tj], o.xo[ti], v16f{}, 2, 2, 0, 127, 0, 127);
+        const v16f sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(o.swo[tj]), as_h8(o.sxo[ti]), v16f{}, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 16; i++) acc[tj][ti][i] = __builtin_fmaf(p[i], sc[i], acc[tj][ti][i]);
       }
   };
 
-  load_stage(0);
-  store_stage(0);
-  if (NS > 1) load_stage(1);
+  // stage s lives in LDS buffer s % 2 and, before that, in register slot s % 2
+  // (the scheduling barriers keep each stage's loads together: the wait counts inside the
+  // loop follow the issue order on every path into it)
+  load_stage(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_stage(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  store_stage(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_stage(2, 0);
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
+  // The global loads are issued unconditionally (a stage past the end re-reads the last
+  // group): loads under a branch would make the wait-count analysis wait for every load.
   auto step = [&](int st, int buf) {
+    if (st < NS) {
 #pragma unroll
-    for (int k = 0; k < KC; k++) {
-      if (st * KC + k < G) compute_group(lds + buf * STAGE + k * GROUP);
+      for (int k = 0; k < KC; k++)
+        if (st * KC + k < G) {
+          read_ops(lds + buf * STAGE + k * GROUP, ops);
+          mma_ops(ops);
+        }
     }
     // keep the next stage's LDS writes (and their wait on the global loads) after this compute
     __builtin_amdgcn_sched_barrier(0);
-    if (st + 1 < NS) {
-      store_stage(buf ^ 1);
-      if (st + 2 < NS) load_stage(st + 2);
-    }
+    if (st + 1 < NS) store_stage(buf ^ 1, buf ^ 1);
+    load_stage(st + 3, buf ^ 1);
     __syncthreads();
   };
   for (int st = 0; st < NS; st += 2) {
     step(st, 0);
-    if (st + 1 < NS) step(st + 1, 1);
+    step(st + 1, 1);
   }
 
   // ---- epilogue.  The ring is free (every wave passed the last barrier).
@@ -267,7 +303,7 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
     constexpr int LS2 = (R + 8) * 2;
     static_assert(BN * LS2 <= E_Y, "L2 staging overlaps the output staging");
     for (int idx = tid; idx < R * (BN / 8); idx += NT) {
-      const int k = idx / (BN / 8), c8 = idx % (BN / 8);
+      const int k = idx % R, c8 = idx / R;   // neighbouring lanes write neighbouring k
       const int n = n0 + c8 * 8;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (n < N) v = *reinterpret_cast<const uint4*>(l2 + (size_t)k * N + n);

@@ -56,7 +56,9 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
   constexpr int CB = FMT == FMT_INT4_E2M3 ? 48 : (FMT == FMT_INT8 ? 64 : 32);   // code bytes per row per chunk
   __shared__ __attribute__((aligned(16))) uint8_t cstage[NW][16 * CB];
   uint8_t* slot = cstage[wave];
-  const size_t code_row = FMT == FMT_INT4_E2M3 ? (size_t)(K >> 6) * 48 : (FMT == FMT_INT8 ? (size_t)K : (size_t)(K >> 1));
+  // row-major codes [M, K * bits / 8]; the 6-bit container is group-major [K/64][M][48]
+  const size_t code_row = FMT == FMT_INT4_E2M3 ? (size_t)48 : (FMT == FMT_INT8 ? (size_t)K : (size_t)(K >> 1));
+  const size_t code_chunk = FMT == FMT_INT4_E2M3 ? (size_t)M * 48 : (size_t)CB;   // bytes between chunks
 
   for (int c0 = wave; c0 < nchunks; c0 += NW * NB) {
     uint4 xv[NB][2];
@@ -159,7 +161,7 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
           const int rr = lane / (CB / 16), part = lane % (CB / 16);
           const int mm = blockIdx.x * 16 + rr;
           const uint4 v16 = *reinterpret_cast<const uint4*>(slot + rr * CB + part * 16);
-          if (mm < M) *reinterpret_cast<uint4*>(xq + (size_t)mm * code_row + (size_t)c * CB + part * 16) = v16;
+          if (mm < M) *reinterpret_cast<uint4*>(xq + (size_t)mm * code_row + (size_t)c * code_chunk + part * 16) = v16;
         }
         __builtin_amdgcn_wave_barrier();
         if (valid) {

@@ -37,7 +37,7 @@ k_quant_weight(const float* __restrict__ r_t, int N, int K, uint8_t* __restrict_
 #pragma unroll
     for (int e = 0; e < G; e++) q[e] = int_code(v[e], s, qmax);
     if (FMT == FMT_INT4_E2M3) {
-      // 48 bytes per group: two halves of 32 six-bit fields
+      // 48 bytes per (group, column): two halves of 32 six-bit fields
       uint32_t wv[12];
 #pragma unroll
       for (int hh = 0; hh < 2; hh++) {
@@ -52,7 +52,7 @@ k_quant_weight(const float* __restrict__ r_t, int N, int K, uint8_t* __restrict_
         wv[6 * hh + 4] = (uint32_t)(f[2] >> 32) | (uint32_t)(f[3] << 16);
         wv[6 * hh + 5] = (uint32_t)(f[3] >> 16);
       }
-      uint4* dst = reinterpret_cast<uint4*>(wq + (size_t)n * (size_t)gpr * 48 + (size_t)g * 48);
+      uint4* dst = reinterpret_cast<uint4*>(wq + ((size_t)g * N + n) * 48);   // group-major [K/64][N][48]
       dst[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
       dst[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
       dst[2] = make_uint4(wv[8], wv[9], wv[10], wv[11]);

@@ -51,11 +51,13 @@
  *  SVDQ_INT4_G64_E2M3 : the SVDQ_INT4_G64 codes and scales, bit for bit, in the
  *                  storage the gfx950 FP6 matrix cores read directly: each code
  *                  q becomes the 6-bit E2M3 pattern of q/8 (a subnormal:
- *                  sign<<5 | |q|).  A row has 48 bytes per group of 64; bytes
- *                  [48g, 48g+24) hold codes 0..31 of group g and [48g+24, 48g+48)
+ *                  sign<<5 | |q|).  A row takes 48 bytes per group of 64:
+ *                  bytes [0, 24) hold codes 0..31 of the group and [24, 48)
  *                  codes 32..63, code j of a half in bits [6j, 6j+6) of the
- *                  little-endian 24 bytes.  Code rows are 3K/4 bytes.  Scales
- *                  are fp16 and group-major: [K/64, rows].  The 4-bit values
+ *                  little-endian 24 bytes.  Codes and scales are group-major:
+ *                  codes [K/64][rows][48 bytes] (the group-g slice of row i at
+ *                  byte (g * rows + i) * 48; 3K/4 bytes per row in total),
+ *                  fp16 scales [K/64][rows].  The 4-bit values
  *                  sit in a 6-bit container (1.5x the bytes of SVDQ_INT4_G64)
  *                  so that the GEMM runs on FP6 MFMA at twice the INT8 rate
  *                  with fp32 partials.
@@ -88,9 +90,10 @@ typedef enum {
   SVDQ_INT4_G64_E2M3 = 3
 } svdq_format;
 
-/* Bytes of one row of codes for K columns (K/2 for 4-bit formats, K for INT8,
- * 3K/4 for the E2M3 container), and bytes of scales per row (K/64 fp16 for the
- * INT formats, K/16 E4M3 bytes for FP4).  Returns 0 for a bad format. */
+/* Bytes of codes per row for K columns (K/2 for 4-bit formats, K for INT8,
+ * 3K/4 for the E2M3 container, whose rows are interleaved group by group), and
+ * bytes of scales per row (K/64 fp16 for the INT formats, K/16 E4M3 bytes for
+ * FP4).  Returns 0 for a bad format. */
 size_t svdq_code_row_bytes(int K, svdq_format fmt);
 size_t svdq_scale_row_bytes(int K, svdq_format fmt);
 

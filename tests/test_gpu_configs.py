@@ -43,6 +43,15 @@ def same_bytes(a, b):
     return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
+def dev_codes(stored, fmt):
+    """Codes in the device layout of the format: the E2M3 container is group-major
+    [K/64][rows][48]; the oracle stores it row by row."""
+    if fmt != "int4_e2m3":
+        return stored
+    rows = stored.shape[0]
+    return np.ascontiguousarray(stored.reshape(rows, -1, 48).transpose(1, 0, 2))
+
+
 def dev_scales(s, fmt):
     return np.ascontiguousarray(s.T) if fmt == "int4_e2m3" else s
 
@@ -62,10 +71,10 @@ def run_layer(P, fmt, x_hat=None, check_codes=True):
     gb = dev(P.bias)
     wq, ws = binding.svdq_quantize_weight(dev(P.res.T), fmt)
     if check_codes:
-        assert same_bytes(host(wq), ref["wstored"]), "weight codes"
+        assert same_bytes(host(wq), dev_codes(ref["wstored"], fmt)), "weight codes"
         assert same_bytes(host(ws), dev_scales(ref["ws"], fmt)), "weight scales"
         xq, xs, t = binding.svdq_quantize_down(gx, gl1t, fmt)
-        assert same_bytes(host(xq), ref["xstored"]), "activation codes"
+        assert same_bytes(host(xq), dev_codes(ref["xstored"], fmt)), "activation codes"
         assert same_bytes(host(xs), dev_scales(ref["xs"], fmt)), "activation scales"
         if r:
             tg = host(t)

@@ -42,6 +42,15 @@ def same_bytes(a, b):
     return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
+def dev_codes(stored, fmt):
+    """Codes in the device layout of the format: the E2M3 container is group-major
+    [K/64][rows][48]; the oracle stores it row by row."""
+    if fmt != "int4_e2m3":
+        return stored
+    rows = stored.shape[0]
+    return np.ascontiguousarray(stored.reshape(rows, -1, 48).transpose(1, 0, 2))
+
+
 def dev_scales(s, fmt):
     """Scales in the device layout of the format (group-major for the E2M3 container)."""
     return np.ascontiguousarray(s.T) if fmt == "int4_e2m3" else s
@@ -76,7 +85,7 @@ def test_quantize_down_parity(fmt, M, K, N, r):
     x_hat, _, l1, _, _ = draw(M * 7 + K + r, M, K, 16, r)
     q, s, stored = oracle.quant.quantize(x_hat, fmt)
     xq, xs, t = binding.svdq_quantize_down(dev(x_hat), dev(l1.T) if r else None, fmt)
-    assert same_bytes(host(xq), stored)
+    assert same_bytes(host(xq), dev_codes(stored, fmt))
     assert same_bytes(host(xs), dev_scales(s, fmt))
     if r:
         tr = oracle.forward.down_projection(x_hat, l1)
@@ -94,7 +103,7 @@ def test_quantize_weight_parity(fmt, N, K):
     r_t = (g.standard_normal((N, K)) * 10.0 ** g.integers(-4, 1, (N, 1))).astype(np.float32)
     q, s, stored = oracle.quant.quantize(r_t, fmt)
     wq, ws = binding.svdq_quantize_weight(dev(r_t), fmt)
-    assert same_bytes(host(wq), stored)
+    assert same_bytes(host(wq), dev_codes(stored, fmt))
     assert same_bytes(host(ws), dev_scales(s, fmt))
 
 
@@ -106,11 +115,11 @@ def test_quantizers_subnormal_scales_and_zero_groups():
     for fmt in FMTS:
         q, s, stored = oracle.quant.quantize(x, fmt)
         xq, xs, _ = binding.svdq_quantize_down(dev(x), None, fmt)
-        assert same_bytes(host(xq), stored), fmt
+        assert same_bytes(host(xq), dev_codes(stored, fmt)), fmt
         assert same_bytes(host(xs), dev_scales(s, fmt)), fmt
         wq, ws = binding.svdq_quantize_weight(dev(x.astype(np.float32)[:, :].repeat(16, axis=0)[:80]), fmt)
         q2, s2, st2 = oracle.quant.quantize(x.astype(np.float32).repeat(16, axis=0)[:80], fmt)
-        assert same_bytes(host(wq), st2), fmt
+        assert same_bytes(host(wq), dev_codes(st2, fmt)), fmt
         assert same_bytes(host(ws), dev_scales(s2, fmt)), fmt
 
 
@@ -130,7 +139,7 @@ def test_gemm_up_parity(fmt, M, K, N, r, with_bias):
     x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs(fmt, M, K, N, r, M + N + K + r)
     bias = b if with_bias else None
     ref = oracle.forward.linear(xq, xs, t, wq, ws, l2, bias, fmt)
-    y = binding.svdq_gemm_w4a4_up(dev(xst), dev(dev_scales(xs, fmt)), dev(t) if r else None, dev(wst),
+    y = binding.svdq_gemm_w4a4_up(dev(dev_codes(xst, fmt)), dev(dev_scales(xs, fmt)), dev(t) if r else None, dev(dev_codes(wst, fmt)),
                                   dev(dev_scales(ws, fmt)), dev(l2) if r else None,
                                   dev(bias) if with_bias else None, K, fmt)
     yg = host(y)
@@ -183,13 +192,13 @@ def test_unfused_matches_fused(fmt):
     x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs(fmt, M, K, N, r, 5)
     ref = oracle.forward.linear(xq, xs, t, wq, ws, l2, b, fmt)
     ws_d = dev(dev_scales(ws, fmt))
-    args = (dev(x_hat), dev(l1.T), dev(wst), ws_d, dev(l2), dev(b), fmt)
+    args = (dev(x_hat), dev(l1.T), dev(dev_codes(wst, fmt)), ws_d, dev(l2), dev(b), fmt)
     yu = host(binding.svdq_linear_unfused(*args))
     yf = host(binding.svdq_linear(*args))
     assert rel_fro(yu, ref) <= TOL
     assert rel_fro(yu, yf) <= TOL
     # r = 0: the unfused path is the bare GEMM
-    y0 = host(binding.svdq_linear_unfused(dev(x_hat), None, dev(wst), ws_d, None, dev(b), fmt))
+    y0 = host(binding.svdq_linear_unfused(dev(x_hat), None, dev(dev_codes(wst, fmt)), ws_d, None, dev(b), fmt))
     ref0 = oracle.forward.linear(xq, xs, np.zeros((M, 0), np.float16), wq, ws, np.zeros((0, N), np.float16), b, fmt)
     assert rel_fro(y0, ref0) <= TOL
 
@@ -225,7 +234,7 @@ def test_gelu_smooth_parity(M, C):
 def test_repeat_runs_are_bitwise_identical(fmt):
     M, K, N, r = 257, 256, 144, 32
     x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs(fmt, M, K, N, r, 11)
-    args = (dev(x_hat), dev(l1.T), dev(wst), dev(dev_scales(ws, fmt)), dev(l2), dev(b), fmt)
+    args = (dev(x_hat), dev(l1.T), dev(dev_codes(wst, fmt)), dev(dev_scales(ws, fmt)), dev(l2), dev(b), fmt)
     first = host(binding.svdq_linear(*args))
     for _ in range(9):
         assert np.array_equal(host(binding.svdq_linear(*args)).view(np.uint16), first.view(np.uint16))
@@ -244,16 +253,16 @@ def test_outputs_stay_inside_their_buffers(fmt):
         return buf, view
 
     cb = binding.code_row_bytes(K, fmt)
-    bq, gq = guarded(M * cb, torch.uint8, (M, cb))
+    bq, gq = guarded(M * cb, torch.uint8, binding.code_shape(M, K, fmt))
     bs, gs = guarded(M * K // 64 * 2, torch.float16, binding.scale_shape(M, K, fmt))
     bt, gt = guarded(M * r * 2, torch.float16, (M, r))
     binding.svdq_quantize_down(dev(x_hat), dev(l1.T), fmt, xq=gq, xs=gs, t=gt)
     by, gy = guarded(M * N * 2, torch.float16, (M, N))
-    binding.svdq_gemm_w4a4_up(gq, gs, gt, dev(wst), dev(dev_scales(ws, fmt)), dev(l2), dev(b), K, fmt, y=gy)
+    binding.svdq_gemm_w4a4_up(gq, gs, gt, dev(dev_codes(wst, fmt)), dev(dev_scales(ws, fmt)), dev(l2), dev(b), K, fmt, y=gy)
     for buf in (bq, bs, bt, by):
         h = host(buf)
         assert (h[:guard] == canary).all() and (h[-guard:] == canary).all()
-    assert same_bytes(host(gq), xst)
+    assert same_bytes(host(gq), dev_codes(xst, fmt))
 
 
 def test_empty_inputs_are_no_ops():
