@@ -26,8 +26,10 @@
 // stages of two groups.  Global -> LDS staging goes through registers: buffer
 // loads whose per-group offset is a scalar, so the address arithmetic costs no
 // vector instructions; while the waves compute stage s from LDS, stage s+1 is
-// written to the other LDS buffer and the loads of stages s+2 and s+3 are in
-// flight in two register slots (two stages of compute cover their latency).
+// written to the other LDS buffer and the loads of stage s+2 are in flight.
+// The grid is persistent (two workgroups per CU, each looping over tiles): the
+// last step of a tile already loads the next tile's first stage, so the next
+// tile's start overlaps this tile's epilogue and its stores.
 // LDS keeps, per group and operand, bytes 0..15 of each (row, half) in one
 // 16-byte slot and bytes 16..23 in one 8-byte slot (the slot order swizzled
 // against bank conflicts), so every MFMA operand is
@@ -127,76 +129,70 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
   const int h = lane >> 5, r32 = lane & 31;
   const int wm = wave >> 1, wn = wave & 1;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int tm, tn;
-  tile_of3(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int mrows = min(BM, M - m0), nrows = min(BN, N - n0);
+  const int tiles = tiles_m * tiles_n;
   const int G = K >> 6;
-  const int NS = (G + KC - 1) / KC;
+  const int NS = (G + KC - 1) / KC;          // stages of a tile
+  const int NSE = (NS + 1) & ~1;             // rounded up to even (the loop takes two per pass)
+  const uint32_t gx_step = (uint32_t)M * GB, gw_step = (uint32_t)N * GB;   // bytes between groups
 
   // ---- staging assignment: thread -> (row tid/2, half tid%2) of both code tiles (a row's
   // 48 bytes come from two neighbouring lanes); rows past the edge re-read the tile's last
-  // valid row (their outputs are never stored)
+  // valid row (their outputs are never stored).  Scales (group-major [G, rows]): waves 0-1
+  // stage sx of rows m0 + tid, waves 2-3 sw of columns n0 + tid - 128.
   const int srow = tid >> 1, shalf = tid & 1;
-  // codes are group-major [G][rows][48]: a tile's rows of one group are contiguous
-  const rsrc_t rx = make_rsrc(xq + (size_t)m0 * GB, ((size_t)(G - 1) * M + mrows) * GB);
-  const rsrc_t rw = make_rsrc(wq + (size_t)n0 * GB, ((size_t)(G - 1) * N + nrows) * GB);
-  const uint32_t vx = (uint32_t)min(srow, mrows - 1) * GB + 24u * shalf;
-  const uint32_t vw = (uint32_t)min(srow, nrows - 1) * GB + 24u * shalf;
-  const uint32_t gx_step = (uint32_t)M * GB, gw_step = (uint32_t)N * GB;   // bytes between groups
-  // scales (group-major [G, rows]): waves 0-1 stage sx of rows m0 + tid, waves 2-3 sw of
-  // columns n0 + tid - 128
   const bool s_x = wave < 2;
-  const int s_rows = s_x ? mrows : nrows;
   const int s_stride = s_x ? M : N;
-  const rsrc_t rs = make_rsrc(s_x ? (const void*)(xs + m0) : (const void*)(ws + n0),
-                              ((size_t)(G - 1) * s_stride + s_rows) * 2);
-  const uint32_t vs = (uint32_t)min(tid & 127, s_rows - 1) * 2;
+  struct Src {                               // where one tile's operands are read from
+    rsrc_t rx, rw, rs;
+    uint32_t vx, vw, vs;
+  };
+  auto tile_src = [&](int tile) {
+    int tm_, tn_;
+    tile_of3(tile, tiles, tiles_m, tiles_n, &tm_, &tn_);
+    const int m0_ = tm_ * BM, n0_ = tn_ * BN;
+    const int mr = min(BM, M - m0_), nr = min(BN, N - n0_);
+    const int sr = s_x ? mr : nr;
+    Src r;
+    // codes are group-major [G][rows][48]: a tile's rows of one group are contiguous
+    r.rx = make_rsrc(xq + (size_t)m0_ * GB, ((size_t)(G - 1) * M + mr) * GB);
+    r.rw = make_rsrc(wq + (size_t)n0_ * GB, ((size_t)(G - 1) * N + nr) * GB);
+    r.rs = make_rsrc(s_x ? (const void*)(xs + m0_) : (const void*)(ws + n0_), ((size_t)(G - 1) * s_stride + sr) * 2);
+    r.vx = (uint32_t)min(srow, mr - 1) * GB + 24u * shalf;
+    r.vw = (uint32_t)min(srow, nr - 1) * GB + 24u * shalf;
+    r.vs = (uint32_t)min(tid & 127, sr - 1) * 2;
+    return r;
+  };
 
-  // two register slots of staged global data: stage s+1 and s+2 are in flight while LDS
-  // holds stage s
-  uint4 xlo[2][KC], wlo[2][KC];
-  uint2 xhi[2][KC], whi[2][KC];
-  uint32_t sv[2][KC];
-  auto load_stage = [&](int st, int slot) {
+  // one register slot of staged global data; stage s of a tile goes through LDS buffer s % 2
+  uint4 xlo[KC], wlo[KC];
+  uint2 xhi[KC], whi[KC];
+  uint32_t sv[KC];
+  auto load_stage = [&](const Src& src, int st) {
 #pragma unroll
     for (int k = 0; k < KC; k++) {
       const int g = min(st * KC + k, G - 1);   // a group past the end re-reads the last one (unused)
       const uint32_t sox = (uint32_t)g * gx_step, sow = (uint32_t)g * gw_step;
-      xlo[slot][k] = ld16(rx, vx, sox);
-      xhi[slot][k] = ld8(rx, vx + 16, sox);
-      wlo[slot][k] = ld16(rw, vw, sow);
-      whi[slot][k] = ld8(rw, vw + 16, sow);
-      sv[slot][k] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)vs, (int)((uint32_t)g * s_stride * 2), 0);
+      xlo[k] = ld16(src.rx, src.vx, sox);
+      xhi[k] = ld8(src.rx, src.vx + 16, sox);
+      wlo[k] = ld16(src.rw, src.vw, sow);
+      whi[k] = ld8(src.rw, src.vw + 16, sow);
+      sv[k] = __builtin_amdgcn_raw_buffer_load_b16(src.rs, (int)src.vs, (int)((uint32_t)g * s_stride * 2), 0);
     }
   };
   const int w_p0 = slot16(srow, shalf), w_p1 = slot8(srow, shalf);
   const int w_s = tid * 8;    // slot of X row tid (waves 0-1) or W row tid - 128 (waves 2-3)
-  auto store_stage = [&](int buf, int slot) {
+  auto store_stage = [&](int buf) {
 #pragma unroll
     for (int k = 0; k < KC; k++) {
       uint8_t* b = lds + buf * STAGE + k * GROUP;
-      *reinterpret_cast<uint4*>(b + L_XP0 + w_p0) = xlo[slot][k];
-      *reinterpret_cast<uint2*>(b + L_XP1 + w_p1) = xhi[slot][k];
-      *reinterpret_cast<uint4*>(b + L_WP0 + w_p0) = wlo[slot][k];
-      *reinterpret_cast<uint2*>(b + L_WP1 + w_p1) = whi[slot][k];
-      *reinterpret_cast<uint2*>(b + L_S + w_s) = make_uint2(sv[slot][k], 0u);   // K slots 0..3: s, 0, 0, 0
+      *reinterpret_cast<uint4*>(b + L_XP0 + w_p0) = xlo[k];
+      *reinterpret_cast<uint2*>(b + L_XP1 + w_p1) = xhi[k];
+      *reinterpret_cast<uint4*>(b + L_WP0 + w_p0) = wlo[k];
+      *reinterpret_cast<uint2*>(b + L_WP1 + w_p1) = whi[k];
+      *reinterpret_cast<uint2*>(b + L_S + w_s) = make_uint2(sv[k], 0u);   // K slots 0..3: s, 0, 0, 0
     }
   };
 
-  // the zero bytes read by the upper-K-half lanes, written once
-  if (tid < 32) {
-#pragma unroll
-    for (int b = 0; b < 2 * KC; b++) *reinterpret_cast<uint2*>(lds + b * GROUP + L_Z + tid * 8) = make_uint2(0u, 0u);
-  }
-
-  v16f acc[2][2];   // [tj][ti]: lane -> row m = ti*32 + r32, reg v -> column 8(v/4) + 4h + v%4 of tile tj
-#pragma unroll
-  for (int a = 0; a < 2; a++)
-#pragma unroll
-    for (int b = 0; b < 2; b++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
 
   // per-lane LDS read bases (tile offsets and stage offsets are immediates)
   int rx_p0[2], rx_p1[2], rw_p0[2], rw_p1[2], rs_x[2], rs_w[2];
@@ -223,6 +219,7 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
     ops.sxo[i] = make_uint4(0, 0, 0, 0);
     ops.swo[i] = make_uint4(0, 0, 0, 0);
   }
+  v16f acc[2][2];   // [tj][ti]: lane -> row m = ti*32 + r32, reg v -> column 8(v/4) + 4h + v%4 of tile tj
 
   auto read_ops = [&](const uint8_t* b, Ops& o) {
 #pragma unroll
@@ -253,130 +250,181 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
       }
   };
 
-  // stage s lives in LDS buffer s % 2 and, before that, in register slot s % 2
-  // (the scheduling barriers keep each stage's loads together: the wait counts inside the
-  // loop follow the issue order on every path into it)
-  load_stage(0, 0);
+  // ---- persistent loop over tiles: tile, tile + gridDim.x, ...  The stages of a tile run
+  // through the register slot and two LDS buffers; during its last step the loads already
+  // fetch the next tile's stage 0, so that the next tile's start overlaps this tile's
+  // epilogue.  The global loads inside the stage loop are unconditional (a stage
+  // past the end re-reads the last group): loads under a branch would make the wait-count
+  // analysis wait for every load; the scheduling barriers keep each stage's loads together
+  // for the same reason.
+  int tile = blockIdx.x;
+  Src ld = tile_src(tile);                   // the tile whose stages are being fetched
+  load_stage(ld, 0);
   __builtin_amdgcn_sched_barrier(0);
-  load_stage(1, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  store_stage(0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  load_stage(2, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();
+  while (true) {
+    const int next = tile + (int)gridDim.x;
+    const bool has_next = next < tiles;
+    const Src nxt = tile_src(has_next ? next : tile);
+    int tm, tn;
+    tile_of3(tile, tiles, tiles_m, tiles_n, &tm, &tn);
+    const int m0 = tm * BM, n0 = tn * BN;
 
-  // The global loads are issued unconditionally (a stage past the end re-reads the last
-  // group): loads under a branch would make the wait-count analysis wait for every load.
-  auto step = [&](int st, int buf) {
-    if (st < NS) {
+    // the zero bytes read by the upper-K-half lanes (the previous epilogue used the ring)
+    if (tid < 32) {
 #pragma unroll
-      for (int k = 0; k < KC; k++)
-        if (st * KC + k < G) {
-          read_ops(lds + buf * STAGE + k * GROUP, ops);
-          mma_ops(ops);
-        }
+      for (int b = 0; b < 2 * KC; b++) *reinterpret_cast<uint2*>(lds + b * GROUP + L_Z + tid * 8) = make_uint2(0u, 0u);
     }
-    // keep the next stage's LDS writes (and their wait on the global loads) after this compute
+    // stage 0 -> LDS buffer 0, stage 1 in flight
+    store_stage(0);
     __builtin_amdgcn_sched_barrier(0);
-    if (st + 1 < NS) store_stage(buf ^ 1, buf ^ 1);
-    load_stage(st + 3, buf ^ 1);
+    load_stage(ld, 1);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-  };
-  for (int st = 0; st < NS; st += 2) {
-    step(st, 0);
-    step(st + 1, 1);
-  }
 
-  // ---- epilogue.  The ring is free (every wave passed the last barrier).
 #pragma unroll
-  for (int a = 0; a < 2; a++)
+    for (int a = 0; a < 2; a++)
 #pragma unroll
-    for (int b = 0; b < 2; b++)
+      for (int b = 0; b < 2; b++)
 #pragma unroll
-      for (int i = 0; i < 16; i++) acc[a][b][i] *= 64.0f;   // P_g / 64 -> P_g (exact)
+        for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
 
-  if (RB > 0) {
-    // L2[:, n0:n0+128] transposed into LDS as [n][k] (row stride (R+8) halves), then
-    // acc += L2^T T^T on v_mfma_f32_32x32x16_f16: row operand L2^T (columns n), column
-    // operand T (rows m, 8 consecutive k per lane: one 16-byte load)
-    constexpr int LS2 = (R + 8) * 2;
-    static_assert(BN * LS2 <= E_Y, "L2 staging overlaps the output staging");
-    for (int idx = tid; idx < R * (BN / 8); idx += NT) {
-      const int k = idx % R, c8 = idx / R;   // neighbouring lanes write neighbouring k
-      const int n = n0 + c8 * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (n < N) v = *reinterpret_cast<const uint4*>(l2 + (size_t)k * N + n);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    int lbase = 0;                           // stage index of ld = step + 2 - lbase
+    auto step = [&](int st, int buf, bool do_load) {
+      if (st < NS) {
 #pragma unroll
-      for (int e = 0; e < 8; e++)
-        *reinterpret_cast<uint16_t*>(lds + (c8 * 8 + e) * LS2 + k * 2) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        for (int k = 0; k < KC; k++)
+          if (st * KC + k < G) {
+            read_ops(lds + buf * STAGE + k * GROUP, ops);
+            mma_ops(ops);
+          }
+      }
+      // keep the next stage's LDS writes (and their wait on the global loads) after this compute
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + 1 < NS) store_stage(buf ^ 1);
+      if (do_load) {
+        if (st + 2 == NSE && has_next) {
+          ld = nxt;
+          lbase = NSE;
+        }
+        load_stage(ld, st + 2 - lbase);
+      }
+      __syncthreads();
+    };
+    for (int st = 0; st + 2 < NSE; st += 2) {
+      step(st, 0, true);
+      step(st + 1, 1, true);
     }
-    uint4 top[RB > 0 ? RB : 1][2];
-#pragma unroll
-    for (int kb = 0; kb < RB; kb++)
-#pragma unroll
-      for (int ti = 0; ti < 2; ti++) {
-        const int m = min(m0 + wm * 64 + ti * 32 + r32, M - 1);
-        top[kb][ti] = *reinterpret_cast<const uint4*>(t + (size_t)m * R + kb * 16 + 8 * h);
-      }
-    __syncthreads();
-#pragma unroll
-    for (int kb = 0; kb < RB; kb++)
-#pragma unroll
-      for (int tj = 0; tj < 2; tj++) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(lds + (wn * 64 + tj * 32 + r32) * LS2 + (kb * 16 + 8 * h) * 2);
-#pragma unroll
-        for (int ti = 0; ti < 2; ti++)
-          acc[tj][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(lo), as_h8(top[kb][ti]), acc[tj][ti], 0, 0, 0);
-      }
-  }
+    step(NSE - 2, 0, true);
+    step(NSE - 1, 1, false);
 
-  // bias, RNE to fp16, 8-byte pieces into this wave's LDS staging, 16-byte row stores
-  uint8_t* ys = lds + E_Y + wave * 64 * E_YS;
+    // ---- epilogue.  The ring is free (every wave passed the last barrier).
 #pragma unroll
-  for (int tj = 0; tj < 2; tj++) {
+    for (int a = 0; a < 2; a++)
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-      const int nl = tj * 32 + 8 * q + 4 * h;    // column within the wave's 64
-      float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (BIAS) {
-        const int n = n0 + wn * 64 + nl;
-        if (n < N) {
-          const uint2 braw = *reinterpret_cast<const uint2*>(bias + n);
-          bv[0] = __half2float(__ushort_as_half((unsigned short)(braw.x & 0xFFFFu)));
-          bv[1] = __half2float(__ushort_as_half((unsigned short)(braw.x >> 16)));
-          bv[2] = __half2float(__ushort_as_half((unsigned short)(braw.y & 0xFFFFu)));
-          bv[3] = __half2float(__ushort_as_half((unsigned short)(braw.y >> 16)));
+      for (int b = 0; b < 2; b++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) acc[a][b][i] *= 64.0f;   // P_g / 64 -> P_g (exact)
+
+    if (RB > 0) {
+      // L2[:, n0:n0+128] transposed into LDS as [n][k] (row stride (R+8) halves), then
+      // acc += L2^T T^T on v_mfma_f32_32x32x16_f16: row operand L2^T (columns n), column
+      // operand T (rows m, 8 consecutive k per lane: one 16-byte load)
+      constexpr int LS2 = (R + 8) * 2;
+      static_assert(BN * LS2 <= E_Y, "L2 staging overlaps the output staging");
+      for (int idx = tid; idx < R * (BN / 8); idx += NT) {
+        const int k = idx % R, c8 = idx / R;   // neighbouring lanes write neighbouring k
+        const int n = n0 + c8 * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (n < N) v = *reinterpret_cast<const uint4*>(l2 + (size_t)k * N + n);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+          *reinterpret_cast<uint16_t*>(lds + (c8 * 8 + e) * LS2 + k * 2) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      }
+      uint4 top[RB > 0 ? RB : 1][2];
+#pragma unroll
+      for (int kb = 0; kb < RB; kb++)
+#pragma unroll
+        for (int ti = 0; ti < 2; ti++) {
+          const int m = min(m0 + wm * 64 + ti * 32 + r32, M - 1);
+          top[kb][ti] = *reinterpret_cast<const uint4*>(t + (size_t)m * R + kb * 16 + 8 * h);
+        }
+      __syncthreads();
+#pragma unroll
+      for (int kb = 0; kb < RB; kb++)
+#pragma unroll
+        for (int tj = 0; tj < 2; tj++) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(lds + (wn * 64 + tj * 32 + r32) * LS2 + (kb * 16 + 8 * h) * 2);
+#pragma unroll
+          for (int ti = 0; ti < 2; ti++)
+            acc[tj][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(lo), as_h8(top[kb][ti]), acc[tj][ti], 0, 0, 0);
+        }
+    }
+
+    // bias, RNE to fp16, 8-byte pieces into this wave's LDS staging, 16-byte row stores
+    uint8_t* ys = lds + E_Y + wave * 64 * E_YS;
+#pragma unroll
+    for (int tj = 0; tj < 2; tj++) {
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int nl = tj * 32 + 8 * q + 4 * h;    // column within the wave's 64
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (BIAS) {
+          const int n = n0 + wn * 64 + nl;
+          if (n < N) {
+            const uint2 braw = *reinterpret_cast<const uint2*>(bias + n);
+            bv[0] = __half2float(__ushort_as_half((unsigned short)(braw.x & 0xFFFFu)));
+            bv[1] = __half2float(__ushort_as_half((unsigned short)(braw.x >> 16)));
+            bv[2] = __half2float(__ushort_as_half((unsigned short)(braw.y & 0xFFFFu)));
+            bv[3] = __half2float(__ushort_as_half((unsigned short)(braw.y >> 16)));
+          }
+        }
+#pragma unroll
+        for (int ti = 0; ti < 2; ti++) {
+          uint32_t hv[4];
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+            hv[j] = __half_as_ushort(__float2half_rn(acc[tj][ti][4 * q + j] + bv[j]));
+          *reinterpret_cast<uint2*>(ys + (ti * 32 + r32) * E_YS + nl * 2) =
+              make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
         }
       }
-#pragma unroll
-      for (int ti = 0; ti < 2; ti++) {
-        uint32_t hv[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-          hv[j] = __half_as_ushort(__float2half_rn(acc[tj][ti][4 * q + j] + bv[j]));
-        *reinterpret_cast<uint2*>(ys + (ti * 32 + r32) * E_YS + nl * 2) =
-            make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
-      }
     }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-  for (int it = 0; it < 8; it++) {
-    const int rl = it * 8 + (lane >> 3), c = (lane & 7) * 8;   // row within the wave's 64, column
-    const uint2 a = *reinterpret_cast<const uint2*>(ys + rl * E_YS + c * 2);
-    const uint2 b = *reinterpret_cast<const uint2*>(ys + rl * E_YS + c * 2 + 8);
-    const int m = m0 + wm * 64 + rl, n = n0 + wn * 64 + c;
-    if (m < M && n < N) *reinterpret_cast<uint4*>(y + (size_t)m * N + n) = make_uint4(a.x, a.y, b.x, b.y);
+    for (int it = 0; it < 8; it++) {
+      const int rl = it * 8 + (lane >> 3), c = (lane & 7) * 8;   // row within the wave's 64, column
+      const uint2 a = *reinterpret_cast<const uint2*>(ys + rl * E_YS + c * 2);
+      const uint2 b = *reinterpret_cast<const uint2*>(ys + rl * E_YS + c * 2 + 8);
+      const int m = m0 + wm * 64 + rl, n = n0 + wn * 64 + c;
+      if (m < M && n < N) *reinterpret_cast<uint4*>(y + (size_t)m * N + n) = make_uint4(a.x, a.y, b.x, b.y);
+    }
+    __syncthreads();                         // the ring is rewritten by the next tile's stage 0
+    if (!has_next) break;
+    tile = next;
+
   }
+}
+
+// Workgroups that fit on the device at once (two per CU), cached per device.
+static int resident_blocks() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = 2 * cus;
+  }
+  return cached[dev];
 }
 
 template <int RB, bool BIAS>
 static hipError_t launch_g3(const GemmArgs& a, hipStream_t s) {
-  const int nb = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const int nb = tiles < resident_blocks() ? tiles : resident_blocks();
   hipLaunchKernelGGL((k_gemm3<RB, BIAS>), dim3(nb), dim3(NT), 0, s, (const uint8_t*)a.xq,
                      (const __half*)a.xs, (const __half*)a.t, (const uint8_t*)a.wq, (const __half*)a.ws,
                      (const __half*)a.l2, (const __half*)a.bias, a.M, a.N, a.K, (__half*)a.y);
