@@ -74,6 +74,11 @@ svdq_status check_gemm(const void* xq, const void* xs, const void* t, const void
   if (!fmt_ok(fmt)) return SVDQ_ERR_FORMAT;
   svdq_status st = check_dims(M, N, K, r);
   if (st != SVDQ_OK) return st;
+  // the 6-bit container kernel addresses each code operand with 32-bit byte offsets
+  if (fmt == SVDQ_INT4_G64_E2M3 &&
+      ((size_t)M * code_bytes(K, (svdq_format)fmt) >= (1ull << 32) ||
+       (size_t)N * code_bytes(K, (svdq_format)fmt) >= (1ull << 32)))
+    return SVDQ_ERR_SHAPE;
   if (M == 0 || N == 0) return SVDQ_OK;
   if (!xq || !xs || !wq || !ws || !y) return SVDQ_ERR_NULL;
   if (r > 0 && (!t || !l2)) return SVDQ_ERR_NULL;

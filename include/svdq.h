@@ -31,7 +31,9 @@
  *  - Shapes: M >= 0 and N >= 0 (0 = nothing to do: SVDQ_OK once the format
  *    and the other dimensions check out, and the pointers may then be NULL,
  *    as a zero-size tensor's are); K > 0 with
- *    K % 64 == 0; N % 16 == 0; r % 16 == 0 and 0 <= r <= 64; M, N, K <= 2^24.
+ *    K % 64 == 0; N % 16 == 0; r % 16 == 0 and 0 <= r <= 64; M, N, K <= 2^24;
+ *    with SVDQ_INT4_G64_E2M3 the GEMM also needs each code operand (M * 3K/4
+ *    and N * 3K/4 bytes) below 4 GiB.
  *  - Non-finite inputs are undefined behaviour.
  *
  * Formats (group quantization along K; groups per token row for activations,
