@@ -3,15 +3,26 @@
 
 One step = one pass of the layer's hot path over one batch: Kernel A
 (quantize + down projection) then Kernel B (W4A4 GEMM + up projection + bias),
-the same two launches svdq_linear makes, on the FLUX-like fused QKV projection
-(M=4608 tokens, K=3072, N=9216, rank 32, int4 group 64) by default.
+the same two launches svdq_linear makes.  The headline line is the FLUX-like
+fused QKV projection (M=4608 tokens, K=3072, N=9216, rank 32, INT4 group 64);
+the same run also times, each on its own seeded layer and with fewer steps:
+  * the FLUX-like MLP pair: fc1 (K=3072, N=12288) and fc2 (K=12288, N=3072);
+  * on the QKV layer: the bare W4A4 GEMM (r = 0: no branch in either kernel),
+    the unfused branch (down projection, quantization, GEMM, up projection as
+    separate launches with an fp16 intermediate), and the W4A16 control (fp16
+    activations times INT4 group-64 weights, no branch).
 
 Inputs are seeded synthetic layers, resident in HBM before timing starts.
 Three copies of every input and output buffer are rotated so that a step never
 finds its operands in the 256 MB last-level cache (MALL) from the previous
 step.  Timing: W warm-up steps, then K timed steps bracketed by device
-synchronizations; HIP events on the launch stream give each kernel's average
-duration.  Prints one JSON line.
+synchronizations (wall clock); HIP events on the launch stream give each
+kernel's average duration.  Prints one JSON line.
+
+The roofline's HBM traffic comes from the committed rocprofv3 counter summary
+of Kernel B (FETCH_SIZE and WRITE_SIZE, calibrated on a plain copy); it is
+reported only while Kernel B's source still has the hash recorded there.
+`--copy-mib N` instead runs the plain copy used for that calibration.
 
 The CPU baseline times the CPU oracle (the layer's plain numpy definition) on
 the first rows of the same layer, on this host's cores.
@@ -19,8 +30,10 @@ the first rows of the same layer, on this host's cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -32,15 +45,18 @@ import numpy as np
 
 METRIC = "µs and effective TOPS per fused W4A4+rank-32 linear (FLUX shapes); % MFMA peak"
 INT8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA, 5.0 POP/s
+FP6_PEAK_TFLOPS = 10100.0        # MI355X dense FP6/FP4 MFMA, 10.1 PFLOP/s
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 
 WORKLOADS = {
-    # name: (M, K, N, r, synth config layer)
+    # name: (M, K, N, r, synthetic layer)
     "qkv": (4608, 3072, 9216, 32, "c1_qkv"),
     "fc1": (4608, 3072, 12288, 32, "c2_fc1"),
     "fc2": (4608, 12288, 3072, 32, "c2_fc2"),
 }
 ROTATE = 3
+KERNEL_B_SOURCE = os.path.join(ROOT, "bit_w4a4_quantized_amd", "csrc", "k_gemm3.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "kernel_b_qkv_4608x3072x9216_traffic.md")
 
 
 def parse():
@@ -51,10 +67,14 @@ def parse():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="qkv")
     ap.add_argument("--rank", type=int, default=None, help="override r (0 = bare W4A4 GEMM)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="headline only: skip the other workloads "
+                                                               "and the bare / unfused / W4A16 comparisons")
+    ap.add_argument("--extra-steps", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
-    ap.add_argument("--variant", choices=["fused", "unfused", "w4a16"], default="fused")
     ap.add_argument("--fmt", choices=["int4_e2m3", "int4"], default="int4_e2m3",
                     help="INT4 g64 codes in the 6-bit E2M3 container (FP6 MFMA) or packed nibbles (INT8 MFMA)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run only a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -65,6 +85,21 @@ def algorithmic_bytes(M, K, N, r, code_bits=4, G=64):
     kb = (int(M * K * cb) + 2 * M * K // G + 2 * M * r + int(K * N * cb) + 2 * K * N // G + 2 * r * N + 2 * N
           + 2 * M * N)
     return ka, kb
+
+
+def kernel_b_traffic(fmt, workload, r):
+    """HBM bytes per Kernel B launch from the committed counter summary, if it was taken on the
+    current source of Kernel B (else None)."""
+    if fmt != "int4_e2m3" or workload != "qkv" or r != 32 or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    m = re.search(r"traffic_json:\s*(\{.*\})", open(TRAFFIC_PROFILE).read())
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    sha = hashlib.sha256(open(KERNEL_B_SOURCE, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec
 
 
 def cpu_baseline(raw, host_layer, fmt, M, K, N, r, target_s):
@@ -101,6 +136,127 @@ def cpu_baseline(raw, host_layer, fmt, M, K, N, r, target_s):
             "seconds": round(dt, 3)}
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Layer:
+    """One seeded layer on the device with ROTATE copies of every operand."""
+
+    def __init__(self, torch, binding, name, fmt, r_override=None):
+        from bit_w4a4_quantized_amd.prepare import prepare_host, to_device
+        from synth import CONFIGS, draw_layer, fc2_calibration_input, LayerShape
+        M, K, N, r, lname = WORKLOADS[name]
+        if r_override is not None:
+            r = r_override
+        shapes = {s.name: s for v in CONFIGS.values() for s in v}
+        s = shapes[lname]
+        t0 = time.time()
+        raw = draw_layer(LayerShape(s.name, s.M, s.K, s.N, r, fmt, s.seed, s.planted_rank))
+        if lname == "c2_fc2":
+            raw.x = fc2_calibration_input(draw_layer(shapes["c2_fc1"]))
+        host = prepare_host(raw.x, raw.w, raw.b, r)
+        dev = to_device(host, fmt)
+        x_hat = torch.from_numpy(host.smooth(raw.x)).cuda()
+        self.name, self.lname, self.fmt, self.M, self.K, self.N, self.r = name, lname, fmt, M, K, N, r
+        self.raw, self.host, self.torch, self.binding = raw, host, torch, binding
+        cp = lambda t: None if t is None else t.clone()
+        self.sets = []
+        for _ in range(ROTATE):
+            self.sets.append(dict(
+                x=x_hat.clone(), l1t=cp(dev.l1t), wq=dev.wq.clone(), ws=dev.ws.clone(), l2=cp(dev.l2),
+                b=dev.bias.clone(),
+                xq=torch.empty(binding.code_shape(M, K, fmt), dtype=torch.uint8, device="cuda"),
+                xs=torch.empty(binding.scale_shape(M, K, fmt), dtype=binding.scale_dtype(fmt), device="cuda"),
+                t=torch.empty((M, r), dtype=torch.float16, device="cuda") if r else None,
+                y=torch.empty((M, N), dtype=torch.float16, device="cuda"),
+            ))
+        torch.cuda.synchronize()
+        log(f"prepared {name} M={M} K={K} N={N} r={r} {fmt} in {time.time() - t0:.1f}s")
+
+    def fused(self, i, ev=None, branch=True):
+        st, b = self.sets[i % ROTATE], self.binding
+        if ev is not None:
+            ev[0].record()
+        b.svdq_quantize_down(st["x"], st["l1t"] if branch else None, self.fmt, xq=st["xq"], xs=st["xs"],
+                             t=st["t"] if branch else None)
+        if ev is not None:
+            ev[1].record()
+        b.svdq_gemm_w4a4_up(st["xq"], st["xs"], st["t"] if branch else None, st["wq"], st["ws"],
+                            st["l2"] if branch else None, st["b"], self.K, self.fmt, y=st["y"])
+        if ev is not None:
+            ev[2].record()
+
+    def time_fused(self, steps, warmup, branch=True):
+        torch = self.torch
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(warmup):
+            self.fused(i, branch=branch)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.fused(i, ev[i], branch=branch)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return {"us_per_layer": wall * 1e6 / steps,
+                "us_per_layer_events": float(np.mean([e[0].elapsed_time(e[2]) for e in ev])) * 1e3,
+                "ka_us": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3,
+                "kb_us": float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3}
+
+    def time_call(self, fn, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return {"us_per_call": (time.perf_counter() - t0) * 1e6 / steps,
+                "us_per_call_events": e0.elapsed_time(e1) * 1e3 / steps}
+
+    def time_unfused(self, steps, warmup):
+        b, torch = self.binding, self.torch
+        wsb = torch.empty(max(16, b.linear_unfused_workspace_bytes(self.M, self.N, self.K, self.r, self.fmt)),
+                          dtype=torch.uint8, device="cuda")
+
+        def fn(i):
+            st = self.sets[i % ROTATE]
+            b.svdq_linear_unfused(st["x"], st["l1t"], st["wq"], st["ws"], st["l2"], st["b"], self.fmt,
+                                  workspace=wsb, y=st["y"])
+        return self.time_call(fn, steps, warmup)
+
+    def time_w4a16(self, steps, warmup):
+        b, torch = self.binding, self.torch
+        w_t = torch.from_numpy(np.ascontiguousarray(self.raw.w.T.astype(np.float32))).cuda()
+        wq16, ws16 = b.svdq_quantize_weight(w_t, "int4")
+        del w_t
+        xr = [torch.from_numpy(self.raw.x).cuda() for _ in range(ROTATE)]
+        wq = [wq16.clone() for _ in range(ROTATE)]
+        ws = [ws16.clone() for _ in range(ROTATE)]
+
+        def fn(i):
+            st = self.sets[i % ROTATE]
+            b.svdq_gemm_w4a16(xr[i % ROTATE], wq[i % ROTATE], ws[i % ROTATE], st["b"], y=st["y"])
+        return self.time_call(fn, steps, warmup)
+
+
+def copy_calibration(mib):
+    """A plain device copy of known size (for FETCH_SIZE / WRITE_SIZE calibration)."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -110,120 +266,36 @@ def main():
         sys.exit(2)
 
     import torch
-    from bit_w4a4_quantized_amd import binding
-    from bit_w4a4_quantized_amd.prepare import prepare_host, to_device
-    from synth import CONFIGS, draw_layer, fc2_calibration_input, LayerShape
-
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_mib:
+        copy_calibration(args.copy_mib)
+        return
+    from bit_w4a4_quantized_amd import binding
     binding.lib()
-    M, K, N, r, lname = WORKLOADS[args.workload]
     fmt = args.fmt
-    if args.rank is not None:
-        r = args.rank
-    shapes = {s.name: s for v in CONFIGS.values() for s in v}
-    s = shapes[lname]
-    t0 = time.time()
-    if lname == "c2_fc2":
-        fc1 = draw_layer(shapes["c2_fc1"])
-        raw = draw_layer(LayerShape(s.name, s.M, s.K, s.N, r, fmt, s.seed, s.planted_rank))
-        raw.x = fc2_calibration_input(fc1)
-    else:
-        raw = draw_layer(LayerShape(s.name, s.M, s.K, s.N, r, fmt, s.seed, s.planted_rank))
-    host = prepare_host(raw.x, raw.w, raw.b, r)
-    layer = to_device(host, fmt)
-    x_hat = torch.from_numpy(host.smooth(raw.x)).cuda()
-    print(f"[bench] prepared {args.workload} M={M} K={K} N={N} r={r} {fmt} in {time.time() - t0:.1f}s",
-          file=sys.stderr, flush=True)
 
-    # rotated copies of every operand so that consecutive steps miss in the MALL
-    sets = []
-    for i in range(ROTATE):
-        cp = lambda t: None if t is None else t.clone()
-        sets.append(dict(
-            x=x_hat.clone(), l1t=cp(layer.l1t), wq=layer.wq.clone(), ws=layer.ws.clone(), l2=cp(layer.l2),
-            b=layer.bias.clone(),
-            xq=torch.empty(binding.code_shape(M, K, fmt), dtype=torch.uint8, device="cuda"),
-            xs=torch.empty(binding.scale_shape(M, K, fmt), dtype=binding.scale_dtype(fmt), device="cuda"),
-            t=torch.empty((M, r), dtype=torch.float16, device="cuda") if r else None,
-            y=torch.empty((M, N), dtype=torch.float16, device="cuda"),
-            ws_buf=torch.empty(max(16, binding.linear_unfused_workspace_bytes(M, N, K, r, fmt)), dtype=torch.uint8, device="cuda"),
-        ))
-    if args.variant == "w4a16":
-        xraw = torch.from_numpy(raw.x).cuda()
-        w_t = torch.from_numpy(np.ascontiguousarray(raw.w.T.astype(np.float32))).cuda()
-        wq16, ws16 = binding.svdq_quantize_weight(w_t, "int4")
-        for st in sets:
-            st["xr"], st["wq16"], st["ws16"] = xraw.clone(), wq16.clone(), ws16.clone()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-
-    n_ev = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
-
-    def step(i, record=None):
-        st = sets[i % ROTATE]
-        if record is not None:
-            record[0].record(stream)
-        if args.variant == "fused":
-            binding.svdq_quantize_down(st["x"], st["l1t"], fmt, xq=st["xq"], xs=st["xs"], t=st["t"])
-            if record is not None:
-                record[1].record(stream)
-            binding.svdq_gemm_w4a4_up(st["xq"], st["xs"], st["t"], st["wq"], st["ws"], st["l2"], st["b"], K, fmt,
-                                      y=st["y"])
-        elif args.variant == "unfused":
-            binding.svdq_linear_unfused(st["x"], st["l1t"], st["wq"], st["ws"], st["l2"], st["b"], fmt,
-                                        workspace=st["ws_buf"], y=st["y"])
-            if record is not None:
-                record[1].record(stream)
-        else:
-            binding.svdq_gemm_w4a16(st["xr"], st["wq16"], st["ws16"], st["b"], y=st["y"])
-            if record is not None:
-                record[1].record(stream)
-        if record is not None:
-            record[2].record(stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(i, ev[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ka_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(n_ev)]
-    kb_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(n_ev)]
-    step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(n_ev)]
-    ms_per_step = wall * 1e3 / args.steps
-    ev_ms = float(np.mean(step_ms))
-
-    # warm-cache figure (same buffers every step), for reference only
-    for _ in range(3):
-        step(0)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    for _ in range(20):
-        step(0)
-    torch.cuda.synchronize()
-    warm_us = (time.perf_counter() - w0) * 1e6 / 20
+    L = Layer(torch, binding, args.workload, fmt, args.rank)
+    M, K, N, r = L.M, L.K, L.N, L.r
+    head = L.time_fused(args.steps, args.warmup)
+    ms_per_step = head["us_per_layer"] * 1e-3
 
     ops = 2.0 * M * N * K
     tops = ops / (ms_per_step * 1e-3) / 1e12
     ka_bytes, kb_bytes = algorithmic_bytes(M, K, N, r, 6 if fmt == "int4_e2m3" else 4)
-    kb_us = float(np.mean(kb_ms)) * 1e3
-    ka_us = float(np.mean(ka_ms)) * 1e3
-    if args.variant == "fused":
-        dom_ops = ops + 2.0 * M * r * N                       # Kernel B: W4A4 GEMM + up projection
-        achieved = dom_ops / (kb_us * 1e-6) / 1e12
-        roof = {"kernel": "k_gemm (Kernel B: W4A4 GEMM + up projection)", "bound": "mfma",
-                "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None,
-                "algorithmic": f"2*M*N*K + 2*M*r*N = {dom_ops:.4g} int8-equivalent ops per launch",
-                "avg_launch_us": round(kb_us, 2)}
-    else:
-        roof = {"kernel": args.variant, "bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS,
-                "unit": "TFLOP/s", "frac": round(tops / INT8_PEAK_TOPS, 4), "traffic": None}
+    ka_us, kb_us = head["ka_us"], head["kb_us"]
+    dom_ops = ops + 2.0 * M * r * N                       # Kernel B: W4A4 GEMM + up projection
+    achieved = dom_ops / (kb_us * 1e-6) / 1e12
+    traffic = kernel_b_traffic(fmt, args.workload, r)
+    roof = {"kernel": "k_gemm3 / k_gemm2 (Kernel B: W4A4 GEMM + up projection + bias)", "bound": "mfma",
+            "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / INT8_PEAK_TOPS, 4),
+            "traffic": None if traffic is None else traffic["hbm_bytes_per_launch"],
+            "algorithmic": f"2*M*N*K + 2*M*r*N = {dom_ops:.4g} int8-equivalent ops per launch",
+            "avg_launch_us": round(kb_us, 2),
+            "frac_of_fp6_peak": round(achieved / FP6_PEAK_TFLOPS, 4) if fmt == "int4_e2m3" else None,
+            "algorithmic_hbm_bytes": kb_bytes}
 
     out = {
         "metric": METRIC,
@@ -238,22 +310,58 @@ def main():
         "vs_baseline": None,
         "dtype": "int4 codes; fp6(e2m3) MFMA" if fmt == "int4_e2m3" else "int4 codes; i8 MFMA",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {lname} M={M} K={K} N={N} r={r} int4 group 64, fp16 scales",
-                   "storage": fmt,
-                   "variant": args.variant, "rotated_buffer_sets": ROTATE},
-        "us_per_layer": round(ms_per_step * 1e3, 2),
-        "us_per_layer_events": round(ev_ms * 1e3, 2),
-        "us_per_layer_warm": round(warm_us, 2),
+        "config": {"workload": f"{args.workload}: {L.lname} M={M} K={K} N={N} r={r} int4 group 64, fp16 scales",
+                   "storage": fmt, "rotated_buffer_sets": ROTATE},
+        "us_per_layer": round(head["us_per_layer"], 2),
+        "us_per_layer_events": round(head["us_per_layer_events"], 2),
         "pct_int8_peak": round(100.0 * tops / INT8_PEAK_TOPS, 2),
         "kernels_us": {"quantize_down": round(ka_us, 2), "gemm_w4a4_up": round(kb_us, 2)},
         "kernel_a_hbm": {"algorithmic_bytes": ka_bytes,
-                         "achieved_GBps": round(ka_bytes / (ka_us * 1e-6) / 1e9, 1) if args.variant == "fused" else None,
-                         "frac_of_8TBps": round(ka_bytes / (ka_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) if args.variant == "fused" else None},
+                         "achieved_GBps": round(ka_bytes / (ka_us * 1e-6) / 1e9, 1),
+                         "frac_of_8TBps": round(ka_bytes / (ka_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": roof,
         "cpu_baseline": None,
     }
+
+    if not args.no_extras:
+        es, ew = args.extra_steps, 5
+        cmp_ = {}
+        bare = L.time_fused(es, ew, branch=False)
+        fused = L.time_fused(es, ew)
+        cmp_["fused_us"] = round(fused["us_per_layer"], 2)
+        cmp_["bare_w4a4_us"] = round(bare["us_per_layer"], 2)
+        cmp_["bare_kernels_us"] = {"quantize": round(bare["ka_us"], 2), "gemm": round(bare["kb_us"], 2)}
+        cmp_["branch_overhead_pct"] = round(100.0 * (fused["us_per_layer"] / bare["us_per_layer"] - 1.0), 2)
+        unf = L.time_unfused(es, ew)
+        cmp_["unfused_us"] = round(unf["us_per_call"], 2)
+        cmp_["unfused_over_fused_pct"] = round(100.0 * (unf["us_per_call"] / fused["us_per_layer"] - 1.0), 2)
+        cmp_["unfused_over_bare_pct"] = round(100.0 * (unf["us_per_call"] / bare["us_per_layer"] - 1.0), 2)
+        w16 = L.time_w4a16(es, ew)
+        cmp_["w4a16_us"] = round(w16["us_per_call"], 2)
+        cmp_["speedup_fused_vs_w4a16"] = round(w16["us_per_call"] / fused["us_per_layer"], 3)
+        out["comparisons_" + args.workload] = cmp_
+        log(f"comparisons: {cmp_}")
+        others = {}
+        for name in ("fc1", "fc2"):
+            if name == args.workload:
+                continue
+            Lo = Layer(torch, binding, name, fmt)
+            res = Lo.time_fused(es, ew)
+            o_ops = 2.0 * Lo.M * Lo.N * Lo.K
+            o_b = o_ops + 2.0 * Lo.M * Lo.r * Lo.N
+            others[name] = {"M": Lo.M, "K": Lo.K, "N": Lo.N, "r": Lo.r,
+                            "us_per_layer": round(res["us_per_layer"], 2),
+                            "tops": round(o_ops / (res["us_per_layer"] * 1e-6) / 1e12, 2),
+                            "pct_int8_peak": round(100.0 * o_ops / (res["us_per_layer"] * 1e-6) / 1e12 / INT8_PEAK_TOPS, 2),
+                            "kernels_us": {"quantize_down": round(res["ka_us"], 2), "gemm_w4a4_up": round(res["kb_us"], 2)},
+                            "kernel_b_pct_int8_peak": round(100.0 * o_b / (res["kb_us"] * 1e-6) / 1e12 / INT8_PEAK_TOPS, 2)}
+            log(f"{name}: {others[name]}")
+            del Lo
+            torch.cuda.empty_cache()
+        out["other_workloads"] = others
+
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(raw, host, "int4", M, K, N, r, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(L.raw, L.host, "int4", M, K, N, r, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
