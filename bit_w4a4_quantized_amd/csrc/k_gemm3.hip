@@ -117,7 +117,7 @@ template <int RB, bool BIAS>
 __global__ void __launch_bounds__(NT, 2)
 k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __half* __restrict__ t,
         const uint8_t* __restrict__ wq, const __half* __restrict__ ws, const __half* __restrict__ l2,
-        const __half* __restrict__ bias, int M, int N, int K, __half* __restrict__ y) {
+        const __half* __restrict__ bias, int M, int N, int K, __half* __restrict__ y, int tiles_run) {
   constexpr int R = RB * 16;
   __shared__ __attribute__((aligned(16))) uint8_t lds[RING];
 
@@ -243,7 +243,7 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
   load_stage(cur, 0, 0);
   while (true) {
     const int next = tile + (int)gridDim.x;
-    const bool has_next = next < tiles;
+    const bool has_next = next < tiles_run;
     const Src nxt = tile_src(has_next ? next : tile);
     int tm, tn;
     tile_of3(tile, tiles, tiles_m, tiles_n, &tm, &tn);
@@ -395,6 +395,112 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
   }
 }
 
+// The last, partial round of tiles: when only a few tiles remain after the full rounds of
+// the persistent kernel, each of them is cut into 16 sub-tiles of 32 x 32 and each sub-tile is
+// one workgroup whose four waves split K (groups w, w + 4, ...); the four partial sums are
+// added in LDS in a fixed order, so the result is deterministic and no global scratch is
+// needed.  Operands come straight from global memory into registers, four groups ahead.
+template <int RB, bool BIAS>
+__global__ void __launch_bounds__(NT, 2)
+k_gemm3_tail(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __half* __restrict__ t,
+             const uint8_t* __restrict__ wq, const __half* __restrict__ ws, const __half* __restrict__ l2,
+             const __half* __restrict__ bias, int M, int N, int K, __half* __restrict__ y, int tile0) {
+  constexpr int R = RB * 16;
+  __shared__ __attribute__((aligned(16))) float red[3][16][64];   // partials of waves 1..3
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, r32 = lane & 31;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int tiles = tiles_m * tiles_n;
+  const int G = K >> 6;
+  int tm, tn;
+  tile_of3(tile0 + (int)(blockIdx.x >> 4), tiles, tiles_m, tiles_n, &tm, &tn);
+  const int sub = blockIdx.x & 15;
+  const int nb = tn * BN + (sub >> 2) * 32, mb = tm * BM + (sub & 3) * 32;   // sub-tile origin
+  const int m = min(mb + r32, M - 1), n = min(nb + r32, N - 1);           // this lane's operand rows
+
+  typedef _Float16 v4h_t __attribute__((ext_vector_type(4)));
+  struct Op { uint4 x0, w0; uint2 x1, w1; uint32_t sx, sw; };
+  auto load = [&](int g, Op& o) {
+    const uint8_t* px = xq + ((size_t)g * M + m) * GB + 24 * h;
+    const uint8_t* pw = wq + ((size_t)g * N + n) * GB + 24 * h;
+    o.x0 = *reinterpret_cast<const uint4*>(px);
+    o.x1 = *reinterpret_cast<const uint2*>(px + 16);
+    o.w0 = *reinterpret_cast<const uint4*>(pw);
+    o.w1 = *reinterpret_cast<const uint2*>(pw + 16);
+    // K slot 0 holds the scale for the lower-K-half lanes; the upper half contributes zeros
+    o.sx = h ? 0u : (uint32_t)reinterpret_cast<const unsigned short*>(xs)[(size_t)g * M + m];
+    o.sw = h ? 0u : (uint32_t)reinterpret_cast<const unsigned short*>(ws)[(size_t)g * N + n];
+  };
+  v16f acc;
+#pragma unroll
+  for (int i = 0; i < 16; i++) acc[i] = 0.f;
+  // a ring of PD groups in flight per wave (groups wave, wave + 4, ...)
+  constexpr int PD = 4;
+  Op ring[PD];
+#pragma unroll
+  for (int j = 0; j < PD; j++)
+    if (wave + 4 * j < G) load(wave + 4 * j, ring[j]);
+  for (int g0 = wave; g0 < G; g0 += 4 * PD) {
+#pragma unroll
+    for (int j = 0; j < PD; j++) {
+      const int g = g0 + 4 * j;
+      if (g >= G) break;
+      const Op cur = ring[j];
+      if (g + 4 * PD < G) load(g + 4 * PD, ring[j]);
+      const v8i xo = v8i{(int)cur.x0.x, (int)cur.x0.y, (int)cur.x0.z, (int)cur.x0.w, (int)cur.x1.x, (int)cur.x1.y, 0, 0};
+      const v8i wo = v8i{(int)cur.w0.x, (int)cur.w0.y, (int)cur.w0.z, (int)cur.w0.w, (int)cur.w1.x, (int)cur.w1.y, 0, 0};
+      const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wo, xo, v16f{}, 2, 2, 0, 127, 0, 127);
+      const v16f sc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h_t, make_uint2(cur.sw, 0u)),
+                                                            __builtin_bit_cast(v4h_t, make_uint2(cur.sx, 0u)),
+                                                            v16f{}, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 16; i++) acc[i] = __builtin_fmaf(p[i], sc[i], acc[i]);
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) red[wave - 1][i][lane] = acc[i];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int i = 0; i < 16; i++) acc[i] = ((acc[i] + red[0][i][lane]) + red[1][i][lane]) + red[2][i][lane];
+#pragma unroll
+  for (int i = 0; i < 16; i++) acc[i] *= 64.0f;   // P_g / 64 -> P_g (exact)
+  // up projection on the 32 x 32 sub-tile: row operand L2^T (columns n), column operand T (rows m)
+#pragma unroll
+  for (int kb = 0; kb < RB; kb++) {
+    const uint4 tv = *reinterpret_cast<const uint4*>(t + (size_t)m * R + kb * 16 + 8 * h);
+    uint16_t lv[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) lv[e] = __half_as_ushort(l2[(size_t)(kb * 16 + 8 * h + e) * N + n]);
+    const uint4 lw = make_uint4(lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16),
+                                lv[4] | ((uint32_t)lv[5] << 16), lv[6] | ((uint32_t)lv[7] << 16));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(lw), as_h8(tv), acc, 0, 0, 0);
+  }
+  // lane owns row mb + r32 and columns nb + 8 q + 4 h + j (reg 4 q + j)
+  const int mo = mb + r32;
+  if (mo >= M) return;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int no = nb + 8 * q + 4 * h;
+    if (no >= N) continue;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (BIAS) {
+      const uint2 braw = *reinterpret_cast<const uint2*>(bias + no);
+      bv[0] = __half2float(__ushort_as_half((unsigned short)(braw.x & 0xFFFFu)));
+      bv[1] = __half2float(__ushort_as_half((unsigned short)(braw.x >> 16)));
+      bv[2] = __half2float(__ushort_as_half((unsigned short)(braw.y & 0xFFFFu)));
+      bv[3] = __half2float(__ushort_as_half((unsigned short)(braw.y >> 16)));
+    }
+    uint32_t hv[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) hv[j] = __half_as_ushort(__float2half_rn(acc[4 * q + j] + bv[j]));
+    *reinterpret_cast<uint2*>(y + (size_t)mo * N + no) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+  }
+}
+
 // Workgroups that fit on the device at once (two per CU), cached per device.
 static int resident_blocks() {
   static int cached[64] = {0};
@@ -408,13 +514,24 @@ static int resident_blocks() {
   return cached[dev];
 }
 
+// Full rounds of the persistent kernel, then (when the remainder is at most a quarter of a
+// round) the remaining tiles as sub-tiles; otherwise the persistent kernel takes them all.
 template <int RB, bool BIAS>
 static hipError_t launch_g3(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  const int nb = tiles < resident_blocks() ? tiles : resident_blocks();
+  const int slots = resident_blocks();
+  const int rem = tiles % slots;
+  const int main_tiles = (tiles > slots && rem > 0 && 4 * rem <= slots) ? tiles - rem : tiles;
+  const int nb = main_tiles < slots ? main_tiles : slots;
   hipLaunchKernelGGL((k_gemm3<RB, BIAS>), dim3(nb), dim3(NT), 0, s, (const uint8_t*)a.xq,
                      (const __half*)a.xs, (const __half*)a.t, (const uint8_t*)a.wq, (const __half*)a.ws,
-                     (const __half*)a.l2, (const __half*)a.bias, a.M, a.N, a.K, (__half*)a.y);
+                     (const __half*)a.l2, (const __half*)a.bias, a.M, a.N, a.K, (__half*)a.y, main_tiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || main_tiles == tiles) return e;
+  hipLaunchKernelGGL((k_gemm3_tail<RB, BIAS>), dim3((tiles - main_tiles) * 16), dim3(NT), 0, s,
+                     (const uint8_t*)a.xq, (const __half*)a.xs, (const __half*)a.t, (const uint8_t*)a.wq,
+                     (const __half*)a.ws, (const __half*)a.l2, (const __half*)a.bias, a.M, a.N, a.K,
+                     (__half*)a.y, main_tiles);
   return hipGetLastError();
 }
 

@@ -150,6 +150,30 @@ def test_gemm_up_parity(fmt, M, K, N, r, with_bias):
     assert ok, worst
 
 
+@pytest.mark.parametrize("r,with_bias", [(32, True), (0, False), (64, True)])
+def test_gemm_e2m3_partial_last_round(r, with_bias):
+    # Tile counts just above a whole number of persistent rounds (two workgroups per CU): the
+    # last few 128 x 128 tiles go to the sub-tile kernel.  Ragged M (last tile 91 rows) and an
+    # odd number of K groups.
+    fmt = "int4_e2m3"
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N, K = 1024, 192
+    tiles_m = -(-(2 * cus + 8) // 8)
+    M = 128 * tiles_m - 37
+    log(f"gemm_w4a4_up tail round {fmt} M={M} K={K} N={N} r={r} CUs={cus}")
+    x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs(fmt, M, K, N, r, 4242 + r)
+    bias = b if with_bias else None
+    ref = oracle.forward.linear(xq, xs, t, wq, ws, l2, bias, fmt)
+    y = binding.svdq_gemm_w4a4_up(dev(dev_codes(xst, fmt)), dev(dev_scales(xs, fmt)), dev(t) if r else None,
+                                  dev(dev_codes(wst, fmt)), dev(dev_scales(ws, fmt)), dev(l2) if r else None,
+                                  dev(bias) if with_bias else None, K, fmt)
+    yg = host(y)
+    assert np.isfinite(yg.astype(np.float32)).all()
+    assert rel_fro(yg, ref) <= TOL
+    ok, worst = within_sum_bound(yg, ref, linear_abs_sum(xq, xs, t, wq, ws, l2, bias, fmt), K // 64 + r + 2)
+    assert ok, worst
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,K,N,r", [(17, 192, 48, 32), (130, 320, 272, 32), (257, 256, 144, 64), (1, 64, 16, 0)])
 def test_linear_end_to_end(fmt, M, K, N, r):
