@@ -30,10 +30,12 @@
 // registers, then issues the next stage's loads, then computes, so its LDS reads
 // never wait on loads in flight.  The last step of a tile loads the next tile's
 // first stage, which thus overlaps this tile's epilogue.
-// LDS keeps, per group and operand, bytes 0..15 of each (row, half) in one
-// 16-byte slot and bytes 8..23 in a second one (the slot order swizzled against
-// bank conflicts), so every MFMA operand is one 16-byte and one 8-byte LDS read
-// straight into its registers.  Scales arrive as one dword per row (the 2-byte
+// The container keeps, per (row, group), half 0's bytes 0..15, half 1's bytes
+// 0..15 and both halves' bytes 16..23 as three 16-byte chunks; LDS keeps each
+// chunk kind as an array over the tile's rows, so a row costs three 16-byte
+// loads, every MFMA operand is one 16-byte and one 8-byte LDS read straight into
+// its registers, and both the loads and the reads touch contiguous bytes (no
+// bank conflicts).  Scales arrive as one dword per row (the 2-byte
 // DMA form zero-extends), which with a zero register is the K-slot-0 operand;
 // the lanes of the upper K half read a zero block.
 // Tile order: each XCD (own L2) works on a contiguous range of tiles, rastered
@@ -46,17 +48,17 @@ namespace {
 
 constexpr int BM = 128, BN = 128, NT = 256, KC = 2;
 constexpr int GB = 48;                      // container bytes per (row, group)
-// LDS layout of one group (byte offsets)
-constexpr int L_XP0 = 0;                    // X: bytes 0..15 of each half, [128 rows][2 slots] x 16
-constexpr int L_XP1 = 4096;                 // X: bytes 8..23 of each half, [128 rows][2 slots] x 16
-constexpr int L_WP0 = 8192;                 // W: as X
-constexpr int L_WP1 = 12288;
-constexpr int L_SX = 16384;                 // X scales, one dword (fp16, zero-extended) per row
-constexpr int L_SW = 16896;                 // W scales
-constexpr int L_Z = 17408;                  // 128 zero bytes
-constexpr int GROUP = L_Z + 128;            // 17536
+// LDS layout of one group (byte offsets): per operand the three 16-byte chunks of each row's
+// 48 container bytes (half 0 bytes 0..15 | half 1 bytes 0..15 | both halves' bytes 16..23),
+// each chunk kind an array [128 rows] x 16
+constexpr int L_X = 0;                      // X chunks 0, 1, 2 at L_X + 2048 c
+constexpr int L_W = 6144;                   // W chunks
+constexpr int L_SX = 12288;                 // X scales, one dword (fp16, zero-extended) per row
+constexpr int L_SW = 12800;                 // W scales
+constexpr int L_Z = 13312;                  // 128 zero bytes
+constexpr int GROUP = L_Z + 128;            // 13440
 constexpr int STAGE = KC * GROUP;
-constexpr int RING = 2 * STAGE;             // 70144 bytes
+constexpr int RING = 2 * STAGE;             // 53760 bytes
 // epilogue: buffer 1 of the ring (buffer 0 already receives the next tile's stage 0)
 constexpr int E_L2 = STAGE;                 // L2^T staging, 128 columns x (r + 8) halves
 constexpr int E_Y = STAGE;                  // fp16 output staging, per wave 32 rows x 136 bytes
@@ -74,6 +76,8 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, size_t bytes) {
 
 // One wave's LDS-DMA load: lane l's 16 bytes (or 2 bytes, zero-extended to a dword) go to
 // dst + 16 l (dst + 4 l).  dst must be wave-uniform.
+// (The instruction's immediate offset would move the LDS destination too; offsets go into the
+// vector or scalar offset, which move only the global address.)
 __device__ __forceinline__ void dma16(rsrc_t r, uint8_t* dst, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)voff, (int)soff, 0, 0);
 }
@@ -87,13 +91,6 @@ __device__ __forceinline__ int opaque(int v) {
   asm volatile("" : "+v"(v));
   return v;
 }
-
-// LDS position of (row, half) in a 16-byte slot array [row][2]: the two halves of a row are
-// neighbours, swapped on a row-bit pattern so that both the loads (neighbouring lanes = the
-// two halves of one row) and the operand reads (neighbouring lanes = consecutive rows, one
-// half) touch distinct banks.
-__device__ __forceinline__ int swz(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
-__device__ __forceinline__ int slot16(int row, int half) { return row * 32 + 16 * (half ^ swz(row)); }
 
 // Tile index -> output tile: contiguous ranges per XCD (workgroups are dealt round-robin to
 // the 8 XCDs and keep their XCD), then 8-tile-row groups within a range.
@@ -131,20 +128,17 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
   const int G = K >> 6;
   const int NS = (G + KC - 1) / KC;          // stages of a tile
   const int NSE = (NS + 1) & ~1;             // rounded up to even: stage s uses buffer s % 2
-  const uint32_t gx_step = (uint32_t)M * GB, gw_step = (uint32_t)N * GB;   // bytes between groups
 
-  // ---- load assignment.  Code slots: lane l of wave w fills 16-byte slot l of rows
-  // 32 w .. 32 w + 31, i.e. row 32 w + l/2, slot l%2 (half = slot ^ swizzle).  Scales: wave w
-  // loads the 64 rows 64 (w%2) .. of the X (waves 0, 1) or W (waves 2, 3) side.  Rows past the
-  // edge re-read the tile's last valid row (their outputs are never stored).
-  const int crow = wave * 32 + (lane >> 1);
-  const int chalf = (lane & 1) ^ swz(crow);
+  // ---- load assignment: wave w loads rows 64 (w%2) + lane of the X (waves 0, 1) or W (waves
+  // 2, 3) tile: the three code chunks of the row and its scale.  Rows past the edge re-read
+  // the tile's last valid row (their outputs are never stored).
   const bool s_x = wave < 2;
-  const int srow = (wave & 1) * 64 + lane;
+  const int lrow = (wave & 1) * 64 + lane;
+  const uint32_t c_step = (uint32_t)(s_x ? M : N) * GB;   // bytes between groups
   const uint32_t s_step = (uint32_t)(s_x ? M : N) * 2;
-  struct Src {                               // where one tile's operands are read from
-    rsrc_t rx, rw, rs;
-    uint32_t vx, vw, vs;
+  struct Src {                               // where this wave reads one tile's operands
+    rsrc_t rc, rs;
+    uint32_t vc, vs;
   };
   auto tile_src = [&](int tile) {
     int tm_, tn_;
@@ -154,39 +148,39 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
     const int sr = s_x ? mr : nr;
     Src r;
     // codes are group-major [G][rows][48]: a tile's rows of one group are contiguous
-    r.rx = make_rsrc(xq + (size_t)m0_ * GB, ((size_t)(G - 1) * M + mr) * GB);
-    r.rw = make_rsrc(wq + (size_t)n0_ * GB, ((size_t)(G - 1) * N + nr) * GB);
+    r.rc = s_x ? make_rsrc(xq + (size_t)m0_ * GB, ((size_t)(G - 1) * M + mr) * GB)
+               : make_rsrc(wq + (size_t)n0_ * GB, ((size_t)(G - 1) * N + nr) * GB);
     r.rs = make_rsrc(s_x ? (const void*)(xs + m0_) : (const void*)(ws + n0_),
                      ((size_t)(G - 1) * (s_x ? M : N) + sr) * 2);
-    r.vx = (uint32_t)min(crow, mr - 1) * GB + 24u * chalf;
-    r.vw = (uint32_t)min(crow, nr - 1) * GB + 24u * chalf;
-    r.vs = (uint32_t)min(srow, sr - 1) * 2;
+    r.vc = (uint32_t)min(lrow, sr - 1) * GB;
+    r.vs = (uint32_t)min(lrow, sr - 1) * 2;
     return r;
   };
-  // all loads of one stage into LDS buffer buf (5 per wave and group)
+  // all loads of one stage into LDS buffer buf (4 per wave and group)
   auto load_stage = [&](const Src& src, int st, int buf) {
 #pragma unroll
     for (int k = 0; k < KC; k++) {
       const int g = min(st * KC + k, G - 1);   // a group past the end re-reads the last one (unused)
-      uint8_t* b = lds + buf * STAGE + k * GROUP;
-      const uint32_t sox = (uint32_t)g * gx_step, sow = (uint32_t)g * gw_step;
-      dma16(src.rx, b + L_XP0 + wave * 1024, src.vx, sox);
-      dma16(src.rx, b + L_XP1 + wave * 1024, src.vx + 8, sox);
-      dma16(src.rw, b + L_WP0 + wave * 1024, src.vw, sow);
-      dma16(src.rw, b + L_WP1 + wave * 1024, src.vw + 8, sow);
-      dma2(src.rs, b + (s_x ? L_SX : L_SW) + (wave & 1) * 256, src.vs, (uint32_t)g * s_step);
+      uint8_t* b = lds + buf * STAGE + k * GROUP + (s_x ? L_X : L_W) + (wave & 1) * 1024;
+      const uint32_t so = (uint32_t)g * c_step;
+      dma16(src.rc, b, src.vc, so);
+      dma16(src.rc, b + 2048, src.vc, so + 16);
+      dma16(src.rc, b + 4096, src.vc, so + 32);
+      dma2(src.rs, lds + buf * STAGE + k * GROUP + (s_x ? L_SX : L_SW) + (wave & 1) * 256, src.vs,
+           (uint32_t)g * s_step);
     }
   };
   auto wait_loads = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   // per-lane LDS read bases (tile, group and stage offsets are immediates)
+  // (operand of lane (row, half h): chunk h of the row, then the 8 bytes at 8 h of chunk 2)
   int rx_p0[2], rx_p1[2], rw_p0[2], rw_p1[2], rs_x[2], rs_w[2];
 #pragma unroll
   for (int i = 0; i < 2; i++) {
-    rx_p0[i] = slot16(wm * 64 + i * 32 + r32, h);
-    rw_p0[i] = slot16(wn * 64 + i * 32 + r32, h);
-    rx_p1[i] = opaque(slot16(wm * 64 + i * 32 + r32, h) + 8);
-    rw_p1[i] = opaque(slot16(wn * 64 + i * 32 + r32, h) + 8);
+    rx_p0[i] = L_X + 2048 * h + (wm * 64 + i * 32 + r32) * 16;
+    rw_p0[i] = L_W + 2048 * h + (wn * 64 + i * 32 + r32) * 16;
+    rx_p1[i] = opaque(L_X + 4096 + (wm * 64 + i * 32 + r32) * 16 + 8 * h);
+    rw_p1[i] = opaque(L_W + 4096 + (wn * 64 + i * 32 + r32) * 16 + 8 * h);
     rs_x[i] = opaque(h ? L_Z + r32 * 4 : L_SX + (wm * 64 + i * 32 + r32) * 4);
     rs_w[i] = opaque(h ? L_Z + r32 * 4 : L_SW + (wn * 64 + i * 32 + r32) * 4);
   }
@@ -211,10 +205,10 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
   auto read_ops = [&](const uint8_t* b, Ops& o) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
-      const uint4 x0 = *reinterpret_cast<const uint4*>(b + L_XP0 + rx_p0[i]);
-      const uint2 x1 = *reinterpret_cast<const uint2*>(b + L_XP1 + rx_p1[i]);
-      const uint4 w0 = *reinterpret_cast<const uint4*>(b + L_WP0 + rw_p0[i]);
-      const uint2 w1 = *reinterpret_cast<const uint2*>(b + L_WP1 + rw_p1[i]);
+      const uint4 x0 = *reinterpret_cast<const uint4*>(b + rx_p0[i]);
+      const uint2 x1 = *reinterpret_cast<const uint2*>(b + rx_p1[i]);
+      const uint4 w0 = *reinterpret_cast<const uint4*>(b + rw_p0[i]);
+      const uint2 w1 = *reinterpret_cast<const uint2*>(b + rw_p1[i]);
       o.xo[i][0] = (int)x0.x; o.xo[i][1] = (int)x0.y; o.xo[i][2] = (int)x0.z; o.xo[i][3] = (int)x0.w;
       o.xo[i][4] = (int)x1.x; o.xo[i][5] = (int)x1.y;
       o.wo[i][0] = (int)w0.x; o.wo[i][1] = (int)w0.y; o.wo[i][2] = (int)w0.z; o.wo[i][3] = (int)w0.w;
@@ -422,12 +416,12 @@ k_gemm3_tail(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, cons
   typedef _Float16 v4h_t __attribute__((ext_vector_type(4)));
   struct Op { uint4 x0, w0; uint2 x1, w1; uint32_t sx, sw; };
   auto load = [&](int g, Op& o) {
-    const uint8_t* px = xq + ((size_t)g * M + m) * GB + 24 * h;
-    const uint8_t* pw = wq + ((size_t)g * N + n) * GB + 24 * h;
-    o.x0 = *reinterpret_cast<const uint4*>(px);
-    o.x1 = *reinterpret_cast<const uint2*>(px + 16);
-    o.w0 = *reinterpret_cast<const uint4*>(pw);
-    o.w1 = *reinterpret_cast<const uint2*>(pw + 16);
+    const uint8_t* px = xq + ((size_t)g * M + m) * GB;
+    const uint8_t* pw = wq + ((size_t)g * N + n) * GB;
+    o.x0 = *reinterpret_cast<const uint4*>(px + 16 * h);
+    o.x1 = *reinterpret_cast<const uint2*>(px + 32 + 8 * h);
+    o.w0 = *reinterpret_cast<const uint4*>(pw + 16 * h);
+    o.w1 = *reinterpret_cast<const uint2*>(pw + 32 + 8 * h);
     // K slot 0 holds the scale for the lower-K-half lanes; the upper half contributes zeros
     o.sx = h ? 0u : (uint32_t)reinterpret_cast<const unsigned short*>(xs)[(size_t)g * M + m];
     o.sw = h ? 0u : (uint32_t)reinterpret_cast<const unsigned short*>(ws)[(size_t)g * N + n];

@@ -121,10 +121,10 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
             *reinterpret_cast<uint32_t*>(srow + 4 * sub) = w0;
             *reinterpret_cast<uint32_t*>(srow + 16 + 4 * sub) = w1;
           } else if (FMT == FMT_INT4_E2M3) {
-            // 6-bit container: group c occupies 48 bytes of the row, half h (codes 32h..32h+31)
-            // 24 bytes; this lane's 8 codes of each half are fields 8 sub .. 8 sub + 7, i.e. the
-            // 6 bytes at offset 6 sub of the half.
-            uint8_t* dst = srow + 6 * sub;
+            // 6-bit container: a (row, group) has 48 bytes; half h (codes 32h..32h+31) is 24
+            // bytes of 6-bit fields whose bytes 0..15 sit at 16h and bytes 16..23 at 32 + 8h.
+            // This lane's 8 codes of each half are fields 8 sub .. 8 sub + 7: the 6 bytes at
+            // offset 6 sub of the half, written as three 16-bit pieces (none crosses byte 16).
 #pragma unroll
             for (int hh = 0; hh < 2; hh++) {
               uint32_t lo = 0;                   // bits 0..31 of the 48-bit run
@@ -134,13 +134,12 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
               lo |= f5 << 30;
               // bits 32..47
               const uint32_t hi = (f5 >> 2) | (e2m3_field(q[8 * hh + 6]) << 4) | (e2m3_field(q[8 * hh + 7]) << 10);
-              uint8_t* d = dst + 24 * hh;
-              if ((sub & 1) == 0) {
-                *reinterpret_cast<uint32_t*>(d) = lo;
-                *reinterpret_cast<uint16_t*>(d + 4) = (uint16_t)hi;
-              } else {
-                *reinterpret_cast<uint16_t*>(d) = (uint16_t)lo;
-                *reinterpret_cast<uint32_t*>(d + 2) = (lo >> 16) | (hi << 16);
+              const uint32_t piece[3] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu};
+#pragma unroll
+              for (int j = 0; j < 3; j++) {
+                const int o = 6 * sub + 2 * j;   // byte offset within the half (even)
+                const int pos = o < 16 ? 16 * hh + o : 32 + 8 * hh + (o - 16);
+                *reinterpret_cast<uint16_t*>(srow + pos) = (uint16_t)piece[j];
               }
             }
           } else {

@@ -52,10 +52,12 @@ k_quant_weight(const float* __restrict__ r_t, int N, int K, uint8_t* __restrict_
         wv[6 * hh + 4] = (uint32_t)(f[2] >> 32) | (uint32_t)(f[3] << 16);
         wv[6 * hh + 5] = (uint32_t)(f[3] >> 16);
       }
-      uint4* dst = reinterpret_cast<uint4*>(wq + ((size_t)g * N + n) * 48);   // group-major [K/64][N][48]
+      // group-major [K/64][N][48]; within the 48 bytes: half 0 bytes 0..15, half 1 bytes 0..15,
+      // half 0 bytes 16..23, half 1 bytes 16..23
+      uint4* dst = reinterpret_cast<uint4*>(wq + ((size_t)g * N + n) * 48);
       dst[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-      dst[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
-      dst[2] = make_uint4(wv[8], wv[9], wv[10], wv[11]);
+      dst[1] = make_uint4(wv[6], wv[7], wv[8], wv[9]);
+      dst[2] = make_uint4(wv[4], wv[5], wv[10], wv[11]);
     } else if (FMT == FMT_INT4) {
       uint32_t* dst = reinterpret_cast<uint32_t*>(wq + (size_t)n * (K >> 1) + (size_t)g * (G >> 1));
 #pragma unroll

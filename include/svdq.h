@@ -54,9 +54,12 @@
  *                  storage the gfx950 FP6 matrix cores read directly: each code
  *                  q becomes the 6-bit E2M3 pattern of q/8 (a subnormal:
  *                  sign<<5 | |q|).  A row takes 48 bytes per group of 64:
- *                  bytes [0, 24) hold codes 0..31 of the group and [24, 48)
- *                  codes 32..63, code j of a half in bits [6j, 6j+6) of the
- *                  little-endian 24 bytes.  Codes and scales are group-major:
+ *                  each half of the group (codes 0..31, 32..63) is a 24-byte
+ *                  little-endian field string, code j of the half in bits
+ *                  [6j, 6j+6); the 48 bytes hold half 0 bytes 0..15, half 1
+ *                  bytes 0..15, half 0 bytes 16..23, half 1 bytes 16..23 (so
+ *                  each half is one 16-byte and one 8-byte aligned piece).
+ *                  Codes and scales are group-major:
  *                  codes [K/64][rows][48 bytes] (the group-g slice of row i at
  *                  byte (g * rows + i) * 48; 3K/4 bytes per row in total),
  *                  fp16 scales [K/64][rows].  The 4-bit values

@@ -44,12 +44,16 @@ def same_bytes(a, b):
 
 
 def dev_codes(stored, fmt):
-    """Codes in the device layout of the format: the E2M3 container is group-major
-    [K/64][rows][48]; the oracle stores it row by row."""
+    """Codes in the device layout of the format.  The E2M3 container is group-major
+    [K/64][rows][48] with the bytes of a group ordered half 0 [0:16], half 1 [0:16],
+    half 0 [16:24], half 1 [16:24]; the oracle stores it row by row, each half's 24 bytes
+    contiguous."""
     if fmt != "int4_e2m3":
         return stored
     rows = stored.shape[0]
-    return np.ascontiguousarray(stored.reshape(rows, -1, 48).transpose(1, 0, 2))
+    g = stored.reshape(rows, -1, 48)
+    g = np.concatenate([g[..., 0:16], g[..., 24:40], g[..., 16:24], g[..., 40:48]], axis=-1)
+    return np.ascontiguousarray(g.transpose(1, 0, 2))
 
 
 def dev_scales(s, fmt):
