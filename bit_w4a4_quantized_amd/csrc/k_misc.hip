@@ -1,7 +1,4 @@
 // Control and glue kernels around the fused layer:
-//   * W4A16 control: fp16 activations times int4 group-64 weights (practice
-//     page "sota-314", sections "Do this" and "What it buys": the W4A16
-//     baseline and the layers that stay W4A16);
 //   * up projection as a separate kernel, for the unfused comparison
 //     ("sota-314", "Do this", latency table);
 //   * GELU(tanh) + smoothing glue between an MLP's two linears.
@@ -9,103 +6,6 @@
 #include "quant_core.h"
 
 namespace svdq {
-
-// ---------------------------------------------------------------- W4A16
-// Tile 128 x 128, four waves of 64 x 64, v_mfma_f32_32x32x16_f16.  The int4
-// codes become exact fp16 integers (fp16 1024 + (q + 8), minus 1032, packed
-// fp16 arithmetic); per group of 64 the fp32 partial X q is scaled by the
-// column's fp16 scale, so the product is that of the exact dequantized weight.
-__device__ __forceinline__ uint32_t nib2_to_h2(uint32_t w, int j) {
-  const uint32_t u = ((w >> (8 * j)) & 0xFu) | (((w >> (8 * j + 4)) & 0xFu) << 16);
-  __half2 hv = __halves2half2(__ushort_as_half((unsigned short)((u ^ 0x6408u) & 0xFFFFu)),
-                              __ushort_as_half((unsigned short)(((u >> 16) ^ 0x6408u) & 0xFFFFu)));
-  hv = __hsub2(hv, __half2half2(__float2half(1032.0f)));
-  uint32_t r;
-  __builtin_memcpy(&r, &hv, 4);
-  return r;
-}
-
-template <bool BIAS>
-__global__ void __launch_bounds__(256)
-k_w4a16(const __half* __restrict__ x, const uint8_t* __restrict__ wq, const __half* __restrict__ ws,
-        const __half* __restrict__ bias, int M, int N, int K, __half* __restrict__ y) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = lane >> 5, l32 = lane & 31;
-  const int m_base = blockIdx.y * 128 + (wave >> 1) * 64;
-  const int n_base = blockIdx.x * 128 + (wave & 1) * 64;
-  int arow[2], bcol[2];
-  bool aok[2], bok[2];
-#pragma unroll
-  for (int i = 0; i < 2; i++) {
-    arow[i] = m_base + i * 32 + l32; aok[i] = arow[i] < M;
-    bcol[i] = n_base + i * 32 + l32; bok[i] = bcol[i] < N;
-  }
-  v16f acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; a++)
-#pragma unroll
-    for (int b = 0; b < 2; b++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
-  const int ngroups = K >> 6;
-  for (int g = 0; g < ngroups; g++) {
-    v16f p[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; a++)
-#pragma unroll
-      for (int b = 0; b < 2; b++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) p[a][b][i] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++) {
-      const int k0 = g * 64 + ks * 16 + 8 * h;
-      uint4 av[2], bv[2];
-#pragma unroll
-      for (int i = 0; i < 2; i++) {
-        av[i] = aok[i] ? *reinterpret_cast<const uint4*>(x + (size_t)arow[i] * K + k0) : make_uint4(0, 0, 0, 0);
-        const uint32_t w = bok[i] ? *reinterpret_cast<const uint32_t*>(wq + (size_t)bcol[i] * (K >> 1) + (k0 >> 1)) : 0u;
-        bv[i] = make_uint4(nib2_to_h2(w, 0), nib2_to_h2(w, 1), nib2_to_h2(w, 2), nib2_to_h2(w, 3));
-      }
-#pragma unroll
-      for (int a = 0; a < 2; a++)
-#pragma unroll
-        for (int b = 0; b < 2; b++)
-          p[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(av[a]), as_h8(bv[b]), p[a][b], 0, 0, 0);
-    }
-#pragma unroll
-    for (int b = 0; b < 2; b++) {
-      const float s = bok[b] ? __half2float(ws[(size_t)bcol[b] * ngroups + g]) : 0.f;
-#pragma unroll
-      for (int a = 0; a < 2; a++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) acc[a][b][i] = __builtin_fmaf(p[a][b][i], s, acc[a][b][i]);
-    }
-  }
-#pragma unroll
-  for (int b = 0; b < 2; b++) {
-    if (!bok[b]) continue;
-    const float bv = BIAS ? __half2float(bias[bcol[b]]) : 0.f;
-#pragma unroll
-    for (int a = 0; a < 2; a++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int mrow = m_base + a * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (mrow < M) y[(size_t)mrow * N + bcol[b]] = __float2half_rn(acc[a][b][i] + bv);
-      }
-  }
-}
-
-hipError_t launch_w4a16(const void* x, const void* wq, const void* ws, const void* bias, int M, int N,
-                        int K, void* y, hipStream_t s) {
-  dim3 grid((N + 127) / 128, (M + 127) / 128);
-  if (bias)
-    hipLaunchKernelGGL(k_w4a16<true>, grid, dim3(256), 0, s, (const __half*)x, (const uint8_t*)wq,
-                       (const __half*)ws, (const __half*)bias, M, N, K, (__half*)y);
-  else
-    hipLaunchKernelGGL(k_w4a16<false>, grid, dim3(256), 0, s, (const __half*)x, (const uint8_t*)wq,
-                       (const __half*)ws, (const __half*)nullptr, M, N, K, (__half*)y);
-  return hipGetLastError();
-}
 
 // ---------------------------------------------------------------- up projection (unfused)
 // Y = fp16( float(Y0) + T L2 ): reads the fp16 output of the bare GEMM back.

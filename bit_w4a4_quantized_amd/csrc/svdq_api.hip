@@ -206,7 +206,8 @@ svdq_status svdq_gemm_w4a16(const void* x, const void* wq, const void* ws, const
   if (!x || !wq || !ws || !y) return SVDQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(wq) || !aligned16(ws) || !aligned16(y)) return SVDQ_ERR_ALIGN;
   if (bias && !aligned16(bias)) return SVDQ_ERR_ALIGN;
-  if (M == 0 || N == 0) return SVDQ_OK;
+  // the kernel addresses X and the codes with 32-bit byte offsets
+  if ((size_t)M * K * 2 >= (1ull << 32) || (size_t)N * K / 2 >= (1ull << 32)) return SVDQ_ERR_SHAPE;
   return map_launch(launch_w4a16(x, wq, ws, bias, M, N, K, y, static_cast<hipStream_t>(stream)));
 }
 

@@ -99,6 +99,23 @@ def within_sum_bound(got, ref, abs_sum, n_terms, extra=0.0):
     return bool(np.all(np.abs(got - ref) <= bound)), float(np.max(np.abs(got - ref) - bound, initial=-np.inf))
 
 
+def w4a16_bound_terms(x, q, s, bias):
+    """(abs_sum, n_terms, extra) for within_sum_bound on the W4A16 control.  The
+    kernel rounds each dequantized weight q s to fp16 once before its fp16
+    matrix multiply (the usual weight-only arithmetic), while the oracle keeps
+    q s exact: |fp16(w) - w| <= 2^-11 |w| + 2^-25 (the second term for fp16
+    subnormals), so the inputs of the sum differ by at most
+    2^-11 sum|x||w| + 2^-25 sum|x|."""
+    xa = np.abs(np.asarray(x, np.float64))
+    wa = np.abs(oracle.quant.dequantize(q, s, "int4"))
+    xw = xa @ wa.T
+    absum = xw * (1.0 + 2.0 ** -11) + 2.0 ** -25 * xa.sum(axis=1, keepdims=True)
+    if bias is not None:
+        absum = absum + np.abs(np.asarray(bias, np.float64))[None, :]
+    extra = 2.0 ** -11 * xw + 2.0 ** -25 * xa.sum(axis=1, keepdims=True)
+    return absum, xa.shape[1] + 2, extra
+
+
 def linear_abs_sum(xq, xs, t, wq, ws, l2, bias, fmt):
     """sum |terms| of Y = deq(xq) deq(wq)^T + T L2 + b, elementwise (float64)."""
     xd = np.abs(oracle.quant.dequantize(xq, xs, fmt))

@@ -16,7 +16,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 import oracle  # noqa: E402
 from bit_w4a4_quantized_amd import binding  # noqa: E402
 from tests.layers import (log, prepared, raw_layer, reference, rel_fro, within_sum_bound,  # noqa: E402
-                          linear_abs_sum, branch_slack)
+                          linear_abs_sum, branch_slack, w4a16_bound_terms)
 
 TOL = 1e-3
 
@@ -149,8 +149,7 @@ def test_c3_w4a16_control():
     err = rel_fro(y, ref)
     log(f"  w4a16 rel_fro={err:.3e}")
     assert err <= TOL
-    absum = np.abs(L.x.astype(np.float64)) @ np.abs(oracle.quant.dequantize(q, s, "int4")).T + np.abs(L.b.astype(np.float64))
-    ok, worst = within_sum_bound(y, ref, absum, L.x.shape[1] + 2)
+    ok, worst = within_sum_bound(y, ref, *w4a16_bound_terms(L.x, q, s, L.b))
     assert ok, worst
 
 

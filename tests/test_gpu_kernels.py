@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 import oracle  # noqa: E402
 from bit_w4a4_quantized_amd import binding  # noqa: E402
-from tests.layers import log, rel_fro, fp16_ulp_diff, within_sum_bound, linear_abs_sum  # noqa: E402
+from tests.layers import log, rel_fro, fp16_ulp_diff, within_sum_bound, linear_abs_sum, w4a16_bound_terms  # noqa: E402
 
 TOL = 1e-3
 
@@ -231,7 +231,7 @@ def test_unfused_matches_fused(fmt):
     assert rel_fro(y0, ref0) <= TOL
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 64, 16), (130, 320, 272), (300, 256, 144)])
+@pytest.mark.parametrize("M,K,N", [(1, 64, 16), (130, 320, 272), (300, 256, 144), (2100, 128, 4096)])
 def test_w4a16_parity(M, K, N):
     g = np.random.default_rng(M * N)
     x = g.standard_normal((M, K)).astype(np.float16)
@@ -242,8 +242,7 @@ def test_w4a16_parity(M, K, N):
     y = binding.svdq_gemm_w4a16(dev(x), dev(st), dev(s), dev(b))
     yg = host(y)
     assert rel_fro(yg, ref) <= TOL
-    absum = np.abs(x.astype(np.float64)) @ np.abs(oracle.quant.dequantize(q, s, "int4")).T + np.abs(b.astype(np.float64))
-    ok, worst = within_sum_bound(yg, ref, absum, K + 2)
+    ok, worst = within_sum_bound(yg, ref, *w4a16_bound_terms(x, q, s, b))
     assert ok, worst
 
 
