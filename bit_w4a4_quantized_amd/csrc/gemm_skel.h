@@ -1,0 +1,256 @@
+// Persistent LDS-DMA GEMM skeleton for gfx950, shared by the INT8 and FP4
+// Kernel B variants: workgroup tile 128 x 128, four waves in 2 x 2 of 64 x 64
+// (2 x 2 MFMA tiles of 32 x 32 each), two workgroups per CU, each looping over
+// tiles.  K advances in stages through two LDS buffers that are filled straight
+// from global memory by LDS-DMA buffer loads one stage ahead: a step reads its
+// stage's operands into registers, issues the next stage's loads (the next
+// tile's first stage after a tile's last step, so those loads overlap the
+// epilogue), computes, waits for its loads and synchronises.
+//
+// The accumulators acc[tj][ti] hold the tile product with the weight tile as
+// the MFMA row operand and the activation tile as the column operand: lane
+// (r32, h) owns output row m = ti*32 + r32 and columns 8(v/4) + 4h + v%4 of
+// tile tj.  The epilogue adds the low-rank up projection T L2 (fp16 matrix
+// cores, L2 staged transposed through LDS) and the bias, rounds to fp16 and
+// writes 16-byte row pieces through LDS ("sota-314", "Do this": the up
+// projection shares the 4-bit kernel's output).
+//
+// A format supplies an operator type Op with
+//   static constexpr int BUF;                       LDS bytes of one stage buffer
+//   int NS;                                         stages per tile
+//   struct Src; Src src(int m0, int n0);            per-lane global offsets of a tile
+//   void load(const Src&, int st, uint8_t* buf);    the stage's LDS-DMA loads
+//   struct Regs; void read(const uint8_t* buf, int st, Regs&);
+//   void mma(const Regs&, int st, v16f (&acc)[2][2]);
+#pragma once
+#include "kernels.h"
+
+namespace svdq {
+namespace skel {
+
+constexpr int BM = 128, BN = 128, NT = 256;
+constexpr int E_YS = 136;                   // output staging: per wave 32 rows x 136 bytes
+
+__host__ __device__ constexpr int epi_bytes(int R) {
+  return BN * (R + 8) * 2 > 4 * 32 * E_YS ? BN * (R + 8) * 2 : 4 * 32 * E_YS;
+}
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, size_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)n, 0x00020000);
+}
+
+// One wave's LDS-DMA load: lane l's 16 (4) bytes go to dst + 16 l (dst + 4 l); 2 bytes are
+// zero-extended to the dword at dst + 4 l.  dst must be wave-uniform.  Offsets go into the
+// vector or scalar offset (the immediate would move the LDS destination as well).
+__device__ __forceinline__ void dma16(rsrc_t r, uint8_t* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)voff, (int)soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(rsrc_t r, uint8_t* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, (int)voff, (int)soff, 0, 0);
+}
+__device__ __forceinline__ void dma2(rsrc_t r, uint8_t* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 2, (int)voff, (int)soff, 0, 0);
+}
+
+// Tile index -> output tile: contiguous ranges per XCD (workgroups are dealt round-robin to
+// the 8 XCDs and keep their XCD), then 8-tile-row groups within a range.
+__device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, int* tm, int* tn) {
+  const int n8 = nblocks & ~7;
+  int lid = bid;
+  if (bid < n8) lid = (bid & 7) * (n8 >> 3) + (bid >> 3);
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int grp = lid / per_group;
+  const int first_m = grp * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int in = lid - grp * per_group;
+  *tm = first_m + in % gm;
+  *tn = in / gm;
+}
+
+// The scale-product operand of v_mfma_f32_32x32x8_f16: the row's fp16 scale in K slot 0 for
+// the lower half of the lanes, zeros elsewhere, so the MFMA returns sw[n] sx[m] exactly.
+typedef _Float16 v4h_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4h_t scale_operand(uint32_t s, int h) {
+  return __builtin_bit_cast(v4h_t, make_uint2(h ? 0u : (s & 0xFFFFu), 0u));
+}
+
+// acc += T L2 (RB > 0), bias, fp16 store.  eb: this workgroup's epilogue LDS (epi_bytes(R)),
+// free of loads in flight.  Ends with a workgroup barrier.
+template <int RB, bool BIAS>
+__device__ __forceinline__ void epilogue(v16f (&acc)[2][2], uint8_t* eb, const __half* __restrict__ t,
+                                         const __half* __restrict__ l2, const __half* __restrict__ bias,
+                                         int M, int N, int m0, int n0, __half* __restrict__ y) {
+  constexpr int R = RB * 16;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, r32 = lane & 31;
+  const int wm = wave >> 1, wn = wave & 1;
+  if (RB > 0) {
+    // L2[:, n0:n0+128] transposed into LDS as [n][k] (row stride R + 8 halves); row operand
+    // L2^T (columns n), column operand T (rows m, 8 consecutive k per lane)
+    constexpr int LS2 = (R + 8) * 2;
+    for (int idx = tid; idx < R * (BN / 8); idx += NT) {
+      const int k = idx % R, c8 = idx / R;
+      const int n = n0 + c8 * 8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (n < N) v = *reinterpret_cast<const uint4*>(l2 + (size_t)k * N + n);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; e++)
+        *reinterpret_cast<uint16_t*>(eb + (c8 * 8 + e) * LS2 + k * 2) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
+    uint4 top[RB > 0 ? RB : 1][2];
+#pragma unroll
+    for (int kb = 0; kb < RB; kb++)
+#pragma unroll
+      for (int ti = 0; ti < 2; ti++) {
+        const int m = min(m0 + wm * 64 + ti * 32 + r32, M - 1);
+        top[kb][ti] = *reinterpret_cast<const uint4*>(t + (size_t)m * R + kb * 16 + 8 * h);
+      }
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < RB; kb++)
+#pragma unroll
+      for (int tj = 0; tj < 2; tj++) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(eb + (wn * 64 + tj * 32 + r32) * LS2 + (kb * 16 + 8 * h) * 2);
+#pragma unroll
+        for (int ti = 0; ti < 2; ti++)
+          acc[tj][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(lo), as_h8(top[kb][ti]), acc[tj][ti], 0, 0, 0);
+      }
+    __syncthreads();                         // the output staging reuses the L2 staging bytes
+  }
+  float bv[2][4][4];
+#pragma unroll
+  for (int tj = 0; tj < 2; tj++)
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) bv[tj][q][j] = 0.f;
+      if (BIAS) {
+        const int n = n0 + wn * 64 + tj * 32 + 8 * q + 4 * h;
+        if (n < N) {
+          const uint2 braw = *reinterpret_cast<const uint2*>(bias + n);
+          bv[tj][q][0] = __half2float(__ushort_as_half((unsigned short)(braw.x & 0xFFFFu)));
+          bv[tj][q][1] = __half2float(__ushort_as_half((unsigned short)(braw.x >> 16)));
+          bv[tj][q][2] = __half2float(__ushort_as_half((unsigned short)(braw.y & 0xFFFFu)));
+          bv[tj][q][3] = __half2float(__ushort_as_half((unsigned short)(braw.y >> 16)));
+        }
+      }
+    }
+  uint8_t* ys = eb + wave * 32 * E_YS;
+#pragma unroll
+  for (int ti = 0; ti < 2; ti++) {
+#pragma unroll
+    for (int tj = 0; tj < 2; tj++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int nl = tj * 32 + 8 * q + 4 * h;    // column within the wave's 64
+        uint32_t hv[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) hv[j] = __half_as_ushort(__float2half_rn(acc[tj][ti][4 * q + j] + bv[tj][q][j]));
+        *reinterpret_cast<uint2*>(ys + r32 * E_YS + nl * 2) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int it = 0; it < 4; it++) {
+      const int rl = it * 8 + (lane >> 3), c = (lane & 7) * 8;   // row within the 32, column
+      const uint2 a = *reinterpret_cast<const uint2*>(ys + rl * E_YS + c * 2);
+      const uint2 b = *reinterpret_cast<const uint2*>(ys + rl * E_YS + c * 2 + 8);
+      const int m = m0 + wm * 64 + ti * 32 + rl, n = n0 + wn * 64 + c;
+      if (m < M && n < N) *reinterpret_cast<uint4*>(y + (size_t)m * N + n) = make_uint4(a.x, a.y, b.x, b.y);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  __syncthreads();                           // the buffer is refilled by the next tile's loads
+}
+
+// The persistent loop: tiles blockIdx.x, blockIdx.x + gridDim.x, ... below tiles_run.
+// lds: 2 Op::BUF bytes; the epilogue uses buffer 1 (buffer 0 already receives the next
+// tile's stage 0).
+template <class Op, int RB, bool BIAS>
+__device__ __forceinline__ void persistent(Op& op, uint8_t* lds, const __half* __restrict__ t,
+                                           const __half* __restrict__ l2, const __half* __restrict__ bias,
+                                           int M, int N, int tiles_run, __half* __restrict__ y) {
+  static_assert(Op::BUF >= epi_bytes(RB * 16), "the epilogue must fit one stage buffer");
+  static_assert(Op::BUF % 16 == 0, "16-byte aligned buffers");
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int tiles = tiles_m * tiles_n;
+  const int NS = op.NS;
+  const int NSE = (NS + 1) & ~1;             // rounded up to even: stage s uses buffer s % 2
+  auto origin = [&](int tile, int* m0, int* n0) {
+    int tm, tn;
+    tile_of(tile, tiles, tiles_m, tiles_n, &tm, &tn);
+    *m0 = tm * BM;
+    *n0 = tn * BN;
+  };
+  auto wait_loads = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+  int tile = blockIdx.x;
+  int m0, n0;
+  origin(tile, &m0, &n0);
+  typename Op::Src cur = op.src(m0, n0);
+  op.load(cur, 0, lds);
+  typename Op::Regs regs;
+  v16f acc[2][2];
+  while (true) {
+    const int next = tile + (int)gridDim.x;
+    const bool has_next = next < tiles_run;
+    int m1, n1;
+    origin(has_next ? next : tile, &m1, &n1);
+    const typename Op::Src nxt = op.src(m1, n1);
+    wait_loads();
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+      for (int b = 0; b < 2; b++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
+
+    auto step = [&](int st, int buf) {
+      if (st < NS) op.read(lds + buf * Op::BUF, st, regs);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + 1 < NS) op.load(cur, st + 1, lds + (buf ^ 1) * Op::BUF);
+      else if (st + 1 == NSE && has_next) op.load(nxt, 0, lds + (buf ^ 1) * Op::BUF);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st < NS) op.mma(regs, st, acc);
+      if (st + 1 < NSE) wait_loads();        // the last step's loads land during the epilogue
+      __syncthreads();
+    };
+    for (int st = 0; st < NSE; st += 2) {
+      step(st, 0);
+      step(st + 1, 1);
+    }
+    epilogue<RB, BIAS>(acc, lds + Op::BUF, t, l2, bias, M, N, m0, n0, y);
+    if (!has_next) break;
+    tile = next;
+    m0 = m1;
+    n0 = n1;
+    cur = nxt;
+  }
+}
+
+// Workgroups that stay resident: two per CU.
+inline int resident_blocks() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = 2 * cus;
+  }
+  return cached[dev];
+}
+
+}  // namespace skel
+}  // namespace svdq

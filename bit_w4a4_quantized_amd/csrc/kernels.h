@@ -54,6 +54,8 @@ hipError_t launch_quant_down(const QuantDownArgs& a, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm2(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm3(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_i8(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_f4(const GemmArgs& a, hipStream_t s);
 hipError_t launch_quant_weight(const float* r_t, int N, int K, int fmt, void* wq, void* ws, hipStream_t s);
 
 // unfused comparison pieces

@@ -74,9 +74,8 @@ svdq_status check_gemm(const void* xq, const void* xs, const void* t, const void
   if (!fmt_ok(fmt)) return SVDQ_ERR_FORMAT;
   svdq_status st = check_dims(M, N, K, r);
   if (st != SVDQ_OK) return st;
-  // the 6-bit container kernel addresses each code operand with 32-bit byte offsets
-  if (fmt == SVDQ_INT4_G64_E2M3 &&
-      ((size_t)M * code_bytes(K, (svdq_format)fmt) >= (1ull << 32) ||
+  // the GEMM kernels address each code operand with 32-bit byte offsets
+  if (((size_t)M * code_bytes(K, (svdq_format)fmt) >= (1ull << 32) ||
        (size_t)N * code_bytes(K, (svdq_format)fmt) >= (1ull << 32)))
     return SVDQ_ERR_SHAPE;
   if (M == 0 || N == 0) return SVDQ_OK;

@@ -32,8 +32,9 @@
  *    and the other dimensions check out, and the pointers may then be NULL,
  *    as a zero-size tensor's are); K > 0 with
  *    K % 64 == 0; N % 16 == 0; r % 16 == 0 and 0 <= r <= 64; M, N, K <= 2^24;
- *    with SVDQ_INT4_G64_E2M3 the GEMM also needs each code operand (M * 3K/4
- *    and N * 3K/4 bytes) below 4 GiB.
+ *    the GEMM entry points also need each code operand (M and N times the
+ *    format's code bytes per row) below 4 GiB, and the W4A16 control needs
+ *    M * 2K and N * K/2 bytes below 4 GiB.
  *  - Non-finite inputs are undefined behaviour.
  *
  * Formats (group quantization along K; groups per token row for activations,

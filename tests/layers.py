@@ -99,6 +99,15 @@ def within_sum_bound(got, ref, abs_sum, n_terms, extra=0.0):
     return bool(np.all(np.abs(got - ref) <= bound)), float(np.max(np.abs(got - ref) - bound, initial=-np.inf))
 
 
+def gemm_terms(fmt, K, r):
+    """Terms of the fp32 sum behind one output of Kernel B, for within_sum_bound: per-group
+    partials P_g (exact) times sx sw for the INT formats; for FP4 the kernel multiplies the
+    exactly dequantized values and sums all K products directly (the same exact terms,
+    regrouped), so its fp32 sum has K terms.  Plus r branch terms, the bias and the final
+    rounding."""
+    return (K if fmt == "fp4" else K // 64) + r + 2
+
+
 def w4a16_bound_terms(x, q, s, bias):
     """(abs_sum, n_terms, extra) for within_sum_bound on the W4A16 control.  The
     kernel rounds each dequantized weight q s to fp16 once before its fp16

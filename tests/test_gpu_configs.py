@@ -16,7 +16,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 import oracle  # noqa: E402
 from bit_w4a4_quantized_amd import binding  # noqa: E402
 from tests.layers import (log, prepared, raw_layer, reference, rel_fro, within_sum_bound,  # noqa: E402
-                          linear_abs_sum, branch_slack, w4a16_bound_terms)
+                          linear_abs_sum, branch_slack, w4a16_bound_terms, gemm_terms)
 
 TOL = 1e-3
 
@@ -66,7 +66,6 @@ def run_layer(P, fmt, x_hat=None, check_codes=True):
     M, K = x_hat.shape
     N = P.res.shape[1]
     r = P.l1.shape[1]
-    G = 16 if fmt == "fp4" else 64
     log(f"GPU {fmt} M={M} K={K} N={N} r={r}")
     ref = reference(P, fmt, x_hat)
     gx = dev(x_hat)
@@ -94,7 +93,7 @@ def run_layer(P, fmt, x_hat=None, check_codes=True):
     # the fused call rounds its own T: allow for T's own bound through L2
     slack = branch_slack(x_hat, P.l1, ref["t"], P.l2) if r else 0.0
     ok, worst = within_sum_bound(y, ref["y"], linear_abs_sum(ref["xq"], ref["xs"], ref["t"], ref["wq"], ref["ws"],
-                                                             P.l2, P.bias, fmt), K // G + r + 2, slack)
+                                                             P.l2, P.bias, fmt), gemm_terms(fmt, K, r), slack)
     assert ok, worst
     return y, ref, (wq, ws)
 
