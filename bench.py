@@ -10,7 +10,10 @@ the same run also times, each on its own seeded layer and with fewer steps:
   * on the QKV layer: the bare W4A4 GEMM (r = 0: no branch in either kernel),
     the unfused branch (down projection, quantization, GEMM, up projection as
     separate launches with an fp16 intermediate), and the W4A16 control (fp16
-    activations times INT4 group-64 weights, no branch).
+    activations times INT4 group-64 weights, no branch) and the fp16 x fp16
+    GEMM of the same shape on the vendor library (torch.matmul);
+  * the same layer shape in the other code formats: INT8 group 64 (rank 16),
+    FP4 E2M1 group 16 with E4M3 scales (rank 32), packed INT4 (rank 32).
 
 Inputs are seeded synthetic layers, resident in HBM before timing starts.
 Three copies of every input and output buffer are rotated so that a step never
@@ -339,8 +342,32 @@ def main():
         w16 = L.time_w4a16(es, ew)
         cmp_["w4a16_us"] = round(w16["us_per_call"], 2)
         cmp_["speedup_fused_vs_w4a16"] = round(w16["us_per_call"] / fused["us_per_layer"], 3)
+        # fp16 x fp16 GEMM of the same shape on the vendor library (torch.matmul -> hipBLASLt)
+        xr16 = [torch.from_numpy(L.raw.x).cuda() for _ in range(ROTATE)]
+        wt16 = [torch.from_numpy(np.ascontiguousarray(L.raw.w.astype(np.float16))).cuda() for _ in range(ROTATE)]
+
+        def mm(i):
+            torch.matmul(xr16[i % ROTATE], wt16[i % ROTATE], out=L.sets[i % ROTATE]["y"])
+        cmp_["fp16_gemm_hipblaslt_us"] = round(L.time_call(mm, es, ew)["us_per_call"], 2)
+        del xr16, wt16
         out["comparisons_" + args.workload] = cmp_
         log(f"comparisons: {cmp_}")
+        # the other code formats on the same layer shape (their own rank per setting)
+        variants = {}
+        for vfmt, vr in (("int8", 16), ("fp4", 32), ("int4", 32)):
+            Lv = Layer(torch, binding, args.workload, vfmt, vr)
+            res = Lv.time_fused(es, ew)
+            v_b = ops + 2.0 * M * vr * N
+            variants[vfmt] = {"r": vr, "us_per_layer": round(res["us_per_layer"], 2),
+                              "tops": round(ops / (res["us_per_layer"] * 1e-6) / 1e12, 2),
+                              "kernels_us": {"quantize_down": round(res["ka_us"], 2),
+                                             "gemm_w4a4_up": round(res["kb_us"], 2)},
+                              "kernel_b_pct_int8_peak": round(100.0 * v_b / (res["kb_us"] * 1e-6) / 1e12 / INT8_PEAK_TOPS, 2),
+                              "speedup_vs_w4a16": round(w16["us_per_call"] / res["us_per_layer"], 3)}
+            log(f"variant {vfmt}: {variants[vfmt]}")
+            del Lv
+            torch.cuda.empty_cache()
+        out["formats_" + args.workload] = variants
         others = {}
         for name in ("fc1", "fc2"):
             if name == args.workload:
