@@ -2,8 +2,9 @@
 """Benchmark of the fused SVDQuant W4A4 linear layer on one MI355X.
 
 One step = one pass of the layer's hot path over one batch: Kernel A
-(quantize + down projection) then Kernel B (W4A4 GEMM + up projection + bias),
-the same two launches svdq_linear makes.  The headline line is the FLUX-like
+(quantize + down projection; K is sliced over workgroups and a small second
+launch adds the slices' partial sums of T) then Kernel B (W4A4 GEMM + up
+projection + bias), the same launches svdq_linear makes.  The headline line is the FLUX-like
 fused QKV projection (M=4608 tokens, K=3072, N=9216, rank 32, INT4 group 64);
 the same run also times, each on its own seeded layer and with fewer steps:
   * the FLUX-like MLP pair: fc1 (K=3072, N=12288) and fc2 (K=12288, N=3072);
@@ -173,6 +174,8 @@ class Layer:
                 xs=torch.empty(binding.scale_shape(M, K, fmt), dtype=binding.scale_dtype(fmt), device="cuda"),
                 t=torch.empty((M, r), dtype=torch.float16, device="cuda") if r else None,
                 y=torch.empty((M, N), dtype=torch.float16, device="cuda"),
+                wsa=torch.empty(max(16, binding.quantize_down_workspace_bytes(M, K, r, fmt)), dtype=torch.uint8,
+                                device="cuda"),
             ))
         torch.cuda.synchronize()
         log(f"prepared {name} M={M} K={K} N={N} r={r} {fmt} in {time.time() - t0:.1f}s")
@@ -182,7 +185,7 @@ class Layer:
         if ev is not None:
             ev[0].record()
         b.svdq_quantize_down(st["x"], st["l1t"] if branch else None, self.fmt, xq=st["xq"], xs=st["xs"],
-                             t=st["t"] if branch else None)
+                             t=st["t"] if branch else None, workspace=st["wsa"])
         if ev is not None:
             ev[1].record()
         b.svdq_gemm_w4a4_up(st["xq"], st["xs"], st["t"] if branch else None, st["wq"], st["ws"],

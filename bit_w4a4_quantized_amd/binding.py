@@ -27,7 +27,8 @@ _c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 _SIGS = {
     "svdq_code_row_bytes": (_c_size, [_c_int, _c_int]),
     "svdq_scale_row_bytes": (_c_size, [_c_int, _c_int]),
-    "svdq_quantize_down": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp]),
+    "svdq_quantize_down": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "svdq_quantize_down_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "svdq_gemm_w4a4_up": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
     "svdq_linear_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "svdq_linear": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _c_size, _vp, _vp]),
@@ -146,8 +147,15 @@ def linear_unfused_workspace_bytes(M: int, N: int, K: int, r: int, fmt) -> int:
 
 
 # ------------------------------------------------------------------ entry points (same names as the C ABI)
-def svdq_quantize_down(x_hat, l1t, fmt, xq=None, xs=None, t=None, stream=None):
-    """Kernel A.  x_hat fp16 [M, K]; l1t fp16 [r, K] or None.  Returns (xq, xs, t)."""
+def quantize_down_workspace_bytes(M: int, K: int, r: int, fmt) -> int:
+    return int(lib().svdq_quantize_down_workspace_bytes(M, K, r, _fmt(fmt)))
+
+
+def svdq_quantize_down(x_hat, l1t, fmt, xq=None, xs=None, t=None, workspace=None, no_workspace=False,
+                       stream=None):
+    """Kernel A.  x_hat fp16 [M, K]; l1t fp16 [r, K] or None.  Returns (xq, xs, t).
+    workspace: uint8 device tensor for the sliced-K partial sums (allocated here when None);
+    no_workspace=True passes NULL (K not sliced)."""
     import torch
     M, K = x_hat.shape
     r = 0 if l1t is None else l1t.shape[0]
@@ -161,8 +169,15 @@ def svdq_quantize_down(x_hat, l1t, fmt, xq=None, xs=None, t=None, stream=None):
         xs = torch.empty(scale_shape(M, K, fmt), dtype=scale_dtype(fmt), device=dev)
     if r and t is None:
         t = torch.empty((M, r), dtype=torch.float16, device=dev)
+    if no_workspace:
+        workspace = None
+    elif workspace is None:
+        nb = quantize_down_workspace_bytes(M, K, r, fmt)
+        workspace = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("svdq_quantize_down", lib().svdq_quantize_down(
-        _p(x_hat), _p(l1t), M, K, r, _fmt(fmt), _p(xq), _p(xs), _p(t), _stream(stream)))
+        _p(x_hat), _p(l1t), M, K, r, _fmt(fmt), _p(xq), _p(xs), _p(t), _p(workspace), ws_bytes,
+        _stream(stream)))
     return xq, xs, t
 
 

@@ -7,170 +7,225 @@
 // read of the activations.
 //
 // Work decomposition (gfx950, wave64):
-//   one workgroup = NW waves = 16 token rows; the waves split K into 64-column
-//   chunks round-robin and each keeps its 16 x r partial of T in MFMA
-//   accumulators; the partials are summed through LDS at the end (fixed order,
-//   deterministic, no atomics).  Eight waves per workgroup and at most 128
-//   VGPRs let two workgroups share a CU, so the last partial round of
-//   workgroups does not leave most CUs idle.
-//   Lane l of a wave owns row (l % 16) and the 8-column slices
-//   [8 (l/16), +8) and [32 + 8 (l/16), +8) of each chunk: one 16-byte load
-//   each.  That is exactly the operand layout of v_mfma_f32_16x16x32_f16 for
-//   the chunk's two 32-column halves, so the fp16 values feed the matrix core
-//   straight from the registers they were quantized from.
+//   a workgroup (four waves) takes a block of 16 NRT token rows and a slice of
+//   K (cpb 64-column chunks); its waves take the slice's chunks round-robin,
+//   two chunks in flight per wave (the next chunk's loads are issued before the
+//   current one is processed).  Slicing K gives enough workgroups to cover
+//   the chip whatever K is, and keeps each wave's chain of dependent loads
+//   short.  Each wave keeps its NRT x r/16 tiles of 16 x 16 partial sums of T
+//   in MFMA accumulators; the four waves' partials are added through LDS in a
+//   fixed order; with one slice the workgroup rounds T to fp16, otherwise it
+//   writes its fp32 partial to the caller's workspace and k_t_finalize adds
+//   the slices in slice order and rounds (deterministic, no atomics).
+//   Lane l of a wave owns row (l % 16) of each 16-row tile and the 8-column
+//   slices [8 (l/16), +8) and [32 + 8 (l/16), +8) of each chunk: one 16-byte
+//   load each, which is exactly the operand layout of v_mfma_f32_16x16x32_f16
+//   for the chunk's two 32-column halves, so the fp16 values feed the matrix
+//   core straight from the registers they are quantized from, and one L1^T
+//   fragment serves all NRT row tiles.
 //   Group absmax: within the lane, then across the 4 lanes of the row with two
 //   cross-lane xor shuffles (INT, group 64) or one (FP4, group 16).
-//   INT codes use the division-free rule of int_code_f16 (exact for fp16
-//   inputs); NB chunks are loaded before any is processed, to keep HBM reads in
-//   flight.
+//   Codes are computed without divisions: the scale from amax times RN(1/qmax)
+//   and the quotient x/s from v_rcp_f32 and one fma refinement, both provably
+//   equal to the divisions' correctly rounded results for fp16 inputs
+//   (quant_core.h); the 6-bit container's fields are packed by the FP6 convert
+//   instruction.  A chunk's codes are assembled in the wave's LDS slot and
+//   written with whole 16-byte stores.
 #include "kernels.h"
 #include "quant_core.h"
 
 namespace svdq {
 
-constexpr int QD_WAVES = 8;
+namespace {
 
-template <int FMT, int RB, bool QUANT>
-__global__ void __launch_bounds__(64 * QD_WAVES, 2)
-k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M, int K,
-             uint8_t* __restrict__ xq, uint8_t* __restrict__ xs, __half* __restrict__ t) {
-  constexpr int NB = 2;                     // chunks in flight per wave
-  constexpr int NW = QD_WAVES;
+constexpr int QD_NT = 256;                  // four waves
+constexpr int QD_WPE = 2;                   // waves per SIMD the register budget allows
+constexpr int QD_NB = 2;                    // chunks in flight per wave (1 or 2)
+constexpr int QD_NRT = 4;                   // 16-row tiles per block for r <= 32 (2 above)
+constexpr int QD_TARGET_BLOCKS = 512;       // workgroups that cover the chip once
+
+template <int FMT>
+__host__ __device__ constexpr int chunk_code_bytes() {   // code bytes per row and 64-column chunk
+  return FMT == FMT_INT4_E2M3 ? 48 : (FMT == FMT_INT8 ? 64 : 32);
+}
+
+__host__ __device__ constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef int v6i_t __attribute__((ext_vector_type(6)));
+__device__ __forceinline__ h2_t as_h2(uint32_t w) { return __builtin_bit_cast(h2_t, w); }
+
+}  // namespace
+
+template <int FMT, int NRT, int RB, bool QUANT>
+__global__ void __launch_bounds__(QD_NT, QD_WPE)
+k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M, int K, int cpb,
+             uint8_t* __restrict__ xq, uint8_t* __restrict__ xs, __half* __restrict__ t,
+             float* __restrict__ part) {
   constexpr int R = RB * 16;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int row = lane & 15;
-  const int sub = lane >> 4;
-  const int m = blockIdx.x * 16 + row;
-  const bool valid = m < M;
-  const int nchunks = K >> 6;
-  const __half* xrow = x + (size_t)(valid ? m : 0) * K;
+  constexpr int RBX = RB > 0 ? RB : 1;
+  constexpr int ROWS = 16 * NRT;
+  constexpr int CB = chunk_code_bytes<FMT>();
+  constexpr bool STAGE = QUANT && FMT != FMT_FP4;          // codes go out through LDS
+  constexpr int RP = R + 4;                                 // padded row of the partial sums
+  constexpr int SMEM = cmax(cmax(STAGE ? 4 * ROWS * CB : 0, RB > 0 ? 4 * ROWS * RP * 4 : 0), 16);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
 
-  v4f acc[RB > 0 ? RB : 1];
-#pragma unroll
-  for (int j = 0; j < (RB > 0 ? RB : 1); j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row = lane & 15, sub = lane >> 4;
+  const int m0 = blockIdx.y * ROWS;
+  const int nch = K >> 6;
+  const int cbeg = blockIdx.x * cpb;
+  const int cend = min(nch, cbeg + cpb);
 
-  // Codes of one chunk (16 rows x CB bytes) are assembled in this wave's LDS slot and
-  // written back with whole 16-byte stores per lane: the per-lane pieces (2 to 6 bytes,
-  // odd offsets for the 6-bit container) would otherwise be many small scattered stores.
-  constexpr int CB = FMT == FMT_INT4_E2M3 ? 48 : (FMT == FMT_INT8 ? 64 : 32);   // code bytes per row per chunk
-  __shared__ __attribute__((aligned(16))) uint8_t cstage[NW][16 * CB];
-  uint8_t* slot = cstage[wave];
-  // row-major codes [M, K * bits / 8]; the 6-bit container is group-major [K/64][M][48]
-  const size_t code_row = FMT == FMT_INT4_E2M3 ? (size_t)48 : (FMT == FMT_INT8 ? (size_t)K : (size_t)(K >> 1));
-  const size_t code_chunk = FMT == FMT_INT4_E2M3 ? (size_t)M * 48 : (size_t)CB;   // bytes between chunks
+  // rows past M re-read row M - 1: T rows are independent, and nothing of theirs is stored
+  const __half* xr[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; rt++) xr[rt] = x + (size_t)min(m0 + rt * 16 + row, M - 1) * K + sub * 8;
+  const __half* lr[RBX];
+#pragma unroll
+  for (int j = 0; j < RBX; j++) lr[j] = RB > 0 ? l1t + (size_t)(j * 16 + row) * K + sub * 8 : nullptr;
 
-  for (int c0 = wave; c0 < nchunks; c0 += NW * NB) {
-    uint4 xv[NB][2];
-    uint4 bv[NB][RB > 0 ? RB : 1][2];
+  v4f acc[NRT][RBX];
 #pragma unroll
-    for (int i = 0; i < NB; i++) {
-      const int c = min(c0 + NW * i, nchunks - 1);   // a chunk past the end re-reads the last (unused)
-      const int col = c * 64 + sub * 8;
-      xv[i][0] = *reinterpret_cast<const uint4*>(xrow + col);
-      xv[i][1] = *reinterpret_cast<const uint4*>(xrow + col + 32);
+  for (int rt = 0; rt < NRT; rt++)
 #pragma unroll
-      for (int j = 0; j < RB; j++) {
-        const __half* lrow = l1t + (size_t)(j * 16 + row) * K + col;
-        bv[i][j][0] = *reinterpret_cast<const uint4*>(lrow);
-        bv[i][j][1] = *reinterpret_cast<const uint4*>(lrow + 32);
-      }
+    for (int j = 0; j < RBX; j++) acc[rt][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  struct Buf {
+    uint4 x[NRT][2];
+    uint4 b[RBX][2];
+  };
+  auto load = [&](int c, Buf& B) {
+    const int col = c * 64;
+#pragma unroll
+    for (int rt = 0; rt < NRT; rt++) {
+      B.x[rt][0] = *reinterpret_cast<const uint4*>(xr[rt] + col);
+      B.x[rt][1] = *reinterpret_cast<const uint4*>(xr[rt] + col + 32);
     }
 #pragma unroll
-    for (int i = 0; i < NB; i++) {
-      const int c = c0 + NW * i;
-      if (c >= nchunks) break;
-      if (!valid) {                          // rows past M contribute zeros to the MFMA
-        xv[i][0] = make_uint4(0, 0, 0, 0);
-        xv[i][1] = make_uint4(0, 0, 0, 0);
-      }
-      // ---- down projection on the matrix core (fp16 in, fp32 accumulate)
+    for (int j = 0; j < RB; j++) {
+      B.b[j][0] = *reinterpret_cast<const uint4*>(lr[j] + col);
+      B.b[j][1] = *reinterpret_cast<const uint4*>(lr[j] + col + 32);
+    }
+  };
+
+  uint8_t* slot = smem + wave * ROWS * CB;   // this wave's code staging (STAGE)
+  const size_t code_row = FMT == FMT_INT8 ? (size_t)K : (size_t)(K >> 1);   // row-major formats
+
+  auto process = [&](int c, const Buf& B) {
+    // ---- down projection on the matrix core (fp16 in, fp32 accumulate)
+#pragma unroll
+    for (int rt = 0; rt < NRT; rt++)
 #pragma unroll
       for (int j = 0; j < RB; j++) {
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(xv[i][0]), as_h8(bv[i][j][0]), acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(xv[i][1]), as_h8(bv[i][j][1]), acc[j], 0, 0, 0);
+        acc[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(B.x[rt][0]), as_h8(B.b[j][0]), acc[rt][j], 0, 0, 0);
+        acc[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(B.x[rt][1]), as_h8(B.b[j][1]), acc[rt][j], 0, 0, 0);
       }
-      if (!QUANT) continue;
-      // ---- quantize
-      float v[16];
-      unpack_h8(xv[i][0], v);
-      unpack_h8(xv[i][1], v + 8);
-      const int col = c * 64 + sub * 8;
-      if (FMT == FMT_INT4 || FMT == FMT_INT8 || FMT == FMT_INT4_E2M3) {
-        const float qmax = FMT == FMT_INT8 ? 127.0f : 7.0f;
-        float amax = 0.f;
+    if (!QUANT) return;
+    // ---- quantize
+    if (FMT == FMT_INT4 || FMT == FMT_INT8 || FMT == FMT_INT4_E2M3) {
+      const float qmax = FMT == FMT_INT8 ? 127.0f : 7.0f;
+      const float inv_qmax = FMT == FMT_INT8 ? 1.0f / 127.0f : 1.0f / 7.0f;   // RN(1 / qmax)
+      // row tiles in pairs (one FP6 convert packs two tiles' fields); NRT == 1: a lone tile
 #pragma unroll
-        for (int e = 0; e < 16; e++) amax = fmaxf(amax, fabsf(v[e]));
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        uint16_t sbits;
-        const float s = int_scale(amax, qmax, &sbits);
-        const float rs = s == 0.0f ? 0.0f : 1.0f / s;
-        float q[16];
+      for (int rp = 0; rp < NRT; rp += 2) {
+        constexpr int NP = NRT > 1 ? 2 : 1;
+        float qv[NP][16];                    // the codes, as floats (+0 for code 0)
 #pragma unroll
-        for (int e = 0; e < 16; e++) q[e] = int_code_f16(v[e], rs, qmax);
-        {
-          uint8_t* srow = slot + row * CB;   // this row's bytes of the chunk, in LDS
+        for (int k = 0; k < NP; k++) {
+          const int rt = rp + k;
+          // group absmax: the lane's 16 fp16 values (packed max), then across the row's 4 lanes
+          h2_t mx = h2_t{(_Float16)0, (_Float16)0};
+#pragma unroll
+          for (int hh = 0; hh < 2; hh++) {
+            const uint32_t w[4] = {B.x[rt][hh].x, B.x[rt][hh].y, B.x[rt][hh].z, B.x[rt][hh].w};
+#pragma unroll
+            for (int i = 0; i < 4; i++) mx = __builtin_elementwise_max(mx, __builtin_elementwise_abs(as_h2(w[i])));
+          }
+          float amax = fmaxf((float)mx.x, (float)mx.y);
+          amax = fmaxf(amax, __shfl_xor(amax, 16));
+          amax = fmaxf(amax, __shfl_xor(amax, 32));
+          uint16_t sbits;
+          const float s = int_scale_f16in(amax, inv_qmax, &sbits);
+          const float r = s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s);
+          float v[16];
+          unpack_h8(B.x[rt][0], v);
+          unpack_h8(B.x[rt][1], v + 8);
+          // code = rint_half_even(clamp(RN(x / s), +-qmax)); + 0.0f turns -0 into +0
+#pragma unroll
+          for (int e = 0; e < 16; e++)
+            qv[k][e] = rintf(__builtin_amdgcn_fmed3f(quot_rn(v[e], s, r), -qmax, qmax)) + 0.0f;
+          const int m = m0 + rt * 16 + row;
+          if (sub == 0 && m < M) {
+            // row-major scales [M, K/64]; the 6-bit container keeps them group-major [K/64, M]
+            const size_t si = FMT == FMT_INT4_E2M3 ? (size_t)c * M + m : (size_t)m * (K >> 6) + c;
+            reinterpret_cast<uint16_t*>(xs)[si] = sbits;
+          }
+          uint8_t* srow = slot + (rt * 16 + row) * CB;   // this row's bytes of the chunk, in LDS
           if (FMT == FMT_INT4) {
             uint32_t w0 = 0, w1 = 0;
 #pragma unroll
             for (int e = 0; e < 8; e++) {
-              w0 |= ((uint32_t)(int)q[e] & 0xFu) << (4 * e);
-              w1 |= ((uint32_t)(int)q[8 + e] & 0xFu) << (4 * e);
+              w0 |= ((uint32_t)(int)qv[k][e] & 0xFu) << (4 * e);
+              w1 |= ((uint32_t)(int)qv[k][8 + e] & 0xFu) << (4 * e);
             }
             *reinterpret_cast<uint32_t*>(srow + 4 * sub) = w0;
             *reinterpret_cast<uint32_t*>(srow + 16 + 4 * sub) = w1;
-          } else if (FMT == FMT_INT4_E2M3) {
-            // 6-bit container: a (row, group) has 48 bytes; half h (codes 32h..32h+31) is 24
-            // bytes of 6-bit fields whose bytes 0..15 sit at 16h and bytes 16..23 at 32 + 8h.
-            // This lane's 8 codes of each half are fields 8 sub .. 8 sub + 7: the 6 bytes at
-            // offset 6 sub of the half, written as three 16-bit pieces (none crosses byte 16).
-#pragma unroll
-            for (int hh = 0; hh < 2; hh++) {
-              uint32_t lo = 0;                   // bits 0..31 of the 48-bit run
-#pragma unroll
-              for (int e = 0; e < 5; e++) lo |= e2m3_field(q[8 * hh + e]) << (6 * e);
-              const uint32_t f5 = e2m3_field(q[8 * hh + 5]);
-              lo |= f5 << 30;
-              // bits 32..47
-              const uint32_t hi = (f5 >> 2) | (e2m3_field(q[8 * hh + 6]) << 4) | (e2m3_field(q[8 * hh + 7]) << 10);
-              const uint32_t piece[3] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu};
-#pragma unroll
-              for (int j = 0; j < 3; j++) {
-                const int o = 6 * sub + 2 * j;   // byte offset within the half (even)
-                const int pos = o < 16 ? 16 * hh + o : 32 + 8 * hh + (o - 16);
-                *reinterpret_cast<uint16_t*>(srow + pos) = (uint16_t)piece[j];
-              }
-            }
-          } else {
+          } else if (FMT == FMT_INT8) {
             uint32_t w[4];
 #pragma unroll
             for (int k4 = 0; k4 < 4; k4++) {
               w[k4] = 0;
 #pragma unroll
-              for (int e = 0; e < 4; e++) w[k4] |= ((uint32_t)(int)q[4 * k4 + e] & 0xFFu) << (8 * e);
+              for (int e = 0; e < 4; e++) w[k4] |= ((uint32_t)(int)qv[k][4 * k4 + e] & 0xFFu) << (8 * e);
             }
             *reinterpret_cast<uint2*>(srow + 8 * sub) = make_uint2(w[0], w[1]);
             *reinterpret_cast<uint2*>(srow + 32 + 8 * sub) = make_uint2(w[2], w[3]);
           }
         }
-        // the wave's 16 x CB bytes go out as CB/16 16-byte pieces per row
-        __builtin_amdgcn_wave_barrier();
-        if (lane < CB) {
-          const int rr = lane / (CB / 16), part = lane % (CB / 16);
-          const int mm = blockIdx.x * 16 + rr;
-          const uint4 v16 = *reinterpret_cast<const uint4*>(slot + rr * CB + part * 16);
-          if (mm < M) *reinterpret_cast<uint4*>(xq + (size_t)mm * code_row + (size_t)c * code_chunk + part * 16) = v16;
-        }
-        __builtin_amdgcn_wave_barrier();
-        if (valid) {
-          if (sub == 0) {
-            // row-major scales [M, K/64]; the 6-bit container format keeps them group-major [K/64, M]
-            const size_t si = FMT == FMT_INT4_E2M3 ? (size_t)c * M + m : (size_t)m * (K >> 6) + c;
-            reinterpret_cast<uint16_t*>(xs)[si] = sbits;
+        if (FMT == FMT_INT4_E2M3) {
+          // 6-bit container: a (row, group) has 48 bytes; half h (codes 32h..32h+31) is 24
+          // bytes of 6-bit fields (the E2M3 encoding of code/8) whose bytes 0..15 sit at 16h
+          // and bytes 16..23 at 32 + 8h.  This lane's 8 codes of each half are fields
+          // 8 sub .. 8 sub + 7: the 6 bytes at offset 6 sub of the half.  One
+          // v_cvt_scalef32_2xpk16_fp6_f32 (scale 8: exact division by 8; field 2j from the
+          // first source, 2j + 1 from the second) packs the pair's 4 runs of 8 fields.
+          v16f ev, od;
+#pragma unroll
+          for (int run = 0; run < 4; run++) {      // run = 2 (tile in the pair) + half
+            const int k = run >> 1, hh = run & 1;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              ev[4 * run + i] = k < NP ? qv[k < NP ? k : 0][8 * hh + 2 * i] : 0.0f;
+              od[4 * run + i] = k < NP ? qv[k < NP ? k : 0][8 * hh + 2 * i + 1] : 0.0f;
+            }
+          }
+          const v6i_t f = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 8.0f);
+          const uint32_t d[6] = {(uint32_t)f[0], (uint32_t)f[1], (uint32_t)f[2], (uint32_t)f[3], (uint32_t)f[4], (uint32_t)f[5]};
+#pragma unroll
+          for (int run = 0; run < 2 * NP; run++) {
+            const int rt = rp + (run >> 1), hh = run & 1;
+            uint8_t* srow = slot + (rt * 16 + row) * CB;
+#pragma unroll
+            for (int j = 0; j < 3; j++) {
+              const int p16 = 3 * run + j;           // 16-bit piece of the 192-bit result
+              const uint16_t piece = (uint16_t)(d[p16 >> 1] >> (16 * (p16 & 1)));
+              const int o = 6 * sub + 2 * j;         // byte offset within the half (even)
+              const int pos = o < 16 ? 16 * hh + o : 32 + 8 * hh + (o - 16);
+              *reinterpret_cast<uint16_t*>(srow + pos) = piece;
+            }
           }
         }
-      } else {  // FP4: groups of 16 = two lanes (sub, sub^1) x 8 values
+      }
+    } else {  // FP4: groups of 16 = two lanes (sub, sub^1) x 8 values
+#pragma unroll
+      for (int rt = 0; rt < NRT; rt++) {
+        float v[16];
+        unpack_h8(B.x[rt][0], v);
+        unpack_h8(B.x[rt][1], v + 8);
+        const int m = m0 + rt * 16 + row;
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; e++) { a0 = fmaxf(a0, fabsf(v[e])); a1 = fmaxf(a1, fabsf(v[8 + e])); }
@@ -179,10 +234,16 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
         uint32_t b0, b1;
         const float s0 = fp4_scale(a0, &b0);
         const float s1 = fp4_scale(a1, &b1);
+        const float r0 = s0 == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s0);
+        const float r1 = s1 == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s1);
         int q[16];
 #pragma unroll
-        for (int e = 0; e < 8; e++) { q[e] = (int)fp4_code(v[e], s0); q[8 + e] = (int)fp4_code(v[8 + e], s1); }
-        if (valid) {
+        for (int e = 0; e < 8; e++) {
+          q[e] = s0 == 0.0f ? 0 : (int)fp4_code_q(quot_rn(v[e], s0, r0));
+          q[8 + e] = s1 == 0.0f ? 0 : (int)fp4_code_q(quot_rn(v[8 + e], s1, r1));
+        }
+        if (m < M) {
+          const int col = c * 64 + sub * 8;
           uint8_t* dst = xq + (size_t)m * (K >> 1);
           *reinterpret_cast<uint32_t*>(dst + (col >> 1)) = pack8(q);
           *reinterpret_cast<uint32_t*>(dst + ((col + 32) >> 1)) = pack8(q + 8);
@@ -194,75 +255,193 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
         }
       }
     }
+    if (STAGE) {
+      // the wave's ROWS x CB bytes go out as 16-byte pieces: the 6-bit container's rows of
+      // one group are contiguous ([K/64][M][48]); the other formats are row-major
+      __builtin_amdgcn_wave_barrier();
+      constexpr int PR = CB / 16;            // pieces per row
+#pragma unroll
+      for (int p0 = 0; p0 < ROWS * PR; p0 += 64) {
+        const int p = p0 + lane;
+        const int rr = p / PR, pc = p % PR;
+        const int mm = m0 + rr;
+        if (p < ROWS * PR && mm < M) {
+          const uint4 v16 = *reinterpret_cast<const uint4*>(slot + rr * CB + pc * 16);
+          uint8_t* dst = FMT == FMT_INT4_E2M3 ? xq + ((size_t)c * M + mm) * 48 + pc * 16
+                                              : xq + (size_t)mm * code_row + (size_t)c * CB + pc * 16;
+          *reinterpret_cast<uint4*>(dst) = v16;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  };
+
+  // ---- this wave's chunks: cbeg + wave, + 4, ... below cend; two in flight
+  int c = cbeg + wave;
+  if (QD_NB == 1) {
+    for (; c < cend; c += 4) {
+      Buf B0;
+      load(c, B0);
+      process(c, B0);
+    }
+  } else if (c < cend) {
+    Buf B0, B1;
+    load(c, B0);
+    while (true) {
+      int cn = c + 4;
+      if (cn < cend) load(cn, B1);
+      process(c, B0);
+      if (cn >= cend) break;
+      c = cn;
+      cn = c + 4;
+      if (cn < cend) load(cn, B0);
+      process(c, B1);
+      if (cn >= cend) break;
+      c = cn;
+    }
   }
 
   if (RB > 0) {
-    // ---- reduce the waves' partials of T (fixed order) and store fp16
-    __shared__ float part[NW][16][R > 0 ? R : 1];
+    // ---- the four waves' partials of T, added in wave order through LDS
+    __syncthreads();                         // the code staging shares these bytes
+    float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
-    for (int j = 0; j < RB; j++)
+    for (int rt = 0; rt < NRT; rt++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) part[wave][4 * sub + i][j * 16 + row] = acc[j][i];
+      for (int j = 0; j < RB; j++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) red[(wave * ROWS + rt * 16 + 4 * sub + i) * RP + j * 16 + row] = acc[rt][j][i];
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * R; idx += 64 * NW) {
-      const int rr = idx / R, cc = idx % R;
-      const int mm = blockIdx.x * 16 + rr;
-      if (mm < M) {
-        float s = 0.f;
+    for (int idx = tid; idx < ROWS * (R / 4); idx += QD_NT) {
+      const int rr = idx / (R / 4), c4 = (idx % (R / 4)) * 4;
+      const int mm = m0 + rr;
+      if (mm >= M) continue;
+      float sum[4];
 #pragma unroll
-        for (int w = 0; w < NW; w++) s += part[w][rr][cc];
-        t[(size_t)mm * R + cc] = __float2half_rn(s);
+      for (int e = 0; e < 4; e++) {
+        float s = red[rr * RP + c4 + e];
+#pragma unroll
+        for (int w = 1; w < 4; w++) s += red[(w * ROWS + rr) * RP + c4 + e];
+        sum[e] = s;
+      }
+      if (part) {
+        *reinterpret_cast<float4*>(part + ((size_t)blockIdx.x * M + mm) * R + c4) = make_float4(sum[0], sum[1], sum[2], sum[3]);
+      } else {
+        const uint32_t h0 = __half_as_ushort(__float2half_rn(sum[0])) | ((uint32_t)__half_as_ushort(__float2half_rn(sum[1])) << 16);
+        const uint32_t h1 = __half_as_ushort(__float2half_rn(sum[2])) | ((uint32_t)__half_as_ushort(__float2half_rn(sum[3])) << 16);
+        *reinterpret_cast<uint2*>(t + (size_t)mm * R + c4) = make_uint2(h0, h1);
       }
     }
   }
 }
 
-template <int FMT, int RB, bool QUANT = true>
-static hipError_t launch_qd(const QuantDownArgs& a, hipStream_t s) {
-  dim3 grid((a.M + 15) / 16);
-  hipLaunchKernelGGL((k_quant_down<FMT, RB, QUANT>), grid, dim3(64 * QD_WAVES), 0, s, (const __half*)a.x,
-                     (const __half*)a.l1t, a.M, a.K, (uint8_t*)a.xq, (uint8_t*)a.xs, (__half*)a.t);
+// T = fp16_rne( sum over slices s = 0, 1, ... of part[s] ), slices added in order; each
+// thread issues up to 8 slices' loads before adding them.
+__global__ void __launch_bounds__(64)
+k_t_finalize(const float* __restrict__ part, int S, size_t MR, __half* __restrict__ t) {
+  const size_t i = ((size_t)blockIdx.x * 64 + threadIdx.x) * 4;
+  if (i >= MR) return;
+  float4 a = *reinterpret_cast<const float4*>(part + i);
+  for (int s0 = 1; s0 < S; s0 += 8) {
+    float4 b[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+      if (s0 + k < S) b[k] = *reinterpret_cast<const float4*>(part + (size_t)(s0 + k) * MR + i);
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+      if (s0 + k < S) { a.x += b[k].x; a.y += b[k].y; a.z += b[k].z; a.w += b[k].w; }
+  }
+  const uint32_t h0 = __half_as_ushort(__float2half_rn(a.x)) | ((uint32_t)__half_as_ushort(__float2half_rn(a.y)) << 16);
+  const uint32_t h1 = __half_as_ushort(__float2half_rn(a.z)) | ((uint32_t)__half_as_ushort(__float2half_rn(a.w)) << 16);
+  *reinterpret_cast<uint2*>(t + i) = make_uint2(h0, h1);
+}
+
+// ---- launch plan: row blocks of 64 (32 for r > 32; 16 when K cannot be sliced for want of a
+// workspace),
+// K sliced into chunks-per-block multiples of 4 so that about QD_TARGET_BLOCKS workgroups
+// cover the chip.
+QuantDownPlan quant_down_plan(int M, int K, int r, bool have_partials) {
+  QuantDownPlan p{};
+  const int nch = K >> 6;
+  const bool can_slice = r == 0 || have_partials;
+  p.nrt = can_slice ? (r <= 32 ? QD_NRT : 2) : 1;   // rows per block within the register budget
+  const long rows_blocks = (M + 16 * p.nrt - 1) / (16 * p.nrt);
+  if (!can_slice) {
+    p.cpb = nch;
+  } else {
+    long q = (long)nch * rows_blocks;                        // wave-chunks
+    long per_wave = (q + 4L * QD_TARGET_BLOCKS / 2) / (4L * QD_TARGET_BLOCKS);
+    if (per_wave < 1) per_wave = 1;
+    p.cpb = (int)(4 * per_wave);
+    if (p.cpb > nch) p.cpb = ((nch + 3) / 4) * 4;
+  }
+  p.slices = (nch + p.cpb - 1) / p.cpb;
+  p.rows_blocks = (int)rows_blocks;
+  p.partial_bytes = (r > 0 && p.slices > 1) ? (size_t)p.slices * M * r * 4 : 0;
+  return p;
+}
+
+template <int FMT, int NRT, int RB, bool QUANT>
+static hipError_t launch_qd(const QuantDownArgs& a, const QuantDownPlan& p, hipStream_t s) {
+  float* part = (RB > 0 && p.slices > 1) ? static_cast<float*>(a.part) : nullptr;
+  hipLaunchKernelGGL((k_quant_down<FMT, NRT, RB, QUANT>), dim3(p.slices, p.rows_blocks), dim3(QD_NT), 0, s,
+                     (const __half*)a.x, (const __half*)a.l1t, a.M, a.K, p.cpb, (uint8_t*)a.xq, (uint8_t*)a.xs,
+                     (__half*)a.t, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !part) return e;
+  const size_t MR = (size_t)a.M * a.r;
+  const unsigned blocks = (unsigned)((MR / 4 + 63) / 64);
+  hipLaunchKernelGGL(k_t_finalize, dim3(blocks), dim3(64), 0, s, (const float*)part, p.slices, MR, (__half*)a.t);
   return hipGetLastError();
 }
 
-template <int FMT>
+template <int FMT, int RB, bool QUANT>
+static hipError_t launch_qd_n(const QuantDownArgs& a, const QuantDownPlan& p, hipStream_t s) {
+  switch (p.nrt) {
+    case 4:
+      if constexpr (RB <= 2 && QD_NRT == 4) return launch_qd<FMT, 4, RB, QUANT>(a, p, s);
+      break;
+    case 2: return launch_qd<FMT, 2, RB, QUANT>(a, p, s);
+    case 1: return launch_qd<FMT, 1, RB, QUANT>(a, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int FMT, bool QUANT>
 static hipError_t launch_qd_r(const QuantDownArgs& a, hipStream_t s) {
+  QuantDownPlan p = quant_down_plan(a.M, a.K, a.r, true);
+  if (p.partial_bytes > 0 && (!a.part || a.part_bytes < p.partial_bytes)) p = quant_down_plan(a.M, a.K, a.r, false);
   switch (a.r) {
-    case 0: return launch_qd<FMT, 0>(a, s);
-    case 16: return launch_qd<FMT, 1>(a, s);
-    case 32: return launch_qd<FMT, 2>(a, s);
-    case 48: return launch_qd<FMT, 3>(a, s);
-    case 64: return launch_qd<FMT, 4>(a, s);
+    case 0: return launch_qd_n<FMT, 0, QUANT>(a, p, s);
+    case 16: return launch_qd_n<FMT, 1, QUANT>(a, p, s);
+    case 32: return launch_qd_n<FMT, 2, QUANT>(a, p, s);
+    case 48: return launch_qd_n<FMT, 3, QUANT>(a, p, s);
+    case 64: return launch_qd_n<FMT, 4, QUANT>(a, p, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_quant_down(const QuantDownArgs& a, hipStream_t s) {
   switch (a.fmt) {
-    case FMT_INT4: return launch_qd_r<FMT_INT4>(a, s);
-    case FMT_INT4_E2M3: return launch_qd_r<FMT_INT4_E2M3>(a, s);
-    case FMT_INT8: return launch_qd_r<FMT_INT8>(a, s);
-    case FMT_FP4: return launch_qd_r<FMT_FP4>(a, s);
+    case FMT_INT4: return launch_qd_r<FMT_INT4, true>(a, s);
+    case FMT_INT4_E2M3: return launch_qd_r<FMT_INT4_E2M3, true>(a, s);
+    case FMT_INT8: return launch_qd_r<FMT_INT8, true>(a, s);
+    case FMT_FP4: return launch_qd_r<FMT_FP4, true>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
 // Unfused comparison: quantization alone (no branch) ...
 hipError_t launch_quant_only(const void* x, int M, int K, int fmt, void* xq, void* xs, hipStream_t s) {
-  QuantDownArgs a{x, nullptr, M, K, 0, fmt, xq, xs, nullptr};
+  QuantDownArgs a{x, nullptr, M, K, 0, fmt, xq, xs, nullptr, nullptr, 0};
   return launch_quant_down(a, s);
 }
 
 // ... and the down projection alone, a second full read of X_hat.
-hipError_t launch_down_only(const void* x, const void* l1t, int M, int K, int r, void* t, hipStream_t s) {
-  QuantDownArgs a{x, l1t, M, K, r, FMT_INT4, nullptr, nullptr, t};
-  switch (r) {
-    case 16: return launch_qd<FMT_INT4, 1, false>(a, s);
-    case 32: return launch_qd<FMT_INT4, 2, false>(a, s);
-    case 48: return launch_qd<FMT_INT4, 3, false>(a, s);
-    case 64: return launch_qd<FMT_INT4, 4, false>(a, s);
-  }
-  return hipErrorInvalidValue;
+hipError_t launch_down_only(const void* x, const void* l1t, int M, int K, int r, void* t, void* part,
+                            size_t part_bytes, hipStream_t s) {
+  QuantDownArgs a{x, l1t, M, K, r, FMT_INT4, nullptr, nullptr, t, part, part_bytes};
+  return launch_qd_r<FMT_INT4, false>(a, s);
 }
 
 }  // namespace svdq

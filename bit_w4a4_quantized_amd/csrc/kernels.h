@@ -42,7 +42,16 @@ __device__ __forceinline__ void unpack_h8(const uint4& u, float* f) {
 struct QuantDownArgs {
   const void* x; const void* l1t; int M, K, r; int fmt;
   void* xq; void* xs; void* t;
+  void* part; size_t part_bytes;             // fp32 partial sums of T when K is sliced (may be null)
 };
+
+// Kernel A's launch: row blocks of 16 nrt rows, K in `slices` slices of cpb 64-column chunks;
+// partial_bytes of fp32 partial sums of T are needed when r > 0 and slices > 1.
+struct QuantDownPlan {
+  int nrt, cpb, slices, rows_blocks;
+  size_t partial_bytes;
+};
+QuantDownPlan quant_down_plan(int M, int K, int r, bool have_partials);
 
 struct GemmArgs {
   const void* xq; const void* xs; const void* t; const void* wq; const void* ws;
@@ -60,7 +69,8 @@ hipError_t launch_quant_weight(const float* r_t, int N, int K, int fmt, void* wq
 
 // unfused comparison pieces
 hipError_t launch_quant_only(const void* x, int M, int K, int fmt, void* xq, void* xs, hipStream_t s);
-hipError_t launch_down_only(const void* x, const void* l1t, int M, int K, int r, void* t, hipStream_t s);
+hipError_t launch_down_only(const void* x, const void* l1t, int M, int K, int r, void* t, void* part,
+                            size_t part_bytes, hipStream_t s);
 hipError_t launch_up_add(const void* y0, const void* t, const void* l2, int M, int N, int r, void* y,
                          hipStream_t s);
 

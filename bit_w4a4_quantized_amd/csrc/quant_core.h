@@ -31,6 +31,31 @@ __device__ __forceinline__ int int_code(float v, float s, float qmax) {
   return (int)t;
 }
 
+// fp16 scale of an INT group whose absmax is an fp16 value, without the division:
+// fp16_rne(amax * RN(1/qmax)) == fp16_rne(RN(amax / qmax)) for qmax in {7, 127}.
+// The product is within one fp32 ulp of amax / qmax, and amax / qmax is never within
+// 32 ulps of a point where fp16 rounding changes, a midpoint m = (2k+1) g of the fp16
+// grid (spacing 2g): qmax m is an odd multiple of g and amax (at least as coarse a grid)
+// an even one, so |amax / qmax - m| >= g / qmax, while an fp32 ulp at m is at most
+// g 2^-12 (subnormal fp16 range included).
+__device__ __forceinline__ float int_scale_f16in(float amax, float inv_qmax, uint16_t* bits) {
+  __half h = __float2half_rn(amax * inv_qmax);
+  *bits = __half_as_ushort(h);
+  return __half2float(h);
+}
+
+// RN(x / s) for fp16 values x and s != 0 (as floats; s may also be an E4M3 value), given
+// r = v_rcp_f32(s) (within one ulp of 1/s): t0 = RN(x r) is within 2^-22 of x/s
+// (relative), the residual x - t0 s is formed exactly by the fma up to one rounding, and
+// t = RN(t0 + (x - t0 s) r) is RN of a value within 2^-44 (relative) of x/s.  The quotient
+// of two fp16 values is never a midpoint of the fp32 grid (that would need 25 significant
+// bits in x) and never within 2^-36 (relative) of one (x - m s is a nonzero multiple of
+// m's grid times s's), so t is the correctly rounded quotient RN(x / s) exactly.
+__device__ __forceinline__ float quot_rn(float x, float s, float r) {
+  const float t0 = x * r;
+  return __builtin_fmaf(__builtin_fmaf(-t0, s, x), r, t0);
+}
+
 // Code of an fp16 value x (as float) against an fp16 scale s, given r = 1/s
 // (fp32, correctly rounded; r = 0 when s == 0).  Equals
 // clamp(rint(fp32(x) / s), -qmax, qmax) for qmax <= 127 without the division:
@@ -92,6 +117,15 @@ __device__ __forceinline__ float fp4_scale(float amax, uint32_t* byte) {
 __device__ __forceinline__ uint32_t fp4_code(float v, float s) {
   if (s == 0.0f) return 0u;
   float t = v / s;
+  float a = fabsf(t);
+  uint32_t idx = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                 (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                 (uint32_t)(a > 5.0f);
+  return (t < 0.0f && idx != 0u) ? (idx | 8u) : idx;
+}
+
+// E2M1 nibble of the quotient t = RN(v / s) (same rule as fp4_code).
+__device__ __forceinline__ uint32_t fp4_code_q(float t) {
   float a = fabsf(t);
   uint32_t idx = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
                  (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +

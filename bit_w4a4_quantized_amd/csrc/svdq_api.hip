@@ -40,8 +40,11 @@ svdq_status map_launch(hipError_t e) {
 }
 
 struct Workspace {
-  void* xq; void* xs; void* t; void* y0; size_t total;
+  void* xq; void* xs; void* t; void* part; size_t part_bytes; void* y0; size_t total;
 };
+
+// Kernel A's partial sums of T (0 bytes when its K is not sliced)
+size_t partial_bytes(int M, int K, int r) { return round256(quant_down_plan(M, K, r, true).partial_bytes); }
 
 Workspace carve(void* base, int M, int N, int K, int r, int fmt, bool with_y0) {
   Workspace w{};
@@ -50,6 +53,8 @@ Workspace carve(void* base, int M, int N, int K, int r, int fmt, bool with_y0) {
   w.xq = b ? b + off : nullptr; off += round256((size_t)M * code_bytes(K, fmt));
   w.xs = b ? b + off : nullptr; off += round256((size_t)M * scale_bytes(K, fmt));
   w.t = (r > 0 && b) ? b + off : nullptr; off += round256((size_t)M * r * 2);
+  w.part_bytes = partial_bytes(M, K, r);
+  w.part = (w.part_bytes && b) ? b + off : nullptr; off += w.part_bytes;
   if (with_y0) { w.y0 = b ? b + off : nullptr; off += round256((size_t)M * N * 2); }
   w.total = off;
   return w;
@@ -101,12 +106,24 @@ size_t svdq_scale_row_bytes(int K, svdq_format fmt) {
   return scale_bytes(K, fmt);
 }
 
+size_t svdq_quantize_down_workspace_bytes(int M, int K, int r, svdq_format fmt) {
+  if (!fmt_ok(fmt) || check_dims(M, 16, K, r) != SVDQ_OK) return 0;
+  return partial_bytes(M, K, r);
+}
+
 svdq_status svdq_quantize_down(const void* x_hat, const void* l1t, int M, int K, int r, svdq_format fmt,
-                               void* xq, void* xs, void* t, void* stream) {
+                               void* xq, void* xs, void* t, void* workspace, size_t workspace_bytes,
+                               void* stream) {
   svdq_status st = check_quant_down(x_hat, l1t, M, K, r, fmt, xq, xs, t);
   if (st != SVDQ_OK) return st;
   if (M == 0) return SVDQ_OK;
-  QuantDownArgs a{x_hat, l1t, M, K, r, (int)fmt, xq, xs, t};
+  // a workspace, when given, must hold the partial sums; without one K is not sliced
+  const size_t need = partial_bytes(M, K, r);
+  if (workspace && need) {
+    if (!aligned16(workspace)) return SVDQ_ERR_ALIGN;
+    if (workspace_bytes < need) return SVDQ_ERR_WORKSPACE;
+  }
+  QuantDownArgs a{x_hat, l1t, M, K, r, (int)fmt, xq, xs, t, need ? workspace : nullptr, need ? workspace_bytes : 0};
   return map_launch(launch_quant_down(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -143,7 +160,7 @@ svdq_status svdq_linear(const void* x_hat, const void* l1t, const void* wq, cons
   if (st != SVDQ_OK) return st;
   if (M == 0 || N == 0) return SVDQ_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  QuantDownArgs qa{x_hat, l1t, M, K, r, (int)fmt, w.xq, w.xs, w.t};
+  QuantDownArgs qa{x_hat, l1t, M, K, r, (int)fmt, w.xq, w.xs, w.t, w.part, w.part_bytes};
   st = map_launch(launch_quant_down(qa, s));
   if (st != SVDQ_OK) return st;
   GemmArgs ga{w.xq, w.xs, w.t, wq, ws, l2, bias, M, N, K, r, (int)fmt, y};
@@ -188,7 +205,7 @@ svdq_status svdq_linear_unfused(const void* x_hat, const void* l1t, const void* 
   st = map_launch(launch_quant_only(x_hat, M, K, (int)fmt, w.xq, w.xs, s));
   if (st != SVDQ_OK) return st;
   if (r > 0) {
-    st = map_launch(launch_down_only(x_hat, l1t, M, K, r, w.t, s));
+    st = map_launch(launch_down_only(x_hat, l1t, M, K, r, w.t, w.part, w.part_bytes, s));
     if (st != SVDQ_OK) return st;
   }
   GemmArgs ga{w.xq, w.xs, nullptr, wq, ws, nullptr, bias, M, N, K, 0, (int)fmt, r > 0 ? w.y0 : y};

@@ -112,10 +112,23 @@ size_t svdq_scale_row_bytes(int K, svdq_format fmt);
  *   xq    : out, codes [M, code_row_bytes(K)].
  *   xs    : out, scales [M, K/G] (fp16 or E4M3 bytes).
  *   t     : out, fp16 [M, r] = fp16_rne(X_hat L1), fp32 accumulation; NULL iff r == 0.
- * The branch reads the unquantized 16-bit X_hat.
+ *   workspace, workspace_bytes : caller-owned device scratch for the fp32
+ *           partial sums of T when the kernel slices K across workgroups
+ *           (svdq_quantize_down_workspace_bytes; 16-byte aligned).  Its
+ *           contents need no initialisation and are dead after the call; two
+ *           calls in flight at once need two workspaces.  NULL is allowed: K
+ *           is then not sliced for r > 0 (same results, slower for long K);
+ *           a non-NULL workspace that is too small is SVDQ_ERR_WORKSPACE.
+ * The branch reads the unquantized 16-bit X_hat.  Results do not depend on
+ * the workspace: the slices' partials are added in a fixed order.
  */
 svdq_status svdq_quantize_down(const void* x_hat, const void* l1t, int M, int K, int r,
-                               svdq_format fmt, void* xq, void* xs, void* t, void* stream);
+                               svdq_format fmt, void* xq, void* xs, void* t, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Workspace bytes svdq_quantize_down uses to slice K (0: no slicing for this
+ * shape, or r == 0, or a bad format or shape). */
+size_t svdq_quantize_down_workspace_bytes(int M, int K, int r, svdq_format fmt);
 
 /*
  * Kernel B: low-bit GEMM + up projection + bias ("sota-314", "Do this": the up
@@ -137,8 +150,9 @@ svdq_status svdq_gemm_w4a4_up(const void* xq, const void* xs, const void* t, con
                               const void* ws, const void* l2, const void* bias, int M, int N, int K,
                               int r, svdq_format fmt, void* y, void* stream);
 
-/* Workspace svdq_linear needs: codes, scales and T for M rows, each part
- * 256-byte aligned.  0 for a bad format or shape. */
+/* Workspace svdq_linear needs: codes, scales and T for M rows, and Kernel A's
+ * partial sums (svdq_quantize_down_workspace_bytes), each part 256-byte
+ * aligned.  0 for a bad format or shape. */
 size_t svdq_linear_workspace_bytes(int M, int K, int r, svdq_format fmt);
 
 /*

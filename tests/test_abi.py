@@ -47,16 +47,31 @@ def test_sizes():
     assert L.svdq_scale_row_bytes(3072, 2) == 192
     assert L.svdq_code_row_bytes(100, 0) == 0
     assert L.svdq_code_row_bytes(64, 7) == 0
-    # codes + scales + T, each 256-byte aligned
+    # codes + scales + T + Kernel A's partial sums, each 256-byte aligned
     M, K, r = 4608, 3072, 32
-    exp = sum(((b + 255) // 256) * 256 for b in (M * K // 2, M * K // 64 * 2, M * r * 2))
+    part = binding.quantize_down_workspace_bytes(M, K, r, "int4")
+    exp = sum(((b + 255) // 256) * 256 for b in (M * K // 2, M * K // 64 * 2, M * r * 2)) + part
     assert binding.linear_workspace_bytes(M, K, r, "int4") == exp
     assert binding.linear_workspace_bytes(M, 100, r, "int4") == 0
     assert binding.linear_unfused_workspace_bytes(M, 9216, K, r, "int4") == exp + M * 9216 * 2
 
 
-def qd(x=P, l1=P, M=16, K=64, r=16, fmt=0, xq=P, xs=P, t=P):
-    return binding.lib().svdq_quantize_down(x, l1, M, K, r, fmt, xq, xs, t, None)
+def test_quantize_down_workspace_sizes():
+    # fp32 partial sums of T: a whole number (>= 2) of [M, r] slices when K is sliced
+    for M, K, r in [(4608, 3072, 32), (4608, 12288, 32), (4608, 12288, 64), (300, 2048, 16)]:
+        b = binding.quantize_down_workspace_bytes(M, K, r, "int4_e2m3")
+        assert b % 256 == 0 and b >= 2 * M * r * 4, (M, K, r, b)
+        slices = b // (M * r * 4)
+        assert slices * M * r * 4 <= b < (slices + 1) * M * r * 4
+        assert slices <= K // 64
+    assert binding.quantize_down_workspace_bytes(4608, 3072, 0, "int4") == 0     # no branch, no partials
+    assert binding.quantize_down_workspace_bytes(16, 128, 16, "int4") == 0       # one slice
+    assert binding.quantize_down_workspace_bytes(16, 100, 16, "int4") == 0       # bad shape
+    assert binding.quantize_down_workspace_bytes(16, 128, 16, 9) == 0            # bad format
+
+
+def qd(x=P, l1=P, M=16, K=64, r=16, fmt=0, xq=P, xs=P, t=P, ws=None, ws_bytes=0):
+    return binding.lib().svdq_quantize_down(x, l1, M, K, r, fmt, xq, xs, t, ws, ws_bytes, None)
 
 
 def test_quantize_down_validation():
@@ -76,6 +91,12 @@ def test_quantize_down_validation():
     assert qd(M=0, r=0, l1=None, t=None) == OK
     assert qd(M=0, x=None, xq=None, xs=None, l1=None, t=None) == OK   # zero-size tensors have NULL data
     assert qd(M=0, K=100) == SHAPE
+    # a workspace that is given must be aligned and large enough (checked before any launch)
+    M, K = 4608, 3072
+    need = binding.quantize_down_workspace_bytes(M, K, 16, "int4")
+    assert need > 0
+    assert qd(M=M, K=K, ws=P, ws_bytes=need - 256) == WORKSPACE
+    assert qd(M=M, K=K, ws=MIS, ws_bytes=need) == ALIGN
 
 
 def gm(xq=P, xs=P, t=P, wq=P, ws=P, l2=P, bias=P, M=16, N=16, K=64, r=16, fmt=0, y=P):

@@ -83,13 +83,20 @@ SHAPES = [  # M, K, N, r
 ]
 
 
+# Kernel A shapes: the GEMM shapes plus long K (K sliced over many workgroups, several chunks per
+# wave) with ragged M, and r = 48 / 64 (32-row blocks)
+QD_SHAPES = SHAPES + [(300, 2048, 16, 32), (77, 12288, 16, 16), (200, 4096, 16, 64), (129, 1024, 16, 48)]
+
+
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M,K,N,r", SHAPES)
-def test_quantize_down_parity(fmt, M, K, N, r):
-    log(f"quantize_down {fmt} M={M} K={K} r={r}")
+@pytest.mark.parametrize("M,K,N,r", QD_SHAPES)
+@pytest.mark.parametrize("sliced", [True, False])
+def test_quantize_down_parity(fmt, M, K, N, r, sliced):
+    log(f"quantize_down {fmt} M={M} K={K} r={r} sliced={sliced} "
+        f"workspace={binding.quantize_down_workspace_bytes(M, K, r, fmt)}")
     x_hat, _, l1, _, _ = draw(M * 7 + K + r, M, K, 16, r)
     q, s, stored = oracle.quant.quantize(x_hat, fmt)
-    xq, xs, t = binding.svdq_quantize_down(dev(x_hat), dev(l1.T) if r else None, fmt)
+    xq, xs, t = binding.svdq_quantize_down(dev(x_hat), dev(l1.T) if r else None, fmt, no_workspace=not sliced)
     assert same_bytes(host(xq), dev_codes(stored, fmt))
     assert same_bytes(host(xs), dev_scales(s, fmt))
     if r:
@@ -98,6 +105,21 @@ def test_quantize_down_parity(fmt, M, K, N, r):
         assert rel_fro(tg, tr) <= TOL
         ok, worst = within_sum_bound(tg, tr, np.abs(x_hat.astype(np.float64)) @ np.abs(l1.astype(np.float64)), K)
         assert ok, worst
+
+
+def test_quantize_down_deterministic_and_workspace_reuse():
+    # the sliced path adds the slices in a fixed order: repeated calls, a reused workspace
+    # holding the previous call's partials, and a larger workspace give identical bytes
+    M, K, r, fmt = 300, 4096, 32, "int4_e2m3"
+    x_hat, _, l1, _, _ = draw(91, M, K, 16, r)
+    gx, gl = dev(x_hat), dev(l1.T)
+    nb = binding.quantize_down_workspace_bytes(M, K, r, fmt)
+    assert nb > 0
+    ws = torch.full((nb + 4096,), 0xFF, dtype=torch.uint8, device="cuda")
+    ref = [host(v) for v in binding.svdq_quantize_down(gx, gl, fmt, workspace=ws)]
+    for _ in range(2):
+        got = [host(v) for v in binding.svdq_quantize_down(gx, gl, fmt, workspace=ws)]
+        assert all(same_bytes(a, b) for a, b in zip(got, ref))
 
 
 @pytest.mark.parametrize("fmt", FMTS)
