@@ -210,33 +210,80 @@ def test_e2m3_format_has_int4_codes_and_scales(rng):
     assert np.array_equal(quant.unpack_e2m3(st6, 128), q4)
 
 
-def _fast_code(x32, s32, qmax):
-    """Kernel A's division-free code rule, simulated in IEEE fp32 (numpy float32 ops)."""
+def _fma32(a, b, c):
+    """IEEE fp32 fused multiply-add RN32(a*b + c) of float32 arrays, exactly: the product is
+    exact in float64, TwoSum gives the sum as s + err exactly, and the only case where
+    RN32(s) differs from RN32(s + err) is s on an fp32 midpoint with err != 0."""
+    p = a.astype(np.float64) * b.astype(np.float64)
+    c64 = c.astype(np.float64)
+    s = p + c64
+    bb = s - p
+    err = (p - (s - bb)) + (c64 - bb)
+    r = s.astype(np.float32)
+    r64 = r.astype(np.float64)
+    up = np.where(r64 < s, np.nextafter(r, np.float32(np.inf)), r)
+    down = np.where(r64 > s, np.nextafter(r, np.float32(-np.inf)), r)
+    mid = (up != down) & (s == (up.astype(np.float64) + down.astype(np.float64)) / 2)
+    return np.where(mid & (err > 0), up, np.where(mid & (err < 0), down, r)).astype(np.float32)
+
+
+def _fast_code(x32, s32, qmax, r_ulps=0):
+    """Kernel A's code rule, simulated in IEEE fp32: r = a reciprocal of s within one ulp
+    (r_ulps moves RN(1/s) by one ulp either way, as v_rcp_f32 may), t0 = RN(x r), one fma
+    refinement t = fma(fma(-t0, s, x), r, t0), then clamp and round half to even."""
     with np.errstate(divide="ignore"):
         r = np.where(s32 == 0, np.float32(0), np.float32(1) / s32).astype(np.float32)
-    t = (x32 * r).astype(np.float32)
-    tf = np.floor(t).astype(np.float32)
-    tie = np.abs((t - tf).astype(np.float32) - np.float32(0.5)) < np.float32(2.0 ** -14)
-    q = np.rint(np.where(tie, (tf + np.float32(0.5)).astype(np.float32), t))
-    return np.clip(q, -qmax, qmax)
+    if r_ulps:
+        r = np.where(s32 == 0, r, np.nextafter(r, np.float32(np.inf * r_ulps))).astype(np.float32)
+    t0 = (x32 * r).astype(np.float32)
+    t = _fma32(_fma32(-t0, s32, x32), r, t0)
+    return np.rint(np.clip(t, -qmax, qmax))
 
 
 @pytest.mark.parametrize("qmax", [7, 127])
-def test_division_free_code_rule_matches_definition_exhaustively(qmax):
-    """Every fp16 value against a spread of fp16 scales (normal and subnormal): the kernel's
-    reciprocal-and-tie rule gives clamp(rint(fp32(x) / s)) exactly."""
+@pytest.mark.parametrize("r_ulps", [0, 1, -1])
+def test_division_free_code_rule_matches_definition_exhaustively(qmax, r_ulps):
+    """Every fp16 value against a spread of fp16 scales (normal and subnormal), with the
+    reciprocal correctly rounded or one ulp off either way: the kernel's reciprocal-and-
+    refinement rule gives clamp(rint(fp32(x) / s)) exactly."""
     xs = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float32)   # all finite >= 0
     xs = np.concatenate([xs, -xs])
     g = np.random.default_rng(qmax)
     scales = np.concatenate([
         np.arange(1, 1024, 37, dtype=np.uint16),                 # subnormal fp16 scales
         g.integers(0x0400, 0x7BFF, 120).astype(np.uint16),       # normal fp16 scales
-        np.array([0x3C00, 0x3800, 0x2E66, 0x0001, 0x03FF], np.uint16),
+        np.array([0x3C00, 0x3800, 0x2E66, 0x0001, 0x03FF, 0x7BFF], np.uint16),
     ]).view(np.float16).astype(np.float32)
     for s in scales:
         s32 = np.float32(s)
         ref = np.clip(np.rint((xs / s32).astype(np.float32)), -qmax, qmax)
-        got = _fast_code(xs, np.full_like(xs, s32), qmax)
+        got = _fast_code(xs, np.full_like(xs, s32), qmax, r_ulps)
         assert np.array_equal(got, ref), float(s)
     # the zero scale gives code 0
     assert not _fast_code(xs[:100], np.zeros(100, np.float32), qmax).any()
+
+
+def test_fma32_emulation():
+    # the fp32 fma emulation against exact rational arithmetic on random and cancelling inputs
+    from fractions import Fraction
+    g = np.random.default_rng(5)
+    a = g.standard_normal(3000).astype(np.float32)
+    b = g.standard_normal(3000).astype(np.float32)
+    c = np.where(g.random(3000) < 0.5, -(a * b).astype(np.float32), g.standard_normal(3000).astype(np.float32))
+    got = _fma32(a, b, c)
+    for i in range(3000):
+        exact = Fraction(float(a[i])) * Fraction(float(b[i])) + Fraction(float(c[i]))
+        lo = np.float32(float(exact))                  # candidates around the exact value
+        cands = [lo, np.nextafter(lo, np.float32(np.inf)), np.nextafter(lo, np.float32(-np.inf))]
+        best = min(cands, key=lambda v: (abs(Fraction(float(v)) - exact), int(np.float32(v).view(np.uint32)) & 1))
+        assert got[i] == best, (a[i], b[i], c[i])
+
+
+@pytest.mark.parametrize("qmax", [7, 127])
+def test_division_free_scale_rule_exhaustively(qmax):
+    """Kernel A's scale fp16_rne(amax * RN(1/qmax)) equals fp16_rne(RN(amax / qmax)) for every
+    finite fp16 absmax."""
+    a = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float32)
+    ref = (a / np.float32(qmax)).astype(np.float32).astype(np.float16)
+    got = (a * (np.float32(1) / np.float32(qmax))).astype(np.float32).astype(np.float16)
+    assert np.array_equal(ref.view(np.uint16), got.view(np.uint16))
