@@ -11,7 +11,9 @@
 // Each INT4 code q is held as the E2M3 subnormal of q/8, so 32 codes of a row
 // (one half of a group) are the six-dword operand of
 // v_mfma_scale_f32_32x32x64_f8f6f4 in FP6 mode, and one MFMA per 32 x 32 tile
-// and group returns P_g / 64 in fp32 exactly.  The scale products
+// and group returns P_g in fp32 exactly: the products of the E2M3 values are P_g / 64, and the
+// instruction's power-of-two block scale for the A operand (E8M0 133 = 2^6) multiplies by 64
+// exactly.  The scale products
 // S = sw sx^T of a tile come from one v_mfma_f32_32x32x8_f16 whose operands
 // carry the scales in K slot 0 and zeros elsewhere (exact), so the vector ALU
 // spends one fma per output element and group: acc += P_g * S.
@@ -223,7 +225,7 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
     for (int tj = 0; tj < 2; tj++)
 #pragma unroll
       for (int ti = 0; ti < 2; ti++) {
-        const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.wo[tj], o.xo[ti], v16f{}, 2, 2, 0, 127, 0, 127);
+        const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.wo[tj], o.xo[ti], v16f{}, 2, 2, 0, 133, 0, 127);
         const v16f sc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h_t, o.swo[tj]),
                                                               __builtin_bit_cast(v4h_t, o.sxo[ti]), v16f{}, 0, 0, 0);
 #pragma unroll
@@ -288,12 +290,6 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
     }
 
     // ---- epilogue in buffer 1 of the ring (every wave passed the last barrier)
-#pragma unroll
-    for (int a = 0; a < 2; a++)
-#pragma unroll
-      for (int b = 0; b < 2; b++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) acc[a][b][i] *= 64.0f;   // P_g / 64 -> P_g (exact)
 
     if (RB > 0) {
       // L2[:, n0:n0+128] transposed into LDS as [n][k] (row stride (R+8) halves), then
@@ -444,7 +440,7 @@ k_gemm3_tail(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, cons
       if (g + 4 * PD < G) load(g + 4 * PD, ring[j]);
       const v8i xo = v8i{(int)cur.x0.x, (int)cur.x0.y, (int)cur.x0.z, (int)cur.x0.w, (int)cur.x1.x, (int)cur.x1.y, 0, 0};
       const v8i wo = v8i{(int)cur.w0.x, (int)cur.w0.y, (int)cur.w0.z, (int)cur.w0.w, (int)cur.w1.x, (int)cur.w1.y, 0, 0};
-      const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wo, xo, v16f{}, 2, 2, 0, 127, 0, 127);
+      const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wo, xo, v16f{}, 2, 2, 0, 133, 0, 127);
       const v16f sc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h_t, make_uint2(cur.sw, 0u)),
                                                             __builtin_bit_cast(v4h_t, make_uint2(cur.sx, 0u)),
                                                             v16f{}, 0, 0, 0);
@@ -460,8 +456,6 @@ k_gemm3_tail(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, cons
   if (wave != 0) return;
 #pragma unroll
   for (int i = 0; i < 16; i++) acc[i] = ((acc[i] + red[0][i][lane]) + red[1][i][lane]) + red[2][i][lane];
-#pragma unroll
-  for (int i = 0; i < 16; i++) acc[i] *= 64.0f;   // P_g / 64 -> P_g (exact)
   // up projection on the 32 x 32 sub-tile: row operand L2^T (columns n), column operand T (rows m)
 #pragma unroll
   for (int kb = 0; kb < RB; kb++) {
