@@ -7,7 +7,9 @@ launch adds the slices' partial sums of T) then Kernel B (W4A4 GEMM + up
 projection + bias), the same launches svdq_linear makes.  The headline line is the FLUX-like
 fused QKV projection (M=4608 tokens, K=3072, N=9216, rank 32, INT4 group 64);
 the same run also times, each on its own seeded layer and with fewer steps:
-  * the FLUX-like MLP pair: fc1 (K=3072, N=12288) and fc2 (K=12288, N=3072);
+  * the FLUX-like MLP pair: fc1 (K=3072, N=12288) and fc2 (K=12288, N=3072), and fc1 on
+    its first 64, 256 and 1024 token rows (small-batch sweep, each point against the bound
+    its arithmetic intensity puts it under: HBM below 625 op/B, MFMA above);
   * on the QKV layer: the bare W4A4 GEMM (r = 0: no branch in either kernel),
     the unfused branch (down projection, quantization, GEMM, up projection as
     separate launches with an fp16 intermediate), and the W4A16 control (fp16
@@ -209,6 +211,44 @@ class Layer:
                 "ka_us": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3,
                 "kb_us": float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3}
 
+    def time_rows(self, m, steps, warmup):
+        """The fused layer on the first m token rows (own code/scale/T/Y buffers, same weights)."""
+        b, torch = self.binding, self.torch
+        K, N, r, fmt = self.K, self.N, self.r, self.fmt
+        sets = []
+        for st in self.sets:
+            sets.append(dict(
+                x=st["x"][:m], l1t=st["l1t"], wq=st["wq"], ws=st["ws"], l2=st["l2"], b=st["b"],
+                xq=torch.empty(b.code_shape(m, K, fmt), dtype=torch.uint8, device="cuda"),
+                xs=torch.empty(b.scale_shape(m, K, fmt), dtype=b.scale_dtype(fmt), device="cuda"),
+                t=torch.empty((m, r), dtype=torch.float16, device="cuda") if r else None,
+                y=torch.empty((m, N), dtype=torch.float16, device="cuda"),
+                wsa=torch.empty(max(16, b.quantize_down_workspace_bytes(m, K, r, fmt)), dtype=torch.uint8,
+                                device="cuda")))
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+
+        def one(i, e=None):
+            st = sets[i % ROTATE]
+            if e is not None:
+                e[0].record()
+            b.svdq_quantize_down(st["x"], st["l1t"], fmt, xq=st["xq"], xs=st["xs"], t=st["t"], workspace=st["wsa"])
+            if e is not None:
+                e[1].record()
+            b.svdq_gemm_w4a4_up(st["xq"], st["xs"], st["t"], st["wq"], st["ws"], st["l2"], st["b"], K, fmt, y=st["y"])
+            if e is not None:
+                e[2].record()
+        for i in range(warmup):
+            one(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            one(i, ev[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return {"us_per_layer": wall * 1e6 / steps,
+                "ka_us": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3,
+                "kb_us": float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3}
+
     def time_call(self, fn, steps, warmup):
         torch = self.torch
         for i in range(warmup):
@@ -386,6 +426,27 @@ def main():
                             "kernels_us": {"quantize_down": round(res["ka_us"], 2), "gemm_w4a4_up": round(res["kb_us"], 2)},
                             "kernel_b_pct_int8_peak": round(100.0 * o_b / (res["kb_us"] * 1e-6) / 1e12 / INT8_PEAK_TOPS, 2)}
             log(f"{name}: {others[name]}")
+            if name == "fc1":
+                # small-batch sweep: where the layer moves from HBM-bound to MFMA-bound
+                sweep = {}
+                for m in (64, 256, 1024):
+                    rs = Lo.time_rows(m, es, ew)
+                    a_b, b_b = algorithmic_bytes(m, Lo.K, Lo.N, Lo.r, 6 if fmt == "int4_e2m3" else 4)
+                    m_ops = 2.0 * m * Lo.N * Lo.K
+                    layer_s = rs["us_per_layer"] * 1e-6
+                    intensity = m_ops / (a_b + b_b)
+                    bound = "hbm" if intensity < INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+                    sweep[str(m)] = {
+                        "us_per_layer": round(rs["us_per_layer"], 2),
+                        "kernels_us": {"quantize_down": round(rs["ka_us"], 2), "gemm_w4a4_up": round(rs["kb_us"], 2)},
+                        "tops": round(m_ops / layer_s / 1e12, 2),
+                        "algorithmic_bytes": a_b + b_b,
+                        "ops_per_byte": round(intensity, 1),
+                        "bound": bound,
+                        "frac_of_int8_peak": round(m_ops / layer_s / 1e12 / INT8_PEAK_TOPS, 4),
+                        "frac_of_8TBps": round((a_b + b_b) / layer_s / 1e9 / HBM_PEAK_GBS, 4)}
+                    log(f"fc1 M={m}: {sweep[str(m)]}")
+                out["small_batch_fc1"] = sweep
             del Lo
             torch.cuda.empty_cache()
         out["other_workloads"] = others
