@@ -489,6 +489,138 @@ k_gemm3_tail(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, cons
   }
 }
 
+// Few token rows (weight-streaming regime): one workgroup per 32 output columns and a slab of
+// up to 128 rows (MT tiles of 32; blockIdx.y picks the slab), so each weight row is read once
+// per slab; its four waves split K
+// (groups w, w + 4, ...), holding PD groups of loads in flight straight into registers, and add
+// their partial sums in LDS in a fixed order, one row tile at a time; wave 0 then applies the up
+// projection and the bias and stores.
+template <int RB, bool BIAS, int MT>
+__global__ void __launch_bounds__(NT, 2)
+k_gemm3_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __half* __restrict__ t,
+               const uint8_t* __restrict__ wq, const __half* __restrict__ ws, const __half* __restrict__ l2,
+               const __half* __restrict__ bias, int M, int N, int K, __half* __restrict__ y) {
+  constexpr int R = RB * 16;
+  constexpr int PD = MT == 1 ? 4 : (MT == 2 ? 2 : 1);   // groups in flight per wave
+  __shared__ __attribute__((aligned(16))) float red[3][16][64];   // partials of waves 1..3, one row tile
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, r32 = lane & 31;
+  const int G = K >> 6;
+  const int nb = blockIdx.x * 32;
+  const int mb = blockIdx.y * 32 * MT;
+  const int n = min(nb + r32, N - 1);                    // this lane's weight row
+  int mrow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) mrow[mt] = min(mb + mt * 32 + r32, M - 1);
+
+  typedef _Float16 v4h_t __attribute__((ext_vector_type(4)));
+  struct Op { uint4 w0; uint2 w1; uint32_t sw; uint4 x0[MT]; uint2 x1[MT]; uint32_t sx[MT]; };
+  auto load = [&](int g, Op& o) {
+    const uint8_t* pw = wq + ((size_t)g * N + n) * GB;
+    o.w0 = *reinterpret_cast<const uint4*>(pw + 16 * h);
+    o.w1 = *reinterpret_cast<const uint2*>(pw + 32 + 8 * h);
+    // K slot 0 holds the scale for the lower-K-half lanes; the upper half contributes zeros
+    o.sw = h ? 0u : (uint32_t)reinterpret_cast<const unsigned short*>(ws)[(size_t)g * N + n];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      const uint8_t* px = xq + ((size_t)g * M + mrow[mt]) * GB;
+      o.x0[mt] = *reinterpret_cast<const uint4*>(px + 16 * h);
+      o.x1[mt] = *reinterpret_cast<const uint2*>(px + 32 + 8 * h);
+      o.sx[mt] = h ? 0u : (uint32_t)reinterpret_cast<const unsigned short*>(xs)[(size_t)g * M + mrow[mt]];
+    }
+  };
+  v16f acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) acc[mt][i] = 0.f;
+  Op ring[PD];
+#pragma unroll
+  for (int j = 0; j < PD; j++)
+    if (wave + 4 * j < G) load(wave + 4 * j, ring[j]);
+  for (int g0 = wave; g0 < G; g0 += 4 * PD) {
+#pragma unroll
+    for (int j = 0; j < PD; j++) {
+      const int g = g0 + 4 * j;
+      if (g >= G) break;
+      const Op cur = ring[j];
+      if (g + 4 * PD < G) load(g + 4 * PD, ring[j]);
+      const v8i wo = v8i{(int)cur.w0.x, (int)cur.w0.y, (int)cur.w0.z, (int)cur.w0.w, (int)cur.w1.x, (int)cur.w1.y, 0, 0};
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) {
+        const v8i xo = v8i{(int)cur.x0[mt].x, (int)cur.x0[mt].y, (int)cur.x0[mt].z, (int)cur.x0[mt].w,
+                           (int)cur.x1[mt].x, (int)cur.x1[mt].y, 0, 0};
+        const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wo, xo, v16f{}, 2, 2, 0, 133, 0, 127);
+        const v16f sc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h_t, make_uint2(cur.sw, 0u)),
+                                                              __builtin_bit_cast(v4h_t, make_uint2(cur.sx[mt], 0u)),
+                                                              v16f{}, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 16; i++) acc[mt][i] = __builtin_fmaf(p[i], sc[i], acc[mt][i]);
+      }
+    }
+  }
+  // the four waves' partials, added in wave order, one row tile at a time
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) {
+    if (wave > 0) {
+#pragma unroll
+      for (int i = 0; i < 16; i++) red[wave - 1][i][lane] = acc[mt][i];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; i++) acc[mt][i] = ((acc[mt][i] + red[0][i][lane]) + red[1][i][lane]) + red[2][i][lane];
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
+  // up projection: row operand L2^T (columns n, gathered once), column operand T (rows m)
+  uint4 lw[RB > 0 ? RB : 1];
+#pragma unroll
+  for (int kb = 0; kb < RB; kb++) {
+    uint16_t lv[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) lv[e] = __half_as_ushort(l2[(size_t)(kb * 16 + 8 * h + e) * N + n]);
+    lw[kb] = make_uint4(lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16),
+                        lv[4] | ((uint32_t)lv[5] << 16), lv[6] | ((uint32_t)lv[7] << 16));
+  }
+  float bv[4][4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int no = nb + 8 * q + 4 * h;
+#pragma unroll
+    for (int j = 0; j < 4; j++) bv[q][j] = 0.f;
+    if (BIAS && no < N) {
+      const uint2 braw = *reinterpret_cast<const uint2*>(bias + no);
+      bv[q][0] = __half2float(__ushort_as_half((unsigned short)(braw.x & 0xFFFFu)));
+      bv[q][1] = __half2float(__ushort_as_half((unsigned short)(braw.x >> 16)));
+      bv[q][2] = __half2float(__ushort_as_half((unsigned short)(braw.y & 0xFFFFu)));
+      bv[q][3] = __half2float(__ushort_as_half((unsigned short)(braw.y >> 16)));
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) {
+#pragma unroll
+    for (int kb = 0; kb < RB; kb++) {
+      const uint4 tv = *reinterpret_cast<const uint4*>(t + (size_t)mrow[mt] * R + kb * 16 + 8 * h);
+      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(lw[kb]), as_h8(tv), acc[mt], 0, 0, 0);
+    }
+    // lane owns row mb + mt*32 + r32 and columns nb + 8 q + 4 h + j (reg 4 q + j)
+    const int mo = mb + mt * 32 + r32;
+    if (mo >= M) continue;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int no = nb + 8 * q + 4 * h;
+      if (no >= N) continue;
+      uint32_t hv[4];
+#pragma unroll
+      for (int j = 0; j < 4; j++) hv[j] = __half_as_ushort(__float2half_rn(acc[mt][4 * q + j] + bv[q][j]));
+      *reinterpret_cast<uint2*>(y + (size_t)mo * N + no) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+    }
+  }
+}
+
 // Workgroups that fit on the device at once (two per CU), cached per device.
 static int resident_blocks() {
   static int cached[64] = {0};
@@ -504,8 +636,24 @@ static int resident_blocks() {
 
 // Full rounds of the persistent kernel, then (when the remainder is at most a quarter of a
 // round) the remaining tiles as sub-tiles; otherwise the persistent kernel takes them all.
+// Up to this many token rows the weight-streaming kernel runs (in 128-row slabs).
+constexpr int kSkinnyRows = 256;
+
+template <int RB, bool BIAS, int MT>
+static hipError_t launch_g3_skinny(const GemmArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm3_skinny<RB, BIAS, MT>), dim3((a.N + 31) / 32, (a.M + 32 * MT - 1) / (32 * MT)),
+                     dim3(NT), 0, s, (const uint8_t*)a.xq,
+                     (const __half*)a.xs, (const __half*)a.t, (const uint8_t*)a.wq, (const __half*)a.ws,
+                     (const __half*)a.l2, (const __half*)a.bias, a.M, a.N, a.K, (__half*)a.y);
+  return hipGetLastError();
+}
+
 template <int RB, bool BIAS>
 static hipError_t launch_g3(const GemmArgs& a, hipStream_t s) {
+  // few token rows: the weight-streaming kernel
+  if (a.M <= 32) return launch_g3_skinny<RB, BIAS, 1>(a, s);
+  if (a.M <= 64) return launch_g3_skinny<RB, BIAS, 2>(a, s);
+  if (a.M <= kSkinnyRows) return launch_g3_skinny<RB, BIAS, 4>(a, s);
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const int slots = resident_blocks();
   const int rem = tiles % slots;
