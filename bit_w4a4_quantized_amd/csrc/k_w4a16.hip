@@ -10,8 +10,9 @@
 // with the bit trick fp16(0x6400 | (u ^ 8)) - 1032 = q (u the nibble), then one
 // packed fp16 multiply by the column's scale.
 //
-// Work decomposition (gfx950, wave64): workgroup tile 128 x 128, four waves in
-// 2 x 2 of 64 x 64, two workgroups per CU, persistent over tiles.  K advances
+// Work decomposition (gfx950, wave64): workgroup tile 128 x 128, each of the four
+// waves owning 32 output columns over all 128 rows (so each weight is dequantized
+// once per tile), two workgroups per CU, persistent over tiles.  K advances
 // one group of 64 at a time through two LDS buffers, filled straight from global
 // memory by LDS-DMA buffer loads one group ahead.  The MFMA K order is permuted
 // the same way for both operands: at k-step ks the upper-half lanes carry
@@ -32,8 +33,8 @@ constexpr int L_W = 16384;                  // W: [128 rows][2 slots of 16 bytes
 constexpr int L_S = 20480;                  // scales: one dword (fp16, zero-extended) per row
 constexpr int GROUP = L_S + 512;            // 20992
 constexpr int RING = 2 * GROUP;
-constexpr int E_Y = GROUP;                  // epilogue: buffer 1, per wave 32 rows x 136 bytes
-constexpr int E_YS = 136;
+constexpr int E_Y = GROUP;                  // epilogue: buffer 1, per wave 32 rows x 80 bytes
+constexpr int E_YS = 80;
 static_assert(E_Y + 4 * 32 * E_YS <= RING, "output staging must fit buffer 1");
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -101,7 +102,6 @@ k_w4a16(const __half* __restrict__ x, const uint8_t* __restrict__ wq, const __ha
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r32 = lane & 31;
-  const int wm = wave >> 1, wn = wave & 1;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int tiles = tiles_m * tiles_n;
   const int G = K >> 6;
@@ -144,15 +144,14 @@ k_w4a16(const __half* __restrict__ x, const uint8_t* __restrict__ wq, const __ha
   };
   auto wait_loads = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
-  int xo[2][4], wo[2], so[2];
+  // per-lane LDS read offsets: X rows i*32 + r32 (row tile i; the swizzle depends on the row
+  // only through r32 % 8, so row tile i is +4096 bytes), this wave's 32 weight rows
+  int xo[4];
 #pragma unroll
-  for (int i = 0; i < 2; i++) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++) xo[i][ks] = L_X + xslot(wm * 64 + i * 32 + r32, 4 * h + ks);
-    wo[i] = L_W + wslot(wn * 64 + i * 32 + r32, h);
-    so[i] = L_S + (wn * 64 + i * 32 + r32) * 4;
-  }
-  v16f acc[2][2];
+  for (int ks = 0; ks < 4; ks++) xo[ks] = L_X + xslot(r32, 4 * h + ks);
+  const int wo = L_W + wslot(wave * 32 + r32, h);
+  const int so = L_S + (wave * 32 + r32) * 4;
+  v16f acc[4];                               // [row tile i]: lane -> row i*32 + r32, this wave's 32 columns
 
   int tile = blockIdx.x;
   Src cur = tile_src(tile);
@@ -167,31 +166,26 @@ k_w4a16(const __half* __restrict__ x, const uint8_t* __restrict__ wq, const __ha
     wait_loads();
     __syncthreads();
 #pragma unroll
-    for (int a = 0; a < 2; a++)
+    for (int a = 0; a < 4; a++)
 #pragma unroll
-      for (int b = 0; b < 2; b++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
+      for (int i = 0; i < 16; i++) acc[a][i] = 0.f;
 
     auto step = [&](int g, int buf) {
-      uint4 wd[2][4];
-      uint4 xv[2][4];
+      uint4 wd[4];
+      uint4 xv[4][4];
       if (g < G) {
         const uint8_t* b = lds + buf * GROUP;
+        const uint4 w = *reinterpret_cast<const uint4*>(b + wo);
+        const uint32_t sc = *reinterpret_cast<const uint32_t*>(b + so);
+        const uint32_t s2 = sc | (sc << 16);
+        wd[0] = dequant8(w.x, s2);
+        wd[1] = dequant8(w.y, s2);
+        wd[2] = dequant8(w.z, s2);
+        wd[3] = dequant8(w.w, s2);
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-          const uint4 w = *reinterpret_cast<const uint4*>(b + wo[j]);
-          const uint32_t s = *reinterpret_cast<const uint32_t*>(b + so[j]);
-          const uint32_t s2 = s | (s << 16);
-          wd[j][0] = dequant8(w.x, s2);
-          wd[j][1] = dequant8(w.y, s2);
-          wd[j][2] = dequant8(w.z, s2);
-          wd[j][3] = dequant8(w.w, s2);
-        }
+        for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-          for (int ks = 0; ks < 4; ks++) xv[i][ks] = *reinterpret_cast<const uint4*>(b + xo[i][ks]);
+          for (int ks = 0; ks < 4; ks++) xv[i][ks] = *reinterpret_cast<const uint4*>(b + xo[ks] + i * 4096);
       }
       __builtin_amdgcn_sched_barrier(0);
       const bool nx = g + 1 >= G;
@@ -202,10 +196,8 @@ k_w4a16(const __half* __restrict__ x, const uint8_t* __restrict__ wq, const __ha
 #pragma unroll
         for (int ks = 0; ks < 4; ks++)
 #pragma unroll
-          for (int j = 0; j < 2; j++)
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-              acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(wd[j][ks]), as_h8(xv[i][ks]), acc[j][i], 0, 0, 0);
+          for (int i = 0; i < 4; i++)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(wd[ks]), as_h8(xv[i][ks]), acc[i], 0, 0, 0);
       }
       if (g + 1 < GE) wait_loads();
       __syncthreads();
@@ -215,40 +207,44 @@ k_w4a16(const __half* __restrict__ x, const uint8_t* __restrict__ wq, const __ha
       step(g + 1, 1);
     }
 
-    // ---- epilogue in buffer 1: bias, fp16, 16-byte row stores through LDS
+    // ---- epilogue in buffer 1: bias, fp16, 16-byte row stores through LDS (per wave 32 rows of
+    // its 32 columns at a time)
     uint8_t* ys = lds + E_Y + wave * 32 * E_YS;
+    float bv[4][4];
 #pragma unroll
-    for (int ti = 0; ti < 2; ti++) {
+    for (int q = 0; q < 4; q++) {
 #pragma unroll
-      for (int tj = 0; tj < 2; tj++)
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-          const int nl = tj * 32 + 8 * q + 4 * h;    // column within the wave's 64
-          float bv[4] = {0.f, 0.f, 0.f, 0.f};
-          if (BIAS) {
-            const int n = n0 + wn * 64 + nl;
-            if (n < N) {
-              const uint2 braw = *reinterpret_cast<const uint2*>(bias + n);
-              bv[0] = __half2float(__ushort_as_half((unsigned short)(braw.x & 0xFFFFu)));
-              bv[1] = __half2float(__ushort_as_half((unsigned short)(braw.x >> 16)));
-              bv[2] = __half2float(__ushort_as_half((unsigned short)(braw.y & 0xFFFFu)));
-              bv[3] = __half2float(__ushort_as_half((unsigned short)(braw.y >> 16)));
-            }
-          }
-          uint32_t hv[4];
-#pragma unroll
-          for (int j = 0; j < 4; j++) hv[j] = __half_as_ushort(__float2half_rn(acc[tj][ti][4 * q + j] + bv[j]));
-          *reinterpret_cast<uint2*>(ys + r32 * E_YS + nl * 2) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+      for (int j = 0; j < 4; j++) bv[q][j] = 0.f;
+      if (BIAS) {
+        const int n = n0 + wave * 32 + 8 * q + 4 * h;
+        if (n < N) {
+          const uint2 braw = *reinterpret_cast<const uint2*>(bias + n);
+          bv[q][0] = __half2float(__ushort_as_half((unsigned short)(braw.x & 0xFFFFu)));
+          bv[q][1] = __half2float(__ushort_as_half((unsigned short)(braw.x >> 16)));
+          bv[q][2] = __half2float(__ushort_as_half((unsigned short)(braw.y & 0xFFFFu)));
+          bv[q][3] = __half2float(__ushort_as_half((unsigned short)(braw.y >> 16)));
         }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int nl = 8 * q + 4 * h;        // column within the wave's 32
+        uint32_t hv[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) hv[j] = __half_as_ushort(__float2half_rn(acc[i][4 * q + j] + bv[q][j]));
+        *reinterpret_cast<uint2*>(ys + r32 * E_YS + nl * 2) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+      }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-      for (int it = 0; it < 4; it++) {
-        const int rl = it * 8 + (lane >> 3), c = (lane & 7) * 8;
+      for (int it = 0; it < 2; it++) {
+        const int rl = it * 16 + (lane >> 2), c = (lane & 3) * 8;   // row within the 32, column
         const uint2 a = *reinterpret_cast<const uint2*>(ys + rl * E_YS + c * 2);
         const uint2 b = *reinterpret_cast<const uint2*>(ys + rl * E_YS + c * 2 + 8);
-        const int m = m0 + wm * 64 + ti * 32 + rl, n = n0 + wn * 64 + c;
+        const int m = m0 + i * 32 + rl, n = n0 + wave * 32 + c;
         if (m < M && n < N) *reinterpret_cast<uint4*>(y + (size_t)m * N + n) = make_uint4(a.x, a.y, b.x, b.y);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
