@@ -25,7 +25,7 @@
 //
 // Work decomposition (gfx950, wave64): workgroup tile 128 x 128, four waves in
 // 2 x 2 of 64 x 64 (2 x 2 MFMA tiles), two workgroups per CU, persistent (each
-// workgroup loops over tiles).  K advances in stages of two groups through two
+// workgroup loops over tiles).  K advances in stages of three groups through two
 // LDS buffers.  Operands go from global memory straight into LDS (buffer loads
 // with the LDS-DMA form: no registers, no LDS store instructions), issued one
 // stage ahead; each wave first reads all of a stage's MFMA operands into
@@ -48,7 +48,7 @@ namespace svdq {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, NT = 256, KC = 2;
+constexpr int BM = 128, BN = 128, NT = 256, KC = 3;   // 3 groups a stage: fewer barriers; 2 x 80640 B of LDS per CU
 constexpr int GB = 48;                      // container bytes per (row, group)
 // LDS layout of one group (byte offsets): per operand the three 16-byte chunks of each row's
 // 48 container bytes (half 0 bytes 0..15 | half 1 bytes 0..15 | both halves' bytes 16..23),
@@ -60,7 +60,7 @@ constexpr int L_SW = 12800;                 // W scales
 constexpr int L_Z = 13312;                  // 128 zero bytes
 constexpr int GROUP = L_Z + 128;            // 13440
 constexpr int STAGE = KC * GROUP;
-constexpr int RING = 2 * STAGE;             // 53760 bytes
+constexpr int RING = 2 * STAGE;             // 80640 bytes
 // epilogue: buffer 1 of the ring (buffer 0 already receives the next tile's stage 0)
 constexpr int E_L2 = STAGE;                 // L2^T staging, 128 columns x (r + 8) halves
 constexpr int E_Y = STAGE;                  // fp16 output staging, per wave 32 rows x 136 bytes
@@ -75,6 +75,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, size_t bytes) {
   const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)n, 0x00020000);
 }
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 as_u4(u32x4_t v) { return make_uint4(v[0], v[1], v[2], v[3]); }
+__device__ __forceinline__ uint2 as_u2(u32x2_t v) { return make_uint2(v[0], v[1]); }
 
 // One wave's LDS-DMA load: lane l's 16 bytes (or 2 bytes, zero-extended to a dword) go to
 // dst + 16 l (dst + 4 l).  dst must be wave-uniform.
@@ -411,41 +416,57 @@ k_gemm3_tail(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, cons
 
   typedef _Float16 v4h_t __attribute__((ext_vector_type(4)));
   struct Op { uint4 x0, w0; uint2 x1, w1; uint32_t sx, sw; };
+  // buffer loads: the group's offset is wave-uniform (scalar offset), the lane's row offset a
+  // vector offset.  (As intrinsics, not plain loads, they are also kept where they are
+  // written: plain loads feeding the ring's loop-carried values get merged into one load
+  // at the use.)
+  const rsrc_t rxq = make_rsrc(xq, (size_t)G * M * GB), rwq = make_rsrc(wq, (size_t)G * N * GB);
+  const rsrc_t rxs = make_rsrc(xs, (size_t)G * M * 2), rws = make_rsrc(ws, (size_t)G * N * 2);
+  const uint32_t vx = (uint32_t)m * GB + 16u * h, vw = (uint32_t)n * GB + 16u * h;
+  const uint32_t vx1 = (uint32_t)m * GB + 32u + 8u * h, vw1 = (uint32_t)n * GB + 32u + 8u * h;
   auto load = [&](int g, Op& o) {
-    const uint8_t* px = xq + ((size_t)g * M + m) * GB;
-    const uint8_t* pw = wq + ((size_t)g * N + n) * GB;
-    o.x0 = *reinterpret_cast<const uint4*>(px + 16 * h);
-    o.x1 = *reinterpret_cast<const uint2*>(px + 32 + 8 * h);
-    o.w0 = *reinterpret_cast<const uint4*>(pw + 16 * h);
-    o.w1 = *reinterpret_cast<const uint2*>(pw + 32 + 8 * h);
-    // K slot 0 holds the scale for the lower-K-half lanes; the upper half contributes zeros
-    o.sx = h ? 0u : (uint32_t)reinterpret_cast<const unsigned short*>(xs)[(size_t)g * M + m];
-    o.sw = h ? 0u : (uint32_t)reinterpret_cast<const unsigned short*>(ws)[(size_t)g * N + n];
+    const uint32_t sx = (uint32_t)g * (uint32_t)M, sw = (uint32_t)g * (uint32_t)N;
+    o.x0 = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rxq, (int)vx, (int)(sx * GB), 0));
+    o.x1 = as_u2(__builtin_amdgcn_raw_buffer_load_b64(rxq, (int)vx1, (int)(sx * GB), 0));
+    o.w0 = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rwq, (int)vw, (int)(sw * GB), 0));
+    o.w1 = as_u2(__builtin_amdgcn_raw_buffer_load_b64(rwq, (int)vw1, (int)(sw * GB), 0));
+    // every lane loads (no branch around a load); the upper K half's scale is zeroed at use
+    o.sx = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rxs, (int)((uint32_t)m * 2u), (int)(sx * 2u), 0);
+    o.sw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rws, (int)((uint32_t)n * 2u), (int)(sw * 2u), 0);
   };
   v16f acc;
 #pragma unroll
   for (int i = 0; i < 16; i++) acc[i] = 0.f;
-  // a ring of PD groups in flight per wave (groups wave, wave + 4, ...)
+  // a ring of PD slots of loads in flight per wave (groups wave, wave + 4, ...): step s
+  // (s = 0, 1, ...) processes slot s % PD, which holds the wave's group s - PD (none for
+  // s < PD: the slots start zeroed and count with a zero scale product, exactly +0), then
+  // refills it with the wave's group s (past the last one it re-reads the last one).  There
+  // is no prologue and no branch in the loop: otherwise the compiler's wait counts, merged
+  // over paths with different loads in flight, make each slot wait for every load issued.
   constexpr int PD = 4;
+  const int ng = wave < G ? (G - 1 - wave) / 4 + 1 : 0;   // this wave's groups
   Op ring[PD];
 #pragma unroll
-  for (int j = 0; j < PD; j++)
-    if (wave + 4 * j < G) load(wave + 4 * j, ring[j]);
-  for (int g0 = wave; g0 < G; g0 += 4 * PD) {
+  for (int j = 0; j < PD; j++) ring[j] = Op{};
+  for (int s0 = 0; s0 < ng + PD; s0 += PD) {
 #pragma unroll
     for (int j = 0; j < PD; j++) {
-      const int g = g0 + 4 * j;
-      if (g >= G) break;
-      const Op cur = ring[j];
-      if (g + 4 * PD < G) load(g + 4 * PD, ring[j]);
+      const int st = s0 + j;
+      const bool zero = h || st < PD || st - PD >= ng;   // upper K half, or an empty slot
+      const Op& cur = ring[j];
       const v8i xo = v8i{(int)cur.x0.x, (int)cur.x0.y, (int)cur.x0.z, (int)cur.x0.w, (int)cur.x1.x, (int)cur.x1.y, 0, 0};
       const v8i wo = v8i{(int)cur.w0.x, (int)cur.w0.y, (int)cur.w0.z, (int)cur.w0.w, (int)cur.w1.x, (int)cur.w1.y, 0, 0};
       const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wo, xo, v16f{}, 2, 2, 0, 133, 0, 127);
-      const v16f sc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h_t, make_uint2(cur.sw, 0u)),
-                                                            __builtin_bit_cast(v4h_t, make_uint2(cur.sx, 0u)),
+      // K slot 0 holds the scale for the lower-K-half lanes; the upper half contributes zeros
+      const v16f sc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h_t, make_uint2(zero ? 0u : cur.sw, 0u)),
+                                                            __builtin_bit_cast(v4h_t, make_uint2(zero ? 0u : cur.sx, 0u)),
                                                             v16f{}, 0, 0, 0);
+      // refill the slot once the MFMAs have read it (loading it earlier would make the
+      // compiler copy the operands, and the copy waits for every load in flight)
+      load(ng > 0 ? wave + 4 * min(st, ng - 1) : 0, ring[j]);
 #pragma unroll
       for (int i = 0; i < 16; i++) acc[i] = __builtin_fmaf(p[i], sc[i], acc[i]);
+      __builtin_amdgcn_sched_barrier(0);     // keep the slots in order: each waits for its own loads only
     }
   }
   if (wave > 0) {
@@ -501,7 +522,7 @@ k_gemm3_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, co
                const uint8_t* __restrict__ wq, const __half* __restrict__ ws, const __half* __restrict__ l2,
                const __half* __restrict__ bias, int M, int N, int K, __half* __restrict__ y) {
   constexpr int R = RB * 16;
-  constexpr int PD = MT == 1 ? 4 : (MT == 2 ? 2 : 1);   // groups in flight per wave
+  constexpr int PD = MT <= 2 ? 4 : 2;       // groups in flight per wave
   __shared__ __attribute__((aligned(16))) float red[3][16][64];   // partials of waves 1..3, one row tile
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -516,18 +537,22 @@ k_gemm3_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, co
 
   typedef _Float16 v4h_t __attribute__((ext_vector_type(4)));
   struct Op { uint4 w0; uint2 w1; uint32_t sw; uint4 x0[MT]; uint2 x1[MT]; uint32_t sx[MT]; };
+  // buffer loads as in k_gemm3_tail (group offset scalar, row offset per lane)
+  const rsrc_t rxq = make_rsrc(xq, (size_t)G * M * GB), rwq = make_rsrc(wq, (size_t)G * N * GB);
+  const rsrc_t rxs = make_rsrc(xs, (size_t)G * M * 2), rws = make_rsrc(ws, (size_t)G * N * 2);
+  const uint32_t vw = (uint32_t)n * GB + 16u * h, vw1 = (uint32_t)n * GB + 32u + 8u * h;
   auto load = [&](int g, Op& o) {
-    const uint8_t* pw = wq + ((size_t)g * N + n) * GB;
-    o.w0 = *reinterpret_cast<const uint4*>(pw + 16 * h);
-    o.w1 = *reinterpret_cast<const uint2*>(pw + 32 + 8 * h);
-    // K slot 0 holds the scale for the lower-K-half lanes; the upper half contributes zeros
-    o.sw = h ? 0u : (uint32_t)reinterpret_cast<const unsigned short*>(ws)[(size_t)g * N + n];
+    const uint32_t sx = (uint32_t)g * (uint32_t)M, sw = (uint32_t)g * (uint32_t)N;
+    o.w0 = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rwq, (int)vw, (int)(sw * GB), 0));
+    o.w1 = as_u2(__builtin_amdgcn_raw_buffer_load_b64(rwq, (int)vw1, (int)(sw * GB), 0));
+    // every lane loads (no branch around a load); the upper K half's scale is zeroed at use
+    o.sw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rws, (int)((uint32_t)n * 2u), (int)(sw * 2u), 0);
 #pragma unroll
     for (int mt = 0; mt < MT; mt++) {
-      const uint8_t* px = xq + ((size_t)g * M + mrow[mt]) * GB;
-      o.x0[mt] = *reinterpret_cast<const uint4*>(px + 16 * h);
-      o.x1[mt] = *reinterpret_cast<const uint2*>(px + 32 + 8 * h);
-      o.sx[mt] = h ? 0u : (uint32_t)reinterpret_cast<const unsigned short*>(xs)[(size_t)g * M + mrow[mt]];
+      const uint32_t vr = (uint32_t)mrow[mt] * GB;
+      o.x0[mt] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rxq, (int)(vr + 16u * h), (int)(sx * GB), 0));
+      o.x1[mt] = as_u2(__builtin_amdgcn_raw_buffer_load_b64(rxq, (int)(vr + 32u + 8u * h), (int)(sx * GB), 0));
+      o.sx[mt] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rxs, (int)((uint32_t)mrow[mt] * 2u), (int)(sx * 2u), 0);
     }
   };
   v16f acc[MT];
@@ -535,29 +560,34 @@ k_gemm3_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, co
   for (int mt = 0; mt < MT; mt++)
 #pragma unroll
     for (int i = 0; i < 16; i++) acc[mt][i] = 0.f;
+  // the ring of k_gemm3_tail: step s processes slot s % PD (the wave's group s - PD, or a
+  // zeroed slot with a zero scale product) and refills it with the wave's group s
+  const int ng = wave < G ? (G - 1 - wave) / 4 + 1 : 0;   // this wave's groups
   Op ring[PD];
 #pragma unroll
-  for (int j = 0; j < PD; j++)
-    if (wave + 4 * j < G) load(wave + 4 * j, ring[j]);
-  for (int g0 = wave; g0 < G; g0 += 4 * PD) {
+  for (int j = 0; j < PD; j++) ring[j] = Op{};
+  for (int s0 = 0; s0 < ng + PD; s0 += PD) {
 #pragma unroll
     for (int j = 0; j < PD; j++) {
-      const int g = g0 + 4 * j;
-      if (g >= G) break;
-      const Op cur = ring[j];
-      if (g + 4 * PD < G) load(g + 4 * PD, ring[j]);
+      const int st = s0 + j;
+      const bool zero = h || st < PD || st - PD >= ng;   // upper K half, or an empty slot
+      const Op& cur = ring[j];
       const v8i wo = v8i{(int)cur.w0.x, (int)cur.w0.y, (int)cur.w0.z, (int)cur.w0.w, (int)cur.w1.x, (int)cur.w1.y, 0, 0};
 #pragma unroll
       for (int mt = 0; mt < MT; mt++) {
         const v8i xo = v8i{(int)cur.x0[mt].x, (int)cur.x0[mt].y, (int)cur.x0[mt].z, (int)cur.x0[mt].w,
                            (int)cur.x1[mt].x, (int)cur.x1[mt].y, 0, 0};
         const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wo, xo, v16f{}, 2, 2, 0, 133, 0, 127);
-        const v16f sc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h_t, make_uint2(cur.sw, 0u)),
-                                                              __builtin_bit_cast(v4h_t, make_uint2(cur.sx[mt], 0u)),
+        // K slot 0 holds the scale for the lower-K-half lanes; the upper half contributes zeros
+        const v16f sc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h_t, make_uint2(zero ? 0u : cur.sw, 0u)),
+                                                              __builtin_bit_cast(v4h_t, make_uint2(zero ? 0u : cur.sx[mt], 0u)),
                                                               v16f{}, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 16; i++) acc[mt][i] = __builtin_fmaf(p[i], sc[i], acc[mt][i]);
       }
+      // refill the slot once the MFMAs have read it (see k_gemm3_tail)
+      load(ng > 0 ? wave + 4 * min(st, ng - 1) : 0, ring[j]);
+      __builtin_amdgcn_sched_barrier(0);     // keep the slots in order: each waits for its own loads only
     }
   }
   // the four waves' partials, added in wave order, one row tile at a time

@@ -39,8 +39,6 @@ namespace svdq {
 namespace {
 
 constexpr int QD_NT = 256;                  // four waves
-constexpr int QD_WPE = 2;                   // waves per SIMD the register budget allows
-constexpr int QD_NB = 2;                    // chunks in flight per wave (1 or 2)
 constexpr int QD_NRT = 4;                   // 16-row tiles per block for r <= 32 (2 above)
 constexpr int QD_TARGET_BLOCKS = 512;       // workgroups that cover the chip once
 
@@ -57,8 +55,13 @@ __device__ __forceinline__ h2_t as_h2(uint32_t w) { return __builtin_bit_cast(h2
 
 }  // namespace
 
+// waves per SIMD that the register budget allows at NRT row tiles and r = 16 RB (no spills)
+__host__ __device__ constexpr int qd_waves_per_simd(int nrt, int rb) {
+  return nrt >= 4 ? 2 : (nrt == 2 ? (rb <= 2 ? 3 : 2) : (rb <= 2 ? 4 : (rb == 3 ? 3 : 2)));
+}
+
 template <int FMT, int NRT, int RB, bool QUANT>
-__global__ void __launch_bounds__(QD_NT, QD_WPE)
+__global__ void __launch_bounds__(QD_NT, qd_waves_per_simd(NRT, RB))
 k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M, int K, int cpb,
              uint8_t* __restrict__ xq, uint8_t* __restrict__ xs, __half* __restrict__ t,
              float* __restrict__ part) {
@@ -150,13 +153,13 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
           uint16_t sbits;
           const float s = int_scale_f16in(amax, inv_qmax, &sbits);
           const float r = s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s);
-          float v[16];
-          unpack_h8(B.x[rt][0], v);
-          unpack_h8(B.x[rt][1], v + 8);
-          // code = rint_half_even(clamp(RN(x / s), +-qmax)); + 0.0f turns -0 into +0
+          const _Float16* hv0 = reinterpret_cast<const _Float16*>(&B.x[rt][0]);
+          const _Float16* hv1 = reinterpret_cast<const _Float16*>(&B.x[rt][1]);
+          // code = rint_half_even(clamp(RN(x / s), +-qmax)); + 0.0f turns -0 into +0.  The fp16
+          // values go into the mixed-precision fmas as they are (quot_rn_h).
 #pragma unroll
           for (int e = 0; e < 16; e++)
-            qv[k][e] = rintf(__builtin_amdgcn_fmed3f(quot_rn(v[e], s, r), -qmax, qmax)) + 0.0f;
+            qv[k][e] = rintf(__builtin_amdgcn_fmed3f(quot_rn_h(e < 8 ? hv0[e] : hv1[e - 8], s, r), -qmax, qmax)) + 0.0f;
           const int m = m0 + rt * 16 + row;
           if (sub == 0 && m < M) {
             // row-major scales [M, K/64]; the 6-bit container keeps them group-major [K/64, M]
@@ -276,28 +279,25 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
     }
   };
 
-  // ---- this wave's chunks: cbeg + wave, + 4, ... below cend; two in flight
+  // ---- this wave's chunks: cbeg + wave, + 4, ... up to clast; the next chunk's loads are
+  // issued before the current one is processed.  The prefetch is unconditional (past clast
+  // it re-reads clast, a cache hit that is never processed): a branch around it would join a
+  // path with loads in flight to one without, and the compiler's wait counts at the join
+  // would make each chunk wait for the next one's loads as well.
   int c = cbeg + wave;
-  if (QD_NB == 1) {
-    for (; c < cend; c += 4) {
-      Buf B0;
-      load(c, B0);
-      process(c, B0);
-    }
-  } else if (c < cend) {
+  if (c < cend) {
+    const int clast = c + ((cend - 1 - c) / 4) * 4;
     Buf B0, B1;
     load(c, B0);
     while (true) {
-      int cn = c + 4;
-      if (cn < cend) load(cn, B1);
+      load(min(c + 4, clast), B1);
       process(c, B0);
-      if (cn >= cend) break;
-      c = cn;
-      cn = c + 4;
-      if (cn < cend) load(cn, B0);
+      c += 4;
+      if (c > clast) break;
+      load(min(c + 4, clast), B0);
       process(c, B1);
-      if (cn >= cend) break;
-      c = cn;
+      c += 4;
+      if (c > clast) break;
     }
   }
 

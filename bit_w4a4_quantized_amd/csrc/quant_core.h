@@ -56,6 +56,15 @@ __device__ __forceinline__ float quot_rn(float x, float s, float r) {
   return __builtin_fmaf(__builtin_fmaf(-t0, s, x), r, t0);
 }
 
+// quot_rn for an fp16 x taken as it is: t0 = RN(x r + 0) equals RN(x r) for x != 0 (and is
+// +0 for x = 0, where the result is 0 either way), so the result is RN(x / s) as above; every
+// use of x is an fma operand, which gfx950 reads from the fp16 half-register directly.
+__device__ __forceinline__ float quot_rn_h(_Float16 xh, float s, float r) {
+  const float x = (float)xh;
+  const float t0 = __builtin_fmaf(x, r, 0.0f);
+  return __builtin_fmaf(__builtin_fmaf(-t0, s, x), r, t0);
+}
+
 // Code of an fp16 value x (as float) against an fp16 scale s, given r = 1/s
 // (fp32, correctly rounded; r = 0 when s == 0).  Equals
 // clamp(rint(fp32(x) / s), -qmax, qmax) for qmax <= 127 without the division:

@@ -80,6 +80,8 @@ SHAPES = [  # M, K, N, r
     (1, 64, 16, 0), (3, 128, 32, 16), (17, 192, 48, 32), (64, 64, 128, 32),
     (130, 320, 272, 32), (257, 256, 144, 64), (300, 128, 400, 48), (128, 256, 256, 32),
     (2100, 128, 4096, 16),  # more 128 x 128 tiles than two workgroups per CU: persistent loop
+    (520, 320, 272, 32),    # 128 x 128 tiles, 5 groups: a full and a partial stage of 3
+    (200, 320, 144, 32),    # few rows (4 row tiles of 32 per workgroup), 5 groups over 4 waves
 ]
 
 
