@@ -9,7 +9,9 @@ fused QKV projection (M=4608 tokens, K=3072, N=9216, rank 32, INT4 group 64);
 the same run also times, each on its own seeded layer and with fewer steps:
   * the FLUX-like MLP pair: fc1 (K=3072, N=12288) and fc2 (K=12288, N=3072), and fc1 on
     its first 64, 256 and 1024 token rows (small-batch sweep, each point against the bound
-    its arithmetic intensity puts it under: HBM below 625 op/B, MFMA above);
+    its arithmetic intensity puts it under: HBM below 625 op/B, MFMA above; these short
+    launches are timed from HIP graph replays, so host launch cost stays out, and the eager
+    per-call time is reported beside them);
   * on the QKV layer: the bare W4A4 GEMM (r = 0: no branch in either kernel),
     the unfused branch (down projection, quantization, GEMM, up projection as
     separate launches with an fp16 intermediate), and the W4A16 control (fp16
@@ -21,9 +23,12 @@ the same run also times, each on its own seeded layer and with fewer steps:
 Inputs are seeded synthetic layers, resident in HBM before timing starts.
 Three copies of every input and output buffer are rotated so that a step never
 finds its operands in the 256 MB last-level cache (MALL) from the previous
-step.  Timing: W warm-up steps, then K timed steps bracketed by device
-synchronizations (wall clock); HIP events on the launch stream give each
-kernel's average duration.  Prints one JSON line.
+step.  Timing: untimed steps of the same work for --settle-ms (default 60 ms: the GPU
+clock ramps up over the first ~25 ms of sustained load), W warm-up steps, then K timed
+steps bracketed by device synchronizations (wall clock); HIP events on the launch stream give each
+kernel's average duration and the layer's 10/50/90th percentiles.  A shorter run on
+one buffer set (operands left in the MALL) gives the warm time beside it.  Prints
+one JSON line.
 
 The roofline's HBM traffic comes from the committed rocprofv3 counter summary
 of Kernel B (FETCH_SIZE and WRITE_SIZE, calibrated on a plain copy); it is
@@ -61,6 +66,21 @@ WORKLOADS = {
     "fc2": (4608, 12288, 3072, 32, "c2_fc2"),
 }
 ROTATE = 3
+SETTLE_MS = 60.0     # set from --settle-ms
+
+
+def settle(torch, fn, ms=None):
+    """Run fn(i) untimed until at least `ms` of wall time have passed (synchronizing every 8
+    calls).  Under sustained load the GPU clock ramps up over the first ~25 ms (per-step times
+    of the QKV layer: ~198 us in the first 100 steps, then a flat ~177 us for thousands of
+    steps), so every timed measurement starts after such a settle phase."""
+    ms = SETTLE_MS if ms is None else ms
+    t0, i = time.perf_counter(), 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
 KERNEL_B_SOURCE = os.path.join(ROOT, "bit_w4a4_quantized_amd", "csrc", "k_gemm3.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "kernel_b_qkv_4608x3072x9216_traffic.md")
 
@@ -77,6 +97,9 @@ def parse():
                                                                "and the bare / unfused / W4A16 comparisons")
     ap.add_argument("--extra-steps", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="untimed steps of the same work for at least this long before each warm-up "
+                         "(the GPU clock ramps up over the first ~25 ms of load)")
     ap.add_argument("--fmt", choices=["int4_e2m3", "int4"], default="int4_e2m3",
                     help="INT4 g64 codes in the 6-bit E2M3 container (FP6 MFMA) or packed nibbles (INT8 MFMA)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -182,8 +205,8 @@ class Layer:
         torch.cuda.synchronize()
         log(f"prepared {name} M={M} K={K} N={N} r={r} {fmt} in {time.time() - t0:.1f}s")
 
-    def fused(self, i, ev=None, branch=True):
-        st, b = self.sets[i % ROTATE], self.binding
+    def fused(self, i, ev=None, branch=True, rotate=ROTATE):
+        st, b = self.sets[i % rotate], self.binding
         if ev is not None:
             ev[0].record()
         b.svdq_quantize_down(st["x"], st["l1t"] if branch else None, self.fmt, xq=st["xq"], xs=st["xs"],
@@ -195,24 +218,74 @@ class Layer:
         if ev is not None:
             ev[2].record()
 
-    def time_fused(self, steps, warmup, branch=True):
+    def time_fused(self, steps, warmup, branch=True, rotate=ROTATE):
+        """rotate = ROTATE: operands leave the MALL between steps (cold); rotate = 1: the same
+        buffers every step (warm)."""
         torch = self.torch
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        settle(torch, lambda i: self.fused(i, branch=branch, rotate=rotate))
         for i in range(warmup):
-            self.fused(i, branch=branch)
+            self.fused(i, branch=branch, rotate=rotate)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            self.fused(i, ev[i], branch=branch)
+            self.fused(i, ev[i], branch=branch, rotate=rotate)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        layer = np.array([e[0].elapsed_time(e[2]) for e in ev]) * 1e3
         return {"us_per_layer": wall * 1e6 / steps,
-                "us_per_layer_events": float(np.mean([e[0].elapsed_time(e[2]) for e in ev])) * 1e3,
+                "us_per_layer_events": float(np.mean(layer)),
+                "us_per_layer_events_p10_p50_p90": [round(float(v), 2) for v in np.percentile(layer, [10, 50, 90])],
                 "ka_us": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3,
                 "kb_us": float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3}
 
-    def time_rows(self, m, steps, warmup):
-        """The fused layer on the first m token rows (own code/scale/T/Y buffers, same weights)."""
+    def time_rows_graph(self, m, replays, warmup, calls=2 * ROTATE):
+        """The fused layer on the first m token rows, timed from HIP graphs: one graph holds
+        `calls` layer calls (rotating buffer sets), another the same Kernel A calls alone, a
+        third the Kernel B calls alone, so host launch cost stays out of these small launches.
+        After the replays, Y must equal the eager call's Y bit for bit (deterministic kernels)."""
+        b, torch = self.binding, self.torch
+        K, fmt = self.K, self.fmt
+        sets = self._row_sets(m)
+
+        def ka(st):
+            b.svdq_quantize_down(st["x"], st["l1t"], fmt, xq=st["xq"], xs=st["xs"], t=st["t"], workspace=st["wsa"])
+
+        def kb(st):
+            b.svdq_gemm_w4a4_up(st["xq"], st["xs"], st["t"], st["wq"], st["ws"], st["l2"], st["b"], K, fmt, y=st["y"])
+        for st in sets:                      # eager: every set's Kernel B inputs are valid
+            ka(st)
+            kb(st)
+        torch.cuda.synchronize()
+        y_eager = sets[0]["y"].clone()
+        side = torch.cuda.Stream()
+        graphs = {}
+        for name, parts in (("layer", (ka, kb)), ("ka", (ka,)), ("kb", (kb,))):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for i in range(calls):
+                    for fn in parts:
+                        fn(sets[i % ROTATE])
+            graphs[name] = g
+        res = {}
+        for name, g in graphs.items():
+            settle(torch, lambda i: g.replay())
+            for _ in range(warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(replays):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) * 1e3 / (replays * calls)
+            if not torch.equal(sets[0]["y"], y_eager):
+                raise RuntimeError(f"graph replay ({name}, M={m}) changed Y")
+        del graphs
+        return {"us_per_layer": res["layer"], "ka_us": res["ka"], "kb_us": res["kb"]}
+
+    def _row_sets(self, m):
         b, torch = self.binding, self.torch
         K, N, r, fmt = self.K, self.N, self.r, self.fmt
         sets = []
@@ -225,6 +298,14 @@ class Layer:
                 y=torch.empty((m, N), dtype=torch.float16, device="cuda"),
                 wsa=torch.empty(max(16, b.quantize_down_workspace_bytes(m, K, r, fmt)), dtype=torch.uint8,
                                 device="cuda")))
+        return sets
+
+    def time_rows(self, m, steps, warmup):
+        """The fused layer on the first m token rows (own code/scale/T/Y buffers, same weights),
+        eager calls: what a Python caller sees, host launch cost included."""
+        b, torch = self.binding, self.torch
+        K, fmt = self.K, self.fmt
+        sets = self._row_sets(m)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
 
         def one(i, e=None):
@@ -237,6 +318,7 @@ class Layer:
             b.svdq_gemm_w4a4_up(st["xq"], st["xs"], st["t"], st["wq"], st["ws"], st["l2"], st["b"], K, fmt, y=st["y"])
             if e is not None:
                 e[2].record()
+        settle(torch, one)
         for i in range(warmup):
             one(i)
         torch.cuda.synchronize()
@@ -251,6 +333,7 @@ class Layer:
 
     def time_call(self, fn, steps, warmup):
         torch = self.torch
+        settle(torch, fn)
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
@@ -290,6 +373,25 @@ class Layer:
         return self.time_call(fn, steps, warmup)
 
 
+def device_facts(torch):
+    """The device and runtime the numbers were taken on."""
+    p = torch.cuda.get_device_properties(0)
+    facts = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+             "hbm_gib": round(p.total_memory / 2**30, 1), "torch_hip": torch.version.hip}
+    try:
+        import ctypes
+        lib = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+        hip = ctypes.CDLL(lib if os.path.exists(lib) else "libamdhip64.so")
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) == 0:      # hipDeviceAttributeClockRate (kHz)
+            facts["peak_clock_mhz"] = v.value // 1000
+        if hip.hipRuntimeGetVersion(ctypes.byref(v)) == 0:
+            facts["hip_runtime"] = v.value
+    except OSError:
+        pass
+    return facts
+
+
 def copy_calibration(mib):
     """A plain device copy of known size (for FETCH_SIZE / WRITE_SIZE calibration)."""
     import torch
@@ -305,6 +407,8 @@ def copy_calibration(mib):
 
 def main():
     args = parse()
+    global SETTLE_MS
+    SETTLE_MS = args.settle_ms
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: the layer runs on a single device and this build has no "
@@ -325,6 +429,7 @@ def main():
     L = Layer(torch, binding, args.workload, fmt, args.rank)
     M, K, N, r = L.M, L.K, L.N, L.r
     head = L.time_fused(args.steps, args.warmup)
+    warm = L.time_fused(max(10, args.steps // 4), 3, rotate=1)
     ms_per_step = head["us_per_layer"] * 1e-3
 
     ops = 2.0 * M * N * K
@@ -357,9 +462,11 @@ def main():
         "dtype": "int4 codes; fp6(e2m3) MFMA" if fmt == "int4_e2m3" else "int4 codes; i8 MFMA",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {L.lname} M={M} K={K} N={N} r={r} int4 group 64, fp16 scales",
-                   "storage": fmt, "rotated_buffer_sets": ROTATE},
+                   "storage": fmt, "rotated_buffer_sets": ROTATE, "settle_ms_before_warmup": SETTLE_MS},
         "us_per_layer": round(head["us_per_layer"], 2),
         "us_per_layer_events": round(head["us_per_layer_events"], 2),
+        "us_per_layer_events_p10_p50_p90": head["us_per_layer_events_p10_p50_p90"],
+        "us_per_layer_warm": round(warm["us_per_layer"], 2),
         "pct_int8_peak": round(100.0 * tops / INT8_PEAK_TOPS, 2),
         "kernels_us": {"quantize_down": round(ka_us, 2), "gemm_w4a4_up": round(kb_us, 2)},
         "kernel_a_hbm": {"algorithmic_bytes": ka_bytes,
@@ -367,6 +474,7 @@ def main():
                          "frac_of_8TBps": round(ka_bytes / (ka_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": roof,
         "cpu_baseline": None,
+        "device": device_facts(torch),
     }
 
     if not args.no_extras:
@@ -430,14 +538,17 @@ def main():
                 # small-batch sweep: where the layer moves from HBM-bound to MFMA-bound
                 sweep = {}
                 for m in (64, 256, 1024):
-                    rs = Lo.time_rows(m, es, ew)
+                    rs = Lo.time_rows_graph(m, 20, 3)
+                    eager = Lo.time_rows(m, es, ew)
                     a_b, b_b = algorithmic_bytes(m, Lo.K, Lo.N, Lo.r, 6 if fmt == "int4_e2m3" else 4)
                     m_ops = 2.0 * m * Lo.N * Lo.K
                     layer_s = rs["us_per_layer"] * 1e-6
                     intensity = m_ops / (a_b + b_b)
                     bound = "hbm" if intensity < INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
                     sweep[str(m)] = {
+                        "timing": "HIP graph replay",
                         "us_per_layer": round(rs["us_per_layer"], 2),
+                        "us_per_layer_eager_calls": round(eager["us_per_layer"], 2),
                         "kernels_us": {"quantize_down": round(rs["ka_us"], 2), "gemm_w4a4_up": round(rs["kb_us"], 2)},
                         "tops": round(m_ops / layer_s / 1e12, 2),
                         "algorithmic_bytes": a_b + b_b,
