@@ -117,6 +117,139 @@ __device__ __forceinline__ void tile_of3(int bid, int nblocks, int tiles_m, int 
 
 }  // namespace
 
+// The last, partial round of tiles: when only a few tiles remain after the full rounds of
+// the persistent loop, each of them is cut into 16 sub-tiles of 32 x 32, and each sub-tile is
+// one job for a whole workgroup, taken by the persistent workgroups once their full tiles are
+// done: its four waves split K (groups w, w + 4, ...) and add their partial sums in LDS (red,
+// 12 KB of the workgroup's LDS) in a fixed order, so the result is deterministic and no
+// global scratch is needed.  Operands come straight from global memory into registers, four
+// groups ahead.  Ends with a barrier (red is reused by the next job).
+template <int RB, bool BIAS>
+__device__ __forceinline__ void gemm3_subtile(const uint8_t* __restrict__ xq, const __half* __restrict__ xs,
+                                              const __half* __restrict__ t, const uint8_t* __restrict__ wq,
+                                              const __half* __restrict__ ws, const __half* __restrict__ l2,
+                                              const __half* __restrict__ bias, int M, int N, int K,
+                                              __half* __restrict__ y, int tile0, int job, float (*red)[16][64]) {
+  constexpr int R = RB * 16;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, r32 = lane & 31;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int tiles = tiles_m * tiles_n;
+  const int G = K >> 6;
+  int tm, tn;
+  tile_of3(tile0 + (job >> 4), tiles, tiles_m, tiles_n, &tm, &tn);
+  const int sub = job & 15;
+  const int nb = tn * BN + (sub >> 2) * 32, mb = tm * BM + (sub & 3) * 32;   // sub-tile origin
+  const int m = min(mb + r32, M - 1), n = min(nb + r32, N - 1);           // this lane's operand rows
+
+  typedef _Float16 v4h_t __attribute__((ext_vector_type(4)));
+  struct Op { uint4 x0, w0; uint2 x1, w1; uint32_t sx, sw; };
+  // buffer loads: the group's offset is wave-uniform (scalar offset), the lane's row offset a
+  // vector offset.  (As intrinsics, not plain loads, they are also kept where they are
+  // written: plain loads feeding the ring's loop-carried values get merged into one load
+  // at the use.)
+  const rsrc_t rxq = make_rsrc(xq, (size_t)G * M * GB), rwq = make_rsrc(wq, (size_t)G * N * GB);
+  const rsrc_t rxs = make_rsrc(xs, (size_t)G * M * 2), rws = make_rsrc(ws, (size_t)G * N * 2);
+  const uint32_t vx = (uint32_t)m * GB + 16u * h, vw = (uint32_t)n * GB + 16u * h;
+  const uint32_t vx1 = (uint32_t)m * GB + 32u + 8u * h, vw1 = (uint32_t)n * GB + 32u + 8u * h;
+  auto load = [&](int g, Op& o) {
+    const uint32_t sx = (uint32_t)g * (uint32_t)M, sw = (uint32_t)g * (uint32_t)N;
+    o.x0 = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rxq, (int)vx, (int)(sx * GB), 0));
+    o.x1 = as_u2(__builtin_amdgcn_raw_buffer_load_b64(rxq, (int)vx1, (int)(sx * GB), 0));
+    o.w0 = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rwq, (int)vw, (int)(sw * GB), 0));
+    o.w1 = as_u2(__builtin_amdgcn_raw_buffer_load_b64(rwq, (int)vw1, (int)(sw * GB), 0));
+    // every lane loads (no branch around a load); the upper K half's scale is zeroed at use
+    o.sx = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rxs, (int)((uint32_t)m * 2u), (int)(sx * 2u), 0);
+    o.sw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rws, (int)((uint32_t)n * 2u), (int)(sw * 2u), 0);
+  };
+  // the epilogue's operands (T rows, L2 columns, bias), loaded by every wave before the K loop
+  // so that their latency overlaps it (wave 0 uses them)
+  uint4 tv[RB > 0 ? RB : 1];
+  uint32_t lv[RB > 0 ? RB : 1][8];
+#pragma unroll
+  for (int kb = 0; kb < RB; kb++) {
+    tv[kb] = *reinterpret_cast<const uint4*>(t + (size_t)m * R + kb * 16 + 8 * h);
+#pragma unroll
+    for (int e = 0; e < 8; e++) lv[kb][e] = __half_as_ushort(l2[(size_t)(kb * 16 + 8 * h + e) * N + n]);
+  }
+  uint2 braw[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++)   // columns past N read the last four (their outputs are not stored)
+    braw[q] = BIAS ? *reinterpret_cast<const uint2*>(bias + min(nb + 8 * q + 4 * h, N - 4)) : make_uint2(0u, 0u);
+  v16f acc;
+#pragma unroll
+  for (int i = 0; i < 16; i++) acc[i] = 0.f;
+  // a ring of PD slots of loads in flight per wave (groups wave, wave + 4, ...): step s
+  // (s = 0, 1, ...) processes slot s % PD, which holds the wave's group s - PD (none for
+  // s < PD: the slots start zeroed and count with a zero scale product, exactly +0), then
+  // refills it with the wave's group s (past the last one it re-reads the last one).  There
+  // is no prologue and no branch in the loop: otherwise the compiler's wait counts, merged
+  // over paths with different loads in flight, make each slot wait for every load issued.
+  constexpr int PD = 4;
+  const int ng = wave < G ? (G - 1 - wave) / 4 + 1 : 0;   // this wave's groups
+  Op ring[PD];
+#pragma unroll
+  for (int j = 0; j < PD; j++) ring[j] = Op{};
+  for (int s0 = 0; s0 < ng + PD; s0 += PD) {
+#pragma unroll
+    for (int j = 0; j < PD; j++) {
+      const int st = s0 + j;
+      const bool zero = h || st < PD || st - PD >= ng;   // upper K half, or an empty slot
+      const Op& cur = ring[j];
+      const v8i xo = v8i{(int)cur.x0.x, (int)cur.x0.y, (int)cur.x0.z, (int)cur.x0.w, (int)cur.x1.x, (int)cur.x1.y, 0, 0};
+      const v8i wo = v8i{(int)cur.w0.x, (int)cur.w0.y, (int)cur.w0.z, (int)cur.w0.w, (int)cur.w1.x, (int)cur.w1.y, 0, 0};
+      const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wo, xo, v16f{}, 2, 2, 0, 133, 0, 127);
+      // K slot 0 holds the scale for the lower-K-half lanes; the upper half contributes zeros
+      const v16f sc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h_t, make_uint2(zero ? 0u : cur.sw, 0u)),
+                                                            __builtin_bit_cast(v4h_t, make_uint2(zero ? 0u : cur.sx, 0u)),
+                                                            v16f{}, 0, 0, 0);
+      // refill the slot once the MFMAs have read it (loading it earlier would make the
+      // compiler copy the operands, and the copy waits for every load in flight)
+      load(ng > 0 ? wave + 4 * min(st, ng - 1) : 0, ring[j]);
+#pragma unroll
+      for (int i = 0; i < 16; i++) acc[i] = __builtin_fmaf(p[i], sc[i], acc[i]);
+      __builtin_amdgcn_sched_barrier(0);     // keep the slots in order: each waits for its own loads only
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) red[wave - 1][i][lane] = acc[i];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) acc[i] = ((acc[i] + red[0][i][lane]) + red[1][i][lane]) + red[2][i][lane];
+    // up projection on the 32 x 32 sub-tile: row operand L2^T (columns n), column operand T (rows m)
+#pragma unroll
+    for (int kb = 0; kb < RB; kb++) {
+      const uint4 lw = make_uint4(lv[kb][0] | (lv[kb][1] << 16), lv[kb][2] | (lv[kb][3] << 16),
+                                  lv[kb][4] | (lv[kb][5] << 16), lv[kb][6] | (lv[kb][7] << 16));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(lw), as_h8(tv[kb]), acc, 0, 0, 0);
+    }
+    // lane owns row mb + r32 and columns nb + 8 q + 4 h + j (reg 4 q + j)
+    const int mo = mb + r32;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      if (mo >= M) break;
+      const int no = nb + 8 * q + 4 * h;
+      if (no >= N) continue;
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (BIAS) {
+        bv[0] = __half2float(__ushort_as_half((unsigned short)(braw[q].x & 0xFFFFu)));
+        bv[1] = __half2float(__ushort_as_half((unsigned short)(braw[q].x >> 16)));
+        bv[2] = __half2float(__ushort_as_half((unsigned short)(braw[q].y & 0xFFFFu)));
+        bv[3] = __half2float(__ushort_as_half((unsigned short)(braw[q].y >> 16)));
+      }
+      uint32_t hv[4];
+#pragma unroll
+      for (int j = 0; j < 4; j++) hv[j] = __half_as_ushort(__float2half_rn(acc[4 * q + j] + bv[j]));
+      *reinterpret_cast<uint2*>(y + (size_t)mo * N + no) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+    }
+  }
+  __syncthreads();
+}
+
 template <int RB, bool BIAS>
 __global__ void __launch_bounds__(NT, 2)
 k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __half* __restrict__ t,
@@ -388,126 +521,14 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
     tile = next;
     cur = nxt;
   }
-}
 
-// The last, partial round of tiles: when only a few tiles remain after the full rounds of
-// the persistent kernel, each of them is cut into 16 sub-tiles of 32 x 32 and each sub-tile is
-// one workgroup whose four waves split K (groups w, w + 4, ...); the four partial sums are
-// added in LDS in a fixed order, so the result is deterministic and no global scratch is
-// needed.  Operands come straight from global memory into registers, four groups ahead.
-template <int RB, bool BIAS>
-__global__ void __launch_bounds__(NT, 2)
-k_gemm3_tail(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __half* __restrict__ t,
-             const uint8_t* __restrict__ wq, const __half* __restrict__ ws, const __half* __restrict__ l2,
-             const __half* __restrict__ bias, int M, int N, int K, __half* __restrict__ y, int tile0) {
-  constexpr int R = RB * 16;
-  __shared__ __attribute__((aligned(16))) float red[3][16][64];   // partials of waves 1..3
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 5, r32 = lane & 31;
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int tiles = tiles_m * tiles_n;
-  const int G = K >> 6;
-  int tm, tn;
-  tile_of3(tile0 + (int)(blockIdx.x >> 4), tiles, tiles_m, tiles_n, &tm, &tn);
-  const int sub = blockIdx.x & 15;
-  const int nb = tn * BN + (sub >> 2) * 32, mb = tm * BM + (sub & 3) * 32;   // sub-tile origin
-  const int m = min(mb + r32, M - 1), n = min(nb + r32, N - 1);           // this lane's operand rows
-
-  typedef _Float16 v4h_t __attribute__((ext_vector_type(4)));
-  struct Op { uint4 x0, w0; uint2 x1, w1; uint32_t sx, sw; };
-  // buffer loads: the group's offset is wave-uniform (scalar offset), the lane's row offset a
-  // vector offset.  (As intrinsics, not plain loads, they are also kept where they are
-  // written: plain loads feeding the ring's loop-carried values get merged into one load
-  // at the use.)
-  const rsrc_t rxq = make_rsrc(xq, (size_t)G * M * GB), rwq = make_rsrc(wq, (size_t)G * N * GB);
-  const rsrc_t rxs = make_rsrc(xs, (size_t)G * M * 2), rws = make_rsrc(ws, (size_t)G * N * 2);
-  const uint32_t vx = (uint32_t)m * GB + 16u * h, vw = (uint32_t)n * GB + 16u * h;
-  const uint32_t vx1 = (uint32_t)m * GB + 32u + 8u * h, vw1 = (uint32_t)n * GB + 32u + 8u * h;
-  auto load = [&](int g, Op& o) {
-    const uint32_t sx = (uint32_t)g * (uint32_t)M, sw = (uint32_t)g * (uint32_t)N;
-    o.x0 = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rxq, (int)vx, (int)(sx * GB), 0));
-    o.x1 = as_u2(__builtin_amdgcn_raw_buffer_load_b64(rxq, (int)vx1, (int)(sx * GB), 0));
-    o.w0 = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rwq, (int)vw, (int)(sw * GB), 0));
-    o.w1 = as_u2(__builtin_amdgcn_raw_buffer_load_b64(rwq, (int)vw1, (int)(sw * GB), 0));
-    // every lane loads (no branch around a load); the upper K half's scale is zeroed at use
-    o.sx = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rxs, (int)((uint32_t)m * 2u), (int)(sx * 2u), 0);
-    o.sw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rws, (int)((uint32_t)n * 2u), (int)(sw * 2u), 0);
-  };
-  v16f acc;
-#pragma unroll
-  for (int i = 0; i < 16; i++) acc[i] = 0.f;
-  // a ring of PD slots of loads in flight per wave (groups wave, wave + 4, ...): step s
-  // (s = 0, 1, ...) processes slot s % PD, which holds the wave's group s - PD (none for
-  // s < PD: the slots start zeroed and count with a zero scale product, exactly +0), then
-  // refills it with the wave's group s (past the last one it re-reads the last one).  There
-  // is no prologue and no branch in the loop: otherwise the compiler's wait counts, merged
-  // over paths with different loads in flight, make each slot wait for every load issued.
-  constexpr int PD = 4;
-  const int ng = wave < G ? (G - 1 - wave) / 4 + 1 : 0;   // this wave's groups
-  Op ring[PD];
-#pragma unroll
-  for (int j = 0; j < PD; j++) ring[j] = Op{};
-  for (int s0 = 0; s0 < ng + PD; s0 += PD) {
-#pragma unroll
-    for (int j = 0; j < PD; j++) {
-      const int st = s0 + j;
-      const bool zero = h || st < PD || st - PD >= ng;   // upper K half, or an empty slot
-      const Op& cur = ring[j];
-      const v8i xo = v8i{(int)cur.x0.x, (int)cur.x0.y, (int)cur.x0.z, (int)cur.x0.w, (int)cur.x1.x, (int)cur.x1.y, 0, 0};
-      const v8i wo = v8i{(int)cur.w0.x, (int)cur.w0.y, (int)cur.w0.z, (int)cur.w0.w, (int)cur.w1.x, (int)cur.w1.y, 0, 0};
-      const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wo, xo, v16f{}, 2, 2, 0, 133, 0, 127);
-      // K slot 0 holds the scale for the lower-K-half lanes; the upper half contributes zeros
-      const v16f sc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h_t, make_uint2(zero ? 0u : cur.sw, 0u)),
-                                                            __builtin_bit_cast(v4h_t, make_uint2(zero ? 0u : cur.sx, 0u)),
-                                                            v16f{}, 0, 0, 0);
-      // refill the slot once the MFMAs have read it (loading it earlier would make the
-      // compiler copy the operands, and the copy waits for every load in flight)
-      load(ng > 0 ? wave + 4 * min(st, ng - 1) : 0, ring[j]);
-#pragma unroll
-      for (int i = 0; i < 16; i++) acc[i] = __builtin_fmaf(p[i], sc[i], acc[i]);
-      __builtin_amdgcn_sched_barrier(0);     // keep the slots in order: each waits for its own loads only
-    }
-  }
-  if (wave > 0) {
-#pragma unroll
-    for (int i = 0; i < 16; i++) red[wave - 1][i][lane] = acc[i];
-  }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int i = 0; i < 16; i++) acc[i] = ((acc[i] + red[0][i][lane]) + red[1][i][lane]) + red[2][i][lane];
-  // up projection on the 32 x 32 sub-tile: row operand L2^T (columns n), column operand T (rows m)
-#pragma unroll
-  for (int kb = 0; kb < RB; kb++) {
-    const uint4 tv = *reinterpret_cast<const uint4*>(t + (size_t)m * R + kb * 16 + 8 * h);
-    uint16_t lv[8];
-#pragma unroll
-    for (int e = 0; e < 8; e++) lv[e] = __half_as_ushort(l2[(size_t)(kb * 16 + 8 * h + e) * N + n]);
-    const uint4 lw = make_uint4(lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16),
-                                lv[4] | ((uint32_t)lv[5] << 16), lv[6] | ((uint32_t)lv[7] << 16));
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(lw), as_h8(tv), acc, 0, 0, 0);
-  }
-  // lane owns row mb + r32 and columns nb + 8 q + 4 h + j (reg 4 q + j)
-  const int mo = mb + r32;
-  if (mo >= M) return;
-#pragma unroll
-  for (int q = 0; q < 4; q++) {
-    const int no = nb + 8 * q + 4 * h;
-    if (no >= N) continue;
-    float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (BIAS) {
-      const uint2 braw = *reinterpret_cast<const uint2*>(bias + no);
-      bv[0] = __half2float(__ushort_as_half((unsigned short)(braw.x & 0xFFFFu)));
-      bv[1] = __half2float(__ushort_as_half((unsigned short)(braw.x >> 16)));
-      bv[2] = __half2float(__ushort_as_half((unsigned short)(braw.y & 0xFFFFu)));
-      bv[3] = __half2float(__ushort_as_half((unsigned short)(braw.y >> 16)));
-    }
-    uint32_t hv[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) hv[j] = __half_as_ushort(__float2half_rn(acc[4 * q + j] + bv[j]));
-    *reinterpret_cast<uint2*>(y + (size_t)mo * N + no) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
-  }
+  // ---- the tiles past tiles_run (a last, partial round) as 32 x 32 sub-tile jobs, taken as
+  // the workgroups finish their full tiles; their partial sums use the ring's first 12 KB
+  // (no loads are in flight: the last tile started none)
+  const int n_sub = (tiles - tiles_run) * 16;
+  for (int job = blockIdx.x; job < n_sub; job += gridDim.x)
+    gemm3_subtile<RB, BIAS>(xq, xs, t, wq, ws, l2, bias, M, N, K, y, tiles_run, job,
+                            reinterpret_cast<float (*)[16][64]>(lds));
 }
 
 // Few token rows (weight-streaming regime): one workgroup per 32 output columns and a slab of
@@ -537,7 +558,7 @@ k_gemm3_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, co
 
   typedef _Float16 v4h_t __attribute__((ext_vector_type(4)));
   struct Op { uint4 w0; uint2 w1; uint32_t sw; uint4 x0[MT]; uint2 x1[MT]; uint32_t sx[MT]; };
-  // buffer loads as in k_gemm3_tail (group offset scalar, row offset per lane)
+  // buffer loads as in gemm3_subtile (group offset scalar, row offset per lane)
   const rsrc_t rxq = make_rsrc(xq, (size_t)G * M * GB), rwq = make_rsrc(wq, (size_t)G * N * GB);
   const rsrc_t rxs = make_rsrc(xs, (size_t)G * M * 2), rws = make_rsrc(ws, (size_t)G * N * 2);
   const uint32_t vw = (uint32_t)n * GB + 16u * h, vw1 = (uint32_t)n * GB + 32u + 8u * h;
@@ -555,12 +576,31 @@ k_gemm3_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, co
       o.sx[mt] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rxs, (int)((uint32_t)mrow[mt] * 2u), (int)(sx * 2u), 0);
     }
   };
+  // the epilogue's operands (L2 columns, bias, and T rows when MT <= 2), loaded by every wave
+  // before the K loop so that their latency overlaps it (wave 0 uses them)
+  constexpr int MTT = MT <= 2 ? MT : 1;
+  uint32_t lv[RB > 0 ? RB : 1][8];
+  uint4 tv[MTT][RB > 0 ? RB : 1];
+#pragma unroll
+  for (int kb = 0; kb < RB; kb++) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) lv[kb][e] = __half_as_ushort(l2[(size_t)(kb * 16 + 8 * h + e) * N + n]);
+    if (MT <= 2) {
+#pragma unroll
+      for (int mt = 0; mt < MTT; mt++)
+        tv[mt][kb] = *reinterpret_cast<const uint4*>(t + (size_t)mrow[mt] * R + kb * 16 + 8 * h);
+    }
+  }
+  uint2 braw[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++)   // columns past N read the last four (their outputs are not stored)
+    braw[q] = BIAS ? *reinterpret_cast<const uint2*>(bias + min(nb + 8 * q + 4 * h, N - 4)) : make_uint2(0u, 0u);
   v16f acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; mt++)
 #pragma unroll
     for (int i = 0; i < 16; i++) acc[mt][i] = 0.f;
-  // the ring of k_gemm3_tail: step s processes slot s % PD (the wave's group s - PD, or a
+  // the ring of gemm3_subtile: step s processes slot s % PD (the wave's group s - PD, or a
   // zeroed slot with a zero scale product) and refills it with the wave's group s
   const int ng = wave < G ? (G - 1 - wave) / 4 + 1 : 0;   // this wave's groups
   Op ring[PD];
@@ -585,7 +625,7 @@ k_gemm3_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, co
 #pragma unroll
         for (int i = 0; i < 16; i++) acc[mt][i] = __builtin_fmaf(p[i], sc[i], acc[mt][i]);
       }
-      // refill the slot once the MFMAs have read it (see k_gemm3_tail)
+      // refill the slot once the MFMAs have read it (see gemm3_subtile)
       load(ng > 0 ? wave + 4 * min(st, ng - 1) : 0, ring[j]);
       __builtin_amdgcn_sched_barrier(0);     // keep the slots in order: each waits for its own loads only
     }
@@ -608,33 +648,24 @@ k_gemm3_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, co
   // up projection: row operand L2^T (columns n, gathered once), column operand T (rows m)
   uint4 lw[RB > 0 ? RB : 1];
 #pragma unroll
-  for (int kb = 0; kb < RB; kb++) {
-    uint16_t lv[8];
-#pragma unroll
-    for (int e = 0; e < 8; e++) lv[e] = __half_as_ushort(l2[(size_t)(kb * 16 + 8 * h + e) * N + n]);
-    lw[kb] = make_uint4(lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16),
-                        lv[4] | ((uint32_t)lv[5] << 16), lv[6] | ((uint32_t)lv[7] << 16));
-  }
+  for (int kb = 0; kb < RB; kb++)
+    lw[kb] = make_uint4(lv[kb][0] | (lv[kb][1] << 16), lv[kb][2] | (lv[kb][3] << 16),
+                        lv[kb][4] | (lv[kb][5] << 16), lv[kb][6] | (lv[kb][7] << 16));
   float bv[4][4];
 #pragma unroll
   for (int q = 0; q < 4; q++) {
-    const int no = nb + 8 * q + 4 * h;
-#pragma unroll
-    for (int j = 0; j < 4; j++) bv[q][j] = 0.f;
-    if (BIAS && no < N) {
-      const uint2 braw = *reinterpret_cast<const uint2*>(bias + no);
-      bv[q][0] = __half2float(__ushort_as_half((unsigned short)(braw.x & 0xFFFFu)));
-      bv[q][1] = __half2float(__ushort_as_half((unsigned short)(braw.x >> 16)));
-      bv[q][2] = __half2float(__ushort_as_half((unsigned short)(braw.y & 0xFFFFu)));
-      bv[q][3] = __half2float(__ushort_as_half((unsigned short)(braw.y >> 16)));
-    }
+    bv[q][0] = BIAS ? __half2float(__ushort_as_half((unsigned short)(braw[q].x & 0xFFFFu))) : 0.f;
+    bv[q][1] = BIAS ? __half2float(__ushort_as_half((unsigned short)(braw[q].x >> 16))) : 0.f;
+    bv[q][2] = BIAS ? __half2float(__ushort_as_half((unsigned short)(braw[q].y & 0xFFFFu))) : 0.f;
+    bv[q][3] = BIAS ? __half2float(__ushort_as_half((unsigned short)(braw[q].y >> 16))) : 0.f;
   }
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
     for (int kb = 0; kb < RB; kb++) {
-      const uint4 tv = *reinterpret_cast<const uint4*>(t + (size_t)mrow[mt] * R + kb * 16 + 8 * h);
-      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(lw[kb]), as_h8(tv), acc[mt], 0, 0, 0);
+      const uint4 tvk = MT <= 2 ? tv[MT <= 2 ? mt : 0][kb]
+                                : *reinterpret_cast<const uint4*>(t + (size_t)mrow[mt] * R + kb * 16 + 8 * h);
+      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(lw[kb]), as_h8(tvk), acc[mt], 0, 0, 0);
     }
     // lane owns row mb + mt*32 + r32 and columns nb + 8 q + 4 h + j (reg 4 q + j)
     const int mo = mb + mt * 32 + r32;
@@ -664,8 +695,9 @@ static int resident_blocks() {
   return cached[dev];
 }
 
-// Full rounds of the persistent kernel, then (when the remainder is at most a quarter of a
-// round) the remaining tiles as sub-tiles; otherwise the persistent kernel takes them all.
+// Full rounds of the persistent loop, then (when the remainder is at most a quarter of a
+// round) the remaining tiles as sub-tile jobs in the same launch; otherwise the persistent
+// loop takes them all.
 // Up to this many token rows the weight-streaming kernel runs (in 128-row slabs).
 constexpr int kSkinnyRows = 256;
 
@@ -692,12 +724,6 @@ static hipError_t launch_g3(const GemmArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((k_gemm3<RB, BIAS>), dim3(nb), dim3(NT), 0, s, (const uint8_t*)a.xq,
                      (const __half*)a.xs, (const __half*)a.t, (const uint8_t*)a.wq, (const __half*)a.ws,
                      (const __half*)a.l2, (const __half*)a.bias, a.M, a.N, a.K, (__half*)a.y, main_tiles);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || main_tiles == tiles) return e;
-  hipLaunchKernelGGL((k_gemm3_tail<RB, BIAS>), dim3((tiles - main_tiles) * 16), dim3(NT), 0, s,
-                     (const uint8_t*)a.xq, (const __half*)a.xs, (const __half*)a.t, (const uint8_t*)a.wq,
-                     (const __half*)a.ws, (const __half*)a.l2, (const __half*)a.bias, a.M, a.N, a.K,
-                     (__half*)a.y, main_tiles);
   return hipGetLastError();
 }
 
