@@ -25,8 +25,9 @@ Three copies of every input and output buffer are rotated so that a step never
 finds its operands in the 256 MB last-level cache (MALL) from the previous
 step.  Timing: untimed steps of the same work for --settle-ms (default 60 ms: the GPU
 clock ramps up over the first ~25 ms of sustained load), W warm-up steps, then K timed
-steps bracketed by device synchronizations (wall clock); HIP events on the launch stream give each
-kernel's average duration and the layer's 10/50/90th percentiles.  A shorter run on
+steps bracketed by device synchronizations (wall clock); HIP events on the launch stream,
+recorded on every 5th timed step (event records add to a step's time), give each kernel's
+average duration and the layer's 10/50/90th percentiles.  A shorter run on
 one buffer set (operands left in the MALL) gives the warm time beside it.  Prints
 one JSON line.
 
@@ -67,6 +68,8 @@ WORKLOADS = {
 }
 ROTATE = 3
 SETTLE_MS = 60.0     # set from --settle-ms
+EVENT_EVERY = 5      # HIP events on every 5th timed step: three event records cost ~7 us of a
+                     # ~178 us step (measured), so recording them on every step would inflate it
 
 
 def settle(torch, fn, ms=None):
@@ -222,16 +225,17 @@ class Layer:
         """rotate = ROTATE: operands leave the MALL between steps (cold); rotate = 1: the same
         buffers every step (warm)."""
         torch = self.torch
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in range(0, steps, EVENT_EVERY)}
         settle(torch, lambda i: self.fused(i, branch=branch, rotate=rotate))
         for i in range(warmup):
             self.fused(i, branch=branch, rotate=rotate)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            self.fused(i, ev[i], branch=branch, rotate=rotate)
+            self.fused(i, ev.get(i), branch=branch, rotate=rotate)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        ev = list(ev.values())
         layer = np.array([e[0].elapsed_time(e[2]) for e in ev]) * 1e3
         return {"us_per_layer": wall * 1e6 / steps,
                 "us_per_layer_events": float(np.mean(layer)),
@@ -462,7 +466,8 @@ def main():
         "dtype": "int4 codes; fp6(e2m3) MFMA" if fmt == "int4_e2m3" else "int4 codes; i8 MFMA",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {L.lname} M={M} K={K} N={N} r={r} int4 group 64, fp16 scales",
-                   "storage": fmt, "rotated_buffer_sets": ROTATE, "settle_ms_before_warmup": SETTLE_MS},
+                   "storage": fmt, "rotated_buffer_sets": ROTATE, "settle_ms_before_warmup": SETTLE_MS,
+                   "kernel_events_on_every_nth_step": EVENT_EVERY},
         "us_per_layer": round(head["us_per_layer"], 2),
         "us_per_layer_events": round(head["us_per_layer_events"], 2),
         "us_per_layer_events_p10_p50_p90": head["us_per_layer_events_p10_p50_p90"],
