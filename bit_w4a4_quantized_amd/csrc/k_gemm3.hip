@@ -11,12 +11,13 @@
 // Each INT4 code q is held as the E2M3 subnormal of q/8, so 32 codes of a row
 // (one half of a group) are the six-dword operand of
 // v_mfma_scale_f32_32x32x64_f8f6f4 in FP6 mode, and one MFMA per 32 x 32 tile
-// and group returns P_g in fp32 exactly: the products of the E2M3 values are P_g / 64, and the
-// instruction's power-of-two block scale for the A operand (E8M0 133 = 2^6) multiplies by 64
-// exactly.  The scale products
-// S = sw sx^T of a tile come from one v_mfma_f32_32x32x8_f16 whose operands
-// carry the scales in K slot 0 and zeros elsewhere (exact), so the vector ALU
-// spends one fma per output element and group: acc += P_g * S.
+// and group returns a power-of-two multiple of P_g in fp32 exactly: the products of the E2M3
+// values are P_g / 64, and the instruction's block scale for the A operand (E8M0) multiplies by
+// a power of two exactly.  The scale products S = sw sx^T of a tile come from one
+// v_mfma_f32_32x32x8_f16 whose operands carry the scales in K slots 0 and 4 (one from each
+// lane half) and zeros elsewhere, so it returns 2 S exactly; with the FP6 MFMA returning
+// P_g / 2 (E8M0 132 = 2^5), the vector ALU spends one fma per output element and group,
+// acc += (P_g / 2) (2 S), whose product is exactly P_g S.
 //
 // The MFMAs take the weight tile as the row operand and the activation tile as
 // the column operand, so each lane's accumulators belong to one output row
@@ -38,8 +39,9 @@
 // loads, every MFMA operand is one 16-byte and one 8-byte LDS read straight into
 // its registers, and both the loads and the reads touch contiguous bytes (no
 // bank conflicts).  Scales arrive as one dword per row (the 2-byte
-// DMA form zero-extends), which with a zero register is the K-slot-0 operand;
-// the lanes of the upper K half read a zero block.
+// DMA form zero-extends), which with a zero register is the scale MFMA's operand
+// (K slot 0 for lanes of the lower K half, slot 4 for the upper; both halves read the
+// same dword, a broadcast).
 // Tile order: each XCD (own L2) works on a contiguous range of tiles, rastered
 // in groups of 8 tile rows.
 #include "kernels.h"
@@ -48,7 +50,7 @@ namespace svdq {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, NT = 256, KC = 3;   // 3 groups a stage: fewer barriers; 2 x 80640 B of LDS per CU
+constexpr int BM = 128, BN = 128, NT = 256, KC = 3;   // 3 groups a stage: fewer barriers; 2 x 79872 B of LDS per CU
 constexpr int GB = 48;                      // container bytes per (row, group)
 // LDS layout of one group (byte offsets): per operand the three 16-byte chunks of each row's
 // 48 container bytes (half 0 bytes 0..15 | half 1 bytes 0..15 | both halves' bytes 16..23),
@@ -57,10 +59,9 @@ constexpr int L_X = 0;                      // X chunks 0, 1, 2 at L_X + 2048 c
 constexpr int L_W = 6144;                   // W chunks
 constexpr int L_SX = 12288;                 // X scales, one dword (fp16, zero-extended) per row
 constexpr int L_SW = 12800;                 // W scales
-constexpr int L_Z = 13312;                  // 128 zero bytes
-constexpr int GROUP = L_Z + 128;            // 13440
+constexpr int GROUP = 13312;
 constexpr int STAGE = KC * GROUP;
-constexpr int RING = 2 * STAGE;             // 80640 bytes
+constexpr int RING = 2 * STAGE;             // 79872 bytes
 // epilogue: buffer 1 of the ring (buffer 0 already receives the next tile's stage 0)
 constexpr int E_L2 = STAGE;                 // L2^T staging, 128 columns x (r + 8) halves
 constexpr int E_Y = STAGE;                  // fp16 output staging, per wave 32 rows x 136 bytes
@@ -321,8 +322,8 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
     rw_p0[i] = L_W + 2048 * h + (wn * 64 + i * 32 + r32) * 16;
     rx_p1[i] = opaque(L_X + 4096 + (wm * 64 + i * 32 + r32) * 16 + 8 * h);
     rw_p1[i] = opaque(L_W + 4096 + (wn * 64 + i * 32 + r32) * 16 + 8 * h);
-    rs_x[i] = opaque(h ? L_Z + r32 * 4 : L_SX + (wm * 64 + i * 32 + r32) * 4);
-    rs_w[i] = opaque(h ? L_Z + r32 * 4 : L_SW + (wn * 64 + i * 32 + r32) * 4);
+    rs_x[i] = opaque(L_SX + (wm * 64 + i * 32 + r32) * 4);   // both lane halves: one address
+    rs_w[i] = opaque(L_SW + (wn * 64 + i * 32 + r32) * 4);
   }
   // MFMA operands of one group.  Scale operands: the second dword stays zero; code operands:
   // six dwords.
@@ -363,7 +364,8 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
     for (int tj = 0; tj < 2; tj++)
 #pragma unroll
       for (int ti = 0; ti < 2; ti++) {
-        const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.wo[tj], o.xo[ti], v16f{}, 2, 2, 0, 133, 0, 127);
+        // P_g / 2 and 2 S (the scales sit in both K halves): the fma's product is exactly P_g S
+        const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.wo[tj], o.xo[ti], v16f{}, 2, 2, 0, 132, 0, 127);
         const v16f sc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h_t, o.swo[tj]),
                                                               __builtin_bit_cast(v4h_t, o.sxo[ti]), v16f{}, 0, 0, 0);
 #pragma unroll
@@ -383,12 +385,7 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
     tile_of3(tile, tiles, tiles_m, tiles_n, &tm, &tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
-    // the zero block of every group (the previous epilogue used buffer 1); stage 0 of this
-    // tile is in flight or landed in buffer 0
-    if (tid < 32) {
-#pragma unroll
-      for (int b = 0; b < 2 * KC; b++) *reinterpret_cast<uint32_t*>(lds + b * GROUP + L_Z + tid * 4) = 0u;
-    }
+    // stage 0 of this tile is in flight or landed in buffer 0
     wait_loads();
     __syncthreads();
 
