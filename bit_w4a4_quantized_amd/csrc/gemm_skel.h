@@ -239,18 +239,6 @@ __device__ __forceinline__ void persistent(Op& op, uint8_t* lds, const __half* _
   }
 }
 
-// Workgroups that stay resident: two per CU.
-inline int resident_blocks() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
-  if (cached[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    cached[dev] = 2 * cus;
-  }
-  return cached[dev];
-}
 
 }  // namespace skel
 }  // namespace svdq

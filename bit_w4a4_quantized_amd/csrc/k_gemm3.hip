@@ -679,18 +679,6 @@ k_gemm3_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, co
   }
 }
 
-// Workgroups that fit on the device at once (two per CU), cached per device.
-static int resident_blocks() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
-  if (cached[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    cached[dev] = 2 * cus;
-  }
-  return cached[dev];
-}
 
 // Full rounds of the persistent loop, then (when the remainder is at most a quarter of a
 // round) the remaining tiles as sub-tile jobs in the same launch; otherwise the persistent
@@ -714,7 +702,7 @@ static hipError_t launch_g3(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 64) return launch_g3_skinny<RB, BIAS, 2>(a, s);
   if (a.M <= kSkinnyRows) return launch_g3_skinny<RB, BIAS, 4>(a, s);
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  const int slots = resident_blocks();
+  const int slots = resident_workgroups();
   const int rem = tiles % slots;
   const int main_tiles = (tiles > slots && rem > 0 && 4 * rem <= slots) ? tiles - rem : tiles;
   const int nb = main_tiles < slots ? main_tiles : slots;

@@ -199,7 +199,7 @@ static hipError_t launch_f4_r(const GemmArgs& a, int nb, hipStream_t s) {
 
 hipError_t launch_gemm_f4(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  const int nb = tiles < resident_blocks() ? tiles : resident_blocks();
+  const int nb = tiles < resident_workgroups() ? tiles : resident_workgroups();
   return a.bias ? launch_f4_r<true>(a, nb, s) : launch_f4_r<false>(a, nb, s);
 }
 

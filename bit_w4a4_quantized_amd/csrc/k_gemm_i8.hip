@@ -160,7 +160,7 @@ static hipError_t launch_i8_r(const GemmArgs& a, int nb, hipStream_t s) {
 
 hipError_t launch_gemm_i8(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  const int nb = tiles < resident_blocks() ? tiles : resident_blocks();
+  const int nb = tiles < resident_workgroups() ? tiles : resident_workgroups();
   return a.bias ? launch_i8_r<true>(a, nb, s) : launch_i8_r<false>(a, nb, s);
 }
 

@@ -2,10 +2,28 @@
 //   * up projection as a separate kernel, for the unfused comparison
 //     ("sota-314", "Do this", latency table);
 //   * GELU(tanh) + smoothing glue between an MLP's two linears.
+#include <atomic>
+
 #include "kernels.h"
 #include "quant_core.h"
 
 namespace svdq {
+
+// Workgroups that stay resident on the current device at two per CU.  The CU count is read once
+// per device and cached (atomically: concurrent first calls store the same value).
+int resident_workgroups() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    v = 2 * cus;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
 
 // ---------------------------------------------------------------- up projection (unfused)
 // Y = fp16( float(Y0) + T L2 ): reads the fp16 output of the bare GEMM back.

@@ -258,22 +258,11 @@ k_w4a16(const __half* __restrict__ x, const uint8_t* __restrict__ wq, const __ha
   }
 }
 
-static int resident_blocks_w() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
-  if (cached[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    cached[dev] = 2 * cus;
-  }
-  return cached[dev];
-}
 
 hipError_t launch_w4a16(const void* x, const void* wq, const void* ws, const void* bias, int M, int N,
                         int K, void* y, hipStream_t s) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const int nb = tiles < resident_blocks_w() ? tiles : resident_blocks_w();
+  const int nb = tiles < resident_workgroups() ? tiles : resident_workgroups();
   if (bias)
     hipLaunchKernelGGL(k_w4a16<true>, dim3(nb), dim3(NT), 0, s, (const __half*)x, (const uint8_t*)wq,
                        (const __half*)ws, (const __half*)bias, M, N, K, (__half*)y);

@@ -53,6 +53,9 @@ struct QuantDownPlan {
 };
 QuantDownPlan quant_down_plan(int M, int K, int r, bool have_partials);
 
+// Workgroups that stay resident on the current device at two per CU (cached per device).
+int resident_workgroups();
+
 struct GemmArgs {
   const void* xq; const void* xs; const void* t; const void* wq; const void* ws;
   const void* l2; const void* bias; int M, N, K, r; int fmt;

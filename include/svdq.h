@@ -21,7 +21,8 @@
  * ---------------------------------------
  *  - Tensor pointers are DEVICE pointers, owned by the caller, row-major,
  *    16-byte aligned.  The library never allocates or frees memory and keeps
- *    no mutable global state; calls are thread-safe.
+ *    no mutable global state beyond a per-device cache of the compute-unit
+ *    count (set atomically on first use); calls are thread-safe.
  *  - `stream` is a hipStream_t (NULL = the default stream).  All work is
  *    enqueued on it asynchronously; nothing synchronizes the device and there
  *    are no host<->device copies.
