@@ -84,6 +84,8 @@ def settle(torch, fn, ms=None):
             fn(i)
             i += 1
         torch.cuda.synchronize()
+
+
 KERNEL_B_SOURCE = os.path.join(ROOT, "bit_w4a4_quantized_amd", "csrc", "k_gemm3.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "kernel_b_qkv_4608x3072x9216_traffic.md")
 

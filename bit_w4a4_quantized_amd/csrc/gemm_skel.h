@@ -22,6 +22,14 @@
 //   void load(const Src&, int st, uint8_t* buf);    the stage's LDS-DMA loads
 //   struct Regs; void read(const uint8_t* buf, int st, Regs&);
 //   void mma(const Regs&, int st, v16f (&acc)[2][2]);
+// and, for an operator whose kernel runs the last partial round as 32 x 32 sub-tile jobs
+// (operands straight into registers; with row-major codes each 16-byte lane load touches 32
+// cache lines, so this pays only where the codes are compact: FP4 yes, INT8 no):
+//   int NU; static constexpr int SUB_PD;            64-column units of K; register ring depth
+//   struct UR; void gload(int u, int m, int n, UR&);  unit u of lane's X row m, W row n (every
+//                                                   lane loads: no branch around a load)
+//   void gmma(const UR&, bool zero, v16f& acc);     acc += the unit's products (zero: the
+//                                                   unit adds exactly +0)
 #pragma once
 #include "kernels.h"
 
@@ -36,6 +44,8 @@ __host__ __device__ constexpr int epi_bytes(int R) {
 }
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 as_u4(u32x4_t v) { return make_uint4(v[0], v[1], v[2], v[3]); }
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, size_t bytes) {
@@ -239,6 +249,124 @@ __device__ __forceinline__ void persistent(Op& op, uint8_t* lds, const __half* _
   }
 }
 
+// One 32 x 32 sub-tile job of the last partial round (tiles past tiles_run, cut into 16 sub-tiles
+// each): the four waves split K (units w, w + 4, ...) through a register ring of PD units and
+// add their partial sums in LDS (red, 12 KB of the workgroup's LDS) in a fixed order, so the
+// result is deterministic.  Step s of the ring processes slot s % PD, which holds the wave's
+// unit s - PD (none for s < PD: zeroed slots, added as exactly +0), then refills it with unit s
+// (past the last one it re-reads the last one): no prologue and no branch in the loop, so the
+// compiler's wait counts let each slot wait for its own loads only.  The epilogue's operands
+// are loaded before the K loop.  Ends with a workgroup barrier (red is reused).
+template <class Op, int RB, bool BIAS>
+__device__ __forceinline__ void subtile_job(const Op& op, float (*red)[16][64], const __half* __restrict__ t,
+                                            const __half* __restrict__ l2, const __half* __restrict__ bias,
+                                            int M, int N, int tile0, int job, __half* __restrict__ y) {
+  constexpr int R = RB * 16;
+  constexpr int PD = Op::SUB_PD;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, r32 = lane & 31;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_of(tile0 + (job >> 4), tiles_m * tiles_n, tiles_m, tiles_n, &tm, &tn);
+  const int sub = job & 15;
+  const int nb = tn * BN + (sub >> 2) * 32, mb = tm * BM + (sub & 3) * 32;   // sub-tile origin
+  const int m = min(mb + r32, M - 1), n = min(nb + r32, N - 1);           // this lane's operand rows
+  uint4 tv[RB > 0 ? RB : 1];
+  uint32_t lv[RB > 0 ? RB : 1][8];
+#pragma unroll
+  for (int kb = 0; kb < RB; kb++) {
+    tv[kb] = *reinterpret_cast<const uint4*>(t + (size_t)m * R + kb * 16 + 8 * h);
+#pragma unroll
+    for (int e = 0; e < 8; e++) lv[kb][e] = __half_as_ushort(l2[(size_t)(kb * 16 + 8 * h + e) * N + n]);
+  }
+  uint2 braw[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++)   // columns past N read the last four (their outputs are not stored)
+    braw[q] = BIAS ? *reinterpret_cast<const uint2*>(bias + min(nb + 8 * q + 4 * h, N - 4)) : make_uint2(0u, 0u);
+  v16f acc;
+#pragma unroll
+  for (int i = 0; i < 16; i++) acc[i] = 0.f;
+  const int NU = op.NU;
+  const int nu = wave < NU ? (NU - 1 - wave) / 4 + 1 : 0;   // this wave's units
+  typename Op::UR ring[PD];
+#pragma unroll
+  for (int j = 0; j < PD; j++) ring[j] = typename Op::UR{};
+  for (int s0 = 0; s0 < nu + PD; s0 += PD) {
+    // the step number, hidden from loop analysis: "st < PD" holds on the first pass only, and
+    // the compiler would peel that pass (its zeroed slots fold to constants) and issue its
+    // loads as one block ordered by type, which merged wait counts then impose on every pass
+    int s0o = s0;
+    asm volatile("" : "+s"(s0o));
+#pragma unroll
+    for (int j = 0; j < PD; j++) {
+      const int st = s0o + j;
+      op.gmma(ring[j], st < PD || st - PD >= nu, acc);
+      op.gload(nu > 0 ? wave + 4 * min(st, nu - 1) : 0, m, n, ring[j]);
+      __builtin_amdgcn_sched_barrier(0);     // keep the slots in order: each waits for its own loads only
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) red[wave - 1][i][lane] = acc[i];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) acc[i] = ((acc[i] + red[0][i][lane]) + red[1][i][lane]) + red[2][i][lane];
+    // up projection: row operand L2^T (columns n), column operand T (rows m)
+#pragma unroll
+    for (int kb = 0; kb < RB; kb++) {
+      const uint4 lw = make_uint4(lv[kb][0] | (lv[kb][1] << 16), lv[kb][2] | (lv[kb][3] << 16),
+                                  lv[kb][4] | (lv[kb][5] << 16), lv[kb][6] | (lv[kb][7] << 16));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(lw), as_h8(tv[kb]), acc, 0, 0, 0);
+    }
+    // lane owns row mb + r32 and columns nb + 8 q + 4 h + j (reg 4 q + j)
+    const int mo = mb + r32;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int no = nb + 8 * q + 4 * h;
+      if (mo >= M || no >= N) continue;
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (BIAS) {
+        bv[0] = __half2float(__ushort_as_half((unsigned short)(braw[q].x & 0xFFFFu)));
+        bv[1] = __half2float(__ushort_as_half((unsigned short)(braw[q].x >> 16)));
+        bv[2] = __half2float(__ushort_as_half((unsigned short)(braw[q].y & 0xFFFFu)));
+        bv[3] = __half2float(__ushort_as_half((unsigned short)(braw[q].y >> 16)));
+      }
+      uint32_t hv[4];
+#pragma unroll
+      for (int j = 0; j < 4; j++) hv[j] = __half_as_ushort(__float2half_rn(acc[4 * q + j] + bv[j]));
+      *reinterpret_cast<uint2*>(y + (size_t)mo * N + no) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+    }
+  }
+  __syncthreads();
+}
+
+// The tiles past tiles_run (a last partial round) as sub-tile jobs, taken by the workgroups as
+// they finish their full tiles.  lds: the workgroup's LDS, free (no loads in flight).
+template <class Op, int RB, bool BIAS>
+__device__ __forceinline__ void subtile_jobs(const Op& op, uint8_t* lds, const __half* __restrict__ t,
+                                             const __half* __restrict__ l2, const __half* __restrict__ bias,
+                                             int M, int N, int tiles_run, __half* __restrict__ y) {
+  static_assert(2 * Op::BUF >= 3 * 16 * 64 * 4, "the sub-tile partial sums must fit the LDS ring");
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int n_sub = (tiles - tiles_run) * 16;
+  for (int job = blockIdx.x; job < n_sub; job += gridDim.x)
+    subtile_job<Op, RB, BIAS>(op, reinterpret_cast<float (*)[16][64]>(lds), t, l2, bias, M, N, tiles_run, job, y);
+}
+
+// Full rounds of the persistent loop, then (when the remainder is at most a quarter of a
+// round) the remaining tiles as sub-tile jobs in the same launch.  Returns the tiles the
+// persistent loop takes; *nb gets the grid size.
+inline int persistent_split(int M, int N, int* nb) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int slots = resident_workgroups();
+  const int rem = tiles % slots;
+  const int main_tiles = (tiles > slots && rem > 0 && 4 * rem <= slots) ? tiles - rem : tiles;
+  *nb = main_tiles < slots ? main_tiles : slots;
+  return main_tiles;
+}
 
 }  // namespace skel
 }  // namespace svdq

@@ -60,11 +60,13 @@ __device__ __forceinline__ void scale_pairs(uint32_t sd, h2_t* lo, h2_t* hi) {
 
 struct OpF4 {
   static constexpr int KC = 2;               // 64-K chunks per stage
+  static constexpr int SUB_PD = 4;           // sub-tile jobs: units in flight per wave
   static constexpr int L_X = 0, L_W = 4096, L_SX = 8192, L_SW = 8704, CHUNK = 9216;
   static constexpr int BUF = KC * CHUNK;
-  int M, N, K, C, NS;
+  int M, N, K, C, NS, NU;
   int lane, h, wave;
   rsrc_t rx, rw, rs;
+  rsrc_t gxs, gws;                           // whole scale arrays, for the sub-tile jobs' loads
   int xo[2], wo[2], sxo[2], swo[2];          // per-lane LDS read offsets within a chunk
 
   struct Src {
@@ -79,6 +81,9 @@ struct OpF4 {
       : M(M_), N(N_), K(K_) {
     C = K >> 6;
     NS = (C + KC - 1) / KC;
+    NU = C;
+    gxs = make_rsrc(xs, (size_t)M * K / 16);
+    gws = make_rsrc(ws, (size_t)N * K / 16);
     lane = threadIdx.x & 63;
     h = lane >> 5;
     wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -134,6 +139,30 @@ struct OpF4 {
       }
     }
   }
+  // sub-tile jobs: chunk u of the lane's X row m and W row n, codes 32 h .. 32 h + 31 (one
+  // 16-byte piece) and their two scale bytes 2 h, 2 h + 1 (the LDS path's mapping)
+  struct UR {
+    uint4 x, w;
+    uint32_t sx, sw;
+  };
+  __device__ void gload(int u, int m, int n, UR& o) const {
+    o.x = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rx, (int)((uint32_t)m * (uint32_t)(K / 2) + 16u * h), u * 32, 0));
+    o.w = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rw, (int)((uint32_t)n * (uint32_t)(K / 2) + 16u * h), u * 32, 0));
+    o.sx = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(gxs, (int)((uint32_t)m * (uint32_t)(K / 16) + 2u * h), u * 4, 0);
+    o.sw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(gws, (int)((uint32_t)n * (uint32_t)(K / 16) + 2u * h), u * 4, 0);
+  }
+  __device__ void gmma(const UR& o, bool zero, v16f& acc) const {
+    h2_t xs_lo, xs_hi, ws_lo, ws_hi;         // a zero scale makes every dequantized value 0
+    scale_pairs(zero ? 0u : o.sx, &xs_lo, &xs_hi);
+    scale_pairs(zero ? 0u : o.sw, &ws_lo, &ws_hi);
+    const uint32_t xd[4] = {o.x.x, o.x.y, o.x.z, o.x.w}, wd[4] = {o.w.x, o.w.y, o.w.z, o.w.w};
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+      const uint4 xv = dequant_fp4x8(xd[ks], ks < 2 ? xs_lo : xs_hi);
+      const uint4 wv = dequant_fp4x8(wd[ks], ks < 2 ? ws_lo : ws_hi);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(wv), as_h8(xv), acc, 0, 0, 0);
+    }
+  }
   __device__ void mma(const Regs& r, int st, v16f (&acc)[2][2]) const {
 #pragma unroll
     for (int k = 0; k < KC; k++) {
@@ -170,37 +199,37 @@ template <int RB, bool BIAS>
 __global__ void __launch_bounds__(NT, 2)
 k_gemm_f4(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const __half* __restrict__ t,
           const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const __half* __restrict__ l2,
-          const __half* __restrict__ bias, int M, int N, int K, __half* __restrict__ y) {
+          const __half* __restrict__ bias, int M, int N, int K, __half* __restrict__ y, int tiles_run) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * OpF4::BUF];
   OpF4 op(xq, xs, wq, ws, M, N, K);
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  persistent<OpF4, RB, BIAS>(op, lds, t, l2, bias, M, N, tiles, y);
+  persistent<OpF4, RB, BIAS>(op, lds, t, l2, bias, M, N, tiles_run, y);
+  subtile_jobs<OpF4, RB, BIAS>(op, lds, t, l2, bias, M, N, tiles_run, y);
 }
 
 template <int RB, bool BIAS>
-static hipError_t launch_f4_t(const GemmArgs& a, int nb, hipStream_t s) {
+static hipError_t launch_f4_t(const GemmArgs& a, hipStream_t s) {
+  int nb;
+  const int main_tiles = persistent_split(a.M, a.N, &nb);
   hipLaunchKernelGGL((k_gemm_f4<RB, BIAS>), dim3(nb), dim3(NT), 0, s, (const uint8_t*)a.xq, (const uint8_t*)a.xs,
                      (const __half*)a.t, (const uint8_t*)a.wq, (const uint8_t*)a.ws, (const __half*)a.l2,
-                     (const __half*)a.bias, a.M, a.N, a.K, (__half*)a.y);
+                     (const __half*)a.bias, a.M, a.N, a.K, (__half*)a.y, main_tiles);
   return hipGetLastError();
 }
 
 template <bool BIAS>
-static hipError_t launch_f4_r(const GemmArgs& a, int nb, hipStream_t s) {
+static hipError_t launch_f4_r(const GemmArgs& a, hipStream_t s) {
   switch (a.r) {
-    case 0: return launch_f4_t<0, BIAS>(a, nb, s);
-    case 16: return launch_f4_t<1, BIAS>(a, nb, s);
-    case 32: return launch_f4_t<2, BIAS>(a, nb, s);
-    case 48: return launch_f4_t<3, BIAS>(a, nb, s);
-    case 64: return launch_f4_t<4, BIAS>(a, nb, s);
+    case 0: return launch_f4_t<0, BIAS>(a, s);
+    case 16: return launch_f4_t<1, BIAS>(a, s);
+    case 32: return launch_f4_t<2, BIAS>(a, s);
+    case 48: return launch_f4_t<3, BIAS>(a, s);
+    case 64: return launch_f4_t<4, BIAS>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_f4(const GemmArgs& a, hipStream_t s) {
-  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  const int nb = tiles < resident_workgroups() ? tiles : resident_workgroups();
-  return a.bias ? launch_f4_r<true>(a, nb, s) : launch_f4_r<false>(a, nb, s);
+  return a.bias ? launch_f4_r<true>(a, s) : launch_f4_r<false>(a, s);
 }
 
 }  // namespace svdq

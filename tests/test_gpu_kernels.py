@@ -178,12 +178,12 @@ def test_gemm_up_parity(fmt, M, K, N, r, with_bias):
     assert ok, worst
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("r,with_bias", [(32, True), (0, False), (64, True)])
-def test_gemm_e2m3_partial_last_round(r, with_bias):
+def test_gemm_partial_last_round(fmt, r, with_bias):
     # Tile counts just above a whole number of persistent rounds (two workgroups per CU): the
-    # last few 128 x 128 tiles go to the sub-tile kernel.  Ragged M (last tile 91 rows) and an
+    # last few 128 x 128 tiles run as 32 x 32 sub-tile jobs.  Ragged M (last tile 91 rows) and an
     # odd number of K groups.
-    fmt = "int4_e2m3"
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     N, K = 1024, 192
     tiles_m = -(-(2 * cus + 8) // 8)
@@ -198,7 +198,7 @@ def test_gemm_e2m3_partial_last_round(r, with_bias):
     yg = host(y)
     assert np.isfinite(yg.astype(np.float32)).all()
     assert rel_fro(yg, ref) <= TOL
-    ok, worst = within_sum_bound(yg, ref, linear_abs_sum(xq, xs, t, wq, ws, l2, bias, fmt), K // 64 + r + 2)
+    ok, worst = within_sum_bound(yg, ref, linear_abs_sum(xq, xs, t, wq, ws, l2, bias, fmt), gemm_terms(fmt, K, r))
     assert ok, worst
 
 
