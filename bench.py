@@ -12,6 +12,8 @@ the same run also times, each on its own seeded layer and with fewer steps:
     its arithmetic intensity puts it under: HBM below 625 op/B, MFMA above; these short
     launches are timed from HIP graph replays, so host launch cost stays out, and the eager
     per-call time is reported beside them);
+  * that MLP pair end to end (fc1, GELU + fc2's smoothing, fc2), with the glue as its own
+    kernel and with it (and fc1's input smoothing) folded into fc1's two kernels;
   * on the QKV layer: the bare W4A4 GEMM (r = 0: no branch in either kernel),
     the unfused branch (down projection, quantization, GEMM, up projection as
     separate launches with an fp16 intermediate), and the W4A16 control (fp16
@@ -194,6 +196,7 @@ class Layer:
         x_hat = torch.from_numpy(host.smooth(raw.x)).cuda()
         self.name, self.lname, self.fmt, self.M, self.K, self.N, self.r = name, lname, fmt, M, K, N, r
         self.raw, self.host, self.torch, self.binding = raw, host, torch, binding
+        self.lam = dev.lam                   # fp32 [K], this layer's smoothing factors
         cp = lambda t: None if t is None else t.clone()
         self.sets = []
         for _ in range(ROTATE):
@@ -379,6 +382,54 @@ class Layer:
         return self.time_call(fn, steps, warmup)
 
 
+def time_mlp_pair(fc1, fc2, steps, warmup):
+    """The MLP pair fc1 -> GELU + fc2's smoothing -> fc2 (the same layers as the fc1 and fc2
+    workloads), with the glue as its own kernel (fc1's input smoothed beforehand on the host,
+    so that step is not timed) and with both steps folded into fc1's kernels (Kernel A smooths
+    fc1's raw input; Kernel B's epilogue writes fc2's smoothed input).  The two give fc2 the
+    same input bit for bit, which is checked."""
+    b, torch, fmt = fc1.binding, fc1.torch, fc1.fmt
+    x_raw = [torch.from_numpy(fc1.raw.x).cuda() for _ in range(ROTATE)]
+
+    def unfolded(i):
+        s1, s2 = fc1.sets[i % ROTATE], fc2.sets[i % ROTATE]
+        fc1.fused(i)
+        b.svdq_gelu_tanh_smooth(s1["y"], fc2.lam, out=s2["x"])
+        fc2.fused(i)
+
+    def folded(i):
+        s1, s2 = fc1.sets[i % ROTATE], fc2.sets[i % ROTATE]
+        b.svdq_quantize_down_smooth(x_raw[i % ROTATE], fc1.lam, s1["l1t"], fmt, xq=s1["xq"], xs=s1["xs"],
+                                    t=s1["t"], workspace=s1["wsa"])
+        b.svdq_gemm_w4a4_up_gelu_smooth(s1["xq"], s1["xs"], s1["t"], s1["wq"], s1["ws"], s1["l2"], s1["b"],
+                                        fc2.lam, fc1.K, fmt, y=s2["x"])
+        fc2.fused(i)
+
+    def glue(i):
+        s1, s2 = fc1.sets[i % ROTATE], fc2.sets[i % ROTATE]
+        b.svdq_gelu_tanh_smooth(s1["y"], fc2.lam, out=s2["x"])
+
+    unfolded(0)
+    torch.cuda.synchronize()
+    ref = fc2.sets[0]["x"].clone()
+    folded(0)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ref.view(torch.int16), fc2.sets[0]["x"].view(torch.int16)))
+    tu = fc1.time_call(unfolded, steps, warmup)
+    tf = fc1.time_call(folded, steps, warmup)
+    tg = fc1.time_call(glue, steps, warmup)
+    res = {"unfolded_us": round(tu["us_per_call"], 2), "folded_us": round(tf["us_per_call"], 2),
+           "glue_kernel_us": round(tg["us_per_call"], 2),
+           "folded_saves_pct": round(100.0 * (1.0 - tf["us_per_call"] / tu["us_per_call"]), 2),
+           "fc2_input_bitwise_equal": same,
+           "note": "unfolded: svdq_linear(fc1 on X_hat smoothed on the host) + svdq_gelu_tanh_smooth + "
+                   "svdq_linear(fc2); folded: svdq_quantize_down_smooth(raw X) + "
+                   "svdq_gemm_w4a4_up_gelu_smooth + svdq_linear(fc2)"}
+    if not same:
+        raise RuntimeError("folded and unfolded MLP pairs gave fc2 different inputs")
+    return res
+
+
 def device_facts(torch):
     """The device and runtime the numbers were taken on."""
     p = torch.cuda.get_device_properties(0)
@@ -527,10 +578,12 @@ def main():
             torch.cuda.empty_cache()
         out["formats_" + args.workload] = variants
         others = {}
+        mlp = {}
         for name in ("fc1", "fc2"):
             if name == args.workload:
                 continue
             Lo = Layer(torch, binding, name, fmt)
+            mlp[name] = Lo
             res = Lo.time_fused(es, ew)
             o_ops = 2.0 * Lo.M * Lo.N * Lo.K
             o_b = o_ops + 2.0 * Lo.M * Lo.r * Lo.N
@@ -566,8 +619,13 @@ def main():
                     log(f"fc1 M={m}: {sweep[str(m)]}")
                 out["small_batch_fc1"] = sweep
             del Lo
-            torch.cuda.empty_cache()
         out["other_workloads"] = others
+        if len(mlp) == 2:
+            pair = time_mlp_pair(mlp["fc1"], mlp["fc2"], es, ew)
+            log(f"mlp pair: {pair}")
+            out["mlp_pair_fc1_fc2"] = pair
+        del mlp
+        torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(L.raw, L.host, "int4", M, K, N, r, args.cpu_seconds)

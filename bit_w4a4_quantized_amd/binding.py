@@ -37,6 +37,12 @@ _SIGS = {
     "svdq_linear_unfused": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _c_size, _vp, _vp]),
     "svdq_gemm_w4a16": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "svdq_gelu_tanh_smooth": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp]),
+    "svdq_quantize_down_smooth": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp,
+                                           _c_size, _vp]),
+    "svdq_gemm_w4a4_up_gelu_smooth": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
+                                               _c_int, _c_int, _vp, _vp]),
+    "svdq_linear_folded": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                    _vp, _c_size, _vp, _vp]),
     "svdq_status_string": (ctypes.c_char_p, [_c_int]),
     "svdq_version": (ctypes.c_char_p, []),
 }
@@ -263,3 +269,71 @@ def svdq_gelu_tanh_smooth(y, lam, out=None, stream=None):
     _check("svdq_gelu_tanh_smooth", lib().svdq_gelu_tanh_smooth(
         _p(y), _p(lam), M, C, _p(out), _stream(stream)))
     return out
+
+
+def svdq_quantize_down_smooth(x, lam, l1t, fmt, xq=None, xs=None, t=None, workspace=None, no_workspace=False,
+                              stream=None):
+    """Kernel A on unsmoothed x fp16 [M, K] with the layer's factors lam fp32 [K]:
+    the codes, scales and T of X_hat = fp16(x / lam).  Returns (xq, xs, t).  Workspace as
+    for svdq_quantize_down."""
+    import torch
+    M, K = x.shape
+    r = 0 if l1t is None else l1t.shape[0]
+    _need(x, torch.float16, None, "x")
+    _need(lam, torch.float32, (K,), "lam")
+    if l1t is not None:
+        _need(l1t, torch.float16, (r, K), "l1t")
+    dev = x.device
+    if xq is None:
+        xq = torch.empty(code_shape(M, K, fmt), dtype=torch.uint8, device=dev)
+    if xs is None:
+        xs = torch.empty(scale_shape(M, K, fmt), dtype=scale_dtype(fmt), device=dev)
+    if r and t is None:
+        t = torch.empty((M, r), dtype=torch.float16, device=dev)
+    if no_workspace:
+        workspace = None
+    elif workspace is None:
+        nb = quantize_down_workspace_bytes(M, K, r, fmt)
+        workspace = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("svdq_quantize_down_smooth", lib().svdq_quantize_down_smooth(
+        _p(x), _p(lam), _p(l1t), M, K, r, _fmt(fmt), _p(xq), _p(xs), _p(t), _p(workspace), ws_bytes,
+        _stream(stream)))
+    return xq, xs, t
+
+
+def svdq_gemm_w4a4_up_gelu_smooth(xq, xs, t, wq, ws, l2, bias, lam_next, K, fmt, y=None, stream=None):
+    """Kernel B with an MLP's glue in its epilogue: fp16(gelu(Y) / lam_next), lam_next fp32 [N]."""
+    import torch
+    M = code_rows(xq)
+    N = code_rows(wq)
+    r = 0 if l2 is None else l2.shape[0]
+    _need(lam_next, torch.float32, (N,), "lam_next")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=xq.device)
+    _check("svdq_gemm_w4a4_up_gelu_smooth", lib().svdq_gemm_w4a4_up_gelu_smooth(
+        _p(xq), _p(xs), _p(t), _p(wq), _p(ws), _p(l2), _p(bias), _p(lam_next), M, N, K, r, _fmt(fmt), _p(y),
+        _stream(stream)))
+    return y
+
+
+def svdq_linear_folded(x, lam_in, l1t, wq, ws, l2, bias, lam_next, fmt, workspace=None, y=None, stream=None):
+    """The layer with either fold: lam_in fp32 [K] (x unsmoothed) and/or lam_next fp32 [N]
+    (output fp16(gelu(Y) / lam_next)); None for a fold not taken.  Returns y fp16 [M, N]."""
+    import torch
+    M, K = x.shape
+    N = code_rows(wq)
+    r = 0 if l1t is None else l1t.shape[0]
+    if lam_in is not None:
+        _need(lam_in, torch.float32, (K,), "lam_in")
+    if lam_next is not None:
+        _need(lam_next, torch.float32, (N,), "lam_next")
+    need = linear_workspace_bytes(M, K, r, fmt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _check("svdq_linear_folded", lib().svdq_linear_folded(
+        _p(x), _p(lam_in), _p(l1t), _p(wq), _p(ws), _p(l2), _p(bias), _p(lam_next), M, N, K, r, _fmt(fmt),
+        _p(workspace), workspace.numel() * workspace.element_size(), _p(y), _stream(stream)))
+    return y

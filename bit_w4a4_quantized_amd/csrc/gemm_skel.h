@@ -43,16 +43,6 @@ __host__ __device__ constexpr int epi_bytes(int R) {
   return BN * (R + 8) * 2 > 4 * 32 * E_YS ? BN * (R + 8) * 2 : 4 * 32 * E_YS;
 }
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 as_u4(u32x4_t v) { return make_uint4(v[0], v[1], v[2], v[3]); }
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, size_t bytes) {
-  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)n, 0x00020000);
-}
-
 // One wave's LDS-DMA load: lane l's 16 (4) bytes go to dst + 16 l (dst + 4 l); 2 bytes are
 // zero-extended to the dword at dst + 4 l.  dst must be wave-uniform.  Offsets go into the
 // vector or scalar offset (the immediate would move the LDS destination as well).
@@ -94,7 +84,8 @@ __device__ __forceinline__ v4h_t scale_operand(uint32_t s, int h) {
 template <int RB, bool BIAS>
 __device__ __forceinline__ void epilogue(v16f (&acc)[2][2], uint8_t* eb, const __half* __restrict__ t,
                                          const __half* __restrict__ l2, const __half* __restrict__ bias,
-                                         int M, int N, int m0, int n0, __half* __restrict__ y) {
+                                         const float* __restrict__ lam, int M, int N, int m0, int n0,
+                                         __half* __restrict__ y) {
   constexpr int R = RB * 16;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -152,6 +143,9 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[2][2], uint8_t* eb, const _
         }
       }
     }
+  // with the MLP glue folded in, the next layer's factors of the 8 columns this lane stores
+  const rsrc_t rl = make_rsrc(lam, lam ? (size_t)N * 4 : 0);
+  const float4 la = load_f4(rl, n0 + wn * 64 + (lane & 7) * 8), lb = load_f4(rl, n0 + wn * 64 + (lane & 7) * 8 + 4);
   uint8_t* ys = eb + wave * 32 * E_YS;
 #pragma unroll
   for (int ti = 0; ti < 2; ti++) {
@@ -171,8 +165,14 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[2][2], uint8_t* eb, const _
 #pragma unroll
     for (int it = 0; it < 4; it++) {
       const int rl = it * 8 + (lane >> 3), c = (lane & 7) * 8;   // row within the 32, column
-      const uint2 a = *reinterpret_cast<const uint2*>(ys + rl * E_YS + c * 2);
-      const uint2 b = *reinterpret_cast<const uint2*>(ys + rl * E_YS + c * 2 + 8);
+      uint2 a = *reinterpret_cast<const uint2*>(ys + rl * E_YS + c * 2);
+      uint2 b = *reinterpret_cast<const uint2*>(ys + rl * E_YS + c * 2 + 8);
+      if (lam) {                             // the MLP glue folded in: fp16(gelu(y) / lam)
+        a.x = gelu_div_h(a.x & 0xFFFFu, la.x) | (gelu_div_h(a.x >> 16, la.y) << 16);
+        a.y = gelu_div_h(a.y & 0xFFFFu, la.z) | (gelu_div_h(a.y >> 16, la.w) << 16);
+        b.x = gelu_div_h(b.x & 0xFFFFu, lb.x) | (gelu_div_h(b.x >> 16, lb.y) << 16);
+        b.y = gelu_div_h(b.y & 0xFFFFu, lb.z) | (gelu_div_h(b.y >> 16, lb.w) << 16);
+      }
       const int m = m0 + wm * 64 + ti * 32 + rl, n = n0 + wn * 64 + c;
       if (m < M && n < N) *reinterpret_cast<uint4*>(y + (size_t)m * N + n) = make_uint4(a.x, a.y, b.x, b.y);
     }
@@ -189,7 +189,8 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[2][2], uint8_t* eb, const _
 template <class Op, int RB, bool BIAS>
 __device__ __forceinline__ void persistent(Op& op, uint8_t* lds, const __half* __restrict__ t,
                                            const __half* __restrict__ l2, const __half* __restrict__ bias,
-                                           int M, int N, int tiles_run, __half* __restrict__ y) {
+                                           const float* __restrict__ lam, int M, int N, int tiles_run,
+                                           __half* __restrict__ y) {
   static_assert(Op::BUF >= epi_bytes(RB * 16), "the epilogue must fit one stage buffer");
   static_assert(Op::BUF % 16 == 0, "16-byte aligned buffers");
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -240,7 +241,7 @@ __device__ __forceinline__ void persistent(Op& op, uint8_t* lds, const __half* _
       step(st, 0);
       step(st + 1, 1);
     }
-    epilogue<RB, BIAS>(acc, lds + Op::BUF, t, l2, bias, M, N, m0, n0, y);
+    epilogue<RB, BIAS>(acc, lds + Op::BUF, t, l2, bias, lam, M, N, m0, n0, y);
     if (!has_next) break;
     tile = next;
     m0 = m1;
@@ -260,7 +261,8 @@ __device__ __forceinline__ void persistent(Op& op, uint8_t* lds, const __half* _
 template <class Op, int RB, bool BIAS>
 __device__ __forceinline__ void subtile_job(const Op& op, float (*red)[16][64], const __half* __restrict__ t,
                                             const __half* __restrict__ l2, const __half* __restrict__ bias,
-                                            int M, int N, int tile0, int job, __half* __restrict__ y) {
+                                            const float* __restrict__ lam, int M, int N, int tile0, int job,
+                                            __half* __restrict__ y) {
   constexpr int R = RB * 16;
   constexpr int PD = Op::SUB_PD;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -281,9 +283,13 @@ __device__ __forceinline__ void subtile_job(const Op& op, float (*red)[16][64], 
     for (int e = 0; e < 8; e++) lv[kb][e] = __half_as_ushort(l2[(size_t)(kb * 16 + 8 * h + e) * N + n]);
   }
   uint2 braw[4];
+  float4 lam4[4];                            // with the MLP glue folded in: the next layer's factors
+  const rsrc_t rl = make_rsrc(lam, lam ? (size_t)N * 4 : 0);
 #pragma unroll
-  for (int q = 0; q < 4; q++)   // columns past N read the last four (their outputs are not stored)
+  for (int q = 0; q < 4; q++) {  // columns past N read the last four (their outputs are not stored)
     braw[q] = BIAS ? *reinterpret_cast<const uint2*>(bias + min(nb + 8 * q + 4 * h, N - 4)) : make_uint2(0u, 0u);
+    lam4[q] = load_f4(rl, min(nb + 8 * q + 4 * h, N - 4));
+  }
   v16f acc;
 #pragma unroll
   for (int i = 0; i < 16; i++) acc[i] = 0.f;
@@ -337,6 +343,11 @@ __device__ __forceinline__ void subtile_job(const Op& op, float (*red)[16][64], 
       uint32_t hv[4];
 #pragma unroll
       for (int j = 0; j < 4; j++) hv[j] = __half_as_ushort(__float2half_rn(acc[4 * q + j] + bv[j]));
+      if (lam) {                             // the MLP glue folded in: fp16(gelu(y) / lam)
+        const float lq[4] = {lam4[q].x, lam4[q].y, lam4[q].z, lam4[q].w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) hv[j] = gelu_div_h(hv[j], lq[j]);
+      }
       *reinterpret_cast<uint2*>(y + (size_t)mo * N + no) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
     }
   }
@@ -348,12 +359,14 @@ __device__ __forceinline__ void subtile_job(const Op& op, float (*red)[16][64], 
 template <class Op, int RB, bool BIAS>
 __device__ __forceinline__ void subtile_jobs(const Op& op, uint8_t* lds, const __half* __restrict__ t,
                                              const __half* __restrict__ l2, const __half* __restrict__ bias,
-                                             int M, int N, int tiles_run, __half* __restrict__ y) {
+                                             const float* __restrict__ lam, int M, int N, int tiles_run,
+                                             __half* __restrict__ y) {
   static_assert(2 * Op::BUF >= 3 * 16 * 64 * 4, "the sub-tile partial sums must fit the LDS ring");
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int n_sub = (tiles - tiles_run) * 16;
   for (int job = blockIdx.x; job < n_sub; job += gridDim.x)
-    subtile_job<Op, RB, BIAS>(op, reinterpret_cast<float (*)[16][64]>(lds), t, l2, bias, M, N, tiles_run, job, y);
+    subtile_job<Op, RB, BIAS>(op, reinterpret_cast<float (*)[16][64]>(lds), t, l2, bias, lam, M, N, tiles_run, job,
+                              y);
 }
 
 // Full rounds of the persistent loop, then (when the remainder is at most a quarter of a

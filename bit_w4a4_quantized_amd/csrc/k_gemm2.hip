@@ -73,7 +73,8 @@ template <int CORE, int RB, bool BIAS>
 __global__ void __launch_bounds__(NTHREADS, 2)
 k_gemm2(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __half* __restrict__ t,
         const uint8_t* __restrict__ wq, const __half* __restrict__ ws, const __half* __restrict__ l2,
-        const __half* __restrict__ bias, int M, int N, int K, __half* __restrict__ y) {
+        const __half* __restrict__ bias, const float* __restrict__ lam, int M, int N, int K,
+        __half* __restrict__ y) {
   using C = CoreCfg<CORE>;
   constexpr int R = RB * 16;
   constexpr int KC = 2;                                  // groups per stage
@@ -252,12 +253,15 @@ k_gemm2(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
   for (int tj = 0; tj < 2; tj++) {
     if (!bok[tj]) continue;
     const float bv = BIAS ? __half2float(bias[bcol[tj]]) : 0.f;
+    const float lv = lam ? lam[bcol[tj]] : 0.f;   // with the MLP glue folded in: the next layer's factor
 #pragma unroll
     for (int ti = 0; ti < 2; ti++)
 #pragma unroll
       for (int i = 0; i < 16; i++) {
         const int mrow = m0 + wm * 64 + ti * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (mrow < M) y[(size_t)mrow * N + bcol[tj]] = __float2half_rn(acc[ti][tj][i] + bv);
+        uint32_t hv = __half_as_ushort(__float2half_rn(acc[ti][tj][i] + bv));
+        if (lam) hv = gelu_div_h(hv, lv);        // fp16(gelu(y) / lam)
+        if (mrow < M) y[(size_t)mrow * N + bcol[tj]] = __ushort_as_half((unsigned short)hv);
       }
   }
 }
@@ -267,7 +271,7 @@ static hipError_t launch_g2(const GemmArgs& a, hipStream_t s) {
   const int nb = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   hipLaunchKernelGGL((k_gemm2<CORE, RB, BIAS>), dim3(nb), dim3(NTHREADS), 0, s, (const uint8_t*)a.xq,
                      (const __half*)a.xs, (const __half*)a.t, (const uint8_t*)a.wq, (const __half*)a.ws,
-                     (const __half*)a.l2, (const __half*)a.bias, a.M, a.N, a.K, (__half*)a.y);
+                     (const __half*)a.l2, (const __half*)a.bias, a.lam, a.M, a.N, a.K, (__half*)a.y);
   return hipGetLastError();
 }
 

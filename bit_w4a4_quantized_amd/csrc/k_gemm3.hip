@@ -69,18 +69,6 @@ constexpr int E_YS = 136;
 static_assert(E_Y + 4 * 32 * E_YS <= RING, "output staging must fit buffer 1");
 static_assert(STAGE % 16 == 0 && GROUP % 16 == 0, "16-byte aligned buffers");
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, size_t bytes) {
-  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)n, 0x00020000);
-}
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint4 as_u4(u32x4_t v) { return make_uint4(v[0], v[1], v[2], v[3]); }
-__device__ __forceinline__ uint2 as_u2(u32x2_t v) { return make_uint2(v[0], v[1]); }
 
 // One wave's LDS-DMA load: lane l's 16 bytes (or 2 bytes, zero-extended to a dword) go to
 // dst + 16 l (dst + 4 l).  dst must be wave-uniform.
@@ -129,8 +117,9 @@ template <int RB, bool BIAS>
 __device__ __forceinline__ void gemm3_subtile(const uint8_t* __restrict__ xq, const __half* __restrict__ xs,
                                               const __half* __restrict__ t, const uint8_t* __restrict__ wq,
                                               const __half* __restrict__ ws, const __half* __restrict__ l2,
-                                              const __half* __restrict__ bias, int M, int N, int K,
-                                              __half* __restrict__ y, int tile0, int job, float (*red)[16][64]) {
+                                              const __half* __restrict__ bias, const float* __restrict__ lam,
+                                              int M, int N, int K, __half* __restrict__ y, int tile0, int job,
+                                              float (*red)[16][64]) {
   constexpr int R = RB * 16;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -175,9 +164,13 @@ __device__ __forceinline__ void gemm3_subtile(const uint8_t* __restrict__ xq, co
     for (int e = 0; e < 8; e++) lv[kb][e] = __half_as_ushort(l2[(size_t)(kb * 16 + 8 * h + e) * N + n]);
   }
   uint2 braw[4];
+  float4 lam4[4];                            // with the MLP glue folded in: the next layer's factors
+  const rsrc_t rl = make_rsrc(lam, lam ? (size_t)N * 4 : 0);
 #pragma unroll
-  for (int q = 0; q < 4; q++)   // columns past N read the last four (their outputs are not stored)
+  for (int q = 0; q < 4; q++) {  // columns past N read the last four (their outputs are not stored)
     braw[q] = BIAS ? *reinterpret_cast<const uint2*>(bias + min(nb + 8 * q + 4 * h, N - 4)) : make_uint2(0u, 0u);
+    lam4[q] = load_f4(rl, min(nb + 8 * q + 4 * h, N - 4));
+  }
   v16f acc;
 #pragma unroll
   for (int i = 0; i < 16; i++) acc[i] = 0.f;
@@ -245,6 +238,11 @@ __device__ __forceinline__ void gemm3_subtile(const uint8_t* __restrict__ xq, co
       uint32_t hv[4];
 #pragma unroll
       for (int j = 0; j < 4; j++) hv[j] = __half_as_ushort(__float2half_rn(acc[4 * q + j] + bv[j]));
+      if (lam) {                             // the MLP glue folded in: fp16(gelu(y) / lam)
+        const float lq[4] = {lam4[q].x, lam4[q].y, lam4[q].z, lam4[q].w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) hv[j] = gelu_div_h(hv[j], lq[j]);
+      }
       *reinterpret_cast<uint2*>(y + (size_t)mo * N + no) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
     }
   }
@@ -255,7 +253,8 @@ template <int RB, bool BIAS>
 __global__ void __launch_bounds__(NT, 2)
 k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __half* __restrict__ t,
         const uint8_t* __restrict__ wq, const __half* __restrict__ ws, const __half* __restrict__ l2,
-        const __half* __restrict__ bias, int M, int N, int K, __half* __restrict__ y, int tiles_run) {
+        const __half* __restrict__ bias, const float* __restrict__ lam, int M, int N, int K,
+        __half* __restrict__ y, int tiles_run) {
   constexpr int R = RB * 16;
   __shared__ __attribute__((aligned(16))) uint8_t lds[RING];
 
@@ -484,6 +483,9 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
           }
         }
       }
+    // with the MLP glue folded in, the next layer's factors of the 8 columns this lane stores
+    const rsrc_t rl = make_rsrc(lam, lam ? (size_t)N * 4 : 0);
+    const float4 la = load_f4(rl, n0 + wn * 64 + (lane & 7) * 8), lb = load_f4(rl, n0 + wn * 64 + (lane & 7) * 8 + 4);
     uint8_t* ys = lds + E_Y + wave * 32 * E_YS;
 #pragma unroll
     for (int ti = 0; ti < 2; ti++) {
@@ -504,8 +506,14 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
 #pragma unroll
       for (int it = 0; it < 4; it++) {
         const int rl = it * 8 + (lane >> 3), c = (lane & 7) * 8;   // row within the 32, column
-        const uint2 a = *reinterpret_cast<const uint2*>(ys + rl * E_YS + c * 2);
-        const uint2 b = *reinterpret_cast<const uint2*>(ys + rl * E_YS + c * 2 + 8);
+        uint2 a = *reinterpret_cast<const uint2*>(ys + rl * E_YS + c * 2);
+        uint2 b = *reinterpret_cast<const uint2*>(ys + rl * E_YS + c * 2 + 8);
+        if (lam) {                           // the MLP glue folded in: fp16(gelu(y) / lam)
+          a.x = gelu_div_h(a.x & 0xFFFFu, la.x) | (gelu_div_h(a.x >> 16, la.y) << 16);
+          a.y = gelu_div_h(a.y & 0xFFFFu, la.z) | (gelu_div_h(a.y >> 16, la.w) << 16);
+          b.x = gelu_div_h(b.x & 0xFFFFu, lb.x) | (gelu_div_h(b.x >> 16, lb.y) << 16);
+          b.y = gelu_div_h(b.y & 0xFFFFu, lb.z) | (gelu_div_h(b.y >> 16, lb.w) << 16);
+        }
         const int m = m0 + wm * 64 + ti * 32 + rl, n = n0 + wn * 64 + c;
         if (m < M && n < N) *reinterpret_cast<uint4*>(y + (size_t)m * N + n) = make_uint4(a.x, a.y, b.x, b.y);
       }
@@ -524,7 +532,7 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
   // (no loads are in flight: the last tile started none)
   const int n_sub = (tiles - tiles_run) * 16;
   for (int job = blockIdx.x; job < n_sub; job += gridDim.x)
-    gemm3_subtile<RB, BIAS>(xq, xs, t, wq, ws, l2, bias, M, N, K, y, tiles_run, job,
+    gemm3_subtile<RB, BIAS>(xq, xs, t, wq, ws, l2, bias, lam, M, N, K, y, tiles_run, job,
                             reinterpret_cast<float (*)[16][64]>(lds));
 }
 
@@ -538,7 +546,8 @@ template <int RB, bool BIAS, int MT>
 __global__ void __launch_bounds__(NT, 2)
 k_gemm3_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __half* __restrict__ t,
                const uint8_t* __restrict__ wq, const __half* __restrict__ ws, const __half* __restrict__ l2,
-               const __half* __restrict__ bias, int M, int N, int K, __half* __restrict__ y) {
+               const __half* __restrict__ bias, const float* __restrict__ lam, int M, int N, int K,
+               __half* __restrict__ y) {
   constexpr int R = RB * 16;
   constexpr int PD = MT <= 2 ? 4 : 2;       // groups in flight per wave
   __shared__ __attribute__((aligned(16))) float red[3][16][64];   // partials of waves 1..3, one row tile
@@ -589,9 +598,13 @@ k_gemm3_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, co
     }
   }
   uint2 braw[4];
+  float4 lam4[4];                            // with the MLP glue folded in: the next layer's factors
+  const rsrc_t rl = make_rsrc(lam, lam ? (size_t)N * 4 : 0);
 #pragma unroll
-  for (int q = 0; q < 4; q++)   // columns past N read the last four (their outputs are not stored)
+  for (int q = 0; q < 4; q++) {  // columns past N read the last four (their outputs are not stored)
     braw[q] = BIAS ? *reinterpret_cast<const uint2*>(bias + min(nb + 8 * q + 4 * h, N - 4)) : make_uint2(0u, 0u);
+    lam4[q] = load_f4(rl, min(nb + 8 * q + 4 * h, N - 4));
+  }
   v16f acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; mt++)
@@ -674,15 +687,17 @@ k_gemm3_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, co
       uint32_t hv[4];
 #pragma unroll
       for (int j = 0; j < 4; j++) hv[j] = __half_as_ushort(__float2half_rn(acc[mt][4 * q + j] + bv[q][j]));
+      if (lam) {                             // the MLP glue folded in: fp16(gelu(y) / lam)
+        const float lq[4] = {lam4[q].x, lam4[q].y, lam4[q].z, lam4[q].w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) hv[j] = gelu_div_h(hv[j], lq[j]);
+      }
       *reinterpret_cast<uint2*>(y + (size_t)mo * N + no) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
     }
   }
 }
 
 
-// Full rounds of the persistent loop, then (when the remainder is at most a quarter of a
-// round) the remaining tiles as sub-tile jobs in the same launch; otherwise the persistent
-// loop takes them all.
 // Up to this many token rows the weight-streaming kernel runs (in 128-row slabs).
 constexpr int kSkinnyRows = 256;
 
@@ -691,7 +706,7 @@ static hipError_t launch_g3_skinny(const GemmArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((k_gemm3_skinny<RB, BIAS, MT>), dim3((a.N + 31) / 32, (a.M + 32 * MT - 1) / (32 * MT)),
                      dim3(NT), 0, s, (const uint8_t*)a.xq,
                      (const __half*)a.xs, (const __half*)a.t, (const uint8_t*)a.wq, (const __half*)a.ws,
-                     (const __half*)a.l2, (const __half*)a.bias, a.M, a.N, a.K, (__half*)a.y);
+                     (const __half*)a.l2, (const __half*)a.bias, a.lam, a.M, a.N, a.K, (__half*)a.y);
   return hipGetLastError();
 }
 
@@ -708,7 +723,7 @@ static hipError_t launch_g3(const GemmArgs& a, hipStream_t s) {
   const int nb = main_tiles < slots ? main_tiles : slots;
   hipLaunchKernelGGL((k_gemm3<RB, BIAS>), dim3(nb), dim3(NT), 0, s, (const uint8_t*)a.xq,
                      (const __half*)a.xs, (const __half*)a.t, (const uint8_t*)a.wq, (const __half*)a.ws,
-                     (const __half*)a.l2, (const __half*)a.bias, a.M, a.N, a.K, (__half*)a.y, main_tiles);
+                     (const __half*)a.l2, (const __half*)a.bias, a.lam, a.M, a.N, a.K, (__half*)a.y, main_tiles);
   return hipGetLastError();
 }
 

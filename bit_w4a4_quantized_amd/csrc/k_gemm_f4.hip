@@ -199,11 +199,12 @@ template <int RB, bool BIAS>
 __global__ void __launch_bounds__(NT, 2)
 k_gemm_f4(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const __half* __restrict__ t,
           const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const __half* __restrict__ l2,
-          const __half* __restrict__ bias, int M, int N, int K, __half* __restrict__ y, int tiles_run) {
+          const __half* __restrict__ bias, const float* __restrict__ lam, int M, int N, int K,
+          __half* __restrict__ y, int tiles_run) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * OpF4::BUF];
   OpF4 op(xq, xs, wq, ws, M, N, K);
-  persistent<OpF4, RB, BIAS>(op, lds, t, l2, bias, M, N, tiles_run, y);
-  subtile_jobs<OpF4, RB, BIAS>(op, lds, t, l2, bias, M, N, tiles_run, y);
+  persistent<OpF4, RB, BIAS>(op, lds, t, l2, bias, lam, M, N, tiles_run, y);
+  subtile_jobs<OpF4, RB, BIAS>(op, lds, t, l2, bias, lam, M, N, tiles_run, y);
 }
 
 template <int RB, bool BIAS>
@@ -212,7 +213,7 @@ static hipError_t launch_f4_t(const GemmArgs& a, hipStream_t s) {
   const int main_tiles = persistent_split(a.M, a.N, &nb);
   hipLaunchKernelGGL((k_gemm_f4<RB, BIAS>), dim3(nb), dim3(NT), 0, s, (const uint8_t*)a.xq, (const uint8_t*)a.xs,
                      (const __half*)a.t, (const uint8_t*)a.wq, (const uint8_t*)a.ws, (const __half*)a.l2,
-                     (const __half*)a.bias, a.M, a.N, a.K, (__half*)a.y, main_tiles);
+                     (const __half*)a.bias, a.lam, a.M, a.N, a.K, (__half*)a.y, main_tiles);
   return hipGetLastError();
 }
 

@@ -131,18 +131,19 @@ template <int RB, bool BIAS>
 __global__ void __launch_bounds__(NT, 2)
 k_gemm_i8(const int8_t* __restrict__ xq, const __half* __restrict__ xs, const __half* __restrict__ t,
           const int8_t* __restrict__ wq, const __half* __restrict__ ws, const __half* __restrict__ l2,
-          const __half* __restrict__ bias, int M, int N, int K, __half* __restrict__ y) {
+          const __half* __restrict__ bias, const float* __restrict__ lam, int M, int N, int K,
+          __half* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * OpI8::BUF];
   OpI8 op(xq, xs, wq, ws, M, N, K);
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  persistent<OpI8, RB, BIAS>(op, lds, t, l2, bias, M, N, tiles, y);
+  persistent<OpI8, RB, BIAS>(op, lds, t, l2, bias, lam, M, N, tiles, y);
 }
 
 template <int RB, bool BIAS>
 static hipError_t launch_i8_t(const GemmArgs& a, int nb, hipStream_t s) {
   hipLaunchKernelGGL((k_gemm_i8<RB, BIAS>), dim3(nb), dim3(NT), 0, s, (const int8_t*)a.xq, (const __half*)a.xs,
                      (const __half*)a.t, (const int8_t*)a.wq, (const __half*)a.ws, (const __half*)a.l2,
-                     (const __half*)a.bias, a.M, a.N, a.K, (__half*)a.y);
+                     (const __half*)a.bias, a.lam, a.M, a.N, a.K, (__half*)a.y);
   return hipGetLastError();
 }
 

@@ -102,16 +102,8 @@ hipError_t launch_up_add(const void* y0, const void* t, const void* l2, int M, i
 }
 
 // ---------------------------------------------------------------- GELU + smoothing glue
-// out = fp16( gelu_tanh(float(y)) / lambda[c] ), fp32 arithmetic, 8 values per thread.
-// 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)) exactly, so gelu_tanh(v) = v / (1 + exp(-2u));
-// this form has no cancellation for negative v, where 1 + tanh(u) would lose
-// most of its bits in fp32.
-__device__ __forceinline__ float gelu_tanh(float v) {
-  const float k0 = 0.7978845608028654f;   // sqrt(2/pi)
-  const float u = k0 * (v + 0.044715f * v * v * v);
-  return v / (1.0f + expf(-2.0f * u));
-}
-
+// out = fp16( gelu_tanh(float(y)) / lambda[c] ) (gelu_div), 8 values per thread: the same
+// arithmetic as a GEMM epilogue with the glue folded in, so the two agree bit for bit.
 __global__ void __launch_bounds__(256)
 k_gelu_smooth(const __half* __restrict__ y, const float* __restrict__ lam, int M, int C,
               __half* __restrict__ out) {
@@ -128,8 +120,8 @@ k_gelu_smooth(const __half* __restrict__ y, const float* __restrict__ lam, int M
   uint32_t w[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const uint32_t a = __half_as_ushort(__float2half_rn(gelu_tanh(v[2 * i]) / lv[2 * i]));
-    const uint32_t b = __half_as_ushort(__float2half_rn(gelu_tanh(v[2 * i + 1]) / lv[2 * i + 1]));
+    const uint32_t a = __half_as_ushort(__float2half_rn(gelu_div(v[2 * i], lv[2 * i])));
+    const uint32_t b = __half_as_ushort(__float2half_rn(gelu_div(v[2 * i + 1], lv[2 * i + 1])));
     w[i] = a | (b << 16);
   }
   reinterpret_cast<uint4*>(out)[idx8] = make_uint4(w[0], w[1], w[2], w[3]);

@@ -31,6 +31,11 @@
 //   (quant_core.h); the 6-bit container's fields are packed by the FP6 convert
 //   instruction.  A chunk's codes are assembled in the wave's LDS slot and
 //   written with whole 16-byte stores.
+// With SMOOTH the input is the unsmoothed x and lam [K] the layer's smoothing factors: each
+// lane fetches one lam value per chunk with the chunk's loads (the chunk's 64 values across
+// the wave), takes its 16 columns' values from the other lanes with cross-lane shuffles, and
+// replaces each fp16 x by X_hat = fp16_rne(x / lam) (IEEE fp32 division, one rounding to
+// fp16) before anything else reads it: codes, scales and T are those of X_hat.
 #include "kernels.h"
 #include "quant_core.h"
 
@@ -55,16 +60,17 @@ __device__ __forceinline__ h2_t as_h2(uint32_t w) { return __builtin_bit_cast(h2
 
 }  // namespace
 
-// waves per SIMD that the register budget allows at NRT row tiles and r = 16 RB (no spills)
-__host__ __device__ constexpr int qd_waves_per_simd(int nrt, int rb) {
-  return nrt >= 4 ? 2 : (nrt == 2 ? (rb <= 2 ? 3 : 2) : (rb <= 2 ? 4 : (rb == 3 ? 3 : 2)));
+// waves per SIMD that the register budget allows at NRT row tiles and r = 16 RB (no spills);
+// the smoothing variant holds the chunk's factors and division temporaries as well
+__host__ __device__ constexpr int qd_waves_per_simd(int nrt, int rb, bool smooth) {
+  return cmax(2, (nrt >= 4 ? 2 : (nrt == 2 ? (rb <= 2 ? 3 : 2) : (rb <= 2 ? 4 : (rb == 3 ? 3 : 2)))) - (smooth ? 1 : 0));
 }
 
-template <int FMT, int NRT, int RB, bool QUANT>
-__global__ void __launch_bounds__(QD_NT, qd_waves_per_simd(NRT, RB))
+template <int FMT, int NRT, int RB, bool QUANT, bool SMOOTH>
+__global__ void __launch_bounds__(QD_NT, qd_waves_per_simd(NRT, RB, SMOOTH))
 k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M, int K, int cpb,
              uint8_t* __restrict__ xq, uint8_t* __restrict__ xs, __half* __restrict__ t,
-             float* __restrict__ part) {
+             float* __restrict__ part, const float* __restrict__ lam) {
   constexpr int R = RB * 16;
   constexpr int RBX = RB > 0 ? RB : 1;
   constexpr int ROWS = 16 * NRT;
@@ -99,9 +105,11 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
   struct Buf {
     uint4 x[NRT][2];
     uint4 b[RBX][2];
+    float l;                                 // SMOOTH: lam of the chunk's column `lane`
   };
   auto load = [&](int c, Buf& B) {
     const int col = c * 64;
+    B.l = SMOOTH ? lam[col + lane] : 0.0f;
 #pragma unroll
     for (int rt = 0; rt < NRT; rt++) {
       B.x[rt][0] = *reinterpret_cast<const uint4*>(xr[rt] + col);
@@ -117,7 +125,29 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
   uint8_t* slot = smem + wave * ROWS * CB;   // this wave's code staging (STAGE)
   const size_t code_row = FMT == FMT_INT8 ? (size_t)K : (size_t)(K >> 1);   // row-major formats
 
-  auto process = [&](int c, const Buf& B) {
+  auto process = [&](int c, Buf& B) {
+    if constexpr (SMOOTH) {
+      // this lane's columns: 8 sub + e (first 16-byte piece) and 32 + 8 sub + e (second)
+      float lv[16];
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        lv[e] = __shfl(B.l, sub * 8 + e);
+        lv[8 + e] = __shfl(B.l, 32 + sub * 8 + e);
+      }
+#pragma unroll
+      for (int rt = 0; rt < NRT; rt++)
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+          float v[8];
+          unpack_h8(B.x[rt][hh], v);
+          uint32_t w[4];
+#pragma unroll
+          for (int i = 0; i < 4; i++)
+            w[i] = (uint32_t)__half_as_ushort(__float2half_rn(v[2 * i] / lv[8 * hh + 2 * i])) |
+                   ((uint32_t)__half_as_ushort(__float2half_rn(v[2 * i + 1] / lv[8 * hh + 2 * i + 1])) << 16);
+          B.x[rt][hh] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
     // ---- down projection on the matrix core (fp16 in, fp32 accumulate)
 #pragma unroll
     for (int rt = 0; rt < NRT; rt++)
@@ -356,16 +386,18 @@ k_t_finalize(const float* __restrict__ part, int S, size_t MR, __half* __restric
   *reinterpret_cast<uint2*>(t + i) = make_uint2(h0, h1);
 }
 
-// ---- launch plan: row blocks of 64 (32 for r > 32; 16 when K cannot be sliced for want of a
-// workspace),
-// K sliced into chunks-per-block multiples of 4 so that about QD_TARGET_BLOCKS workgroups
-// cover the chip.
-QuantDownPlan quant_down_plan(int M, int K, int r, bool have_partials) {
+// ---- launch plan: row blocks of 64 (32 for r > 32, and for r = 32 with smoothing; 16 when K
+// cannot be sliced for want of a workspace), K sliced into chunks-per-block multiples of 4 so
+// that about QD_TARGET_BLOCKS workgroups cover the chip.  The slicing is that of the plain
+// variant's row blocks in both variants: T's partial sums are then added in the same groups
+// and order, and the smoothing variant's T equals the plain one's on the smoothed input.
+QuantDownPlan quant_down_plan(int M, int K, int r, bool have_partials, bool smooth) {
   QuantDownPlan p{};
   const int nch = K >> 6;
   const bool can_slice = r == 0 || have_partials;
-  p.nrt = can_slice ? (r <= 32 ? QD_NRT : 2) : 1;   // rows per block within the register budget
-  const long rows_blocks = (M + 16 * p.nrt - 1) / (16 * p.nrt);
+  const int nrt_plain = can_slice ? (r <= 32 ? QD_NRT : 2) : 1;   // rows per block within the
+  p.nrt = smooth && can_slice && r == 32 ? 2 : nrt_plain;          // register budget
+  const long rows_blocks = (M + 16 * nrt_plain - 1) / (16 * nrt_plain);
   if (!can_slice) {
     p.cpb = nch;
   } else {
@@ -376,17 +408,17 @@ QuantDownPlan quant_down_plan(int M, int K, int r, bool have_partials) {
     if (p.cpb > nch) p.cpb = ((nch + 3) / 4) * 4;
   }
   p.slices = (nch + p.cpb - 1) / p.cpb;
-  p.rows_blocks = (int)rows_blocks;
+  p.rows_blocks = (M + 16 * p.nrt - 1) / (16 * p.nrt);
   p.partial_bytes = (r > 0 && p.slices > 1) ? (size_t)p.slices * M * r * 4 : 0;
   return p;
 }
 
-template <int FMT, int NRT, int RB, bool QUANT>
+template <int FMT, int NRT, int RB, bool QUANT, bool SMOOTH>
 static hipError_t launch_qd(const QuantDownArgs& a, const QuantDownPlan& p, hipStream_t s) {
   float* part = (RB > 0 && p.slices > 1) ? static_cast<float*>(a.part) : nullptr;
-  hipLaunchKernelGGL((k_quant_down<FMT, NRT, RB, QUANT>), dim3(p.slices, p.rows_blocks), dim3(QD_NT), 0, s,
+  hipLaunchKernelGGL((k_quant_down<FMT, NRT, RB, QUANT, SMOOTH>), dim3(p.slices, p.rows_blocks), dim3(QD_NT), 0, s,
                      (const __half*)a.x, (const __half*)a.l1t, a.M, a.K, p.cpb, (uint8_t*)a.xq, (uint8_t*)a.xs,
-                     (__half*)a.t, part);
+                     (__half*)a.t, part, a.lam);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !part) return e;
   const size_t MR = (size_t)a.M * a.r;
@@ -395,40 +427,45 @@ static hipError_t launch_qd(const QuantDownArgs& a, const QuantDownPlan& p, hipS
   return hipGetLastError();
 }
 
-template <int FMT, int RB, bool QUANT>
+template <int FMT, int RB, bool QUANT, bool SMOOTH>
 static hipError_t launch_qd_n(const QuantDownArgs& a, const QuantDownPlan& p, hipStream_t s) {
   switch (p.nrt) {
     case 4:
-      if constexpr (RB <= 2 && QD_NRT == 4) return launch_qd<FMT, 4, RB, QUANT>(a, p, s);
+      if constexpr (RB <= 2 && QD_NRT == 4 && !(SMOOTH && RB == 2)) return launch_qd<FMT, 4, RB, QUANT, SMOOTH>(a, p, s);
       break;
-    case 2: return launch_qd<FMT, 2, RB, QUANT>(a, p, s);
-    case 1: return launch_qd<FMT, 1, RB, QUANT>(a, p, s);
+    case 2: return launch_qd<FMT, 2, RB, QUANT, SMOOTH>(a, p, s);
+    case 1: return launch_qd<FMT, 1, RB, QUANT, SMOOTH>(a, p, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <int FMT, bool QUANT>
+template <int FMT, bool QUANT, bool SMOOTH = false>
 static hipError_t launch_qd_r(const QuantDownArgs& a, hipStream_t s) {
-  QuantDownPlan p = quant_down_plan(a.M, a.K, a.r, true);
-  if (p.partial_bytes > 0 && (!a.part || a.part_bytes < p.partial_bytes)) p = quant_down_plan(a.M, a.K, a.r, false);
+  QuantDownPlan p = quant_down_plan(a.M, a.K, a.r, true, SMOOTH);
+  if (p.partial_bytes > 0 && (!a.part || a.part_bytes < p.partial_bytes)) p = quant_down_plan(a.M, a.K, a.r, false, SMOOTH);
   switch (a.r) {
-    case 0: return launch_qd_n<FMT, 0, QUANT>(a, p, s);
-    case 16: return launch_qd_n<FMT, 1, QUANT>(a, p, s);
-    case 32: return launch_qd_n<FMT, 2, QUANT>(a, p, s);
-    case 48: return launch_qd_n<FMT, 3, QUANT>(a, p, s);
-    case 64: return launch_qd_n<FMT, 4, QUANT>(a, p, s);
+    case 0: return launch_qd_n<FMT, 0, QUANT, SMOOTH>(a, p, s);
+    case 16: return launch_qd_n<FMT, 1, QUANT, SMOOTH>(a, p, s);
+    case 32: return launch_qd_n<FMT, 2, QUANT, SMOOTH>(a, p, s);
+    case 48: return launch_qd_n<FMT, 3, QUANT, SMOOTH>(a, p, s);
+    case 64: return launch_qd_n<FMT, 4, QUANT, SMOOTH>(a, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool SMOOTH>
+static hipError_t launch_quant_down_s(const QuantDownArgs& a, hipStream_t s) {
+  switch (a.fmt) {
+    case FMT_INT4: return launch_qd_r<FMT_INT4, true, SMOOTH>(a, s);
+    case FMT_INT4_E2M3: return launch_qd_r<FMT_INT4_E2M3, true, SMOOTH>(a, s);
+    case FMT_INT8: return launch_qd_r<FMT_INT8, true, SMOOTH>(a, s);
+    case FMT_FP4: return launch_qd_r<FMT_FP4, true, SMOOTH>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_quant_down(const QuantDownArgs& a, hipStream_t s) {
-  switch (a.fmt) {
-    case FMT_INT4: return launch_qd_r<FMT_INT4, true>(a, s);
-    case FMT_INT4_E2M3: return launch_qd_r<FMT_INT4_E2M3, true>(a, s);
-    case FMT_INT8: return launch_qd_r<FMT_INT8, true>(a, s);
-    case FMT_FP4: return launch_qd_r<FMT_FP4, true>(a, s);
-  }
-  return hipErrorInvalidValue;
+  return a.lam ? launch_quant_down_s<true>(a, s) : launch_quant_down_s<false>(a, s);
 }
 
 // Unfused comparison: quantization alone (no branch) ...

@@ -37,13 +37,6 @@ constexpr int E_Y = GROUP;                  // epilogue: buffer 1, per wave 32 r
 constexpr int E_YS = 80;
 static_assert(E_Y + 4 * 32 * E_YS <= RING, "output staging must fit buffer 1");
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, size_t bytes) {
-  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)n, 0x00020000);
-}
 // LDS-DMA loads: lane l's 16 bytes go to dst + 16 l, its 2 bytes zero-extended to dst + 4 l
 __device__ __forceinline__ void dma16(rsrc_t r, uint8_t* dst, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)voff, (int)soff, 0, 0);

@@ -44,7 +44,8 @@ struct Workspace {
 };
 
 // Kernel A's partial sums of T (0 bytes when its K is not sliced)
-size_t partial_bytes(int M, int K, int r) { return round256(quant_down_plan(M, K, r, true).partial_bytes); }
+// Kernel A's partial sums (the plain and the smoothing variant slice K alike)
+size_t partial_bytes(int M, int K, int r) { return round256(quant_down_plan(M, K, r, true, false).partial_bytes); }
 
 Workspace carve(void* base, int M, int N, int K, int r, int fmt, bool with_y0) {
   Workspace w{};
@@ -167,6 +168,62 @@ svdq_status svdq_linear(const void* x_hat, const void* l1t, const void* wq, cons
   return map_launch(launch_gemm(ga, s));
 }
 
+svdq_status svdq_quantize_down_smooth(const void* x, const float* lambda, const void* l1t, int M, int K, int r,
+                                      svdq_format fmt, void* xq, void* xs, void* t, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  svdq_status st = check_quant_down(x, l1t, M, K, r, fmt, xq, xs, t);
+  if (st != SVDQ_OK) return st;
+  if (M == 0) return SVDQ_OK;
+  if (!lambda) return SVDQ_ERR_NULL;
+  if (!aligned16(lambda)) return SVDQ_ERR_ALIGN;
+  const size_t need = partial_bytes(M, K, r);
+  if (workspace && need) {
+    if (!aligned16(workspace)) return SVDQ_ERR_ALIGN;
+    if (workspace_bytes < need) return SVDQ_ERR_WORKSPACE;
+  }
+  QuantDownArgs a{x, l1t, M, K, r, (int)fmt, xq, xs, t, need ? workspace : nullptr, need ? workspace_bytes : 0, lambda};
+  return map_launch(launch_quant_down(a, static_cast<hipStream_t>(stream)));
+}
+
+svdq_status svdq_gemm_w4a4_up_gelu_smooth(const void* xq, const void* xs, const void* t, const void* wq,
+                                          const void* ws, const void* l2, const void* bias,
+                                          const float* lambda_next, int M, int N, int K, int r, svdq_format fmt,
+                                          void* y, void* stream) {
+  svdq_status st = check_gemm(xq, xs, t, wq, ws, l2, bias, M, N, K, r, fmt, y);
+  if (st != SVDQ_OK) return st;
+  if (M == 0 || N == 0) return SVDQ_OK;
+  if (!lambda_next) return SVDQ_ERR_NULL;
+  if (!aligned16(lambda_next)) return SVDQ_ERR_ALIGN;
+  GemmArgs a{xq, xs, t, wq, ws, l2, bias, M, N, K, r, (int)fmt, y, lambda_next};
+  return map_launch(launch_gemm(a, static_cast<hipStream_t>(stream)));
+}
+
+svdq_status svdq_linear_folded(const void* x, const float* lambda_in, const void* l1t, const void* wq,
+                               const void* ws, const void* l2, const void* bias, const float* lambda_next, int M,
+                               int N, int K, int r, svdq_format fmt, void* workspace, size_t workspace_bytes,
+                               void* y, void* stream) {
+  if (!fmt_ok(fmt)) return SVDQ_ERR_FORMAT;
+  svdq_status st = check_dims(M, N, K, r);
+  if (st != SVDQ_OK) return st;
+  if (M == 0 || N == 0) return SVDQ_OK;
+  if (!x || !wq || !ws || !y || !workspace) return SVDQ_ERR_NULL;
+  if (r > 0 && (!l1t || !l2)) return SVDQ_ERR_NULL;
+  if (!aligned16(workspace)) return SVDQ_ERR_ALIGN;
+  if ((lambda_in && !aligned16(lambda_in)) || (lambda_next && !aligned16(lambda_next))) return SVDQ_ERR_ALIGN;
+  const Workspace w = carve(workspace, M, N, K, r, fmt, false);
+  if (workspace_bytes < w.total) return SVDQ_ERR_WORKSPACE;
+  st = check_quant_down(x, l1t, M, K, r, fmt, w.xq, w.xs, w.t);
+  if (st != SVDQ_OK) return st;
+  st = check_gemm(w.xq, w.xs, w.t, wq, ws, l2, bias, M, N, K, r, fmt, y);
+  if (st != SVDQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QuantDownArgs qa{x, l1t, M, K, r, (int)fmt, w.xq, w.xs, w.t, w.part, w.part_bytes, lambda_in};
+  st = map_launch(launch_quant_down(qa, s));
+  if (st != SVDQ_OK) return st;
+  GemmArgs ga{w.xq, w.xs, w.t, wq, ws, l2, bias, M, N, K, r, (int)fmt, y, lambda_next};
+  return map_launch(launch_gemm(ga, s));
+}
+
 svdq_status svdq_quantize_weight(const float* r_t, int N, int K, svdq_format fmt, void* wq, void* ws,
                                  void* stream) {
   if (!fmt_ok(fmt)) return SVDQ_ERR_FORMAT;
@@ -232,7 +289,6 @@ svdq_status svdq_gelu_tanh_smooth(const void* y, const float* lambda, int M, int
   if (M == 0) return SVDQ_OK;
   if (!y || !lambda || !out) return SVDQ_ERR_NULL;
   if (!aligned16(y) || !aligned16(lambda) || !aligned16(out)) return SVDQ_ERR_ALIGN;
-  if (M == 0) return SVDQ_OK;
   return map_launch(launch_gelu_smooth(y, lambda, M, C, out, static_cast<hipStream_t>(stream)));
 }
 

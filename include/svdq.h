@@ -207,12 +207,68 @@ svdq_status svdq_gemm_w4a16(const void* x, const void* wq, const void* ws, const
 /*
  * GELU(tanh) + smoothing glue between an MLP's two linears:
  *   out[m, c] = fp16_rne( gelu_tanh(float(y[m, c])) / lambda[c] ),
- *   gelu_tanh(v) = 0.5 v (1 + tanh( sqrt(2/pi) (v + 0.044715 v^3) )), in fp32.
+ *   gelu_tanh(v) = 0.5 v (1 + tanh( sqrt(2/pi) (v + 0.044715 v^3) )),
+ *   evaluated in fp32 as gelu_div(v, lam) = v / ((1 + exp(-2u)) lam) with
+ *   u = sqrt(2/pi) (v + 0.044715 v^3) (the same value; no cancellation for
+ *   negative v), exp and the reciprocal from the hardware's approximations:
+ *   within one fp16 ulp of the exactly rounded result.
  *   y: fp16 [M, C]; lambda: fp32 [C] (the second layer's smoothing factors);
  *   out: fp16 [M, C] (may not alias y).  C % 8 == 0.
  */
 svdq_status svdq_gelu_tanh_smooth(const void* y, const float* lambda, int M, int C, void* out,
                                   void* stream);
+
+/*
+ * Folding the neighbouring steps into the two kernels.  The pages fuse the
+ * branch with the low-bit kernels because the fused steps share an operand
+ * ("sota-314", "Do this"); the same argument carries the steps on either side
+ * of a layer into the kernels: the smoothing of the layer's input into Kernel A
+ * (both read X) and an MLP's GELU + next-layer smoothing into Kernel B's
+ * epilogue (both write the output).  The pages do not describe this fold.
+ *
+ * Kernel A on the unsmoothed activations ("sota-314", "Do this": smoothing
+ * divides each input channel by its factor, X_hat = X diag(lambda)^-1):
+ *   x      : fp16 [M, K], unsmoothed.
+ *   lambda : fp32 [K], the layer's smoothing factors (> 0), 16-byte aligned.
+ *   Every value is first replaced by X_hat = fp16_rne(fp32(x) / lambda[k])
+ *   (IEEE fp32 division, then one rounding); codes, scales and T are then
+ *   exactly those svdq_quantize_down gives for that X_hat.  Other arguments,
+ *   the workspace rules and errors as for svdq_quantize_down; lambda NULL is
+ *   SVDQ_ERR_NULL.
+ */
+svdq_status svdq_quantize_down_smooth(const void* x, const float* lambda, const void* l1t, int M, int K,
+                                      int r, svdq_format fmt, void* xq, void* xs, void* t,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Kernel B with an MLP's glue in its epilogue: writes
+ *   y[m, n] = fp16_rne( gelu_div( Y[m, n], lambda_next[n] ) ),
+ * where Y is the fp16 output svdq_gemm_w4a4_up would write and gelu_div is the
+ * arithmetic of svdq_gelu_tanh_smooth, so the result equals
+ * svdq_gelu_tanh_smooth(svdq_gemm_w4a4_up(...), lambda_next) bit for bit
+ * without the fp16 round trip of Y through memory.
+ *   lambda_next : fp32 [N], the next layer's smoothing factors (> 0), 16-byte
+ *                 aligned; NULL is SVDQ_ERR_NULL.
+ * Other arguments and errors as for svdq_gemm_w4a4_up.
+ */
+svdq_status svdq_gemm_w4a4_up_gelu_smooth(const void* xq, const void* xs, const void* t, const void* wq,
+                                          const void* ws, const void* l2, const void* bias,
+                                          const float* lambda_next, int M, int N, int K, int r,
+                                          svdq_format fmt, void* y, void* stream);
+
+/*
+ * The fused layer with either fold: svdq_linear's Kernel A then Kernel B, with
+ * lambda_in != NULL taking x unsmoothed (as svdq_quantize_down_smooth) and
+ * lambda_next != NULL writing fp16(gelu(Y) / lambda_next) (as
+ * svdq_gemm_w4a4_up_gelu_smooth).  With both NULL it is svdq_linear.  An
+ * MLP's first layer runs with both; its output is then the second layer's
+ * X_hat, for svdq_linear.  Workspace as for svdq_linear
+ * (svdq_linear_workspace_bytes covers the smoothing variant's plan too).
+ */
+svdq_status svdq_linear_folded(const void* x, const float* lambda_in, const void* l1t, const void* wq,
+                               const void* ws, const void* l2, const void* bias, const float* lambda_next,
+                               int M, int N, int K, int r, svdq_format fmt, void* workspace,
+                               size_t workspace_bytes, void* y, void* stream);
 
 /* Static description of a status code. */
 const char* svdq_status_string(svdq_status s);

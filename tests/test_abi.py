@@ -148,6 +148,35 @@ def test_weight_gelu_w4a16_validation():
     assert L.svdq_gemm_w4a16(P, P, P, None, 0, 16, 64, P, None) == OK
 
 
+def test_folded_entry_points_validation():
+    # the steps folded into the kernels: the factor vectors are required where the entry point
+    # names them, and checked for alignment; everything else as for the plain entry points
+    L = binding.lib()
+    qs = lambda x=P, lam=P, l1=P, M=16, K=64, r=16, fmt=0, xq=P: L.svdq_quantize_down_smooth(
+        x, lam, l1, M, K, r, fmt, xq, P, P, None, 0, None)
+    assert qs(lam=None) == NULL
+    assert qs(lam=MIS) == ALIGN
+    assert qs(x=None) == NULL
+    assert qs(K=96) == SHAPE
+    assert qs(fmt=7) == FORMAT
+    assert qs(M=0, lam=None) == OK
+    gg = lambda lam=P, M=16, N=16, bias=P, fmt=0: L.svdq_gemm_w4a4_up_gelu_smooth(
+        P, P, P, P, P, P, bias, lam, M, N, 64, 16, fmt, P, None)
+    assert gg(lam=None) == NULL
+    assert gg(lam=MIS) == ALIGN
+    assert gg(bias=MIS) == ALIGN
+    assert gg(N=24) == SHAPE
+    assert gg(N=0, lam=None) == OK
+    need = L.svdq_linear_workspace_bytes(16, 64, 16, 0)
+    lf = lambda lam_in=None, lam_next=None, nbytes=need, ws=P, M=16: L.svdq_linear_folded(
+        P, lam_in, P, P, P, P, None, lam_next, M, 16, 64, 16, 0, ws, nbytes, P, None)
+    assert lf(lam_in=MIS) == ALIGN
+    assert lf(lam_next=MIS) == ALIGN
+    assert lf(nbytes=need - 1) == WORKSPACE
+    assert lf(ws=None) == NULL
+    assert lf(M=0) == OK
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_lib", None)
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
