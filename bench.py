@@ -14,7 +14,8 @@ the same run also times, each on its own seeded layer and with fewer steps:
     per-call time is reported beside them);
   * that MLP pair end to end (fc1, GELU + fc2's smoothing, fc2), with the glue as its own
     kernel and with it (and fc1's input smoothing) folded into fc1's two kernels;
-  * on the QKV layer: the bare W4A4 GEMM (r = 0: no branch in either kernel),
+  * on the QKV layer: the layer with a rank-16 and a rank-32 LoRA adapter carried by its
+    branch (rank 48 and 64, same codes), the bare W4A4 GEMM (r = 0: no branch in either kernel),
     the unfused branch (down projection, quantization, GEMM, up projection as
     separate launches with an fp16 intermediate), and the W4A16 control (fp16
     activations times INT4 group-64 weights, no branch) and the fp16 x fp16
@@ -382,6 +383,35 @@ class Layer:
         return self.time_call(fn, steps, warmup)
 
 
+def time_lora(L, steps, warmup):
+    """The layer with a LoRA adapter of rank 16 and of rank 32 carried by its branch
+    (attach_lora: rank 48 and 64), the residual's codes reused; per-layer time beside the
+    plain rank-32 layer's from the same call."""
+    from bit_w4a4_quantized_amd.prepare import attach_lora
+    torch = L.torch
+    g = np.random.default_rng(5)
+    res = {"r32_us": round(L.time_fused(steps, warmup)["us_per_layer"], 2)}
+    keys = ("l1t", "l2", "t", "wsa")
+    saved = [{k: st[k] for k in keys} for st in L.sets]
+    for ra in (16, 32):
+        a = (g.standard_normal((L.K, ra)) * 0.02).astype(np.float16)
+        b = (g.standard_normal((ra, L.N)) * 0.02).astype(np.float16)
+        hl = attach_lora(L.host, a, b, 1.0)
+        rr = hl.l1t.shape[0]
+        for st in L.sets:
+            st["l1t"] = torch.from_numpy(hl.l1t).cuda()
+            st["l2"] = torch.from_numpy(hl.l2).cuda()
+            st["t"] = torch.empty((L.M, rr), dtype=torch.float16, device="cuda")
+            st["wsa"] = torch.empty(max(16, L.binding.quantize_down_workspace_bytes(L.M, L.K, rr, L.fmt)),
+                                    dtype=torch.uint8, device="cuda")
+        t = L.time_fused(steps, warmup)
+        res[f"r32_plus_lora{ra}_us"] = round(t["us_per_layer"], 2)
+        res[f"r32_plus_lora{ra}_kernels_us"] = {"quantize_down": round(t["ka_us"], 2), "gemm_w4a4_up": round(t["kb_us"], 2)}
+    for st, sv in zip(L.sets, saved):
+        st.update(sv)
+    return res
+
+
 def time_mlp_pair(fc1, fc2, steps, warmup):
     """The MLP pair fc1 -> GELU + fc2's smoothing -> fc2 (the same layers as the fc1 and fc2
     workloads), with the glue as its own kernel (fc1's input smoothed beforehand on the host,
@@ -559,6 +589,8 @@ def main():
             torch.matmul(xr16[i % ROTATE], wt16[i % ROTATE], out=L.sets[i % ROTATE]["y"])
         cmp_["fp16_gemm_hipblaslt_us"] = round(L.time_call(mm, es, ew)["us_per_call"], 2)
         del xr16, wt16
+        if L.r == 32:
+            cmp_["lora_in_branch"] = time_lora(L, es, ew)
         out["comparisons_" + args.workload] = cmp_
         log(f"comparisons: {cmp_}")
         # the other code formats on the same layer shape (their own rank per setting)

@@ -64,6 +64,27 @@ def prepare_host(x_cal: np.ndarray, w: np.ndarray, bias: np.ndarray, r: int) -> 
                      np.asarray(bias, dtype=np.float16))
 
 
+def attach_lora(h: HostLayer, a: np.ndarray, b: np.ndarray, scale: float = 1.0) -> HostLayer:
+    """The layer with a LoRA adapter (delta W = scale A B; A [K, ra], B [ra, N]) in its 16-bit
+    branch ("sota-314", "Known implementations": adapters load without re-quantization).
+    X A B = X_hat diag(lambda) A B, so the branch grows to
+        L1^T' = [L1^T; fp16(diag(lambda) A)^T],   L2' = [L2; fp16(scale B)]
+    (products in float64, one rounding each), zero rows padding the rank to a multiple of 16
+    (the kernels' granularity; a zero row adds exactly 0).  The residual R is unchanged, so
+    its device codes can be reused (with_branch)."""
+    K, ra = a.shape
+    N = h.l2.shape[1]
+    la_t = (h.lam.astype(np.float64)[:, None] * np.asarray(a, np.float64)).astype(np.float16).T
+    lb = (float(scale) * np.asarray(b, np.float64)).astype(np.float16)
+    r = h.l1t.shape[0] + ra
+    pad = (-r) % 16
+    l1t = np.concatenate([h.l1t, la_t, np.zeros((pad, K), np.float16)], axis=0)
+    l2 = np.concatenate([h.l2, lb, np.zeros((pad, N), np.float16)], axis=0)
+    if l1t.shape[0] > 64:
+        raise ValueError(f"branch rank {l1t.shape[0]} exceeds the kernels' 64")
+    return HostLayer(h.lam, np.ascontiguousarray(l1t), np.ascontiguousarray(l2), h.r_t, h.bias)
+
+
 @dataclass
 class DeviceLayer:
     """The prepared layer resident in device memory, ready for svdq_linear."""
@@ -93,3 +114,13 @@ def to_device(h: HostLayer, fmt: str, device="cuda", stream=None) -> DeviceLayer
     lam = torch.from_numpy(h.lam).to(device)
     del r_t
     return DeviceLayer(fmt, K, N, r, l1t, l2, wq, ws, bias, lam)
+
+
+def with_branch(d: DeviceLayer, h: HostLayer, device="cuda") -> DeviceLayer:
+    """The device layer with the branch of host layer h (e.g. after attach_lora): new L1^T and
+    L2 uploads, the residual's codes and scales reused as they are (no re-quantization)."""
+    import torch
+    r = h.l1t.shape[0]
+    l1t = torch.from_numpy(h.l1t).to(device) if r else None
+    l2 = torch.from_numpy(h.l2).to(device) if r else None
+    return DeviceLayer(d.fmt, d.K, d.N, r, l1t, l2, d.wq, d.ws, d.bias, d.lam)

@@ -80,3 +80,24 @@ def prepare_layer(x: np.ndarray, w: np.ndarray, b: np.ndarray, r: int, x_cal: np
     w_hat = smooth_weight(w, lam)
     l1, l2, res, sig = low_rank(w_hat, r, svd)
     return PreparedLayer(lam, x_hat, l1, l2, res, np.asarray(b, np.float16), sig)
+
+
+def lora_branch(l1: np.ndarray, l2: np.ndarray, lam: np.ndarray, a: np.ndarray, b: np.ndarray,
+                scale: float = 1.0):
+    """A LoRA adapter carried by the 16-bit branch (practice page "sota-314", section "Known
+    implementations": the engine loads off-the-shelf adapters without re-quantization).
+
+    The adapted layer is X (W + scale A B) with A [K, ra], B [ra, N].  In smoothed coordinates
+    X = X_hat diag(lambda), so X A B = X_hat (diag(lambda) A) B and the adapter joins the
+    branch:  L1' = [L1, fp16(diag(lambda) A)],  L2' = [L2; fp16(scale B)]  (products in
+    float64, one rounding to fp16 each), zero-padded to a rank that is a multiple of 16 (zero
+    columns / rows add exactly 0).  The residual R and its codes are unchanged.
+    Returns (L1' fp16 [K, r'], L2' fp16 [r', N])."""
+    K, ra = a.shape
+    la = (lam.astype(np.float64)[:, None] * np.asarray(a, np.float64)).astype(np.float16)
+    lb = (float(scale) * np.asarray(b, np.float64)).astype(np.float16)
+    r = l1.shape[1] + ra
+    pad = (-r) % 16
+    l1p = np.concatenate([np.asarray(l1, np.float16), la, np.zeros((K, pad), np.float16)], axis=1)
+    l2p = np.concatenate([np.asarray(l2, np.float16), lb, np.zeros((pad, lb.shape[1]), np.float16)], axis=0)
+    return l1p, l2p

@@ -114,3 +114,28 @@ def test_planted_spectrum_is_steep():
     s = np.linalg.svd(L.w.astype(np.float64), compute_uv=False)
     assert s[5] / s[6] > 3.0
     assert s[6] / s[40] < 2.0
+
+
+@pytest.mark.parametrize("r,ra", [(32, 16), (32, 32), (16, 8), (0, 16)])
+def test_lora_branch_adds_the_adapter_exactly(r, ra):
+    # with power-of-two factors and scale and fp16-exact adapter entries, every product is
+    # exact, so the grown branch must reproduce X_hat L1 L2 + scale X A B exactly (X = X_hat
+    # diag(lambda)); a missing, inverted or misplaced lambda, a transposed factor or a lost
+    # scale changes the sum
+    g = np.random.default_rng(r + ra)
+    M, K, N = 24, 64, 40
+    lam = 2.0 ** g.integers(-3, 4, K).astype(np.float64)
+    x_hat = (g.integers(-64, 65, (M, K)) / 32.0).astype(np.float16)
+    x = x_hat.astype(np.float64) * lam[None, :]
+    l1 = (g.integers(-64, 65, (K, r)) / 64.0).astype(np.float16)
+    l2 = (g.integers(-64, 65, (r, N)) / 64.0).astype(np.float16)
+    a = (g.integers(-32, 33, (K, ra)) / 64.0).astype(np.float16)
+    b = (g.integers(-32, 33, (ra, N)) / 64.0).astype(np.float16)
+    scale = 0.5
+    l1p, l2p = prep.lora_branch(l1, l2, lam.astype(np.float32), a, b, scale)
+    assert l1p.shape == (K, -(-(r + ra) // 16) * 16) and l2p.shape == (l1p.shape[1], N)
+    assert not l1p[:, r + ra:].any() and not l2p[r + ra:].any()
+    got = x_hat.astype(np.float64) @ l1p.astype(np.float64) @ l2p.astype(np.float64)
+    want = x_hat.astype(np.float64) @ l1.astype(np.float64) @ l2.astype(np.float64) \
+        + scale * (x @ a.astype(np.float64) @ b.astype(np.float64))
+    assert np.array_equal(got, want)

@@ -24,3 +24,19 @@ def test_product_prep_equals_oracle_prep(shape):
     assert np.array_equal(h.l1t.T.view(np.uint16), o.l1.view(np.uint16))
     assert np.array_equal(h.l2.view(np.uint16), o.l2.view(np.uint16))
     assert np.array_equal(h.r_t.T.view(np.uint32), o.res.view(np.uint32))
+
+
+@pytest.mark.parametrize("ra", [16, 32, 8])
+def test_product_lora_equals_oracle_lora(ra):
+    from bit_w4a4_quantized_amd.prepare import attach_lora
+    shape = LayerShape("a", 128, 256, 256, 32, "int4", 1000, 8)
+    raw = draw_layer(shape)
+    h = prepare_host(raw.x, raw.w, raw.b, shape.r)
+    g = np.random.default_rng(ra)
+    a = (g.standard_normal((256, ra)) * 0.05).astype(np.float16)
+    b = (g.standard_normal((ra, 256)) * 0.05).astype(np.float16)
+    hl = attach_lora(h, a, b, 0.75)
+    l1p, l2p = prep.lora_branch(h.l1t.T, h.l2, h.lam, a, b, 0.75)
+    assert np.array_equal(hl.l1t.T.view(np.uint16), l1p.view(np.uint16))
+    assert np.array_equal(hl.l2.view(np.uint16), l2p.view(np.uint16))
+    assert hl.r_t is h.r_t                   # the residual (and so its codes) is untouched
