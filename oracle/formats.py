@@ -86,3 +86,9 @@ def e2m1_encode(t) -> np.ndarray:
     idx = np.where(pref.any(axis=-1), np.argmax(pref, axis=-1), np.argmax(cand, axis=-1))
     neg = (t < 0) & (idx != 0)
     return (idx | np.where(neg, 8, 0)).astype(np.uint8)
+
+
+def e8m0_decode(b) -> np.ndarray:
+    """E8M0 scale byte (OCP Microscaling Formats v1.0: an 8-bit biased exponent, no sign or
+    mantissa) -> 2^(b - 127) as float64; 255 (NaN) is never produced here."""
+    return np.ldexp(1.0, np.asarray(b, dtype=np.int64) - 127)

@@ -18,6 +18,16 @@ FP4 (E2M1 codes, group 16, E4M3 scales):
     s8  = e4m3_rne_sat( fp32(a) / 6.0f ),  s = float(s8)
     q_k = 0 if s == 0 else e2m1_nearest_even( fp32(v_k) / s )
 
+MXFP4 (E2M1 codes, group 32, E8M0 scales; OCP Microscaling Formats v1.0, the
+format gfx950's block-scaled matrix cores take natively; practice page "sota-314",
+section "Conditions": which format wins is a property of the hardware's native
+group support):
+    e   = floor(log2 a) - 2  (2 = the exponent of E2M1's largest value, 6 = 1.5 * 2^2),
+          clamped to [-127, 127]; e = -127 for a = 0
+    b8  = e + 127 (the E8M0 byte), X = 2^e
+    q_k = e2m1_nearest_even( fp32(v_k) / X )  (exact: X is a power of two), saturating
+          at 6: a group's largest values in (6 X, 8 X) become 6 X
+
 Packing of 4-bit codes: two per byte along K, byte b holds code 2b in its low
 nibble and code 2b+1 in its high nibble.  INT4 nibbles are two's complement;
 E2M1 nibbles are sign<<3 | magnitude index.  INT8 codes are one int8 per byte.
@@ -26,7 +36,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import e2m1_encode, e2m1_decode, e4m3_encode_rne_sat, e4m3_decode
+from .formats import e2m1_encode, e2m1_decode, e4m3_encode_rne_sat, e4m3_decode, e8m0_decode
 
 INT4_QMAX = 7
 INT8_QMAX = 127
@@ -68,6 +78,26 @@ def quantize_fp4(v: np.ndarray, G: int = 16):
     t = np.where(s[..., None] == 0, 0.0, t)
     codes = e2m1_encode(t.astype(np.float64))
     return codes.reshape(v32.shape).astype(np.uint8), s8
+
+
+def quantize_mx(v: np.ndarray, G: int = 32):
+    """MXFP4: E2M1 codes with E8M0 group scales.  Returns (codes uint8 nibbles [rows, K],
+    scales uint8 [rows, K/G])."""
+    v32 = np.asarray(v).astype(np.float32)
+    g = _groups(v32, G).astype(np.float64)
+    a = np.abs(g).max(axis=-1)
+    _, ex = np.frexp(a)                          # a = m 2^ex with m in [0.5, 1): floor(log2 a) = ex - 1
+    e = np.where(a > 0, ex - 1 - 2, -127)
+    e = np.clip(e, -127, 127)
+    t = np.ldexp(g, -e[..., None])               # v / 2^e, exact
+    codes = e2m1_encode(t)
+    return codes.reshape(v32.shape).astype(np.uint8), (e + 127).astype(np.uint8)
+
+
+def dequant_mx(codes: np.ndarray, scales8: np.ndarray, G: int = 32) -> np.ndarray:
+    q = e2m1_decode(codes)
+    s = e8m0_decode(scales8)
+    return (q.reshape(q.shape[0], -1, G) * s[..., None]).reshape(q.shape)
 
 
 def pack_nibbles(codes: np.ndarray) -> np.ndarray:
@@ -138,6 +168,7 @@ FORMATS = {
     "int8": (64, 8, "fp16"),
     "fp4": (16, 4, "e4m3"),
     "int4_e2m3": (64, 6, "fp16"),   # INT4 codes in a 6-bit container
+    "mxfp4": (32, 4, "e8m0"),
 }
 
 
@@ -159,6 +190,9 @@ def quantize(v: np.ndarray, fmt: str):
     if fmt == "fp4":
         q, s = quantize_fp4(v, 16)
         return q, s, pack_nibbles(q)
+    if fmt == "mxfp4":
+        q, s = quantize_mx(v, 32)
+        return q, s, pack_nibbles(q)
     raise ValueError(fmt)
 
 
@@ -167,4 +201,6 @@ def dequantize(codes, scales, fmt: str) -> np.ndarray:
         return dequant_int(codes, scales, 64)
     if fmt == "fp4":
         return dequant_fp4(codes, scales, 16)
+    if fmt == "mxfp4":
+        return dequant_mx(codes, scales, 32)
     raise ValueError(fmt)
