@@ -595,7 +595,7 @@ def main():
         log(f"comparisons: {cmp_}")
         # the other code formats on the same layer shape (their own rank per setting)
         variants = {}
-        for vfmt, vr in (("int8", 16), ("fp4", 32), ("int4", 32)):
+        for vfmt, vr in (("int8", 16), ("fp4", 32), ("int4", 32), ("mxfp4", 32)):
             Lv = Layer(torch, binding, args.workload, vfmt, vr)
             res = Lv.time_fused(es, ew)
             v_b = ops + 2.0 * M * vr * N

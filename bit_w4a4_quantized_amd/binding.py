@@ -16,8 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # SVDQ_LIBRARY may name another build of the same library (same ABI), e.g. a tuning variant.
 LIB_PATH = os.environ.get("SVDQ_LIBRARY") or os.path.join(HERE, "libsvdq.so")
 
-FORMATS = {"int4": 0, "int8": 1, "fp4": 2, "int4_e2m3": 3}
-GROUP = {"int4": 64, "int8": 64, "fp4": 16, "int4_e2m3": 64}
+FORMATS = {"int4": 0, "int8": 1, "fp4": 2, "int4_e2m3": 3, "mxfp4": 4}
+GROUP = {"int4": 64, "int8": 64, "fp4": 16, "int4_e2m3": 64, "mxfp4": 32}
 FMT_NAMES = {v: k for k, v in FORMATS.items()}
 
 _lib = None
@@ -117,10 +117,14 @@ def code_row_bytes(K: int, fmt) -> int:
 
 
 def code_shape(rows: int, K: int, fmt):
-    """Shape of a code tensor: [rows, row bytes], or group-major [K/64, rows, 48] for the
-    E2M3 container."""
+    """Shape of a code tensor: [rows, row bytes], group-major [K/64, rows, 48] for the E2M3
+    container, chunk-major [K/64, rows, 32] for MXFP4."""
     name = fmt if isinstance(fmt, str) else FMT_NAMES[int(fmt)]
-    return (K // 64, rows, 48) if name == "int4_e2m3" else (rows, code_row_bytes(K, fmt))
+    if name == "int4_e2m3":
+        return (K // 64, rows, 48)
+    if name == "mxfp4":
+        return (K // 64, rows, 32)
+    return (rows, code_row_bytes(K, fmt))
 
 
 def code_rows(q) -> int:
@@ -134,14 +138,19 @@ def scale_row_entries(K: int, fmt) -> int:
 
 
 def scale_shape(rows: int, K: int, fmt):
-    """Shape of the scale tensor: [rows, K/G], or group-major [K/64, rows] for the E2M3 container."""
+    """Shape of the scale tensor: [rows, K/G], group-major [K/64, rows] for the E2M3 container,
+    chunk-major [K/64, rows, 2] for MXFP4."""
     name = fmt if isinstance(fmt, str) else FMT_NAMES[int(fmt)]
-    return (K // 64, rows) if name == "int4_e2m3" else (rows, K // GROUP[name])
+    if name == "int4_e2m3":
+        return (K // 64, rows)
+    if name == "mxfp4":
+        return (K // 64, rows, 2)
+    return (rows, K // GROUP[name])
 
 
 def scale_dtype(fmt):
     import torch
-    return torch.uint8 if _fmt(fmt) == 2 else torch.float16
+    return torch.uint8 if _fmt(fmt) in (2, 4) else torch.float16   # E4M3 / E8M0 bytes
 
 
 def linear_workspace_bytes(M: int, K: int, r: int, fmt) -> int:

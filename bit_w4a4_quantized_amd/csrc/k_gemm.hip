@@ -19,6 +19,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     case FMT_INT4_E2M3: return launch_gemm3(a, s);
     case FMT_INT8: return launch_gemm_i8(a, s);
     case FMT_FP4: return launch_gemm_f4(a, s);
+    case FMT_MXFP4: return launch_gemm_mx(a, s);
   }
   return hipErrorInvalidValue;
 }

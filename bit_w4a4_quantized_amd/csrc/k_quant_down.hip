@@ -75,7 +75,7 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
   constexpr int RBX = RB > 0 ? RB : 1;
   constexpr int ROWS = 16 * NRT;
   constexpr int CB = chunk_code_bytes<FMT>();
-  constexpr bool STAGE = QUANT && FMT != FMT_FP4;          // codes go out through LDS
+  constexpr bool STAGE = QUANT && FMT != FMT_FP4 && FMT != FMT_MXFP4;   // codes go out through LDS
   constexpr int RP = R + 4;                                 // padded row of the partial sums
   constexpr int SMEM = cmax(cmax(STAGE ? 4 * ROWS * CB : 0, RB > 0 ? 4 * ROWS * RP * 4 : 0), 16);
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
@@ -250,6 +250,35 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
               *reinterpret_cast<uint16_t*>(srow + pos) = piece;
             }
           }
+        }
+      }
+    } else if (FMT == FMT_MXFP4) {  // MXFP4: groups of 32 = the row's four lanes x 8 values, per half
+#pragma unroll
+      for (int rt = 0; rt < NRT; rt++) {
+        float v[16];
+        unpack_h8(B.x[rt][0], v);
+        unpack_h8(B.x[rt][1], v + 8);
+        const int m = m0 + rt * 16 + row;
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) { a0 = fmaxf(a0, fabsf(v[e])); a1 = fmaxf(a1, fabsf(v[8 + e])); }
+        a0 = fmaxf(a0, __shfl_xor(a0, 16));
+        a0 = fmaxf(a0, __shfl_xor(a0, 32));
+        a1 = fmaxf(a1, __shfl_xor(a1, 16));
+        a1 = fmaxf(a1, __shfl_xor(a1, 32));
+        const int e0 = mx_exponent(a0), e1 = mx_exponent(a1);
+        int q[16];
+#pragma unroll
+        for (int e = 0; e < 8; e++) {            // v / 2^e is exact
+          q[e] = (int)fp4_code_q(ldexpf(v[e], -e0));
+          q[8 + e] = (int)fp4_code_q(ldexpf(v[8 + e], -e1));
+        }
+        if (m < M) {                             // chunk-major: the chunk's 32 bytes of row m
+          uint8_t* dst = xq + ((size_t)c * M + m) * 32;
+          *reinterpret_cast<uint32_t*>(dst + 4 * sub) = pack8(q);
+          *reinterpret_cast<uint32_t*>(dst + 16 + 4 * sub) = pack8(q + 8);
+          if (sub == 0)                          // the row's two E8M0 bytes of this chunk
+            *reinterpret_cast<uint16_t*>(xs + ((size_t)c * M + m) * 2) = (uint16_t)((e0 + 127) | ((e1 + 127) << 8));
         }
       }
     } else {  // FP4: groups of 16 = two lanes (sub, sub^1) x 8 values
@@ -460,6 +489,7 @@ static hipError_t launch_quant_down_s(const QuantDownArgs& a, hipStream_t s) {
     case FMT_INT4_E2M3: return launch_qd_r<FMT_INT4_E2M3, true, SMOOTH>(a, s);
     case FMT_INT8: return launch_qd_r<FMT_INT8, true, SMOOTH>(a, s);
     case FMT_FP4: return launch_qd_r<FMT_FP4, true, SMOOTH>(a, s);
+    case FMT_MXFP4: return launch_qd_r<FMT_MXFP4, true, SMOOTH>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -12,7 +12,7 @@ template <int FMT>
 __global__ void __launch_bounds__(256)
 k_quant_weight(const float* __restrict__ r_t, int N, int K, uint8_t* __restrict__ wq,
                uint8_t* __restrict__ ws) {
-  constexpr int G = FMT == FMT_FP4 ? 16 : 64;
+  constexpr int G = FMT == FMT_FP4 ? 16 : (FMT == FMT_MXFP4 ? 32 : 64);
   const int gpr = K / G;
   const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (size_t)N * gpr) return;
@@ -67,6 +67,18 @@ k_quant_weight(const float* __restrict__ r_t, int N, int K, uint8_t* __restrict_
 #pragma unroll
       for (int e = 0; e < G; e += 4) dst[e >> 2] = pack4_i8(q + e);
     }
+  } else if (FMT == FMT_MXFP4) {
+    // chunk-major: group g is half g % 2 of 64-K chunk g / 2; codes [K/64][N][32 bytes],
+    // E8M0 bytes [K/64][N][2]
+    const int ex = mx_exponent(amax);
+    const size_t cn = (size_t)(g >> 1) * N + n;
+    ws[cn * 2 + (g & 1)] = (uint8_t)(ex + 127);
+    int q[G];
+#pragma unroll
+    for (int e = 0; e < G; e++) q[e] = (int)fp4_code_q(ldexpf(v[e], -ex));   // v / 2^ex, exact
+    uint32_t* dst = reinterpret_cast<uint32_t*>(wq + cn * 32 + (g & 1) * 16);
+#pragma unroll
+    for (int e = 0; e < G; e += 8) dst[e >> 3] = pack8(q + e);
   } else {
     uint32_t b;
     const float s = fp4_scale(amax, &b);
@@ -81,7 +93,7 @@ k_quant_weight(const float* __restrict__ r_t, int N, int K, uint8_t* __restrict_
 }
 
 hipError_t launch_quant_weight(const float* r_t, int N, int K, int fmt, void* wq, void* ws, hipStream_t s) {
-  const int G = fmt == FMT_FP4 ? 16 : 64;
+  const int G = fmt == FMT_FP4 ? 16 : (fmt == FMT_MXFP4 ? 32 : 64);
   const size_t groups = (size_t)N * (K / G);
   dim3 grid((unsigned)((groups + 255) / 256));
   switch (fmt) {
@@ -96,6 +108,9 @@ hipError_t launch_quant_weight(const float* r_t, int N, int K, int fmt, void* wq
       break;
     case FMT_FP4:
       hipLaunchKernelGGL(k_quant_weight<FMT_FP4>, grid, dim3(256), 0, s, r_t, N, K, (uint8_t*)wq, (uint8_t*)ws);
+      break;
+    case FMT_MXFP4:
+      hipLaunchKernelGGL(k_quant_weight<FMT_MXFP4>, grid, dim3(256), 0, s, r_t, N, K, (uint8_t*)wq, (uint8_t*)ws);
       break;
     default:
       return hipErrorInvalidValue;

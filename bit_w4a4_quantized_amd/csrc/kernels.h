@@ -8,7 +8,7 @@
 
 namespace svdq {
 
-enum Fmt { FMT_INT4 = 0, FMT_INT8 = 1, FMT_FP4 = 2, FMT_INT4_E2M3 = 3 };
+enum Fmt { FMT_INT4 = 0, FMT_INT8 = 1, FMT_FP4 = 2, FMT_INT4_E2M3 = 3, FMT_MXFP4 = 4 };
 enum Core { CORE_E2M3 = 0, CORE_I4 = 1 };
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -109,6 +109,7 @@ hipError_t launch_gemm2(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm3(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_i8(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_f4(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t s);
 hipError_t launch_quant_weight(const float* r_t, int N, int K, int fmt, void* wq, void* ws, hipStream_t s);
 
 // unfused comparison pieces

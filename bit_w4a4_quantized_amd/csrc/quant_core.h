@@ -142,6 +142,16 @@ __device__ __forceinline__ uint32_t fp4_code_q(float t) {
   return (t < 0.0f && idx != 0u) ? (idx | 8u) : idx;
 }
 
+// MXFP4 shared exponent of a group (OCP Microscaling Formats v1.0): e = floor(log2 amax) - 2
+// (2: the exponent of E2M1's largest value 6 = 1.5 * 2^2), clamped to [-127, 127]; -127 for
+// amax = 0.  v_frexp_exp gives amax = m 2^x with m in [0.5, 1), subnormals included, so
+// floor(log2 amax) = x - 1.  The E8M0 byte is e + 127; codes are fp4_code_q(v * 2^-e) (exact).
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (amax == 0.0f) return -127;
+  const int e = __builtin_amdgcn_frexp_expf(amax) - 1 - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
 // Pack 8 4-bit codes (low nibble first) into one 32-bit word.
 __device__ __forceinline__ uint32_t pack8(const int* q) {
   uint32_t w = 0;

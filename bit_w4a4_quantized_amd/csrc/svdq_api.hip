@@ -14,7 +14,8 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 inline bool fmt_ok(int f) {
-  return f == SVDQ_INT4_G64 || f == SVDQ_INT8_G64 || f == SVDQ_FP4_G16 || f == SVDQ_INT4_G64_E2M3;
+  return f == SVDQ_INT4_G64 || f == SVDQ_INT8_G64 || f == SVDQ_FP4_G16 || f == SVDQ_INT4_G64_E2M3 ||
+         f == SVDQ_MXFP4_G32;
 }
 
 inline size_t code_bytes(int K, int fmt) {
@@ -23,7 +24,7 @@ inline size_t code_bytes(int K, int fmt) {
   return (size_t)K / 2;
 }
 inline size_t scale_bytes(int K, int fmt) {
-  return fmt == SVDQ_FP4_G16 ? (size_t)K / 16 : (size_t)K / 64 * 2;
+  return fmt == SVDQ_FP4_G16 ? (size_t)K / 16 : (fmt == SVDQ_MXFP4_G32 ? (size_t)K / 32 : (size_t)K / 64 * 2);
 }
 
 svdq_status check_dims(int M, int N, int K, int r) {

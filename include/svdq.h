@@ -69,6 +69,21 @@
  *                  so that the GEMM runs on the FP6 matrix cores, which return
  *                  fp32 partials and, measured on MI355X, do 1.57x the INT8
  *                  instruction's work per K element.
+ *  SVDQ_MXFP4_G32 : MXFP4 (OCP Microscaling Formats v1.0), the block-scaled
+ *                  format gfx950's matrix cores apply natively ("sota-314",
+ *                  "Conditions": the format ranking follows the hardware's
+ *                  native group support; "Quantization", "KV cache
+ *                  quantization": OCP MXFP4 among the production formats).
+ *                  E2M1 codes packed as SVDQ_FP4_G16, one E8M0 byte per 32
+ *                  along K: e = floor(log2 absmax) - 2 clamped to [-127, 127]
+ *                  (-127 for an all-zero group), byte = e + 127; code =
+ *                  nearest E2M1 to v / 2^e (exact division), ties to the even
+ *                  mantissa, saturating at 6, -0 -> +0.  Codes and scales are
+ *                  chunk-major, so that a tile's rows of one 64-wide chunk of K
+ *                  are contiguous: codes [K/64][rows][32 bytes] (chunk c of
+ *                  row i at byte (c * rows + i) * 32; within it the two 16-byte
+ *                  halves are the groups, two codes per byte as SVDQ_FP4_G16),
+ *                  E8M0 bytes [K/64][rows][2].
  */
 #ifndef SVDQ_H
 #define SVDQ_H
@@ -95,7 +110,8 @@ typedef enum {
   SVDQ_INT4_G64 = 0,
   SVDQ_INT8_G64 = 1,
   SVDQ_FP4_G16 = 2,
-  SVDQ_INT4_G64_E2M3 = 3
+  SVDQ_INT4_G64_E2M3 = 3,
+  SVDQ_MXFP4_G32 = 4
 } svdq_format;
 
 /* Bytes of codes per row for K columns (K/2 for 4-bit formats, K for INT8,

@@ -103,9 +103,10 @@ def gemm_terms(fmt, K, r):
     """Terms of the fp32 sum behind one output of Kernel B, for within_sum_bound: per-group
     partials P_g (exact) times sx sw for the INT formats; for FP4 the kernel multiplies the
     exactly dequantized values and sums all K products directly (the same exact terms,
-    regrouped), so its fp32 sum has K terms.  Plus r branch terms, the bias and the final
+    regrouped), so its fp32 sum has K terms; MXFP4's block-scaled matrix instruction forms
+    the same exact products, counted the same way.  Plus r branch terms, the bias and the final
     rounding."""
-    return (K if fmt == "fp4" else K // 64) + r + 2
+    return (K if fmt in ("fp4", "mxfp4") else K // 64) + r + 2
 
 
 def w4a16_bound_terms(x, q, s, bias):

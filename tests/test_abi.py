@@ -45,6 +45,8 @@ def test_sizes():
     L = binding.lib()
     assert L.svdq_scale_row_bytes(3072, 0) == 96
     assert L.svdq_scale_row_bytes(3072, 2) == 192
+    assert L.svdq_scale_row_bytes(3072, 4) == 96           # MXFP4: one E8M0 byte per 32
+    assert L.svdq_code_row_bytes(3072, 4) == 1536
     assert L.svdq_code_row_bytes(100, 0) == 0
     assert L.svdq_code_row_bytes(64, 7) == 0
     # codes + scales + T + Kernel A's partial sums, each 256-byte aligned
@@ -84,7 +86,7 @@ def test_quantize_down_validation():
     assert qd(M=-1) == SHAPE
     assert qd(r=8) == SHAPE
     assert qd(r=80) == SHAPE
-    assert qd(fmt=4) == FORMAT
+    assert qd(fmt=5) == FORMAT
     assert qd(x=MIS) == ALIGN
     assert qd(t=MIS) == ALIGN
     assert qd(M=0) == OK            # empty input: nothing enqueued

@@ -46,7 +46,10 @@ def dev_codes(stored, fmt):
     """Codes in the device layout of the format.  The E2M3 container is group-major
     [K/64][rows][48] with the bytes of a group ordered half 0 [0:16], half 1 [0:16],
     half 0 [16:24], half 1 [16:24]; the oracle stores it row by row, each half's 24 bytes
-    contiguous."""
+    contiguous.  MXFP4 is chunk-major [K/64][rows][32] (the oracle: packed rows)."""
+    if fmt == "mxfp4":
+        rows = stored.shape[0]
+        return np.ascontiguousarray(stored.reshape(rows, -1, 32).transpose(1, 0, 2))
     if fmt != "int4_e2m3":
         return stored
     rows = stored.shape[0]
@@ -56,11 +59,14 @@ def dev_codes(stored, fmt):
 
 
 def dev_scales(s, fmt):
-    """Scales in the device layout of the format (group-major for the E2M3 container)."""
+    """Scales in the device layout of the format (group-major for the E2M3 container,
+    chunk-major [K/64][rows][2] for MXFP4)."""
+    if fmt == "mxfp4":
+        return np.ascontiguousarray(s.reshape(s.shape[0], -1, 2).transpose(1, 0, 2))
     return np.ascontiguousarray(s.T) if fmt == "int4_e2m3" else s
 
 
-FMTS = ["int4", "int8", "fp4", "int4_e2m3"]
+FMTS = ["int4", "int8", "fp4", "int4_e2m3", "mxfp4"]
 
 
 def draw(seed, M, K, N, r, xscale=0.7, rscale=0.05):
@@ -291,7 +297,7 @@ def test_repeat_runs_are_bitwise_identical(fmt):
         assert np.array_equal(host(binding.svdq_linear(*args)).view(np.uint16), first.view(np.uint16))
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int4_e2m3"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_outputs_stay_inside_their_buffers(fmt):
     M, K, N, r = 130, 192, 48, 32
     x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs(fmt, M, K, N, r, 12)
@@ -305,7 +311,8 @@ def test_outputs_stay_inside_their_buffers(fmt):
 
     cb = binding.code_row_bytes(K, fmt)
     bq, gq = guarded(M * cb, torch.uint8, binding.code_shape(M, K, fmt))
-    bs, gs = guarded(M * K // 64 * 2, torch.float16, binding.scale_shape(M, K, fmt))
+    sb = binding.lib().svdq_scale_row_bytes(K, binding.FORMATS[fmt])
+    bs, gs = guarded(M * sb, binding.scale_dtype(fmt), binding.scale_shape(M, K, fmt))
     bt, gt = guarded(M * r * 2, torch.float16, (M, r))
     binding.svdq_quantize_down(dev(x_hat), dev(l1.T), fmt, xq=gq, xs=gs, t=gt)
     by, gy = guarded(M * N * 2, torch.float16, (M, N))
