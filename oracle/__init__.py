@@ -15,9 +15,10 @@ Modules:
   forward  -- the layer: down projection, low-bit GEMM, up projection, bias;
               the W4A16 control; the GELU(tanh) + smoothing glue
   brute    -- independent float64 loops of the per-group integer form (tiny shapes)
+  gptq     -- GPTQ rounding of the residual (error compensation over the Hessian of X_hat)
 
 Every function is pinned by a CPU test against something other than itself
 (closed forms, worked special cases, library routines, exhaustive tables or
 brute force); none is "parity unpinned".
 """
-from . import formats, quant, prep, forward, brute  # noqa: F401
+from . import formats, quant, prep, forward, brute, gptq  # noqa: F401
