@@ -33,6 +33,7 @@ _SIGS = {
     "svdq_linear_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "svdq_linear": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _c_size, _vp, _vp]),
     "svdq_quantize_weight": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "svdq_pack_weight": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "svdq_linear_unfused_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "svdq_linear_unfused": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _c_size, _vp, _vp]),
     "svdq_gemm_w4a16": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
@@ -237,6 +238,22 @@ def svdq_quantize_weight(r_t, fmt, wq=None, ws=None, stream=None):
         ws = torch.empty(scale_shape(N, K, fmt), dtype=scale_dtype(fmt), device=r_t.device)
     _check("svdq_quantize_weight", lib().svdq_quantize_weight(
         _p(r_t), N, K, _fmt(fmt), _p(wq), _p(ws), _stream(stream)))
+    return wq, ws
+
+
+def svdq_pack_weight(codes, scales, fmt, wq=None, ws=None, stream=None):
+    """Codes int8 [N, K] and fp16 scales [N, K/64] computed elsewhere (e.g. GPTQ) -> (wq, ws) in
+    the layouts Kernel B reads (INT formats)."""
+    import torch
+    N, K = codes.shape
+    _need(codes, torch.int8, None, "codes")
+    _need(scales, torch.float16, (N, K // 64), "scales")
+    if wq is None:
+        wq = torch.empty(code_shape(N, K, fmt), dtype=torch.uint8, device=codes.device)
+    if ws is None:
+        ws = torch.empty(scale_shape(N, K, fmt), dtype=scale_dtype(fmt), device=codes.device)
+    _check("svdq_pack_weight", lib().svdq_pack_weight(_p(codes), _p(scales), N, K, _fmt(fmt), _p(wq), _p(ws),
+                                                      _stream(stream)))
     return wq, ws
 
 

@@ -111,6 +111,8 @@ hipError_t launch_gemm_i8(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_f4(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t s);
 hipError_t launch_quant_weight(const float* r_t, int N, int K, int fmt, void* wq, void* ws, hipStream_t s);
+hipError_t launch_pack_weight(const int8_t* codes, const uint16_t* scales, int N, int K, int fmt, void* wq,
+                              void* ws, hipStream_t s);
 
 // unfused comparison pieces
 hipError_t launch_quant_only(const void* x, int M, int K, int fmt, void* xq, void* xs, hipStream_t s);

@@ -225,6 +225,18 @@ svdq_status svdq_linear_folded(const void* x, const float* lambda_in, const void
   return map_launch(launch_gemm(ga, s));
 }
 
+svdq_status svdq_pack_weight(const int8_t* codes, const void* scales, int N, int K, svdq_format fmt, void* wq,
+                             void* ws, void* stream) {
+  if (!fmt_ok(fmt)) return SVDQ_ERR_FORMAT;
+  if (fmt != SVDQ_INT4_G64 && fmt != SVDQ_INT4_G64_E2M3 && fmt != SVDQ_INT8_G64) return SVDQ_ERR_FORMAT;
+  if (N < 0 || K <= 0 || K % 64 != 0 || N % 16 != 0 || N > kMaxDim || K > kMaxDim) return SVDQ_ERR_SHAPE;
+  if (N == 0) return SVDQ_OK;
+  if (!codes || !scales || !wq || !ws) return SVDQ_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(wq) || !aligned16(ws)) return SVDQ_ERR_ALIGN;
+  return map_launch(launch_pack_weight(codes, static_cast<const uint16_t*>(scales), N, K, (int)fmt, wq, ws,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 svdq_status svdq_quantize_weight(const float* r_t, int N, int K, svdq_format fmt, void* wq, void* ws,
                                  void* stream) {
   if (!fmt_ok(fmt)) return SVDQ_ERR_FORMAT;

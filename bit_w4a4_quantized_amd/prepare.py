@@ -85,6 +85,45 @@ def attach_lora(h: HostLayer, a: np.ndarray, b: np.ndarray, scale: float = 1.0) 
     return HostLayer(h.lam, np.ascontiguousarray(l1t), np.ascontiguousarray(l2), h.r_t, h.bias)
 
 
+def gptq_residual(h: HostLayer, x_cal_hat: np.ndarray, fmt: str, damp: float = 0.01):
+    """GPTQ codes of the residual ("sota-314", "Do this": the residual weights are quantized
+    with GPTQ rather than round-to-nearest; Frantar et al. 2022, "GPTQ", Algorithm 1, without
+    its lazy batching, which only regroups the same updates).  x_cal_hat: smoothed calibration
+    activations [M, K] (the inputs R multiplies).  Each input channel in turn is rounded with
+    the round-to-nearest rule (fp16 group scale from the group's current weights at its first
+    channel) and its error moved onto the channels not yet rounded through the upper
+    Cholesky factor of the damped inverse Hessian of 2 X^T X (float64).  INT formats only.
+    Returns (codes int8 [N, K], scales fp16 [N, K/64]) for svdq_pack_weight."""
+    if fmt not in ("int4", "int4_e2m3", "int8"):
+        raise ValueError(f"GPTQ codes are produced for the INT formats, not {fmt}")
+    qmax = np.float32(127.0 if fmt == "int8" else 7.0)
+    w = np.asarray(h.r_t, dtype=np.float64).copy()       # [N, K]
+    x = np.asarray(x_cal_hat, dtype=np.float64)
+    hess = 2.0 * x.T @ x
+    K = hess.shape[0]
+    idle = np.diag(hess) == 0                             # channels never active: weight 0
+    hess[idle, idle] = 1.0
+    w[:, idle] = 0.0
+    hess[np.diag_indices(K)] += damp * np.mean(np.diag(hess))
+    chol_u = np.linalg.cholesky(np.linalg.inv(hess)).T   # H^-1 = U^T U, U upper
+    codes = np.zeros(w.shape, np.int8)
+    scales = np.zeros((w.shape[0], K // 64), np.float16)
+    for j in range(K):
+        grp = j // 64
+        if j % 64 == 0:
+            amax = np.abs(w[:, j:j + 64].astype(np.float32)).max(axis=1)
+            scales[:, grp] = (amax / qmax).astype(np.float32).astype(np.float16)
+        s32 = scales[:, grp].astype(np.float32)
+        col = w[:, j].astype(np.float32)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            quot = np.where(s32 == 0, np.float32(0.0), col / s32)
+        q = np.clip(np.rint(quot), -qmax, qmax).astype(np.int8)
+        codes[:, j] = q
+        err = (w[:, j] - q.astype(np.float64) * s32.astype(np.float64)) / chol_u[j, j]
+        w[:, j + 1:] -= np.outer(err, chol_u[j, j + 1:])
+    return codes, scales
+
+
 @dataclass
 class DeviceLayer:
     """The prepared layer resident in device memory, ready for svdq_linear."""
@@ -114,6 +153,22 @@ def to_device(h: HostLayer, fmt: str, device="cuda", stream=None) -> DeviceLayer
     lam = torch.from_numpy(h.lam).to(device)
     del r_t
     return DeviceLayer(fmt, K, N, r, l1t, l2, wq, ws, bias, lam)
+
+
+def to_device_packed(h: HostLayer, fmt: str, codes: np.ndarray, scales: np.ndarray, device="cuda",
+                     stream=None) -> DeviceLayer:
+    """Upload the host layer with residual codes computed on the host (e.g. gptq_residual),
+    packed into Kernel B's layout by svdq_pack_weight."""
+    import torch
+    from .binding import svdq_pack_weight
+    r = h.l1t.shape[0]
+    N, K = h.r_t.shape
+    wq, ws = svdq_pack_weight(torch.from_numpy(np.ascontiguousarray(codes)).to(device),
+                              torch.from_numpy(np.ascontiguousarray(scales)).to(device), fmt, stream=stream)
+    l1t = torch.from_numpy(h.l1t).to(device) if r else None
+    l2 = torch.from_numpy(h.l2).to(device) if r else None
+    return DeviceLayer(fmt, K, N, r, l1t, l2, wq, ws, torch.from_numpy(h.bias).to(device),
+                       torch.from_numpy(h.lam).to(device))
 
 
 def with_branch(d: DeviceLayer, h: HostLayer, device="cuda") -> DeviceLayer:

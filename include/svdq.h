@@ -193,6 +193,22 @@ svdq_status svdq_linear(const void* x_hat, const void* l1t, const void* wq, cons
 svdq_status svdq_quantize_weight(const float* r_t, int N, int K, svdq_format fmt, void* wq,
                                  void* ws, void* stream);
 
+/*
+ * Codes and scales of the residual computed elsewhere -- e.g. GPTQ on the host
+ * ("sota-314", "Do this": the residual weights are quantized with GPTQ rather
+ * than round-to-nearest) -- put into the layouts Kernel B reads, for the INT
+ * formats (SVDQ_INT4_G64, SVDQ_INT4_G64_E2M3, SVDQ_INT8_G64; others are
+ * SVDQ_ERR_FORMAT):
+ *   codes  : int8 [N, K], one code per byte (in [-7, 7] or [-127, 127]; not
+ *            checked), K contiguous per output column.
+ *   scales : fp16 [N, K/64].
+ *   wq, ws : out, as svdq_quantize_weight writes them.
+ * With round-to-nearest codes and scales this reproduces svdq_quantize_weight
+ * bit for bit.  Pointers 16-byte aligned; N % 16 == 0, K % 64 == 0.
+ */
+svdq_status svdq_pack_weight(const int8_t* codes, const void* scales, int N, int K, svdq_format fmt,
+                             void* wq, void* ws, void* stream);
+
 /* Workspace of the unfused comparison: svdq_linear's workspace plus an fp16
  * [M, N] intermediate, 256-byte aligned. */
 size_t svdq_linear_unfused_workspace_bytes(int M, int N, int K, int r, svdq_format fmt);

@@ -184,3 +184,15 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         binding.lib()
+
+
+def test_pack_weight_validation():
+    L = binding.lib()
+    pk = lambda c=P, s=P, N=16, K=64, fmt=0, wq=P: L.svdq_pack_weight(c, s, N, K, fmt, wq, P, None)
+    assert pk(fmt=2) == FORMAT                 # FP4 and MXFP4 codes are not packed from ints
+    assert pk(fmt=4) == FORMAT
+    assert pk(c=None) == NULL
+    assert pk(K=96) == SHAPE
+    assert pk(N=24) == SHAPE
+    assert pk(wq=MIS) == ALIGN
+    assert pk(N=0) == OK

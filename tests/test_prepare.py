@@ -40,3 +40,17 @@ def test_product_lora_equals_oracle_lora(ra):
     assert np.array_equal(hl.l1t.T.view(np.uint16), l1p.view(np.uint16))
     assert np.array_equal(hl.l2.view(np.uint16), l2p.view(np.uint16))
     assert hl.r_t is h.r_t                   # the residual (and so its codes) is untouched
+
+
+@pytest.mark.parametrize("fmt", ["int4", "int8"])
+def test_product_gptq_equals_oracle_gptq(fmt):
+    from bit_w4a4_quantized_amd.prepare import gptq_residual
+    from oracle import gptq
+    shape = LayerShape("g", 256, 192, 96, 16, fmt, 21, 6)
+    raw = draw_layer(shape)
+    h = prepare_host(raw.x, raw.w, raw.b, shape.r)
+    x_hat = h.smooth(raw.x)
+    codes, scales = gptq_residual(h, x_hat, fmt)
+    oc, os_ = gptq.gptq(h.r_t, gptq.hessian(x_hat), fmt)
+    assert np.array_equal(codes, oc)
+    assert np.array_equal(scales.view(np.uint16), os_.view(np.uint16))
