@@ -108,8 +108,10 @@ def parse():
     ap.add_argument("--settle-ms", type=float, default=60.0,
                     help="untimed steps of the same work for at least this long before each warm-up "
                          "(the GPU clock ramps up over the first ~25 ms of load)")
-    ap.add_argument("--fmt", choices=["int4_e2m3", "int4"], default="int4_e2m3",
-                    help="INT4 g64 codes in the 6-bit E2M3 container (FP6 MFMA) or packed nibbles (INT8 MFMA)")
+    ap.add_argument("--fmt", choices=["int4_e2m3", "int4", "mxfp4"], default="int4_e2m3",
+                    help="INT4 g64 codes in the 6-bit E2M3 container (FP6 MFMA, the default), packed "
+                         "nibbles (INT8 MFMA), or the MXFP4 format (E2M1 g32, E8M0 scales) on the "
+                         "block-scaled FP4 MFMA")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run only a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -526,13 +528,18 @@ def main():
     dom_ops = ops + 2.0 * M * r * N                       # Kernel B: W4A4 GEMM + up projection
     achieved = dom_ops / (kb_us * 1e-6) / 1e12
     traffic = kernel_b_traffic(fmt, args.workload, r)
-    roof = {"kernel": "k_gemm3 / k_gemm2 (Kernel B: W4A4 GEMM + up projection + bias)", "bound": "mfma",
-            "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / INT8_PEAK_TOPS, 4),
+    kname = {"int4_e2m3": "k_gemm3", "int4": "k_gemm2", "mxfp4": "k_gemm_mx"}[fmt]
+    # a contraction is priced at its own dtype's dense peak: INT8 for the INT4 paths (their
+    # integer products), FP4 for MXFP4
+    peak = FP6_PEAK_TFLOPS if fmt == "mxfp4" else INT8_PEAK_TOPS
+    roof = {"kernel": f"{kname} (Kernel B: W4A4 GEMM + up projection + bias)", "bound": "mfma",
+            "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
             "traffic": None if traffic is None else traffic["hbm_bytes_per_launch"],
             "algorithmic": f"2*M*N*K + 2*M*r*N = {dom_ops:.4g} int8-equivalent ops per launch",
             "avg_launch_us": round(kb_us, 2),
             "frac_of_fp6_peak": round(achieved / FP6_PEAK_TFLOPS, 4) if fmt == "int4_e2m3" else None,
+            "frac_of_int8_peak": round(achieved / INT8_PEAK_TOPS, 4),
             "algorithmic_hbm_bytes": kb_bytes}
 
     out = {
@@ -546,9 +553,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 codes; fp6(e2m3) MFMA" if fmt == "int4_e2m3" else "int4 codes; i8 MFMA",
+        "dtype": {"int4_e2m3": "int4 codes; fp6(e2m3) MFMA", "int4": "int4 codes; i8 MFMA",
+                  "mxfp4": "e2m1 codes, e8m0 scales; block-scaled fp4 MFMA"}[fmt],
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {L.lname} M={M} K={K} N={N} r={r} int4 group 64, fp16 scales",
+        "config": {"workload": f"{args.workload}: {L.lname} M={M} K={K} N={N} r={r} "
+                               + ("mxfp4 group 32, e8m0 scales" if fmt == "mxfp4" else "int4 group 64, fp16 scales"),
                    "storage": fmt, "rotated_buffer_sets": ROTATE, "settle_ms_before_warmup": SETTLE_MS,
                    "kernel_events_on_every_nth_step": EVENT_EVERY},
         "us_per_layer": round(head["us_per_layer"], 2),
