@@ -75,7 +75,7 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
   constexpr int RBX = RB > 0 ? RB : 1;
   constexpr int ROWS = 16 * NRT;
   constexpr int CB = chunk_code_bytes<FMT>();
-  constexpr bool STAGE = QUANT && FMT != FMT_FP4 && FMT != FMT_MXFP4;   // codes go out through LDS
+  constexpr bool STAGE = QUANT && FMT != FMT_FP4;          // codes go out through LDS
   constexpr int RP = R + 4;                                 // padded row of the partial sums
   constexpr int SMEM = cmax(cmax(STAGE ? 4 * ROWS * CB : 0, RB > 0 ? 4 * ROWS * RP * 4 : 0), 16);
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
@@ -273,13 +273,12 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
           q[e] = (int)fp4_code_q(ldexpf(v[e], -e0));
           q[8 + e] = (int)fp4_code_q(ldexpf(v[8 + e], -e1));
         }
-        if (m < M) {                             // chunk-major: the chunk's 32 bytes of row m
-          uint8_t* dst = xq + ((size_t)c * M + m) * 32;
-          *reinterpret_cast<uint32_t*>(dst + 4 * sub) = pack8(q);
-          *reinterpret_cast<uint32_t*>(dst + 16 + 4 * sub) = pack8(q + 8);
-          if (sub == 0)                          // the row's two E8M0 bytes of this chunk
-            *reinterpret_cast<uint16_t*>(xs + ((size_t)c * M + m) * 2) = (uint16_t)((e0 + 127) | ((e1 + 127) << 8));
-        }
+        // the row's 32 code bytes of this chunk, in LDS (written out chunk-major below)
+        uint8_t* srow = slot + (rt * 16 + row) * CB;
+        *reinterpret_cast<uint32_t*>(srow + 4 * sub) = pack8(q);
+        *reinterpret_cast<uint32_t*>(srow + 16 + 4 * sub) = pack8(q + 8);
+        if (sub == 0 && m < M)                   // the row's two E8M0 bytes of this chunk
+          *reinterpret_cast<uint16_t*>(xs + ((size_t)c * M + m) * 2) = (uint16_t)((e0 + 127) | ((e1 + 127) << 8));
       }
     } else {  // FP4: groups of 16 = two lanes (sub, sub^1) x 8 values
 #pragma unroll
@@ -318,8 +317,9 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
       }
     }
     if (STAGE) {
-      // the wave's ROWS x CB bytes go out as 16-byte pieces: the 6-bit container's rows of
-      // one group are contiguous ([K/64][M][48]); the other formats are row-major
+      // the wave's ROWS x CB bytes go out as 16-byte pieces: the rows of one 64-K chunk are
+      // contiguous in the 6-bit container ([K/64][M][48]) and in MXFP4 ([K/64][M][32]); the
+      // other formats are row-major
       __builtin_amdgcn_wave_barrier();
       constexpr int PR = CB / 16;            // pieces per row
 #pragma unroll
@@ -329,8 +329,8 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
         const int mm = m0 + rr;
         if (p < ROWS * PR && mm < M) {
           const uint4 v16 = *reinterpret_cast<const uint4*>(slot + rr * CB + pc * 16);
-          uint8_t* dst = FMT == FMT_INT4_E2M3 ? xq + ((size_t)c * M + mm) * 48 + pc * 16
-                                              : xq + (size_t)mm * code_row + (size_t)c * CB + pc * 16;
+          uint8_t* dst = FMT == FMT_INT4_E2M3 || FMT == FMT_MXFP4 ? xq + ((size_t)c * M + mm) * CB + pc * 16
+                                                                  : xq + (size_t)mm * code_row + (size_t)c * CB + pc * 16;
           *reinterpret_cast<uint4*>(dst) = v16;
         }
       }
