@@ -332,3 +332,32 @@ def test_empty_inputs_are_no_ops():
     wq, ws = binding.svdq_quantize_weight(torch.zeros((N, K), dtype=torch.float32, device="cuda"), "int4")
     y = binding.svdq_linear(x, None, wq, ws, None, None, "int4")
     assert y.shape == (0, N)
+
+
+def test_mxfp4_ties_saturation_and_signed_zero():
+    # values on the E2M1 tie points (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 times the group's
+    # scale), above the largest code (6.5, 7.9: saturate to 6), tiny ones (0.1: a negative one
+    # must give code +0, not -0), zeros and exact grid values, in both signs; each group's
+    # first value 7.5 2^e
+    # fixes its scale at 2^e (e = floor(log2 7.5) + e - 2), e different per group
+    M, K = 32, 256
+    g = np.random.default_rng(9)
+    pts = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.5, 7.9, 0.1, 0.0, 0.5, 1.5, 3.0, 4.0, 6.0])
+    x = np.zeros((M, K))
+    for m in range(M):
+        for grp in range(K // 32):
+            e = int(g.integers(-8, 6))
+            vals = g.choice(pts, 32) * np.where(g.random(32) < 0.5, -1.0, 1.0)
+            vals[0] = 7.5 * (1 if g.random() < 0.5 else -1)
+            x[m, grp * 32:(grp + 1) * 32] = vals * 2.0 ** e
+    x16 = x.astype(np.float16)
+    q, s, stored = oracle.quant.quantize(x16, "mxfp4")
+    xq, xs, _ = binding.svdq_quantize_down(dev(x16), None, "mxfp4")
+    assert same_bytes(host(xq), dev_codes(stored, "mxfp4"))
+    assert same_bytes(host(xs), dev_scales(s, "mxfp4"))
+    w32 = x16.astype(np.float32)
+    q2, s2, st2 = oracle.quant.quantize(w32, "mxfp4")
+    wq, ws = binding.svdq_quantize_weight(dev(w32), "mxfp4")
+    assert same_bytes(host(wq), dev_codes(st2, "mxfp4"))
+    assert same_bytes(host(ws), dev_scales(s2, "mxfp4"))
+    assert set(np.unique(q).tolist()) == set(range(16)) - {8}   # every code but -0 is reached
