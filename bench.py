@@ -500,7 +500,7 @@ def main():
     SETTLE_MS = args.settle_ms
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU: the layer runs on a single device and this build has no "
+        print(f"bench.py measures one GPU: the layer runs on a single device and the library has no "
               f"multi-GPU path (asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
 

@@ -3,7 +3,7 @@
 // the epilogue, fp16 store.
 //
 // Practice page "sota-314", section "Do this": the up projection is fused
-// with the 4-bit compute because both write the same output.
+// with the 4-bit compute since both produce Y.
 //
 //   Y[m,n] = fp16_rne( sum_g sx[m,g] sw[n,g] P_g[m,n] + (T L2)[m,n] + b[n] )
 //   P_g    = sum_{k in group g} q_x[m,k] q_w[n,k]   (exact)

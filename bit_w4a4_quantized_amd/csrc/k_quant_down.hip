@@ -2,7 +2,7 @@
 // T = X_hat L1 in one pass over X_hat.
 //
 // Practice page "sota-314", section "Do this": the down projection is fused
-// with quantization because the two read the same input; reading note
+// with quantization since both consume X_hat; reading note
 // "note-257", section "Key results": unfused, the branch pays an extra 16-bit
 // read of the activations.
 //

@@ -66,7 +66,8 @@ def prepare_host(x_cal: np.ndarray, w: np.ndarray, bias: np.ndarray, r: int) -> 
 
 def attach_lora(h: HostLayer, a: np.ndarray, b: np.ndarray, scale: float = 1.0) -> HostLayer:
     """The layer with a LoRA adapter (delta W = scale A B; A [K, ra], B [ra, N]) in its 16-bit
-    branch ("sota-314", "Known implementations": adapters load without re-quantization).
+    branch ("sota-314", "Known implementations": the authors' engine attaches adapters and keeps
+    the quantized weights as they are).
     X A B = X_hat diag(lambda) A B, so the branch grows to
         L1^T' = [L1^T; fp16(diag(lambda) A)^T],   L2' = [L2; fp16(scale B)]
     (products in float64, one rounding each), zero rows padding the rank to a multiple of 16
@@ -87,7 +88,7 @@ def attach_lora(h: HostLayer, a: np.ndarray, b: np.ndarray, scale: float = 1.0) 
 
 def gptq_residual(h: HostLayer, x_cal_hat: np.ndarray, fmt: str, damp: float = 0.01):
     """GPTQ codes of the residual ("sota-314", "Do this": the residual weights are quantized
-    with GPTQ rather than round-to-nearest; Frantar et al. 2022, "GPTQ", Algorithm 1, without
+    with GPTQ in the authors' pipeline, not to nearest; Frantar et al. 2022, "GPTQ", Algorithm 1, without
     its lazy batching, which only regroups the same updates).  x_cal_hat: smoothed calibration
     activations [M, K] (the inputs R multiplies).  Each input channel in turn is rounded with
     the round-to-nearest rule (fp16 group scale from the group's current weights at its first

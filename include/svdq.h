@@ -123,7 +123,7 @@ size_t svdq_scale_row_bytes(int K, svdq_format fmt);
 
 /*
  * Kernel A: quantize + down projection ("sota-314", "Do this": the down
- * projection is fused with quantization because both read the same input;
+ * projection is fused with quantization since both consume X_hat;
  * "note-257", "Key results").
  *   x_hat : fp16 [M, K], the smoothed activations (smoothing already applied).
  *   l1t   : fp16 [r, K] = L1^T; NULL iff r == 0.
@@ -195,8 +195,8 @@ svdq_status svdq_quantize_weight(const float* r_t, int N, int K, svdq_format fmt
 
 /*
  * Codes and scales of the residual computed elsewhere -- e.g. GPTQ on the host
- * ("sota-314", "Do this": the residual weights are quantized with GPTQ rather
- * than round-to-nearest) -- put into the layouts Kernel B reads, for the INT
+ * ("sota-314", "Do this": the authors' pipeline rounds the residual with GPTQ,
+ * not to nearest) -- put into the layouts Kernel B reads, for the INT
  * formats (SVDQ_INT4_G64, SVDQ_INT4_G64_E2M3, SVDQ_INT8_G64; others are
  * SVDQ_ERR_FORMAT):
  *   codes  : int8 [N, K], one code per byte (in [-7, 7] or [-127, 127]; not

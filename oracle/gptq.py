@@ -1,8 +1,8 @@
 """GPTQ rounding of the residual (oracle).
 
-Practice page "sota-314", section "Do this": the residual weights are quantized with GPTQ
-rather than round-to-nearest, which improves quality in most of the paper's settings; this
-build's default remains round-to-nearest (codes as a pure function of the weights).  GPTQ (Frantar, Ashkboos,
+Practice page "sota-314", section "Do this": the authors' pipeline rounds the residual with
+GPTQ instead of to nearest, and reports better quality for it in most settings; the default
+here stays round-to-nearest (codes as a pure function of the weights).  GPTQ (Frantar, Ashkboos,
 Hoefler, Alistarh 2022, "GPTQ: Accurate Post-Training Quantization for Generative
 Pre-trained Transformers", Algorithm 1) rounds the weight one input channel (column of K) at
 a time and spreads each column's rounding error over the channels not yet rounded, weighted

@@ -85,7 +85,8 @@ def prepare_layer(x: np.ndarray, w: np.ndarray, b: np.ndarray, r: int, x_cal: np
 def lora_branch(l1: np.ndarray, l2: np.ndarray, lam: np.ndarray, a: np.ndarray, b: np.ndarray,
                 scale: float = 1.0):
     """A LoRA adapter carried by the 16-bit branch (practice page "sota-314", section "Known
-    implementations": the engine loads off-the-shelf adapters without re-quantization).
+    implementations": the authors' engine attaches existing adapters and leaves the
+    quantized weights as they are).
 
     The adapted layer is X (W + scale A B) with A [K, ra], B [ra, N].  In smoothed coordinates
     X = X_hat diag(lambda), so X A B = X_hat (diag(lambda) A) B and the adapter joins the
