@@ -118,14 +118,13 @@ def code_row_bytes(K: int, fmt) -> int:
 
 
 def code_shape(rows: int, K: int, fmt):
-    """Shape of a code tensor: [rows, row bytes], group-major [K/64, rows, 48] for the E2M3
-    container, chunk-major [K/64, rows, 32] for MXFP4."""
+    """Shape of a code tensor: row-major [rows, K/2] for packed INT4; chunk-major
+    [K/64, rows, bytes per 64-K chunk] otherwise (48 for the E2M3 container, 64 for INT8, 32
+    for FP4 and MXFP4)."""
     name = fmt if isinstance(fmt, str) else FMT_NAMES[int(fmt)]
-    if name == "int4_e2m3":
-        return (K // 64, rows, 48)
-    if name == "mxfp4":
-        return (K // 64, rows, 32)
-    return (rows, code_row_bytes(K, fmt))
+    if name == "int4":
+        return (rows, code_row_bytes(K, fmt))
+    return (K // 64, rows, {"int4_e2m3": 48, "int8": 64, "fp4": 32, "mxfp4": 32}[name])
 
 
 def code_rows(q) -> int:
@@ -139,14 +138,15 @@ def scale_row_entries(K: int, fmt) -> int:
 
 
 def scale_shape(rows: int, K: int, fmt):
-    """Shape of the scale tensor: [rows, K/G], group-major [K/64, rows] for the E2M3 container,
-    chunk-major [K/64, rows, 2] for MXFP4."""
+    """Shape of the scale tensor: row-major [rows, K/64] for packed INT4; group-major
+    [K/64, rows] for the E2M3 container and INT8; chunk-major [K/64, rows, 4] (FP4) or
+    [K/64, rows, 2] (MXFP4)."""
     name = fmt if isinstance(fmt, str) else FMT_NAMES[int(fmt)]
-    if name == "int4_e2m3":
+    if name == "int4":
+        return (rows, K // 64)
+    if name in ("int4_e2m3", "int8"):
         return (K // 64, rows)
-    if name == "mxfp4":
-        return (K // 64, rows, 2)
-    return (rows, K // GROUP[name])
+    return (K // 64, rows, {"fp4": 4, "mxfp4": 2}[name])
 
 
 def scale_dtype(fmt):

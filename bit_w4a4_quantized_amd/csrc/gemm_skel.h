@@ -23,8 +23,7 @@
 //   struct Regs; void read(const uint8_t* buf, int st, Regs&);
 //   void mma(const Regs&, int st, v16f (&acc)[2][2]);
 // and, for an operator whose kernel runs the last partial round as 32 x 32 sub-tile jobs
-// (operands straight into registers; with row-major codes each 16-byte lane load touches 32
-// cache lines, so this pays only where the codes are compact: FP4 yes, INT8 no):
+// (operands straight into registers; used by FP4 and MXFP4):
 //   int NU; static constexpr int SUB_PD;            64-column units of K; register ring depth
 //   struct UR; void gload(int u, int m, int n, UR&);  unit u of lane's X row m, W row n (every
 //                                                   lane loads: no branch around a load)

@@ -108,11 +108,10 @@ struct OpF4 {
     const int row = wave * 32 + (lane >> 1);
     const int c = (lane & 1) ^ ((row >> 3) & 1);
     Src s;
-    s.vx = (uint32_t)min(m0 + row, M - 1) * (uint32_t)(K / 2) + 16u * c;
-    s.vw = (uint32_t)min(n0 + row, N - 1) * (uint32_t)(K / 2) + 16u * c;
+    s.vx = (uint32_t)min(m0 + row, M - 1) * 32u + 16u * c;
+    s.vw = (uint32_t)min(n0 + row, N - 1) * 32u + 16u * c;
     const int srow = (wave & 1) * 64 + lane;
-    s.vs = wave < 2 ? (uint32_t)min(m0 + srow, M - 1) * (uint32_t)(K / 16)
-                    : (uint32_t)min(n0 + srow, N - 1) * (uint32_t)(K / 16);
+    s.vs = wave < 2 ? (uint32_t)min(m0 + srow, M - 1) * 4u : (uint32_t)min(n0 + srow, N - 1) * 4u;
     return s;
   }
   __device__ void load(const Src& s, int st, uint8_t* buf) const {
@@ -120,9 +119,9 @@ struct OpF4 {
     for (int k = 0; k < KC; k++) {
       const int c = min(st * KC + k, C - 1);  // a chunk past the end re-reads the last one (unused)
       uint8_t* b = buf + k * CHUNK;
-      dma16(rx, b + L_X + wave * 1024, s.vx, (uint32_t)c * 32u);
-      dma16(rw, b + L_W + wave * 1024, s.vw, (uint32_t)c * 32u);
-      dma4(rs, b + (wave < 2 ? L_SX : L_SW) + (wave & 1) * 256, s.vs, (uint32_t)c * 4u);
+      dma16(rx, b + L_X + wave * 1024, s.vx, (uint32_t)c * (uint32_t)M * 32u);
+      dma16(rw, b + L_W + wave * 1024, s.vw, (uint32_t)c * (uint32_t)N * 32u);
+      dma4(rs, b + (wave < 2 ? L_SX : L_SW) + (wave & 1) * 256, s.vs, (uint32_t)c * (uint32_t)(wave < 2 ? M : N) * 4u);
     }
   }
   __device__ void read(const uint8_t* buf, int st, Regs& r) const {
@@ -146,10 +145,10 @@ struct OpF4 {
     uint32_t sx, sw;
   };
   __device__ void gload(int u, int m, int n, UR& o) const {
-    o.x = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rx, (int)((uint32_t)m * (uint32_t)(K / 2) + 16u * h), u * 32, 0));
-    o.w = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rw, (int)((uint32_t)n * (uint32_t)(K / 2) + 16u * h), u * 32, 0));
-    o.sx = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(gxs, (int)((uint32_t)m * (uint32_t)(K / 16) + 2u * h), u * 4, 0);
-    o.sw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(gws, (int)((uint32_t)n * (uint32_t)(K / 16) + 2u * h), u * 4, 0);
+    o.x = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rx, (int)((uint32_t)m * 32u + 16u * h), (int)((uint32_t)u * (uint32_t)M * 32u), 0));
+    o.w = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rw, (int)((uint32_t)n * 32u + 16u * h), (int)((uint32_t)u * (uint32_t)N * 32u), 0));
+    o.sx = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(gxs, (int)((uint32_t)m * 4u + 2u * h), (int)((uint32_t)u * (uint32_t)M * 4u), 0);
+    o.sw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(gws, (int)((uint32_t)n * 4u + 2u * h), (int)((uint32_t)u * (uint32_t)N * 4u), 0);
   }
   __device__ void gmma(const UR& o, bool zero, v16f& acc) const {
     h2_t xs_lo, xs_hi, ws_lo, ws_hi;         // a zero scale makes every dequantized value 0

@@ -29,6 +29,7 @@ struct OpI8 {
   int M, N, K, G, NS;
   int lane, h, wave;
   bool s_x;                                  // this wave loads X (waves 0, 1) or W (2, 3)
+  int rows;                                  // rows of the operand this wave loads (M or N)
   rsrc_t rc, rs;
   int xo[2][2], wo[2][2], sxo[2], swo[2];    // per-lane LDS read offsets within a group
 
@@ -48,6 +49,7 @@ struct OpI8 {
     h = lane >> 5;
     wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     s_x = wave < 2;
+    rows = s_x ? M : N;
     rc = s_x ? make_rsrc(xq, (size_t)M * K) : make_rsrc(wq, (size_t)N * K);
     rs = s_x ? make_rsrc(xs, (size_t)M * G * 2) : make_rsrc(ws, (size_t)N * G * 2);
     const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31;
@@ -65,18 +67,20 @@ struct OpI8 {
   }
 
   // wave w loads rows 64 (w % 2) .. + 63 of its operand: four 16-row DMAs of codes (lane ->
-  // row lane / 4, slot lane % 4 holding the swizzled piece) and one of scales.  Rows past the
-  // edge re-read the last row (their outputs are never stored).
+  // row lane / 4, slot lane % 4 holding the swizzled piece) and one of scales.  Codes are
+  // group-major ([K/64][rows][64 bytes], scales [K/64][rows]): the group's offset is scalar,
+  // and a DMA's 16 rows are one contiguous 1 KB run.  Rows past the edge re-read the last row
+  // (their outputs are never stored).
   __device__ Src src(int m0, int n0) const {
-    const int r0 = s_x ? m0 : n0, rows = s_x ? M : N;
+    const int r0 = s_x ? m0 : n0;
     Src s;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int row = (wave & 1) * 64 + 16 * i + (lane >> 2);
       const int c = (lane & 3) ^ ((row >> 2) & 3);
-      s.vc[i] = (uint32_t)min(r0 + row, rows - 1) * (uint32_t)K + 16u * c;
+      s.vc[i] = (uint32_t)min(r0 + row, rows - 1) * 64u + 16u * c;
     }
-    s.vs = (uint32_t)min(r0 + (wave & 1) * 64 + lane, rows - 1) * (uint32_t)G * 2u;
+    s.vs = (uint32_t)min(r0 + (wave & 1) * 64 + lane, rows - 1) * 2u;
     return s;
   }
   __device__ void load(const Src& s, int st, uint8_t* buf) const {
@@ -85,8 +89,9 @@ struct OpI8 {
       const int g = min(st * KC + k, G - 1);  // a group past the end re-reads the last one (unused)
       uint8_t* b = buf + k * GROUP;
 #pragma unroll
-      for (int i = 0; i < 4; i++) dma16(rc, b + (s_x ? L_X : L_W) + ((wave & 1) * 64 + 16 * i) * 64, s.vc[i], (uint32_t)g * 64u);
-      dma2(rs, b + (s_x ? L_SX : L_SW) + (wave & 1) * 256, s.vs, (uint32_t)g * 2u);
+      for (int i = 0; i < 4; i++)
+        dma16(rc, b + (s_x ? L_X : L_W) + ((wave & 1) * 64 + 16 * i) * 64, s.vc[i], (uint32_t)g * (uint32_t)rows * 64u);
+      dma2(rs, b + (s_x ? L_SX : L_SW) + (wave & 1) * 256, s.vs, (uint32_t)g * (uint32_t)rows * 2u);
     }
   }
   __device__ void read(const uint8_t* buf, int st, Regs& r) const {

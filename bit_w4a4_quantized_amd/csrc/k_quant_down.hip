@@ -75,7 +75,7 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
   constexpr int RBX = RB > 0 ? RB : 1;
   constexpr int ROWS = 16 * NRT;
   constexpr int CB = chunk_code_bytes<FMT>();
-  constexpr bool STAGE = QUANT && FMT != FMT_FP4;          // codes go out through LDS
+  constexpr bool STAGE = QUANT;                            // codes go out through LDS
   constexpr int RP = R + 4;                                 // padded row of the partial sums
   constexpr int SMEM = cmax(cmax(STAGE ? 4 * ROWS * CB : 0, RB > 0 ? 4 * ROWS * RP * 4 : 0), 16);
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
@@ -193,7 +193,7 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
           const int m = m0 + rt * 16 + row;
           if (sub == 0 && m < M) {
             // row-major scales [M, K/64]; the 6-bit container keeps them group-major [K/64, M]
-            const size_t si = FMT == FMT_INT4_E2M3 ? (size_t)c * M + m : (size_t)m * (K >> 6) + c;
+            const size_t si = FMT == FMT_INT4 ? (size_t)m * (K >> 6) + c : (size_t)c * M + m;
             reinterpret_cast<uint16_t*>(xs)[si] = sbits;
           }
           uint8_t* srow = slot + (rt * 16 + row) * CB;   // this row's bytes of the chunk, in LDS
@@ -317,23 +317,20 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
           q[e] = s0 == 0.0f ? 0 : (int)fp4_code_q(quot_rn(v[e], s0, r0));
           q[8 + e] = s1 == 0.0f ? 0 : (int)fp4_code_q(quot_rn(v[8 + e], s1, r1));
         }
-        if (m < M) {
-          const int col = c * 64 + sub * 8;
-          uint8_t* dst = xq + (size_t)m * (K >> 1);
-          *reinterpret_cast<uint32_t*>(dst + (col >> 1)) = pack8(q);
-          *reinterpret_cast<uint32_t*>(dst + ((col + 32) >> 1)) = pack8(q + 8);
-          if ((sub & 1) == 0) {
-            uint8_t* sd = xs + (size_t)m * (K >> 4) + c * 4 + (sub >> 1);
-            sd[0] = (uint8_t)b0;
-            sd[2] = (uint8_t)b1;
-          }
+        // the row's 32 code bytes of this chunk, in LDS (written out chunk-major below)
+        uint8_t* srow = slot + (rt * 16 + row) * CB;
+        *reinterpret_cast<uint32_t*>(srow + 4 * sub) = pack8(q);
+        *reinterpret_cast<uint32_t*>(srow + 16 + 4 * sub) = pack8(q + 8);
+        if (m < M && (sub & 1) == 0) {           // E4M3 bytes chunk-major [K/64][M][4]
+          uint8_t* sd = xs + ((size_t)c * M + m) * 4 + (sub >> 1);
+          sd[0] = (uint8_t)b0;
+          sd[2] = (uint8_t)b1;
         }
       }
     }
     if (STAGE) {
       // the wave's ROWS x CB bytes go out as 16-byte pieces: the rows of one 64-K chunk are
-      // contiguous in the 6-bit container ([K/64][M][48]) and in MXFP4 ([K/64][M][32]); the
-      // other formats are row-major
+      // contiguous ([K/64][M][CB]) in every format but packed INT4, which is row-major
       __builtin_amdgcn_wave_barrier();
       constexpr int PR = CB / 16;            // pieces per row
 #pragma unroll
@@ -343,8 +340,8 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
         const int mm = m0 + rr;
         if (p < ROWS * PR && mm < M) {
           const uint4 v16 = *reinterpret_cast<const uint4*>(slot + rr * CB + pc * 16);
-          uint8_t* dst = FMT == FMT_INT4_E2M3 || FMT == FMT_MXFP4 ? xq + ((size_t)c * M + mm) * CB + pc * 16
-                                                                  : xq + (size_t)mm * code_row + (size_t)c * CB + pc * 16;
+          uint8_t* dst = FMT != FMT_INT4 ? xq + ((size_t)c * M + mm) * CB + pc * 16
+                                         : xq + (size_t)mm * code_row + (size_t)c * CB + pc * 16;
           *reinterpret_cast<uint4*>(dst) = v16;
         }
       }

@@ -9,14 +9,15 @@
 namespace svdq {
 
 // One INT group's codes (64 values, code e of group g of output column n) and fp16 scale bits
-// into the layouts Kernel B reads: packed nibbles [N, K/2] (INT4), int8 [N, K] (INT8), or the
-// 6-bit container, group-major [K/64][N][48] with group-major scales (INT4_E2M3).
+// into the layouts Kernel B reads: packed nibbles [N, K/2] (INT4), int8 group-major
+// [K/64][N][64] (INT8), or the 6-bit container, group-major [K/64][N][48] (INT4_E2M3); the
+// scales row-major [N, K/64] for INT4, group-major [K/64, N] otherwise.
 template <int FMT>
 __device__ __forceinline__ void store_int_group(const int* q, uint16_t sbits, int n, int g, int N, int K,
                                                 uint8_t* __restrict__ wq, uint8_t* __restrict__ ws) {
   constexpr int G = 64;
   const int gpr = K / G;
-  reinterpret_cast<uint16_t*>(ws)[FMT == FMT_INT4_E2M3 ? (size_t)g * N + n : (size_t)n * gpr + g] = sbits;
+  reinterpret_cast<uint16_t*>(ws)[FMT == FMT_INT4 ? (size_t)n * gpr + g : (size_t)g * N + n] = sbits;
   if (FMT == FMT_INT4_E2M3) {
     // 48 bytes per (group, column): two halves of 32 six-bit fields
     uint32_t wv[12];
@@ -44,7 +45,7 @@ __device__ __forceinline__ void store_int_group(const int* q, uint16_t sbits, in
 #pragma unroll
     for (int e = 0; e < G; e += 8) dst[e >> 3] = pack8(q + e);
   } else {
-    uint32_t* dst = reinterpret_cast<uint32_t*>(wq + (size_t)n * K + (size_t)g * G);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(wq + ((size_t)g * N + n) * 64);
 #pragma unroll
     for (int e = 0; e < G; e += 4) dst[e >> 2] = pack4_i8(q + e);
   }
@@ -90,13 +91,16 @@ k_quant_weight(const float* __restrict__ r_t, int N, int K, uint8_t* __restrict_
 #pragma unroll
     for (int e = 0; e < G; e += 8) dst[e >> 3] = pack8(q + e);
   } else {
+    // chunk-major: group g of 16 is piece g % 4 of 64-K chunk g / 4; codes [K/64][N][32 bytes],
+    // E4M3 bytes [K/64][N][4]
     uint32_t b;
     const float s = fp4_scale(amax, &b);
-    ws[(size_t)n * gpr + g] = (uint8_t)b;
+    const size_t cn = (size_t)(g >> 2) * N + n;
+    ws[cn * 4 + (g & 3)] = (uint8_t)b;
     int q[G];
 #pragma unroll
     for (int e = 0; e < G; e++) q[e] = (int)fp4_code(v[e], s);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(wq + (size_t)n * (K >> 1) + (size_t)g * (G >> 1));
+    uint32_t* dst = reinterpret_cast<uint32_t*>(wq + cn * 32 + (g & 3) * 8);
 #pragma unroll
     for (int e = 0; e < G; e += 8) dst[e >> 3] = pack8(q + e);
   }

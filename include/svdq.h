@@ -46,12 +46,18 @@
  *                  scale = fp16_rne(fp32(absmax) / 7.0f); code =
  *                  clamp(rint_half_even(fp32(v) / scale), -7, 7); scale 0 ->
  *                  codes 0.
- *  SVDQ_INT8_G64 : same rule with 127; one int8 code per byte.
+ *  SVDQ_INT8_G64 : same rule with 127; one int8 code per byte.  Codes
+ *                  group-major [K/64][rows][64 bytes] (group g of row i at
+ *                  byte (g * rows + i) * 64), fp16 scales group-major
+ *                  [K/64][rows]: a GEMM tile's rows of one group are one
+ *                  contiguous run.
  *  SVDQ_FP4_G16  : E2M1 codes (sign<<3 | magnitude index, magnitudes
  *                  0,0.5,1,1.5,2,3,4,6), packed as INT4; one E4M3FN scale byte
  *                  per 16: scale = e4m3_rne_sat(fp32(absmax) / 6.0f); code =
  *                  nearest E2M1 to fp32(v)/scale, ties to the even mantissa,
- *                  -0 -> +0.
+ *                  -0 -> +0.  Codes chunk-major [K/64][rows][32 bytes] (chunk c of
+ *                  row i at byte (c * rows + i) * 32, two codes per byte as
+ *                  above), E4M3 bytes [K/64][rows][4].
  *  SVDQ_INT4_G64_E2M3 : the SVDQ_INT4_G64 codes and scales, bit for bit, in the
  *                  storage the gfx950 FP6 matrix cores read directly: each code
  *                  q becomes the 6-bit E2M3 pattern of q/8 (a subnormal:

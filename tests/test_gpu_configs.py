@@ -17,6 +17,7 @@ import oracle  # noqa: E402
 from bit_w4a4_quantized_amd import binding  # noqa: E402
 from tests.layers import (log, prepared, raw_layer, reference, rel_fro, within_sum_bound,  # noqa: E402
                           linear_abs_sum, branch_slack, w4a16_bound_terms, gemm_terms)
+from tests.test_gpu_kernels import dev_codes, dev_scales  # noqa: E402
 
 TOL = 1e-3
 
@@ -41,23 +42,6 @@ def host(t):
 def same_bytes(a, b):
     a, b = np.ascontiguousarray(a), np.ascontiguousarray(b)
     return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
-
-
-def dev_codes(stored, fmt):
-    """Codes in the device layout of the format.  The E2M3 container is group-major
-    [K/64][rows][48] with the bytes of a group ordered half 0 [0:16], half 1 [0:16],
-    half 0 [16:24], half 1 [16:24]; the oracle stores it row by row, each half's 24 bytes
-    contiguous."""
-    if fmt != "int4_e2m3":
-        return stored
-    rows = stored.shape[0]
-    g = stored.reshape(rows, -1, 48)
-    g = np.concatenate([g[..., 0:16], g[..., 24:40], g[..., 16:24], g[..., 40:48]], axis=-1)
-    return np.ascontiguousarray(g.transpose(1, 0, 2))
-
-
-def dev_scales(s, fmt):
-    return np.ascontiguousarray(s.T) if fmt == "int4_e2m3" else s
 
 
 def run_layer(P, fmt, x_hat=None, check_codes=True):

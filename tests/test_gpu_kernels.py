@@ -43,13 +43,14 @@ def same_bytes(a, b):
 
 
 def dev_codes(stored, fmt):
-    """Codes in the device layout of the format.  The E2M3 container is group-major
-    [K/64][rows][48] with the bytes of a group ordered half 0 [0:16], half 1 [0:16],
-    half 0 [16:24], half 1 [16:24]; the oracle stores it row by row, each half's 24 bytes
-    contiguous.  MXFP4 is chunk-major [K/64][rows][32] (the oracle: packed rows)."""
-    if fmt == "mxfp4":
+    """Codes in the device layout of the format (the oracle stores every format row by row).
+    The E2M3 container is group-major [K/64][rows][48] with the bytes of a group ordered
+    half 0 [0:16], half 1 [0:16], half 0 [16:24], half 1 [16:24] (the oracle: each half's 24
+    bytes contiguous); INT8, FP4 and MXFP4 are chunk-major [K/64][rows][bytes per chunk];
+    packed INT4 stays row-major."""
+    if fmt in ("int8", "fp4", "mxfp4"):
         rows = stored.shape[0]
-        return np.ascontiguousarray(stored.reshape(rows, -1, 32).transpose(1, 0, 2))
+        return np.ascontiguousarray(stored.reshape(rows, -1, 64 if fmt == "int8" else 32).transpose(1, 0, 2))
     if fmt != "int4_e2m3":
         return stored
     rows = stored.shape[0]
@@ -59,11 +60,12 @@ def dev_codes(stored, fmt):
 
 
 def dev_scales(s, fmt):
-    """Scales in the device layout of the format (group-major for the E2M3 container,
-    chunk-major [K/64][rows][2] for MXFP4)."""
-    if fmt == "mxfp4":
-        return np.ascontiguousarray(s.reshape(s.shape[0], -1, 2).transpose(1, 0, 2))
-    return np.ascontiguousarray(s.T) if fmt == "int4_e2m3" else s
+    """Scales in the device layout of the format: group-major [K/64][rows] for the E2M3
+    container and INT8, chunk-major [K/64][rows][4] (FP4) or [K/64][rows][2] (MXFP4), row-major
+    for packed INT4."""
+    if fmt in ("fp4", "mxfp4"):
+        return np.ascontiguousarray(s.reshape(s.shape[0], -1, 4 if fmt == "fp4" else 2).transpose(1, 0, 2))
+    return np.ascontiguousarray(s.T) if fmt in ("int4_e2m3", "int8") else s
 
 
 FMTS = ["int4", "int8", "fp4", "int4_e2m3", "mxfp4"]
