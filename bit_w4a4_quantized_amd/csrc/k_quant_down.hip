@@ -272,25 +272,10 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
         // saturating at 6, two values per instruction -- the quantizer's rule, checked against
         // it on tie points, saturation and signed zeros; a negative value that rounds to zero
         // comes out as -0 and is made +0.  (fp16 inputs keep e >= -26, a normal scale.)
-        const float s0 = ldexpf(1.0f, e0), s1 = ldexpf(1.0f, e1);
-        uint32_t w0 = 0, w1 = 0;
-        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[0], v[1], s0, 0);
-        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[2], v[3], s0, 1);
-        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[4], v[5], s0, 2);
-        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[6], v[7], s0, 3);
-        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[8], v[9], s1, 0);
-        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[10], v[11], s1, 1);
-        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[12], v[13], s1, 2);
-        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[14], v[15], s1, 3);
-        auto plus_zero = [](uint32_t w) {         // clear the sign of nibbles whose magnitude is 0
-          const uint32_t mag = w & 0x77777777u;
-          const uint32_t nz = (mag | (mag >> 1) | (mag >> 2)) & 0x11111111u;
-          return mag | (w & (nz << 3));
-        };
         // the row's 32 code bytes of this chunk, in LDS (written out chunk-major below)
         uint8_t* srow = slot + (rt * 16 + row) * CB;
-        *reinterpret_cast<uint32_t*>(srow + 4 * sub) = plus_zero(w0);
-        *reinterpret_cast<uint32_t*>(srow + 16 + 4 * sub) = plus_zero(w1);
+        *reinterpret_cast<uint32_t*>(srow + 4 * sub) = fp4_codes8(v, ldexpf(1.0f, e0));
+        *reinterpret_cast<uint32_t*>(srow + 16 + 4 * sub) = fp4_codes8(v + 8, ldexpf(1.0f, e1));
         if (sub == 0 && m < M)                   // the row's two E8M0 bytes of this chunk
           *reinterpret_cast<uint16_t*>(xs + ((size_t)c * M + m) * 2) = (uint16_t)((e0 + 127) | ((e1 + 127) << 8));
       }
@@ -311,16 +296,17 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
         const float s1 = fp4_scale(a1, &b1);
         const float r0 = s0 == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s0);
         const float r1 = s1 == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s1);
-        int q[16];
+        // codes of the exact quotients t = RN(v / s) from the hardware convert at scale 1
+        float t[16];
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-          q[e] = s0 == 0.0f ? 0 : (int)fp4_code_q(quot_rn(v[e], s0, r0));
-          q[8 + e] = s1 == 0.0f ? 0 : (int)fp4_code_q(quot_rn(v[8 + e], s1, r1));
+          t[e] = s0 == 0.0f ? 0.0f : quot_rn(v[e], s0, r0);
+          t[8 + e] = s1 == 0.0f ? 0.0f : quot_rn(v[8 + e], s1, r1);
         }
         // the row's 32 code bytes of this chunk, in LDS (written out chunk-major below)
         uint8_t* srow = slot + (rt * 16 + row) * CB;
-        *reinterpret_cast<uint32_t*>(srow + 4 * sub) = pack8(q);
-        *reinterpret_cast<uint32_t*>(srow + 16 + 4 * sub) = pack8(q + 8);
+        *reinterpret_cast<uint32_t*>(srow + 4 * sub) = fp4_codes8(t, 1.0f);
+        *reinterpret_cast<uint32_t*>(srow + 16 + 4 * sub) = fp4_codes8(t + 8, 1.0f);
         if (m < M && (sub & 1) == 0) {           // E4M3 bytes chunk-major [K/64][M][4]
           uint8_t* sd = xs + ((size_t)c * M + m) * 4 + (sub >> 1);
           sd[0] = (uint8_t)b0;

@@ -152,6 +152,27 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+// Eight E2M1 codes from the hardware convert with -0 made +0: v_cvt_scalef32_pk_fp4_f32 rounds
+// to the nearest E2M1 value, ties to the even mantissa, saturating at 6 (the quantizers' rule)
+// but keeps the sign of a negative value that rounds to zero; clear the sign bit of every
+// nibble whose magnitude is 0.
+__device__ __forceinline__ uint32_t fp4_plus_zero(uint32_t w) {
+  const uint32_t mag = w & 0x77777777u;
+  const uint32_t nz = (mag | (mag >> 1) | (mag >> 2)) & 0x11111111u;
+  return mag | (w & (nz << 3));
+}
+
+// Eight values (already divided by their scale, or to be divided by the power of two s) as
+// E2M1 codes, one word, code j in bits 4j..4j+3.
+__device__ __forceinline__ uint32_t fp4_codes8(const float* t, float s) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[0], t[1], s, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[2], t[3], s, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[4], t[5], s, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[6], t[7], s, 3);
+  return fp4_plus_zero(w);
+}
+
 // Pack 8 4-bit codes (low nibble first) into one 32-bit word.
 __device__ __forceinline__ uint32_t pack8(const int* q) {
   uint32_t w = 0;
