@@ -5,16 +5,18 @@ One step = one pass of the layer's hot path over one batch: Kernel A
 (quantize + down projection; K is sliced over workgroups and a small second
 launch adds the slices' partial sums of T) then Kernel B (W4A4 GEMM + up
 projection + bias), the same launches svdq_linear makes.  The headline line is the FLUX-like
-fused QKV projection (M=4608 tokens, K=3072, N=9216, rank 32, INT4 group 64);
-the same run also times, each on its own seeded layer and with fewer steps:
-  * the FLUX-like MLP pair: fc1 (K=3072, N=12288) and fc2 (K=12288, N=3072), and fc1 on
-    its first 64, 256 and 1024 token rows (small-batch sweep, each point against the bound
+MLP's first linear fc1 (M=4608 tokens, K=3072, N=12288, rank 32, INT4 group 64), the shape
+the >= 50%-of-INT8-peak target is stated on; the same run also times, each on its own seeded
+layer and with fewer steps:
+  * the FLUX-like fused QKV projection (K=3072, N=9216) and the MLP's fc2 (K=12288,
+    N=3072), and fc1 on its first 64, 256 and 1024 token rows (small-batch sweep, each point
+    against the bound
     its arithmetic intensity puts it under: HBM below 625 op/B, MFMA above; these short
     launches are timed from HIP graph replays, so host launch cost stays out, and the eager
     per-call time is reported beside them);
   * that MLP pair end to end (fc1, GELU + fc2's smoothing, fc2), with the glue as its own
     kernel and with it (and fc1's input smoothing) folded into fc1's two kernels;
-  * on the QKV layer: the layer with a rank-16 and a rank-32 LoRA adapter carried by its
+  * on the headline layer: the layer with a rank-16 and a rank-32 LoRA adapter carried by its
     branch (rank 48 and 64, same codes), the bare W4A4 GEMM (r = 0: no branch in either kernel),
     the unfused branch (down projection, quantization, GEMM, up projection as
     separate launches with an fp16 intermediate), and the W4A16 control (fp16
@@ -34,13 +36,16 @@ average duration and the layer's 10/50/90th percentiles.  A shorter run on
 one buffer set (operands left in the MALL) gives the warm time beside it.  Prints
 one JSON line.
 
-The roofline's HBM traffic comes from the committed rocprofv3 counter summary
-of Kernel B (FETCH_SIZE and WRITE_SIZE, calibrated on a plain copy); it is
-reported only while Kernel B's source still has the hash recorded there.
+Algorithmic bytes count the method's 4-bit codes (half a byte per code); the bytes the 6-bit
+container moves beyond them are reported as their own field.  The roofline's HBM traffic comes
+from the committed rocprofv3 counter summary of Kernel B at the same workload (FETCH_SIZE and
+WRITE_SIZE, calibrated on a plain copy); it is reported only while Kernel B's sources still
+have the hash recorded there.
 `--copy-mib N` instead runs the plain copy used for that calibration.
 
-The CPU baseline times the CPU oracle (the layer's plain numpy definition) on
-the first rows of the same layer, on this host's cores.
+The CPU baseline times the CPU oracle (the layer's plain numpy definition, its GEMM in
+float64 on the exactly dequantized operands) on the first rows of the same layer, on this
+host's cores.
 """
 from __future__ import annotations
 
@@ -89,8 +94,9 @@ def settle(torch, fn, ms=None):
         torch.cuda.synchronize()
 
 
-KERNEL_B_SOURCE = os.path.join(ROOT, "bit_w4a4_quantized_amd", "csrc", "k_gemm3.hip")
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "kernel_b_qkv_4608x3072x9216_traffic.md")
+CSRC = os.path.join(ROOT, "bit_w4a4_quantized_amd", "csrc")
+KERNEL_B_SOURCES = {"int4_e2m3": ("k_gemm3.hip", "kernels.h"), "int4": ("k_gemm2.hip", "kernels.h"),
+                    "mxfp4": ("k_gemm_mx.hip", "kernels.h")}
 
 
 def parse():
@@ -98,7 +104,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="qkv")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="fc1")
     ap.add_argument("--rank", type=int, default=None, help="override r (0 = bare W4A4 GEMM)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline only: skip the other workloads "
@@ -117,26 +123,52 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(M, K, N, r, code_bits=4, G=64):
-    """HBM bytes the two kernels must move at minimum (codes at code_bits, fp16 scales / T / Y)."""
-    cb = code_bits / 8
-    ka = 2 * M * K + 2 * K * r + int(M * K * cb) + 2 * M * K // G + 2 * M * r
-    kb = (int(M * K * cb) + 2 * M * K // G + 2 * M * r + int(K * N * cb) + 2 * K * N // G + 2 * r * N + 2 * N
+# scale bytes per element of K: fp16 per 64 (INT4 g64), one E8M0 byte per 32 (MXFP4)
+SCALE_BYTES_PER_K = {"int4_e2m3": 2 / 64, "int4": 2 / 64, "mxfp4": 1 / 32}
+
+
+def algorithmic_bytes(M, K, N, r, fmt="int4"):
+    """HBM bytes the two kernels must move at minimum: the method's 4-bit codes (half a byte
+    each), the format's scales, fp16 X_hat / T / L1 / L2 / bias / Y."""
+    sb = SCALE_BYTES_PER_K[fmt]
+    ka = 2 * M * K + 2 * K * r + M * K // 2 + int(M * K * sb) + 2 * M * r
+    kb = (M * K // 2 + int(M * K * sb) + 2 * M * r + K * N // 2 + int(K * N * sb) + 2 * r * N + 2 * N
           + 2 * M * N)
     return ka, kb
 
 
-def kernel_b_traffic(fmt, workload, r):
-    """HBM bytes per Kernel B launch from the committed counter summary, if it was taken on the
-    current source of Kernel B (else None)."""
-    if fmt != "int4_e2m3" or workload != "qkv" or r != 32 or not os.path.exists(TRAFFIC_PROFILE):
+def container_bytes(M, K, N, fmt):
+    """Bytes the storage moves beyond the 4-bit codes: the 6-bit container holds each code in
+    three quarters of a byte, so Kernel A writes, and Kernel B reads, M K / 4 more bytes of
+    activation codes, and Kernel B reads N K / 4 more of weight codes."""
+    if fmt != "int4_e2m3":
+        return 0, 0
+    return M * K // 4, M * K // 4 + N * K // 4
+
+
+def kernel_sources_sha256(fmt):
+    """One SHA-256 over Kernel B's sources for this format (the files, in order)."""
+    h = hashlib.sha256()
+    for f in KERNEL_B_SOURCES.get(fmt, ()):
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
+
+
+def traffic_profile(workload, M, K, N):
+    return os.path.join(ROOT, "profiles", f"kernel_b_{workload}_{M}x{K}x{N}_traffic.md")
+
+
+def kernel_b_traffic(fmt, workload, M, K, N, r):
+    """HBM bytes per Kernel B launch from the committed counter summary of this workload, if it
+    was taken on the current sources of Kernel B (else None)."""
+    path = traffic_profile(workload, M, K, N)
+    if fmt != "int4_e2m3" or r != 32 or not os.path.exists(path):
         return None
-    m = re.search(r"traffic_json:\s*(\{.*\})", open(TRAFFIC_PROFILE).read())
+    m = re.search(r"traffic_json:\s*(\{.*\})", open(path).read())
     if not m:
         return None
     rec = json.loads(m.group(1))
-    sha = hashlib.sha256(open(KERNEL_B_SOURCE, "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != sha:
+    if rec.get("kernel_sources_sha256") != kernel_sources_sha256(fmt):
         return None
     return rec
 
@@ -172,6 +204,8 @@ def cpu_baseline(raw, host_layer, fmt, M, K, N, r, target_s):
             "sample": f"first {m} of {M} token rows of the same layer; one oracle call (quantize X, "
                       f"float64 GEMM on dequantized codes, rank-{r} branch, bias, fp16 rounding) took "
                       f"{dt:.2f} s; value = 2*m*N*K / time",
+            "gemm_precision": "float64 (the oracle as it stands: exact dequantized operands, "
+                              "numpy BLAS dgemm)",
             "seconds": round(dt, 3)}
 
 
@@ -494,6 +528,47 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
 
 
+def layer_entry(Lo, res, fmt):
+    """Per-layer timing record of a workload other than the headline."""
+    o_ops = 2.0 * Lo.M * Lo.N * Lo.K
+    o_b = o_ops + 2.0 * Lo.M * Lo.r * Lo.N
+    return {"M": Lo.M, "K": Lo.K, "N": Lo.N, "r": Lo.r,
+            "us_per_layer": round(res["us_per_layer"], 2),
+            "tops": round(o_ops / (res["us_per_layer"] * 1e-6) / 1e12, 2),
+            "pct_int8_peak": round(100.0 * o_ops / (res["us_per_layer"] * 1e-6) / 1e12 / INT8_PEAK_TOPS, 2),
+            "kernels_us": {"quantize_down": round(res["ka_us"], 2), "gemm_w4a4_up": round(res["kb_us"], 2)},
+            "kernel_b_pct_int8_peak": round(100.0 * o_b / (res["kb_us"] * 1e-6) / 1e12 / INT8_PEAK_TOPS, 2)}
+
+
+def small_batch_sweep(Lo, fmt, es, ew):
+    """fc1's shape on its first 64, 256 and 1024 token rows: where the layer moves from
+    HBM-bound to MFMA-bound (ridge 625 op/B for INT8), timed from HIP graph replays."""
+    sweep = {}
+    for m in (64, 256, 1024):
+        rs = Lo.time_rows_graph(m, 20, 3)
+        eager = Lo.time_rows(m, es, ew)
+        a_b, b_b = algorithmic_bytes(m, Lo.K, Lo.N, Lo.r, fmt)
+        c_a, c_b = container_bytes(m, Lo.K, Lo.N, fmt)
+        m_ops = 2.0 * m * Lo.N * Lo.K
+        layer_s = rs["us_per_layer"] * 1e-6
+        intensity = m_ops / (a_b + b_b)
+        bound = "hbm" if intensity < INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+        sweep[str(m)] = {
+            "timing": "HIP graph replay",
+            "us_per_layer": round(rs["us_per_layer"], 2),
+            "us_per_layer_eager_calls": round(eager["us_per_layer"], 2),
+            "kernels_us": {"quantize_down": round(rs["ka_us"], 2), "gemm_w4a4_up": round(rs["kb_us"], 2)},
+            "tops": round(m_ops / layer_s / 1e12, 2),
+            "algorithmic_bytes": a_b + b_b,
+            "container_extra_bytes": c_a + c_b,
+            "ops_per_byte": round(intensity, 1),
+            "bound": bound,
+            "frac_of_int8_peak": round(m_ops / layer_s / 1e12 / INT8_PEAK_TOPS, 4),
+            "frac_of_8TBps": round((a_b + b_b) / layer_s / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"fc1 M={m}: {sweep[str(m)]}")
+    return sweep
+
+
 def main():
     args = parse()
     global SETTLE_MS
@@ -523,11 +598,12 @@ def main():
 
     ops = 2.0 * M * N * K
     tops = ops / (ms_per_step * 1e-3) / 1e12
-    ka_bytes, kb_bytes = algorithmic_bytes(M, K, N, r, 6 if fmt == "int4_e2m3" else 4)
+    ka_bytes, kb_bytes = algorithmic_bytes(M, K, N, r, fmt)
+    ka_extra, kb_extra = container_bytes(M, K, N, fmt)
     ka_us, kb_us = head["ka_us"], head["kb_us"]
     dom_ops = ops + 2.0 * M * r * N                       # Kernel B: W4A4 GEMM + up projection
     achieved = dom_ops / (kb_us * 1e-6) / 1e12
-    traffic = kernel_b_traffic(fmt, args.workload, r)
+    traffic = kernel_b_traffic(fmt, args.workload, M, K, N, r)
     kname = {"int4_e2m3": "k_gemm3", "int4": "k_gemm2", "mxfp4": "k_gemm_mx"}[fmt]
     # a contraction is priced at its own dtype's dense peak: INT8 for the INT4 paths (their
     # integer products), FP4 for MXFP4
@@ -540,7 +616,8 @@ def main():
             "avg_launch_us": round(kb_us, 2),
             "frac_of_fp6_peak": round(achieved / FP6_PEAK_TFLOPS, 4) if fmt == "int4_e2m3" else None,
             "frac_of_int8_peak": round(achieved / INT8_PEAK_TOPS, 4),
-            "algorithmic_hbm_bytes": kb_bytes}
+            "algorithmic_hbm_bytes": kb_bytes,
+            "container_extra_hbm_bytes": kb_extra}
 
     out = {
         "metric": METRIC,
@@ -567,6 +644,7 @@ def main():
         "pct_int8_peak": round(100.0 * tops / INT8_PEAK_TOPS, 2),
         "kernels_us": {"quantize_down": round(ka_us, 2), "gemm_w4a4_up": round(kb_us, 2)},
         "kernel_a_hbm": {"algorithmic_bytes": ka_bytes,
+                         "container_extra_bytes": ka_extra,
                          "achieved_GBps": round(ka_bytes / (ka_us * 1e-6) / 1e9, 1),
                          "frac_of_8TBps": round(ka_bytes / (ka_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": roof,
@@ -597,6 +675,8 @@ def main():
         def mm(i):
             torch.matmul(xr16[i % ROTATE], wt16[i % ROTATE], out=L.sets[i % ROTATE]["y"])
         cmp_["fp16_gemm_hipblaslt_us"] = round(L.time_call(mm, es, ew)["us_per_call"], 2)
+        cmp_["speedup_fused_vs_fp16_hipblaslt"] = round(cmp_["fp16_gemm_hipblaslt_us"] / fused["us_per_layer"], 3)
+        cmp_["speedup_w4a16_control_vs_fp16_hipblaslt"] = round(cmp_["fp16_gemm_hipblaslt_us"] / w16["us_per_call"], 3)
         del xr16, wt16
         if L.r == 32:
             cmp_["lora_in_branch"] = time_lora(L, es, ew)
@@ -614,58 +694,28 @@ def main():
                                              "gemm_w4a4_up": round(res["kb_us"], 2)},
                               "kernel_b_pct_int8_peak": round(100.0 * v_b / (res["kb_us"] * 1e-6) / 1e12 / INT8_PEAK_TOPS, 2),
                               "speedup_vs_w4a16": round(w16["us_per_call"] / res["us_per_layer"], 3)}
+            if vfmt == "mxfp4":
+                variants[vfmt]["kernel_b_pct_fp4_peak"] = round(
+                    100.0 * v_b / (res["kb_us"] * 1e-6) / 1e12 / FP6_PEAK_TFLOPS, 2)
             log(f"variant {vfmt}: {variants[vfmt]}")
             del Lv
             torch.cuda.empty_cache()
         out["formats_" + args.workload] = variants
         others = {}
-        mlp = {}
-        for name in ("fc1", "fc2"):
-            if name == args.workload:
+        layers = {args.workload: L} if args.rank is None else {}
+        for name in ("fc1", "qkv", "fc2"):
+            if name == args.workload and args.rank is None:
                 continue
             Lo = Layer(torch, binding, name, fmt)
-            mlp[name] = Lo
-            res = Lo.time_fused(es, ew)
-            o_ops = 2.0 * Lo.M * Lo.N * Lo.K
-            o_b = o_ops + 2.0 * Lo.M * Lo.r * Lo.N
-            others[name] = {"M": Lo.M, "K": Lo.K, "N": Lo.N, "r": Lo.r,
-                            "us_per_layer": round(res["us_per_layer"], 2),
-                            "tops": round(o_ops / (res["us_per_layer"] * 1e-6) / 1e12, 2),
-                            "pct_int8_peak": round(100.0 * o_ops / (res["us_per_layer"] * 1e-6) / 1e12 / INT8_PEAK_TOPS, 2),
-                            "kernels_us": {"quantize_down": round(res["ka_us"], 2), "gemm_w4a4_up": round(res["kb_us"], 2)},
-                            "kernel_b_pct_int8_peak": round(100.0 * o_b / (res["kb_us"] * 1e-6) / 1e12 / INT8_PEAK_TOPS, 2)}
+            layers[name] = Lo
+            others[name] = layer_entry(Lo, Lo.time_fused(es, ew), fmt)
             log(f"{name}: {others[name]}")
-            if name == "fc1":
-                # small-batch sweep: where the layer moves from HBM-bound to MFMA-bound
-                sweep = {}
-                for m in (64, 256, 1024):
-                    rs = Lo.time_rows_graph(m, 20, 3)
-                    eager = Lo.time_rows(m, es, ew)
-                    a_b, b_b = algorithmic_bytes(m, Lo.K, Lo.N, Lo.r, 6 if fmt == "int4_e2m3" else 4)
-                    m_ops = 2.0 * m * Lo.N * Lo.K
-                    layer_s = rs["us_per_layer"] * 1e-6
-                    intensity = m_ops / (a_b + b_b)
-                    bound = "hbm" if intensity < INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
-                    sweep[str(m)] = {
-                        "timing": "HIP graph replay",
-                        "us_per_layer": round(rs["us_per_layer"], 2),
-                        "us_per_layer_eager_calls": round(eager["us_per_layer"], 2),
-                        "kernels_us": {"quantize_down": round(rs["ka_us"], 2), "gemm_w4a4_up": round(rs["kb_us"], 2)},
-                        "tops": round(m_ops / layer_s / 1e12, 2),
-                        "algorithmic_bytes": a_b + b_b,
-                        "ops_per_byte": round(intensity, 1),
-                        "bound": bound,
-                        "frac_of_int8_peak": round(m_ops / layer_s / 1e12 / INT8_PEAK_TOPS, 4),
-                        "frac_of_8TBps": round((a_b + b_b) / layer_s / 1e9 / HBM_PEAK_GBS, 4)}
-                    log(f"fc1 M={m}: {sweep[str(m)]}")
-                out["small_batch_fc1"] = sweep
-            del Lo
         out["other_workloads"] = others
-        if len(mlp) == 2:
-            pair = time_mlp_pair(mlp["fc1"], mlp["fc2"], es, ew)
-            log(f"mlp pair: {pair}")
-            out["mlp_pair_fc1_fc2"] = pair
-        del mlp
+        out["small_batch_fc1"] = small_batch_sweep(layers["fc1"], fmt, es, ew)
+        pair = time_mlp_pair(layers["fc1"], layers["fc2"], es, ew)
+        log(f"mlp pair: {pair}")
+        out["mlp_pair_fc1_fc2"] = pair
+        del layers
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:

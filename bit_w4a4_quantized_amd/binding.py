@@ -9,6 +9,7 @@ run when the library is missing.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional
 
@@ -44,6 +45,7 @@ _SIGS = {
                                                _c_int, _c_int, _vp, _vp]),
     "svdq_linear_folded": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     _vp, _c_size, _vp, _vp]),
+    "svdq_relayout": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "svdq_status_string": (ctypes.c_char_p, [_c_int]),
     "svdq_version": (ctypes.c_char_p, []),
 }
@@ -98,12 +100,14 @@ def _check(name: str, st: int):
 
 
 def _need(t, dtype, shape, what):
-    import torch
+    """A device tensor of this dtype and shape (None: any), contiguous; else ValueError.  The
+    C ABI sees only pointers, so a wrong size would become an out-of-bounds device access:
+    every tensor argument is checked here, before any launch."""
     if t is None:
         raise ValueError(f"{what} is required")
     if not t.is_cuda:
         raise ValueError(f"{what} must be a device tensor")
-    if dtype is not None and t.dtype != dtype:
+    if dtype is not None and t.dtype != dtype and not (isinstance(dtype, tuple) and t.dtype in dtype):
         raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{what} must have shape {tuple(shape)}, got {tuple(t.shape)}")
@@ -112,11 +116,73 @@ def _need(t, dtype, shape, what):
     return t
 
 
+def _bytes_dtypes():
+    """Code tensors are bytes: uint8, or int8 (e.g. INT8 codes as they were computed)."""
+    import torch
+    return (torch.uint8, torch.int8)
+
+
+def _absent(t, what, why):
+    if t is not None:
+        raise ValueError(f"{what} must be None {why}")
+
+
+def _check_kernel_b(xq, xs, t, wq, ws, l2, bias, K, fmt, y, lam_next=None):
+    """Shapes of Kernel B's operands: (M, N, r).  r comes from l2 and must match t."""
+    import torch
+    if xq is None or wq is None:
+        raise ValueError("xq and wq are required")
+    M, N = code_rows(xq), code_rows(wq)
+    r = 0 if l2 is None else int(l2.shape[0])
+    f16 = torch.float16
+    _need(xq, _bytes_dtypes(), code_shape(M, K, fmt), "xq")
+    _need(xs, scale_dtype(fmt), scale_shape(M, K, fmt), "xs")
+    _need(wq, _bytes_dtypes(), code_shape(N, K, fmt), "wq")
+    _need(ws, scale_dtype(fmt), scale_shape(N, K, fmt), "ws")
+    if r:
+        _need(l2, f16, (r, N), "l2")
+        _need(t, f16, (M, r), "t")
+    else:
+        _absent(t, "t", "when l2 is None (no branch)")
+    if bias is not None:
+        _need(bias, f16, (N,), "bias")
+    if y is not None:
+        _need(y, f16, (M, N), "y")
+    if lam_next is not None:
+        _need(lam_next, torch.float32, (N,), "lam_next")
+    return M, N, r
+
+
+def _check_weight(wq, ws, K, fmt):
+    import torch
+    if wq is None:
+        raise ValueError("wq is required")
+    N = code_rows(wq)
+    _need(wq, _bytes_dtypes(), code_shape(N, K, fmt), "wq")
+    _need(ws, scale_dtype(fmt), scale_shape(N, K, fmt), "ws")
+    return N
+
+
+def _check_branch(l1t, l2, K, N):
+    """r from l1t [r, K] and l2 [r, N]: both present or both None."""
+    import torch
+    if (l1t is None) != (l2 is None):
+        raise ValueError("l1t and l2 must both be given or both be None")
+    if l1t is None:
+        return 0
+    r = int(l1t.shape[0])
+    _need(l1t, torch.float16, (r, K), "l1t")
+    _need(l2, torch.float16, (r, N), "l2")
+    return r
+
+
 # ------------------------------------------------------------------ sizes
+@functools.lru_cache(maxsize=1024)
 def code_row_bytes(K: int, fmt) -> int:
     return int(lib().svdq_code_row_bytes(K, _fmt(fmt)))
 
 
+@functools.lru_cache(maxsize=4096)
 def code_shape(rows: int, K: int, fmt):
     """Shape of a code tensor: row-major [rows, K/2] for packed INT4; chunk-major
     [K/64, rows, bytes per 64-K chunk] otherwise (48 for the E2M3 container, 64 for INT8, 32
@@ -137,6 +203,7 @@ def scale_row_entries(K: int, fmt) -> int:
     return K // GROUP[name]
 
 
+@functools.lru_cache(maxsize=4096)
 def scale_shape(rows: int, K: int, fmt):
     """Shape of the scale tensor: row-major [rows, K/64] for packed INT4; group-major
     [K/64, rows] for the E2M3 container and INT8; chunk-major [K/64, rows, 4] (FP4) or
@@ -154,17 +221,53 @@ def scale_dtype(fmt):
     return torch.uint8 if _fmt(fmt) in (2, 4) else torch.float16   # E4M3 / E8M0 bytes
 
 
+@functools.lru_cache(maxsize=4096)
 def linear_workspace_bytes(M: int, K: int, r: int, fmt) -> int:
     return int(lib().svdq_linear_workspace_bytes(M, K, r, _fmt(fmt)))
 
 
+@functools.lru_cache(maxsize=4096)
 def linear_unfused_workspace_bytes(M: int, N: int, K: int, r: int, fmt) -> int:
     return int(lib().svdq_linear_unfused_workspace_bytes(M, N, K, r, _fmt(fmt)))
 
 
 # ------------------------------------------------------------------ entry points (same names as the C ABI)
+@functools.lru_cache(maxsize=4096)
 def quantize_down_workspace_bytes(M: int, K: int, r: int, fmt) -> int:
     return int(lib().svdq_quantize_down_workspace_bytes(M, K, r, _fmt(fmt)))
+
+
+def _outputs_kernel_a(M, K, r, fmt, dev, xq, xs, t):
+    """Kernel A's outputs: every given one is checked before any missing one is allocated."""
+    import torch
+    if xq is not None:
+        _need(xq, _bytes_dtypes(), code_shape(M, K, fmt), "xq")
+    if xs is not None:
+        _need(xs, scale_dtype(fmt), scale_shape(M, K, fmt), "xs")
+    if r:
+        if t is not None:
+            _need(t, torch.float16, (M, r), "t")
+    else:
+        _absent(t, "t", "when l1t is None (no branch)")
+    if xq is None:
+        xq = torch.empty(code_shape(M, K, fmt), dtype=torch.uint8, device=dev)
+    if xs is None:
+        xs = torch.empty(scale_shape(M, K, fmt), dtype=scale_dtype(fmt), device=dev)
+    if r and t is None:
+        t = torch.empty((M, r), dtype=torch.float16, device=dev)
+    return xq, xs, t
+
+
+def _workspace_kernel_a(M, K, r, fmt, dev, workspace, no_workspace):
+    import torch
+    if no_workspace:
+        return None, 0
+    if workspace is None:
+        nb = quantize_down_workspace_bytes(M, K, r, fmt)
+        workspace = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+    else:
+        _need(workspace, None, None, "workspace")
+    return workspace, (0 if workspace is None else workspace.numel() * workspace.element_size())
 
 
 def svdq_quantize_down(x_hat, l1t, fmt, xq=None, xs=None, t=None, workspace=None, no_workspace=False,
@@ -173,24 +276,14 @@ def svdq_quantize_down(x_hat, l1t, fmt, xq=None, xs=None, t=None, workspace=None
     workspace: uint8 device tensor for the sliced-K partial sums (allocated here when None);
     no_workspace=True passes NULL (K not sliced)."""
     import torch
-    M, K = x_hat.shape
-    r = 0 if l1t is None else l1t.shape[0]
     _need(x_hat, torch.float16, None, "x_hat")
+    M, K = x_hat.shape
+    r = 0 if l1t is None else int(l1t.shape[0])
     if l1t is not None:
         _need(l1t, torch.float16, (r, K), "l1t")
     dev = x_hat.device
-    if xq is None:
-        xq = torch.empty(code_shape(M, K, fmt), dtype=torch.uint8, device=dev)
-    if xs is None:
-        xs = torch.empty(scale_shape(M, K, fmt), dtype=scale_dtype(fmt), device=dev)
-    if r and t is None:
-        t = torch.empty((M, r), dtype=torch.float16, device=dev)
-    if no_workspace:
-        workspace = None
-    elif workspace is None:
-        nb = quantize_down_workspace_bytes(M, K, r, fmt)
-        workspace = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    xq, xs, t = _outputs_kernel_a(M, K, r, fmt, dev, xq, xs, t)
+    workspace, ws_bytes = _workspace_kernel_a(M, K, r, fmt, dev, workspace, no_workspace)
     _check("svdq_quantize_down", lib().svdq_quantize_down(
         _p(x_hat), _p(l1t), M, K, r, _fmt(fmt), _p(xq), _p(xs), _p(t), _p(workspace), ws_bytes,
         _stream(stream)))
@@ -200,9 +293,7 @@ def svdq_quantize_down(x_hat, l1t, fmt, xq=None, xs=None, t=None, workspace=None
 def svdq_gemm_w4a4_up(xq, xs, t, wq, ws, l2, bias, K, fmt, y=None, stream=None):
     """Kernel B.  Returns y fp16 [M, N]."""
     import torch
-    M = code_rows(xq)
-    N = code_rows(wq)
-    r = 0 if l2 is None else l2.shape[0]
+    M, N, r = _check_kernel_b(xq, xs, t, wq, ws, l2, bias, K, fmt, y)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float16, device=xq.device)
     _check("svdq_gemm_w4a4_up", lib().svdq_gemm_w4a4_up(
@@ -210,32 +301,58 @@ def svdq_gemm_w4a4_up(xq, xs, t, wq, ws, l2, bias, K, fmt, y=None, stream=None):
     return y
 
 
+def _layer_args(x, l1t, wq, ws, l2, bias, fmt, y, workspace, need_fn, what="x_hat"):
+    """Checks of a whole-layer call's tensors; returns (M, N, K, r, y, workspace, bytes)."""
+    import torch
+    _need(x, torch.float16, None, what)
+    M, K = x.shape
+    N = _check_weight(wq, ws, K, fmt)
+    r = _check_branch(l1t, l2, K, N)
+    if bias is not None:
+        _need(bias, torch.float16, (N,), "bias")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(y, torch.float16, (M, N), "y")
+    need = need_fn(M, N, K, r)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    else:
+        _need(workspace, None, None, "workspace")
+    return M, N, K, r, y, workspace, workspace.numel() * workspace.element_size()
+
+
 def svdq_linear(x_hat, l1t, wq, ws, l2, bias, fmt, workspace=None, y=None, stream=None):
     """Kernel A then Kernel B.  Returns y fp16 [M, N]."""
-    import torch
-    M, K = x_hat.shape
-    N = code_rows(wq)
-    r = 0 if l1t is None else l1t.shape[0]
-    need = linear_workspace_bytes(M, K, r, fmt)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x_hat.device)
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.float16, device=x_hat.device)
+    M, N, K, r, y, workspace, wb = _layer_args(x_hat, l1t, wq, ws, l2, bias, fmt, y, workspace,
+                                               lambda M, N, K, r: linear_workspace_bytes(M, K, r, fmt))
     _check("svdq_linear", lib().svdq_linear(
         _p(x_hat), _p(l1t), _p(wq), _p(ws), _p(l2), _p(bias), M, N, K, r, _fmt(fmt),
-        _p(workspace), workspace.numel() * workspace.element_size(), _p(y), _stream(stream)))
+        _p(workspace), wb, _p(y), _stream(stream)))
     return y
+
+
+def _outputs_weight(N, K, fmt, dev, wq, ws):
+    """The weight quantizer's outputs: every given one is checked before any missing one is
+    allocated."""
+    import torch
+    if wq is not None:
+        _need(wq, _bytes_dtypes(), code_shape(N, K, fmt), "wq")
+    if ws is not None:
+        _need(ws, scale_dtype(fmt), scale_shape(N, K, fmt), "ws")
+    if wq is None:
+        wq = torch.empty(code_shape(N, K, fmt), dtype=torch.uint8, device=dev)
+    if ws is None:
+        ws = torch.empty(scale_shape(N, K, fmt), dtype=scale_dtype(fmt), device=dev)
+    return wq, ws
 
 
 def svdq_quantize_weight(r_t, fmt, wq=None, ws=None, stream=None):
     """Offline: R^T fp32 [N, K] -> (wq, ws)."""
     import torch
-    N, K = r_t.shape
     _need(r_t, torch.float32, None, "r_t")
-    if wq is None:
-        wq = torch.empty(code_shape(N, K, fmt), dtype=torch.uint8, device=r_t.device)
-    if ws is None:
-        ws = torch.empty(scale_shape(N, K, fmt), dtype=scale_dtype(fmt), device=r_t.device)
+    N, K = r_t.shape
+    wq, ws = _outputs_weight(N, K, fmt, r_t.device, wq, ws)
     _check("svdq_quantize_weight", lib().svdq_quantize_weight(
         _p(r_t), N, K, _fmt(fmt), _p(wq), _p(ws), _stream(stream)))
     return wq, ws
@@ -245,13 +362,10 @@ def svdq_pack_weight(codes, scales, fmt, wq=None, ws=None, stream=None):
     """Codes int8 [N, K] and fp16 scales [N, K/64] computed elsewhere (e.g. GPTQ) -> (wq, ws) in
     the layouts Kernel B reads (INT formats)."""
     import torch
-    N, K = codes.shape
     _need(codes, torch.int8, None, "codes")
+    N, K = codes.shape
     _need(scales, torch.float16, (N, K // 64), "scales")
-    if wq is None:
-        wq = torch.empty(code_shape(N, K, fmt), dtype=torch.uint8, device=codes.device)
-    if ws is None:
-        ws = torch.empty(scale_shape(N, K, fmt), dtype=scale_dtype(fmt), device=codes.device)
+    wq, ws = _outputs_weight(N, K, fmt, codes.device, wq, ws)
     _check("svdq_pack_weight", lib().svdq_pack_weight(_p(codes), _p(scales), N, K, _fmt(fmt), _p(wq), _p(ws),
                                                       _stream(stream)))
     return wq, ws
@@ -259,28 +373,27 @@ def svdq_pack_weight(codes, scales, fmt, wq=None, ws=None, stream=None):
 
 def svdq_linear_unfused(x_hat, l1t, wq, ws, l2, bias, fmt, workspace=None, y=None, stream=None):
     """The branch as separate kernels (measurement only).  Returns y fp16 [M, N]."""
-    import torch
-    M, K = x_hat.shape
-    N = code_rows(wq)
-    r = 0 if l1t is None else l1t.shape[0]
-    need = linear_unfused_workspace_bytes(M, N, K, r, fmt)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x_hat.device)
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.float16, device=x_hat.device)
+    M, N, K, r, y, workspace, wb = _layer_args(
+        x_hat, l1t, wq, ws, l2, bias, fmt, y, workspace,
+        lambda M, N, K, r: linear_unfused_workspace_bytes(M, N, K, r, fmt))
     _check("svdq_linear_unfused", lib().svdq_linear_unfused(
         _p(x_hat), _p(l1t), _p(wq), _p(ws), _p(l2), _p(bias), M, N, K, r, _fmt(fmt),
-        _p(workspace), workspace.numel() * workspace.element_size(), _p(y), _stream(stream)))
+        _p(workspace), wb, _p(y), _stream(stream)))
     return y
 
 
 def svdq_gemm_w4a16(x, wq, ws, bias, y=None, stream=None):
     """W4A16 control.  x fp16 [M, K]; wq uint8 [N, K/2]; ws fp16 [N, K/64]."""
     import torch
+    _need(x, torch.float16, None, "x")
     M, K = x.shape
-    N = code_rows(wq)
+    N = _check_weight(wq, ws, K, "int4")
+    if bias is not None:
+        _need(bias, torch.float16, (N,), "bias")
     if y is None:
         y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(y, torch.float16, (M, N), "y")
     _check("svdq_gemm_w4a16", lib().svdq_gemm_w4a16(
         _p(x), _p(wq), _p(ws), _p(bias), M, N, K, _p(y), _stream(stream)))
     return y
@@ -289,9 +402,13 @@ def svdq_gemm_w4a16(x, wq, ws, bias, y=None, stream=None):
 def svdq_gelu_tanh_smooth(y, lam, out=None, stream=None):
     """fp16(gelu_tanh(y) / lam) for y fp16 [M, C], lam fp32 [C]."""
     import torch
+    _need(y, torch.float16, None, "y")
     M, C = y.shape
+    _need(lam, torch.float32, (C,), "lam")
     if out is None:
         out = torch.empty_like(y)
+    else:
+        _need(out, torch.float16, (M, C), "out")
     _check("svdq_gelu_tanh_smooth", lib().svdq_gelu_tanh_smooth(
         _p(y), _p(lam), M, C, _p(out), _stream(stream)))
     return out
@@ -303,25 +420,15 @@ def svdq_quantize_down_smooth(x, lam, l1t, fmt, xq=None, xs=None, t=None, worksp
     the codes, scales and T of X_hat = fp16(x / lam).  Returns (xq, xs, t).  Workspace as
     for svdq_quantize_down."""
     import torch
-    M, K = x.shape
-    r = 0 if l1t is None else l1t.shape[0]
     _need(x, torch.float16, None, "x")
+    M, K = x.shape
+    r = 0 if l1t is None else int(l1t.shape[0])
     _need(lam, torch.float32, (K,), "lam")
     if l1t is not None:
         _need(l1t, torch.float16, (r, K), "l1t")
     dev = x.device
-    if xq is None:
-        xq = torch.empty(code_shape(M, K, fmt), dtype=torch.uint8, device=dev)
-    if xs is None:
-        xs = torch.empty(scale_shape(M, K, fmt), dtype=scale_dtype(fmt), device=dev)
-    if r and t is None:
-        t = torch.empty((M, r), dtype=torch.float16, device=dev)
-    if no_workspace:
-        workspace = None
-    elif workspace is None:
-        nb = quantize_down_workspace_bytes(M, K, r, fmt)
-        workspace = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    xq, xs, t = _outputs_kernel_a(M, K, r, fmt, dev, xq, xs, t)
+    workspace, ws_bytes = _workspace_kernel_a(M, K, r, fmt, dev, workspace, no_workspace)
     _check("svdq_quantize_down_smooth", lib().svdq_quantize_down_smooth(
         _p(x), _p(lam), _p(l1t), M, K, r, _fmt(fmt), _p(xq), _p(xs), _p(t), _p(workspace), ws_bytes,
         _stream(stream)))
@@ -331,10 +438,9 @@ def svdq_quantize_down_smooth(x, lam, l1t, fmt, xq=None, xs=None, t=None, worksp
 def svdq_gemm_w4a4_up_gelu_smooth(xq, xs, t, wq, ws, l2, bias, lam_next, K, fmt, y=None, stream=None):
     """Kernel B with an MLP's glue in its epilogue: fp16(gelu(Y) / lam_next), lam_next fp32 [N]."""
     import torch
-    M = code_rows(xq)
-    N = code_rows(wq)
-    r = 0 if l2 is None else l2.shape[0]
-    _need(lam_next, torch.float32, (N,), "lam_next")
+    if lam_next is None:
+        raise ValueError("lam_next is required")
+    M, N, r = _check_kernel_b(xq, xs, t, wq, ws, l2, bias, K, fmt, y, lam_next)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float16, device=xq.device)
     _check("svdq_gemm_w4a4_up_gelu_smooth", lib().svdq_gemm_w4a4_up_gelu_smooth(
@@ -347,19 +453,53 @@ def svdq_linear_folded(x, lam_in, l1t, wq, ws, l2, bias, lam_next, fmt, workspac
     """The layer with either fold: lam_in fp32 [K] (x unsmoothed) and/or lam_next fp32 [N]
     (output fp16(gelu(Y) / lam_next)); None for a fold not taken.  Returns y fp16 [M, N]."""
     import torch
-    M, K = x.shape
-    N = code_rows(wq)
-    r = 0 if l1t is None else l1t.shape[0]
+    M, N, K, r, y, workspace, wb = _layer_args(x, l1t, wq, ws, l2, bias, fmt, y, workspace,
+                                               lambda M, N, K, r: linear_workspace_bytes(M, K, r, fmt), "x")
     if lam_in is not None:
         _need(lam_in, torch.float32, (K,), "lam_in")
     if lam_next is not None:
         _need(lam_next, torch.float32, (N,), "lam_next")
-    need = linear_workspace_bytes(M, K, r, fmt)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
     _check("svdq_linear_folded", lib().svdq_linear_folded(
         _p(x), _p(lam_in), _p(l1t), _p(wq), _p(ws), _p(l2), _p(bias), _p(lam_next), M, N, K, r, _fmt(fmt),
-        _p(workspace), workspace.numel() * workspace.element_size(), _p(y), _stream(stream)))
+        _p(workspace), wb, _p(y), _stream(stream)))
     return y
+
+
+def canonical_code_shape(rows: int, K: int, fmt):
+    """Exchange layout of codes: [rows, K] for INT8, [rows, K/2] (two 4-bit codes a byte) otherwise."""
+    return (rows, K if _fmt(fmt) == FORMATS["int8"] else K // 2)
+
+
+def canonical_scale_shape(rows: int, K: int, fmt):
+    name = fmt if isinstance(fmt, str) else FMT_NAMES[int(fmt)]
+    return (rows, K // GROUP[name])
+
+
+def svdq_relayout(codes, scales, K, fmt, to_canonical, codes_out=None, scales_out=None, stream=None):
+    """Codes and scales between the exchange layout (row-major, see canonical_code_shape) and the
+    format's device layout.  to_canonical=True: device -> exchange.  Returns (codes, scales)."""
+    import torch
+    if codes is None:
+        raise ValueError("codes is required")
+    if to_canonical:
+        rows = code_rows(codes)
+        src_c, src_s = code_shape(rows, K, fmt), scale_shape(rows, K, fmt)
+        dst_c, dst_s = canonical_code_shape(rows, K, fmt), canonical_scale_shape(rows, K, fmt)
+    else:
+        rows = int(codes.shape[0])
+        src_c, src_s = canonical_code_shape(rows, K, fmt), canonical_scale_shape(rows, K, fmt)
+        dst_c, dst_s = code_shape(rows, K, fmt), scale_shape(rows, K, fmt)
+    _need(codes, _bytes_dtypes(), src_c, "codes")
+    _need(scales, scale_dtype(fmt), src_s, "scales")
+    if codes_out is not None:
+        _need(codes_out, _bytes_dtypes(), dst_c, "codes_out")
+    if scales_out is not None:
+        _need(scales_out, scale_dtype(fmt), dst_s, "scales_out")
+    if codes_out is None:
+        codes_out = torch.empty(dst_c, dtype=torch.uint8, device=codes.device)
+    if scales_out is None:
+        scales_out = torch.empty(dst_s, dtype=scale_dtype(fmt), device=codes.device)
+    _check("svdq_relayout", lib().svdq_relayout(_p(codes), _p(scales), rows, K, _fmt(fmt), 1 if to_canonical else 0,
+                                                _p(codes_out), _p(scales_out), _stream(stream)))
+    return codes_out, scales_out
+

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsvdq.so")
 SOURCES = ["svdq_api.hip", "k_quant_down.hip", "k_quant_weight.hip", "k_gemm.hip", "k_gemm2.hip",
-           "k_gemm3.hip", "k_gemm_i8.hip", "k_gemm_f4.hip", "k_gemm_mx.hip", "k_w4a16.hip", "k_misc.hip"]
+           "k_gemm3.hip", "k_gemm_i8.hip", "k_gemm_f4.hip", "k_gemm_mx.hip", "k_w4a16.hip", "k_misc.hip", "k_relayout.hip"]
 # -amdgpu-mfma-vgpr-form: MFMA results in VGPRs, so the per-group rescale reads
 # them without v_accvgpr_read copies.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

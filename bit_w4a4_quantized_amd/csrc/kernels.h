@@ -114,6 +114,10 @@ hipError_t launch_quant_weight(const float* r_t, int N, int K, int fmt, void* wq
 hipError_t launch_pack_weight(const int8_t* codes, const uint16_t* scales, int N, int K, int fmt, void* wq,
                               void* ws, hipStream_t s);
 
+// codes and scales between the exchange layout (row-major) and the device layouts
+hipError_t launch_relayout(const void* codes_in, const void* scales_in, int rows, int K, int fmt, bool to_canonical,
+                           void* codes_out, void* scales_out, hipStream_t s);
+
 // unfused comparison pieces
 hipError_t launch_quant_only(const void* x, int M, int K, int fmt, void* xq, void* xs, hipStream_t s);
 hipError_t launch_down_only(const void* x, const void* l1t, int M, int K, int r, void* t, void* part,

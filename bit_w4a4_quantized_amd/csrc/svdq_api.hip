@@ -6,6 +6,7 @@
 
 using namespace svdq;
 
+
 namespace {
 
 constexpr int kMaxDim = 1 << 24;
@@ -94,6 +95,21 @@ svdq_status check_gemm(const void* xq, const void* xs, const void* t, const void
   return SVDQ_OK;
 }
 
+// svdq_linear's work once the workspace is known: checks of the carved buffers, Kernel A, Kernel B.
+svdq_status run_linear(const void* x_hat, const void* l1t, const void* wq, const void* ws, const void* l2,
+                       const void* bias, int M, int N, int K, int r, int fmt, const Workspace& w, void* y,
+                       hipStream_t s) {
+  svdq_status st = check_quant_down(x_hat, l1t, M, K, r, fmt, w.xq, w.xs, w.t);
+  if (st != SVDQ_OK) return st;
+  st = check_gemm(w.xq, w.xs, w.t, wq, ws, l2, bias, M, N, K, r, fmt, y);
+  if (st != SVDQ_OK) return st;
+  QuantDownArgs qa{x_hat, l1t, M, K, r, fmt, w.xq, w.xs, w.t, w.part, w.part_bytes};
+  st = map_launch(launch_quant_down(qa, s));
+  if (st != SVDQ_OK) return st;
+  GemmArgs ga{w.xq, w.xs, w.t, wq, ws, l2, bias, M, N, K, r, fmt, y};
+  return map_launch(launch_gemm(ga, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -156,17 +172,7 @@ svdq_status svdq_linear(const void* x_hat, const void* l1t, const void* wq, cons
   if (!aligned16(workspace)) return SVDQ_ERR_ALIGN;
   const Workspace w = carve(workspace, M, N, K, r, fmt, false);
   if (workspace_bytes < w.total) return SVDQ_ERR_WORKSPACE;
-  st = check_quant_down(x_hat, l1t, M, K, r, fmt, w.xq, w.xs, w.t);
-  if (st != SVDQ_OK) return st;
-  st = check_gemm(w.xq, w.xs, w.t, wq, ws, l2, bias, M, N, K, r, fmt, y);
-  if (st != SVDQ_OK) return st;
-  if (M == 0 || N == 0) return SVDQ_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  QuantDownArgs qa{x_hat, l1t, M, K, r, (int)fmt, w.xq, w.xs, w.t, w.part, w.part_bytes};
-  st = map_launch(launch_quant_down(qa, s));
-  if (st != SVDQ_OK) return st;
-  GemmArgs ga{w.xq, w.xs, w.t, wq, ws, l2, bias, M, N, K, r, (int)fmt, y};
-  return map_launch(launch_gemm(ga, s));
+  return run_linear(x_hat, l1t, wq, ws, l2, bias, M, N, K, r, (int)fmt, w, y, static_cast<hipStream_t>(stream));
 }
 
 svdq_status svdq_quantize_down_smooth(const void* x, const float* lambda, const void* l1t, int M, int K, int r,
@@ -235,6 +241,19 @@ svdq_status svdq_pack_weight(const int8_t* codes, const void* scales, int N, int
   if (!aligned16(codes) || !aligned16(scales) || !aligned16(wq) || !aligned16(ws)) return SVDQ_ERR_ALIGN;
   return map_launch(launch_pack_weight(codes, static_cast<const uint16_t*>(scales), N, K, (int)fmt, wq, ws,
                                        static_cast<hipStream_t>(stream)));
+}
+
+svdq_status svdq_relayout(const void* codes_in, const void* scales_in, int rows, int K, svdq_format fmt,
+                          int to_canonical, void* codes_out, void* scales_out, void* stream) {
+  if (!fmt_ok(fmt)) return SVDQ_ERR_FORMAT;
+  if (rows < 0 || K <= 0 || K % 64 != 0 || rows > kMaxDim || K > kMaxDim) return SVDQ_ERR_SHAPE;
+  if (to_canonical != 0 && to_canonical != 1) return SVDQ_ERR_SHAPE;
+  if (rows == 0) return SVDQ_OK;
+  if (!codes_in || !scales_in || !codes_out || !scales_out) return SVDQ_ERR_NULL;
+  if (!aligned16(codes_in) || !aligned16(scales_in) || !aligned16(codes_out) || !aligned16(scales_out))
+    return SVDQ_ERR_ALIGN;
+  return map_launch(launch_relayout(codes_in, scales_in, rows, K, (int)fmt, to_canonical != 0, codes_out, scales_out,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 svdq_status svdq_quantize_weight(const float* r_t, int N, int K, svdq_format fmt, void* wq, void* ws,

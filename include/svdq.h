@@ -215,6 +215,30 @@ svdq_status svdq_quantize_weight(const float* r_t, int N, int K, svdq_format fmt
 svdq_status svdq_pack_weight(const int8_t* codes, const void* scales, int N, int K, svdq_format fmt,
                              void* wq, void* ws, void* stream);
 
+/*
+ * Codes and scales between the exchange layout and the layout of the format's kernels
+ * (the exchange layout is the one the bit-exact comparisons with a plain implementation of
+ * the quantizers are stated in; "sota-314", "Do this": INT4 group 64 with 16-bit scales,
+ * NVFP4 group 16 with FP8 scales, rank 16 at 8 bits -- the formats fix codes and scales, not
+ * a memory order).
+ *   Exchange layout: row-major, K contiguous per row (token, or output column of a weight):
+ *     codes  [rows, K/2] for the 4-bit formats (two codes a byte, code 2b in the low nibble;
+ *            two's-complement INT4 for SVDQ_INT4_G64 and SVDQ_INT4_G64_E2M3, E2M1 nibbles for
+ *            SVDQ_FP4_G16 and SVDQ_MXFP4_G32) or [rows, K] for SVDQ_INT8_G64;
+ *     scales [rows, K/G]: fp16 (INT formats), E4M3 bytes (SVDQ_FP4_G16), E8M0 bytes
+ *            (SVDQ_MXFP4_G32).
+ *   Device layout: the format's layout above (chunk- or group-major; for SVDQ_INT4_G64 it is
+ *   the exchange layout itself, and the call copies).  SVDQ_INT4_G64_E2M3's INT4 codes are
+ *   turned into or out of their 6-bit E2M3 fields exactly; exchange codes must lie in [-7, 7].
+ *   to_canonical : 1 = device -> exchange, 0 = exchange -> device.
+ *   codes_in, scales_in : the source layout; codes_out, scales_out : the destination layout
+ *   (caller-allocated, svdq_code_row_bytes(K, SVDQ_INT4_G64 or fmt) and
+ *   svdq_scale_row_bytes(K, fmt) bytes a row; may not alias the sources).
+ *   rows >= 0 (any count), K % 64 == 0.  Offline / exchange work, not on the layer's path.
+ */
+svdq_status svdq_relayout(const void* codes_in, const void* scales_in, int rows, int K, svdq_format fmt,
+                          int to_canonical, void* codes_out, void* scales_out, void* stream);
+
 /* Workspace of the unfused comparison: svdq_linear's workspace plus an fp16
  * [M, N] intermediate, 256-byte aligned. */
 size_t svdq_linear_unfused_workspace_bytes(int M, int N, int K, int r, svdq_format fmt);

@@ -54,9 +54,21 @@ def quantize(v, fmt):
     return q, s, stored
 
 
+_REF = {}
+
+
 def reference(P, fmt, x_hat=None):
-    """Oracle codes/scales/T/Y for prepared layer P (optionally another smoothed input)."""
-    x_hat = P.x_hat if x_hat is None else x_hat
+    """Oracle codes/scales/T/Y for prepared layer P (optionally another smoothed input).  On
+    the layer's own input the result is kept per (layer, format) for the process."""
+    if x_hat is None:
+        key = (id(P), fmt)
+        if key not in _REF:
+            _REF[key] = _reference(P, fmt, P.x_hat)
+        return _REF[key]
+    return _reference(P, fmt, x_hat)
+
+
+def _reference(P, fmt, x_hat):
     xq, xs, xst = quantize(x_hat, fmt)
     wq, ws, wst = quantize(P.res.T, fmt)
     t = oracle.forward.down_projection(x_hat, P.l1)

@@ -196,3 +196,29 @@ def test_pack_weight_validation():
     assert pk(N=24) == SHAPE
     assert pk(wq=MIS) == ALIGN
     assert pk(N=0) == OK
+
+
+def test_relayout_validation():
+    L = binding.lib()
+    rl = lambda ci=P, si=P, rows=16, K=64, fmt=3, d=1, co=P, so=P: L.svdq_relayout(ci, si, rows, K, fmt, d, co, so,
+                                                                                    None)
+    assert rl(ci=None) == NULL
+    assert rl(so=None) == NULL
+    assert rl(K=96) == SHAPE
+    assert rl(K=0) == SHAPE
+    assert rl(rows=-1) == SHAPE
+    assert rl(d=2) == SHAPE                    # direction is 0 or 1
+    assert rl(fmt=5) == FORMAT
+    assert rl(co=MIS) == ALIGN
+    assert rl(si=MIS) == ALIGN
+    assert rl(rows=0, ci=None, si=None, co=None, so=None) == OK
+
+
+
+def test_relayout_shapes():
+    # exchange layout: row-major codes (K/2 bytes a row, K for INT8) and [rows, K/G] scales
+    assert binding.canonical_code_shape(300, 320, "int4_e2m3") == (300, 160)
+    assert binding.canonical_code_shape(300, 320, "int8") == (300, 320)
+    assert binding.canonical_scale_shape(300, 320, "fp4") == (300, 20)
+    assert binding.canonical_scale_shape(300, 320, "mxfp4") == (300, 10)
+    assert binding.canonical_scale_shape(300, 320, "int4_e2m3") == (300, 5)

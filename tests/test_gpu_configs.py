@@ -6,6 +6,8 @@ comparison is complete, not sampled: codes and scales bit-exact on the full
 tensors, Y within 1e-3 relative Frobenius error and within the elementwise fp32
 reassociation bound.
 """
+import functools
+
 import numpy as np
 import pytest
 
@@ -118,10 +120,13 @@ def test_c2_mlp_pair():
     assert err <= TOL
 
 
+@pytest.mark.parametrize("fmt", ["int4", "int4_e2m3"])
 @pytest.mark.parametrize("m", [64, 256, 1024])
-def test_c3_small_batch(m):
+def test_c3_small_batch(m, fmt):
+    # in the 6-bit container M = 64 and 256 run the weight-streaming kernel, whose four waves
+    # each walk 12 of the 48 groups through their register ring; M = 1024 runs the tiled kernel
     P = prepared("c2_fc1", 32)
-    run_layer(P, "int4", x_hat=np.ascontiguousarray(P.x_hat[:m]))
+    run_layer(P, fmt, x_hat=np.ascontiguousarray(P.x_hat[:m]))
 
 
 def test_c3_w4a16_control():
@@ -144,15 +149,92 @@ def test_c4_int8():
     run_layer(prepared("c2_fc1", 16), "int8")
 
 
-def test_c1_unfused_and_bare():
-    P = prepared("c1_qkv", 32)
-    ref = reference(P, "int4")
-    wq, ws = binding.svdq_quantize_weight(dev(P.res.T), "int4")
-    args = (dev(P.x_hat), dev(P.l1.T), wq, ws, dev(P.l2), dev(P.bias), "int4")
+@pytest.mark.parametrize("fmt", ["int4", "int4_e2m3"])
+@pytest.mark.parametrize("name", ["c1_qkv", "c2_fc1"])
+def test_unfused_and_bare(name, fmt):
+    P = prepared(name, 32)
+    log(f"unfused and bare {name} {fmt}")
+    ref = reference(P, fmt)
+    wq, ws = binding.svdq_quantize_weight(dev(P.res.T), fmt)
+    args = (dev(P.x_hat), dev(P.l1.T), wq, ws, dev(P.l2), dev(P.bias), fmt)
     yu = host(binding.svdq_linear_unfused(*args))
     assert rel_fro(yu, ref["y"]) <= TOL
-    y0 = host(binding.svdq_linear(dev(P.x_hat), None, wq, ws, None, dev(P.bias), "int4"))
+    y0 = host(binding.svdq_linear(dev(P.x_hat), None, wq, ws, None, dev(P.bias), fmt))
     M, N = y0.shape
     ref0 = oracle.forward.linear(ref["xq"], ref["xs"], np.zeros((M, 0), np.float16), ref["wq"], ref["ws"],
-                                 np.zeros((0, N), np.float16), P.bias, "int4")
+                                 np.zeros((0, N), np.float16), P.bias, fmt)
     assert rel_fro(y0, ref0) <= TOL
+    ok, worst = within_sum_bound(y0, ref0, linear_abs_sum(ref["xq"], ref["xs"], None, ref["wq"], ref["ws"], None,
+                                                          P.bias, fmt), gemm_terms(fmt, P.x_hat.shape[1], 0))
+    assert ok, worst
+
+
+@functools.lru_cache(maxsize=None)
+def fc2_input():
+    """The oracle's fc2 input: fp16(gelu(Y1) / lambda2) of the oracle's fc1 output."""
+    P1, P2 = prepared("c2_fc1", 32), prepared("c2_fc2", 32)
+    return oracle.forward.gelu_smooth(reference(P1, "int4")["y"], P2.lam)
+
+
+def test_c2_fc2_e2m3_container():
+    # K = 12288: 192 groups, 64 stages of three in the tiled kernel
+    run_layer(prepared("c2_fc2", 32), "int4_e2m3", x_hat=fc2_input())
+
+
+@pytest.mark.parametrize("name", ["c1_qkv", "c2_fc1"])
+def test_mxfp4_full_size(name):
+    run_layer(prepared(name, 32), "mxfp4")
+
+
+def test_c2_mlp_pair_folded():
+    # the MLP pair as the benchmark times it, in the 6-bit container: fc1's Kernel A on the raw
+    # activations with fc1's smoothing folded in, fc1's Kernel B writing fc2's smoothed input,
+    # then fc2
+    fmt = "int4_e2m3"
+    P1, P2 = prepared("c2_fc1", 32), prepared("c2_fc2", 32)
+    L1 = raw_layer("c2_fc1")
+    log("GPU folded MLP pair, full size")
+    wq1, ws1 = binding.svdq_quantize_weight(dev(P1.res.T), fmt)
+    xq, xs, t = binding.svdq_quantize_down_smooth(dev(L1.x), dev(P1.lam), dev(P1.l1.T), fmt)
+    _, s_ref, st_ref = oracle.quant.quantize(P1.x_hat, fmt)
+    assert same_bytes(host(xq), dev_codes(st_ref, fmt)), "codes of the smoothed activations"
+    assert same_bytes(host(xs), dev_scales(s_ref, fmt)), "scales of the smoothed activations"
+    _, _, tp = binding.svdq_quantize_down(dev(P1.x_hat), dev(P1.l1.T), fmt)
+    assert same_bytes(host(t), host(tp)), "T from the smoothing variant equals T on the smoothed input"
+    args = (xq, xs, t, wq1, ws1, dev(P1.l2), dev(P1.bias))
+    x2 = binding.svdq_gemm_w4a4_up_gelu_smooth(*args, dev(P2.lam), P1.x_hat.shape[1], fmt)
+    glued = binding.svdq_gelu_tanh_smooth(binding.svdq_gemm_w4a4_up(*args, P1.x_hat.shape[1], fmt), dev(P2.lam))
+    x2h = host(x2)
+    assert same_bytes(x2h, host(glued)), "folded epilogue equals the glue on the plain output"
+    err = rel_fro(x2h, fc2_input())
+    log(f"  fc2 input rel_fro={err:.3e}")
+    assert err <= TOL
+    # fc2 on the GPU's own input (the oracle quantizes the same fp16 values)
+    run_layer(P2, fmt, x_hat=x2h)
+
+
+@pytest.mark.parametrize("ra", [16, 32])
+def test_lora_full_size(ra):
+    # fc1 with a LoRA adapter in the branch (rank 32 + ra = 48 or 64), the residual's codes as
+    # they are, in the 6-bit container
+    fmt = "int4_e2m3"
+    P = prepared("c2_fc1", 32)
+    K, N = P.res.shape
+    g = np.random.default_rng(5 + ra)
+    a = (g.standard_normal((K, ra)) * 0.02).astype(np.float16)
+    b = (g.standard_normal((ra, N)) * 0.02).astype(np.float16)
+    l1p, l2p = oracle.prep.lora_branch(P.l1, P.l2, P.lam, a, b, 1.0)
+    rr = l1p.shape[1]
+    log(f"GPU LoRA fc1 r={rr}")
+    ref = reference(P, fmt)
+    tref = oracle.forward.down_projection(P.x_hat, l1p)
+    yref = oracle.forward.linear(ref["xq"], ref["xs"], tref, ref["wq"], ref["ws"], l2p, P.bias, fmt)
+    wq, ws = binding.svdq_quantize_weight(dev(P.res.T), fmt)
+    y = host(binding.svdq_linear(dev(P.x_hat), dev(l1p.T), wq, ws, dev(l2p), dev(P.bias), fmt))
+    err = rel_fro(y, yref)
+    log(f"  rel_fro={err:.3e}")
+    assert err <= TOL
+    slack = branch_slack(P.x_hat, l1p, tref, l2p)
+    ok, worst = within_sum_bound(y, yref, linear_abs_sum(ref["xq"], ref["xs"], tref, ref["wq"], ref["ws"], l2p,
+                                                         P.bias, fmt), gemm_terms(fmt, K, rr), slack)
+    assert ok, worst

@@ -71,6 +71,21 @@ def dev_scales(s, fmt):
 FMTS = ["int4", "int8", "fp4", "int4_e2m3", "mxfp4"]
 
 
+def canonical(q, s, stored, fmt):
+    """The oracle's codes and scales in the exchange layout: its row-major storage, with the
+    6-bit container's INT4 codes as two's-complement nibbles."""
+    return (oracle.quant.pack_nibbles(q) if fmt == "int4_e2m3" else stored), s
+
+
+def assert_canonical(xq, xs, K, fmt, q, s, stored):
+    """The device codes and scales, turned into the exchange layout on the GPU, equal the
+    oracle's exchange bytes."""
+    cc, cs = canonical(q, s, stored, fmt)
+    gc, gs = binding.svdq_relayout(xq, xs, K, fmt, to_canonical=True)
+    assert same_bytes(host(gc), cc), "codes in the exchange layout"
+    assert same_bytes(host(gs), cs), "scales in the exchange layout"
+
+
 def draw(seed, M, K, N, r, xscale=0.7, rscale=0.05):
     g = np.random.default_rng(seed)
     x_hat = (g.standard_normal((M, K)) * xscale)
@@ -109,6 +124,7 @@ def test_quantize_down_parity(fmt, M, K, N, r, sliced):
     xq, xs, t = binding.svdq_quantize_down(dev(x_hat), dev(l1.T) if r else None, fmt, no_workspace=not sliced)
     assert same_bytes(host(xq), dev_codes(stored, fmt))
     assert same_bytes(host(xs), dev_scales(s, fmt))
+    assert_canonical(xq, xs, K, fmt, q, s, stored)
     if r:
         tr = oracle.forward.down_projection(x_hat, l1)
         tg = host(t)
@@ -142,6 +158,7 @@ def test_quantize_weight_parity(fmt, N, K):
     wq, ws = binding.svdq_quantize_weight(dev(r_t), fmt)
     assert same_bytes(host(wq), dev_codes(stored, fmt))
     assert same_bytes(host(ws), dev_scales(s, fmt))
+    assert_canonical(wq, ws, K, fmt, q, s, stored)
 
 
 def test_quantizers_subnormal_scales_and_zero_groups():
@@ -158,6 +175,25 @@ def test_quantizers_subnormal_scales_and_zero_groups():
         q2, s2, st2 = oracle.quant.quantize(x.astype(np.float32).repeat(16, axis=0)[:80], fmt)
         assert same_bytes(host(wq), dev_codes(st2, fmt)), fmt
         assert same_bytes(host(ws), dev_scales(s2, fmt)), fmt
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("rows,K", [(1, 64), (16, 320), (300, 1024)])
+def test_relayout_round_trip(fmt, rows, K):
+    # exchange -> device gives exactly what Kernel A writes; device -> exchange gives the
+    # oracle's bytes back; both directions on every format (the 6-bit container's fields are
+    # converted from and to INT4 nibbles)
+    log(f"relayout {fmt} rows={rows} K={K}")
+    g = np.random.default_rng(rows + K)
+    v = (g.standard_normal((rows, K)) * 10.0 ** g.integers(-3, 2, (rows, 1))).astype(np.float16)
+    v[:, :64][0] = 0                         # a zero group: scale 0, codes 0
+    q, s, stored = oracle.quant.quantize(v, fmt)
+    cc, cs = canonical(q, s, stored, fmt)
+    xq, xs, _ = binding.svdq_quantize_down(dev(v), None, fmt)
+    dq, ds = binding.svdq_relayout(dev(cc), dev(cs), K, fmt, to_canonical=False)
+    assert same_bytes(host(dq), host(xq)) and same_bytes(host(ds), host(xs))
+    bc, bs = binding.svdq_relayout(dq, ds, K, fmt, to_canonical=True)
+    assert same_bytes(host(bc), cc) and same_bytes(host(bs), cs)
 
 
 def _gemm_inputs(fmt, M, K, N, r, seed):
@@ -207,6 +243,47 @@ def test_gemm_partial_last_round(fmt, r, with_bias):
     assert np.isfinite(yg.astype(np.float32)).all()
     assert rel_fro(yg, ref) <= TOL
     ok, worst = within_sum_bound(yg, ref, linear_abs_sum(xq, xs, t, wq, ws, l2, bias, fmt), gemm_terms(fmt, K, r))
+    assert ok, worst
+
+
+# Long K at few rows: each wave of the weight-streaming kernel (6-bit container, M <= 256) walks
+# K/256 groups through its register ring, and the other formats' K loops run many stages, so
+# every ring wraps several times; one case per row-tile count of the streaming kernel (1, 2, 4)
+RING_SHAPES = [(17, 1024, 272, 32), (64, 3072, 272, 32), (130, 3072, 272, 32), (256, 1024, 272, 64),
+               (64, 1024, 272, 0), (300, 3072, 272, 32)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M,K,N,r", RING_SHAPES)
+def test_gemm_long_k_rings(fmt, M, K, N, r):
+    log(f"gemm_w4a4_up long K {fmt} M={M} K={K} N={N} r={r}")
+    x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs(fmt, M, K, N, r, 7 * M + K + r)
+    ref = oracle.forward.linear(xq, xs, t, wq, ws, l2, b, fmt)
+    y = binding.svdq_gemm_w4a4_up(dev(dev_codes(xst, fmt)), dev(dev_scales(xs, fmt)), dev(t) if r else None,
+                                  dev(dev_codes(wst, fmt)), dev(dev_scales(ws, fmt)), dev(l2) if r else None,
+                                  dev(b), K, fmt)
+    yg = host(y)
+    assert rel_fro(yg, ref) <= TOL
+    ok, worst = within_sum_bound(yg, ref, linear_abs_sum(xq, xs, t, wq, ws, l2, b, fmt), gemm_terms(fmt, K, r))
+    assert ok, worst
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_partial_last_round_long_k(fmt):
+    # the sub-tile jobs of a last partial round at K = 3072 (48 groups): each job's four waves
+    # walk 12 groups (6-bit container) or 12 chunks (MXFP4, FP4) through their register rings
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N, K, r = 1024, 3072, 32
+    tiles_m = -(-(2 * cus + 8) // 8)
+    M = 128 * tiles_m - 37
+    log(f"gemm_w4a4_up tail round, long K {fmt} M={M} K={K} N={N} r={r} CUs={cus}")
+    x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs(fmt, M, K, N, r, 4343)
+    ref = oracle.forward.linear(xq, xs, t, wq, ws, l2, b, fmt)
+    y = binding.svdq_gemm_w4a4_up(dev(dev_codes(xst, fmt)), dev(dev_scales(xs, fmt)), dev(t), dev(dev_codes(wst, fmt)),
+                                  dev(dev_scales(ws, fmt)), dev(l2), dev(b), K, fmt)
+    yg = host(y)
+    assert rel_fro(yg, ref) <= TOL
+    ok, worst = within_sum_bound(yg, ref, linear_abs_sum(xq, xs, t, wq, ws, l2, b, fmt), gemm_terms(fmt, K, r))
     assert ok, worst
 
 
