@@ -46,6 +46,7 @@ _SIGS = {
     "svdq_linear_folded": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     _vp, _c_size, _vp, _vp]),
     "svdq_relayout": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "svdq_linear_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
     "svdq_status_string": (ctypes.c_char_p, [_c_int]),
     "svdq_version": (ctypes.c_char_p, []),
 }
@@ -503,3 +504,25 @@ def svdq_relayout(codes, scales, K, fmt, to_canonical, codes_out=None, scales_ou
                                                 _p(codes_out), _p(scales_out), _stream(stream)))
     return codes_out, scales_out
 
+
+# svdq_linear_noalloc's static device scratch (SVDQ_STATIC_SCRATCH_BYTES in include/svdq.h)
+STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def svdq_linear_noalloc(x_hat, l1t, wq, ws, l2, bias, fmt, y, stream=None):
+    """The fused layer with its intermediates in the library's static per-device scratch: no
+    device allocation in the library, and none here either (the output y fp16 [M, N] is the
+    caller's).  Calls that overlap on one GPU race on the scratch."""
+    import torch
+    if y is None:
+        raise ValueError("y is required (this entry point allocates nothing)")
+    _need(x_hat, torch.float16, None, "x_hat")
+    M, K = x_hat.shape
+    N = _check_weight(wq, ws, K, fmt)
+    r = _check_branch(l1t, l2, K, N)
+    if bias is not None:
+        _need(bias, torch.float16, (N,), "bias")
+    _need(y, torch.float16, (M, N), "y")
+    _check("svdq_linear_noalloc", lib().svdq_linear_noalloc(
+        _p(x_hat), _p(l1t), _p(wq), _p(ws), _p(l2), _p(bias), M, N, K, r, _fmt(fmt), _p(y), _stream(stream)))
+    return y

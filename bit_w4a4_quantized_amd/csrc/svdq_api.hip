@@ -1,11 +1,19 @@
 // C-ABI layer: host-side argument validation and kernel launches for the
 // entry points declared in include/svdq.h.  Every check happens before any
 // HIP call; no exception leaves this file.
+#include <atomic>
+#include <mutex>
+
 #include "../../include/svdq.h"
 #include "kernels.h"
 
 using namespace svdq;
 
+// svdq_linear_noalloc's workspace: a static device array, one per GPU the library runs on (each
+// holds its own copy, at its own address, until the process ends).  In host code `scratch` is
+// only a stand-in for the symbol: its device address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[SVDQ_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -95,6 +103,28 @@ svdq_status check_gemm(const void* xq, const void* xs, const void* t, const void
   return SVDQ_OK;
 }
 
+// The device address of `scratch` on the current device, looked up on the first call made on
+// that device and kept: lookups are serialized by a mutex, readers take the published value.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+svdq_status static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SVDQ_ERR_DEVICE;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SVDQ_ERR_DEVICE;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SVDQ_OK;
+}
+
 // svdq_linear's work once the workspace is known: checks of the carved buffers, Kernel A, Kernel B.
 svdq_status run_linear(const void* x_hat, const void* l1t, const void* wq, const void* ws, const void* l2,
                        const void* bias, int M, int N, int K, int r, int fmt, const Workspace& w, void* y,
@@ -172,6 +202,24 @@ svdq_status svdq_linear(const void* x_hat, const void* l1t, const void* wq, cons
   if (!aligned16(workspace)) return SVDQ_ERR_ALIGN;
   const Workspace w = carve(workspace, M, N, K, r, fmt, false);
   if (workspace_bytes < w.total) return SVDQ_ERR_WORKSPACE;
+  return run_linear(x_hat, l1t, wq, ws, l2, bias, M, N, K, r, (int)fmt, w, y, static_cast<hipStream_t>(stream));
+}
+
+svdq_status svdq_linear_noalloc(const void* x_hat, const void* l1t, const void* wq, const void* ws, const void* l2,
+                                const void* bias, int M, int N, int K, int r, svdq_format fmt, void* y,
+                                void* stream) {
+  if (!fmt_ok(fmt)) return SVDQ_ERR_FORMAT;
+  svdq_status st = check_dims(M, N, K, r);
+  if (st != SVDQ_OK) return st;
+  if (M == 0 || N == 0) return SVDQ_OK;
+  if (!x_hat || !wq || !ws || !y) return SVDQ_ERR_NULL;
+  if (r > 0 && (!l1t || !l2)) return SVDQ_ERR_NULL;
+  // the whole workspace (codes, scales, T, Kernel A's partial sums) must fit the static array
+  if (carve(nullptr, M, N, K, r, fmt, false).total > (size_t)SVDQ_STATIC_SCRATCH_BYTES) return SVDQ_ERR_WORKSPACE;
+  void* base = nullptr;
+  st = static_scratch(&base);
+  if (st != SVDQ_OK) return st;
+  const Workspace w = carve(base, M, N, K, r, fmt, false);
   return run_linear(x_hat, l1t, wq, ws, l2, bias, M, N, K, r, (int)fmt, w, y, static_cast<hipStream_t>(stream));
 }
 
@@ -331,7 +379,7 @@ const char* svdq_status_string(svdq_status s) {
     case SVDQ_ERR_SHAPE: return "shape outside the supported constraints (K % 64 == 0, N % 16 == 0, r in {0,16,32,48,64}, dims <= 2^24)";
     case SVDQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case SVDQ_ERR_FORMAT: return "unknown or unsupported format";
-    case SVDQ_ERR_WORKSPACE: return "workspace too small";
+    case SVDQ_ERR_WORKSPACE: return "workspace too small (for svdq_linear_noalloc: the shape needs more than its static scratch)";
     case SVDQ_ERR_DEVICE: return "no gfx950 code object for the current device";
     case SVDQ_ERR_LAUNCH: return "kernel launch failed";
   }

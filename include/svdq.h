@@ -190,6 +190,28 @@ svdq_status svdq_linear(const void* x_hat, const void* l1t, const void* wq, cons
                         void* stream);
 
 /*
+ * The fused layer without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): svdq_linear with its codes, scales, T and Kernel A's partial sums in a static
+ * device array of SVDQ_STATIC_SCRATCH_BYTES inside the library.  Each GPU the library runs on
+ * holds its own copy of the array until the process ends; the first call on a device looks up
+ * that copy's address (hipGetSymbolAddress, with the device current) and keeps it.  The call
+ * allocates nothing (no hipMalloc / hipFree, no allocating library routine).
+ *   Limit: shapes whose svdq_linear_workspace_bytes(M, K, r, fmt) exceeds
+ *   SVDQ_STATIC_SCRATCH_BYTES return SVDQ_ERR_WORKSPACE before anything is enqueued (the FLUX
+ *   shapes, M = 4608 with K = 3072 or 12288, fit in every format).
+ *   Concurrency: every call on one GPU shares that GPU's array and its contents persist from
+ *   call to call (nothing in it needs to start at zero).  Calls that overlap on one GPU -- on
+ *   two streams, or from two host threads without ordering -- race on it and give wrong
+ *   results: order them on one stream.
+ * Other arguments, results (bit for bit those of svdq_linear) and errors as for svdq_linear.
+ */
+#define SVDQ_STATIC_SCRATCH_BYTES (64u << 20)
+svdq_status svdq_linear_noalloc(const void* x_hat, const void* l1t, const void* wq, const void* ws,
+                                const void* l2, const void* bias, int M, int N, int K, int r,
+                                svdq_format fmt, void* y, void* stream);
+
+/*
  * Offline weight quantizer: the residual R = W_hat - L1 L2, given as
  * R^T fp32 [N, K] (K contiguous per output column), to codes wq and scales ws
  * in the layouts Kernel B reads ("sota-314", "Do this": quantize only the
