@@ -65,5 +65,31 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# The C ABI's host code (argument validation, workspace carving) built with AddressSanitizer
+# and UndefinedBehaviorSanitizer for the host pass only (each -fsanitize after -Xarch_host), linked
+# with tests/abi_check.cpp: a program that drives every validation path without a GPU.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+HOST_CHECK = os.path.join(BUILD_DIR, "svdq_abi_check")
+
+
+def build_host_check(verbose: bool = False) -> str:
+    """Compile svdq_api.hip with the sanitizers (the other objects come from build()) and link
+    the ABI check program; returns its path."""
+    if not all(os.path.exists(os.path.join(BUILD_DIR, s.replace(".hip", ".o"))) for s in SOURCES):
+        build(verbose)
+    cc = hipcc()
+    api = os.path.join(BUILD_DIR, "svdq_api_sanitized.o")
+    _run([cc, *FLAGS, *SANITIZE, "-c", os.path.join(CSRC, "svdq_api.hip"), "-o", api], verbose)
+    objs = [api] + [os.path.join(BUILD_DIR, s.replace(".hip", ".o")) for s in SOURCES if s != "svdq_api.hip"]
+    check = os.path.join(os.path.dirname(HERE), "tests", "abi_check.cpp")
+    _run([cc, "--offload-arch=gfx950", *SANITIZE, "-x", "c++", check, "-x", "none", *objs, "-o", HOST_CHECK],
+         verbose)
+    return HOST_CHECK
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-check" in sys.argv:
+        print(build_host_check(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

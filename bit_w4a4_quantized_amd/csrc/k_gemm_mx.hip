@@ -18,7 +18,8 @@
 // with rows laid out along K instead, each 16-byte load would touch 32 cache lines 1.5 KB apart
 // and the staging ran at half the bandwidth.
 //
-// Stages of two 64-K chunks on the shared persistent skeleton.  Per chunk and workgroup: each
+// Stages of four 64-K chunks on the shared persistent skeleton (two chunks a stage left each
+// stage waiting on the next one's loads: 142 -> 129 us at the fc1 shape).  Per chunk and workgroup: each
 // operand's 128 rows x 32 code bytes arrive by 16-byte LDS-DMA loads into 16-byte slots
 // swapped by row (slot c of row r at c ^ ((r / 8) % 2)), and the rows' 2 scale bytes by 2-byte
 // loads into 4-byte slots.  Lane half h reads the chunk's codes 32 h .. 32 h + 31 (one
@@ -41,7 +42,7 @@ __device__ __forceinline__ v16f mx_mma(const uint4& w, const uint4& x, uint32_t 
 }
 
 struct OpMX {
-  static constexpr int KC = 2;               // 64-K chunks per stage
+  static constexpr int KC = 4;               // 64-K chunks per stage: 4 x 9 KB of operands in flight per load
   static constexpr int SUB_PD = 4;           // sub-tile jobs: units in flight per wave
   static constexpr int L_X = 0, L_W = 4096, L_SX = 8192, L_SW = 8704, CHUNK = 9216;
   static constexpr int BUF = KC * CHUNK;

@@ -117,7 +117,12 @@ typedef enum {
   SVDQ_INT8_G64 = 1,
   SVDQ_FP4_G16 = 2,
   SVDQ_INT4_G64_E2M3 = 3,
-  SVDQ_MXFP4_G32 = 4
+  SVDQ_MXFP4_G32 = 4,
+  /* Not formats: these two make the type span every int, so that any value a caller passes is
+   * a valid value of the type (in C++ an enum holds only the values its enumerators' range
+   * covers) and an unknown one is rejected with SVDQ_ERR_FORMAT. */
+  SVDQ_FORMAT_INT_MIN_ = -2147483647 - 1,
+  SVDQ_FORMAT_INT_MAX_ = 2147483647
 } svdq_format;
 
 /* Bytes of codes per row for K columns (K/2 for 4-bit formats, K for INT8,
