@@ -377,6 +377,19 @@ class Layer:
                 "ka_us": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3,
                 "kb_us": float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3}
 
+    def time_rows_prepared(self, m, steps, warmup):
+        """The fused layer on the first m token rows through the prepared-layer binding
+        (SvdqLinear: weight side checked once, one svdq_linear call per step): eager calls, host
+        launch cost included."""
+        b = self.binding
+        sets = self._row_sets(m)
+        layers = [b.SvdqLinear(st["wq"], st["ws"], st["l1t"], st["l2"], st["b"], self.K, self.fmt) for st in sets]
+
+        def one(i):
+            k = i % ROTATE
+            layers[k](sets[k]["x"], sets[k]["y"])
+        return self.time_call(one, steps, warmup)
+
     def time_call(self, fn, steps, warmup):
         torch = self.torch
         settle(torch, fn)
@@ -547,6 +560,7 @@ def small_batch_sweep(Lo, fmt, es, ew):
     for m in (64, 256, 1024):
         rs = Lo.time_rows_graph(m, 20, 3)
         eager = Lo.time_rows(m, es, ew)
+        prepared = Lo.time_rows_prepared(m, es, ew)
         a_b, b_b = algorithmic_bytes(m, Lo.K, Lo.N, Lo.r, fmt)
         c_a, c_b = container_bytes(m, Lo.K, Lo.N, fmt)
         m_ops = 2.0 * m * Lo.N * Lo.K
@@ -557,6 +571,7 @@ def small_batch_sweep(Lo, fmt, es, ew):
             "timing": "HIP graph replay",
             "us_per_layer": round(rs["us_per_layer"], 2),
             "us_per_layer_eager_calls": round(eager["us_per_layer"], 2),
+            "us_per_layer_eager_prepared_layer": round(prepared["us_per_call"], 2),
             "kernels_us": {"quantize_down": round(rs["ka_us"], 2), "gemm_w4a4_up": round(rs["kb_us"], 2)},
             "tops": round(m_ops / layer_s / 1e12, 2),
             "algorithmic_bytes": a_b + b_b,

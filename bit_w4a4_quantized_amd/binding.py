@@ -95,6 +95,16 @@ def _stream(stream) -> Optional[int]:
     return torch.cuda.current_stream().cuda_stream
 
 
+def _raw_stream_fn():
+    """A cheap reader of the current stream's handle for a device index: torch's raw-stream
+    accessor when it has one (no Stream object per call), else current_stream()."""
+    import torch
+    fn = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if fn is not None:
+        return fn
+    return lambda dev: torch.cuda.current_stream(dev).cuda_stream
+
+
 def _check(name: str, st: int):
     if st != 0:
         raise SvdqError(name, st)
@@ -110,7 +120,7 @@ def _need(t, dtype, shape, what):
         raise ValueError(f"{what} must be a device tensor")
     if dtype is not None and t.dtype != dtype and not (isinstance(dtype, tuple) and t.dtype in dtype):
         raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != tuple(shape):
         raise ValueError(f"{what} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
@@ -526,3 +536,57 @@ def svdq_linear_noalloc(x_hat, l1t, wq, ws, l2, bias, fmt, y, stream=None):
     _check("svdq_linear_noalloc", lib().svdq_linear_noalloc(
         _p(x_hat), _p(l1t), _p(wq), _p(ws), _p(l2), _p(bias), M, N, K, r, _fmt(fmt), _p(y), _stream(stream)))
     return y
+
+
+class SvdqLinear:
+    """The fused layer prepared for repeated calls (a serving loop, a benchmark's eager steps).
+
+    The weight-side tensors -- residual codes and scales, L1^T, L2, bias -- are checked once
+    here and their pointers kept (with references that keep the tensors alive); each call then
+    checks only its activations and output, reuses a workspace kept for the largest M seen, and
+    makes one svdq_linear call: the same kernels and results as svdq_linear, with a fraction of
+    its per-call host work.
+    """
+
+    def __init__(self, wq, ws, l1t, l2, bias, K: int, fmt):
+        import torch
+        self.K, self.fmt, self._F = int(K), fmt, _fmt(fmt)
+        self.N = _check_weight(wq, ws, K, fmt)
+        self.r = _check_branch(l1t, l2, K, self.N)
+        if bias is not None:
+            _need(bias, torch.float16, (self.N,), "bias")
+        self._keep = (wq, ws, l1t, l2, bias)
+        self._ptrs = (_p(l1t), _p(wq), _p(ws), _p(l2), _p(bias))
+        self.device = wq.device
+        self._dev_index = wq.device.index if wq.device.index is not None else torch.cuda.current_device()
+        self._f16 = torch.float16
+        self._ws, self._ws_bytes, self._ws_rows = None, 0, -1
+        self._fn = lib().svdq_linear
+        self._raw_stream = _raw_stream_fn()
+
+    def _workspace(self, M: int):
+        if M > self._ws_rows:
+            import torch
+            nb = max(linear_workspace_bytes(M, self.K, self.r, self.fmt), 16)
+            self._ws = torch.empty(nb, dtype=torch.uint8, device=self.device)
+            self._ws_bytes, self._ws_rows = nb, M
+        return self._ws
+
+    def __call__(self, x_hat, y=None, stream=None):
+        """x_hat fp16 [M, K] (smoothed) -> y fp16 [M, N] (allocated when None)."""
+        if not (x_hat.is_cuda and x_hat.dtype == self._f16 and x_hat.dim() == 2 and x_hat.shape[1] == self.K
+                and x_hat.is_contiguous()):
+            _need(x_hat, self._f16, (x_hat.shape[0] if x_hat.dim() == 2 else -1, self.K), "x_hat")
+        M = int(x_hat.shape[0])
+        if y is None:
+            import torch
+            y = torch.empty((M, self.N), dtype=self._f16, device=x_hat.device)
+        elif not (y.is_cuda and y.dtype == self._f16 and y.shape == (M, self.N) and y.is_contiguous()):
+            _need(y, self._f16, (M, self.N), "y")
+        ws = self._workspace(M)
+        l1t, wq, ws_, l2, b = self._ptrs
+        st = self._fn(x_hat.data_ptr(), l1t, wq, ws_, l2, b, M, self.N, self.K, self.r, self._F, ws.data_ptr(),
+                      self._ws_bytes, y.data_ptr(), self._raw_stream(self._dev_index) if stream is None else stream)
+        if st != 0:
+            raise SvdqError("svdq_linear", st)
+        return y

@@ -24,7 +24,7 @@ class Dev:
         self.dtype = dtype
         self._contig = contiguous
         self.is_cuda = cuda
-        self.device = "cuda:0"
+        self.device = torch.device("cuda:0")
 
     def dim(self):
         return len(self.shape)
@@ -221,3 +221,27 @@ def test_w4a16_glue_and_weight_entry_points_check_tensors(rec):
         binding.svdq_pack_weight(Dev((N, K), I8), Dev((N, K // 64), F16), "int4",
                                  ws=Dev(binding.scale_shape(N, K, "int4"), F32), stream=0)
     assert rec.calls == []
+
+
+def test_prepared_layer_checks_once_and_calls_svdq_linear(rec, monkeypatch):
+    # the weight side is checked at construction; a call checks only its activations and output
+    # and reaches svdq_linear with the layer's sizes and the kept workspace
+    a = layer_args()
+    for bad in (dict(l2=Dev((16, N), F16)), dict(bias=Dev((N - 16,), F16)), dict(ws=Dev((3, N), F16)),
+                dict(l1t=None)):
+        b = dict(a, **bad)
+        with pytest.raises(ValueError):
+            binding.SvdqLinear(b["wq"], b["ws"], b["l1t"], b["l2"], b["bias"], K, FMT)
+    layer = binding.SvdqLinear(a["wq"], a["ws"], a["l1t"], a["l2"], a["bias"], K, FMT)
+    ws = Dev((1 << 20,), U8)
+    monkeypatch.setattr(layer, "_workspace", lambda M: ws)
+    layer._ws_bytes = 1 << 20
+    for bad in (dict(x=Dev((M, K + 64), F16)), dict(x=Dev((M, K), F32)), dict(x=Dev((M, K), F16, contiguous=False)),
+                dict(y=Dev((M, N + 16), F16)), dict(y=Dev((M, N), F32))):
+        b = dict(a, **bad)
+        with pytest.raises(ValueError):
+            layer(b["x"], b["y"], stream=0)
+    assert rec.calls == []
+    layer(a["x"], a["y"], stream=0)
+    (name, args), = rec.calls
+    assert name == "svdq_linear" and args[6:11] == (M, N, K, R, binding.FORMATS[FMT]) and args[12] == 1 << 20

@@ -298,6 +298,20 @@ def test_linear_end_to_end(fmt, M, K, N, r):
     assert rel_fro(host(y), ref) <= TOL
 
 
+@pytest.mark.parametrize("fmt", ["int4_e2m3", "mxfp4"])
+def test_prepared_layer_equals_linear(fmt):
+    # SvdqLinear: weight side checked once, a workspace kept for the largest M seen; a call on
+    # more rows regrows it, a call on fewer reuses it -- every output equals svdq_linear's
+    K, N, r = 320, 272, 32
+    x_hat, l1, l2, b, _, _, _ = _gemm_inputs(fmt, 300, K, N, r, 77)
+    gw, gs = binding.svdq_quantize_weight(dev(_rt(fmt, 300, K, N, r)), fmt)
+    layer = binding.SvdqLinear(gw, gs, dev(l1.T), dev(l2), dev(b), K, fmt)
+    for M in (17, 300, 130):
+        gx = dev(x_hat[:M])
+        ref = host(binding.svdq_linear(gx, dev(l1.T), gw, gs, dev(l2), dev(b), fmt))
+        assert np.array_equal(host(layer(gx)).view(np.uint16), ref.view(np.uint16))
+
+
 def _rt(fmt, M, K, N, r):
     return draw(99 + M, M, K, N, r)[1]
 
