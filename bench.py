@@ -95,8 +95,8 @@ def settle(torch, fn, ms=None):
 
 
 CSRC = os.path.join(ROOT, "bit_w4a4_quantized_amd", "csrc")
-KERNEL_B_SOURCES = {"int4_e2m3": ("k_gemm3.hip", "kernels.h"), "int4": ("k_gemm2.hip", "kernels.h"),
-                    "mxfp4": ("k_gemm_mx.hip", "kernels.h")}
+KERNEL_B_SOURCES = {"int4_e2m3": ("k_gemm3.hip",), "int4": ("k_gemm2.hip",),
+                    "mxfp4": ("k_gemm_mx.hip", "gemm_skel.h")}
 
 
 def parse():
