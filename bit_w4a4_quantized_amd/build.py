@@ -88,8 +88,21 @@ def build_host_check(verbose: bool = False) -> str:
     return HOST_CHECK
 
 
+MICROBENCH = os.path.join(BUILD_DIR, "mfma_valu")
+
+
+def build_microbench(verbose: bool = False) -> str:
+    """The matrix-core / vector-ALU overlap microbenchmark (microbench/mfma_valu.hip), a program
+    of its own (not part of the library)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    _run([hipcc(), *FLAGS, os.path.join(HERE, "microbench", "mfma_valu.hip"), "-o", MICROBENCH], verbose)
+    return MICROBENCH
+
+
 if __name__ == "__main__":
-    if "--host-check" in sys.argv:
+    if "--microbench" in sys.argv:
+        print(build_microbench(verbose="-v" in sys.argv))
+    elif "--host-check" in sys.argv:
         print(build_host_check(verbose="-v" in sys.argv))
     else:
         print(build(verbose="-v" in sys.argv))
