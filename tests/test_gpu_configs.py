@@ -19,7 +19,7 @@ import oracle  # noqa: E402
 from bit_w4a4_quantized_amd import binding  # noqa: E402
 from tests.layers import (log, prepared, raw_layer, reference, rel_fro, within_sum_bound,  # noqa: E402
                           linear_abs_sum, branch_slack, w4a16_bound_terms, gemm_terms)
-from tests.test_gpu_kernels import dev_codes, dev_scales  # noqa: E402
+from tests.layouts import dev_codes, dev_scales  # noqa: E402
 
 TOL = 1e-3
 

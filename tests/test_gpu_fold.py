@@ -18,8 +18,8 @@ pytestmark = pytest.mark.gpu
 import oracle  # noqa: E402
 from bit_w4a4_quantized_amd import binding  # noqa: E402
 from tests.layers import log, rel_fro, fp16_ulp_diff  # noqa: E402
-from tests.test_gpu_kernels import (FMTS, TOL, _gemm_inputs, dev, dev_codes, dev_scales, host,  # noqa: E402
-                                    same_bytes)
+from tests.layouts import dev_codes, dev_scales  # noqa: E402
+from tests.test_gpu_kernels import FMTS, TOL, _gemm_inputs, dev, host, same_bytes  # noqa: E402
 
 
 @pytest.fixture(scope="module", autouse=True)

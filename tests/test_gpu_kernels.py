@@ -15,6 +15,7 @@ pytestmark = pytest.mark.gpu
 import oracle  # noqa: E402
 from bit_w4a4_quantized_amd import binding  # noqa: E402
 from tests.layers import log, rel_fro, fp16_ulp_diff, within_sum_bound, linear_abs_sum, w4a16_bound_terms, gemm_terms  # noqa: E402
+from tests.layouts import dev_codes, dev_scales  # noqa: E402
 
 TOL = 1e-3
 
@@ -42,39 +43,12 @@ def same_bytes(a, b):
     return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
-def dev_codes(stored, fmt):
-    """Codes in the device layout of the format (the oracle stores every format row by row).
-    The E2M3 container is group-major [K/64][rows][48] with the bytes of a group ordered
-    half 0 [0:16], half 1 [0:16], half 0 [16:24], half 1 [16:24] (the oracle: each half's 24
-    bytes contiguous); INT8, FP4 and MXFP4 are chunk-major [K/64][rows][bytes per chunk];
-    packed INT4 stays row-major."""
-    if fmt in ("int8", "fp4", "mxfp4"):
-        rows = stored.shape[0]
-        return np.ascontiguousarray(stored.reshape(rows, -1, 64 if fmt == "int8" else 32).transpose(1, 0, 2))
-    if fmt != "int4_e2m3":
-        return stored
-    rows = stored.shape[0]
-    g = stored.reshape(rows, -1, 48)
-    g = np.concatenate([g[..., 0:16], g[..., 24:40], g[..., 16:24], g[..., 40:48]], axis=-1)
-    return np.ascontiguousarray(g.transpose(1, 0, 2))
-
-
-def dev_scales(s, fmt):
-    """Scales in the device layout of the format: group-major [K/64][rows] for the E2M3
-    container and INT8, chunk-major [K/64][rows][4] (FP4) or [K/64][rows][2] (MXFP4), row-major
-    for packed INT4."""
-    if fmt in ("fp4", "mxfp4"):
-        return np.ascontiguousarray(s.reshape(s.shape[0], -1, 4 if fmt == "fp4" else 2).transpose(1, 0, 2))
-    return np.ascontiguousarray(s.T) if fmt in ("int4_e2m3", "int8") else s
-
-
 FMTS = ["int4", "int8", "fp4", "int4_e2m3", "mxfp4"]
 
 
 def canonical(q, s, stored, fmt):
-    """The oracle's codes and scales in the exchange layout: its row-major storage, with the
-    6-bit container's INT4 codes as two's-complement nibbles."""
-    return (oracle.quant.pack_nibbles(q) if fmt == "int4_e2m3" else stored), s
+    """The oracle's codes and scales in the exchange layout (its row-major storage)."""
+    return stored, s
 
 
 def assert_canonical(xq, xs, K, fmt, q, s, stored):

@@ -179,35 +179,12 @@ def test_packing_round_trip(rng):
     assert np.array_equal(quant.unpack_nibbles(quant.pack_nibbles(nib)), nib)
 
 
-def _e2m3_value(f):
-    """E2M3 from its definition: sign bit 5, exponent bits 4..3 (bias 1), mantissa bits 2..0."""
-    s = -1.0 if f & 32 else 1.0
-    e, m = (f >> 3) & 3, f & 7
-    return s * (m / 8.0 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 1))
-
-
-def test_e2m3_container_round_trip_and_values(rng):
-    q = rng.integers(-7, 8, (6, 256)).astype(np.int8)
-    st = quant.pack_e2m3(q)
-    assert st.shape == (6, 256 * 3 // 4)
-    assert np.array_equal(quant.unpack_e2m3(st, 256), q)
-    # each 6-bit field decodes (as E2M3) to q/8; field j of a 32-code run sits at bits 6j..6j+5
-    bits = np.unpackbits(st[0, :24], bitorder="little")
-    for j in range(32):
-        f = int(sum(int(bits[6 * j + i]) << i for i in range(6)))
-        assert _e2m3_value(f) == q[0, j] / 8.0
-    # the second run (codes 32..63 of group 0) starts at byte 24
-    bits = np.unpackbits(st[0, 24:48], bitorder="little")
-    f = int(sum(int(bits[i]) << i for i in range(6)))
-    assert _e2m3_value(f) == q[0, 32] / 8.0
-
-
 def test_e2m3_format_has_int4_codes_and_scales(rng):
     v = rng.standard_normal((8, 128)).astype(np.float32)
-    q4, s4, _ = quant.quantize(v, "int4")
+    q4, s4, st4 = quant.quantize(v, "int4")
     q6, s6, st6 = quant.quantize(v, "int4_e2m3")
     assert np.array_equal(q4, q6) and np.array_equal(s4.view(np.uint16), s6.view(np.uint16))
-    assert np.array_equal(quant.unpack_e2m3(st6, 128), q4)
+    assert np.array_equal(st6, st4) and np.array_equal(quant.unpack_int4(st6), q4)
 
 
 def _fma32(a, b, c):
