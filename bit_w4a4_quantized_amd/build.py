@@ -92,10 +92,13 @@ MICROBENCH = os.path.join(BUILD_DIR, "mfma_valu")
 
 
 def build_microbench(verbose: bool = False) -> str:
-    """The matrix-core / vector-ALU overlap microbenchmark (microbench/mfma_valu.hip), a program
-    of its own (not part of the library)."""
+    """The microbenchmarks, programs of their own (not part of the library): matrix-core /
+    vector-ALU overlap (microbench/mfma_valu.hip) and the operand load paths
+    (microbench/load_paths.hip).  Returns the first program's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     _run([hipcc(), *FLAGS, os.path.join(HERE, "microbench", "mfma_valu.hip"), "-o", MICROBENCH], verbose)
+    _run([hipcc(), *FLAGS, os.path.join(HERE, "microbench", "load_paths.hip"), "-o",
+          os.path.join(BUILD_DIR, "load_paths")], verbose)
     return MICROBENCH
 
 
