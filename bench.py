@@ -553,11 +553,11 @@ def layer_entry(Lo, res, fmt):
             "kernel_b_pct_int8_peak": round(100.0 * o_b / (res["kb_us"] * 1e-6) / 1e12 / INT8_PEAK_TOPS, 2)}
 
 
-def small_batch_sweep(Lo, fmt, es, ew):
+def small_batch_sweep(Lo, fmt, es, ew, rows=(64, 256, 1024)):
     """fc1's shape on its first 64, 256 and 1024 token rows: where the layer moves from
     HBM-bound to MFMA-bound (ridge 625 op/B for INT8), timed from HIP graph replays."""
     sweep = {}
-    for m in (64, 256, 1024):
+    for m in rows:
         rs = Lo.time_rows_graph(m, 20, 3)
         eager = Lo.time_rows(m, es, ew)
         prepared = Lo.time_rows_prepared(m, es, ew)
@@ -727,6 +727,13 @@ def main():
             log(f"{name}: {others[name]}")
         out["other_workloads"] = others
         out["small_batch_fc1"] = small_batch_sweep(layers["fc1"], fmt, es, ew)
+        if fmt != "int4":
+            # few token rows read mostly weights: the packed layout moves 2/3 of the container's
+            # weight bytes (its own weight-streaming kernel, INT8 matrix cores)
+            Lp = Layer(torch, binding, "fc1", "int4")
+            out["small_batch_fc1_packed_int4"] = small_batch_sweep(Lp, "int4", es, ew, rows=(64, 256))
+            del Lp
+            torch.cuda.empty_cache()
         pair = time_mlp_pair(layers["fc1"], layers["fc2"], es, ew)
         log(f"mlp pair: {pair}")
         out["mlp_pair_fc1_fc2"] = pair

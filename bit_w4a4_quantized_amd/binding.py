@@ -195,13 +195,10 @@ def code_row_bytes(K: int, fmt) -> int:
 
 @functools.lru_cache(maxsize=4096)
 def code_shape(rows: int, K: int, fmt):
-    """Shape of a code tensor: row-major [rows, K/2] for packed INT4; chunk-major
-    [K/64, rows, bytes per 64-K chunk] otherwise (48 for the E2M3 container, 64 for INT8, 32
-    for FP4 and MXFP4)."""
+    """Shape of a code tensor: chunk-major [K/64, rows, bytes per 64-K chunk] (32 for packed
+    INT4, FP4 and MXFP4, 48 for the E2M3 container, 64 for INT8)."""
     name = fmt if isinstance(fmt, str) else FMT_NAMES[int(fmt)]
-    if name == "int4":
-        return (rows, code_row_bytes(K, fmt))
-    return (K // 64, rows, {"int4_e2m3": 48, "int8": 64, "fp4": 32, "mxfp4": 32}[name])
+    return (K // 64, rows, {"int4": 32, "int4_e2m3": 48, "int8": 64, "fp4": 32, "mxfp4": 32}[name])
 
 
 def code_rows(q) -> int:
@@ -216,13 +213,10 @@ def scale_row_entries(K: int, fmt) -> int:
 
 @functools.lru_cache(maxsize=4096)
 def scale_shape(rows: int, K: int, fmt):
-    """Shape of the scale tensor: row-major [rows, K/64] for packed INT4; group-major
-    [K/64, rows] for the E2M3 container and INT8; chunk-major [K/64, rows, 4] (FP4) or
-    [K/64, rows, 2] (MXFP4)."""
+    """Shape of the scale tensor: group-major [K/64, rows] for the INT formats; chunk-major
+    [K/64, rows, 4] (FP4) or [K/64, rows, 2] (MXFP4)."""
     name = fmt if isinstance(fmt, str) else FMT_NAMES[int(fmt)]
-    if name == "int4":
-        return (rows, K // 64)
-    if name in ("int4_e2m3", "int8"):
+    if name in ("int4", "int4_e2m3", "int8"):
         return (K // 64, rows)
     return (K // 64, rows, {"fp4": 4, "mxfp4": 2}[name])
 
@@ -394,7 +388,8 @@ def svdq_linear_unfused(x_hat, l1t, wq, ws, l2, bias, fmt, workspace=None, y=Non
 
 
 def svdq_gemm_w4a16(x, wq, ws, bias, y=None, stream=None):
-    """W4A16 control.  x fp16 [M, K]; wq uint8 [N, K/2]; ws fp16 [N, K/64]."""
+    """W4A16 control.  x fp16 [M, K]; wq, ws: SVDQ_INT4_G64 codes and scales of the N output
+    columns (code_shape / scale_shape)."""
     import torch
     _need(x, torch.float16, None, "x")
     M, K = x.shape

@@ -10,8 +10,10 @@
 //
 // Each lane reads 16 bytes of packed nibbles and turns them into int8 16q with
 // two masks and a shift; two v_mfma_i32_32x32x32_i8 per tile per group; the
-// int32 partial is converted to fp32.  Scales are row-major.  (The 6-bit
-// container format has its own kernel on the FP6 matrix cores.)
+// int32 partial is converted to fp32.  Codes and scales are group-major
+// ([K/64][rows][32 bytes], [K/64][rows] fp16), so a tile's rows of one group are
+// one contiguous run.  (The 6-bit container format has its own kernel on the
+// FP6 matrix cores.)
 //
 // Tiling (gfx950, wave64): workgroup tile 128 x 128, four waves in 2 x 2 of
 // 64 x 64 (2 x 2 MFMA tiles of 32 x 32), two workgroups per CU.  K advances in
@@ -97,10 +99,12 @@ k_gemm2(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
   const int m0 = tm * BM, n0 = tn * BN;
   const int G = K >> 6;
   const int NS = (G + KC - 1) / KC;                       // stages
-  const size_t row_bytes = (size_t)G * C::GB;
 
   // ---- per-thread staging assignment (global -> registers -> LDS)
+  // codes and scales are group-major ([K/64][rows][32], [K/64][rows]): a tile's rows of one
+  // group are contiguous
   const uint8_t* src[C::CHUNKS];
+  size_t gstep[C::CHUNKS];                                // bytes between consecutive groups
   int dst[C::CHUNKS];
   bool ok[C::CHUNKS];
 #pragma unroll
@@ -112,7 +116,8 @@ k_gemm2(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
     const int grow = (tile == 0 ? m0 : n0) + row;
     ok[i] = grow < (tile == 0 ? M : N);
     // rows past the edge re-read row 0 of the tile's operand and are never stored
-    src[i] = (tile == 0 ? xq : wq) + (size_t)(ok[i] ? grow : 0) * row_bytes + part * 16;
+    src[i] = (tile == 0 ? xq : wq) + (size_t)(ok[i] ? grow : 0) * C::GB + part * 16;
+    gstep[i] = (size_t)(tile == 0 ? M : N) * C::GB;
     dst[i] = tile * TILE_BYTES + row * C::LS + part * 16;
   }
   // scale staging: thread < 128 -> sx of row m0+tid, else sw of column n0+tid-128 (raw fp16)
@@ -120,8 +125,8 @@ k_gemm2(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
   const int s_row = (s_is_x ? m0 : n0) + (tid & 127);
   const bool s_ok = s_row < (s_is_x ? M : N);
   const unsigned short* s_base = reinterpret_cast<const unsigned short*>(s_is_x ? xs : ws);
-  const unsigned short* s_ptr = s_base + (size_t)(s_ok ? s_row : 0) * G;
-  const size_t s_step = 1;   // between consecutive groups
+  const unsigned short* s_ptr = s_base + (s_ok ? s_row : 0);
+  const size_t s_step = (size_t)(s_is_x ? M : N);   // between consecutive groups
 
   uint4 stage_reg[KC][C::CHUNKS];
   unsigned short stage_s[KC];
@@ -130,7 +135,7 @@ k_gemm2(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
     for (int k = 0; k < KC; k++) {
       const int g = min(st * KC + k, G - 1);   // a group past the end re-reads the last one (unused)
 #pragma unroll
-      for (int i = 0; i < C::CHUNKS; i++) stage_reg[k][i] = *reinterpret_cast<const uint4*>(src[i] + (size_t)g * C::GB);
+      for (int i = 0; i < C::CHUNKS; i++) stage_reg[k][i] = *reinterpret_cast<const uint4*>(src[i] + (size_t)g * gstep[i]);
       stage_s[k] = s_ptr[(size_t)g * s_step];
     }
   };
@@ -266,8 +271,191 @@ k_gemm2(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
   }
 }
 
+// Few token rows (the weight-streaming regime, M <= 256): one workgroup per 32 output columns
+// and a slab of up to 128 rows (MT tiles of 32; blockIdx.y picks the slab), so each weight row
+// is read once per slab, in its packed layout (half the bytes of the 6-bit container).  The
+// four waves split K (groups w, w + 4, ...), each holding PD groups of loads in flight straight
+// into registers: lane (r32, h) loads the 16 bytes of codes 32 h .. 32 h + 31 of its weight row
+// and of each of its token rows, which, unpacked to 16 q with two masks and a shift, are its
+// operands of the two v_mfma_i32_32x32x32_i8 of a group (the same K order on both sides).  The
+// int32 result is 256 P_g exactly; the scale-product MFMA gives S = sw sx, one fma per element
+// and group adds 256 P_g S, and the accumulator is scaled by 1/256 once (exact).  The waves'
+// partial sums are added in LDS in wave order; wave 0 adds T L2 and the bias and stores.
+template <int RB, bool BIAS, int MT>
+__global__ void __launch_bounds__(NTHREADS, 2)
+k_gemm2_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __half* __restrict__ t,
+               const uint8_t* __restrict__ wq, const __half* __restrict__ ws, const __half* __restrict__ l2,
+               const __half* __restrict__ bias, const float* __restrict__ lam, int M, int N, int K,
+               __half* __restrict__ y) {
+  constexpr int R = RB * 16;
+  constexpr int PD = MT <= 2 ? 4 : 2;       // groups in flight per wave
+  __shared__ __attribute__((aligned(16))) float red[3][16][64];   // partials of waves 1..3, one row tile
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, r32 = lane & 31;
+  const int G = K >> 6;
+  const int nb = blockIdx.x * 32;
+  const int mb = blockIdx.y * 32 * MT;
+  const int n = min(nb + r32, N - 1);                    // this lane's weight row
+  int mrow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) mrow[mt] = min(mb + mt * 32 + r32, M - 1);
+
+  typedef _Float16 v4h_t __attribute__((ext_vector_type(4)));
+  struct Op { uint4 w; uint32_t sw; uint4 x[MT]; uint32_t sx[MT]; };
+  // codes group-major [K/64][rows][32], scales [K/64][rows]: group offsets in the scalar
+  // offset, row offsets per lane
+  const rsrc_t rxq = make_rsrc(xq, (size_t)M * (K >> 1)), rwq = make_rsrc(wq, (size_t)N * (K >> 1));
+  const rsrc_t rxs = make_rsrc(xs, (size_t)M * G * 2), rws = make_rsrc(ws, (size_t)N * G * 2);
+  const uint32_t vw = (uint32_t)n * 32u + 16u * h, vsw = (uint32_t)n * 2u;
+  auto load = [&](int g, Op& o) {
+    const uint32_t gx = (uint32_t)g * (uint32_t)M, gw = (uint32_t)g * (uint32_t)N;
+    o.w = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rwq, (int)vw, (int)(gw * 32u), 0));
+    // every lane loads (no branch around a load); the upper K half's scale is zeroed at use
+    o.sw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rws, (int)vsw, (int)(gw * 2u), 0);
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      o.x[mt] = as_u4(__builtin_amdgcn_raw_buffer_load_b128(rxq, (int)((uint32_t)mrow[mt] * 32u + 16u * h),
+                                                            (int)(gx * 32u), 0));
+      o.sx[mt] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rxs, (int)((uint32_t)mrow[mt] * 2u), (int)(gx * 2u), 0);
+    }
+  };
+  // the epilogue's operands (L2 columns, bias, and T rows when MT <= 2), loaded by every wave
+  // before the K loop so that their latency overlaps it (wave 0 uses them)
+  constexpr int MTT = MT <= 2 ? MT : 1;
+  uint32_t lv[RB > 0 ? RB : 1][8];
+  uint4 tv[MTT][RB > 0 ? RB : 1];
+#pragma unroll
+  for (int kb = 0; kb < RB; kb++) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) lv[kb][e] = __half_as_ushort(l2[(size_t)(kb * 16 + 8 * h + e) * N + n]);
+    if (MT <= 2) {
+#pragma unroll
+      for (int mt = 0; mt < MTT; mt++)
+        tv[mt][kb] = *reinterpret_cast<const uint4*>(t + (size_t)mrow[mt] * R + kb * 16 + 8 * h);
+    }
+  }
+  uint2 braw[4];
+  float4 lam4[4];                            // with the MLP glue folded in: the next layer's factors
+  const rsrc_t rl = make_rsrc(lam, lam ? (size_t)N * 4 : 0);
+#pragma unroll
+  for (int q = 0; q < 4; q++) {  // columns past N read the last four (their outputs are not stored)
+    braw[q] = BIAS ? *reinterpret_cast<const uint2*>(bias + min(nb + 8 * q + 4 * h, N - 4)) : make_uint2(0u, 0u);
+    lam4[q] = load_f4(rl, min(nb + 8 * q + 4 * h, N - 4));
+  }
+  v16f acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) acc[mt][i] = 0.f;
+  // step s processes slot s % PD (the wave's group s - PD, or, for s < PD and past the wave's
+  // last group, a zeroed slot whose scale product is zero: exactly +0) and refills it with the
+  // wave's group s (past the last one: the last one again, unused)
+  const int ng = wave < G ? (G - 1 - wave) / 4 + 1 : 0;   // this wave's groups
+  Op ring[PD];
+#pragma unroll
+  for (int j = 0; j < PD; j++) ring[j] = Op{};
+  for (int s0 = 0; s0 < ng + PD; s0 += PD) {
+#pragma unroll
+    for (int j = 0; j < PD; j++) {
+      const int st = s0 + j;
+      const bool zero = h || st < PD || st - PD >= ng;   // upper K half, or an empty slot
+      const Op& cur = ring[j];
+      const v4i w0 = v4i{(int)nib_lo16(cur.w.x), (int)nib_hi16(cur.w.x), (int)nib_lo16(cur.w.y), (int)nib_hi16(cur.w.y)};
+      const v4i w1 = v4i{(int)nib_lo16(cur.w.z), (int)nib_hi16(cur.w.z), (int)nib_lo16(cur.w.w), (int)nib_hi16(cur.w.w)};
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) {
+        const uint4 xc = cur.x[mt];
+        const v4i x0 = v4i{(int)nib_lo16(xc.x), (int)nib_hi16(xc.x), (int)nib_lo16(xc.y), (int)nib_hi16(xc.y)};
+        const v4i x1 = v4i{(int)nib_lo16(xc.z), (int)nib_hi16(xc.z), (int)nib_lo16(xc.w), (int)nib_hi16(xc.w)};
+        v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(w0, x0, v16i{}, 0, 0, 0);
+        p = __builtin_amdgcn_mfma_i32_32x32x32_i8(w1, x1, p, 0, 0, 0);
+        // K slot 0 holds the scale for the lower-K-half lanes; the upper half contributes zeros
+        const v16f sc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h_t, make_uint2(zero ? 0u : cur.sw, 0u)),
+                                                              __builtin_bit_cast(v4h_t, make_uint2(zero ? 0u : cur.sx[mt], 0u)),
+                                                              v16f{}, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 16; i++) acc[mt][i] = __builtin_fmaf((float)p[i], sc[i], acc[mt][i]);
+      }
+      load(ng > 0 ? wave + 4 * min(st, ng - 1) : 0, ring[j]);
+      __builtin_amdgcn_sched_barrier(0);     // keep the slots in order: each waits for its own loads only
+    }
+  }
+  // the four waves' partials (256 P_g S), added in wave order, one row tile at a time
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) {
+    if (wave > 0) {
+#pragma unroll
+      for (int i = 0; i < 16; i++) red[wave - 1][i][lane] = acc[mt][i];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; i++)
+        acc[mt][i] = (((acc[mt][i] + red[0][i][lane]) + red[1][i][lane]) + red[2][i][lane]) * (1.0f / 256.0f);
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
+  // up projection: row operand L2^T (columns n, gathered once), column operand T (rows m)
+  uint4 lw[RB > 0 ? RB : 1];
+#pragma unroll
+  for (int kb = 0; kb < RB; kb++)
+    lw[kb] = make_uint4(lv[kb][0] | (lv[kb][1] << 16), lv[kb][2] | (lv[kb][3] << 16),
+                        lv[kb][4] | (lv[kb][5] << 16), lv[kb][6] | (lv[kb][7] << 16));
+  float bv[4][4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    bv[q][0] = BIAS ? __half2float(__ushort_as_half((unsigned short)(braw[q].x & 0xFFFFu))) : 0.f;
+    bv[q][1] = BIAS ? __half2float(__ushort_as_half((unsigned short)(braw[q].x >> 16))) : 0.f;
+    bv[q][2] = BIAS ? __half2float(__ushort_as_half((unsigned short)(braw[q].y & 0xFFFFu))) : 0.f;
+    bv[q][3] = BIAS ? __half2float(__ushort_as_half((unsigned short)(braw[q].y >> 16))) : 0.f;
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) {
+#pragma unroll
+    for (int kb = 0; kb < RB; kb++) {
+      const uint4 tvk = MT <= 2 ? tv[MT <= 2 ? mt : 0][kb]
+                                : *reinterpret_cast<const uint4*>(t + (size_t)mrow[mt] * R + kb * 16 + 8 * h);
+      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(lw[kb]), as_h8(tvk), acc[mt], 0, 0, 0);
+    }
+    // lane owns row mb + mt*32 + r32 and columns nb + 8 q + 4 h + j (reg 4 q + j)
+    const int mo = mb + mt * 32 + r32;
+    if (mo >= M) continue;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int no = nb + 8 * q + 4 * h;
+      if (no >= N) continue;
+      uint32_t hv[4];
+#pragma unroll
+      for (int j = 0; j < 4; j++) hv[j] = __half_as_ushort(__float2half_rn(acc[mt][4 * q + j] + bv[q][j]));
+      if (lam) {                             // the MLP glue folded in: fp16(gelu(y) / lam)
+        const float lq[4] = {lam4[q].x, lam4[q].y, lam4[q].z, lam4[q].w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) hv[j] = gelu_div_h(hv[j], lq[j]);
+      }
+      *reinterpret_cast<uint2*>(y + (size_t)mo * N + no) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+    }
+  }
+}
+
+// Up to this many token rows the weight-streaming kernel runs (in 128-row slabs).
+constexpr int kSkinnyRows2 = 256;
+
+template <int RB, bool BIAS, int MT>
+static hipError_t launch_g2_skinny(const GemmArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm2_skinny<RB, BIAS, MT>), dim3((a.N + 31) / 32, (a.M + 32 * MT - 1) / (32 * MT)),
+                     dim3(NTHREADS), 0, s, (const uint8_t*)a.xq, (const __half*)a.xs, (const __half*)a.t,
+                     (const uint8_t*)a.wq, (const __half*)a.ws, (const __half*)a.l2, (const __half*)a.bias, a.lam,
+                     a.M, a.N, a.K, (__half*)a.y);
+  return hipGetLastError();
+}
+
 template <int CORE, int RB, bool BIAS>
 static hipError_t launch_g2(const GemmArgs& a, hipStream_t s) {
+  if (a.M <= 32) return launch_g2_skinny<RB, BIAS, 1>(a, s);
+  if (a.M <= 64) return launch_g2_skinny<RB, BIAS, 2>(a, s);
+  if (a.M <= kSkinnyRows2) return launch_g2_skinny<RB, BIAS, 4>(a, s);
   const int nb = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   hipLaunchKernelGGL((k_gemm2<CORE, RB, BIAS>), dim3(nb), dim3(NTHREADS), 0, s, (const uint8_t*)a.xq,
                      (const __half*)a.xs, (const __half*)a.t, (const uint8_t*)a.wq, (const __half*)a.ws,

@@ -124,7 +124,6 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
   };
 
   uint8_t* slot = smem + wave * ROWS * CB;   // this wave's code staging (STAGE)
-  const size_t code_row = FMT == FMT_INT8 ? (size_t)K : (size_t)(K >> 1);   // row-major formats
 
   auto process = [&](int c, Buf& B) {
     if constexpr (SMOOTH) {
@@ -193,9 +192,8 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
             qv[k][e] = rintf(__builtin_amdgcn_fmed3f(quot_rn_h(e < 8 ? hv0[e] : hv1[e - 8], s, r), -qmax, qmax)) + 0.0f;
           const int m = m0 + rt * 16 + row;
           if (sub == 0 && m < M) {
-            // row-major scales [M, K/64]; the 6-bit container keeps them group-major [K/64, M]
-            const size_t si = FMT == FMT_INT4 ? (size_t)m * (K >> 6) + c : (size_t)c * M + m;
-            reinterpret_cast<uint16_t*>(xs)[si] = sbits;
+            // group-major scales [K/64, M]
+            reinterpret_cast<uint16_t*>(xs)[(size_t)c * M + m] = sbits;
           }
           uint8_t* srow = slot + (rt * 16 + row) * CB;   // this row's bytes of the chunk, in LDS
           if (FMT == FMT_INT4) {
@@ -317,7 +315,7 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
     }
     if (STAGE) {
       // the wave's ROWS x CB bytes go out as 16-byte pieces: the rows of one 64-K chunk are
-      // contiguous ([K/64][M][CB]) in every format but packed INT4, which is row-major
+      // contiguous ([K/64][M][CB]) in every format
       __builtin_amdgcn_wave_barrier();
       constexpr int PR = CB / 16;            // pieces per row
 #pragma unroll
@@ -327,8 +325,7 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
         const int mm = m0 + rr;
         if (p < ROWS * PR && mm < M) {
           const uint4 v16 = *reinterpret_cast<const uint4*>(slot + rr * CB + pc * 16);
-          uint8_t* dst = FMT != FMT_INT4 ? xq + ((size_t)c * M + mm) * CB + pc * 16
-                                         : xq + (size_t)mm * code_row + (size_t)c * CB + pc * 16;
+          uint8_t* dst = xq + ((size_t)c * M + mm) * CB + pc * 16;
           *reinterpret_cast<uint4*>(dst) = v16;
         }
       }

@@ -9,15 +9,14 @@
 namespace svdq {
 
 // One INT group's codes (64 values, code e of group g of output column n) and fp16 scale bits
-// into the layouts Kernel B reads: packed nibbles [N, K/2] (INT4), int8 group-major
-// [K/64][N][64] (INT8), or the 6-bit container, group-major [K/64][N][48] (INT4_E2M3); the
-// scales row-major [N, K/64] for INT4, group-major [K/64, N] otherwise.
+// into the layouts Kernel B reads, all group-major: packed nibbles [K/64][N][32] (INT4), int8
+// [K/64][N][64] (INT8), or the 6-bit container [K/64][N][48] (INT4_E2M3); the scales
+// [K/64, N].
 template <int FMT>
-__device__ __forceinline__ void store_int_group(const int* q, uint16_t sbits, int n, int g, int N, int K,
+__device__ __forceinline__ void store_int_group(const int* q, uint16_t sbits, int n, int g, int N,
                                                 uint8_t* __restrict__ wq, uint8_t* __restrict__ ws) {
   constexpr int G = 64;
-  const int gpr = K / G;
-  reinterpret_cast<uint16_t*>(ws)[FMT == FMT_INT4 ? (size_t)n * gpr + g : (size_t)g * N + n] = sbits;
+  reinterpret_cast<uint16_t*>(ws)[(size_t)g * N + n] = sbits;
   if (FMT == FMT_INT4_E2M3) {
     // 48 bytes per (group, column): two halves of 32 six-bit fields
     uint32_t wv[12];
@@ -41,7 +40,7 @@ __device__ __forceinline__ void store_int_group(const int* q, uint16_t sbits, in
     dst[1] = make_uint4(wv[6], wv[7], wv[8], wv[9]);
     dst[2] = make_uint4(wv[4], wv[5], wv[10], wv[11]);
   } else if (FMT == FMT_INT4) {
-    uint32_t* dst = reinterpret_cast<uint32_t*>(wq + (size_t)n * (K >> 1) + (size_t)g * (G >> 1));
+    uint32_t* dst = reinterpret_cast<uint32_t*>(wq + ((size_t)g * N + n) * (G >> 1));
 #pragma unroll
     for (int e = 0; e < G; e += 8) dst[e >> 3] = pack8(q + e);
   } else {
@@ -77,7 +76,7 @@ k_quant_weight(const float* __restrict__ r_t, int N, int K, uint8_t* __restrict_
     int q[G];
 #pragma unroll
     for (int e = 0; e < G; e++) q[e] = int_code(v[e], s, qmax);
-    store_int_group<FMT>(q, sbits, n, g, N, K, wq, ws);
+    store_int_group<FMT>(q, sbits, n, g, N, wq, ws);
   } else if constexpr (FMT == FMT_MXFP4) {
     // chunk-major: group g is half g % 2 of 64-K chunk g / 2; codes [K/64][N][32 bytes],
     // E8M0 bytes [K/64][N][2]
@@ -125,7 +124,7 @@ k_pack_weight(const int8_t* __restrict__ codes, const uint16_t* __restrict__ sca
 #pragma unroll
     for (int i = 0; i < 16; i++) q[e + i] = (int)(int8_t)(w[i >> 2] >> (8 * (i & 3)));
   }
-  store_int_group<FMT>(q, scales[(size_t)n * gpr + g], n, g, N, K, wq, ws);
+  store_int_group<FMT>(q, scales[(size_t)n * gpr + g], n, g, N, wq, ws);
 }
 
 hipError_t launch_pack_weight(const int8_t* codes, const uint16_t* scales, int N, int K, int fmt, void* wq,

@@ -6,9 +6,9 @@
 //   codes  [rows, K/2] two 4-bit codes a byte (code 2b in the low nibble), or [rows, K] for
 //          INT8; the 6-bit container's INT4 codes are exchanged as INT4 nibbles;
 //   scales [rows, K/G]: fp16 (INT formats), E4M3 bytes (FP4, G = 16), E8M0 bytes (MXFP4, G = 32).
-// Device layouts: packed INT4 is the exchange layout itself; every other format is chunk-major,
-// the rows of one 64-wide chunk of K contiguous ([K/64][rows][bytes per chunk], scales
-// [K/64][rows][scale bytes per chunk]), with the INT4 codes of the 6-bit container held as E2M3
+// Device layouts: every format is chunk-major, the rows of one 64-wide chunk of K contiguous
+// ([K/64][rows][bytes per chunk], scales [K/64][rows][scale bytes per chunk]), with the INT4
+// codes of the 6-bit container held as E2M3
 // fields (sign << 5 | |q|, 24 bytes per half-group, stored as half 0 bytes 0..15, half 1 bytes
 // 0..15, half 0 bytes 16..23, half 1 bytes 16..23).
 //
@@ -78,10 +78,9 @@ k_relayout(const uint8_t* __restrict__ ci, const uint8_t* __restrict__ si, int r
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (size_t)rows * nch) return;
   const int row = (int)(idx / nch), c = (int)(idx % nch);
-  // packed INT4's device layout is the exchange layout
-  const size_t dcode = FMT == FMT_INT4 ? (size_t)row * nch * CBC + (size_t)c * CBC : ((size_t)c * rows + row) * CBD;
+  const size_t dcode = ((size_t)c * rows + row) * CBD;
   const size_t ccode = (size_t)row * nch * CBC + (size_t)c * CBC;
-  const size_t dscale = FMT == FMT_INT4 ? ((size_t)row * nch + c) * SB : ((size_t)c * rows + row) * SB;
+  const size_t dscale = ((size_t)c * rows + row) * SB;
   const size_t cscale = ((size_t)row * nch + c) * SB;
   const uint8_t* src = ci + (TO_CANON ? dcode : ccode);
   uint8_t* dst = co + (TO_CANON ? ccode : dcode);

@@ -1,6 +1,6 @@
 // W4A16 control: Y = fp16( X deq(W)^T + b ) with fp16 activations X [M, K] and
-// SVDQ_INT4_G64 weights (packed nibbles [N, K/2], fp16 scales [N, K/64]), no
-// low-rank branch.  Practice page "sota-314", sections "Do this" and "What it
+// SVDQ_INT4_G64 weights (packed nibbles, group-major [K/64][N][32 bytes]; fp16
+// scales group-major [K/64][N]), no low-rank branch.  Practice page "sota-314", sections "Do this" and "What it
 // buys": the W4A16 baseline the W4A4 layer is compared with, and the layers that
 // stay W4A16.
 //
@@ -123,8 +123,8 @@ k_w4a16(const __half* __restrict__ x, const uint8_t* __restrict__ wq, const __ha
       const int m = min(m0_ + row, M - 1);
       r.vx[i] = (uint32_t)m * K * 2 + 16u * (uint32_t)(xb ^ (row & 7));
     }
-    r.vw = (uint32_t)min(n0_ + wr, N - 1) * (K / 2) + 16u * wc;
-    r.vs = (uint32_t)min(n0_ + sr, N - 1) * G * 2;
+    r.vw = (uint32_t)min(n0_ + wr, N - 1) * 32u + 16u * wc;   // codes [K/64][N][32]
+    r.vs = (uint32_t)min(n0_ + sr, N - 1) * 2u;                // scales [K/64][N]
     return r;
   };
   auto load_group = [&](const Src& src, int g, int buf) {
@@ -132,8 +132,8 @@ k_w4a16(const __half* __restrict__ x, const uint8_t* __restrict__ wq, const __ha
     uint8_t* b = lds + buf * GROUP;
 #pragma unroll
     for (int i = 0; i < 4; i++) dma16(rxb, b + L_X + (wave * 32 + i * 8) * 128, src.vx[i], (uint32_t)g * 128);
-    dma16(rwb, b + L_W + wave * 1024, src.vw, (uint32_t)g * 32);
-    if (wave < 2) dma2(rsb, b + L_S + wave * 256, src.vs, (uint32_t)g * 2);
+    dma16(rwb, b + L_W + wave * 1024, src.vw, (uint32_t)g * (uint32_t)N * 32u);
+    if (wave < 2) dma2(rsb, b + L_S + wave * 256, src.vs, (uint32_t)g * (uint32_t)N * 2u);
   };
   auto wait_loads = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 

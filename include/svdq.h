@@ -45,7 +45,10 @@
  *                  (byte b = code 2b | code 2b+1 << 4); fp16 scale per 64.
  *                  scale = fp16_rne(fp32(absmax) / 7.0f); code =
  *                  clamp(rint_half_even(fp32(v) / scale), -7, 7); scale 0 ->
- *                  codes 0.
+ *                  codes 0.  Codes group-major [K/64][rows][32 bytes] (group g
+ *                  of row i at byte (g * rows + i) * 32), fp16 scales
+ *                  group-major [K/64][rows]: a GEMM tile's rows of one group
+ *                  are one contiguous run.
  *  SVDQ_INT8_G64 : same rule with 127; one int8 code per byte.  Codes
  *                  group-major [K/64][rows][64 bytes] (group g of row i at
  *                  byte (g * rows + i) * 64), fp16 scales group-major
@@ -126,9 +129,9 @@ typedef enum {
 } svdq_format;
 
 /* Bytes of codes per row for K columns (K/2 for 4-bit formats, K for INT8,
- * 3K/4 for the E2M3 container, whose rows are interleaved group by group), and
- * bytes of scales per row (K/64 fp16 for the INT formats, K/16 E4M3 bytes for
- * FP4).  Returns 0 for a bad format. */
+ * 3K/4 for the E2M3 container; the device layouts interleave the rows group by
+ * group), and bytes of scales per row (K/64 fp16 for the INT formats, K/16 E4M3
+ * bytes for FP4, K/32 E8M0 bytes for MXFP4).  Returns 0 for a bad format. */
 size_t svdq_code_row_bytes(int K, svdq_format fmt);
 size_t svdq_scale_row_bytes(int K, svdq_format fmt);
 
@@ -138,8 +141,8 @@ size_t svdq_scale_row_bytes(int K, svdq_format fmt);
  * "note-257", "Key results").
  *   x_hat : fp16 [M, K], the smoothed activations (smoothing already applied).
  *   l1t   : fp16 [r, K] = L1^T; NULL iff r == 0.
- *   xq    : out, codes [M, code_row_bytes(K)].
- *   xs    : out, scales [M, K/G] (fp16 or E4M3 bytes).
+ *   xq    : out, codes, M * code_row_bytes(K) bytes in the format's layout.
+ *   xs    : out, scales, M * scale_row_bytes(K) bytes in the format's layout.
  *   t     : out, fp16 [M, r] = fp16_rne(X_hat L1), fp32 accumulation; NULL iff r == 0.
  *   workspace, workspace_bytes : caller-owned device scratch for the fp32
  *           partial sums of T when the kernel slices K across workgroups
@@ -168,8 +171,9 @@ size_t svdq_quantize_down_workspace_bytes(int M, int K, int r, svdq_format fmt);
  *   of the rescaled partials).
  *   xq, xs : Kernel A's codes and scales for M rows.
  *   t      : fp16 [M, r]; NULL iff r == 0.
- *   wq     : codes [N, code_row_bytes(K)] -- K contiguous per output column.
- *   ws     : scales [N, K/G].
+ *   wq     : codes of the N output columns, N * code_row_bytes(K) bytes in the
+ *            format's layout (rows = output columns).
+ *   ws     : their scales, N * scale_row_bytes(K) bytes in the format's layout.
  *   l2     : fp16 [r, N]; NULL iff r == 0.
  *   bias   : fp16 [N], or NULL for none.
  *   y      : out, fp16 [M, N].
@@ -254,8 +258,7 @@ svdq_status svdq_pack_weight(const int8_t* codes, const void* scales, int N, int
  *            SVDQ_FP4_G16 and SVDQ_MXFP4_G32) or [rows, K] for SVDQ_INT8_G64;
  *     scales [rows, K/G]: fp16 (INT formats), E4M3 bytes (SVDQ_FP4_G16), E8M0 bytes
  *            (SVDQ_MXFP4_G32).
- *   Device layout: the format's layout above (chunk- or group-major; for SVDQ_INT4_G64 it is
- *   the exchange layout itself, and the call copies).  SVDQ_INT4_G64_E2M3's INT4 codes are
+ *   Device layout: the format's layout above (chunk- or group-major).  SVDQ_INT4_G64_E2M3's INT4 codes are
  *   turned into or out of their 6-bit E2M3 fields exactly; exchange codes must lie in [-7, 7].
  *   to_canonical : 1 = device -> exchange, 0 = exchange -> device.
  *   codes_in, scales_in : the source layout; codes_out, scales_out : the destination layout
@@ -287,8 +290,9 @@ svdq_status svdq_linear_unfused(const void* x_hat, const void* l1t, const void* 
 /*
  * W4A16 control ("sota-314", "Do this" and "What it buys": the W4A16
  * baseline and the layers kept at W4A16): Y = fp16_rne( X deq(W) + b ) with
- * X fp16 [M, K] unquantized, W as SVDQ_INT4_G64 codes wq [N, K/2] and fp16
- * scales ws [N, K/64], fp32 accumulation; bias may be NULL.  No branch.
+ * X fp16 [M, K] unquantized, W as SVDQ_INT4_G64 codes wq and fp16 scales ws
+ * (the format's layout, rows = output columns), fp32 accumulation; bias may be
+ * NULL.  No branch.
  */
 svdq_status svdq_gemm_w4a16(const void* x, const void* wq, const void* ws, const void* bias,
                             int M, int N, int K, void* y, void* stream);

@@ -41,13 +41,12 @@ def uncontainer_e2m3(stored: np.ndarray, K: int) -> np.ndarray:
 
 def dev_codes(stored, fmt):
     """The oracle's stored codes (exchange layout) in the device layout of the format: the
-    E2M3 container group-major [K/64][rows][48] in the device's byte order; INT8, FP4 and
-    MXFP4 chunk-major [K/64][rows][bytes per chunk]; packed INT4 stays row-major."""
-    if fmt in ("int8", "fp4", "mxfp4"):
+    E2M3 container group-major [K/64][rows][48] in the device's byte order; packed INT4, INT8,
+    FP4 and MXFP4 chunk-major [K/64][rows][bytes per chunk]."""
+    if fmt in ("int4", "int8", "fp4", "mxfp4"):
         rows = stored.shape[0]
         return np.ascontiguousarray(stored.reshape(rows, -1, 64 if fmt == "int8" else 32).transpose(1, 0, 2))
-    if fmt != "int4_e2m3":
-        return stored
+    assert fmt == "int4_e2m3", fmt
     q = oracle.quant.unpack_int4(stored)
     g = container_e2m3(q)
     rows = g.shape[0]
@@ -57,9 +56,9 @@ def dev_codes(stored, fmt):
 
 
 def dev_scales(s, fmt):
-    """Scales in the device layout of the format: group-major [K/64][rows] for the E2M3
-    container and INT8, chunk-major [K/64][rows][4] (FP4) or [K/64][rows][2] (MXFP4), row-major
-    for packed INT4."""
+    """Scales in the device layout of the format: group-major [K/64][rows] for the INT formats,
+    chunk-major [K/64][rows][4] (FP4) or [K/64][rows][2] (MXFP4)."""
     if fmt in ("fp4", "mxfp4"):
         return np.ascontiguousarray(s.reshape(s.shape[0], -1, 4 if fmt == "fp4" else 2).transpose(1, 0, 2))
-    return np.ascontiguousarray(s.T) if fmt in ("int4_e2m3", "int8") else s
+    assert fmt in ("int4", "int4_e2m3", "int8"), fmt
+    return np.ascontiguousarray(s.T)

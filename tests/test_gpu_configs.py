@@ -133,7 +133,7 @@ def test_c3_w4a16_control():
     L = raw_layer("c2_fc1")
     q, s, st = oracle.quant.quantize(L.w.T.astype(np.float32), "int4")
     ref = oracle.forward.w4a16(L.x, q, s, L.b)
-    y = host(binding.svdq_gemm_w4a16(dev(L.x), dev(st), dev(s), dev(L.b)))
+    y = host(binding.svdq_gemm_w4a16(dev(L.x), dev(dev_codes(st, "int4")), dev(dev_scales(s, "int4")), dev(L.b)))
     err = rel_fro(y, ref)
     log(f"  w4a16 rel_fro={err:.3e}")
     assert err <= TOL

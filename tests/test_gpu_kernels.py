@@ -336,7 +336,7 @@ def test_w4a16_parity(M, K, N):
     b = (g.standard_normal(N) * 0.01).astype(np.float16)
     q, s, st = oracle.quant.quantize(w_t, "int4")
     ref = oracle.forward.w4a16(x, q, s, b)
-    y = binding.svdq_gemm_w4a16(dev(x), dev(st), dev(s), dev(b))
+    y = binding.svdq_gemm_w4a16(dev(x), dev(dev_codes(st, "int4")), dev(dev_scales(s, "int4")), dev(b))
     yg = host(y)
     assert rel_fro(yg, ref) <= TOL
     ok, worst = within_sum_bound(yg, ref, *w4a16_bound_terms(x, q, s, b))
@@ -395,7 +395,7 @@ def test_empty_inputs_are_no_ops():
     K, N = 64, 16
     x = torch.zeros((0, K), dtype=torch.float16, device="cuda")
     xq, xs, t = binding.svdq_quantize_down(x, None, "int4")
-    assert xq.shape == (0, K // 2)
+    assert tuple(xq.shape) == binding.code_shape(0, K, "int4") == (K // 64, 0, 32)
     wq, ws = binding.svdq_quantize_weight(torch.zeros((N, K), dtype=torch.float32, device="cuda"), "int4")
     y = binding.svdq_linear(x, None, wq, ws, None, None, "int4")
     assert y.shape == (0, N)

@@ -52,12 +52,12 @@ def test_chunk_major_layouts(rng):
     d = dev_codes(b8, "int8")
     assert d.shape == (K // 64, rows, 64) and np.array_equal(d[2, 1], b8[1, 128:192])
     nib = oracle.quant.pack_nibbles(rng.integers(0, 16, (rows, K)).astype(np.uint8))
-    for fmt in ("fp4", "mxfp4"):
+    for fmt in ("int4", "fp4", "mxfp4"):
         d = dev_codes(nib, fmt)
         assert d.shape == (K // 64, rows, 32) and np.array_equal(d[3, 2], nib[2, 96:128])
-    assert dev_codes(nib, "int4") is nib
     s16 = rng.standard_normal((rows, K // 64)).astype(np.float16)
-    assert np.array_equal(dev_scales(s16, "int8"), s16.T) and np.array_equal(dev_scales(s16, "int4"), s16)
+    for fmt in ("int4", "int4_e2m3", "int8"):
+        assert np.array_equal(dev_scales(s16, fmt), s16.T)
     e4 = rng.integers(0, 256, (rows, K // 16)).astype(np.uint8)
     assert np.array_equal(dev_scales(e4, "fp4")[1, 2], e4[2, 4:8])
     e8 = rng.integers(0, 256, (rows, K // 32)).astype(np.uint8)
