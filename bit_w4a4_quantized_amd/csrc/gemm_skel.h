@@ -22,6 +22,7 @@
 //   void load(const Src&, int st, uint8_t* buf);    the stage's LDS-DMA loads
 //   struct Regs; void read(const uint8_t* buf, int st, Regs&);
 //   void mma(const Regs&, int st, v16f (&acc)[2][2]);
+//   void finish(v16f (&acc)[2][2]);                 once per tile, before the epilogue
 // and, for an operator whose kernel runs the last partial round as 32 x 32 sub-tile jobs
 // (operands straight into registers; used by FP4 and MXFP4):
 //   int NU; static constexpr int SUB_PD;            64-column units of K; register ring depth
@@ -240,6 +241,7 @@ __device__ __forceinline__ void persistent(Op& op, uint8_t* lds, const __half* _
       step(st, 0);
       step(st + 1, 1);
     }
+    op.finish(acc);
     epilogue<RB, BIAS>(acc, lds + Op::BUF, t, l2, bias, lam, M, N, m0, n0, y);
     if (!has_next) break;
     tile = next;

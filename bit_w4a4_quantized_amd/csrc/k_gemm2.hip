@@ -1,275 +1,37 @@
-// Kernel B for the canonical packed-nibble format (SVDQ_INT4_G64), LDS-staged:
-// low-bit GEMM on the INT8 matrix cores, per-group rescale into fp32, up
-// projection and bias in the epilogue.
+// Kernel B for the packed-nibble format (SVDQ_INT4_G64): the low-bit GEMM on the INT8 matrix
+// cores, the per-group rescale into fp32, the up projection and the bias in the epilogue.
 //
-// Practice page "sota-314", section "Do this": the up projection is fused
-// with the 4-bit compute since both produce Y.
+// Practice page "sota-314", section "Do this": the up projection is fused with the 4-bit
+// compute since both produce Y.
 //
 //   Y[m,n] = fp16_rne( sum_g sx[m,g] sw[n,g] P_g[m,n] + (T L2)[m,n] + b[n] )
 //   P_g    = sum_{k in group g} q_x[m,k] q_w[n,k]   (exact)
 //
-// Each lane reads 16 bytes of packed nibbles and turns them into int8 16q with
-// two masks and a shift; two v_mfma_i32_32x32x32_i8 per tile per group; the
-// int32 partial is converted to fp32.  Codes and scales are group-major
-// ([K/64][rows][32 bytes], [K/64][rows] fp16), so a tile's rows of one group are
-// one contiguous run.  (The 6-bit container format has its own kernel on the
-// FP6 matrix cores.)
+// Codes and scales are group-major ([K/64][rows][32 bytes], [K/64][rows] fp16), so a GEMM
+// tile's rows of one group are one contiguous run.  A lane takes the 16 bytes of codes
+// 32 h .. 32 h + 31 of its row's group (h its half of the wave) and turns them into int8 16 q
+// with two masks and a shift: the operands of two v_mfma_i32_32x32x32_i8, in the same K order
+// for both operands, whose int32 result is 256 P_g exactly.  The scale products S = sw sx of
+// a 32 x 32 tile come from one v_mfma_f32_32x32x8_f16 with the scales in K slot 0 (exact);
+// the vector ALU converts the partial to fp32 (exact) and does one fma per element and group,
+// acc += 256 P_g S; the accumulator is scaled by 1/256 once (exact: a power of two).
 //
-// Tiling (gfx950, wave64): workgroup tile 128 x 128, four waves in 2 x 2 of
-// 64 x 64 (2 x 2 MFMA tiles of 32 x 32), two workgroups per CU.  K advances in
-// stages of KC groups of 64: the workgroup stages both code tiles and the
-// 256 fp16 scales per group in LDS, in a ring of two stages, and the
-// global loads run two stages ahead of the compute (registers hold stage s+2
-// while LDS holds s and s+1), so a stage's HBM/L2 latency is covered by a full
-// stage of compute.  LDS row strides (56 and 48 bytes) make the
-// per-lane 8- and 16-byte reads of 16 / 8 consecutive rows hit distinct banks.
-// The block index is remapped so that each XCD (own L2) works on a
-// contiguous range of tiles, rastered in groups of 8 tile rows.
-//
-// Rescale: the per-group scale products S = sx sw^T of a 32 x 32 tile come from
-// one v_mfma_f32_32x32x16_f16 with the scales in a single K slot (exact), so
-// the vector ALU does one fma per element and group, acc += P_g * S.
-//
-// Epilogue: acc += T L2 on v_mfma_f32_32x32x16_f16 (fp16 in, fp32 out),
-// + bias, RNE to fp16, store.
-#include <type_traits>
-
-#include "kernels.h"
+// Two kernels: the tiled one on the shared persistent LDS-DMA skeleton (gemm_skel.h), and, for
+// few token rows, a weight-streaming one.  (The 6-bit container format has its own kernels on
+// the FP6 matrix cores.)
+#include "gemm_skel.h"
 #include "quant_core.h"
 
 namespace svdq {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, NTHREADS = 256;
-
-template <int CORE> struct CoreCfg;
-template <> struct CoreCfg<CORE_I4> {
-  static constexpr int GB = 32;
-  static constexpr int LS = 48;
-  static constexpr int CHUNKS = 2;
-};
+constexpr int NTHREADS = 256;
 
 __device__ __forceinline__ uint32_t nib_lo16(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
 __device__ __forceinline__ uint32_t nib_hi16(uint32_t w) { return w & 0xF0F0F0F0u; }
 
-// Map the launch index to an output tile: contiguous ranges per XCD (blocks are
-// dealt round-robin to the 8 XCDs), then 8-tile-row groups within a range.
-__device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, int* tm, int* tn) {
-  const int n8 = nblocks & ~7;
-  int lid = bid;
-  if (bid < n8) lid = (bid & 7) * (n8 >> 3) + (bid >> 3);
-  constexpr int GM = 8;
-  const int per_group = GM * tiles_n;
-  const int grp = lid / per_group;
-  const int first_m = grp * GM;
-  const int gm = min(tiles_m - first_m, GM);
-  const int in = lid - grp * per_group;
-  *tm = first_m + in % gm;
-  *tn = in / gm;
-}
-
 }  // namespace
-
-template <int CORE, int RB, bool BIAS>
-__global__ void __launch_bounds__(NTHREADS, 2)
-k_gemm2(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __half* __restrict__ t,
-        const uint8_t* __restrict__ wq, const __half* __restrict__ ws, const __half* __restrict__ l2,
-        const __half* __restrict__ bias, const float* __restrict__ lam, int M, int N, int K,
-        __half* __restrict__ y) {
-  using C = CoreCfg<CORE>;
-  constexpr int R = RB * 16;
-  constexpr int KC = 2;                                  // groups per stage
-  constexpr int TILE_BYTES = BM * C::LS;                 // one operand tile of one group in LDS
-  constexpr int GROUP_BYTES = 2 * TILE_BYTES + 256 * 2;  // A, B, 128 + 128 fp16 scales
-  constexpr int STAGE_BYTES = KC * GROUP_BYTES;
-  // The MFMA partial of one group times PFACT is P_g (the operands are 16q).
-  // Every rescaled partial carries the same factor, so it is applied once to the
-  // accumulator (exact: a power of two) before the branch is added.
-  constexpr float PFACT = 1.0f / 256.0f;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE_BYTES];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, r32 = lane & 31;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int G = K >> 6;
-  const int NS = (G + KC - 1) / KC;                       // stages
-
-  // ---- per-thread staging assignment (global -> registers -> LDS)
-  // codes and scales are group-major ([K/64][rows][32], [K/64][rows]): a tile's rows of one
-  // group are contiguous
-  const uint8_t* src[C::CHUNKS];
-  size_t gstep[C::CHUNKS];                                // bytes between consecutive groups
-  int dst[C::CHUNKS];
-  bool ok[C::CHUNKS];
-#pragma unroll
-  for (int i = 0; i < C::CHUNKS; i++) {
-    const int c = tid + NTHREADS * i;                        // chunk id over both tiles
-    const int per_tile = BM * C::CHUNKS;
-    const int tile = c / per_tile, rr = c % per_tile;
-    const int row = rr / C::CHUNKS, part = rr % C::CHUNKS;
-    const int grow = (tile == 0 ? m0 : n0) + row;
-    ok[i] = grow < (tile == 0 ? M : N);
-    // rows past the edge re-read row 0 of the tile's operand and are never stored
-    src[i] = (tile == 0 ? xq : wq) + (size_t)(ok[i] ? grow : 0) * C::GB + part * 16;
-    gstep[i] = (size_t)(tile == 0 ? M : N) * C::GB;
-    dst[i] = tile * TILE_BYTES + row * C::LS + part * 16;
-  }
-  // scale staging: thread < 128 -> sx of row m0+tid, else sw of column n0+tid-128 (raw fp16)
-  const bool s_is_x = tid < 128;
-  const int s_row = (s_is_x ? m0 : n0) + (tid & 127);
-  const bool s_ok = s_row < (s_is_x ? M : N);
-  const unsigned short* s_base = reinterpret_cast<const unsigned short*>(s_is_x ? xs : ws);
-  const unsigned short* s_ptr = s_base + (s_ok ? s_row : 0);
-  const size_t s_step = (size_t)(s_is_x ? M : N);   // between consecutive groups
-
-  uint4 stage_reg[KC][C::CHUNKS];
-  unsigned short stage_s[KC];
-  auto load_stage = [&](int st) {
-#pragma unroll
-    for (int k = 0; k < KC; k++) {
-      const int g = min(st * KC + k, G - 1);   // a group past the end re-reads the last one (unused)
-#pragma unroll
-      for (int i = 0; i < C::CHUNKS; i++) stage_reg[k][i] = *reinterpret_cast<const uint4*>(src[i] + (size_t)g * gstep[i]);
-      stage_s[k] = s_ptr[(size_t)g * s_step];
-    }
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int k = 0; k < KC; k++) {
-      uint8_t* base = lds + buf * STAGE_BYTES + k * GROUP_BYTES;
-#pragma unroll
-      for (int i = 0; i < C::CHUNKS; i++) {
-        uint4 v = ok[i] ? stage_reg[k][i] : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(base + dst[i]) = v;
-      }
-      reinterpret_cast<unsigned short*>(base + 2 * TILE_BYTES)[tid] = s_ok ? stage_s[k] : (unsigned short)0;
-    }
-  };
-
-  v16f acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; a++)
-#pragma unroll
-    for (int b = 0; b < 2; b++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
-
-  load_stage(0);
-  store_stage(0);
-  if (NS > 1) load_stage(1);
-  __syncthreads();
-
-  const int arow0 = wm * 64 + r32;          // LDS row of this lane's A operand (tile 0)
-  const int brow0 = wn * 64 + r32;
-  const int a_off = arow0 * C::LS + h * 16;
-  const int b_off = TILE_BYTES + brow0 * C::LS + h * 16;
-  const int sx_off = 2 * TILE_BYTES + 2 * arow0;
-  const int sw_off = 2 * TILE_BYTES + 2 * (128 + brow0);
-  for (int st = 0; st < NS; st++) {
-    const int buf = st & 1;
-#pragma unroll
-    for (int k = 0; k < KC; k++) {
-      if (st * KC + k >= G) break;
-      const uint8_t* base = lds + buf * STAGE_BYTES + k * GROUP_BYTES;
-      // scale operands for the outer product S = sx sw^T on v_mfma_f32_32x32x16_f16: the
-      // scale sits in K-slot 0 (element 0 of the lanes of the first half), every other slot
-      // is zero, so the MFMA returns sx[m] * sw[n] exactly (fp16 x fp16 in fp32) in the
-      // accumulator layout of the partials.
-      v8h sa[2], sb[2];
-#pragma unroll
-      for (int i = 0; i < 2; i++) {
-        const unsigned short xa = *reinterpret_cast<const unsigned short*>(base + sx_off + 64 * i);
-        const unsigned short xb = *reinterpret_cast<const unsigned short*>(base + sw_off + 64 * i);
-        sa[i] = as_h8(make_uint4(h ? 0u : (uint32_t)xa, 0u, 0u, 0u));
-        sb[i] = as_h8(make_uint4(h ? 0u : (uint32_t)xb, 0u, 0u, 0u));
-      }
-      v4i a[2][2], b[2][2];
-#pragma unroll
-      for (int i = 0; i < 2; i++) {
-        const uint4 ua = *reinterpret_cast<const uint4*>(base + a_off + i * 32 * C::LS);
-        const uint4 ub = *reinterpret_cast<const uint4*>(base + b_off + i * 32 * C::LS);
-        a[i][0] = v4i{(int)nib_lo16(ua.x), (int)nib_hi16(ua.x), (int)nib_lo16(ua.y), (int)nib_hi16(ua.y)};
-        a[i][1] = v4i{(int)nib_lo16(ua.z), (int)nib_hi16(ua.z), (int)nib_lo16(ua.w), (int)nib_hi16(ua.w)};
-        b[i][0] = v4i{(int)nib_lo16(ub.x), (int)nib_hi16(ub.x), (int)nib_lo16(ub.y), (int)nib_hi16(ub.y)};
-        b[i][1] = v4i{(int)nib_lo16(ub.z), (int)nib_hi16(ub.z), (int)nib_lo16(ub.w), (int)nib_hi16(ub.w)};
-      }
-#pragma unroll
-      for (int ti = 0; ti < 2; ti++)
-#pragma unroll
-        for (int tj = 0; tj < 2; tj++) {
-          v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ti][0], b[tj][0], v16i{}, 0, 0, 0);
-          p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ti][1], b[tj][1], p, 0, 0, 0);
-          const v16f sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[ti], sb[tj], v16f{}, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 16; i++) acc[ti][tj][i] = __builtin_fmaf((float)p[i], sc[i], acc[ti][tj][i]);
-        }
-    }
-    // keep the next stage's LDS writes (and their wait on the global loads) after this compute
-    __builtin_amdgcn_sched_barrier(0);
-    if (st + 1 < NS) {
-      store_stage(buf ^ 1);
-      if (st + 2 < NS) load_stage(st + 2);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int a = 0; a < 2; a++)
-#pragma unroll
-    for (int b = 0; b < 2; b++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) acc[a][b][i] *= PFACT;
-
-  // ---- epilogue: up projection T L2 on the matrix core, bias, fp16 store
-  int arow[2], bcol[2];
-  bool aok[2], bok[2];
-#pragma unroll
-  for (int i = 0; i < 2; i++) {
-    arow[i] = m0 + arow0 + i * 32; aok[i] = arow[i] < M;
-    bcol[i] = n0 + brow0 + i * 32; bok[i] = bcol[i] < N;
-  }
-  if (RB > 0) {
-#pragma unroll
-    for (int kb = 0; kb < RB; kb++) {
-      uint4 ta[2], lb[2];
-#pragma unroll
-      for (int i = 0; i < 2; i++) {
-        ta[i] = aok[i] ? *reinterpret_cast<const uint4*>(t + (size_t)arow[i] * R + kb * 16 + 8 * h) : make_uint4(0, 0, 0, 0);
-        uint16_t hv[8];
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-          hv[e] = bok[i] ? __half_as_ushort(l2[(size_t)(kb * 16 + 8 * h + e) * N + bcol[i]]) : (uint16_t)0;
-        lb[i] = make_uint4(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16),
-                           hv[4] | ((uint32_t)hv[5] << 16), hv[6] | ((uint32_t)hv[7] << 16));
-      }
-#pragma unroll
-      for (int ti = 0; ti < 2; ti++)
-#pragma unroll
-        for (int tj = 0; tj < 2; tj++)
-          acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(ta[ti]), as_h8(lb[tj]), acc[ti][tj], 0, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int tj = 0; tj < 2; tj++) {
-    if (!bok[tj]) continue;
-    const float bv = BIAS ? __half2float(bias[bcol[tj]]) : 0.f;
-    const float lv = lam ? lam[bcol[tj]] : 0.f;   // with the MLP glue folded in: the next layer's factor
-#pragma unroll
-    for (int ti = 0; ti < 2; ti++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int mrow = m0 + wm * 64 + ti * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        uint32_t hv = __half_as_ushort(__float2half_rn(acc[ti][tj][i] + bv));
-        if (lam) hv = gelu_div_h(hv, lv);        // fp16(gelu(y) / lam)
-        if (mrow < M) y[(size_t)mrow * N + bcol[tj]] = __ushort_as_half((unsigned short)hv);
-      }
-  }
-}
 
 // Few token rows (the weight-streaming regime, M <= 256): one workgroup per 32 output columns
 // and a slab of up to 128 rows (MT tiles of 32; blockIdx.y picks the slab), so each weight row
@@ -439,6 +201,151 @@ k_gemm2_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, co
   }
 }
 
+// The tiled kernel on the shared persistent LDS-DMA skeleton (gemm_skel.h), in stages of three
+// groups (fc1 shape: 306 us against 309 with four and 313 with two; the register-staged kernel
+// it replaced took 334).  Per group and workgroup each operand's 128 rows x 32 code bytes arrive by 16-byte
+// LDS-DMA loads into 16-byte slots swapped by row (slot c of row r at c ^ ((r / 8) % 2)), and
+// the rows' fp16 scales by 2-byte loads into 4-byte slots.  Lane half h reads the group's codes
+// 32 h .. 32 h + 31 of its rows (one 16-byte read), unpacked to 16 q for the two
+// v_mfma_i32_32x32x32_i8 (the same K order for both operands), so each partial is 256 P_g and
+// the accumulator is scaled by 1/256 once per tile (exact).
+using skel::dma16;
+using skel::dma2;
+using skel::scale_operand;
+
+struct OpI4 {
+  static constexpr int KC = 3;               // groups per stage
+  static constexpr int L_X = 0, L_W = 4096, L_SX = 8192, L_SW = 8704, GROUP = 9216;
+  static constexpr int BUF = KC * GROUP;
+  int M, N, K, G, NS;
+  int lane, h, wave;
+  rsrc_t rx, rw, rs;
+  int xo[2], wo[2], sxo[2], swo[2];          // per-lane LDS read offsets within a group
+
+  struct Src {
+    uint32_t vx, vw, vs;
+  };
+  struct Regs {
+    uint4 x[KC][2], w[KC][2];
+    uint32_t sx[KC][2], sw[KC][2];
+  };
+
+  __device__ OpI4(const uint8_t* xq, const __half* xs, const uint8_t* wq, const __half* ws, int M_, int N_, int K_)
+      : M(M_), N(N_), K(K_) {
+    G = K >> 6;
+    NS = (G + KC - 1) / KC;
+    lane = threadIdx.x & 63;
+    h = lane >> 5;
+    wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    rx = make_rsrc(xq, (size_t)M * K / 2);
+    rw = make_rsrc(wq, (size_t)N * K / 2);
+    rs = wave < 2 ? make_rsrc(xs, (size_t)M * G * 2) : make_rsrc(ws, (size_t)N * G * 2);
+    const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const int xr = wm * 64 + i * 32 + r32, wr = wn * 64 + i * 32 + r32;
+      xo[i] = L_X + xr * 32 + 16 * (h ^ ((xr >> 3) & 1));
+      wo[i] = L_W + wr * 32 + 16 * (h ^ ((wr >> 3) & 1));
+      sxo[i] = L_SX + xr * 4;
+      swo[i] = L_SW + wr * 4;
+    }
+  }
+
+  // wave w loads rows 32 w .. 32 w + 31 of both code tiles (lane -> row lane / 2, slot
+  // lane % 2 holding the swapped piece) and rows 64 (w % 2) .. + 63 of the X (w < 2) or W
+  // scales.  Rows past the edge re-read the last row (their outputs are never stored).
+  __device__ Src src(int m0, int n0) const {
+    const int row = wave * 32 + (lane >> 1);
+    const int c = (lane & 1) ^ ((row >> 3) & 1);
+    Src s;
+    s.vx = (uint32_t)min(m0 + row, M - 1) * 32u + 16u * c;
+    s.vw = (uint32_t)min(n0 + row, N - 1) * 32u + 16u * c;
+    const int srow = (wave & 1) * 64 + lane;
+    s.vs = wave < 2 ? (uint32_t)min(m0 + srow, M - 1) * 2u : (uint32_t)min(n0 + srow, N - 1) * 2u;
+    return s;
+  }
+  __device__ void load(const Src& s, int st, uint8_t* buf) const {
+#pragma unroll
+    for (int k = 0; k < KC; k++) {
+      const int g = min(st * KC + k, G - 1);  // a group past the end re-reads the last one (unused)
+      uint8_t* b = buf + k * GROUP;
+      dma16(rx, b + L_X + wave * 1024, s.vx, (uint32_t)g * (uint32_t)M * 32u);
+      dma16(rw, b + L_W + wave * 1024, s.vw, (uint32_t)g * (uint32_t)N * 32u);
+      dma2(rs, b + (wave < 2 ? L_SX : L_SW) + (wave & 1) * 256, s.vs, (uint32_t)g * (uint32_t)(wave < 2 ? M : N) * 2u);
+    }
+  }
+  __device__ void read(const uint8_t* buf, int st, Regs& r) const {
+#pragma unroll
+    for (int k = 0; k < KC; k++) {
+      if (st * KC + k >= G) break;
+      const uint8_t* b = buf + k * GROUP;
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        r.x[k][i] = *reinterpret_cast<const uint4*>(b + xo[i]);
+        r.w[k][i] = *reinterpret_cast<const uint4*>(b + wo[i]);
+        r.sx[k][i] = *reinterpret_cast<const uint32_t*>(b + sxo[i]);
+        r.sw[k][i] = *reinterpret_cast<const uint32_t*>(b + swo[i]);
+      }
+    }
+  }
+  __device__ void finish(v16f (&acc)[2][2]) const {
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+      for (int b = 0; b < 2; b++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) acc[a][b][i] *= 1.0f / 256.0f;
+  }
+  __device__ void mma(const Regs& r, int st, v16f (&acc)[2][2]) const {
+#pragma unroll
+    for (int k = 0; k < KC; k++) {
+      if (st * KC + k >= G) break;
+      v4i w[2][2], x[2][2];
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        const uint4 a = r.w[k][i], c = r.x[k][i];
+        w[i][0] = v4i{(int)nib_lo16(a.x), (int)nib_hi16(a.x), (int)nib_lo16(a.y), (int)nib_hi16(a.y)};
+        w[i][1] = v4i{(int)nib_lo16(a.z), (int)nib_hi16(a.z), (int)nib_lo16(a.w), (int)nib_hi16(a.w)};
+        x[i][0] = v4i{(int)nib_lo16(c.x), (int)nib_hi16(c.x), (int)nib_lo16(c.y), (int)nib_hi16(c.y)};
+        x[i][1] = v4i{(int)nib_lo16(c.z), (int)nib_hi16(c.z), (int)nib_lo16(c.w), (int)nib_hi16(c.w)};
+      }
+#pragma unroll
+      for (int tj = 0; tj < 2; tj++)
+#pragma unroll
+        for (int ti = 0; ti < 2; ti++) {
+          v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(w[tj][0], x[ti][0], v16i{}, 0, 0, 0);
+          p = __builtin_amdgcn_mfma_i32_32x32x32_i8(w[tj][1], x[ti][1], p, 0, 0, 0);
+          const v16f sc = __builtin_amdgcn_mfma_f32_32x32x8f16(scale_operand(r.sw[k][tj], h),
+                                                                scale_operand(r.sx[k][ti], h), v16f{}, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 16; i++) acc[tj][ti][i] = __builtin_fmaf((float)p[i], sc[i], acc[tj][ti][i]);
+        }
+    }
+  }
+};
+
+template <int RB, bool BIAS>
+__global__ void __launch_bounds__(skel::NT, 2)
+k_gemm2_lds(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __half* __restrict__ t,
+            const uint8_t* __restrict__ wq, const __half* __restrict__ ws, const __half* __restrict__ l2,
+            const __half* __restrict__ bias, const float* __restrict__ lam, int M, int N, int K,
+            __half* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * OpI4::BUF];
+  OpI4 op(xq, xs, wq, ws, M, N, K);
+  const int tiles = ((M + skel::BM - 1) / skel::BM) * ((N + skel::BN - 1) / skel::BN);
+  skel::persistent<OpI4, RB, BIAS>(op, lds, t, l2, bias, lam, M, N, tiles, y);
+}
+
+template <int RB, bool BIAS>
+static hipError_t launch_g2_lds(const GemmArgs& a, hipStream_t s) {
+  const int tiles = ((a.M + skel::BM - 1) / skel::BM) * ((a.N + skel::BN - 1) / skel::BN);
+  const int nb = tiles < resident_workgroups() ? tiles : resident_workgroups();
+  hipLaunchKernelGGL((k_gemm2_lds<RB, BIAS>), dim3(nb), dim3(skel::NT), 0, s, (const uint8_t*)a.xq,
+                     (const __half*)a.xs, (const __half*)a.t, (const uint8_t*)a.wq, (const __half*)a.ws,
+                     (const __half*)a.l2, (const __half*)a.bias, a.lam, a.M, a.N, a.K, (__half*)a.y);
+  return hipGetLastError();
+}
+
 // Up to this many token rows the weight-streaming kernel runs (in 128-row slabs).
 constexpr int kSkinnyRows2 = 256;
 
@@ -451,33 +358,29 @@ static hipError_t launch_g2_skinny(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int CORE, int RB, bool BIAS>
+template <int RB, bool BIAS>
 static hipError_t launch_g2(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 32) return launch_g2_skinny<RB, BIAS, 1>(a, s);
   if (a.M <= 64) return launch_g2_skinny<RB, BIAS, 2>(a, s);
   if (a.M <= kSkinnyRows2) return launch_g2_skinny<RB, BIAS, 4>(a, s);
-  const int nb = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((k_gemm2<CORE, RB, BIAS>), dim3(nb), dim3(NTHREADS), 0, s, (const uint8_t*)a.xq,
-                     (const __half*)a.xs, (const __half*)a.t, (const uint8_t*)a.wq, (const __half*)a.ws,
-                     (const __half*)a.l2, (const __half*)a.bias, a.lam, a.M, a.N, a.K, (__half*)a.y);
-  return hipGetLastError();
+  return launch_g2_lds<RB, BIAS>(a, s);
 }
 
-template <int CORE, bool BIAS>
+template <bool BIAS>
 static hipError_t launch_g2_r(const GemmArgs& a, hipStream_t s) {
   switch (a.r) {
-    case 0: return launch_g2<CORE, 0, BIAS>(a, s);
-    case 16: return launch_g2<CORE, 1, BIAS>(a, s);
-    case 32: return launch_g2<CORE, 2, BIAS>(a, s);
-    case 48: return launch_g2<CORE, 3, BIAS>(a, s);
-    case 64: return launch_g2<CORE, 4, BIAS>(a, s);
+    case 0: return launch_g2<0, BIAS>(a, s);
+    case 16: return launch_g2<1, BIAS>(a, s);
+    case 32: return launch_g2<2, BIAS>(a, s);
+    case 48: return launch_g2<3, BIAS>(a, s);
+    case 64: return launch_g2<4, BIAS>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm2(const GemmArgs& a, hipStream_t s) {
   const bool b = a.bias != nullptr;
-  if (a.fmt == FMT_INT4) return b ? launch_g2_r<CORE_I4, true>(a, s) : launch_g2_r<CORE_I4, false>(a, s);
+  if (a.fmt == FMT_INT4) return b ? launch_g2_r<true>(a, s) : launch_g2_r<false>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -162,6 +162,7 @@ struct OpF4 {
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(wv), as_h8(xv), acc, 0, 0, 0);
     }
   }
+  __device__ void finish(v16f (&)[2][2]) const {}
   __device__ void mma(const Regs& r, int st, v16f (&acc)[2][2]) const {
 #pragma unroll
     for (int k = 0; k < KC; k++) {

@@ -111,6 +111,7 @@ struct OpI8 {
       }
     }
   }
+  __device__ void finish(v16f (&)[2][2]) const {}
   __device__ void mma(const Regs& r, int st, v16f (&acc)[2][2]) const {
 #pragma unroll
     for (int k = 0; k < KC; k++) {

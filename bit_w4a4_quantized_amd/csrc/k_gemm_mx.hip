@@ -137,6 +137,7 @@ struct OpMX {
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);   // zero codes: the unit adds exactly +0
     acc = mx_mma(zero ? z : o.w, zero ? z : o.x, o.sw, o.sx, acc);
   }
+  __device__ void finish(v16f (&)[2][2]) const {}
   __device__ void mma(const Regs& r, int st, v16f (&acc)[2][2]) const {
 #pragma unroll
     for (int k = 0; k < KC; k++) {

@@ -9,7 +9,6 @@
 namespace svdq {
 
 enum Fmt { FMT_INT4 = 0, FMT_INT8 = 1, FMT_FP4 = 2, FMT_INT4_E2M3 = 3, FMT_MXFP4 = 4 };
-enum Core { CORE_E2M3 = 0, CORE_I4 = 1 };
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
