@@ -35,7 +35,7 @@ __device__ __forceinline__ uint32_t nib_hi16(uint32_t w) { return w & 0xF0F0F0F0
 
 // Few token rows (the weight-streaming regime, M <= 256): one workgroup per 32 output columns
 // and a slab of up to 128 rows (MT tiles of 32; blockIdx.y picks the slab), so each weight row
-// is read once per slab, in its packed layout (half the bytes of the 6-bit container).  The
+// is read once per slab, in its packed layout (2/3 of the 6-bit container's bytes).  The
 // four waves split K (groups w, w + 4, ...), each holding PD groups of loads in flight straight
 // into registers: lane (r32, h) loads the 16 bytes of codes 32 h .. 32 h + 31 of its weight row
 // and of each of its token rows, which, unpacked to 16 q with two masks and a shift, are its
