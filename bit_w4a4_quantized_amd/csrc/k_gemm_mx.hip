@@ -153,6 +153,422 @@ struct OpMX {
 
 }  // namespace
 
+namespace {
+
+// ---------------------------------------------------------------------------------------------
+// Large tiles.  With 128 x 128 tiles each CU stages 17 KB per chunk (LDS-DMA) for 32 tile-groups
+// and its waves read 32 KB of operand fragments from LDS.  Here one workgroup of WM x WN waves
+// per CU owns a BM x BN tile and each wave a TI x TJ block of 32 x 32 tiles: at 256 x 256 with
+// 2 x 4 per wave, 17 KB of LDS-DMA per chunk serve 64 tile-groups, and each wave reads 6
+// fragments for 8 MFMAs instead of 4 for 4.  The accumulators stay with the matrix cores (no
+// vector work per chunk), so 128 of them fit.  Codes, scales and the swapped 16-byte slots are
+// those of the 128 x 128 kernel; K goes through a ring of four LDS buffers (below).  Chunks are
+// added in the same order and the epilogue makes the same operations, so the output is
+// bit-identical to the 128 x 128 kernel's.
+template <int WM_, int WN_, int TI_, int TJ_, int KC_>
+struct Big {
+  static constexpr int WM = WM_, WN = WN_, TI = TI_, TJ = TJ_, KC = KC_;
+  static constexpr int NW = WM * WN, NTH = 64 * NW;
+  static constexpr int BM = WM * TI * 32, BN = WN * TJ * 32;
+  static constexpr int L_X = 0, L_W = BM * 32, L_SX = L_W + BN * 32, L_SW = L_SX + BM * 4;
+  static constexpr int CHUNK = L_SW + BN * 4;
+  static constexpr int BUF = KC * CHUNK;
+  // LDS-DMA instructions per chunk: 32 code rows or 64 scale rows each
+  static constexpr int NX = BM / 32, NWC = BN / 32, NSX = BM / 64, NSW = BN / 64;
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "scale rows go 64 to an instruction");
+};
+
+template <class C>
+struct BigOp {
+  // a wave's LDS-DMA instructions per chunk: code slots j (instruction wave + j NW of the NX
+  // X-row and NWC W-row ones, 32 rows each) and scale slots (of the NSX + NSW, 64 rows each);
+  // the kind of each slot is fixed for the wave, so its resource, LDS offset and chunk stride
+  // are set once
+  static constexpr int NCODE = C::NX + C::NWC, NSCALE = C::NSX + C::NSW;
+  static constexpr int PC = (NCODE + C::NW - 1) / C::NW, PS = (NSCALE + C::NW - 1) / C::NW;
+  int M, N, C_, NS;
+  int lane, h, wave, wm, wn;
+  rsrc_t crs[PC], srs[PS];
+  int cdst[PC], sdst[PS];                    // LDS offsets within a chunk
+  uint32_t cstr[PC], sstr[PS];               // global bytes per chunk
+  struct Frag {
+    uint4 x[C::TI], w[C::TJ];
+    uint32_t sx[C::TI], sw[C::TJ];
+  };
+  struct Src {
+    uint32_t c[PC], s[PS];
+  };
+
+  __device__ BigOp(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, int M_, int N_, int K)
+      : M(M_), N(N_) {
+    C_ = K >> 6;
+    NS = (C_ + C::KC - 1) / C::KC;
+    lane = threadIdx.x & 63;
+    h = lane >> 5;
+    wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    wm = wave / C::WN;
+    wn = wave % C::WN;
+    const rsrc_t rx = make_rsrc(xq, (size_t)M * K / 2), rw = make_rsrc(wq, (size_t)N * K / 2);
+    const rsrc_t rsx = make_rsrc(xs, (size_t)M * K / 32), rsw = make_rsrc(ws, (size_t)N * K / 32);
+#pragma unroll
+    for (int j = 0; j < PC; j++) {
+      const int i = wave + j * C::NW;
+      const bool isx = i < C::NX;
+      crs[j] = isx ? rx : rw;
+      cdst[j] = isx ? C::L_X + i * 1024 : C::L_W + (i - C::NX) * 1024;
+      cstr[j] = (uint32_t)(isx ? M : N) * 32u;
+    }
+#pragma unroll
+    for (int j = 0; j < PS; j++) {
+      const int i = wave + j * C::NW;
+      const bool isx = i < C::NSX;
+      srs[j] = isx ? rsx : rsw;
+      sdst[j] = isx ? C::L_SX + i * 256 : C::L_SW + (i - C::NSX) * 256;
+      sstr[j] = (uint32_t)(isx ? M : N) * 2u;
+    }
+  }
+
+  // per-lane global offsets of the slots for the tile at (m0, n0): a code slot's lane l moves
+  // row 32 i' + l / 2 (i' its instruction within X or W), into LDS slot l % 2, which holds piece
+  // (l % 2) ^ ((row / 8) % 2); a scale slot's lane l moves row 64 i' + l.  Rows past the edge
+  // re-read the last row.
+  __device__ Src src(int m0, int n0) const {
+    Src o;
+#pragma unroll
+    for (int j = 0; j < PC; j++) {
+      const int i = wave + j * C::NW;
+      const bool isx = i < C::NX;
+      const int row = (isx ? i : i - C::NX) * 32 + (lane >> 1);
+      const int piece = (lane & 1) ^ ((row >> 3) & 1);
+      o.c[j] = (uint32_t)(isx ? min(m0 + row, M - 1) : min(n0 + row, N - 1)) * 32u + 16u * (uint32_t)piece;
+    }
+#pragma unroll
+    for (int j = 0; j < PS; j++) {
+      const int i = wave + j * C::NW;
+      const bool isx = i < C::NSX;
+      const int row = (isx ? i : i - C::NSX) * 64 + lane;
+      o.s[j] = (uint32_t)(isx ? min(m0 + row, M - 1) : min(n0 + row, N - 1)) * 2u;
+    }
+    return o;
+  }
+  __device__ void load(const Src& v, int st, uint8_t* buf) const {
+#pragma unroll
+    for (int k = 0; k < C::KC; k++) {
+      const uint32_t c = (uint32_t)min(st * C::KC + k, C_ - 1);  // past the end: the last chunk again (unused)
+      uint8_t* b = buf + k * C::CHUNK;
+#pragma unroll
+      for (int j = 0; j < PC; j++)
+        if (NCODE % C::NW == 0 || wave + j * C::NW < NCODE) dma16(crs[j], b + cdst[j], v.c[j], c * cstr[j]);
+#pragma unroll
+      for (int j = 0; j < PS; j++)
+        if (NSCALE % C::NW == 0 || wave + j * C::NW < NSCALE) dma2(srs[j], b + sdst[j], v.s[j], c * sstr[j]);
+    }
+  }
+  // lane (r32, h) reads codes 32 h .. 32 h + 31 (one 16-byte slot) and scale byte h of its rows
+  __device__ void read(const uint8_t* b, Frag& f) const {
+    const int r32 = lane & 31;
+    const int xr = wm * C::TI * 32 + r32, wr = wn * C::TJ * 32 + r32;
+    const int xo = C::L_X + xr * 32 + 16 * (h ^ ((xr >> 3) & 1));   // + 1024 per 32-row tile
+    const int wo = C::L_W + wr * 32 + 16 * (h ^ ((wr >> 3) & 1));
+#pragma unroll
+    for (int ti = 0; ti < C::TI; ti++) {
+      f.x[ti] = *reinterpret_cast<const uint4*>(b + xo + ti * 1024);
+      f.sx[ti] = (*reinterpret_cast<const uint32_t*>(b + C::L_SX + (xr + ti * 32) * 4) >> (8 * h)) & 0xFFu;
+    }
+#pragma unroll
+    for (int tj = 0; tj < C::TJ; tj++) {
+      f.w[tj] = *reinterpret_cast<const uint4*>(b + wo + tj * 1024);
+      f.sw[tj] = (*reinterpret_cast<const uint32_t*>(b + C::L_SW + (wr + tj * 32) * 4) >> (8 * h)) & 0xFFu;
+    }
+  }
+  __device__ void mma(const Frag& f, v16f (&acc)[C::TJ][C::TI]) const {
+#pragma unroll
+    for (int tj = 0; tj < C::TJ; tj++)
+#pragma unroll
+      for (int ti = 0; ti < C::TI; ti++) acc[tj][ti] = mx_mma(f.w[tj], f.x[ti], f.sw[tj], f.sx[ti], acc[tj][ti]);
+  }
+};
+
+// Workgroup barriers that leave loads from global memory in flight (a __syncthreads() would wait
+// for every LDS-DMA load of the ring): the wave's LDS operations complete, and with N, its
+// vector-memory operations but the N most recent ones.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void vm_lds_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+
+// acc += T L2 (RB > 0), bias, fp16 store: the 128 x 128 epilogue's operations for a TI x TJ block
+// of tiles per wave.  eb: epilogue LDS, free.  Its own global loads go out first, then issue()
+// (the next tile's loads), so that waiting for them does not wait for those.  Ends with an
+// LDS-only barrier.
+template <class C, int RB, bool BIAS, class Issue>
+__device__ __forceinline__ void big_epilogue(v16f (&acc)[C::TJ][C::TI], uint8_t* eb, const __half* __restrict__ t,
+                                             const __half* __restrict__ l2, const __half* __restrict__ bias,
+                                             const float* __restrict__ lam, int M, int N, int m0, int n0,
+                                             __half* __restrict__ y, Issue&& issue) {
+  constexpr int R = RB * 16;
+  constexpr int LS2 = (R + 8) * 2;           // L2 staged transposed: [n][k], row stride R + 8 halves
+  constexpr int L2P = RB > 0 ? (R * (C::BN / 8) + C::NTH - 1) / C::NTH : 1;   // 8-column pieces per thread
+  constexpr int NG = (C::TJ + 1) / 2;        // output column groups of (up to) two tiles
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, r32 = lane & 31;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int mw = m0 + wm * C::TI * 32, nw = n0 + wn * C::TJ * 32;   // the wave's block
+  // ---- the epilogue's global loads
+  uint4 lv[L2P];
+  uint4 top[RB > 0 ? RB : 1][C::TI];
+  if (RB > 0) {
+#pragma unroll
+    for (int j = 0; j < L2P; j++) {
+      const int idx = tid + j * C::NTH;
+      const int k = idx % R, c8 = idx / R;
+      const int n = n0 + c8 * 8;
+      lv[j] = make_uint4(0, 0, 0, 0);
+      if (idx < R * (C::BN / 8) && n < N) lv[j] = *reinterpret_cast<const uint4*>(l2 + (size_t)k * N + n);
+    }
+#pragma unroll
+    for (int kb = 0; kb < RB; kb++)
+#pragma unroll
+      for (int ti = 0; ti < C::TI; ti++) {
+        const int m = min(mw + ti * 32 + r32, M - 1);
+        top[kb][ti] = *reinterpret_cast<const uint4*>(t + (size_t)m * R + kb * 16 + 8 * h);
+      }
+  }
+  uint2 braw[C::TJ][4];
+#pragma unroll
+  for (int tj = 0; tj < C::TJ; tj++)
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int n = nw + tj * 32 + 8 * q + 4 * h;
+      braw[tj][q] = make_uint2(0u, 0u);
+      if (BIAS && n < N) braw[tj][q] = *reinterpret_cast<const uint2*>(bias + n);
+    }
+  // with the MLP glue folded in, the next layer's factors of the 8 columns this lane stores per group
+  const rsrc_t rl = make_rsrc(lam, lam ? (size_t)N * 4 : 0);
+  float4 la[NG], lb[NG];
+#pragma unroll
+  for (int g = 0; g < NG; g++) {
+    const int pr = (C::TJ - 2 * g >= 2 ? 2 : 1) * 4;
+    const int cl = (lane % pr) * 8;
+    la[g] = load_f4(rl, nw + g * 64 + cl);
+    lb[g] = load_f4(rl, nw + g * 64 + cl + 4);
+  }
+  issue();
+  if (RB > 0) {
+#pragma unroll
+    for (int j = 0; j < L2P; j++) {
+      const int idx = tid + j * C::NTH;
+      const int k = idx % R, c8 = idx / R;
+      if (idx < R * (C::BN / 8)) {
+        const uint32_t w[4] = {lv[j].x, lv[j].y, lv[j].z, lv[j].w};
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+          *reinterpret_cast<uint16_t*>(eb + (c8 * 8 + e) * LS2 + k * 2) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int kb = 0; kb < RB; kb++)
+#pragma unroll
+      for (int tj = 0; tj < C::TJ; tj++) {
+        const uint4 lo =
+            *reinterpret_cast<const uint4*>(eb + (wn * C::TJ * 32 + tj * 32 + r32) * LS2 + (kb * 16 + 8 * h) * 2);
+#pragma unroll
+        for (int ti = 0; ti < C::TI; ti++)
+          acc[tj][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(lo), as_h8(top[kb][ti]), acc[tj][ti], 0, 0, 0);
+      }
+    lds_barrier();                           // the output staging reuses the L2 staging bytes
+  }
+  uint8_t* ys = eb + wave * 32 * E_YS;
+  // columns in groups of two tiles (64 columns; a lone tile last when TJ is odd): each lane
+  // stages its 16 values per tile as fp16 row pieces, then the group's rows leave as 16-byte
+  // pieces
+#pragma unroll
+  for (int g = 0; g < NG; g++) {
+    const int g0 = 2 * g;
+    const int gt = C::TJ - g0 >= 2 ? 2 : 1;   // tiles in the group
+    const int pr = gt * 4;                    // 16-byte pieces per staged row
+    const int cl = (lane % pr) * 8;           // this lane's 8 columns within the group
+#pragma unroll
+    for (int ti = 0; ti < C::TI; ti++) {
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        if (u >= gt) continue;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const uint2 br = braw[g0 + u][q];
+          const float bv[4] = {__half2float(__ushort_as_half((unsigned short)(br.x & 0xFFFFu))),
+                               __half2float(__ushort_as_half((unsigned short)(br.x >> 16))),
+                               __half2float(__ushort_as_half((unsigned short)(br.y & 0xFFFFu))),
+                               __half2float(__ushort_as_half((unsigned short)(br.y >> 16)))};
+          const int nl = u * 32 + 8 * q + 4 * h;
+          uint32_t hv[4];
+#pragma unroll
+          for (int j = 0; j < 4; j++) hv[j] = __half_as_ushort(__float2half_rn(acc[g0 + u][ti][4 * q + j] + bv[j]));
+          *reinterpret_cast<uint2*>(ys + r32 * E_YS + nl * 2) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's staging writes are done
+      __builtin_amdgcn_wave_barrier();
+      const int rows_it = 64 / pr;            // rows per pass
+#pragma unroll
+      for (int it = 0; it < 32 / rows_it; it++) {
+        const int rl = it * rows_it + lane / pr;
+        uint2 a = *reinterpret_cast<const uint2*>(ys + rl * E_YS + cl * 2);
+        uint2 b = *reinterpret_cast<const uint2*>(ys + rl * E_YS + cl * 2 + 8);
+        if (lam) {                           // the MLP glue folded in: fp16(gelu(y) / lam)
+          a.x = gelu_div_h(a.x & 0xFFFFu, la[g].x) | (gelu_div_h(a.x >> 16, la[g].y) << 16);
+          a.y = gelu_div_h(a.y & 0xFFFFu, la[g].z) | (gelu_div_h(a.y >> 16, la[g].w) << 16);
+          b.x = gelu_div_h(b.x & 0xFFFFu, lb[g].x) | (gelu_div_h(b.x >> 16, lb[g].y) << 16);
+          b.y = gelu_div_h(b.y & 0xFFFFu, lb[g].z) | (gelu_div_h(b.y >> 16, lb[g].w) << 16);
+        }
+        const int m = mw + ti * 32 + rl, n = nw + g0 * 32 + cl;
+        if (m < M && n < N) *reinterpret_cast<uint4*>(y + (size_t)m * N + n) = make_uint4(a.x, a.y, b.x, b.y);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the staging is read before it is rewritten
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  lds_barrier();                             // the buffer is refilled by the next tile's loads
+}
+
+}  // namespace
+
+// The persistent loop over BM x BN tiles: tiles blockIdx.x, + gridDim.x, ...  K goes in steps of
+// KC chunks through a ring of four LDS buffers (separate arrays, so that the compiler does not
+// make a buffer's reads wait for loads into another), three steps ahead: step s computes from
+// buffer s % 4 while the loads of steps s + 1 .. s + 3 are in flight, and each step ends with
+// every wave's loads of step s + 1 done and a barrier that leaves the later loads in flight.
+// Across a tile boundary the ring carries on into the next tile: its first step is loaded three
+// steps before the end, its second and third by the epilogue, which works in the buffer of the
+// tile's last step, after its own loads.
+template <class C, int RB, bool BIAS>
+__global__ void __launch_bounds__(C::NTH, 1)
+k_gemm_mxb(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const __half* __restrict__ t,
+           const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const __half* __restrict__ l2,
+           const __half* __restrict__ bias, const float* __restrict__ lam, int M, int N, int K,
+           __half* __restrict__ y) {
+  using Op = BigOp<C>;
+  static_assert(Op::NCODE % C::NW == 0 && Op::NSCALE % C::NW == 0, "every wave issues as many loads");
+  constexpr int LPS = C::KC * (Op::PC + Op::PS);   // LDS-DMA instructions per wave and step
+  static_assert(C::BUF >= C::NW * 32 * E_YS && C::BUF >= C::BN * (RB * 16 + 8) * 2, "the epilogue must fit a buffer");
+  __shared__ __attribute__((aligned(16))) uint8_t b0[C::BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t b1[C::BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t b2[C::BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t b3[C::BUF];
+  Op op(xq, xs, wq, ws, M, N, K);
+  const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
+  const int tiles = tiles_m * tiles_n;
+  const int NS = op.NS;
+  const int NSE = (NS + 3) & ~3;             // steps per tile: a multiple of the ring's four
+  auto origin = [&](int tile, int* m0, int* n0) {
+    int tm, tn;
+    tile_of(tile, tiles, tiles_m, tiles_n, &tm, &tn);
+    *m0 = tm * C::BM;
+    *n0 = tn * C::BN;
+  };
+
+  int tile = blockIdx.x;
+  int m0, n0;
+  origin(tile, &m0, &n0);
+  typename Op::Src cur = op.src(m0, n0);
+  op.load(cur, 0, b0);
+  op.load(cur, 1, b1);
+  op.load(cur, 2, b2);
+  vm_lds_barrier<2 * LPS>();
+  v16f acc[C::TJ][C::TI];
+  while (true) {
+    const int next = tile + (int)gridDim.x;
+    const bool has_next = next < tiles;
+    int m1, n1;
+    origin(has_next ? next : tile, &m1, &n1);   // without a next tile its loads re-read this one (unused)
+    const typename Op::Src nxt = op.src(m1, n1);
+#pragma unroll
+    for (int a = 0; a < C::TJ; a++)
+#pragma unroll
+      for (int b = 0; b < C::TI; b++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
+
+    // step st: compute from sb; with LOAD, first issue step lst's loads (of ls) into ob; then
+    // wait for all but the WAIT most recent loads and synchronise
+    auto step = [&](auto wait_c, auto load_c, int st, const uint8_t* sb, uint8_t* ob, const typename Op::Src& ls,
+                    int lst) {
+      typename Op::Frag f0, f1;
+      const bool live = st < NS;
+      if (live) op.read(sb, f0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (decltype(load_c)::value) op.load(ls, lst, ob);
+      __builtin_amdgcn_sched_barrier(0);
+      if (live) {
+#pragma unroll
+        for (int k = 0; k < C::KC; k++) {
+          if (st * C::KC + k >= op.C_) break;
+          typename Op::Frag& fc = (k & 1) ? f1 : f0;
+          typename Op::Frag& fn = (k & 1) ? f0 : f1;
+          if (k + 1 < C::KC && st * C::KC + k + 1 < op.C_) op.read(sb + (k + 1) * C::CHUNK, fn);
+          op.mma(fc, acc);
+        }
+      }
+      vm_lds_barrier<decltype(wait_c)::value>();
+    };
+    int st = 0;
+    for (; st < NSE - 4; st += 4) {
+      step(IC<2 * LPS>{}, IC<1>{}, st, b0, b3, cur, st + 3);
+      step(IC<2 * LPS>{}, IC<1>{}, st + 1, b1, b0, cur, st + 4);
+      step(IC<2 * LPS>{}, IC<1>{}, st + 2, b2, b1, cur, st + 5);
+      step(IC<2 * LPS>{}, IC<1>{}, st + 3, b3, b2, cur, st + 6);
+    }
+    step(IC<2 * LPS>{}, IC<1>{}, st, b0, b3, cur, st + 3);     // the tile's last step
+    step(IC<2 * LPS>{}, IC<1>{}, st + 1, b1, b0, nxt, 0);      // the next tile's first
+    step(IC<LPS>{}, IC<0>{}, st + 2, b2, b1, cur, 0);
+    step(IC<0>{}, IC<0>{}, st + 3, b3, b2, cur, 0);
+    big_epilogue<C, RB, BIAS>(acc, b3, t, l2, bias, lam, M, N, m0, n0, y, [&]() {
+      op.load(nxt, 1, b1);
+      op.load(nxt, 2, b2);
+    });
+    if (!has_next) break;
+    tile = next;
+    m0 = m1;
+    n0 = n1;
+    cur = nxt;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS-DMA in flight when the workgroup ends
+}
+
+// 256 x 256 tiles: waves of 64 x 128, two chunks a step
+using BigA = Big<4, 2, 2, 4, 2>;
+
+template <class C, int RB, bool BIAS>
+static hipError_t launch_mxb_t(const GemmArgs& a, hipStream_t s) {
+  const int tiles = ((a.M + C::BM - 1) / C::BM) * ((a.N + C::BN - 1) / C::BN);
+  const int cus = resident_workgroups() / 2;
+  const int nb = tiles < cus ? tiles : cus;
+  hipLaunchKernelGGL((k_gemm_mxb<C, RB, BIAS>), dim3(nb), dim3(C::NTH), 0, s, (const uint8_t*)a.xq,
+                     (const uint8_t*)a.xs, (const __half*)a.t, (const uint8_t*)a.wq, (const uint8_t*)a.ws,
+                     (const __half*)a.l2, (const __half*)a.bias, a.lam, a.M, a.N, a.K, (__half*)a.y);
+  return hipGetLastError();
+}
+
+template <class C, bool BIAS>
+static hipError_t launch_mxb_r(const GemmArgs& a, hipStream_t s) {
+  switch (a.r) {
+    case 0: return launch_mxb_t<C, 0, BIAS>(a, s);
+    case 16: return launch_mxb_t<C, 1, BIAS>(a, s);
+    case 32: return launch_mxb_t<C, 2, BIAS>(a, s);
+    case 48: return launch_mxb_t<C, 3, BIAS>(a, s);
+    case 64: return launch_mxb_t<C, 4, BIAS>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int RB, bool BIAS>
 __global__ void __launch_bounds__(NT, 2)
 k_gemm_mx(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const __half* __restrict__ t,
@@ -187,7 +603,30 @@ static hipError_t launch_mx_r(const GemmArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// Rounds of the 128 x 128 kernel: full rounds of its persistent loop, and a last partial round
+// whole, or, when it is at most a quarter of a round, as sub-tile jobs (about a quarter of a
+// round per job and workgroup).
+static double rounds_128(int M, int N, int slots) {
+  const long tiles = (long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (tiles <= slots) return 1.0;
+  const long full = tiles / slots, rem = tiles % slots;
+  if (rem == 0) return (double)full;
+  if (4 * rem <= slots) return (double)full + 0.25 * (double)((16 * rem + slots - 1) / slots);
+  return (double)(full + 1);
+}
+
+// One round of 256 x 256 tiles (one per CU) takes this many rounds of 128 x 128 tiles (two per
+// CU): measured at the fc1 shape (K = 3072) and the fc2 shape (K = 12288).
+constexpr double kBigRound = 1.68;
+
+// 256 x 256 tiles where their rounds cost less than the 128 x 128 kernel's (large M and N; at
+// few token rows most of a 256-row tile would be padding).
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t s) {
+  const int slots = resident_workgroups(), cus = slots / 2;
+  const long big_tiles = (long)((a.M + BigA::BM - 1) / BigA::BM) * ((a.N + BigA::BN - 1) / BigA::BN);
+  const double big = kBigRound * (double)((big_tiles + cus - 1) / cus);
+  if (big < rounds_128(a.M, a.N, slots))
+    return a.bias ? launch_mxb_r<BigA, true>(a, s) : launch_mxb_r<BigA, false>(a, s);
   return a.bias ? launch_mx_r<true>(a, s) : launch_mx_r<false>(a, s);
 }
 

@@ -181,9 +181,10 @@ def test_c2_fc2_e2m3_container():
     run_layer(prepared("c2_fc2", 32), "int4_e2m3", x_hat=fc2_input())
 
 
-@pytest.mark.parametrize("name", ["c1_qkv", "c2_fc1"])
+@pytest.mark.parametrize("name", ["c1_qkv", "c2_fc1", "c2_fc2"])
 def test_mxfp4_full_size(name):
-    run_layer(prepared(name, 32), "mxfp4")
+    # 256 x 256 tiles (fc2: K = 12288, one round)
+    run_layer(prepared(name, 32), "mxfp4", x_hat=fc2_input() if name == "c2_fc2" else None)
 
 
 def test_c2_mlp_pair_folded():

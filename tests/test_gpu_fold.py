@@ -101,6 +101,24 @@ def test_gemm_gelu_smooth_is_glue_of_gemm(fmt, shape, with_bias):
     assert rel_fro(host(folded), ref) <= TOL
 
 
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_gemm_gelu_smooth_mxfp4_large_tiles(with_bias):
+    # the 256 x 256 tile epilogue with the glue folded in (MXFP4, one round of large tiles on 256
+    # CUs, ragged edges)
+    fmt, M, K, N, r = "mxfp4", 4000, 192, 4000, 32
+    log(f"gemm_w4a4_up_gelu_smooth large tiles {fmt} M={M} K={K} N={N} r={r} bias={with_bias}")
+    x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs(fmt, M, K, N, r, 5 * M + N)
+    lam = np.exp(np.random.default_rng(N + 1).uniform(np.log(0.2), np.log(8.0), N)).astype(np.float32)
+    args = (dev(dev_codes(xst, fmt)), dev(dev_scales(xs, fmt)), dev(t), dev(dev_codes(wst, fmt)),
+            dev(dev_scales(ws, fmt)), dev(l2), dev(b) if with_bias else None)
+    folded = binding.svdq_gemm_w4a4_up_gelu_smooth(*args, dev(lam), K, fmt)
+    plain = binding.svdq_gemm_w4a4_up(*args, K, fmt)
+    glued = binding.svdq_gelu_tanh_smooth(plain, dev(lam))
+    assert same_bytes(host(folded), host(glued))
+    ref = oracle.forward.gelu_smooth(oracle.forward.linear(xq, xs, t, wq, ws, l2, b if with_bias else None, fmt), lam)
+    assert rel_fro(host(folded), ref) <= TOL
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,K,N,r", [(17, 192, 48, 32), (300, 320, 272, 32), (1, 64, 16, 0)])
 def test_linear_folded(fmt, M, K, N, r):

@@ -261,6 +261,28 @@ def test_gemm_partial_last_round_long_k(fmt):
     assert ok, worst
 
 
+# MXFP4 at sizes where the launch takes 256 x 256 tiles (on 256 CUs): one round with ragged last
+# tile row and column and padded ring steps (K = 192: three chunks in two-chunk steps); two
+# tiles per workgroup, so the ring runs on into the next tile, with a one-chunk last step
+# (K = 320) and r = 64; and four rounds, the last one partial, with a half-empty last tile row
+@pytest.mark.parametrize("M,K,N,r,with_bias", [(4000, 192, 4000, 32, True), (4000, 192, 4000, 0, False),
+                                               (4096, 320, 8192, 64, True), (4224, 128, 12288, 32, True)])
+def test_mxfp4_large_tiles(M, K, N, r, with_bias):
+    fmt = "mxfp4"
+    log(f"gemm_w4a4_up large tiles {fmt} M={M} K={K} N={N} r={r} bias={with_bias}")
+    x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs(fmt, M, K, N, r, 9 * M + K + r)
+    bias = b if with_bias else None
+    ref = oracle.forward.linear(xq, xs, t, wq, ws, l2, bias, fmt)
+    y = binding.svdq_gemm_w4a4_up(dev(dev_codes(xst, fmt)), dev(dev_scales(xs, fmt)), dev(t) if r else None,
+                                  dev(dev_codes(wst, fmt)), dev(dev_scales(ws, fmt)), dev(l2) if r else None,
+                                  dev(bias) if with_bias else None, K, fmt)
+    yg = host(y)
+    assert np.isfinite(yg.astype(np.float32)).all()
+    assert rel_fro(yg, ref) <= TOL
+    ok, worst = within_sum_bound(yg, ref, linear_abs_sum(xq, xs, t, wq, ws, l2, bias, fmt), gemm_terms(fmt, K, r))
+    assert ok, worst
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,K,N,r", [(17, 192, 48, 32), (130, 320, 272, 32), (257, 256, 144, 64), (1, 64, 16, 0)])
 def test_linear_end_to_end(fmt, M, K, N, r):
