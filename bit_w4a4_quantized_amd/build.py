@@ -93,12 +93,14 @@ MICROBENCH = os.path.join(BUILD_DIR, "mfma_valu")
 
 def build_microbench(verbose: bool = False) -> str:
     """The microbenchmarks, programs of their own (not part of the library): matrix-core /
-    vector-ALU overlap (microbench/mfma_valu.hip) and the operand load paths
-    (microbench/load_paths.hip).  Returns the first program's path."""
+    vector-ALU overlap (microbench/mfma_valu.hip), the operand load paths
+    (microbench/load_paths.hip) and the sustained matrix-core rates with the clock they hold
+    (microbench/mfma_clock.hip).  Returns the first program's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     _run([hipcc(), *FLAGS, os.path.join(HERE, "microbench", "mfma_valu.hip"), "-o", MICROBENCH], verbose)
-    _run([hipcc(), *FLAGS, os.path.join(HERE, "microbench", "load_paths.hip"), "-o",
-          os.path.join(BUILD_DIR, "load_paths")], verbose)
+    for prog in ("load_paths", "mfma_clock"):
+        _run([hipcc(), *FLAGS, os.path.join(HERE, "microbench", prog + ".hip"), "-o", os.path.join(BUILD_DIR, prog)],
+             verbose)
     return MICROBENCH
 
 
