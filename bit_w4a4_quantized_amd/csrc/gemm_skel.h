@@ -43,8 +43,8 @@ __host__ __device__ constexpr int epi_bytes(int R) {
   return BN * (R + 8) * 2 > 4 * 32 * E_YS ? BN * (R + 8) * 2 : 4 * 32 * E_YS;
 }
 
-// One wave's LDS-DMA load: lane l's 16 (4) bytes go to dst + 16 l (dst + 4 l); 2 bytes are
-// zero-extended to the dword at dst + 4 l.  dst must be wave-uniform.  Offsets go into the
+// One wave's LDS-DMA load: lane l's 16 (4) bytes go to dst + 16 l (dst + 4 l); 2 bytes or 1 byte
+// are zero-extended to the dword at dst + 4 l.  dst must be wave-uniform.  Offsets go into the
 // vector or scalar offset (the immediate would move the LDS destination as well).
 __device__ __forceinline__ void dma16(rsrc_t r, uint8_t* dst, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)voff, (int)soff, 0, 0);
@@ -54,6 +54,9 @@ __device__ __forceinline__ void dma4(rsrc_t r, uint8_t* dst, uint32_t voff, uint
 }
 __device__ __forceinline__ void dma2(rsrc_t r, uint8_t* dst, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 2, (int)voff, (int)soff, 0, 0);
+}
+__device__ __forceinline__ void dma1(rsrc_t r, uint8_t* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 1, (int)voff, (int)soff, 0, 0);
 }
 
 // Tile index -> output tile: contiguous ranges per XCD (workgroups are dealt round-robin to

@@ -161,21 +161,26 @@ namespace {
 // per CU owns a BM x BN tile and each wave a TI x TJ block of 32 x 32 tiles: at 256 x 256 with
 // 2 x 4 per wave, 17 KB of LDS-DMA per chunk serve 64 tile-groups, and each wave reads 6
 // fragments for 8 MFMAs instead of 4 for 4.  The accumulators stay with the matrix cores (no
-// vector work per chunk), so 128 of them fit.  Codes, scales and the swapped 16-byte slots are
-// those of the 128 x 128 kernel; K goes through a ring of four LDS buffers (below).  Chunks are
-// added in the same order and the epilogue makes the same operations, so the output is
-// bit-identical to the 128 x 128 kernel's.
+// vector work per chunk), so 128 of them fit.  Codes sit in the 128 x 128 kernel's swapped
+// 16-byte slots; each scale byte gets a dword of its own (1-byte LDS-DMA, zero-extended),
+// placed so that a lane reads all its scales of a chunk with one 8-byte and one 16-byte read
+// and hands them to the MFMA as they are.  K goes through a ring of four LDS buffers (below).
+// Chunks are added in the same order and the epilogue makes the same operations, so the output
+// is bit-identical to the 128 x 128 kernel's.
 template <int WM_, int WN_, int TI_, int TJ_, int KC_>
 struct Big {
   static constexpr int WM = WM_, WN = WN_, TI = TI_, TJ = TJ_, KC = KC_;
   static constexpr int NW = WM * WN, NTH = 64 * NW;
   static constexpr int BM = WM * TI * 32, BN = WN * TJ * 32;
-  static constexpr int L_X = 0, L_W = BM * 32, L_SX = L_W + BN * 32, L_SW = L_SX + BM * 4;
-  static constexpr int CHUNK = L_SW + BN * 4;
+  // scales: one dword per (row, half), the E8M0 byte zero-extended, ordered so that a lane's
+  // TI (TJ) scales are consecutive: X [WM][32][2][TI], W [WN][32][2][TJ] (see BigOp::src)
+  static constexpr int L_X = 0, L_W = BM * 32, L_SX = L_W + BN * 32, L_SW = L_SX + 2 * BM * 4;
+  static constexpr int CHUNK = L_SW + 2 * BN * 4;
   static constexpr int BUF = KC * CHUNK;
-  // LDS-DMA instructions per chunk: 32 code rows or 64 scale rows each
-  static constexpr int NX = BM / 32, NWC = BN / 32, NSX = BM / 64, NSW = BN / 64;
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "scale rows go 64 to an instruction");
+  // LDS-DMA instructions per chunk: 32 code rows, or 64 (row, half) scale bytes, each
+  static constexpr int NX = BM / 32, NWC = BN / 32, NSX = 2 * BM / 64, NSW = 2 * BN / 64;
+  static_assert(BM % 32 == 0 && BN % 32 == 0, "whole 32-row tiles");
+  static_assert(TI == 2 && TJ == 4, "the scale reads are 8 and 16 bytes");
 };
 
 template <class C>
@@ -230,8 +235,10 @@ struct BigOp {
 
   // per-lane global offsets of the slots for the tile at (m0, n0): a code slot's lane l moves
   // row 32 i' + l / 2 (i' its instruction within X or W), into LDS slot l % 2, which holds piece
-  // (l % 2) ^ ((row / 8) % 2); a scale slot's lane l moves row 64 i' + l.  Rows past the edge
-  // re-read the last row.
+  // (l % 2) ^ ((row / 8) % 2); a scale slot's lane l moves the byte of (row, half) that belongs
+  // in scale dword s = 64 i' + l: for X, s = ((wm 32 + r32) 2 + h) TI + ti holds row
+  // wm TI 32 + ti 32 + r32 (W alike with TJ), so that lane (r32, h) of wave (wm, wn) finds its TI
+  // X and TJ W scales in consecutive dwords.  Rows past the edge re-read the last row.
   __device__ Src src(int m0, int n0) const {
     Src o;
 #pragma unroll
@@ -246,8 +253,11 @@ struct BigOp {
     for (int j = 0; j < PS; j++) {
       const int i = wave + j * C::NW;
       const bool isx = i < C::NSX;
-      const int row = (isx ? i : i - C::NSX) * 64 + lane;
-      o.s[j] = (uint32_t)(isx ? min(m0 + row, M - 1) : min(n0 + row, N - 1)) * 2u;
+      const int t = isx ? C::TI : C::TJ;
+      const int sl = (isx ? i : i - C::NSX) * 64 + lane;
+      const int tt = sl % t, hh = (sl / t) & 1, r = (sl / t / 2) & 31, g = sl / t / 64;
+      const int row = (g * t + tt) * 32 + r;
+      o.s[j] = (uint32_t)(isx ? min(m0 + row, M - 1) : min(n0 + row, N - 1)) * 2u + (uint32_t)hh;
     }
     return o;
   }
@@ -261,29 +271,41 @@ struct BigOp {
         if (NCODE % C::NW == 0 || wave + j * C::NW < NCODE) dma16(crs[j], b + cdst[j], v.c[j], c * cstr[j]);
 #pragma unroll
       for (int j = 0; j < PS; j++)
-        if (NSCALE % C::NW == 0 || wave + j * C::NW < NSCALE) dma2(srs[j], b + sdst[j], v.s[j], c * sstr[j]);
+        if (NSCALE % C::NW == 0 || wave + j * C::NW < NSCALE) dma1(srs[j], b + sdst[j], v.s[j], c * sstr[j]);
     }
   }
-  // lane (r32, h) reads codes 32 h .. 32 h + 31 (one 16-byte slot) and scale byte h of its rows
-  __device__ void read(const uint8_t* b, Frag& f) const {
+  // lane (r32, h) reads codes 32 h .. 32 h + 31 (one 16-byte slot) of its rows and their scale
+  // dwords (the E8M0 byte in the low byte: the MFMA's scale operand as it is).  In two parts, so
+  // that a chunk's reads can go out between the previous chunk's MFMAs with few LDS reads in
+  // flight: part 0 the X fragments, the X scales and the first half of the W fragments, part 1
+  // the rest of the W fragments and the W scales.
+  __device__ void read(const uint8_t* b, Frag& f, int part) const {
     const int r32 = lane & 31;
     const int xr = wm * C::TI * 32 + r32, wr = wn * C::TJ * 32 + r32;
     const int xo = C::L_X + xr * 32 + 16 * (h ^ ((xr >> 3) & 1));   // + 1024 per 32-row tile
     const int wo = C::L_W + wr * 32 + 16 * (h ^ ((wr >> 3) & 1));
+    if (part == 0) {
 #pragma unroll
-    for (int ti = 0; ti < C::TI; ti++) {
-      f.x[ti] = *reinterpret_cast<const uint4*>(b + xo + ti * 1024);
-      f.sx[ti] = (*reinterpret_cast<const uint32_t*>(b + C::L_SX + (xr + ti * 32) * 4) >> (8 * h)) & 0xFFu;
+      for (int ti = 0; ti < C::TI; ti++) f.x[ti] = *reinterpret_cast<const uint4*>(b + xo + ti * 1024);
+      const uint2 sx = *reinterpret_cast<const uint2*>(b + C::L_SX + ((wm * 32 + r32) * 2 + h) * C::TI * 4);
+      f.sx[0] = sx.x;
+      f.sx[1] = sx.y;
     }
 #pragma unroll
-    for (int tj = 0; tj < C::TJ; tj++) {
+    for (int tj = part * C::TJ / 2; tj < (part + 1) * C::TJ / 2; tj++)
       f.w[tj] = *reinterpret_cast<const uint4*>(b + wo + tj * 1024);
-      f.sw[tj] = (*reinterpret_cast<const uint32_t*>(b + C::L_SW + (wr + tj * 32) * 4) >> (8 * h)) & 0xFFu;
+    if (part == 1) {
+      const uint4 sw = *reinterpret_cast<const uint4*>(b + C::L_SW + ((wn * 32 + r32) * 2 + h) * C::TJ * 4);
+      f.sw[0] = sw.x;
+      f.sw[1] = sw.y;
+      f.sw[2] = sw.z;
+      f.sw[3] = sw.w;
     }
   }
-  __device__ void mma(const Frag& f, v16f (&acc)[C::TJ][C::TI]) const {
+  // the MFMAs of W tiles part * TJ / 2 .. (part + 1) * TJ / 2 - 1
+  __device__ void mma(const Frag& f, v16f (&acc)[C::TJ][C::TI], int part) const {
 #pragma unroll
-    for (int tj = 0; tj < C::TJ; tj++)
+    for (int tj = part * C::TJ / 2; tj < (part + 1) * C::TJ / 2; tj++)
 #pragma unroll
       for (int ti = 0; ti < C::TI; ti++) acc[tj][ti] = mx_mma(f.w[tj], f.x[ti], f.sw[tj], f.sx[ti], acc[tj][ti]);
   }
@@ -350,15 +372,24 @@ __device__ __forceinline__ void big_epilogue(v16f (&acc)[C::TJ][C::TI], uint8_t*
       braw[tj][q] = make_uint2(0u, 0u);
       if (BIAS && n < N) braw[tj][q] = *reinterpret_cast<const uint2*>(bias + n);
     }
-  // with the MLP glue folded in, the next layer's factors of the 8 columns this lane stores per group
+  // with the MLP glue folded in, the next layer's factors of the 8 columns this lane stores per
+  // group (loaded only then: a load whose result no path uses would stay pending into the next
+  // tile, and the compiler's wait before its registers are rewritten would wait for every load)
   const rsrc_t rl = make_rsrc(lam, lam ? (size_t)N * 4 : 0);
   float4 la[NG], lb[NG];
 #pragma unroll
   for (int g = 0; g < NG; g++) {
-    const int pr = (C::TJ - 2 * g >= 2 ? 2 : 1) * 4;
-    const int cl = (lane % pr) * 8;
-    la[g] = load_f4(rl, nw + g * 64 + cl);
-    lb[g] = load_f4(rl, nw + g * 64 + cl + 4);
+    la[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+    lb[g] = la[g];
+  }
+  if (lam) {
+#pragma unroll
+    for (int g = 0; g < NG; g++) {
+      const int pr = (C::TJ - 2 * g >= 2 ? 2 : 1) * 4;
+      const int cl = (lane % pr) * 8;
+      la[g] = load_f4(rl, nw + g * 64 + cl);
+      lb[g] = load_f4(rl, nw + g * 64 + cl + 4);
+    }
   }
   issue();
   if (RB > 0) {
@@ -459,6 +490,7 @@ k_gemm_mxb(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const
   static_assert(Op::NCODE % C::NW == 0 && Op::NSCALE % C::NW == 0, "every wave issues as many loads");
   constexpr int LPS = C::KC * (Op::PC + Op::PS);   // LDS-DMA instructions per wave and step
   static_assert(C::BUF >= C::NW * 32 * E_YS && C::BUF >= C::BN * (RB * 16 + 8) * 2, "the epilogue must fit a buffer");
+  static_assert(C::KC == 2, "steps of two chunks");
   __shared__ __attribute__((aligned(16))) uint8_t b0[C::BUF];
   __shared__ __attribute__((aligned(16))) uint8_t b1[C::BUF];
   __shared__ __attribute__((aligned(16))) uint8_t b2[C::BUF];
@@ -503,18 +535,25 @@ k_gemm_mxb(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const
                     int lst) {
       typename Op::Frag f0, f1;
       const bool live = st < NS;
-      if (live) op.read(sb, f0);
+      const bool two = 2 * st + 1 < op.C_;   // the step's second chunk exists
+      // every LDS read of the step goes out first, then the step's LDS-DMA loads, then the MFMAs
+      // (the compiler makes an LDS read issued after LDS-DMA loads it cannot tell apart wait for
+      // all of them).  Past the last chunk the reads stay in bounds and go unused.
+      if (live) {
+        op.read(sb, f0, 0);
+        op.read(sb, f0, 1);
+        op.read(sb + C::CHUNK, f1, 0);
+        op.read(sb + C::CHUNK, f1, 1);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (decltype(load_c)::value) op.load(ls, lst, ob);
       __builtin_amdgcn_sched_barrier(0);
       if (live) {
-#pragma unroll
-        for (int k = 0; k < C::KC; k++) {
-          if (st * C::KC + k >= op.C_) break;
-          typename Op::Frag& fc = (k & 1) ? f1 : f0;
-          typename Op::Frag& fn = (k & 1) ? f0 : f1;
-          if (k + 1 < C::KC && st * C::KC + k + 1 < op.C_) op.read(sb + (k + 1) * C::CHUNK, fn);
-          op.mma(fc, acc);
+        op.mma(f0, acc, 0);
+        op.mma(f0, acc, 1);
+        if (two) {
+          op.mma(f1, acc, 0);
+          op.mma(f1, acc, 1);
         }
       }
       vm_lds_barrier<decltype(wait_c)::value>();
