@@ -97,7 +97,11 @@ def build_microbench(verbose: bool = False) -> str:
     (microbench/load_paths.hip) and the sustained matrix-core rates with the clock they hold
     (microbench/mfma_clock.hip).  Returns the first program's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    _run([hipcc(), *FLAGS, os.path.join(HERE, "microbench", "mfma_valu.hip"), "-o", MICROBENCH], verbose)
+    # mfma_valu without the VGPR-form flag: its AGPR cases need the compiler free to put MFMA
+    # results in AGPRs (the others get the VGPR form either way)
+    no_vgpr_form = [f for i, f in enumerate(FLAGS) if f != "-amdgpu-mfma-vgpr-form" and
+                    not (f == "-mllvm" and i + 1 < len(FLAGS) and FLAGS[i + 1] == "-amdgpu-mfma-vgpr-form")]
+    _run([hipcc(), *no_vgpr_form, os.path.join(HERE, "microbench", "mfma_valu.hip"), "-o", MICROBENCH], verbose)
     for prog in ("load_paths", "mfma_clock"):
         _run([hipcc(), *FLAGS, os.path.join(HERE, "microbench", prog + ".hip"), "-o", os.path.join(BUILD_DIR, prog)],
              verbose)

@@ -9,6 +9,9 @@
 // MFMA operands differ per tile and change every iteration, so the compiler can merge or hoist
 // nothing; each thread stores one value at the end (out has one float per thread).
 //
+// The AGPR case puts P and S in AGPRs (the form the compiler picks once a kernel uses AGPRs):
+// the vector ALU cannot read AGPRs, so each result comes back with v_accvgpr_read first.
+//
 // Build and run (gfx950):
 //   python -m bit_w4a4_quantized_amd.build --microbench && bit_w4a4_quantized_amd/_build/mfma_valu
 #include <hip/hip_runtime.h>
@@ -32,6 +35,7 @@ enum Case {
   PAIR_AND_FMA,      // MFMA_PAIR and FMA_ONLY in one loop, independent of each other
   PAIR_AND_ADD,      // MFMA_PAIR and 16 two-operand adds per tile
   KERNEL_B_PATTERN,  // P = FP6 MFMA, S = scale MFMA (C = 0), acc += P S: Kernel B's dependency
+  KERNEL_B_AGPR,     // KERNEL_B_PATTERN with P and S in AGPRs (the fmas read them back: v_accvgpr_read)
 };
 
 __device__ __forceinline__ v8i codes(unsigned s) {   // six dwords of 6-bit fields (any pattern is an FP6 value)
@@ -45,6 +49,8 @@ __device__ __forceinline__ v8i codes(unsigned s) {   // six dwords of 6-bit fiel
 
 template <Case C>
 __global__ void __launch_bounds__(NT, 2) probe(float* out, float fa, float fb) {
+  // an AGPR clobber makes the compiler allocate AGPRs, and MFMA results then go there
+  if constexpr (C == KERNEL_B_AGPR) asm volatile("" ::: "a0");
   const unsigned tid = threadIdx.x + blockIdx.x * NT;
   v8i a[TILES], b[TILES];
   v4h sa[TILES], sb[TILES];
@@ -72,9 +78,10 @@ __global__ void __launch_bounds__(NT, 2) probe(float* out, float fa, float fb) {
       // bit of the scale), so no MFMA is loop-invariant
       a[t][0] ^= it;
       sa[t][1] = (_Float16)(float)(it & 1);
-      if constexpr (C == FP6_ONLY || C == MFMA_PAIR || C == PAIR_AND_FMA || C == PAIR_AND_ADD)
+      constexpr bool PAIR = C == MFMA_PAIR || C == PAIR_AND_FMA || C == PAIR_AND_ADD;
+      if constexpr (C == FP6_ONLY || PAIR)
         acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[t], b[t], acc[t], 2, 2, 0, 132, 0, 127);
-      if constexpr (C == SCALE_ONLY || C == MFMA_PAIR || C == PAIR_AND_FMA || C == PAIR_AND_ADD)
+      if constexpr (C == SCALE_ONLY || PAIR)
         acc2[t] = __builtin_amdgcn_mfma_f32_32x32x8f16(sa[t], sb[t], acc2[t], 0, 0, 0);
       if constexpr (C == FMA_ONLY || C == PAIR_AND_FMA) {
 #pragma unroll
@@ -84,7 +91,7 @@ __global__ void __launch_bounds__(NT, 2) probe(float* out, float fa, float fb) {
 #pragma unroll
         for (int i = 0; i < 16; i++) v[t][i] = v[t][i] + fb;
       }
-      if constexpr (C == KERNEL_B_PATTERN) {
+      if constexpr (C == KERNEL_B_PATTERN || C == KERNEL_B_AGPR) {
         const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[t], b[t], v16f{}, 2, 2, 0, 132, 0, 127);
         const v16f s = __builtin_amdgcn_mfma_f32_32x32x8f16(sa[t], sb[t], v16f{}, 0, 0, 0);
 #pragma unroll
@@ -141,6 +148,8 @@ int main() {
               run<PAIR_AND_ADD>(out, grid1, 1));
   std::printf("%-44s %8.2f %8.2f\n", "Kernel B pattern (P, S, acc += P S)", run<KERNEL_B_PATTERN>(out, grid2, 2),
               run<KERNEL_B_PATTERN>(out, grid1, 1));
+  std::printf("%-44s %8.2f %8.2f\n", "Kernel B pattern, P and S in AGPRs", run<KERNEL_B_AGPR>(out, grid2, 2),
+              run<KERNEL_B_AGPR>(out, grid1, 1));
   const hipError_t e = hipGetLastError();
   std::printf("status: %s\n", hipGetErrorString(e));
   (void)hipFree(out);
