@@ -67,6 +67,11 @@ METRIC = "µs and effective TOPS per fused W4A4+rank-32 linear (FLUX shapes); % 
 INT8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA, 5.0 POP/s
 FP6_PEAK_TFLOPS = 10100.0        # MI355X dense FP6/FP4 MFMA, 10.1 PFLOP/s
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
+# Dense matrix-core rates the chip sustains with every SIMD issuing back to back (it then holds
+# 1.96 GHz for INT8, 1.9 GHz for FP4, not 2.4): bit_w4a4_quantized_amd/microbench/mfma_clock.hip,
+# summarized in profiles/microbench_mfma_clock.md.  Context beside the datasheet peaks above.
+INT8_SUSTAINED_TOPS = 3800.0
+FP4_SUSTAINED_TFLOPS = 7150.0
 
 WORKLOADS = {
     # name: (M, K, N, r, synthetic layer)
@@ -631,6 +636,11 @@ def main():
             "avg_launch_us": round(kb_us, 2),
             "frac_of_fp6_peak": round(achieved / FP6_PEAK_TFLOPS, 4) if fmt == "int4_e2m3" else None,
             "frac_of_int8_peak": round(achieved / INT8_PEAK_TOPS, 4),
+            "frac_of_sustained_mfma_rate": round(achieved / (FP4_SUSTAINED_TFLOPS if fmt == "mxfp4"
+                                                             else INT8_SUSTAINED_TOPS), 4),
+            "sustained_mfma_rate": {"value": FP4_SUSTAINED_TFLOPS if fmt == "mxfp4" else INT8_SUSTAINED_TOPS,
+                                    "source": "profiles/microbench_mfma_clock.md (all SIMDs issuing "
+                                              "MFMAs back to back hold 1.9-1.96 GHz)"},
             "algorithmic_hbm_bytes": kb_bytes,
             "container_extra_hbm_bytes": kb_extra}
 
