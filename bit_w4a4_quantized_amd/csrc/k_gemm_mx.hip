@@ -186,7 +186,8 @@ struct Big {
 template <class C>
 struct BigOp {
   // a wave's LDS-DMA instructions per chunk: code slots j (instruction wave + j NW of the NX
-  // X-row and NWC W-row ones, 32 rows each) and scale slots (of the NSX + NSW, 64 rows each);
+  // X-row and NWC W-row ones, 32 rows each) and scale slots (of the NSX + NSW, 64 scale bytes
+  // each);
   // the kind of each slot is fixed for the wave, so its resource, LDS offset and chunk stride
   // are set once
   static constexpr int NCODE = C::NX + C::NWC, NSCALE = C::NSX + C::NSW;
