@@ -19,11 +19,21 @@ LIB = os.path.join(HERE, "libsvdq.so")
 SOURCES = ["svdq_api.hip", "k_quant_down.hip", "k_quant_weight.hip", "k_gemm.hip", "k_gemm2.hip",
            "k_gemm3.hip", "k_gemm_i8.hip", "k_gemm_f4.hip", "k_gemm_mx.hip", "k_w4a16.hip", "k_misc.hip", "k_relayout.hip"]
 # -amdgpu-mfma-vgpr-form: MFMA results in VGPRs, so the per-group rescale reads
-# them without v_accvgpr_read copies.
+# them without v_accvgpr_read copies.  Not for the MXFP4 GEMM, whose four-wave kernel keeps
+# 256 accumulators per lane in the accumulation registers (its other kernels come out the same
+# either way).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wno-unused-result"]
+AGPR_SOURCES = {"k_gemm_mx.hip"}
+
+
+def source_flags(src: str) -> list:
+    if src not in AGPR_SOURCES:
+        return FLAGS
+    return [f for i, f in enumerate(FLAGS) if f != "-amdgpu-mfma-vgpr-form" and
+            not (f == "-mllvm" and i + 1 < len(FLAGS) and FLAGS[i + 1] == "-amdgpu-mfma-vgpr-form")]
 BUILD_DIR = os.path.join(HERE, "_build")
 
 
@@ -56,7 +66,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *source_flags(src), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1, 8)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
@@ -99,8 +109,7 @@ def build_microbench(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     # mfma_valu without the VGPR-form flag: its AGPR cases need the compiler free to put MFMA
     # results in AGPRs (the others get the VGPR form either way)
-    no_vgpr_form = [f for i, f in enumerate(FLAGS) if f != "-amdgpu-mfma-vgpr-form" and
-                    not (f == "-mllvm" and i + 1 < len(FLAGS) and FLAGS[i + 1] == "-amdgpu-mfma-vgpr-form")]
+    no_vgpr_form = source_flags("k_gemm_mx.hip")
     _run([hipcc(), *no_vgpr_form, os.path.join(HERE, "microbench", "mfma_valu.hip"), "-o", MICROBENCH], verbose)
     for prog in ("load_paths", "mfma_clock"):
         _run([hipcc(), *FLAGS, os.path.join(HERE, "microbench", prog + ".hip"), "-o", os.path.join(BUILD_DIR, prog)],

@@ -159,12 +159,11 @@ namespace {
 // Large tiles.  With 128 x 128 tiles each CU stages 17 KB per chunk (LDS-DMA) for 32 tile-groups
 // and its waves read 32 KB of operand fragments from LDS.  Here one workgroup of WM x WN waves
 // per CU owns a BM x BN tile and each wave a TI x TJ block of 32 x 32 tiles: at 256 x 256 with
-// 2 x 4 per wave, 17 KB of LDS-DMA per chunk serve 64 tile-groups, and each wave reads 6
-// fragments for 8 MFMAs instead of 4 for 4.  The accumulators stay with the matrix cores (no
-// vector work per chunk), so 128 of them fit.  Codes sit in the 128 x 128 kernel's swapped
-// 16-byte slots; each scale byte gets a dword of its own (1-byte LDS-DMA, zero-extended),
-// placed so that a lane reads all its scales of a chunk with one 8-byte and one 16-byte read
-// and hands them to the MFMA as they are.  K goes through a ring of four LDS buffers (below).
+// 4 x 4 per wave (four waves), 18 KB of LDS-DMA per chunk serve 64 tile-groups, and each wave
+// reads 8 fragments for 16 MFMAs.  The accumulators stay with the matrix cores (no vector work
+// per chunk).  Codes sit in the 128 x 128 kernel's swapped 16-byte slots; each row's two scale
+// bytes of a chunk arrive by one 2-byte LDS-DMA lane into a dword of their own (zero-extended),
+// from which a lane shifts out its byte.  K goes through a ring of four LDS buffers (below).
 // Chunks are added in the same order and the epilogue makes the same operations, so the output
 // is bit-identical to the 128 x 128 kernel's.
 template <int WM_, int WN_, int TI_, int TJ_, int KC_>
@@ -172,26 +171,25 @@ struct Big {
   static constexpr int WM = WM_, WN = WN_, TI = TI_, TJ = TJ_, KC = KC_;
   static constexpr int NW = WM * WN, NTH = 64 * NW;
   static constexpr int BM = WM * TI * 32, BN = WN * TJ * 32;
-  // scales: one dword per (row, half), the E8M0 byte zero-extended, ordered so that a lane's
-  // TI (TJ) scales are consecutive: X [WM][32][2][TI], W [WN][32][2][TJ] (see BigOp::src)
-  static constexpr int L_X = 0, L_W = BM * 32, L_SX = L_W + BN * 32, L_SW = L_SX + 2 * BM * 4;
-  static constexpr int CHUNK = L_SW + 2 * BN * 4;
+  // per chunk: codes X [BM][32 bytes], W [BN][32 bytes]; scales one dword per row (bytes 0 and
+  // 1: the row's two groups), X [BM], W [BN]
+  static constexpr int L_X = 0, L_W = BM * 32, L_SX = L_W + BN * 32, L_SW = L_SX + BM * 4;
+  static constexpr int CHUNK = L_SW + BN * 4;
   static constexpr int BUF = KC * CHUNK;
-  // LDS-DMA instructions per chunk: 32 code rows, or 64 (row, half) scale bytes, each
-  static constexpr int NX = BM / 32, NWC = BN / 32, NSX = 2 * BM / 64, NSW = 2 * BN / 64;
-  static_assert(BM % 32 == 0 && BN % 32 == 0, "whole 32-row tiles");
-  static_assert(TI == 2 && TJ == 4, "the scale reads are 8 and 16 bytes");
+  // LDS-DMA instructions per chunk: 32 code rows, or 64 scale rows, each
+  static constexpr int NX = BM / 32, NWC = BN / 32, NSX = BM / 64, NSW = BN / 64;
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "whole 64-row scale loads");
 };
 
 template <class C>
 struct BigOp {
   // a wave's LDS-DMA instructions per chunk: code slots j (instruction wave + j NW of the NX
-  // X-row and NWC W-row ones, 32 rows each) and scale slots (of the NSX + NSW, 64 scale bytes
-  // each);
+  // X-row and NWC W-row ones, 32 rows each) and scale slots (of the NSX + NSW, 64 rows each);
   // the kind of each slot is fixed for the wave, so its resource, LDS offset and chunk stride
   // are set once
   static constexpr int NCODE = C::NX + C::NWC, NSCALE = C::NSX + C::NSW;
   static constexpr int PC = (NCODE + C::NW - 1) / C::NW, PS = (NSCALE + C::NW - 1) / C::NW;
+  static_assert(NCODE % C::NW == 0 && NSCALE % C::NW == 0, "every wave issues as many loads");
   int M, N, C_, NS;
   int lane, h, wave, wm, wn;
   rsrc_t crs[PC], srs[PS];
@@ -236,10 +234,8 @@ struct BigOp {
 
   // per-lane global offsets of the slots for the tile at (m0, n0): a code slot's lane l moves
   // row 32 i' + l / 2 (i' its instruction within X or W), into LDS slot l % 2, which holds piece
-  // (l % 2) ^ ((row / 8) % 2); a scale slot's lane l moves the byte of (row, half) that belongs
-  // in scale dword s = 64 i' + l: for X, s = ((wm 32 + r32) 2 + h) TI + ti holds row
-  // wm TI 32 + ti 32 + r32 (W alike with TJ), so that lane (r32, h) of wave (wm, wn) finds its TI
-  // X and TJ W scales in consecutive dwords.  Rows past the edge re-read the last row.
+  // (l % 2) ^ ((row / 8) % 2); a scale slot's lane l moves the two bytes of row 64 i' + l.  Rows
+  // past the edge re-read the last row.
   __device__ Src src(int m0, int n0) const {
     Src o;
 #pragma unroll
@@ -254,53 +250,49 @@ struct BigOp {
     for (int j = 0; j < PS; j++) {
       const int i = wave + j * C::NW;
       const bool isx = i < C::NSX;
-      const int t = isx ? C::TI : C::TJ;
-      const int sl = (isx ? i : i - C::NSX) * 64 + lane;
-      const int tt = sl % t, hh = (sl / t) & 1, r = (sl / t / 2) & 31, g = sl / t / 64;
-      const int row = (g * t + tt) * 32 + r;
-      o.s[j] = (uint32_t)(isx ? min(m0 + row, M - 1) : min(n0 + row, N - 1)) * 2u + (uint32_t)hh;
+      const int row = (isx ? i : i - C::NSX) * 64 + lane;
+      o.s[j] = (uint32_t)(isx ? min(m0 + row, M - 1) : min(n0 + row, N - 1)) * 2u;
     }
     return o;
   }
+  // step st's chunks; a chunk past the end of K reads as zeros (an offset past the buffer's
+  // range): zero codes add exactly +0 whatever the scales
   __device__ void load(const Src& v, int st, uint8_t* buf) const {
 #pragma unroll
     for (int k = 0; k < C::KC; k++) {
-      const uint32_t c = (uint32_t)min(st * C::KC + k, C_ - 1);  // past the end: the last chunk again (unused)
+      const int ci = st * C::KC + k;
+      const bool past = ci >= C_;
+      const uint32_t c = (uint32_t)min(ci, C_ - 1);
       uint8_t* b = buf + k * C::CHUNK;
 #pragma unroll
-      for (int j = 0; j < PC; j++)
-        if (NCODE % C::NW == 0 || wave + j * C::NW < NCODE) dma16(crs[j], b + cdst[j], v.c[j], c * cstr[j]);
+      for (int j = 0; j < PC; j++) dma16(crs[j], b + cdst[j], past ? 0x80000000u : v.c[j], c * cstr[j]);
 #pragma unroll
-      for (int j = 0; j < PS; j++)
-        if (NSCALE % C::NW == 0 || wave + j * C::NW < NSCALE) dma1(srs[j], b + sdst[j], v.s[j], c * sstr[j]);
+      for (int j = 0; j < PS; j++) dma2(srs[j], b + sdst[j], past ? 0x80000000u : v.s[j], c * sstr[j]);
     }
   }
-  // lane (r32, h) reads codes 32 h .. 32 h + 31 (one 16-byte slot) of its rows and their scale
-  // dwords (the E8M0 byte in the low byte: the MFMA's scale operand as it is).  In two parts, so
-  // that a chunk's reads can go out between the previous chunk's MFMAs with few LDS reads in
-  // flight: part 0 the X fragments, the X scales and the first half of the W fragments, part 1
-  // the rest of the W fragments and the W scales.
+  // lane (r32, h) reads codes 32 h .. 32 h + 31 (one 16-byte slot) of its rows and byte h of
+  // their scale dwords (the MFMA's scale operand: the E8M0 byte in the low byte).  In two parts:
+  // part 0 the X fragments and scales and the first half of the W fragments, part 1 the rest of
+  // the W fragments and the W scales.
   __device__ void read(const uint8_t* b, Frag& f, int part) const {
     const int r32 = lane & 31;
     const int xr = wm * C::TI * 32 + r32, wr = wn * C::TJ * 32 + r32;
     const int xo = C::L_X + xr * 32 + 16 * (h ^ ((xr >> 3) & 1));   // + 1024 per 32-row tile
     const int wo = C::L_W + wr * 32 + 16 * (h ^ ((wr >> 3) & 1));
+    const uint32_t* sx = reinterpret_cast<const uint32_t*>(b + C::L_SX) + xr;   // + 32 per tile
+    const uint32_t* sw = reinterpret_cast<const uint32_t*>(b + C::L_SW) + wr;
     if (part == 0) {
 #pragma unroll
       for (int ti = 0; ti < C::TI; ti++) f.x[ti] = *reinterpret_cast<const uint4*>(b + xo + ti * 1024);
-      const uint2 sx = *reinterpret_cast<const uint2*>(b + C::L_SX + ((wm * 32 + r32) * 2 + h) * C::TI * 4);
-      f.sx[0] = sx.x;
-      f.sx[1] = sx.y;
+#pragma unroll
+      for (int ti = 0; ti < C::TI; ti++) f.sx[ti] = (sx[ti * 32] >> (8 * h)) & 0xFFu;
     }
 #pragma unroll
     for (int tj = part * C::TJ / 2; tj < (part + 1) * C::TJ / 2; tj++)
       f.w[tj] = *reinterpret_cast<const uint4*>(b + wo + tj * 1024);
     if (part == 1) {
-      const uint4 sw = *reinterpret_cast<const uint4*>(b + C::L_SW + ((wn * 32 + r32) * 2 + h) * C::TJ * 4);
-      f.sw[0] = sw.x;
-      f.sw[1] = sw.y;
-      f.sw[2] = sw.z;
-      f.sw[3] = sw.w;
+#pragma unroll
+      for (int tj = 0; tj < C::TJ; tj++) f.sw[tj] = (sw[tj * 32] >> (8 * h)) & 0xFFu;
     }
   }
   // the MFMAs of W tiles part * TJ / 2 .. (part + 1) * TJ / 2 - 1
@@ -312,58 +304,94 @@ struct BigOp {
   }
 };
 
-// Workgroup barriers that leave loads from global memory in flight (a __syncthreads() would wait
-// for every LDS-DMA load of the ring): the wave's LDS operations complete, and with N, its
-// vector-memory operations but the N most recent ones.
+// A workgroup barrier that leaves loads from global memory in flight (a __syncthreads() would
+// wait for every LDS-DMA load of the ring): the wave's LDS operations complete.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// A workgroup barrier after waiting for the wave's LDS operations and for all but its N most
+// recent vector-memory operations, written with the builtins (not inline asm) so that the
+// compiler's own wait insertion knows what has completed: it then adds no wait of its own for
+// fragments read before the barrier.  The empty asm statements keep memory accesses from
+// moving across.
 template <int N>
-__device__ __forceinline__ void vm_lds_barrier() {
+__device__ __forceinline__ void wait_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));   // vmcnt(N) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
+
+// Scheduling groups: an MFMA, then (while they last) one LDS read and one vector-memory load,
+// NM times.
+template <int I, int NM, int NR, int NV>
+__device__ __forceinline__ void interleave() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (I < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if constexpr (I < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    interleave<I + 1, NM, NR, NV>();
+  }
+}
+
 template <int V>
 struct IC {
   static constexpr int value = V;
 };
 
-// acc += T L2 (RB > 0), bias, fp16 store: the 128 x 128 epilogue's operations for a TI x TJ block
-// of tiles per wave.  eb: epilogue LDS, free.  Its own global loads go out first, then issue()
-// (the next tile's loads), so that waiting for them does not wait for those.  Ends with an
-// LDS-only barrier.
-template <class C, int RB, bool BIAS, class Issue>
-__device__ __forceinline__ void big_epilogue(v16f (&acc)[C::TJ][C::TI], uint8_t* eb, const __half* __restrict__ t,
-                                             const __half* __restrict__ l2, const __half* __restrict__ bias,
-                                             const float* __restrict__ lam, int M, int N, int m0, int n0,
-                                             __half* __restrict__ y, Issue&& issue) {
+// The epilogue's operands from global memory that are needed first: the tile's columns of L2
+// (staged through LDS) and the wave's rows of T.  Loaded before the tile's last step, so that
+// their latency hides behind its MFMAs.
+template <class C, int RB>
+struct BigEpiIn {
+  static constexpr int R = RB * 16;
+  static constexpr int L2P = RB > 0 ? (R * (C::BN / 8) + C::NTH - 1) / C::NTH : 1;   // 8-column pieces per thread
+  uint4 lv[L2P];
+  uint4 top[RB > 0 ? RB : 1][C::TI];
+};
+
+template <class C, int RB>
+__device__ __forceinline__ void big_epi_load(BigEpiIn<C, RB>& e, const __half* __restrict__ t,
+                                             const __half* __restrict__ l2, int M, int N, int m0, int n0) {
   constexpr int R = RB * 16;
-  constexpr int LS2 = (R + 8) * 2;           // L2 staged transposed: [n][k], row stride R + 8 halves
-  constexpr int L2P = RB > 0 ? (R * (C::BN / 8) + C::NTH - 1) / C::NTH : 1;   // 8-column pieces per thread
-  constexpr int NG = (C::TJ + 1) / 2;        // output column groups of (up to) two tiles
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r32 = lane & 31;
-  const int wm = wave / C::WN, wn = wave % C::WN;
-  const int mw = m0 + wm * C::TI * 32, nw = n0 + wn * C::TJ * 32;   // the wave's block
-  // ---- the epilogue's global loads
-  uint4 lv[L2P];
-  uint4 top[RB > 0 ? RB : 1][C::TI];
+  const int mw = m0 + (wave / C::WN) * C::TI * 32;
   if (RB > 0) {
 #pragma unroll
-    for (int j = 0; j < L2P; j++) {
+    for (int j = 0; j < BigEpiIn<C, RB>::L2P; j++) {
       const int idx = tid + j * C::NTH;
       const int k = idx % R, c8 = idx / R;
       const int n = n0 + c8 * 8;
-      lv[j] = make_uint4(0, 0, 0, 0);
-      if (idx < R * (C::BN / 8) && n < N) lv[j] = *reinterpret_cast<const uint4*>(l2 + (size_t)k * N + n);
+      e.lv[j] = make_uint4(0, 0, 0, 0);
+      if (idx < R * (C::BN / 8) && n < N) e.lv[j] = *reinterpret_cast<const uint4*>(l2 + (size_t)k * N + n);
     }
 #pragma unroll
     for (int kb = 0; kb < RB; kb++)
 #pragma unroll
       for (int ti = 0; ti < C::TI; ti++) {
         const int m = min(mw + ti * 32 + r32, M - 1);
-        top[kb][ti] = *reinterpret_cast<const uint4*>(t + (size_t)m * R + kb * 16 + 8 * h);
+        e.top[kb][ti] = *reinterpret_cast<const uint4*>(t + (size_t)m * R + kb * 16 + 8 * h);
       }
   }
+}
+
+// acc += T L2 (RB > 0), bias, fp16 store: the 128 x 128 epilogue's operations for a TI x TJ block
+// of tiles per wave, with L2 and T from e.  eb: epilogue LDS, free.  Ends with the wave's LDS
+// work done but no barrier.
+template <class C, int RB, bool BIAS>
+__device__ __forceinline__ void big_epilogue(v16f (&acc)[C::TJ][C::TI], uint8_t* eb, const BigEpiIn<C, RB>& e,
+                                             const __half* __restrict__ bias, const float* __restrict__ lam, int M,
+                                             int N, int m0, int n0, __half* __restrict__ y) {
+  constexpr int R = RB * 16;
+  constexpr int LS2 = (R + 8) * 2;           // L2 staged transposed: [n][k], row stride R + 8 halves
+  constexpr int L2P = BigEpiIn<C, RB>::L2P;
+  constexpr int NG = (C::TJ + 1) / 2;        // output column groups of (up to) two tiles
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, r32 = lane & 31;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int mw = m0 + wm * C::TI * 32, nw = n0 + wn * C::TJ * 32;   // the wave's block
   uint2 braw[C::TJ][4];
 #pragma unroll
   for (int tj = 0; tj < C::TJ; tj++)
@@ -392,14 +420,13 @@ __device__ __forceinline__ void big_epilogue(v16f (&acc)[C::TJ][C::TI], uint8_t*
       lb[g] = load_f4(rl, nw + g * 64 + cl + 4);
     }
   }
-  issue();
   if (RB > 0) {
 #pragma unroll
     for (int j = 0; j < L2P; j++) {
       const int idx = tid + j * C::NTH;
       const int k = idx % R, c8 = idx / R;
       if (idx < R * (C::BN / 8)) {
-        const uint32_t w[4] = {lv[j].x, lv[j].y, lv[j].z, lv[j].w};
+        const uint32_t w[4] = {e.lv[j].x, e.lv[j].y, e.lv[j].z, e.lv[j].w};
 #pragma unroll
         for (int e = 0; e < 8; e++)
           *reinterpret_cast<uint16_t*>(eb + (c8 * 8 + e) * LS2 + k * 2) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
@@ -414,7 +441,7 @@ __device__ __forceinline__ void big_epilogue(v16f (&acc)[C::TJ][C::TI], uint8_t*
             *reinterpret_cast<const uint4*>(eb + (wn * C::TJ * 32 + tj * 32 + r32) * LS2 + (kb * 16 + 8 * h) * 2);
 #pragma unroll
         for (int ti = 0; ti < C::TI; ti++)
-          acc[tj][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(lo), as_h8(top[kb][ti]), acc[tj][ti], 0, 0, 0);
+          acc[tj][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(lo), as_h8(e.top[kb][ti]), acc[tj][ti], 0, 0, 0);
       }
     lds_barrier();                           // the output staging reuses the L2 staging bytes
   }
@@ -468,30 +495,32 @@ __device__ __forceinline__ void big_epilogue(v16f (&acc)[C::TJ][C::TI], uint8_t*
       __builtin_amdgcn_wave_barrier();
     }
   }
-  lds_barrier();                             // the buffer is refilled by the next tile's loads
 }
 
 }  // namespace
 
-// The persistent loop over BM x BN tiles: tiles blockIdx.x, + gridDim.x, ...  K goes in steps of
-// KC chunks through a ring of four LDS buffers (separate arrays, so that the compiler does not
-// make a buffer's reads wait for loads into another), three steps ahead: step s computes from
-// buffer s % 4 while the loads of steps s + 1 .. s + 3 are in flight, and each step ends with
-// every wave's loads of step s + 1 done and a barrier that leaves the later loads in flight.
-// Across a tile boundary the ring carries on into the next tile: its first step is loaded three
-// steps before the end, its second and third by the epilogue, which works in the buffer of the
-// tile's last step, after its own loads.
+// Four waves per CU, one per SIMD, each owning a 128 x 128 block (4 x 4 tiles of 32 x 32, its
+// 256 accumulators in the matrix cores' registers), with the LDS reads one step ahead of the
+// MFMAs: while a step's MFMAs run on fragments already in registers, the next step's fragment
+// reads and the step's LDS-DMA loads go out one after each MFMA, so the matrix core works while
+// the LDS serves the reads.  Per chunk and CU the LDS carries 20 KB of DMA writes and 40 KB of
+// fragment reads for 64 tile-MFMAs (eight waves of 64 x 128: 60 KB).  Ring of four buffers,
+// loads four steps ahead: a buffer is read into registers one step before its MFMAs, so the
+// step after that may load it again.  At a tile's end the ring carries on into the next tile:
+// the tile's last four steps load the next tile's first three and the last step loads nothing
+// and reads nothing; the epilogue works in the last step's buffer, then the next tile's first
+// fragments are read and its fourth step loaded into that buffer.
 template <class C, int RB, bool BIAS>
 __global__ void __launch_bounds__(C::NTH, 1)
-k_gemm_mxb(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const __half* __restrict__ t,
+k_gemm_mxw(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const __half* __restrict__ t,
            const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const __half* __restrict__ l2,
            const __half* __restrict__ bias, const float* __restrict__ lam, int M, int N, int K,
            __half* __restrict__ y) {
   using Op = BigOp<C>;
-  static_assert(Op::NCODE % C::NW == 0 && Op::NSCALE % C::NW == 0, "every wave issues as many loads");
+  using Frag = typename Op::Frag;
   constexpr int LPS = C::KC * (Op::PC + Op::PS);   // LDS-DMA instructions per wave and step
+  static_assert(2 * LPS < 64, "vmcnt range");
   static_assert(C::BUF >= C::NW * 32 * E_YS && C::BUF >= C::BN * (RB * 16 + 8) * 2, "the epilogue must fit a buffer");
-  static_assert(C::KC == 2, "steps of two chunks");
   __shared__ __attribute__((aligned(16))) uint8_t b0[C::BUF];
   __shared__ __attribute__((aligned(16))) uint8_t b1[C::BUF];
   __shared__ __attribute__((aligned(16))) uint8_t b2[C::BUF];
@@ -507,6 +536,13 @@ k_gemm_mxb(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const
     *m0 = tm * C::BM;
     *n0 = tn * C::BN;
   };
+  auto read_step = [&](const uint8_t* b, Frag (&f)[C::KC]) {
+#pragma unroll
+    for (int k = 0; k < C::KC; k++) {
+      op.read(b + k * C::CHUNK, f[k], 0);
+      op.read(b + k * C::CHUNK, f[k], 1);
+    }
+  };
 
   int tile = blockIdx.x;
   int m0, n0;
@@ -515,7 +551,11 @@ k_gemm_mxb(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const
   op.load(cur, 0, b0);
   op.load(cur, 1, b1);
   op.load(cur, 2, b2);
-  vm_lds_barrier<2 * LPS>();
+  op.load(cur, 3, b3);
+  Frag fa[C::KC], fb[C::KC];
+  wait_barrier<2 * LPS>();                   // steps 0 and 1 are in
+  read_step(b0, fa);
+  wait_barrier<63>();                        // b0 is read before step 0 loads step 4 into it
   v16f acc[C::TJ][C::TI];
   while (true) {
     const int next = tile + (int)gridDim.x;
@@ -530,51 +570,54 @@ k_gemm_mxb(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const
 #pragma unroll
         for (int i = 0; i < 16; i++) acc[a][b][i] = 0.f;
 
-    // step st: compute from sb; with LOAD, first issue step lst's loads (of ls) into ob; then
-    // wait for all but the WAIT most recent loads and synchronise
-    auto step = [&](auto wait_c, auto load_c, int st, const uint8_t* sb, uint8_t* ob, const typename Op::Src& ls,
-                    int lst) {
-      typename Op::Frag f0, f1;
-      const bool live = st < NS;
-      const bool two = 2 * st + 1 < op.C_;   // the step's second chunk exists
-      // every LDS read of the step goes out first, then the step's LDS-DMA loads, then the MFMAs
-      // (the compiler makes an LDS read issued after LDS-DMA loads it cannot tell apart wait for
-      // all of them).  Past the last chunk the reads stay in bounds and go unused.
-      if (live) {
-        op.read(sb, f0, 0);
-        op.read(sb, f0, 1);
-        op.read(sb + C::CHUNK, f1, 0);
-        op.read(sb + C::CHUNK, f1, 1);
+    // step: the MFMAs on fc; with NEXT, the next step's fragment reads (from nb into fn) and
+    // step lst's loads (of ls, into ob) go out one after each MFMA, and the step ends waiting
+    // for all but the two most recent steps' loads and synchronising.  Chunks past the end of K
+    // (and padding steps) are loaded as zeros and computed like the others: no step branches.
+    auto step = [&](auto next_c, const uint8_t* nb, uint8_t* ob, const Frag (&fc)[C::KC], Frag (&fn)[C::KC],
+                    const typename Op::Src& ls, int lst) {
+      constexpr bool NEXT = decltype(next_c)::value;
+#pragma unroll
+      for (int k = 0; k < C::KC; k++) {
+        op.mma(fc[k], acc, 0);
+        if (NEXT) op.read(nb + k * C::CHUNK, fn[k], 0);
+        op.mma(fc[k], acc, 1);
+        if (NEXT) op.read(nb + k * C::CHUNK, fn[k], 1);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      if (decltype(load_c)::value) op.load(ls, lst, ob);
-      __builtin_amdgcn_sched_barrier(0);
-      if (live) {
-        op.mma(f0, acc, 0);
-        op.mma(f0, acc, 1);
-        if (two) {
-          op.mma(f1, acc, 0);
-          op.mma(f1, acc, 1);
-        }
+      if constexpr (NEXT) {
+        op.load(ls, lst, ob);
+        interleave<0, C::KC * C::TI * C::TJ, C::KC * (C::TI + C::TJ + 4), LPS>();
       }
-      vm_lds_barrier<decltype(wait_c)::value>();
+      // the step's MFMAs stay in the step (the compiler would otherwise move the last steps'
+      // down to the epilogue, where all their fragments would be live at once)
+#pragma unroll
+      for (int a = 0; a < C::TJ; a++)
+#pragma unroll
+        for (int b = 0; b < C::TI; b++) asm volatile("" ::"a"(acc[a][b]));
+      if constexpr (NEXT) wait_barrier<2 * LPS>();
     };
     int st = 0;
-    for (; st < NSE - 4; st += 4) {
-      step(IC<2 * LPS>{}, IC<1>{}, st, b0, b3, cur, st + 3);
-      step(IC<2 * LPS>{}, IC<1>{}, st + 1, b1, b0, cur, st + 4);
-      step(IC<2 * LPS>{}, IC<1>{}, st + 2, b2, b1, cur, st + 5);
-      step(IC<2 * LPS>{}, IC<1>{}, st + 3, b3, b2, cur, st + 6);
-    }
-    step(IC<2 * LPS>{}, IC<1>{}, st, b0, b3, cur, st + 3);     // the tile's last step
-    step(IC<2 * LPS>{}, IC<1>{}, st + 1, b1, b0, nxt, 0);      // the next tile's first
-    step(IC<LPS>{}, IC<0>{}, st + 2, b2, b1, cur, 0);
-    step(IC<0>{}, IC<0>{}, st + 3, b3, b2, cur, 0);
-    big_epilogue<C, RB, BIAS>(acc, b3, t, l2, bias, lam, M, N, m0, n0, y, [&]() {
-      op.load(nxt, 1, b1);
-      op.load(nxt, 2, b2);
-    });
+    do {                                       // NSE >= 8: at least once
+      step(IC<1>{}, b1, b0, fa, fb, cur, st + 4);
+      step(IC<1>{}, b2, b1, fb, fa, cur, st + 5);
+      step(IC<1>{}, b3, b2, fa, fb, cur, st + 6);
+      step(IC<1>{}, b0, b3, fb, fa, cur, st + 7);
+      st += 4;
+    } while (st < NSE - 4);
+    step(IC<1>{}, b1, b0, fa, fb, nxt, 0);
+    step(IC<1>{}, b2, b1, fb, fa, nxt, 1);
+    step(IC<1>{}, b3, b2, fa, fb, nxt, 2);
+    BigEpiIn<C, RB> ein;
+    big_epi_load<C, RB>(ein, t, l2, M, N, m0, n0);   // in flight during the last step's MFMAs
+    step(IC<0>{}, b0, b3, fb, fa, nxt, 3);
+    // b3 was read by the previous step (all waves: its barrier); the next tile's second step
+    // must be in before the barrier below
+    __builtin_amdgcn_s_waitcnt((LPS & 15) | (7 << 4) | ((LPS >> 4) << 14));   // vmcnt(LPS)
+    big_epilogue<C, RB, BIAS>(acc, b3, ein, bias, lam, M, N, m0, n0, y);
     if (!has_next) break;
+    read_step(b0, fa);                        // the next tile's first step
+    wait_barrier<63>();                       // the epilogue is done with b3, and b0 is read
+    op.load(nxt, 3, b3);
     tile = next;
     m0 = m1;
     n0 = n1;
@@ -583,28 +626,28 @@ k_gemm_mxb(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS-DMA in flight when the workgroup ends
 }
 
-// 256 x 256 tiles: waves of 64 x 128, two chunks a step
-using BigA = Big<4, 2, 2, 4, 2>;
+// 256 x 256 tiles: four waves of 128 x 128, two chunks a step
+using BigW = Big<2, 2, 4, 4, 2>;
 
 template <class C, int RB, bool BIAS>
-static hipError_t launch_mxb_t(const GemmArgs& a, hipStream_t s) {
+static hipError_t launch_mxw_t(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + C::BM - 1) / C::BM) * ((a.N + C::BN - 1) / C::BN);
   const int cus = resident_workgroups() / 2;
   const int nb = tiles < cus ? tiles : cus;
-  hipLaunchKernelGGL((k_gemm_mxb<C, RB, BIAS>), dim3(nb), dim3(C::NTH), 0, s, (const uint8_t*)a.xq,
+  hipLaunchKernelGGL((k_gemm_mxw<C, RB, BIAS>), dim3(nb), dim3(C::NTH), 0, s, (const uint8_t*)a.xq,
                      (const uint8_t*)a.xs, (const __half*)a.t, (const uint8_t*)a.wq, (const uint8_t*)a.ws,
                      (const __half*)a.l2, (const __half*)a.bias, a.lam, a.M, a.N, a.K, (__half*)a.y);
   return hipGetLastError();
 }
 
 template <class C, bool BIAS>
-static hipError_t launch_mxb_r(const GemmArgs& a, hipStream_t s) {
+static hipError_t launch_mxw_r(const GemmArgs& a, hipStream_t s) {
   switch (a.r) {
-    case 0: return launch_mxb_t<C, 0, BIAS>(a, s);
-    case 16: return launch_mxb_t<C, 1, BIAS>(a, s);
-    case 32: return launch_mxb_t<C, 2, BIAS>(a, s);
-    case 48: return launch_mxb_t<C, 3, BIAS>(a, s);
-    case 64: return launch_mxb_t<C, 4, BIAS>(a, s);
+    case 0: return launch_mxw_t<C, 0, BIAS>(a, s);
+    case 16: return launch_mxw_t<C, 1, BIAS>(a, s);
+    case 32: return launch_mxw_t<C, 2, BIAS>(a, s);
+    case 48: return launch_mxw_t<C, 3, BIAS>(a, s);
+    case 64: return launch_mxw_t<C, 4, BIAS>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -663,10 +706,10 @@ constexpr double kBigRound = 1.68;
 // few token rows most of a 256-row tile would be padding).
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t s) {
   const int slots = resident_workgroups(), cus = slots / 2;
-  const long big_tiles = (long)((a.M + BigA::BM - 1) / BigA::BM) * ((a.N + BigA::BN - 1) / BigA::BN);
+  const long big_tiles = (long)((a.M + BigW::BM - 1) / BigW::BM) * ((a.N + BigW::BN - 1) / BigW::BN);
   const double big = kBigRound * (double)((big_tiles + cus - 1) / cus);
-  if (big < rounds_128(a.M, a.N, slots))
-    return a.bias ? launch_mxb_r<BigA, true>(a, s) : launch_mxb_r<BigA, false>(a, s);
+  if (a.K >= 1024 && big < rounds_128(a.M, a.N, slots))
+    return a.bias ? launch_mxw_r<BigW, true>(a, s) : launch_mxw_r<BigW, false>(a, s);
   return a.bias ? launch_mx_r<true>(a, s) : launch_mx_r<false>(a, s);
 }
 

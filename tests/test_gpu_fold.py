@@ -104,8 +104,8 @@ def test_gemm_gelu_smooth_is_glue_of_gemm(fmt, shape, with_bias):
 @pytest.mark.parametrize("with_bias", [True, False])
 def test_gemm_gelu_smooth_mxfp4_large_tiles(with_bias):
     # the 256 x 256 tile epilogue with the glue folded in (MXFP4, one round of large tiles on 256
-    # CUs, ragged edges)
-    fmt, M, K, N, r = "mxfp4", 4000, 192, 4000, 32
+    # CUs, ragged edges, padding steps)
+    fmt, M, K, N, r = "mxfp4", 4000, 1088, 4000, 32
     log(f"gemm_w4a4_up_gelu_smooth large tiles {fmt} M={M} K={K} N={N} r={r} bias={with_bias}")
     x_hat, l1, l2, b, (xq, xs, xst), (wq, ws, wst), t = _gemm_inputs(fmt, M, K, N, r, 5 * M + N)
     lam = np.exp(np.random.default_rng(N + 1).uniform(np.log(0.2), np.log(8.0), N)).astype(np.float32)

@@ -261,12 +261,15 @@ def test_gemm_partial_last_round_long_k(fmt):
     assert ok, worst
 
 
-# MXFP4 at sizes where the launch takes 256 x 256 tiles (on 256 CUs): one round with ragged last
-# tile row and column and padded ring steps (K = 192: three chunks in two-chunk steps); two
-# tiles per workgroup, so the ring runs on into the next tile, with a one-chunk last step
-# (K = 320) and r = 64; and four rounds, the last one partial, with a half-empty last tile row
-@pytest.mark.parametrize("M,K,N,r,with_bias", [(4000, 192, 4000, 32, True), (4000, 192, 4000, 0, False),
-                                               (4096, 320, 8192, 64, True), (4224, 128, 12288, 32, True)])
+# MXFP4 at sizes where the launch takes 256 x 256 tiles (on 256 CUs, K >= 1024): one round with
+# ragged last tile row and column, a one-chunk last step and three padding steps (K = 1088: 17
+# chunks in two-chunk steps, rounded up to a multiple of four steps); two tiles per workgroup,
+# so the ring runs on into the next tile, with padding (K = 1216) and r = 64; four rounds, the
+# last one partial, with a half-empty last tile row, at the smallest K (1024: eight steps); and
+# a shape of the same size at K = 192, which stays on the 128 x 128 tiles
+@pytest.mark.parametrize("M,K,N,r,with_bias", [(4000, 1088, 4000, 32, True), (4000, 1088, 4000, 0, False),
+                                               (4096, 1216, 8192, 64, True), (4224, 1024, 12288, 32, True),
+                                               (4000, 192, 4000, 32, True)])
 def test_mxfp4_large_tiles(M, K, N, r, with_bias):
     fmt = "mxfp4"
     log(f"gemm_w4a4_up large tiles {fmt} M={M} K={K} N={N} r={r} bias={with_bias}")
