@@ -698,17 +698,23 @@ static double rounds_128(int M, int N, int slots) {
   return (double)(full + 1);
 }
 
-// One round of 256 x 256 tiles (one per CU) takes this many rounds of 128 x 128 tiles (two per
-// CU): measured at the fc1 shape (K = 3072) and the fc2 shape (K = 12288).
-constexpr double kBigRound = 1.68;
+// The 256 x 256 kernel's time in rounds of the 128 x 128 kernel: 1.40 of them per round of large
+// tiles with every CU busy, a last partial round 0.6 + 0.4 x its share of busy CUs (with fewer
+// CUs at work the chip holds a higher clock), and 0.35 for the start.  Fitted on M = 256 ... 4608
+// at K = 3072 (N = 12288, 9216, 4096) and on K = 12288; it picks the faster kernel at every
+// measured shape but M = 768 (K = 3072), where the two estimates tie.
+static double rounds_big(long tiles, int cus) {
+  const long full = tiles / cus, rem = tiles % cus;
+  const double u = (double)full + (rem ? 0.6 + 0.4 * (double)rem / (double)cus : 0.0);
+  return 0.35 + 1.40 * u;
+}
 
-// 256 x 256 tiles where their rounds cost less than the 128 x 128 kernel's (large M and N; at
-// few token rows most of a 256-row tile would be padding).
+// 256 x 256 tiles where they cost less than the 128 x 128 kernel's (large M and N; at few token
+// rows most of a 256-row tile would be padding), for K >= 1024 (the ring's eight steps).
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t s) {
   const int slots = resident_workgroups(), cus = slots / 2;
   const long big_tiles = (long)((a.M + BigW::BM - 1) / BigW::BM) * ((a.N + BigW::BN - 1) / BigW::BN);
-  const double big = kBigRound * (double)((big_tiles + cus - 1) / cus);
-  if (a.K >= 1024 && big < rounds_128(a.M, a.N, slots))
+  if (a.K >= 1024 && rounds_big(big_tiles, cus) < rounds_128(a.M, a.N, slots))
     return a.bias ? launch_mxw_r<BigW, true>(a, s) : launch_mxw_r<BigW, false>(a, s);
   return a.bias ? launch_mx_r<true>(a, s) : launch_mx_r<false>(a, s);
 }
