@@ -32,6 +32,9 @@ namespace {
 
 using namespace skel;
 
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ v8i fp4_operand(const uint4& c) {
   return v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
 }
@@ -338,15 +341,19 @@ struct IC {
   static constexpr int value = V;
 };
 
-// The epilogue's operands from global memory that are needed first: the tile's columns of L2
-// (staged through LDS) and the wave's rows of T.  Loaded before the tile's last step, so that
-// their latency hides behind its MFMAs.
+// The epilogue's operands from global memory: the tile's columns of L2 (staged through LDS) and
+// the wave's rows of T, loaded before the tile's last step so that their latency hides behind its
+// MFMAs (up to rank 32); the bias of the lane's columns and, with the MLP glue folded in, the next
+// layer's factors, loaded as the epilogue starts (earlier, their registers would spill).
 template <class C, int RB>
 struct BigEpiIn {
   static constexpr int R = RB * 16;
   static constexpr int L2P = RB > 0 ? (R * (C::BN / 8) + C::NTH - 1) / C::NTH : 1;   // 8-column pieces per thread
+  static constexpr int NG = (C::TJ + 1) / 2;   // output column groups of (up to) two tiles
   uint4 lv[L2P];
   uint4 top[RB > 0 ? RB : 1][C::TI];
+  uint2 braw[C::TJ][4];                       // the bias of the lane's columns
+  float4 la[NG], lb[NG];                      // with the MLP glue folded in: the next layer's factors
 };
 
 template <class C, int RB>
@@ -376,13 +383,46 @@ __device__ __forceinline__ void big_epi_load(BigEpiIn<C, RB>& e, const __half* _
   }
 }
 
+template <class C, int RB, bool BIAS>
+__device__ __forceinline__ void big_epi_load_bias(BigEpiIn<C, RB>& e, const __half* __restrict__ bias,
+                                                  const float* __restrict__ lam, int N, int n0) {
+  const int lane = threadIdx.x & 63, h = lane >> 5;
+  const int nw = n0 + (__builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) % C::WN) * C::TJ * 32;
+#pragma unroll
+  for (int tj = 0; tj < C::TJ; tj++)
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int n = nw + tj * 32 + 8 * q + 4 * h;
+      e.braw[tj][q] = make_uint2(0u, 0u);
+      if (BIAS && n < N) e.braw[tj][q] = *reinterpret_cast<const uint2*>(bias + n);
+    }
+  // the factors of the 8 columns this lane stores per group (loaded only with the glue: a load
+  // whose result no path uses would stay pending into the next tile, and the compiler's wait
+  // before its registers are rewritten would wait for every load)
+  const rsrc_t rl = make_rsrc(lam, lam ? (size_t)N * 4 : 0);
+#pragma unroll
+  for (int g = 0; g < BigEpiIn<C, RB>::NG; g++) {
+    e.la[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+    e.lb[g] = e.la[g];
+  }
+  if (lam) {
+#pragma unroll
+    for (int g = 0; g < BigEpiIn<C, RB>::NG; g++) {
+      const int pr = (C::TJ - 2 * g >= 2 ? 2 : 1) * 4;
+      const int cl = (lane % pr) * 8;
+      e.la[g] = load_f4(rl, nw + g * 64 + cl);
+      e.lb[g] = load_f4(rl, nw + g * 64 + cl + 4);
+    }
+  }
+}
+
 // acc += T L2 (RB > 0), bias, fp16 store: the 128 x 128 epilogue's operations for a TI x TJ block
 // of tiles per wave, with L2 and T from e.  eb: epilogue LDS, free.  Ends with the wave's LDS
 // work done but no barrier.
 template <class C, int RB, bool BIAS>
 __device__ __forceinline__ void big_epilogue(v16f (&acc)[C::TJ][C::TI], uint8_t* eb, const BigEpiIn<C, RB>& e,
-                                             const __half* __restrict__ bias, const float* __restrict__ lam, int M,
-                                             int N, int m0, int n0, __half* __restrict__ y) {
+                                             const float* __restrict__ lam, int M, int N, int m0, int n0,
+                                             __half* __restrict__ y) {
   constexpr int R = RB * 16;
   constexpr int LS2 = (R + 8) * 2;           // L2 staged transposed: [n][k], row stride R + 8 halves
   constexpr int L2P = BigEpiIn<C, RB>::L2P;
@@ -392,34 +432,6 @@ __device__ __forceinline__ void big_epilogue(v16f (&acc)[C::TJ][C::TI], uint8_t*
   const int h = lane >> 5, r32 = lane & 31;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int mw = m0 + wm * C::TI * 32, nw = n0 + wn * C::TJ * 32;   // the wave's block
-  uint2 braw[C::TJ][4];
-#pragma unroll
-  for (int tj = 0; tj < C::TJ; tj++)
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      const int n = nw + tj * 32 + 8 * q + 4 * h;
-      braw[tj][q] = make_uint2(0u, 0u);
-      if (BIAS && n < N) braw[tj][q] = *reinterpret_cast<const uint2*>(bias + n);
-    }
-  // with the MLP glue folded in, the next layer's factors of the 8 columns this lane stores per
-  // group (loaded only then: a load whose result no path uses would stay pending into the next
-  // tile, and the compiler's wait before its registers are rewritten would wait for every load)
-  const rsrc_t rl = make_rsrc(lam, lam ? (size_t)N * 4 : 0);
-  float4 la[NG], lb[NG];
-#pragma unroll
-  for (int g = 0; g < NG; g++) {
-    la[g] = make_float4(0.f, 0.f, 0.f, 0.f);
-    lb[g] = la[g];
-  }
-  if (lam) {
-#pragma unroll
-    for (int g = 0; g < NG; g++) {
-      const int pr = (C::TJ - 2 * g >= 2 ? 2 : 1) * 4;
-      const int cl = (lane % pr) * 8;
-      la[g] = load_f4(rl, nw + g * 64 + cl);
-      lb[g] = load_f4(rl, nw + g * 64 + cl + 4);
-    }
-  }
   if (RB > 0) {
 #pragma unroll
     for (int j = 0; j < L2P; j++) {
@@ -445,54 +457,79 @@ __device__ __forceinline__ void big_epilogue(v16f (&acc)[C::TJ][C::TI], uint8_t*
       }
     lds_barrier();                           // the output staging reuses the L2 staging bytes
   }
-  uint8_t* ys = eb + wave * 32 * E_YS;
   // columns in groups of two tiles (64 columns; a lone tile last when TJ is odd): each lane
   // stages its 16 values per tile as fp16 row pieces, then the group's rows leave as 16-byte
-  // pieces
+  // pieces.  Two staging slots per wave, used in turn, so that one wait per block of rows
+  // covers both its staging writes and the reads of the slot's previous use.
+  static_assert(C::BUF >= 2 * C::NW * 32 * E_YS, "two staging slots per wave");
+  // the wave's output rows from mw on: a store at an offset past M - mw rows is dropped
+  const rsrc_t ry = make_rsrc(y + (size_t)mw * N, mw < M ? (size_t)(M - mw) * N * 2 : 0);
 #pragma unroll
   for (int g = 0; g < NG; g++) {
     const int g0 = 2 * g;
     const int gt = C::TJ - g0 >= 2 ? 2 : 1;   // tiles in the group
     const int pr = gt * 4;                    // 16-byte pieces per staged row
     const int cl = (lane % pr) * 8;           // this lane's 8 columns within the group
+    float bv[2][4][4];                        // the bias of the lane's columns, once per group
+#pragma unroll
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const uint2 br = e.braw[u < gt ? g0 + u : g0][q];
+        bv[u][q][0] = __half2float(__ushort_as_half((unsigned short)(br.x & 0xFFFFu)));
+        bv[u][q][1] = __half2float(__ushort_as_half((unsigned short)(br.x >> 16)));
+        bv[u][q][2] = __half2float(__ushort_as_half((unsigned short)(br.y & 0xFFFFu)));
+        bv[u][q][3] = __half2float(__ushort_as_half((unsigned short)(br.y >> 16)));
+      }
 #pragma unroll
     for (int ti = 0; ti < C::TI; ti++) {
+      uint8_t* ys = eb + (wave * 2 + ((g * C::TI + ti) & 1)) * 32 * E_YS;
 #pragma unroll
       for (int u = 0; u < 2; u++) {
         if (u >= gt) continue;
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-          const uint2 br = braw[g0 + u][q];
-          const float bv[4] = {__half2float(__ushort_as_half((unsigned short)(br.x & 0xFFFFu))),
-                               __half2float(__ushort_as_half((unsigned short)(br.x >> 16))),
-                               __half2float(__ushort_as_half((unsigned short)(br.y & 0xFFFFu))),
-                               __half2float(__ushort_as_half((unsigned short)(br.y >> 16)))};
+          const v2f lo = {acc[g0 + u][ti][4 * q] + bv[u][q][0], acc[g0 + u][ti][4 * q + 1] + bv[u][q][1]};
+          const v2f hi = {acc[g0 + u][ti][4 * q + 2] + bv[u][q][2], acc[g0 + u][ti][4 * q + 3] + bv[u][q][3]};
           const int nl = u * 32 + 8 * q + 4 * h;
-          uint32_t hv[4];
-#pragma unroll
-          for (int j = 0; j < 4; j++) hv[j] = __half_as_ushort(__float2half_rn(acc[g0 + u][ti][4 * q + j] + bv[j]));
-          *reinterpret_cast<uint2*>(ys + r32 * E_YS + nl * 2) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+          *reinterpret_cast<uint2*>(ys + r32 * E_YS + nl * 2) =    // two round-to-nearest-even pairs
+              make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, v2h)),
+                         __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, v2h)));
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's staging writes are done
       __builtin_amdgcn_wave_barrier();
-      const int rows_it = 64 / pr;            // rows per pass
+      // the block's rows leave in NP passes of 64 / pr rows: every read first, the glue (one
+      // branch) on all of them, then buffer stores that drop what lies past the edge (no branch
+      // per store: a branch between a read and its store made each read wait for the last)
+      constexpr int NP = 32 * 8 / 64;         // passes (pr pieces per row, 64 lanes)
+      static_assert(C::TJ % 2 == 0, "two-tile groups");
+      uint2 pa[NP], pb[NP];
 #pragma unroll
-      for (int it = 0; it < 32 / rows_it; it++) {
-        const int rl = it * rows_it + lane / pr;
-        uint2 a = *reinterpret_cast<const uint2*>(ys + rl * E_YS + cl * 2);
-        uint2 b = *reinterpret_cast<const uint2*>(ys + rl * E_YS + cl * 2 + 8);
-        if (lam) {                           // the MLP glue folded in: fp16(gelu(y) / lam)
-          a.x = gelu_div_h(a.x & 0xFFFFu, la[g].x) | (gelu_div_h(a.x >> 16, la[g].y) << 16);
-          a.y = gelu_div_h(a.y & 0xFFFFu, la[g].z) | (gelu_div_h(a.y >> 16, la[g].w) << 16);
-          b.x = gelu_div_h(b.x & 0xFFFFu, lb[g].x) | (gelu_div_h(b.x >> 16, lb[g].y) << 16);
-          b.y = gelu_div_h(b.y & 0xFFFFu, lb[g].z) | (gelu_div_h(b.y >> 16, lb[g].w) << 16);
-        }
-        const int m = mw + ti * 32 + rl, n = nw + g0 * 32 + cl;
-        if (m < M && n < N) *reinterpret_cast<uint4*>(y + (size_t)m * N + n) = make_uint4(a.x, a.y, b.x, b.y);
+      for (int it = 0; it < NP; it++) {
+        const int rl = it * (64 / pr) + lane / pr;
+        pa[it] = *reinterpret_cast<const uint2*>(ys + rl * E_YS + cl * 2);
+        pb[it] = *reinterpret_cast<const uint2*>(ys + rl * E_YS + cl * 2 + 8);
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the staging is read before it is rewritten
-      __builtin_amdgcn_wave_barrier();
+      if (lam) {                             // the MLP glue folded in: fp16(gelu(y) / lam)
+#pragma unroll
+        for (int it = 0; it < NP; it++) {
+          uint2& a = pa[it];
+          uint2& b = pb[it];
+          a.x = gelu_div_h(a.x & 0xFFFFu, e.la[g].x) | (gelu_div_h(a.x >> 16, e.la[g].y) << 16);
+          a.y = gelu_div_h(a.y & 0xFFFFu, e.la[g].z) | (gelu_div_h(a.y >> 16, e.la[g].w) << 16);
+          b.x = gelu_div_h(b.x & 0xFFFFu, e.lb[g].x) | (gelu_div_h(b.x >> 16, e.lb[g].y) << 16);
+          b.y = gelu_div_h(b.y & 0xFFFFu, e.lb[g].z) | (gelu_div_h(b.y >> 16, e.lb[g].w) << 16);
+        }
+      }
+      const int n = nw + g0 * 32 + cl;
+#pragma unroll
+      for (int it = 0; it < NP; it++) {
+        const int rr = ti * 32 + it * (64 / pr) + lane / pr;   // row within the wave's block
+        const uint32_t off = n < N ? ((uint32_t)rr * (uint32_t)N + (uint32_t)n) * 2u : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4_t{pa[it].x, pa[it].y, pb[it].x, pb[it].y}, ry, (int)off, 0, 0);
+      }
     }
   }
 }
@@ -608,12 +645,15 @@ k_gemm_mxw(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const
     step(IC<1>{}, b2, b1, fb, fa, nxt, 1);
     step(IC<1>{}, b3, b2, fa, fb, nxt, 2);
     BigEpiIn<C, RB> ein;
-    big_epi_load<C, RB>(ein, t, l2, M, N, m0, n0);   // in flight during the last step's MFMAs
+    constexpr bool EARLY = RB <= 2;            // above rank 32 the registers would spill
+    if (EARLY) big_epi_load<C, RB>(ein, t, l2, M, N, m0, n0);   // in flight during the last step's MFMAs
     step(IC<0>{}, b0, b3, fb, fa, nxt, 3);
     // b3 was read by the previous step (all waves: its barrier); the next tile's second step
     // must be in before the barrier below
     __builtin_amdgcn_s_waitcnt((LPS & 15) | (7 << 4) | ((LPS >> 4) << 14));   // vmcnt(LPS)
-    big_epilogue<C, RB, BIAS>(acc, b3, ein, bias, lam, M, N, m0, n0, y);
+    if (!EARLY) big_epi_load<C, RB>(ein, t, l2, M, N, m0, n0);
+    big_epi_load_bias<C, RB, BIAS>(ein, bias, lam, N, n0);
+    big_epilogue<C, RB, BIAS>(acc, b3, ein, lam, M, N, m0, n0, y);
     if (!has_next) break;
     read_step(b0, fa);                        // the next tile's first step
     wait_barrier<63>();                       // the epilogue is done with b3, and b0 is read
