@@ -265,10 +265,12 @@ def test_gemm_partial_last_round_long_k(fmt):
 # ragged last tile row and column, a one-chunk last step and three padding steps (K = 1088: 17
 # chunks in two-chunk steps, rounded up to a multiple of four steps); two tiles per workgroup,
 # so the ring runs on into the next tile, with padding (K = 1216) and r = 64; four rounds, the
-# last one partial, with a half-empty last tile row, at the smallest K (1024: eight steps); and
+# last one partial, with a half-empty last tile row, at the smallest K (1024: eight steps); every
+# rank (the epilogue's operands load before the last step up to r = 32, at its start above); and
 # a shape of the same size at K = 192, which stays on the 128 x 128 tiles
 @pytest.mark.parametrize("M,K,N,r,with_bias", [(4000, 1088, 4000, 32, True), (4000, 1088, 4000, 0, False),
                                                (4096, 1216, 8192, 64, True), (4224, 1024, 12288, 32, True),
+                                               (4000, 1024, 4000, 16, True), (4000, 1024, 4000, 48, False),
                                                (4000, 192, 4000, 32, True)])
 def test_mxfp4_large_tiles(M, K, N, r, with_bias):
     fmt = "mxfp4"
