@@ -18,12 +18,13 @@
 // with rows laid out along K instead, each 16-byte load would touch 32 cache lines 1.5 KB apart
 // and the staging ran at half the bandwidth.
 //
-// Stages of four 64-K chunks on the shared persistent skeleton (two chunks a stage left each
-// stage waiting on the next one's loads: 142 -> 129 us at the fc1 shape).  Per chunk and workgroup: each
-// operand's 128 rows x 32 code bytes arrive by 16-byte LDS-DMA loads into 16-byte slots
-// swapped by row (slot c of row r at c ^ ((r / 8) % 2)), and the rows' 2 scale bytes by 2-byte
-// loads into 4-byte slots.  Lane half h reads the chunk's codes 32 h .. 32 h + 31 (one
-// 16-byte read) and scale byte h.
+// Two kernels.  128 x 128 tiles: stages of four 64-K chunks on the shared persistent skeleton
+// (two chunks a stage left each stage waiting on the next one's loads: 142 -> 129 us at the fc1
+// shape).  Per chunk and workgroup: each operand's 128 rows x 32 code bytes arrive by 16-byte
+// LDS-DMA loads into 16-byte slots swapped by row (slot c of row r at c ^ ((r / 8) % 2)), and
+// the rows' 2 scale bytes by 2-byte loads into 4-byte slots.  Lane half h reads the chunk's codes
+// 32 h .. 32 h + 31 (one 16-byte read) and scale byte h.  256 x 256 tiles on four waves for
+// large M, N and K (k_gemm_mxw, below); launch_gemm_mx picks the cheaper.
 #include "gemm_skel.h"
 
 namespace svdq {
@@ -540,8 +541,8 @@ __device__ __forceinline__ void big_epilogue(v16f (&acc)[C::TJ][C::TI], uint8_t*
 // 256 accumulators in the matrix cores' registers), with the LDS reads one step ahead of the
 // MFMAs: while a step's MFMAs run on fragments already in registers, the next step's fragment
 // reads and the step's LDS-DMA loads go out one after each MFMA, so the matrix core works while
-// the LDS serves the reads.  Per chunk and CU the LDS carries 20 KB of DMA writes and 40 KB of
-// fragment reads for 64 tile-MFMAs (eight waves of 64 x 128: 60 KB).  Ring of four buffers,
+// the LDS serves the reads.  Per chunk and CU the LDS carries 18 KB of DMA writes and 40 KB of
+// fragment and scale reads for 64 tile-MFMAs (eight waves of 64 x 128 would read 60 KB).  Ring of four buffers,
 // loads four steps ahead: a buffer is read into registers one step before its MFMAs, so the
 // step after that may load it again.  At a tile's end the ring carries on into the next tile:
 // the tile's last four steps load the next tile's first three and the last step loads nothing
