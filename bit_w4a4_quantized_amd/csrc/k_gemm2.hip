@@ -43,14 +43,13 @@ __device__ __forceinline__ uint32_t nib_hi16(uint32_t w) { return w & 0xF0F0F0F0
 // int32 result is 256 P_g exactly; the scale-product MFMA gives S = sw sx, one fma per element
 // and group adds 256 P_g S, and the accumulator is scaled by 1/256 once (exact).  The waves'
 // partial sums are added in LDS in wave order; wave 0 adds T L2 and the bias and stores.
-template <int RB, bool BIAS, int MT>
+template <int RB, bool BIAS, int MT, int PD>
 __global__ void __launch_bounds__(NTHREADS, 2)
 k_gemm2_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __half* __restrict__ t,
                const uint8_t* __restrict__ wq, const __half* __restrict__ ws, const __half* __restrict__ l2,
                const __half* __restrict__ bias, const float* __restrict__ lam, int M, int N, int K,
                __half* __restrict__ y) {
   constexpr int R = RB * 16;
-  constexpr int PD = MT <= 2 ? 4 : 2;       // groups in flight per wave
   __shared__ __attribute__((aligned(16))) float red[3][16][64];   // partials of waves 1..3, one row tile
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -121,8 +120,12 @@ k_gemm2_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, co
 #pragma unroll
     for (int j = 0; j < PD; j++) {
       const int st = s0 + j;
-      const bool zero = h || st < PD || st - PD >= ng;   // upper K half, or an empty slot
+      // a slot without a group (st < PD, or past the wave's last group) adds nothing: its
+      // work is skipped (a wave-uniform branch; the slot's refill below is unconditional)
+      const bool empty = st < PD || st - PD >= ng;
+      const bool zero = h;                   // the upper K half's lanes carry no scale
       const Op& cur = ring[j];
+      if (!empty) {
       const v4i w0 = v4i{(int)nib_lo16(cur.w.x), (int)nib_hi16(cur.w.x), (int)nib_lo16(cur.w.y), (int)nib_hi16(cur.w.y)};
       const v4i w1 = v4i{(int)nib_lo16(cur.w.z), (int)nib_hi16(cur.w.z), (int)nib_lo16(cur.w.w), (int)nib_hi16(cur.w.w)};
 #pragma unroll
@@ -138,6 +141,7 @@ k_gemm2_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, co
                                                               v16f{}, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 16; i++) acc[mt][i] = __builtin_fmaf((float)p[i], sc[i], acc[mt][i]);
+      }
       }
       load(ng > 0 ? wave + 4 * min(st, ng - 1) : 0, ring[j]);
       __builtin_amdgcn_sched_barrier(0);     // keep the slots in order: each waits for its own loads only
@@ -346,12 +350,12 @@ static hipError_t launch_g2_lds(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Up to this many token rows the weight-streaming kernel runs (in 128-row slabs).
+// Up to this many token rows the weight-streaming kernel runs (in 32- or 128-row slabs).
 constexpr int kSkinnyRows2 = 256;
 
-template <int RB, bool BIAS, int MT>
+template <int RB, bool BIAS, int MT, int PD = (MT <= 2 ? 4 : 2)>
 static hipError_t launch_g2_skinny(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm2_skinny<RB, BIAS, MT>), dim3((a.N + 31) / 32, (a.M + 32 * MT - 1) / (32 * MT)),
+  hipLaunchKernelGGL((k_gemm2_skinny<RB, BIAS, MT, PD>), dim3((a.N + 31) / 32, (a.M + 32 * MT - 1) / (32 * MT)),
                      dim3(NTHREADS), 0, s, (const uint8_t*)a.xq, (const __half*)a.xs, (const __half*)a.t,
                      (const uint8_t*)a.wq, (const __half*)a.ws, (const __half*)a.l2, (const __half*)a.bias, a.lam,
                      a.M, a.N, a.K, (__half*)a.y);
@@ -360,8 +364,10 @@ static hipError_t launch_g2_skinny(const GemmArgs& a, hipStream_t s) {
 
 template <int RB, bool BIAS>
 static hipError_t launch_g2(const GemmArgs& a, hipStream_t s) {
-  if (a.M <= 32) return launch_g2_skinny<RB, BIAS, 1>(a, s);
-  if (a.M <= 64) return launch_g2_skinny<RB, BIAS, 2>(a, s);
+  // 32-row slabs up to 192 rows: three such workgroups fit a CU, which spreads the column
+  // blocks over the CUs more evenly than 64- or 128-row slabs; at 256 rows the 128-row slabs,
+  // which unpack each weight fragment once for four row tiles, are faster
+  if (a.M <= 192) return launch_g2_skinny<RB, BIAS, 1>(a, s);
   if (a.M <= kSkinnyRows2) return launch_g2_skinny<RB, BIAS, 4>(a, s);
   return launch_g2_lds<RB, BIAS>(a, s);
 }

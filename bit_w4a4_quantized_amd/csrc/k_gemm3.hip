@@ -542,14 +542,13 @@ k_gemm3(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __h
 // (groups w, w + 4, ...), holding PD groups of loads in flight straight into registers, and add
 // their partial sums in LDS in a fixed order, one row tile at a time; wave 0 then applies the up
 // projection and the bias and stores.
-template <int RB, bool BIAS, int MT>
+template <int RB, bool BIAS, int MT, int PD>
 __global__ void __launch_bounds__(NT, 2)
 k_gemm3_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, const __half* __restrict__ t,
                const uint8_t* __restrict__ wq, const __half* __restrict__ ws, const __half* __restrict__ l2,
                const __half* __restrict__ bias, const float* __restrict__ lam, int M, int N, int K,
                __half* __restrict__ y) {
   constexpr int R = RB * 16;
-  constexpr int PD = MT <= 2 ? 4 : 2;       // groups in flight per wave
   __shared__ __attribute__((aligned(16))) float red[3][16][64];   // partials of waves 1..3, one row tile
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -620,6 +619,7 @@ k_gemm3_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, co
 #pragma unroll
     for (int j = 0; j < PD; j++) {
       const int st = s0 + j;
+      // (skipping the work of the empty slots behind a wave-uniform branch measured slower here)
       const bool zero = h || st < PD || st - PD >= ng;   // upper K half, or an empty slot
       const Op& cur = ring[j];
       const v8i wo = v8i{(int)cur.w0.x, (int)cur.w0.y, (int)cur.w0.z, (int)cur.w0.w, (int)cur.w1.x, (int)cur.w1.y, 0, 0};
@@ -701,9 +701,9 @@ k_gemm3_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, co
 // Up to this many token rows the weight-streaming kernel runs (in 128-row slabs).
 constexpr int kSkinnyRows = 256;
 
-template <int RB, bool BIAS, int MT>
+template <int RB, bool BIAS, int MT, int PD = (MT <= 2 ? 4 : 2)>
 static hipError_t launch_g3_skinny(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm3_skinny<RB, BIAS, MT>), dim3((a.N + 31) / 32, (a.M + 32 * MT - 1) / (32 * MT)),
+  hipLaunchKernelGGL((k_gemm3_skinny<RB, BIAS, MT, PD>), dim3((a.N + 31) / 32, (a.M + 32 * MT - 1) / (32 * MT)),
                      dim3(NT), 0, s, (const uint8_t*)a.xq,
                      (const __half*)a.xs, (const __half*)a.t, (const uint8_t*)a.wq, (const __half*)a.ws,
                      (const __half*)a.l2, (const __half*)a.bias, a.lam, a.M, a.N, a.K, (__half*)a.y);
