@@ -115,6 +115,9 @@ def parse():
     ap.add_argument("--no-extras", action="store_true", help="headline only: skip the other workloads "
                                                                "and the bare / unfused / W4A16 comparisons")
     ap.add_argument("--extra-steps", type=int, default=30)
+    ap.add_argument("--small-batch-only", action="store_true",
+                    help="only the small-batch sweep of the fc1 shape (M = 64, 256, 1024) in --fmt, "
+                         "one JSON object (for kernel traces of these launches)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
     ap.add_argument("--settle-ms", type=float, default=60.0,
                     help="untimed steps of the same work for at least this long before each warm-up "
@@ -610,6 +613,11 @@ def main():
     binding.lib()
     fmt = args.fmt
 
+    if args.small_batch_only:
+        Lo = Layer(torch, binding, "fc1", fmt)
+        print(json.dumps({"small_batch_fc1": small_batch_sweep(Lo, fmt, args.extra_steps, 5), "fmt": fmt}),
+              flush=True)
+        return
     L = Layer(torch, binding, args.workload, fmt, args.rank)
     M, K, N, r = L.M, L.K, L.N, L.r
     head = L.time_fused(args.steps, args.warmup)

@@ -104,14 +104,15 @@ MICROBENCH = os.path.join(BUILD_DIR, "mfma_valu")
 def build_microbench(verbose: bool = False) -> str:
     """The microbenchmarks, programs of their own (not part of the library): matrix-core /
     vector-ALU overlap (microbench/mfma_valu.hip), the operand load paths
-    (microbench/load_paths.hip) and the sustained matrix-core rates with the clock they hold
-    (microbench/mfma_clock.hip).  Returns the first program's path."""
+    (microbench/load_paths.hip), the sustained matrix-core rates with the clock they hold
+    (microbench/mfma_clock.hip) and the weight stream of the few-token-rows kernel
+    (microbench/weight_stream.hip).  Returns the first program's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     # mfma_valu without the VGPR-form flag: its AGPR cases need the compiler free to put MFMA
     # results in AGPRs (the others get the VGPR form either way)
     no_vgpr_form = source_flags("k_gemm_mx.hip")
     _run([hipcc(), *no_vgpr_form, os.path.join(HERE, "microbench", "mfma_valu.hip"), "-o", MICROBENCH], verbose)
-    for prog in ("load_paths", "mfma_clock"):
+    for prog in ("load_paths", "mfma_clock", "weight_stream"):
         _run([hipcc(), *FLAGS, os.path.join(HERE, "microbench", prog + ".hip"), "-o", os.path.join(BUILD_DIR, prog)],
              verbose)
     return MICROBENCH

@@ -390,19 +390,21 @@ k_quant_down(const __half* __restrict__ x, const __half* __restrict__ l1t, int M
 }
 
 // T = fp16_rne( sum over slices s = 0, 1, ... of part[s] ), slices added in order; each
-// thread issues up to 8 slices' loads before adding them.
+// thread issues up to 16 slices' loads before adding them (few token rows slice K into 12:
+// one round of loads instead of two).
 __global__ void __launch_bounds__(64)
 k_t_finalize(const float* __restrict__ part, int S, size_t MR, __half* __restrict__ t) {
+  constexpr int SR = 16;
   const size_t i = ((size_t)blockIdx.x * 64 + threadIdx.x) * 4;
   if (i >= MR) return;
   float4 a = *reinterpret_cast<const float4*>(part + i);
-  for (int s0 = 1; s0 < S; s0 += 8) {
-    float4 b[8];
+  for (int s0 = 1; s0 < S; s0 += SR) {
+    float4 b[SR];
 #pragma unroll
-    for (int k = 0; k < 8; k++)
+    for (int k = 0; k < SR; k++)
       if (s0 + k < S) b[k] = *reinterpret_cast<const float4*>(part + (size_t)(s0 + k) * MR + i);
 #pragma unroll
-    for (int k = 0; k < 8; k++)
+    for (int k = 0; k < SR; k++)
       if (s0 + k < S) { a.x += b[k].x; a.y += b[k].y; a.z += b[k].z; a.w += b[k].w; }
   }
   const uint32_t h0 = __half_as_ushort(__float2half_rn(a.x)) | ((uint32_t)__half_as_ushort(__float2half_rn(a.y)) << 16);

@@ -1,0 +1,113 @@
+// Weight-stream microbenchmark: how long one kernel takes to read the packed INT4 weights of
+// the fc1 shape (N = 12288, K = 3072: 18.9 MB, group-major [K/64][N][32 bytes]) with no
+// arithmetic, in the access pattern of the few-token-rows kernel and as a plain contiguous
+// read, against an empty launch.  Three copies of the buffer rotate, as in the benchmark.
+//
+//   python -m bit_w4a4_quantized_amd.build --microbench
+//   timeout -k 10 60 bit_w4a4_quantized_amd/_build/weight_stream
+//
+// Every kernel xors what it reads into a register and stores it only under a condition the
+// data never meet, so the loads stay and nothing is written.
+#include <hip/hip_runtime.h>
+#include <cstdio>
+#include <vector>
+
+#define CK(x)                                                                        \
+  do {                                                                               \
+    hipError_t e_ = (x);                                                             \
+    if (e_ != hipSuccess) {                                                          \
+      std::printf("HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__);     \
+      return 1;                                                                      \
+    }                                                                                \
+  } while (0)
+
+__device__ __forceinline__ void mix(uint4& a, const uint4& v) { a.x ^= v.x; a.y ^= v.y; a.z ^= v.z; a.w ^= v.w; }
+
+// grid-stride contiguous read, 16 bytes per lane, U loads per lane in flight
+template <int U>
+__global__ void __launch_bounds__(256) read_contiguous(const uint4* __restrict__ p, size_t n16, uint4* __restrict__ sink) {
+  const size_t tid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * 256;
+  uint4 acc = make_uint4(0, 0, 0, 0);
+  for (size_t i = tid; i < n16; i += stride * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const size_t idx = i + (size_t)u * stride;
+      v[u] = idx < n16 ? p[idx] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) mix(acc, v[u]);
+  }
+  if (acc.x == 0x9e3779b9u && acc.y == 1u) sink[tid & 1023] = acc;
+}
+
+// the few-token-rows kernel's pattern: one workgroup per 32 weight rows, wave w reads groups
+// w, w + 4, ...; lane (r, h) the 16 bytes at (g N + n) 32 + 16 h; U groups in flight per wave
+template <int U>
+__global__ void __launch_bounds__(256) read_weight_slabs(const uint8_t* __restrict__ p, int N, int G, uint4* __restrict__ sink) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = blockIdx.x * 32 + (lane & 31), h = lane >> 5;
+  uint4 acc = make_uint4(0, 0, 0, 0);
+  for (int g0 = wave; g0 < G; g0 += 4 * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int g = g0 + 4 * u;
+      v[u] = g < G ? *reinterpret_cast<const uint4*>(p + ((size_t)g * N + n) * 32 + 16 * h) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) mix(acc, v[u]);
+  }
+  if (acc.x == 0x9e3779b9u && acc.y == 1u) sink[threadIdx.x] = acc;
+}
+
+int main() {
+  const int N = 12288, K = 3072, G = K / 64;
+  const size_t bytes = (size_t)N * K / 2;
+  const size_t n16 = bytes / 16;
+  constexpr int NB = 3;
+  uint8_t* bufs[NB];
+  for (int i = 0; i < NB; i++) {
+    CK(hipMalloc(&bufs[i], bytes));
+    CK(hipMemset(bufs[i], i + 1, bytes));
+  }
+  uint4* sink;
+  CK(hipMalloc(&sink, 1024 * sizeof(uint4)));
+  hipEvent_t e0, e1;
+  CK(hipEventCreate(&e0));
+  CK(hipEventCreate(&e1));
+  std::printf("%.1f MB per read; microseconds per launch, back-to-back launches, best of 5 x 60\n", bytes / 1e6);
+  auto timeit = [&](const char* name, auto launch) -> int {
+    for (int i = 0; i < 300; i++) launch(bufs[i % NB]);
+    CK(hipDeviceSynchronize());
+    float best = 1e30f;
+    for (int rep = 0; rep < 5; rep++) {
+      CK(hipEventRecord(e0));
+      for (int i = 0; i < 60; i++) launch(bufs[i % NB]);
+      CK(hipEventRecord(e1));
+      CK(hipEventSynchronize(e1));
+      float ms;
+      CK(hipEventElapsedTime(&ms, e0, e1));
+      best = ms < best ? ms : best;
+    }
+    CK(hipGetLastError());
+    const double us = best * 1e3 / 60;
+    std::printf("| %s | %.2f | %.0f |\n", name, us, bytes / us / 1e3);
+    return 0;
+  };
+  std::printf("| kernel | us | GB/s of the 18.9 MB |\n|---|---|---|\n");
+  if (timeit("empty launch, 4096 workgroups", [&](uint8_t* b) { read_contiguous<1><<<4096, 256>>>((const uint4*)b, 0, sink); })) return 1;
+  for (int wg : {512, 1024, 2048, 4096}) {
+    char nm[96];
+    std::snprintf(nm, sizeof nm, "contiguous, %d workgroups, 1 load in flight per lane", wg);
+    if (timeit(nm, [&](uint8_t* b) { read_contiguous<1><<<wg, 256>>>((const uint4*)b, n16, sink); })) return 1;
+    std::snprintf(nm, sizeof nm, "contiguous, %d workgroups, 4 loads in flight per lane", wg);
+    if (timeit(nm, [&](uint8_t* b) { read_contiguous<4><<<wg, 256>>>((const uint4*)b, n16, sink); })) return 1;
+  }
+  if (timeit("weight slabs (384 workgroups), 2 groups in flight per wave", [&](uint8_t* b) { read_weight_slabs<2><<<N / 32, 256>>>(b, N, G, sink); })) return 1;
+  if (timeit("weight slabs (384 workgroups), 4 groups in flight per wave", [&](uint8_t* b) { read_weight_slabs<4><<<N / 32, 256>>>(b, N, G, sink); })) return 1;
+  if (timeit("weight slabs (384 workgroups), 12 groups in flight per wave", [&](uint8_t* b) { read_weight_slabs<12><<<N / 32, 256>>>(b, N, G, sink); })) return 1;
+  std::printf("done\n");
+  return 0;
+}
