@@ -75,9 +75,10 @@ def _partial_round_shape():
     return 128 * tiles_m - 37, 192, 1024
 
 
-GELU_SHAPES = [  # M, K, N, r: every Kernel B path (weight streaming at M <= 256 for the 6-bit
-    # container, tiles, the sub-tile jobs of a last partial round, ragged edges)
-    (1, 64, 16, 0), (33, 192, 48, 32), (200, 320, 144, 32), (520, 320, 272, 32), (300, 128, 400, 48),
+GELU_SHAPES = [  # M, K, N, r: every Kernel B path (weight streaming at M <= 256 in 32-, 64- and
+    # 128-row slabs, tiles, the sub-tile jobs of a last partial round, ragged edges)
+    (1, 64, 16, 0), (33, 192, 48, 32), (150, 256, 80, 32), (200, 320, 144, 32), (520, 320, 272, 32),
+    (300, 128, 400, 48),
     "partial",
 ]
 
