@@ -80,6 +80,7 @@ WORKLOADS = {
     "fc2": (4608, 12288, 3072, 32, "c2_fc2"),
 }
 ROTATE = 3
+COLD_WEIGHT_COPIES = 16                # 16 weight copies: > 256 MB of MALL at fc1's shape
 SETTLE_MS = 60.0     # set from --settle-ms
 EVENT_EVERY = 5      # HIP events on every 5th timed step: three event records cost ~7 us of a
                      # ~178 us step (measured), so recording them on every step would inflate it
@@ -339,6 +340,55 @@ class Layer:
         del graphs
         return {"us_per_layer": res["layer"], "ka_us": res["ka"], "kb_us": res["kb"]}
 
+    def time_rows_graph_cold(self, m, replays, warmup, copies=COLD_WEIGHT_COPIES):
+        """As time_rows_graph, but every call of a graph reads its own copy of the weights
+        (codes, scales, L2, bias): `copies` copies hold more bytes than the 256 MB MALL, so each
+        call streams its weights from HBM, as a layer does when other layers' weights have
+        passed through the MALL since its last call.  Returns the layer's and Kernel B's us."""
+        b, torch = self.binding, self.torch
+        K, fmt = self.K, self.fmt
+        sets = self._row_sets(m)
+        st0 = self.sets[0]
+        wc = [dict(wq=st0["wq"].clone(), ws=st0["ws"].clone(), l2=None if st0["l2"] is None else st0["l2"].clone(),
+                   b=st0["b"].clone()) for _ in range(copies)]
+
+        def ka(st):
+            b.svdq_quantize_down(st["x"], st["l1t"], fmt, xq=st["xq"], xs=st["xs"], t=st["t"], workspace=st["wsa"])
+
+        def kb(st, w):
+            b.svdq_gemm_w4a4_up(st["xq"], st["xs"], st["t"], w["wq"], w["ws"], w["l2"], w["b"], K, fmt, y=st["y"])
+        for st in sets:
+            ka(st)
+            kb(st, wc[0])
+        torch.cuda.synchronize()
+        y_eager = sets[0]["y"].clone()
+        side = torch.cuda.Stream()
+        res = {}
+        for name, with_a in (("layer", True), ("kb", False)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for i in range(copies):
+                    if with_a:
+                        ka(sets[i % ROTATE])
+                    kb(sets[i % ROTATE], wc[i])
+            settle(torch, lambda i: g.replay())
+            for _ in range(warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(replays):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) * 1e3 / (replays * copies)
+            if not torch.equal(sets[0]["y"], y_eager):
+                raise RuntimeError(f"cold graph replay ({name}, M={m}) changed Y")
+            del g
+        del wc
+        torch.cuda.empty_cache()
+        return {"us_per_layer": res["layer"], "kb_us": res["kb"]}
+
     def _row_sets(self, m):
         b, torch = self.binding, self.torch
         K, N, r, fmt = self.K, self.N, self.r, self.fmt
@@ -567,6 +617,7 @@ def small_batch_sweep(Lo, fmt, es, ew, rows=(64, 256, 1024)):
     sweep = {}
     for m in rows:
         rs = Lo.time_rows_graph(m, 20, 3)
+        cold = Lo.time_rows_graph_cold(m, 10, 3)
         eager = Lo.time_rows(m, es, ew)
         prepared = Lo.time_rows_prepared(m, es, ew)
         a_b, b_b = algorithmic_bytes(m, Lo.K, Lo.N, Lo.r, fmt)
@@ -581,6 +632,9 @@ def small_batch_sweep(Lo, fmt, es, ew, rows=(64, 256, 1024)):
             "us_per_layer_eager_calls": round(eager["us_per_layer"], 2),
             "us_per_layer_eager_prepared_layer": round(prepared["us_per_call"], 2),
             "kernels_us": {"quantize_down": round(rs["ka_us"], 2), "gemm_w4a4_up": round(rs["kb_us"], 2)},
+            "us_per_layer_cold_weights": round(cold["us_per_layer"], 2),
+            "gemm_w4a4_up_us_cold_weights": round(cold["kb_us"], 2),
+            "cold_weights": f"{COLD_WEIGHT_COPIES} weight copies, one per call of the graph (more bytes than the 256 MB MALL)",
             "tops": round(m_ops / layer_s / 1e12, 2),
             "algorithmic_bytes": a_b + b_b,
             "container_extra_bytes": c_a + c_b,

@@ -1,7 +1,8 @@
 // Weight-stream microbenchmark: how long one kernel takes to read the packed INT4 weights of
 // the fc1 shape (N = 12288, K = 3072: 18.9 MB, group-major [K/64][N][32 bytes]) with no
 // arithmetic, in the access pattern of the few-token-rows kernel and as a plain contiguous
-// read, against an empty launch.  Three copies of the buffer rotate, as in the benchmark.
+// read, against an empty launch.  Copies of the buffer rotate: 3 (57 MB, which stay in the
+// 256 MB MALL, as the benchmark's three buffer sets do) or 16 (302 MB: every read from HBM).
 //
 //   python -m bit_w4a4_quantized_amd.build --microbench
 //   timeout -k 10 60 bit_w4a4_quantized_amd/_build/weight_stream
@@ -66,9 +67,10 @@ int main() {
   const int N = 12288, K = 3072, G = K / 64;
   const size_t bytes = (size_t)N * K / 2;
   const size_t n16 = bytes / 16;
-  constexpr int NB = 3;
-  uint8_t* bufs[NB];
-  for (int i = 0; i < NB; i++) {
+  constexpr int NBMAX = 16;
+  int NB = 3;
+  uint8_t* bufs[NBMAX];
+  for (int i = 0; i < NBMAX; i++) {
     CK(hipMalloc(&bufs[i], bytes));
     CK(hipMemset(bufs[i], i + 1, bytes));
   }
@@ -96,18 +98,21 @@ int main() {
     std::printf("| %s | %.2f | %.0f |\n", name, us, bytes / us / 1e3);
     return 0;
   };
-  std::printf("| kernel | us | GB/s of the 18.9 MB |\n|---|---|---|\n");
-  if (timeit("empty launch, 4096 workgroups", [&](uint8_t* b) { read_contiguous<1><<<4096, 256>>>((const uint4*)b, 0, sink); })) return 1;
-  for (int wg : {512, 1024, 2048, 4096}) {
-    char nm[96];
-    std::snprintf(nm, sizeof nm, "contiguous, %d workgroups, 1 load in flight per lane", wg);
-    if (timeit(nm, [&](uint8_t* b) { read_contiguous<1><<<wg, 256>>>((const uint4*)b, n16, sink); })) return 1;
-    std::snprintf(nm, sizeof nm, "contiguous, %d workgroups, 4 loads in flight per lane", wg);
-    if (timeit(nm, [&](uint8_t* b) { read_contiguous<4><<<wg, 256>>>((const uint4*)b, n16, sink); })) return 1;
+  for (int nb : {3, NBMAX}) {
+    NB = nb;
+    std::printf("\n%d rotating copies (%.0f MB)\n\n| kernel | us | GB/s of the 18.9 MB |\n|---|---|---|\n", nb, nb * bytes / 1e6);
+    if (timeit("empty launch, 4096 workgroups", [&](uint8_t* b) { read_contiguous<1><<<4096, 256>>>((const uint4*)b, 0, sink); })) return 1;
+    for (int wg : {512, 1024, 2048, 4096}) {
+      char nm[96];
+      std::snprintf(nm, sizeof nm, "contiguous, %d workgroups, 1 load in flight per lane", wg);
+      if (timeit(nm, [&](uint8_t* b) { read_contiguous<1><<<wg, 256>>>((const uint4*)b, n16, sink); })) return 1;
+      std::snprintf(nm, sizeof nm, "contiguous, %d workgroups, 4 loads in flight per lane", wg);
+      if (timeit(nm, [&](uint8_t* b) { read_contiguous<4><<<wg, 256>>>((const uint4*)b, n16, sink); })) return 1;
+    }
+    if (timeit("weight slabs (384 workgroups), 2 groups in flight per wave", [&](uint8_t* b) { read_weight_slabs<2><<<N / 32, 256>>>(b, N, G, sink); })) return 1;
+    if (timeit("weight slabs (384 workgroups), 4 groups in flight per wave", [&](uint8_t* b) { read_weight_slabs<4><<<N / 32, 256>>>(b, N, G, sink); })) return 1;
+    if (timeit("weight slabs (384 workgroups), 12 groups in flight per wave", [&](uint8_t* b) { read_weight_slabs<12><<<N / 32, 256>>>(b, N, G, sink); })) return 1;
   }
-  if (timeit("weight slabs (384 workgroups), 2 groups in flight per wave", [&](uint8_t* b) { read_weight_slabs<2><<<N / 32, 256>>>(b, N, G, sink); })) return 1;
-  if (timeit("weight slabs (384 workgroups), 4 groups in flight per wave", [&](uint8_t* b) { read_weight_slabs<4><<<N / 32, 256>>>(b, N, G, sink); })) return 1;
-  if (timeit("weight slabs (384 workgroups), 12 groups in flight per wave", [&](uint8_t* b) { read_weight_slabs<12><<<N / 32, 256>>>(b, N, G, sink); })) return 1;
   std::printf("done\n");
   return 0;
 }
