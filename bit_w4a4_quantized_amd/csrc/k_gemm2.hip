@@ -81,28 +81,43 @@ k_gemm2_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, co
       o.sx[mt] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rxs, (int)((uint32_t)mrow[mt] * 2u), (int)(gx * 2u), 0);
     }
   };
-  // the epilogue's operands (L2 columns, bias, and T rows when MT <= 2), loaded by every wave
-  // before the K loop so that their latency overlaps it (wave 0 uses them)
+  // the epilogue's operands (L2 columns, bias, and T rows when MT <= 2), loaded by wave 0, which
+  // alone uses them, before the K loop so that their latency overlaps it (from every wave they
+  // were 26 more load instructions per wave ahead of the ring's)
   constexpr int MTT = MT <= 2 ? MT : 1;
   uint32_t lv[RB > 0 ? RB : 1][8];
   uint4 tv[MTT][RB > 0 ? RB : 1];
-#pragma unroll
-  for (int kb = 0; kb < RB; kb++) {
-#pragma unroll
-    for (int e = 0; e < 8; e++) lv[kb][e] = __half_as_ushort(l2[(size_t)(kb * 16 + 8 * h + e) * N + n]);
-    if (MT <= 2) {
-#pragma unroll
-      for (int mt = 0; mt < MTT; mt++)
-        tv[mt][kb] = *reinterpret_cast<const uint4*>(t + (size_t)mrow[mt] * R + kb * 16 + 8 * h);
-    }
-  }
   uint2 braw[4];
   float4 lam4[4];                            // with the MLP glue folded in: the next layer's factors
-  const rsrc_t rl = make_rsrc(lam, lam ? (size_t)N * 4 : 0);
 #pragma unroll
-  for (int q = 0; q < 4; q++) {  // columns past N read the last four (their outputs are not stored)
-    braw[q] = BIAS ? *reinterpret_cast<const uint2*>(bias + min(nb + 8 * q + 4 * h, N - 4)) : make_uint2(0u, 0u);
-    lam4[q] = load_f4(rl, min(nb + 8 * q + 4 * h, N - 4));
+  for (int kb = 0; kb < (RB > 0 ? RB : 1); kb++) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) lv[kb][e] = 0u;
+#pragma unroll
+    for (int mt = 0; mt < MTT; mt++) tv[mt][kb] = make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    braw[q] = make_uint2(0u, 0u);
+    lam4[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (wave == 0) {
+#pragma unroll
+    for (int kb = 0; kb < RB; kb++) {
+#pragma unroll
+      for (int e = 0; e < 8; e++) lv[kb][e] = __half_as_ushort(l2[(size_t)(kb * 16 + 8 * h + e) * N + n]);
+      if (MT <= 2) {
+#pragma unroll
+        for (int mt = 0; mt < MTT; mt++)
+          tv[mt][kb] = *reinterpret_cast<const uint4*>(t + (size_t)mrow[mt] * R + kb * 16 + 8 * h);
+      }
+    }
+    const rsrc_t rl = make_rsrc(lam, lam ? (size_t)N * 4 : 0);
+#pragma unroll
+    for (int q = 0; q < 4; q++) {  // columns past N read the last four (their outputs are not stored)
+      if (BIAS) braw[q] = *reinterpret_cast<const uint2*>(bias + min(nb + 8 * q + 4 * h, N - 4));
+      if (lam) lam4[q] = load_f4(rl, min(nb + 8 * q + 4 * h, N - 4));
+    }
   }
   v16f acc[MT];
 #pragma unroll
@@ -160,7 +175,7 @@ k_gemm2_skinny(const uint8_t* __restrict__ xq, const __half* __restrict__ xs, co
       for (int i = 0; i < 16; i++)
         acc[mt][i] = (((acc[mt][i] + red[0][i][lane]) + red[1][i][lane]) + red[2][i][lane]) * (1.0f / 256.0f);
     }
-    __syncthreads();
+    if (mt + 1 < MT) __syncthreads();        // red is reused by the next row tile
   }
   if (wave != 0) return;
   // up projection: row operand L2^T (columns n, gathered once), column operand T (rows m)
