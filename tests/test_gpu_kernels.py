@@ -220,11 +220,14 @@ def test_gemm_partial_last_round(fmt, r, with_bias):
     assert ok, worst
 
 
-# Long K at few rows: each wave of the weight-streaming kernel (6-bit container, M <= 256) walks
-# K/256 groups through its register ring, and the other formats' K loops run many stages, so
-# every ring wraps several times; one case per row-tile count of the streaming kernel (1, 2, 4)
+# Long K at few rows: each wave of the weight-streaming kernels (6-bit container and packed INT4,
+# M <= 256) walks K/256 groups through its register ring, and the other formats' K loops run
+# many stages, so every ring wraps several times; cases for each row-tile count of the streaming
+# kernels (1, 2, 4 rows of 32 tiles per workgroup)
 RING_SHAPES = [(17, 1024, 272, 32), (64, 3072, 272, 32), (130, 3072, 272, 32), (256, 1024, 272, 64),
-               (64, 1024, 272, 0), (300, 3072, 272, 32)]
+               (64, 1024, 272, 0), (300, 3072, 272, 32),
+               # either side of the packed format's switch from 32- to 128-row slabs
+               (192, 1024, 272, 32), (193, 1024, 272, 32)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
