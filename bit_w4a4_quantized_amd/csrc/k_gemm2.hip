@@ -381,9 +381,12 @@ template <int RB, bool BIAS>
 static hipError_t launch_g2(const GemmArgs& a, hipStream_t s) {
   // 32-row slabs up to 192 rows: three such workgroups fit a CU, which spreads the column
   // blocks over the CUs more evenly than 64- or 128-row slabs; at 256 rows the 128-row slabs,
-  // which unpack each weight fragment once for four row tiles, are faster
-  if (a.M <= 192) return launch_g2_skinny<RB, BIAS, 1>(a, s);
-  if (a.M <= kSkinnyRows2) return launch_g2_skinny<RB, BIAS, 4>(a, s);
+  // which unpack each weight fragment once for four row tiles, are faster.  Ring depth: fewer
+  // groups in flight per wave get each wave's data sooner once every wave also has work to
+  // do with it (4 up to 32 rows, then 2; 1 for the 128-row slabs)
+  if (a.M <= 32) return launch_g2_skinny<RB, BIAS, 1, 4>(a, s);
+  if (a.M <= 192) return launch_g2_skinny<RB, BIAS, 1, 2>(a, s);
+  if (a.M <= kSkinnyRows2) return launch_g2_skinny<RB, BIAS, 4, 1>(a, s);
   return launch_g2_lds<RB, BIAS>(a, s);
 }
 

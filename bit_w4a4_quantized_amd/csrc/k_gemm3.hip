@@ -728,9 +728,11 @@ static hipError_t launch_g3_skinny(const GemmArgs& a, hipStream_t s) {
 template <int RB, bool BIAS>
 static hipError_t launch_g3(const GemmArgs& a, hipStream_t s) {
   // few token rows: the weight-streaming kernel
-  if (a.M <= 32) return launch_g3_skinny<RB, BIAS, 1>(a, s);
-  if (a.M <= 64) return launch_g3_skinny<RB, BIAS, 2>(a, s);
-  if (a.M <= kSkinnyRows) return launch_g3_skinny<RB, BIAS, 4>(a, s);
+  // ring depth: two groups in flight per wave (one for 128-row slabs) get each wave's data
+  // sooner than four (two) did
+  if (a.M <= 32) return launch_g3_skinny<RB, BIAS, 1, 2>(a, s);
+  if (a.M <= 64) return launch_g3_skinny<RB, BIAS, 2, 2>(a, s);
+  if (a.M <= kSkinnyRows) return launch_g3_skinny<RB, BIAS, 4, 1>(a, s);
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const int slots = resident_workgroups();
   const int rem = tiles % slots;
